@@ -1,0 +1,64 @@
+"""The five synthetic group shapes the path is tested and measured on.
+
+Shapes follow the workloads the PrefixFlow page trains on (flat GRPO groups
+[P || S_i], PrefixFlow §2.1; long-prefix RAG groups, §5.2 Claim 2.1; the
+large-N prefix-ratio sweep, §5.4 Claim 3) and the rollout trees of the HARTS
+page (§2.1, compact representation).  Inputs are synthetic N(0,1) draws; no
+dataset item is reproduced.
+"""
+from dataclasses import dataclass, field
+from typing import List, Optional, Tuple
+
+
+@dataclass(frozen=True)
+class Config:
+    cid: int
+    name: str
+    dtype: str                 # "f32" or "bf16": the dtype of every Q/K/V/O/dO tensor
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    prefix_len: int            # P (0 for the tree config)
+    # flat groups: suffix lengths (fixed) or a (lo, hi) range drawn per seed
+    n_suffix: int = 0
+    suffix_len: Optional[int] = None
+    suffix_len_range: Optional[Tuple[int, int]] = None
+    microbatches: int = 1      # Phase B calls; microbatch k takes suffixes in index order
+    # tree config: fan-out per level and node length per level (root first)
+    tree_levels: Optional[Tuple[Tuple[int, int], ...]] = None
+    seed: int = 0
+    note: str = ""
+
+    @property
+    def is_tree(self) -> bool:
+        return self.tree_levels is not None
+
+    @property
+    def group_size(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+
+CONFIGS: List[Config] = [
+    Config(1, "tiny-f32", "f32", 2, 2, 64, 256, n_suffix=4, suffix_len=64, seed=1,
+           note="parity only; fp32 end to end"),
+    Config(2, "gqa-bf16-p4096-n8x512", "bf16", 32, 8, 128, 4096, n_suffix=8, suffix_len=512,
+           seed=2, note="89% prefix ratio; one Phase-B call with all 8 suffixes"),
+    Config(3, "rag-bf16-p16384-n16-varlen", "bf16", 32, 8, 128, 16384, n_suffix=16,
+           suffix_len_range=(256, 2048), microbatches=4, seed=3,
+           note="suffix lengths uniform on [256, 2048] inclusive; 4 calls of 4 suffixes"),
+    Config(4, "sweep-bf16-p8192-n64x256", "bf16", 32, 8, 128, 8192, n_suffix=64, suffix_len=256,
+           microbatches=8, seed=4,
+           note="8 calls of 8 suffixes; the stated 83% prefix ratio does not match these "
+                "shapes (P/(P+S) = 97%); the shapes rule"),
+    Config(5, "tree-bf16-4096-4x1024-16x256", "bf16", 16, 4, 128, 0,
+           tree_levels=((1, 4096), (4, 1024), (4, 256)), seed=5,
+           note="DFS-preorder compact rows: root 4096, 4 children of 1024, 4 leaves of 256 each; "
+                "12288 compact rows, 16 trajectories"),
+]
+
+
+def get_config(cid: int) -> Config:
+    for c in CONFIGS:
+        if c.cid == cid:
+            return c
+    raise KeyError(f"no config {cid}")
