@@ -1,0 +1,385 @@
+#!/usr/bin/env python3
+"""Benchmark of the group attention hot path on one MI355X.
+
+One step = the whole path over one synthetic group: zero the fp32 gK/gV
+accumulators, Phase A (prefix causal forward), Phase B (suffix forward and
+backward over the cached prefix, accumulating gK/gV; one call per
+microbatch) and Phase C (prefix backward with gK/gV injected).  For the tree
+workload a step is the tree forward and backward.
+
+Printed JSON (one line): `value` is the Phase-B forward+backward throughput
+in algorithmic TFLOP/s (12 * head_dim FLOPs per visible (query, key) pair
+per query head: 4 forward, 8 backward; the backward's recompute of the
+scores is not counted), with inputs resident in HBM.  `roofline` is for the
+kernel with the largest share of the step, timed with HIP events recorded
+on its own stream around each of its launches.  `cpu_baseline` is the CPU
+oracle (fp32 numpy) timed on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3        # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, help="workload (1..5); 2 is the headline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample (0 disables)")
+    ap.add_argument("--json-out", default=None)
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------- work counts
+
+def flat_pairs(p, lens):
+    """Visible (query, key) pairs per query head of Phase B and of Phase A/C."""
+    lens = np.asarray(lens, dtype=np.int64)
+    return int(np.sum(lens * p + lens * (lens + 1) // 2)), p * (p + 1) // 2
+
+
+def tree_pairs(node_off, parent):
+    n = len(parent)
+    depth_rows = np.zeros(n, dtype=np.int64)   # rows of strict ancestors
+    for v in range(1, n):
+        u = parent[v]
+        depth_rows[v] = depth_rows[u] + (node_off[u + 1] - node_off[u])
+    total = 0
+    for v in range(n):
+        ln = int(node_off[v + 1] - node_off[v])
+        total += ln * int(depth_rows[v]) + ln * (ln + 1) // 2
+    return total
+
+
+# ---------------------------------------------------------------- GPU side
+
+class KernelTimer:
+    """Launch-hook consumer: HIP events around every kernel, on its own stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.open = {}
+        self.spans = []          # (label, start_event, end_event)
+        self.streams = {}
+
+    def __call__(self, label, stream, end):
+        torch = self.torch
+        if stream not in self.streams:
+            self.streams[stream] = torch.cuda.ExternalStream(stream) if stream else \
+                torch.cuda.default_stream()
+        ev = torch.cuda.Event(enable_timing=True)
+        ev.record(self.streams[stream])
+        if end == 0:
+            self.open[(label, stream)] = ev
+        else:
+            self.spans.append((label, self.open.pop((label, stream)), ev))
+
+    def summary(self):
+        out = {}
+        for label, a, b in self.spans:
+            ms = a.elapsed_time(b)
+            t = out.setdefault(label, [0, 0.0])
+            t[0] += 1
+            t[1] += ms
+        return {k: {"launches": n, "avg_ms": tot / n, "total_ms": tot} for k, (n, tot) in out.items()}
+
+
+def run_gpu(cfg, data, steps, warmup):
+    import torch
+
+    import shared_prefix_attention_pf_amd as pf
+
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    pdt = pf.PF_BF16 if cfg.dtype == "bf16" else pf.PF_F32
+    desc = pf.AttnDesc(cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, pdt)
+
+    def to_dev(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).to(tdt).to(dev)
+
+    stream = torch.cuda.current_stream()
+    res = {}
+    if cfg.is_tree:
+        node_off, parent = data["node_off"], data["parent"]
+        q, k, v, do = (to_dev(data[n]) for n in ("q", "k", "v", "do"))
+        c = q.shape[0]
+        o = torch.empty_like(q)
+        lse = torch.empty(cfg.num_q_heads, c, device=dev)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws_f = torch.empty(max(16, pf.pf_workspace_size(pf.PF_OP_TREE_FWD, desc, 0, c)),
+                           dtype=torch.uint8, device=dev)
+        ws_b = torch.empty(max(16, pf.pf_workspace_size(pf.PF_OP_TREE_BWD, desc, 0, c)),
+                           dtype=torch.uint8, device=dev)
+
+        def step(ev=None):
+            if ev:
+                ev[0].record(stream)
+            pf.pf_tree_attn_fwd(desc, node_off, parent, q, k, v, o, lse, ws_f)
+            pf.pf_tree_attn_bwd(desc, node_off, parent, q, k, v, o, lse, do, dq, dk, dv, ws_b)
+            if ev:
+                ev[1].record(stream)
+                ev[2].record(stream)
+                ev[3].record(stream)
+        phase_names = ("tree",)
+    else:
+        p = cfg.prefix_len
+        cu = data["cu_seqlens"]
+        q_p, k_p, v_p, do_p = (to_dev(data[n]) for n in ("q_p", "k_p", "v_p", "do_p"))
+        q_s, k_s, v_s, do_s = (to_dev(data[n]) for n in ("q_s", "k_s", "v_s", "do_s"))
+        t_rows = q_s.shape[0]
+        o_p = torch.empty_like(q_p)
+        lse_p = torch.empty(cfg.num_q_heads, p, device=dev)
+        o_s = torch.empty_like(q_s)
+        lse_s = torch.empty(cfg.num_q_heads, t_rows, device=dev)
+        dq_s, dk_s, dv_s = torch.empty_like(q_s), torch.empty_like(k_s), torch.empty_like(v_s)
+        dq_p, dk_p, dv_p = torch.empty_like(q_p), torch.empty_like(k_p), torch.empty_like(v_p)
+        gk = torch.empty(p, cfg.num_kv_heads, cfg.head_dim, device=dev)
+        gv = torch.empty_like(gk)
+        mbs = []
+        for a, b in data["microbatches"]:
+            r0, r1 = int(cu[a]), int(cu[b])
+            sub_cu = (cu[a:b + 1] - cu[a]).astype(np.int32)
+            sl = slice(r0, r1)
+            mbs.append(dict(cu=sub_cu, q=q_s[sl], k=k_s[sl], v=v_s[sl], do=do_s[sl], o=o_s[sl],
+                            lse=lse_s[:, sl], dq=dq_s[sl], dk=dk_s[sl], dv=dv_s[sl]))
+        max_rows = max(int(m["cu"][-1]) for m in mbs)
+        ws_bytes = max(pf.pf_workspace_size(op, desc, p, max_rows) for op in
+                       (pf.PF_OP_SUFFIX_FWD, pf.PF_OP_SUFFIX_BWD))
+        ws_bytes = max(ws_bytes, pf.pf_workspace_size(pf.PF_OP_PREFIX_BWD, desc, p, p))
+        ws = torch.empty(max(16, ws_bytes), dtype=torch.uint8, device=dev)
+        # LSE slices of a [Hq, rows] array are not contiguous: give each
+        # microbatch its own contiguous LSE buffer
+        for m in mbs:
+            m["lse"] = torch.empty(cfg.num_q_heads, int(m["cu"][-1]), device=dev)
+
+        def step(ev=None):
+            gk.zero_()
+            gv.zero_()
+            if ev:
+                ev[0].record(stream)
+            pf.pf_prefix_fwd(desc, p, q_p, k_p, v_p, o_p, lse_p, ws)
+            if ev:
+                ev[1].record(stream)
+            for m in mbs:
+                pf.pf_suffix_attn_fwd(desc, p, k_p, v_p, m["cu"], m["q"], m["k"], m["v"], m["o"],
+                                      m["lse"], ws)
+                pf.pf_suffix_attn_bwd_accum(desc, p, k_p, v_p, m["cu"], m["q"], m["k"], m["v"],
+                                            m["o"], m["lse"], m["do"], m["dq"], m["dk"], m["dv"],
+                                            gk, gv, ws)
+            if ev:
+                ev[2].record(stream)
+            pf.pf_prefix_bwd_inject(desc, p, q_p, k_p, v_p, o_p, lse_p, do_p, gk, gv, dq_p, dk_p,
+                                    dv_p, pdt, ws)
+            if ev:
+                ev[3].record(stream)
+        phase_names = ("A", "B", "C")
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K steps, per-phase events inside each step
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    phase_ms = {}
+    if cfg.is_tree:
+        phase_ms["tree"] = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+    else:
+        phase_ms["A"] = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+        phase_ms["B"] = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
+        phase_ms["C"] = sum(e[2].elapsed_time(e[3]) for e in evs) / steps
+    res["wall_ms_per_step"] = wall * 1e3 / steps
+    res["phase_ms"] = phase_ms
+
+    # per-kernel durations: the same steps again with the launch hook recording
+    # HIP events around every kernel on the stream it is launched on
+    timer = KernelTimer(torch)
+    pf.pf_set_launch_hook(timer)
+    try:
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+    finally:
+        pf.pf_set_launch_hook(None)
+    res["kernels"] = timer.summary()
+    res["device"] = torch.cuda.get_device_name(0)
+    res["cus"] = torch.cuda.get_device_properties(0).multi_processor_count
+    return res
+
+
+# ---------------------------------------------------------------- CPU oracle baseline
+
+def cpu_baseline(cfg, data, target_s):
+    """Time the oracle as it stands (fp32 numpy) on whole KV-head groups of the
+    workload until about target_s seconds of work; scale to TFLOP/s."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        pools = threadpool_info()
+        threads = max((p.get("num_threads", 1) for p in pools), default=1)
+        blas = ",".join(sorted({p.get("internal_api", "?") for p in pools}))
+    except Exception:
+        threads, blas = os.cpu_count(), "unknown"
+    g = cfg.group_size
+    d = cfg.head_dim
+    scale = 1.0 / math.sqrt(d)
+    hmap = np.zeros(g, dtype=np.int64)
+    done_groups, elapsed, flops = 0, 0.0, 0.0
+    for kvh in range(cfg.num_kv_heads):
+        heads = slice(kvh * g, (kvh + 1) * g)
+        t0 = time.perf_counter()
+        if cfg.is_tree:
+            oracle.tree_attention_direct(data["q"][:, heads], data["k"][:, kvh:kvh + 1],
+                                         data["v"][:, kvh:kvh + 1], data["do"][:, heads],
+                                         data["node_off"], data["parent"], scale, hmap,
+                                         dtype=np.float32)
+            pairs = tree_pairs(data["node_off"], data["parent"])
+        else:
+            oracle.suffix_attention(data["k_p"][:, kvh:kvh + 1], data["v_p"][:, kvh:kvh + 1],
+                                    data["q_s"][:, heads], data["k_s"][:, kvh:kvh + 1],
+                                    data["v_s"][:, kvh:kvh + 1], data["do_s"][:, heads],
+                                    data["cu_seqlens"], scale, hmap, dtype=np.float32)
+            pairs, _ = flat_pairs(cfg.prefix_len, np.diff(data["cu_seqlens"]))
+        elapsed += time.perf_counter() - t0
+        flops += 12.0 * d * pairs * g
+        done_groups += 1
+        if elapsed >= target_s:
+            break
+    what = "tree fwd+bwd" if cfg.is_tree else "Phase B fwd+bwd"
+    return {
+        "value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{what} of config {cfg.cid} on {done_groups} of {cfg.num_kv_heads} KV-head "
+                  f"groups ({done_groups * g} query heads), fp32 numpy, {elapsed:.1f} s",
+        "seconds": elapsed, "os_cpu_count": os.cpu_count(),
+        "affinity_cpus": len(os.sched_getaffinity(0)), "blas": blas,
+        "full_workload_seconds_extrapolated": elapsed * cfg.num_kv_heads / done_groups,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path runs on one GPU; see the sharding notes in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    from workloads import generate, get_config
+    cfg = get_config(args.config)
+    print(f"[bench] generating config {cfg.cid} ({cfg.name})", flush=True)
+    data = generate(cfg)
+    print("[bench] running GPU steps", flush=True)
+    gres = run_gpu(cfg, data, args.steps, args.warmup)
+    d, hq = cfg.head_dim, cfg.num_q_heads
+    if cfg.is_tree:
+        pairs_b = tree_pairs(data["node_off"], data["parent"])
+        pairs_a = 0
+        compact = int(data["node_off"][-1])
+        from oracle import tree_trajectories
+        expanded = int(sum(len(t) for t in tree_trajectories(data["node_off"], data["parent"])))
+        b_ms = gres["phase_ms"]["tree"]
+    else:
+        lens = np.diff(data["cu_seqlens"])
+        pairs_b, pairs_a = flat_pairs(cfg.prefix_len, lens)
+        compact = cfg.prefix_len + int(lens.sum())
+        expanded = int(np.sum(cfg.prefix_len + lens))
+        b_ms = gres["phase_ms"]["B"]
+    flops_b = 12.0 * d * pairs_b * hq
+    step_ms = sum(gres["phase_ms"].values())
+    value = flops_b / (b_ms * 1e-3) / 1e12
+
+    # roofline of the kernel with the largest total time
+    kern = gres["kernels"]
+    dom = max(kern, key=lambda k: kern[k]["total_ms"])
+    # algorithmic FLOPs per launch of each kernel (per visible pair per query head):
+    # forward 4d; dQ kernel 2d (dQ = dS K); dK/dV kernel 6d (dV, dP, dK)
+    per_pair = {"pf_fwd_bf16": 4, "pf_bwd_dq_bf16": 2, "pf_bwd_dkv_bf16": 6,
+                "pf_fwd_f32": 4, "pf_bwd_dq_f32": 2, "pf_bwd_dkv_f32": 6}
+    if dom in per_pair:
+        kn = kern[dom]
+        launches_per_step = kn["launches"] / args.steps
+        # total algorithmic pairs this kernel processes per step: Phase B pairs
+        # plus the prefix pairs of Phase A (fwd) or Phase C (bwd)
+        pairs_step = pairs_b + pairs_a
+        flops_per_launch = per_pair[dom] * d * pairs_step * hq / launches_per_step
+        achieved = flops_per_launch / (kn["avg_ms"] * 1e-3) / 1e12
+        peak = PEAK_BF16_TFLOPS if "bf16" in dom else PEAK_F32_TFLOPS
+        roofline = {"bound": "mfma" if "bf16" in dom else "alu", "kernel": dom,
+                    "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                    "frac": round(achieved / peak, 4), "traffic": None,
+                    "avg_launch_ms": round(kn["avg_ms"], 4),
+                    "algorithmic_flops_per_launch": flops_per_launch}
+    else:
+        roofline = {"bound": "hbm", "kernel": dom, "achieved": None, "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": None, "traffic": None}
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        print("[bench] timing the CPU oracle", flush=True)
+        cpu = cpu_baseline(cfg, data, args.cpu_seconds)
+
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    out = {
+        "metric": "suffix attn fwd+bwd TFLOP/s & % bf16 MFMA peak; group tokens/s vs oracle",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": f"config {cfg.cid}: {cfg.name}",
+            "num_q_heads": hq, "num_kv_heads": cfg.num_kv_heads, "head_dim": d,
+            "prefix_len": cfg.prefix_len,
+            "suffix_lens": (None if cfg.is_tree else
+                            np.diff(data["cu_seqlens"]).astype(int).tolist()),
+            "microbatches": None if cfg.is_tree else len(data["microbatches"]),
+            "parallelism": "single GPU",
+        },
+        "pct_of_bf16_peak": round(100.0 * value / peak, 2),
+        "phase_ms": {k: round(v, 4) for k, v in gres["phase_ms"].items()},
+        "phase_b_gflop": round(flops_b / 1e9, 2),
+        "group_tokens_per_s": {"compact": round(compact / (step_ms * 1e-3), 1),
+                               "expanded": round(expanded / (step_ms * 1e-3), 1)},
+        "wall_ms_per_step": round(gres["wall_ms_per_step"], 4),
+        "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv)
+                        for kk, vv in v.items()} for k, v in kern.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "device": gres["device"], "compute_units": gres["cus"],
+    }
+    if cpu:
+        # the oracle's rate on the same unit, and group tokens/s at that rate
+        ratio = value / cpu["value"] if cpu["value"] > 0 else None
+        out["gpu_over_oracle"] = round(ratio, 1) if ratio else None
+    line = json.dumps(out)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(line + "\n")
+    print(line, flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,212 @@
+/*
+ * pf.h — C ABI of the prefix/suffix attention library (gfx950 / MI355X).
+ *
+ * The library computes the attention work of one rollout group trained with
+ * a training-time KV cache, as described in "PrefixFlow: Training-Time KV
+ * Caching for Schedule-Level Prefix Reuse in LLM RL Training":
+ *
+ *   Phase A  pf_prefix_fwd             causal attention over the shared prefix,
+ *                                      run once per group (§3.1, "Phase A").
+ *   Phase B  pf_suffix_attn_fwd        suffix queries over the cached prefix
+ *            pf_suffix_attn_bwd_accum  K/V plus their own causal suffix, and its
+ *                                      backward, which ADDS the prefix-side
+ *                                      gradients gK/gV into fp32 accumulators
+ *                                      (§3.1 "Phase B", §3.3, §4.1, §4.2).
+ *   Phase C  pf_prefix_bwd_inject      the delayed prefix backward, with the
+ *                                      accumulated gK/gV added to the prefix
+ *                                      K/V gradients (§3.1 "Phase C", §4.1).
+ *   Trees    pf_tree_attn_fwd/bwd      compact rollout-tree rows under an
+ *                                      ancestor mask ("HARTS: A Prefix-Sharing
+ *                                      Training System for Agentic RL with
+ *                                      Hybrid-Attention Models", §2.1, §2.2, §3).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors of rows are [tokens, heads, head_dim] with head_dim contiguous,
+ *    described by pf_tensor (element strides).  Device pointers, 16-byte
+ *    aligned; strides multiples of 8 elements (bf16) or 4 (fp32).
+ *  - LSE arrays are fp32 [num_q_heads, rows], contiguous, natural log.
+ *  - gK/gV accumulators are fp32 [prefix_len, num_kv_heads, head_dim],
+ *    contiguous.
+ *  - Suffix and tree structure (cu_seqlens, node_off, parent) are HOST
+ *    arrays.  They are validated on the host and passed to the kernels by
+ *    value, so no call reads host memory after it returns.
+ *  - The caller allocates every device buffer, including the workspace,
+ *    sized by pf_workspace_size().  The library allocates nothing, keeps no
+ *    state between calls, never synchronises and never frees.
+ *  - All work is enqueued on `stream` (a hipStream_t; NULL = default stream)
+ *    and is asynchronous: a return of PF_OK means "launched".
+ *  - Every argument is validated before anything is launched.  On an error
+ *    return no HIP call has been made (except PF_ERR_HIP) and no output has
+ *    been touched; pf_last_error() gives a message (thread-local).
+ *  - Results are bitwise identical from run to run for the same inputs,
+ *    call sequence and device; there are no floating-point atomics.
+ *  - Calls on different streams may run concurrently unless they write the
+ *    same buffers; calls that add into one gK/gV accumulator must be ordered
+ *    (the same stream, or events).
+ */
+#ifndef PF_H_
+#define PF_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PF_ABI_VERSION 1
+/* Suffixes per Phase-B call, or nodes per tree. */
+#define PF_MAX_SEGMENTS 256
+/* Query heads per call. */
+#define PF_MAX_HEADS 256
+
+typedef enum {
+  PF_OK = 0,
+  PF_ERR_INVALID_ARG = 1,  /* a shape, pointer, stride or structure is invalid   */
+  PF_ERR_UNSUPPORTED = 2,  /* valid, but outside what the kernels implement      */
+  PF_ERR_WORKSPACE = 3,    /* workspace NULL or smaller than pf_workspace_size() */
+  PF_ERR_HIP = 4           /* a HIP launch failed; see pf_last_error()           */
+} pf_status;
+
+typedef enum { PF_F32 = 0, PF_BF16 = 1 } pf_dtype;
+
+typedef enum {
+  PF_OP_PREFIX_FWD = 0,
+  PF_OP_SUFFIX_FWD = 1,
+  PF_OP_SUFFIX_BWD = 2,
+  PF_OP_PREFIX_BWD = 3,
+  PF_OP_TREE_FWD = 4,
+  PF_OP_TREE_BWD = 5
+} pf_op;
+
+/* Attention head configuration of one layer (the caller's local head shard). */
+typedef struct {
+  int32_t num_q_heads;     /* Hq >= 1                                             */
+  int32_t num_kv_heads;    /* Hkv >= 1, Hq % Hkv == 0                             */
+  int32_t head_dim;        /* bf16: 128; fp32: 64 or 128                          */
+  int32_t dtype;           /* pf_dtype of Q, K, V, O, dO, dQ, dK, dV              */
+  float softmax_scale;     /* > 0, or <= 0 for 1/sqrt(head_dim)                   */
+  const int32_t* q_to_kv;  /* host [Hq]: KV head read by each query head, every KV
+                              head read by exactly Hq/Hkv query heads; or NULL for
+                              contiguous groups (query head h reads h / (Hq/Hkv)) */
+} pf_attn_desc;
+
+/* A [tokens, heads, head_dim] device tensor; head_dim is contiguous. */
+typedef struct {
+  void* data;
+  int64_t stride_tok;      /* elements between consecutive tokens */
+  int64_t stride_head;     /* elements between consecutive heads  */
+} pf_tensor;
+
+/* Bytes of device workspace `op` needs.  rows = prefix_len for the prefix
+ * ops, the total packed suffix rows for the suffix ops and the compact rows
+ * for the tree ops.  Pure host arithmetic; never fails (0 for bad args). */
+size_t pf_workspace_size(int32_t op, const pf_attn_desc* desc, int32_t prefix_len, int32_t rows);
+
+/* Phase A (PrefixFlow §3.1 "Phase A: prefix forward"): causal attention of
+ * the prefix over itself.
+ *   q_p [P, Hq, d], k_p, v_p [P, Hkv, d]  in
+ *   o_p [P, Hq, d]                        out (overwritten)
+ *   lse_p [Hq, P] fp32                    out (overwritten)              */
+pf_status pf_prefix_fwd(const pf_attn_desc* desc, int32_t prefix_len, pf_tensor q_p,
+                        pf_tensor k_p, pf_tensor v_p, pf_tensor o_p, float* lse_p,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Phase B forward (PrefixFlow §4.1: each suffix query sees every prefix
+ * token and its own suffix causally, never another suffix; §4.2: packed
+ * suffixes read the cached prefix K/V as one shared read-only block).  The
+ * prefix K/V are read in place; nothing is concatenated.
+ *   k_p, v_p [P, Hkv, d]                  in  (the cached prefix; P >= 0)
+ *   cu_seqlens host [n_suffix + 1]        in  (0 = cu[0] <= cu[1] <= ...; rows = cu[n])
+ *   q_s [rows, Hq, d], k_s, v_s [rows, Hkv, d]  in
+ *   o_s [rows, Hq, d]                     out
+ *   lse_s [Hq, rows] fp32                 out                            */
+pf_status pf_suffix_attn_fwd(const pf_attn_desc* desc, int32_t prefix_len, pf_tensor k_p,
+                             pf_tensor v_p, int32_t n_suffix, const int32_t* cu_seqlens,
+                             pf_tensor q_s, pf_tensor k_s, pf_tensor v_s, pf_tensor o_s,
+                             float* lse_s, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/* Phase B backward (PrefixFlow §3.3: prefix backward is linear in the
+ * adjoints at the K/V boundary, so per-suffix gK/gV may be summed; §4.1: the
+ * cached leaves accumulate them across suffix waves).
+ *   (forward arguments as above), o_s, lse_s from pf_suffix_attn_fwd,
+ *   do_s [rows, Hq, d]                    in
+ *   dq_s [rows, Hq, d]                    out (overwritten)
+ *   dk_s, dv_s [rows, Hkv, d]             out (overwritten; own-suffix part only)
+ *   gk_acc, gv_acc fp32 [P, Hkv, d]       in/out: this call's prefix-side
+ *                                         gradients are ADDED.  The caller zeroes
+ *                                         them once per group; replaying a call
+ *                                         adds twice.                          */
+pf_status pf_suffix_attn_bwd_accum(const pf_attn_desc* desc, int32_t prefix_len,
+                                   pf_tensor k_p, pf_tensor v_p, int32_t n_suffix,
+                                   const int32_t* cu_seqlens, pf_tensor q_s, pf_tensor k_s,
+                                   pf_tensor v_s, pf_tensor o_s, const float* lse_s,
+                                   pf_tensor do_s, pf_tensor dq_s, pf_tensor dk_s,
+                                   pf_tensor dv_s, float* gk_acc, float* gv_acc,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Phase C (PrefixFlow §3.1 "Phase C: prefix backward", §4.1): the causal
+ * prefix backward, with the accumulated gK/gV added in fp32 before the one
+ * rounding of dK_P/dV_P.
+ *   q_p, k_p, v_p, o_p, lse_p             in  (Phase A inputs and outputs)
+ *   do_p [P, Hq, d]                       in; do_p.data == NULL means a zero
+ *                                         upstream (dQ_P = 0, dK_P = gK_acc)
+ *   gk_acc, gv_acc fp32 [P, Hkv, d]       in
+ *   dq_p [P, Hq, d] (desc dtype)          out
+ *   dk_p, dv_p [P, Hkv, d] (dkv_dtype)    out; dkv_dtype is PF_F32 or desc dtype */
+pf_status pf_prefix_bwd_inject(const pf_attn_desc* desc, int32_t prefix_len, pf_tensor q_p,
+                               pf_tensor k_p, pf_tensor v_p, pf_tensor o_p, const float* lse_p,
+                               pf_tensor do_p, const float* gk_acc, const float* gv_acc,
+                               pf_tensor dq_p, pf_tensor dk_p, pf_tensor dv_p, int32_t dkv_dtype,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Tree forward (HARTS §2.1: positions with equal token prefixes share one
+ * compact row; §2.2: full attention reads ancestor K/V through a tree mask).
+ * Nodes are numbered in DFS preorder: parent[0] = -1, parent[i] < i, and a
+ * node's subtree occupies consecutive node numbers.  Node i owns compact
+ * rows [node_off[i], node_off[i+1]).  A row sees the rows of every strict
+ * ancestor of its node and the rows of its own node up to itself.
+ *   node_off host [n_nodes + 1], parent host [n_nodes]   in
+ *   q [C, Hq, d], k, v [C, Hkv, d]        in  (C = node_off[n_nodes])
+ *   o [C, Hq, d], lse [Hq, C] fp32        out                            */
+pf_status pf_tree_attn_fwd(const pf_attn_desc* desc, int32_t n_nodes, const int32_t* node_off,
+                           const int32_t* parent, pf_tensor q, pf_tensor k, pf_tensor v,
+                           pf_tensor o, float* lse, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* Tree backward (HARTS §3: the backward of a gather of ancestor K/V sums the
+ * gradients into the shared compact rows).  dK/dV of a row sum over every
+ * descendant row that reads it, and over the query heads of its KV head.
+ *   o, lse from pf_tree_attn_fwd; dout [C, Hq, d]    in
+ *   dq [C, Hq, d], dk, dv [C, Hkv, d]                out (overwritten)   */
+pf_status pf_tree_attn_bwd(const pf_attn_desc* desc, int32_t n_nodes, const int32_t* node_off,
+                           const int32_t* parent, pf_tensor q, pf_tensor k, pf_tensor v,
+                           pf_tensor o, const float* lse, pf_tensor dout, pf_tensor dq,
+                           pf_tensor dk, pf_tensor dv, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* Host-only helper: the end row of each node's subtree (exclusive), the
+ * bound of the rows that can read that node's keys.  Validates the tree.
+ * Used by the tree entry points; exposed for testing without a GPU.     */
+pf_status pf_tree_subtree_end(int32_t n_nodes, const int32_t* node_off, const int32_t* parent,
+                              int32_t* subtree_end);
+
+/* Profiling aid: when a hook is set, the library calls it on the host right
+ * before (end = 0) and right after (end = 1) enqueuing each kernel, with a
+ * short kernel label and the stream the kernel goes to, so a caller can
+ * record timing events on that stream around each kernel.  NULL removes the
+ * hook.  The hook is process-wide; set it while no other thread launches. */
+typedef void (*pf_launch_hook)(const char* kernel, void* stream, int32_t end, void* user);
+void pf_set_launch_hook(pf_launch_hook hook, void* user);
+
+const char* pf_status_string(pf_status status);
+const char* pf_last_error(void);
+int32_t pf_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PF_H_ */

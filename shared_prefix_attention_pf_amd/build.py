@@ -1,0 +1,66 @@
+"""Build libpf.so (the C-ABI library) in-tree with hipcc for gfx950.
+
+    python shared_prefix_attention_pf_amd/build.py
+
+Compiles every source under csrc/ into shared_prefix_attention_pf_amd/libpf.so.
+Packed fp32 VALU instructions are disabled for all device code.
+"""
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libpf.so")
+SOURCES = ["pf_api.cpp", "pf_prep.hip", "pf_attn_bf16.hip", "pf_attn_f32.hip"]
+ARCH = os.environ.get("PF_OFFLOAD_ARCH", "gfx950")
+
+
+def hipcc() -> str:
+    for cand in (os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc"),
+                 shutil.which("hipcc") or ""):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libpf.so)")
+
+
+def common_flags():
+    return [
+        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+        "-I", INCLUDE, "-I", CSRC,
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-Wall", "-Wno-unused-function",
+    ]
+
+
+def build(verbose: bool = False, resource_usage: bool = False) -> str:
+    cc = hipcc()
+    with tempfile.TemporaryDirectory(prefix="pf_build_") as tmp:
+        objs = []
+        for src in SOURCES:
+            obj = os.path.join(tmp, src + ".o")
+            cmd = [cc] + common_flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+            if src.endswith(".cpp"):
+                cmd[1:1] = ["-x", "hip"]
+            if resource_usage and src.endswith(".hip"):
+                cmd.append("-Rpass-analysis=kernel-resource-usage")
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            subprocess.run(cmd, check=True)
+            objs.append(obj)
+        tmp_lib = os.path.join(tmp, "libpf.so")
+        cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp_lib] + objs
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        shutil.copyfile(tmp_lib, LIB + ".tmp")
+        os.replace(LIB + ".tmp", LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv, resource_usage="--usage" in sys.argv))

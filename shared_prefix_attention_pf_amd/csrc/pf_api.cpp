@@ -1,0 +1,574 @@
+// Host side of the C ABI declared in include/pf.h: argument validation,
+// workspace layout, and the launch sequence of each entry point.  No entry
+// point allocates, synchronises or keeps state; every check runs before the
+// first HIP call.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "pf_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pf_status fail(pf_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+pf_status hip_fail(hipError_t e, const char* where) {
+  return fail(PF_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int elem_bytes(int32_t dtype) { return dtype == PF_BF16 ? 2 : 4; }
+
+// ---------------------------------------------------------------- validation
+
+struct Desc {
+  int hq, hkv, group, d, dtype;
+  float scale;
+  pf::HeadTable heads;
+};
+
+pf_status check_desc(const pf_attn_desc* desc, Desc* out) {
+  if (!desc) return fail(PF_ERR_INVALID_ARG, "desc is NULL");
+  const int hq = desc->num_q_heads, hkv = desc->num_kv_heads, d = desc->head_dim;
+  if (hq < 1 || hkv < 1) return fail(PF_ERR_INVALID_ARG, "head counts must be >= 1 (Hq=%d Hkv=%d)", hq, hkv);
+  if (hq % hkv) return fail(PF_ERR_INVALID_ARG, "num_q_heads (%d) is not a multiple of num_kv_heads (%d)", hq, hkv);
+  if (hq > PF_MAX_HEADS) return fail(PF_ERR_UNSUPPORTED, "num_q_heads %d exceeds %d", hq, PF_MAX_HEADS);
+  if (desc->dtype != PF_F32 && desc->dtype != PF_BF16)
+    return fail(PF_ERR_INVALID_ARG, "dtype %d is not PF_F32 or PF_BF16", desc->dtype);
+  if (desc->dtype == PF_BF16 && d != 128)
+    return fail(PF_ERR_UNSUPPORTED, "bf16 kernels need head_dim 128 (got %d)", d);
+  if (desc->dtype == PF_F32 && d != 64 && d != 128)
+    return fail(PF_ERR_UNSUPPORTED, "fp32 kernels need head_dim 64 or 128 (got %d)", d);
+  if (!isfinite(desc->softmax_scale)) return fail(PF_ERR_INVALID_ARG, "softmax_scale is not finite");
+  const int group = hq / hkv;
+  if (group > 256) return fail(PF_ERR_UNSUPPORTED, "more than 256 query heads per KV head");
+  out->hq = hq;
+  out->hkv = hkv;
+  out->group = group;
+  out->d = d;
+  out->dtype = desc->dtype;
+  out->scale = desc->softmax_scale > 0.f ? desc->softmax_scale : 1.0f / sqrtf((float)d);
+  int fill[PF_MAX_HEADS];
+  for (int g = 0; g < hkv; ++g) fill[g] = 0;
+  for (int h = 0; h < hq; ++h) {
+    const int g = desc->q_to_kv ? desc->q_to_kv[h] : h / group;
+    if (g < 0 || g >= hkv) return fail(PF_ERR_INVALID_ARG, "q_to_kv[%d] = %d is out of range", h, g);
+    if (fill[g] >= group)
+      return fail(PF_ERR_INVALID_ARG, "KV head %d is read by more than %d query heads", g, group);
+    out->heads.qhead[g * group + fill[g]++] = (int16_t)h;
+  }
+  return PF_OK;
+}
+
+pf_status check_tensor(const char* name, const pf_tensor& t, int64_t rows, int heads, const Desc& d,
+                       int dtype) {
+  if (rows == 0) return PF_OK;
+  if (!t.data) return fail(PF_ERR_INVALID_ARG, "%s.data is NULL", name);
+  if ((uintptr_t)t.data % 16) return fail(PF_ERR_INVALID_ARG, "%s.data is not 16-byte aligned", name);
+  const int align = 16 / elem_bytes(dtype);
+  if (t.stride_tok < 0 || t.stride_head < 0)
+    return fail(PF_ERR_INVALID_ARG, "%s has a negative stride", name);
+  if (t.stride_tok % align || t.stride_head % align)
+    return fail(PF_ERR_INVALID_ARG, "%s strides must be multiples of %d elements", name, align);
+  if (heads > 1 && t.stride_head < d.d)
+    return fail(PF_ERR_INVALID_ARG, "%s.stride_head (%lld) < head_dim", name, (long long)t.stride_head);
+  if (rows > 1 && t.stride_tok < (int64_t)(heads - 1) * t.stride_head + d.d)
+    return fail(PF_ERR_INVALID_ARG, "%s.stride_tok (%lld) makes rows overlap", name,
+                (long long)t.stride_tok);
+  return PF_OK;
+}
+
+pf_status check_ptr(const char* name, const void* p, size_t align) {
+  if (!p) return fail(PF_ERR_INVALID_ARG, "%s is NULL", name);
+  if ((uintptr_t)p % align) return fail(PF_ERR_INVALID_ARG, "%s is not %zu-byte aligned", name, align);
+  return PF_OK;
+}
+
+pf_status check_cu(int32_t n, const int32_t* cu, int32_t* rows) {
+  if (n < 0) return fail(PF_ERR_INVALID_ARG, "n_suffix is negative");
+  if (n > PF_MAX_SEGMENTS) return fail(PF_ERR_UNSUPPORTED, "more than %d suffixes in one call", PF_MAX_SEGMENTS);
+  if (n == 0) {
+    *rows = 0;
+    return PF_OK;
+  }
+  if (!cu) return fail(PF_ERR_INVALID_ARG, "cu_seqlens is NULL");
+  if (cu[0] != 0) return fail(PF_ERR_INVALID_ARG, "cu_seqlens[0] must be 0 (got %d)", cu[0]);
+  for (int i = 0; i < n; ++i)
+    if (cu[i + 1] < cu[i]) return fail(PF_ERR_INVALID_ARG, "cu_seqlens decreases at %d", i + 1);
+  *rows = cu[n];
+  return PF_OK;
+}
+
+pf_status check_tree(int32_t n, const int32_t* node_off, const int32_t* parent, int32_t* subtree_end) {
+  if (n < 1) return fail(PF_ERR_INVALID_ARG, "a tree needs at least one node");
+  if (n > PF_MAX_SEGMENTS) return fail(PF_ERR_UNSUPPORTED, "more than %d tree nodes", PF_MAX_SEGMENTS);
+  if (!node_off || !parent) return fail(PF_ERR_INVALID_ARG, "node_off or parent is NULL");
+  if (node_off[0] != 0) return fail(PF_ERR_INVALID_ARG, "node_off[0] must be 0");
+  for (int i = 0; i < n; ++i)
+    if (node_off[i + 1] < node_off[i]) return fail(PF_ERR_INVALID_ARG, "node_off decreases at %d", i + 1);
+  if (parent[0] != -1) return fail(PF_ERR_INVALID_ARG, "parent[0] must be -1 (node 0 is the root)");
+  for (int i = 1; i < n; ++i) {
+    if (parent[i] < 0 || parent[i] >= i)
+      return fail(PF_ERR_INVALID_ARG, "parent[%d] = %d: nodes must be numbered in preorder", i, parent[i]);
+    // preorder: the parent of node i is node i-1 or one of its ancestors
+    int u = i - 1;
+    while (u >= 0 && u != parent[i]) u = parent[u];
+    if (u != parent[i])
+      return fail(PF_ERR_INVALID_ARG, "node %d breaks DFS preorder (parent %d is not on the path to node %d)",
+                  i, parent[i], i - 1);
+  }
+  for (int i = 0; i < n; ++i) subtree_end[i] = node_off[i + 1];
+  for (int i = n - 1; i >= 1; --i)
+    if (subtree_end[i] > subtree_end[parent[i]]) subtree_end[parent[i]] = subtree_end[i];
+  return PF_OK;
+}
+
+pf_status check_stream_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return PF_OK;
+  if (!ws) return fail(PF_ERR_WORKSPACE, "workspace is NULL but %zu bytes are needed", need);
+  if ((uintptr_t)ws % 16) return fail(PF_ERR_WORKSPACE, "workspace is not 16-byte aligned");
+  if (ws_bytes < need) return fail(PF_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, need);
+  return PF_OK;
+}
+
+// ------------------------------------------------------------- workspace
+
+struct WsLayout {
+  size_t kend = 0, bmax = 0, bmin = 0, dsum = 0, gk_part = 0, gv_part = 0, total = 0;
+  int32_t n_chunks = 1;
+};
+
+WsLayout layout(int32_t op, const Desc& d, int32_t n_ext, int32_t rows) {
+  WsLayout w;
+  size_t off = 0;
+  const size_t nb = (size_t)((rows + 31) / 32);
+  w.kend = off; off += align_up((size_t)rows * 4);
+  w.bmax = off; off += align_up(nb * 4);
+  w.bmin = off; off += align_up(nb * 4);
+  const bool bwd = op == PF_OP_SUFFIX_BWD || op == PF_OP_PREFIX_BWD || op == PF_OP_TREE_BWD;
+  if (bwd) {
+    w.dsum = off;
+    off += align_up((size_t)d.hq * rows * 4);
+  }
+  if (op == PF_OP_SUFFIX_BWD) {
+    w.n_chunks = pf::ext_chunks(n_ext, rows, d.hq, d.hkv, d.d, d.dtype);
+    if (w.n_chunks > 1) {
+      const size_t part = (size_t)w.n_chunks * n_ext * d.hkv * d.d * 4;
+      w.gk_part = off; off += align_up(part);
+      w.gv_part = off; off += align_up(part);
+    }
+  }
+  w.total = rows > 0 ? off : 0;
+  return w;
+}
+
+pf::RowInfo row_info(void* ws, const WsLayout& w) {
+  char* b = (char*)ws;
+  pf::RowInfo ri;
+  ri.kend = (int32_t*)(b + w.kend);
+  ri.bmax = (int32_t*)(b + w.bmax);
+  ri.bmin = (int32_t*)(b + w.bmin);
+  return ri;
+}
+
+pf::AttnArgs base_args(const Desc& d, int32_t rows) {
+  pf::AttnArgs a;
+  memset(&a, 0, sizeof(a));
+  a.rows = rows;
+  a.hq = d.hq;
+  a.hkv = d.hkv;
+  a.group = d.group;
+  a.scale = d.scale;
+  a.scale_log2 = d.scale * 1.4426950408889634f;
+  a.heads = d.heads;
+  a.n_chunks = 1;
+  return a;
+}
+
+void set_q(pf::AttnArgs& a, const pf_tensor& t) { a.q = t.data; a.q_st = t.stride_tok; a.q_sh = t.stride_head; }
+void set_o(pf::AttnArgs& a, const pf_tensor& t) { a.o = t.data; a.o_st = t.stride_tok; a.o_sh = t.stride_head; }
+void set_do(pf::AttnArgs& a, const pf_tensor& t) { a.dout = t.data; a.do_st = t.stride_tok; a.do_sh = t.stride_head; }
+void set_out(pf::AttnArgs& a, const pf_tensor& t) { a.out = t.data; a.out_st = t.stride_tok; a.out_sh = t.stride_head; }
+void set_ext(pf::AttnArgs& a, const pf_tensor& k, const pf_tensor& v, int32_t n) {
+  a.k_ext = k.data; a.kx_st = k.stride_tok; a.kx_sh = k.stride_head;
+  a.v_ext = v.data; a.vx_st = v.stride_tok; a.vx_sh = v.stride_head;
+  a.n_ext = n;
+}
+void set_own(pf::AttnArgs& a, const pf_tensor& k, const pf_tensor& v) {
+  a.k_own = k.data; a.ko_st = k.stride_tok; a.ko_sh = k.stride_head;
+  a.v_own = v.data; a.vo_st = v.stride_tok; a.vo_sh = v.stride_head;
+}
+void set_dkv(pf::AttnArgs& a, const pf_tensor& dk, const pf_tensor& dv) {
+  a.dk_own = dk.data; a.dko_st = dk.stride_tok; a.dko_sh = dk.stride_head;
+  a.dv_own = dv.data; a.dvo_st = dv.stride_tok; a.dvo_sh = dv.stride_head;
+}
+
+pf::SegTable flat_segments(int32_t n, const int32_t* cu) {
+  pf::SegTable s;
+  memset(&s, 0, sizeof(s));
+  s.n = n;
+  for (int i = 0; i <= n; ++i) s.start[i] = cu[i];
+  for (int i = 0; i < n; ++i) s.vis_end[i] = cu[i + 1];
+  return s;
+}
+
+pf::SegTable causal_segment(int32_t rows) {
+  pf::SegTable s;
+  memset(&s, 0, sizeof(s));
+  s.n = 1;
+  s.start[0] = 0;
+  s.start[1] = rows;
+  s.vis_end[0] = rows;
+  return s;
+}
+
+pf::SegTable tree_segments(int32_t n, const int32_t* node_off, const int32_t* subtree_end) {
+  pf::SegTable s;
+  memset(&s, 0, sizeof(s));
+  s.n = n;
+  for (int i = 0; i <= n; ++i) s.start[i] = node_off[i];
+  for (int i = 0; i < n; ++i) s.vis_end[i] = subtree_end[i];
+  return s;
+}
+
+// ------------------------------------------------------------- launches
+
+pf_status run_fwd(const Desc& d, const pf::AttnArgs& a, const pf::SegTable& seg, hipStream_t st) {
+  hipError_t e = pf::launch_prep(seg, a.ri, st);
+  if (e != hipSuccess) return hip_fail(e, "prep");
+  e = d.dtype == PF_BF16 ? pf::launch_fwd_bf16(a, d.d, st) : pf::launch_fwd_f32(a, d.d, st);
+  if (e != hipSuccess) return hip_fail(e, "forward");
+  return PF_OK;
+}
+
+pf_status run_bwd(const Desc& d, const pf::AttnArgs& a, const pf::SegTable& seg, hipStream_t st) {
+  hipError_t e = pf::launch_prep(seg, a.ri, st);
+  if (e != hipSuccess) return hip_fail(e, "prep");
+  e = d.dtype == PF_BF16 ? pf::launch_bwd_dq_bf16(a, d.d, st) : pf::launch_bwd_dq_f32(a, d.d, st);
+  if (e != hipSuccess) return hip_fail(e, "dq");
+  e = d.dtype == PF_BF16 ? pf::launch_bwd_dkv_bf16(a, d.d, st) : pf::launch_bwd_dkv_f32(a, d.d, st);
+  if (e != hipSuccess) return hip_fail(e, "dkv");
+  if (a.n_chunks > 1 && a.n_ext > 0) {
+    const int64_t n = (int64_t)a.n_ext * d.hkv * d.d;
+    e = pf::launch_reduce_partials(a.gk_part, a.gk_acc, a.n_chunks, n, st);
+    if (e == hipSuccess) e = pf::launch_reduce_partials(a.gv_part, a.gv_acc, a.n_chunks, n, st);
+    if (e != hipSuccess) return hip_fail(e, "reduce");
+  }
+  return PF_OK;
+}
+
+}  // namespace
+
+namespace pf {
+
+namespace {
+pf_launch_hook g_hook = nullptr;
+void* g_hook_user = nullptr;
+}  // namespace
+
+void launch_hook(const char* kernel, hipStream_t stream, int end) {
+  const pf_launch_hook h = g_hook;
+  if (h) h(kernel, (void*)stream, end, g_hook_user);
+}
+
+int32_t ext_chunks(int32_t n_ext, int32_t rows, int32_t hq, int32_t hkv, int32_t head_dim,
+                   int32_t dtype) {
+  (void)head_dim;
+  if (dtype != PF_BF16 || n_ext <= 0 || rows <= 0) return 1;
+  // aim for >= 512 workgroups of prefix keys (two per CU on 256 CUs), while
+  // each chunk keeps at least 64 query steps of 32 rows
+  const int64_t wgs = (int64_t)((n_ext + 127) / 128) * hkv;
+  const int64_t steps = (int64_t)((rows + 31) / 32) * (hq / hkv);
+  int32_t nc = 1;
+  while (nc < 8 && wgs * nc < 512 && steps / (2 * nc) >= 64) nc *= 2;
+  return nc;
+}
+
+}  // namespace pf
+
+extern "C" {
+
+int32_t pf_abi_version(void) { return PF_ABI_VERSION; }
+
+void pf_set_launch_hook(pf_launch_hook hook, void* user) {
+  pf::g_hook_user = user;
+  pf::g_hook = hook;
+}
+
+const char* pf_last_error(void) { return g_last_error.c_str(); }
+
+const char* pf_status_string(pf_status s) {
+  switch (s) {
+    case PF_OK: return "PF_OK";
+    case PF_ERR_INVALID_ARG: return "PF_ERR_INVALID_ARG";
+    case PF_ERR_UNSUPPORTED: return "PF_ERR_UNSUPPORTED";
+    case PF_ERR_WORKSPACE: return "PF_ERR_WORKSPACE";
+    case PF_ERR_HIP: return "PF_ERR_HIP";
+  }
+  return "unknown pf_status";
+}
+
+size_t pf_workspace_size(int32_t op, const pf_attn_desc* desc, int32_t prefix_len, int32_t rows) {
+  Desc d;
+  if (check_desc(desc, &d) != PF_OK || rows < 0 || prefix_len < 0) return 0;
+  if (op == PF_OP_PREFIX_FWD || op == PF_OP_PREFIX_BWD) rows = prefix_len;
+  const int32_t n_ext = (op == PF_OP_SUFFIX_FWD || op == PF_OP_SUFFIX_BWD) ? prefix_len : 0;
+  if (op < PF_OP_PREFIX_FWD || op > PF_OP_TREE_BWD) return 0;
+  return layout(op, d, n_ext, rows).total;
+}
+
+pf_status pf_tree_subtree_end(int32_t n_nodes, const int32_t* node_off, const int32_t* parent,
+                              int32_t* subtree_end) {
+  if (!subtree_end) return fail(PF_ERR_INVALID_ARG, "subtree_end is NULL");
+  int32_t tmp[PF_MAX_SEGMENTS];
+  const pf_status s = check_tree(n_nodes, node_off, parent, tmp);
+  if (s != PF_OK) return s;
+  for (int i = 0; i < n_nodes; ++i) subtree_end[i] = tmp[i];
+  return PF_OK;
+}
+
+pf_status pf_prefix_fwd(const pf_attn_desc* desc, int32_t prefix_len, pf_tensor q_p, pf_tensor k_p,
+                        pf_tensor v_p, pf_tensor o_p, float* lse_p, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  Desc d;
+  pf_status s = check_desc(desc, &d);
+  if (s != PF_OK) return s;
+  if (prefix_len < 0) return fail(PF_ERR_INVALID_ARG, "prefix_len is negative");
+  if ((s = check_tensor("q_p", q_p, prefix_len, d.hq, d, d.dtype)) != PF_OK) return s;
+  if ((s = check_tensor("k_p", k_p, prefix_len, d.hkv, d, d.dtype)) != PF_OK) return s;
+  if ((s = check_tensor("v_p", v_p, prefix_len, d.hkv, d, d.dtype)) != PF_OK) return s;
+  if ((s = check_tensor("o_p", o_p, prefix_len, d.hq, d, d.dtype)) != PF_OK) return s;
+  if (prefix_len > 0 && (s = check_ptr("lse_p", lse_p, 4)) != PF_OK) return s;
+  const WsLayout w = layout(PF_OP_PREFIX_FWD, d, 0, prefix_len);
+  if ((s = check_stream_ws(workspace, workspace_bytes, w.total)) != PF_OK) return s;
+  if (prefix_len == 0) return PF_OK;
+  pf::AttnArgs a = base_args(d, prefix_len);
+  set_q(a, q_p);
+  set_out(a, o_p);
+  set_own(a, k_p, v_p);
+  a.lse = lse_p;
+  a.ri = row_info(workspace, w);
+  return run_fwd(d, a, causal_segment(prefix_len), (hipStream_t)stream);
+}
+
+pf_status pf_suffix_attn_fwd(const pf_attn_desc* desc, int32_t prefix_len, pf_tensor k_p,
+                             pf_tensor v_p, int32_t n_suffix, const int32_t* cu_seqlens,
+                             pf_tensor q_s, pf_tensor k_s, pf_tensor v_s, pf_tensor o_s,
+                             float* lse_s, void* workspace, size_t workspace_bytes, void* stream) {
+  Desc d;
+  pf_status s = check_desc(desc, &d);
+  if (s != PF_OK) return s;
+  if (prefix_len < 0) return fail(PF_ERR_INVALID_ARG, "prefix_len is negative");
+  int32_t rows = 0;
+  if ((s = check_cu(n_suffix, cu_seqlens, &rows)) != PF_OK) return s;
+  if ((s = check_tensor("k_p", k_p, prefix_len, d.hkv, d, d.dtype)) != PF_OK) return s;
+  if ((s = check_tensor("v_p", v_p, prefix_len, d.hkv, d, d.dtype)) != PF_OK) return s;
+  if ((s = check_tensor("q_s", q_s, rows, d.hq, d, d.dtype)) != PF_OK) return s;
+  if ((s = check_tensor("k_s", k_s, rows, d.hkv, d, d.dtype)) != PF_OK) return s;
+  if ((s = check_tensor("v_s", v_s, rows, d.hkv, d, d.dtype)) != PF_OK) return s;
+  if ((s = check_tensor("o_s", o_s, rows, d.hq, d, d.dtype)) != PF_OK) return s;
+  if (rows > 0 && (s = check_ptr("lse_s", lse_s, 4)) != PF_OK) return s;
+  const WsLayout w = layout(PF_OP_SUFFIX_FWD, d, prefix_len, rows);
+  if ((s = check_stream_ws(workspace, workspace_bytes, w.total)) != PF_OK) return s;
+  if (rows == 0) return PF_OK;
+  pf::AttnArgs a = base_args(d, rows);
+  set_q(a, q_s);
+  set_out(a, o_s);
+  set_ext(a, k_p, v_p, prefix_len);
+  set_own(a, k_s, v_s);
+  a.lse = lse_s;
+  a.ri = row_info(workspace, w);
+  return run_fwd(d, a, flat_segments(n_suffix, cu_seqlens), (hipStream_t)stream);
+}
+
+pf_status pf_suffix_attn_bwd_accum(const pf_attn_desc* desc, int32_t prefix_len, pf_tensor k_p,
+                                   pf_tensor v_p, int32_t n_suffix, const int32_t* cu_seqlens,
+                                   pf_tensor q_s, pf_tensor k_s, pf_tensor v_s, pf_tensor o_s,
+                                   const float* lse_s, pf_tensor do_s, pf_tensor dq_s,
+                                   pf_tensor dk_s, pf_tensor dv_s, float* gk_acc, float* gv_acc,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  Desc d;
+  pf_status s = check_desc(desc, &d);
+  if (s != PF_OK) return s;
+  if (prefix_len < 0) return fail(PF_ERR_INVALID_ARG, "prefix_len is negative");
+  int32_t rows = 0;
+  if ((s = check_cu(n_suffix, cu_seqlens, &rows)) != PF_OK) return s;
+  if ((s = check_tensor("k_p", k_p, prefix_len, d.hkv, d, d.dtype)) != PF_OK) return s;
+  if ((s = check_tensor("v_p", v_p, prefix_len, d.hkv, d, d.dtype)) != PF_OK) return s;
+  if ((s = check_tensor("q_s", q_s, rows, d.hq, d, d.dtype)) != PF_OK) return s;
+  if ((s = check_tensor("k_s", k_s, rows, d.hkv, d, d.dtype)) != PF_OK) return s;
+  if ((s = check_tensor("v_s", v_s, rows, d.hkv, d, d.dtype)) != PF_OK) return s;
+  if ((s = check_tensor("o_s", o_s, rows, d.hq, d, d.dtype)) != PF_OK) return s;
+  if ((s = check_tensor("do_s", do_s, rows, d.hq, d, d.dtype)) != PF_OK) return s;
+  if ((s = check_tensor("dq_s", dq_s, rows, d.hq, d, d.dtype)) != PF_OK) return s;
+  if ((s = check_tensor("dk_s", dk_s, rows, d.hkv, d, d.dtype)) != PF_OK) return s;
+  if ((s = check_tensor("dv_s", dv_s, rows, d.hkv, d, d.dtype)) != PF_OK) return s;
+  if (rows > 0 && (s = check_ptr("lse_s", lse_s, 4)) != PF_OK) return s;
+  if (rows > 0 && prefix_len > 0) {
+    if ((s = check_ptr("gk_acc", gk_acc, 16)) != PF_OK) return s;
+    if ((s = check_ptr("gv_acc", gv_acc, 16)) != PF_OK) return s;
+  }
+  const WsLayout w = layout(PF_OP_SUFFIX_BWD, d, prefix_len, rows);
+  if ((s = check_stream_ws(workspace, workspace_bytes, w.total)) != PF_OK) return s;
+  if (rows == 0) return PF_OK;
+  pf::AttnArgs a = base_args(d, rows);
+  set_q(a, q_s);
+  set_o(a, o_s);
+  set_do(a, do_s);
+  set_out(a, dq_s);
+  set_ext(a, k_p, v_p, prefix_len);
+  set_own(a, k_s, v_s);
+  set_dkv(a, dk_s, dv_s);
+  a.dkv_f32 = d.dtype == PF_F32;
+  a.lse = const_cast<float*>(lse_s);
+  a.gk_acc = gk_acc;
+  a.gv_acc = gv_acc;
+  a.n_chunks = w.n_chunks;
+  if (w.n_chunks > 1) {
+    a.gk_part = (float*)((char*)workspace + w.gk_part);
+    a.gv_part = (float*)((char*)workspace + w.gv_part);
+  }
+  a.dsum = (float*)((char*)workspace + w.dsum);
+  a.ri = row_info(workspace, w);
+  return run_bwd(d, a, flat_segments(n_suffix, cu_seqlens), (hipStream_t)stream);
+}
+
+pf_status pf_prefix_bwd_inject(const pf_attn_desc* desc, int32_t prefix_len, pf_tensor q_p,
+                               pf_tensor k_p, pf_tensor v_p, pf_tensor o_p, const float* lse_p,
+                               pf_tensor do_p, const float* gk_acc, const float* gv_acc,
+                               pf_tensor dq_p, pf_tensor dk_p, pf_tensor dv_p, int32_t dkv_dtype,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  Desc d;
+  pf_status s = check_desc(desc, &d);
+  if (s != PF_OK) return s;
+  if (prefix_len < 0) return fail(PF_ERR_INVALID_ARG, "prefix_len is negative");
+  if (dkv_dtype != PF_F32 && dkv_dtype != d.dtype)
+    return fail(PF_ERR_INVALID_ARG, "dkv_dtype must be PF_F32 or the input dtype");
+  const bool has_do = do_p.data != nullptr;
+  if (has_do) {
+    if ((s = check_tensor("q_p", q_p, prefix_len, d.hq, d, d.dtype)) != PF_OK) return s;
+    if ((s = check_tensor("k_p", k_p, prefix_len, d.hkv, d, d.dtype)) != PF_OK) return s;
+    if ((s = check_tensor("v_p", v_p, prefix_len, d.hkv, d, d.dtype)) != PF_OK) return s;
+    if ((s = check_tensor("o_p", o_p, prefix_len, d.hq, d, d.dtype)) != PF_OK) return s;
+    if ((s = check_tensor("do_p", do_p, prefix_len, d.hq, d, d.dtype)) != PF_OK) return s;
+    if (prefix_len > 0 && (s = check_ptr("lse_p", lse_p, 4)) != PF_OK) return s;
+  }
+  if ((s = check_tensor("dq_p", dq_p, prefix_len, d.hq, d, d.dtype)) != PF_OK) return s;
+  if ((s = check_tensor("dk_p", dk_p, prefix_len, d.hkv, d, dkv_dtype)) != PF_OK) return s;
+  if ((s = check_tensor("dv_p", dv_p, prefix_len, d.hkv, d, dkv_dtype)) != PF_OK) return s;
+  if (prefix_len > 0) {
+    if ((s = check_ptr("gk_acc", gk_acc, 16)) != PF_OK) return s;
+    if ((s = check_ptr("gv_acc", gv_acc, 16)) != PF_OK) return s;
+  }
+  const WsLayout w = layout(PF_OP_PREFIX_BWD, d, 0, prefix_len);
+  if (has_do && (s = check_stream_ws(workspace, workspace_bytes, w.total)) != PF_OK) return s;
+  if (prefix_len == 0) return PF_OK;
+  hipStream_t st = (hipStream_t)stream;
+  if (!has_do) {
+    // zero upstream: dQ_P = 0 and the prefix K/V gradients are the accumulators
+    const int eb = elem_bytes(d.dtype);
+    hipError_t e = pf::launch_fill_zero(dq_p.data, prefix_len, d.hq, d.d, dq_p.stride_tok,
+                                        dq_p.stride_head, eb, st);
+    if (e == hipSuccess)
+      e = pf::launch_convert_acc(gk_acc, dk_p.data, prefix_len, d.hkv, d.d, dk_p.stride_tok,
+                                 dk_p.stride_head, dkv_dtype == PF_F32, st);
+    if (e == hipSuccess)
+      e = pf::launch_convert_acc(gv_acc, dv_p.data, prefix_len, d.hkv, d.d, dv_p.stride_tok,
+                                 dv_p.stride_head, dkv_dtype == PF_F32, st);
+    if (e != hipSuccess) return hip_fail(e, "inject");
+    return PF_OK;
+  }
+  pf::AttnArgs a = base_args(d, prefix_len);
+  set_q(a, q_p);
+  set_o(a, o_p);
+  set_do(a, do_p);
+  set_out(a, dq_p);
+  set_own(a, k_p, v_p);
+  set_dkv(a, dk_p, dv_p);
+  a.dkv_f32 = dkv_dtype == PF_F32;
+  a.gk_init = gk_acc;
+  a.gv_init = gv_acc;
+  a.lse = const_cast<float*>(lse_p);
+  a.dsum = (float*)((char*)workspace + w.dsum);
+  a.ri = row_info(workspace, w);
+  return run_bwd(d, a, causal_segment(prefix_len), st);
+}
+
+pf_status pf_tree_attn_fwd(const pf_attn_desc* desc, int32_t n_nodes, const int32_t* node_off,
+                           const int32_t* parent, pf_tensor q, pf_tensor k, pf_tensor v, pf_tensor o,
+                           float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  Desc d;
+  pf_status s = check_desc(desc, &d);
+  if (s != PF_OK) return s;
+  int32_t send[PF_MAX_SEGMENTS];
+  if ((s = check_tree(n_nodes, node_off, parent, send)) != PF_OK) return s;
+  const int32_t rows = node_off[n_nodes];
+  if ((s = check_tensor("q", q, rows, d.hq, d, d.dtype)) != PF_OK) return s;
+  if ((s = check_tensor("k", k, rows, d.hkv, d, d.dtype)) != PF_OK) return s;
+  if ((s = check_tensor("v", v, rows, d.hkv, d, d.dtype)) != PF_OK) return s;
+  if ((s = check_tensor("o", o, rows, d.hq, d, d.dtype)) != PF_OK) return s;
+  if (rows > 0 && (s = check_ptr("lse", lse, 4)) != PF_OK) return s;
+  const WsLayout w = layout(PF_OP_TREE_FWD, d, 0, rows);
+  if ((s = check_stream_ws(workspace, workspace_bytes, w.total)) != PF_OK) return s;
+  if (rows == 0) return PF_OK;
+  pf::AttnArgs a = base_args(d, rows);
+  set_q(a, q);
+  set_out(a, o);
+  set_own(a, k, v);
+  a.lse = lse;
+  a.ri = row_info(workspace, w);
+  return run_fwd(d, a, tree_segments(n_nodes, node_off, send), (hipStream_t)stream);
+}
+
+pf_status pf_tree_attn_bwd(const pf_attn_desc* desc, int32_t n_nodes, const int32_t* node_off,
+                           const int32_t* parent, pf_tensor q, pf_tensor k, pf_tensor v, pf_tensor o,
+                           const float* lse, pf_tensor dout, pf_tensor dq, pf_tensor dk,
+                           pf_tensor dv, void* workspace, size_t workspace_bytes, void* stream) {
+  Desc d;
+  pf_status s = check_desc(desc, &d);
+  if (s != PF_OK) return s;
+  int32_t send[PF_MAX_SEGMENTS];
+  if ((s = check_tree(n_nodes, node_off, parent, send)) != PF_OK) return s;
+  const int32_t rows = node_off[n_nodes];
+  if ((s = check_tensor("q", q, rows, d.hq, d, d.dtype)) != PF_OK) return s;
+  if ((s = check_tensor("k", k, rows, d.hkv, d, d.dtype)) != PF_OK) return s;
+  if ((s = check_tensor("v", v, rows, d.hkv, d, d.dtype)) != PF_OK) return s;
+  if ((s = check_tensor("o", o, rows, d.hq, d, d.dtype)) != PF_OK) return s;
+  if ((s = check_tensor("dout", dout, rows, d.hq, d, d.dtype)) != PF_OK) return s;
+  if ((s = check_tensor("dq", dq, rows, d.hq, d, d.dtype)) != PF_OK) return s;
+  if ((s = check_tensor("dk", dk, rows, d.hkv, d, d.dtype)) != PF_OK) return s;
+  if ((s = check_tensor("dv", dv, rows, d.hkv, d, d.dtype)) != PF_OK) return s;
+  if (rows > 0 && (s = check_ptr("lse", lse, 4)) != PF_OK) return s;
+  const WsLayout w = layout(PF_OP_TREE_BWD, d, 0, rows);
+  if ((s = check_stream_ws(workspace, workspace_bytes, w.total)) != PF_OK) return s;
+  if (rows == 0) return PF_OK;
+  pf::AttnArgs a = base_args(d, rows);
+  set_q(a, q);
+  set_o(a, o);
+  set_do(a, dout);
+  set_out(a, dq);
+  set_own(a, k, v);
+  set_dkv(a, dk, dv);
+  a.dkv_f32 = d.dtype == PF_F32;
+  a.lse = const_cast<float*>(lse);
+  a.dsum = (float*)((char*)workspace + w.dsum);
+  a.ri = row_info(workspace, w);
+  return run_bwd(d, a, tree_segments(n_nodes, node_off, send), (hipStream_t)stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,120 @@
+// Internal declarations shared by the kernels and the host entry points.
+//
+// Every attention call in this library is one instance of a single problem:
+// a set of query rows, an optional block of "external" keys that every query
+// row sees (the cached prefix K/V in Phase B), and a set of "own" keys that
+// are indexed like the query rows.  Own key k is visible to query q iff
+//
+//        k <= q   and   q < kend[k]
+//
+// where kend[k] is the end of the row range that may read key k.  With rows
+// in DFS preorder this one rule covers:
+//   - Phase A / Phase C (causal prefix):     kend[k] = P;
+//   - Phase B own suffix keys:               kend[k] = end of k's suffix, so a
+//     suffix never sees another suffix (PrefixFlow §4.1);
+//   - trees:                                  kend[k] = end of the subtree of
+//     k's node, i.e. the rows of the node and its descendants (HARTS §2.1,
+//     §2.2).
+// kend[] and per-block summaries of it are built on the device from the
+// segment table by the prep kernel.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pf.h"
+
+namespace pf {
+
+constexpr int kWave = 64;
+constexpr int kKeyBlockSummary = 32;   // granularity of the kend min/max summaries
+
+// Segment table passed by value to the prep kernel: segment i covers rows
+// [start[i], start[i+1]); keys in it are visible up to row vis_end[i].
+struct SegTable {
+  int32_t n;
+  int32_t start[PF_MAX_SEGMENTS + 1];
+  int32_t vis_end[PF_MAX_SEGMENTS];
+};
+
+// Per-row visibility data in the workspace.
+struct RowInfo {
+  int32_t* kend;      // [rows]
+  int32_t* bmax;      // [ceil(rows/32)]: max kend over each 32-key block
+  int32_t* bmin;      // [ceil(rows/32)]: min kend over the valid keys of the block
+};
+
+// Query heads grouped by the KV head they read: qhead[g * G + j] is the j-th
+// query head of KV head g.
+struct HeadTable {
+  int16_t qhead[PF_MAX_HEADS];
+};
+
+// Arguments of every attention kernel (passed by value).
+struct AttnArgs {
+  // query side, [rows, Hq, d]
+  const void* q;  int64_t q_st, q_sh;
+  const void* o;  int64_t o_st, o_sh;     // forward output (read by backward)
+  const void* dout; int64_t do_st, do_sh; // upstream gradient
+  void* out; int64_t out_st, out_sh;      // O (forward) or dQ (backward)
+  float* lse;                             // [Hq, rows]
+  float* dsum;                            // [Hq, rows] D = rowsum(dO * O), workspace
+  // external keys (every query row sees all of them), [n_ext, Hkv, d]
+  const void* k_ext; int64_t kx_st, kx_sh;
+  const void* v_ext; int64_t vx_st, vx_sh;
+  int32_t n_ext;
+  // own keys, indexed like the query rows, [rows, Hkv, d]
+  const void* k_own; int64_t ko_st, ko_sh;
+  const void* v_own; int64_t vo_st, vo_sh;
+  // dK/dV outputs of the own keys, [rows, Hkv, d]
+  void* dk_own; int64_t dko_st, dko_sh;
+  void* dv_own; int64_t dvo_st, dvo_sh;
+  int32_t dkv_f32;                        // dK/dV own outputs are fp32 (else input dtype)
+  const float* gk_init;                   // optional fp32 [rows, Hkv, d] added into own dK
+  const float* gv_init;                   //   and dV before the rounding (Phase C)
+  // external-key gradient destination: fp32 [n_ext, Hkv, d]
+  float* gk_acc; float* gv_acc;           // accumulators (RMW when n_chunks == 1)
+  float* gk_part; float* gv_part;         // partials [n_chunks, n_ext, Hkv, d]
+  int32_t n_chunks;                       // query chunks per external key block
+  RowInfo ri;
+  int32_t rows;
+  int32_t hq, hkv, group;                 // group = Hq / Hkv
+  float scale;                            // softmax scale
+  float scale_log2;                       // scale * log2(e)
+  HeadTable heads;
+};
+
+// Calls the caller's launch hook (if any) around one kernel launch.
+void launch_hook(const char* kernel, hipStream_t stream, int end);
+
+#define PF_LAUNCH(label, kernel, grid, block, stream, ...)                    \
+  do {                                                                        \
+    ::pf::launch_hook(label, stream, 0);                                      \
+    hipLaunchKernelGGL(kernel, grid, block, 0, stream, __VA_ARGS__);          \
+    ::pf::launch_hook(label, stream, 1);                                      \
+  } while (0)
+
+// Launchers (return hipSuccess or the launch error).
+hipError_t launch_prep(const SegTable& seg, RowInfo ri, hipStream_t stream);
+hipError_t launch_reduce_partials(const float* part, float* acc, int32_t n_chunks, int64_t n,
+                                  hipStream_t stream);
+hipError_t launch_fill_zero(void* dst, int64_t rows, int32_t heads, int32_t d, int64_t st,
+                            int64_t sh, int32_t elem_bytes, hipStream_t stream);
+hipError_t launch_convert_acc(const float* src, void* dst, int64_t rows, int32_t heads, int32_t d,
+                              int64_t st, int64_t sh, int32_t dst_f32, hipStream_t stream);
+
+hipError_t launch_fwd_bf16(const AttnArgs& a, int32_t head_dim, hipStream_t stream);
+hipError_t launch_bwd_dq_bf16(const AttnArgs& a, int32_t head_dim, hipStream_t stream);
+hipError_t launch_bwd_dkv_bf16(const AttnArgs& a, int32_t head_dim, hipStream_t stream);
+
+hipError_t launch_fwd_f32(const AttnArgs& a, int32_t head_dim, hipStream_t stream);
+hipError_t launch_bwd_dq_f32(const AttnArgs& a, int32_t head_dim, hipStream_t stream);
+hipError_t launch_bwd_dkv_f32(const AttnArgs& a, int32_t head_dim, hipStream_t stream);
+
+// Number of query chunks the KV-stationary backward splits the external
+// (prefix) keys into.  A function of the shapes only, so results do not
+// depend on the device.
+int32_t ext_chunks(int32_t n_ext, int32_t rows, int32_t hq, int32_t hkv, int32_t head_dim,
+                   int32_t dtype);
+
+}  // namespace pf

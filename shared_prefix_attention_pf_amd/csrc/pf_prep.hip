@@ -1,0 +1,150 @@
+// Small device kernels around the attention kernels:
+//   - prep: per-row kend[] and its 32-key block min/max from the segment table;
+//   - reduce: gK/gV accumulator += sum of per-chunk partials, in a fixed
+//     pairwise order (contention-free and run-to-run deterministic; this is
+//     the per-suffix accumulation of PrefixFlow §3.1 "Savings over the
+//     baseline", an element-wise O(|P| d) add);
+//   - zero fill and fp32 -> output conversion for Phase C with no upstream.
+#include "pf_internal.h"
+
+namespace pf {
+
+__global__ __launch_bounds__(256) void prep_kernel(SegTable seg, RowInfo ri) {
+  const int rows = seg.start[seg.n];
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  int kend = -1;          // rows past the end: ignored by both summaries
+  if (t < rows) {
+    // segment of row t: the last i with start[i] <= t (empty segments skipped)
+    int lo = 0, hi = seg.n - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (seg.start[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    kend = seg.vis_end[lo];
+    ri.kend[t] = kend;
+  }
+  // 32-key block summaries: lanes [32b, 32b+32) of the wave hold one block
+  int mx = kend;
+  int mn = (t < rows) ? kend : 0x7fffffff;
+#pragma unroll
+  for (int off = 16; off >= 1; off >>= 1) {
+    mx = max(mx, __shfl_xor(mx, off, 32));
+    mn = min(mn, __shfl_xor(mn, off, 32));
+  }
+  if ((threadIdx.x & 31) == 0 && t < rows) {
+    ri.bmax[t >> 5] = mx;
+    ri.bmin[t >> 5] = mn;
+  }
+}
+
+hipError_t launch_prep(const SegTable& seg, RowInfo ri, hipStream_t stream) {
+  const int rows = seg.start[seg.n];
+  if (rows <= 0) return hipSuccess;
+  const int blocks = (rows + 255) / 256;
+  PF_LAUNCH("pf_prep", prep_kernel, dim3(blocks), dim3(256), stream, seg, ri);
+  return hipGetLastError();
+}
+
+// acc[i] += (((p0 + p1) + (p2 + p3)) + ...)  over n_chunks partials of n floats.
+template <int NC>
+__device__ inline float4 tree_sum(const float4* part, int64_t n4, int64_t i, int nc) {
+  float4 v[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) v[c] = (c < nc) ? part[c * n4 + i] : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int w = 1; w < NC; w <<= 1) {
+#pragma unroll
+    for (int c = 0; c + w < NC; c += 2 * w) {
+      v[c].x += v[c + w].x; v[c].y += v[c + w].y; v[c].z += v[c + w].z; v[c].w += v[c + w].w;
+    }
+  }
+  return v[0];
+}
+
+__global__ __launch_bounds__(256) void reduce_partials_kernel(const float4* __restrict__ part,
+                                                              float4* __restrict__ acc,
+                                                              int nc, int64_t n4) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+    float4 s;
+    if (nc <= 2) s = tree_sum<2>(part, n4, i, nc);
+    else if (nc <= 4) s = tree_sum<4>(part, n4, i, nc);
+    else s = tree_sum<8>(part, n4, i, nc);
+    float4 a = acc[i];
+    a.x += s.x; a.y += s.y; a.z += s.z; a.w += s.w;
+    acc[i] = a;
+  }
+}
+
+hipError_t launch_reduce_partials(const float* part, float* acc, int32_t n_chunks, int64_t n,
+                                  hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const int64_t n4 = n / 4;  // n is a multiple of head_dim (>= 64)
+  int64_t blocks = (n4 + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  PF_LAUNCH("pf_reduce", reduce_partials_kernel, dim3((unsigned)blocks), dim3(256), stream, (const float4*)part, (float4*)acc, (int)n_chunks, n4);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(char* dst, int64_t rows, int heads,
+                                                        int row_bytes, int64_t st_b,
+                                                        int64_t sh_b) {
+  // one thread per 16 bytes of one (row, head) vector
+  const int per = row_bytes / 16;
+  const int64_t total = rows * heads * per;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+    const int c = (int)(i % per);
+    const int64_t rh = i / per;
+    const int h = (int)(rh % heads);
+    const int64_t r = rh / heads;
+    *(uint4*)(dst + r * st_b + h * sh_b + c * 16) = make_uint4(0, 0, 0, 0);
+  }
+}
+
+hipError_t launch_fill_zero(void* dst, int64_t rows, int32_t heads, int32_t d, int64_t st,
+                            int64_t sh, int32_t elem_bytes, hipStream_t stream) {
+  if (rows <= 0) return hipSuccess;
+  const int64_t total = rows * heads * (d * elem_bytes / 16);
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  PF_LAUNCH("pf_fill_zero", fill_zero_kernel, dim3((unsigned)blocks), dim3(256), stream, (char*)dst,
+                     rows, (int)heads, (int)(d * elem_bytes), st * elem_bytes, sh * elem_bytes);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void convert_acc_kernel(const float4* __restrict__ src,
+                                                          char* dst, int64_t rows, int heads,
+                                                          int d, int64_t st, int64_t sh,
+                                                          int dst_f32) {
+  const int per = d / 4;
+  const int64_t total = rows * heads * per;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+    const int c = (int)(i % per);
+    const int64_t rh = i / per;
+    const int h = (int)(rh % heads);
+    const int64_t r = rh / heads;
+    const float4 v = src[i];
+    const int64_t off = r * st + (int64_t)h * sh + c * 4;   // elements
+    if (dst_f32) {
+      *(float4*)((float*)dst + off) = v;
+    } else {
+      __bf16* o = (__bf16*)dst + off;
+      o[0] = (__bf16)v.x; o[1] = (__bf16)v.y; o[2] = (__bf16)v.z; o[3] = (__bf16)v.w;
+    }
+  }
+}
+
+hipError_t launch_convert_acc(const float* src, void* dst, int64_t rows, int32_t heads, int32_t d,
+                              int64_t st, int64_t sh, int32_t dst_f32, hipStream_t stream) {
+  if (rows <= 0) return hipSuccess;
+  const int64_t total = rows * heads * (d / 4);
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  PF_LAUNCH("pf_convert_acc", convert_acc_kernel, dim3((unsigned)blocks), dim3(256), stream, (const float4*)src, (char*)dst, rows, (int)heads, (int)d, st, sh,
+                     (int)dst_f32);
+  return hipGetLastError();
+}
+
+}  // namespace pf

@@ -1,0 +1,151 @@
+"""Host-side tests of the C ABI (no GPU needed).
+
+The library must load, export every function include/pf.h declares, and
+reject invalid arguments with the documented status before any HIP call.
+The tree helper is checked against the oracle's ancestor mask.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import shared_prefix_attention_pf_amd as pf
+from oracle import tree_ancestor_mask
+from workloads.gen import random_tree
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000   # a 16-byte aligned address that validation-failing calls never dereference
+
+
+def _header_functions():
+    src = open(os.path.join(ROOT, "include", "pf.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(pf_[a-z_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(pf.LIB_PATH)
+    names = _header_functions()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(pf.EXPORTED)
+
+
+def test_abi_version_and_status_strings():
+    assert pf.pf_abi_version() == 1
+    for s in range(5):
+        assert pf._lib.pf_status_string(s).decode().startswith("PF_")
+
+
+def _t(rows_heads_d=None, addr=FAKE, st=None, sh=None, heads=8, d=128):
+    st = heads * d if st is None else st
+    sh = d if sh is None else sh
+    return pf._Tensor(addr, st, sh)
+
+
+def _desc(hq=32, hkv=8, d=128, dtype=pf.PF_BF16, q_to_kv=None):
+    return pf.AttnDesc(hq, hkv, d, dtype, 0.0, q_to_kv)._c()
+
+
+def _suffix_fwd(desc_keep, cu, ws=FAKE, ws_bytes=1 << 30, q=None, kp=None, lse=FAKE):
+    d, _keep = desc_keep
+    cu_arr = np.asarray(cu, dtype=np.int32)
+    cu_p = cu_arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    q = q or _t(heads=d.num_q_heads, d=d.head_dim)
+    kv = _t(heads=d.num_kv_heads, d=d.head_dim)
+    kp = kp or kv
+    return pf._lib.pf_suffix_attn_fwd(ctypes.byref(d), 64, kp, kv, len(cu) - 1, cu_p, q, kv, kv, q,
+                                      ctypes.c_void_p(lse), ctypes.c_void_p(ws), ws_bytes,
+                                      ctypes.c_void_p(0))
+
+
+def test_rejects_bad_head_config():
+    assert _suffix_fwd(_desc(hq=30, hkv=8), [0, 4]) == pf.PF_ERR_INVALID_ARG
+    assert _suffix_fwd(_desc(hq=0, hkv=8), [0, 4]) == pf.PF_ERR_INVALID_ARG
+    assert _suffix_fwd(_desc(d=96), [0, 4]) == pf.PF_ERR_UNSUPPORTED
+    assert _suffix_fwd(_desc(d=64), [0, 4]) == pf.PF_ERR_UNSUPPORTED          # bf16 needs 128
+    assert _suffix_fwd(_desc(hq=4, hkv=2, q_to_kv=[0, 0, 0, 1]), [0, 4]) == pf.PF_ERR_INVALID_ARG
+    assert _suffix_fwd(_desc(hq=4, hkv=2, q_to_kv=[0, 1, 2, 1]), [0, 4]) == pf.PF_ERR_INVALID_ARG
+    msg = pf._lib.pf_last_error().decode()
+    assert "q_to_kv" in msg
+
+
+def test_rejects_bad_cu_seqlens():
+    assert _suffix_fwd(_desc(), [1, 4]) == pf.PF_ERR_INVALID_ARG
+    assert _suffix_fwd(_desc(), [0, 8, 4]) == pf.PF_ERR_INVALID_ARG
+    assert _suffix_fwd(_desc(), list(range(pf.PF_MAX_SEGMENTS + 2))) == pf.PF_ERR_UNSUPPORTED
+
+
+def test_rejects_bad_tensors():
+    d = _desc()
+    assert _suffix_fwd(d, [0, 4], q=_t(addr=FAKE + 8, heads=32)) == pf.PF_ERR_INVALID_ARG
+    assert _suffix_fwd(d, [0, 4], q=_t(addr=0, heads=32)) == pf.PF_ERR_INVALID_ARG
+    assert _suffix_fwd(d, [0, 4], q=_t(st=32 * 128 + 3, heads=32)) == pf.PF_ERR_INVALID_ARG
+    assert _suffix_fwd(d, [0, 4], q=_t(st=64, sh=64, heads=32)) == pf.PF_ERR_INVALID_ARG
+    assert _suffix_fwd(d, [0, 4], kp=_t(addr=0)) == pf.PF_ERR_INVALID_ARG
+    assert _suffix_fwd(d, [0, 4], lse=0) == pf.PF_ERR_INVALID_ARG
+
+
+def test_rejects_small_workspace():
+    d = pf.AttnDesc(32, 8, 128)
+    need = pf.pf_workspace_size(pf.PF_OP_SUFFIX_FWD, d, 64, 4)
+    assert need > 0
+    assert _suffix_fwd(d._c(), [0, 4], ws_bytes=need - 1) == pf.PF_ERR_WORKSPACE
+    assert _suffix_fwd(d._c(), [0, 4], ws=0) == pf.PF_ERR_WORKSPACE
+
+
+def test_workspace_sizes():
+    d = pf.AttnDesc(32, 8, 128)
+    assert pf.pf_workspace_size(pf.PF_OP_SUFFIX_FWD, d, 4096, 0) == 0
+    small = pf.pf_workspace_size(pf.PF_OP_SUFFIX_BWD, d, 4096, 512)
+    big = pf.pf_workspace_size(pf.PF_OP_SUFFIX_BWD, d, 4096, 4096)
+    assert big >= small > 0
+    # the fp32 family never splits the prefix keys into chunks: no partials
+    f = pf.AttnDesc(2, 2, 64, pf.PF_F32)
+    assert pf.pf_workspace_size(pf.PF_OP_SUFFIX_BWD, f, 256, 256) < 64 * 1024
+    bad = pf.AttnDesc(3, 2, 128)
+    assert pf.pf_workspace_size(pf.PF_OP_SUFFIX_FWD, bad, 16, 16) == 0
+
+
+def test_rejects_bad_trees():
+    def subtree(node_off, parent):
+        no = np.asarray(node_off, dtype=np.int32)
+        pa = np.asarray(parent, dtype=np.int32)
+        out = np.zeros(len(pa), dtype=np.int32)
+        p32 = ctypes.POINTER(ctypes.c_int32)
+        return pf._lib.pf_tree_subtree_end(len(pa), no.ctypes.data_as(p32), pa.ctypes.data_as(p32),
+                                           out.ctypes.data_as(p32))
+    assert subtree([0, 4, 6], [-1, 0]) == pf.PF_OK
+    assert subtree([0, 4, 6], [0, 0]) == pf.PF_ERR_INVALID_ARG          # root must have -1
+    assert subtree([0, 4, 6, 7], [-1, 2, 0]) == pf.PF_ERR_INVALID_ARG   # parent after child
+    assert subtree([0, 4, 3], [-1, 0]) == pf.PF_ERR_INVALID_ARG          # offsets decrease
+    # 0 -> 1 -> 2 and 0 -> 3, then node 4 claiming parent 1 breaks preorder
+    assert subtree([0, 1, 2, 3, 4, 5], [-1, 0, 1, 0, 1]) == pf.PF_ERR_INVALID_ARG
+
+
+def test_tree_visibility_rule_matches_ancestor_mask():
+    """The library's subtree ends give k <= q < end(node(k)) == the oracle's ancestor mask."""
+    for seed in range(60):
+        rng = np.random.default_rng(seed)
+        node_off, parent = random_tree(seed, int(rng.integers(1, 14)), max_len=5, min_len=0)
+        if node_off[-1] == 0:
+            continue
+        end = pf.pf_tree_subtree_end(node_off, parent)
+        c = int(node_off[-1])
+        node = np.searchsorted(node_off, np.arange(c), side="right") - 1
+        rows = np.arange(c)
+        rule = (rows[None, :] <= rows[:, None]) & (rows[:, None] < end[node][None, :])
+        np.testing.assert_array_equal(rule, tree_ancestor_mask(node_off, parent), err_msg=str(seed))
+
+
+def test_prefix_bwd_rejects_bad_dkv_dtype():
+    d, _keep = _desc()
+    t = _t(heads=32)
+    kv = _t()
+    st = pf._lib.pf_prefix_bwd_inject(ctypes.byref(d), 64, t, kv, kv, t, ctypes.c_void_p(FAKE), t,
+                                      ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), t, kv, kv, 7,
+                                      ctypes.c_void_p(FAKE), 1 << 30, ctypes.c_void_p(0))
+    assert st == pf.PF_ERR_INVALID_ARG

@@ -1,0 +1,217 @@
+"""GPU parity of every entry point against the fp64 oracle, on small groups
+that still span several tiles and ragged tails, plus the degenerate cases.
+
+Tolerance: normwise max |x - y| / max |y| <= 2e-2 for bf16 groups and 1e-4
+for fp32 groups, per output tensor.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_util import TOL, check, dev, host
+from workloads.gen import random_small_group, random_tree, random_tree_group
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import shared_prefix_attention_pf_amd as pf
+    from shared_prefix_attention_pf_amd import group as G
+
+
+def _desc(hq, hkv, d, dtype, q_to_kv=None):
+    return pf.AttnDesc(hq, hkv, d, pf.PF_BF16 if dtype == "bf16" else pf.PF_F32, 0.0, q_to_kv)
+
+
+SUFFIX_CASES = [
+    # (hq, hkv, d, dtype, P, suffix lengths, head map)
+    (8, 2, 128, "bf16", 300, [1, 77, 130, 0, 64], None),
+    (4, 4, 128, "bf16", 64, [200], None),
+    (8, 1, 128, "bf16", 129, [33, 257], None),
+    (6, 2, 128, "bf16", 70, [50, 90], None),
+    (4, 2, 128, "bf16", 0, [100, 30], None),
+    (4, 2, 128, "bf16", 96, [40, 41], [1, 0, 0, 1]),
+    (2, 2, 64, "f32", 256, [64, 64, 64, 64], None),
+    (4, 2, 128, "f32", 100, [3, 70, 0], None),
+]
+
+
+@pytest.mark.parametrize("case", SUFFIX_CASES, ids=lambda c: f"{c[3]}-h{c[0]}x{c[1]}-P{c[4]}-{c[5]}")
+def test_suffix_phase_b(case):
+    hq, hkv, d, dtype, p, lens, qmap = case
+    print(f"\ncase {case}", flush=True)
+    g = random_small_group(17, hq, hkv, d, p, lens, dtype)
+    cu = g["cu_seqlens"]
+    desc = _desc(hq, hkv, d, dtype, qmap)
+    scale = 1.0 / math.sqrt(d)
+    t = {k: dev(g[k], dtype) for k in ("k_p", "v_p", "q_s", "k_s", "v_s", "do_s")}
+    o_s, lse_s = G.suffix_fwd(desc, t["k_p"], t["v_p"], cu, t["q_s"], t["k_s"], t["v_s"])
+    gk = torch.zeros(p, hkv, d, dtype=torch.float32, device="cuda")
+    gv = torch.zeros_like(gk)
+    dq, dk, dv = G.suffix_bwd(desc, t["k_p"], t["v_p"], cu, t["q_s"], t["k_s"], t["v_s"], o_s,
+                              lse_s, t["do_s"], gk, gv)
+    torch.cuda.synchronize()
+    hmap = oracle.head_map(hq, hkv, qmap)
+    ref = oracle.suffix_attention(g["k_p"], g["v_p"], g["q_s"], g["k_s"], g["v_s"], g["do_s"], cu,
+                                  scale, hmap)
+    tol = TOL[dtype]
+    check("O_S", host(o_s), ref["o_s"], tol)
+    check("LSE_S", host(lse_s), ref["lse_s"], tol)
+    check("dQ_S", host(dq), ref["dq_s"], tol)
+    check("dK_S", host(dk), ref["dk_s"], tol)
+    check("dV_S", host(dv), ref["dv_s"], tol)
+    if p > 0:
+        check("gK", host(gk), ref["gk"], tol)
+        check("gV", host(gv), ref["gv"], tol)
+
+
+PREFIX_CASES = [
+    (8, 2, 128, "bf16", 300, True),
+    (4, 4, 128, "bf16", 64, True),
+    (8, 2, 128, "bf16", 257, False),
+    (2, 2, 64, "f32", 256, True),
+    (4, 2, 128, "f32", 77, False),
+]
+
+
+@pytest.mark.parametrize("case", PREFIX_CASES, ids=lambda c: f"{c[3]}-h{c[0]}x{c[1]}-P{c[4]}-do{c[5]}")
+def test_prefix_phases_a_and_c(case):
+    hq, hkv, d, dtype, p, with_do = case
+    print(f"\ncase {case}", flush=True)
+    g = random_small_group(23, hq, hkv, d, p, [1], dtype)
+    desc = _desc(hq, hkv, d, dtype)
+    scale = 1.0 / math.sqrt(d)
+    rng = np.random.default_rng(5)
+    gk_np = rng.standard_normal((p, hkv, d)).astype(np.float32)
+    gv_np = rng.standard_normal((p, hkv, d)).astype(np.float32)
+    t = {k: dev(g[k], dtype) for k in ("q_p", "k_p", "v_p", "do_p")}
+    o_p, lse_p = G.prefix_fwd(desc, t["q_p"], t["k_p"], t["v_p"])
+    gk, gv = torch.from_numpy(gk_np).cuda(), torch.from_numpy(gv_np).cuda()
+    do_p = t["do_p"] if with_do else None
+    res = {}
+    for dkv_dtype in {desc.dtype, pf.PF_F32}:
+        res[dkv_dtype] = G.prefix_bwd(desc, t["q_p"], t["k_p"], t["v_p"], o_p, lse_p, do_p, gk, gv,
+                                      dkv_dtype)
+    torch.cuda.synchronize()
+    hmap = oracle.head_map(hq, hkv)
+    ro, rlse = oracle.prefix_forward(g["q_p"], g["k_p"], g["v_p"], scale, hmap)
+    rdq, rdk, rdv = oracle.prefix_backward_inject(g["q_p"], g["k_p"], g["v_p"],
+                                                  g["do_p"] if with_do else None, gk_np, gv_np,
+                                                  scale, hmap)
+    tol = TOL[dtype]
+    check("O_P", host(o_p), ro, tol)
+    check("LSE_P", host(lse_p), rlse, tol)
+    for dkv_dtype, (dq, dk, dv) in res.items():
+        check(f"dQ_P[{dkv_dtype}]", host(dq), rdq, tol)
+        check(f"dK_P[{dkv_dtype}]", host(dk), rdk, tol)
+        check(f"dV_P[{dkv_dtype}]", host(dv), rdv, tol)
+    if not with_do:
+        assert torch.count_nonzero(res[desc.dtype][0]).item() == 0
+        # fp32 outputs equal the accumulators exactly
+        np.testing.assert_array_equal(host(res[pf.PF_F32][1]), gk_np)
+
+
+@pytest.mark.parametrize("seed,hq,hkv,dtype", [(0, 8, 2, "bf16"), (1, 4, 4, "bf16"),
+                                               (2, 2, 1, "f32"), (3, 8, 2, "bf16")])
+def test_tree(seed, hq, hkv, dtype):
+    d = 128 if dtype == "bf16" else 64
+    node_off, parent = random_tree(seed, 9, max_len=90, min_len=0)
+    print(f"\ntree seed {seed}: node_off {node_off.tolist()} parent {parent.tolist()}", flush=True)
+    g = random_tree_group(seed, node_off, hq, hkv, d, dtype)
+    desc = _desc(hq, hkv, d, dtype)
+    t = {k: dev(g[k], dtype) for k in ("q", "k", "v", "do")}
+    o, lse = G.tree_fwd(desc, node_off, parent, t["q"], t["k"], t["v"])
+    dq, dk, dv = G.tree_bwd(desc, node_off, parent, t["q"], t["k"], t["v"], o, lse, t["do"])
+    torch.cuda.synchronize()
+    ref = oracle.tree_attention_direct(g["q"], g["k"], g["v"], g["do"], node_off, parent,
+                                       1.0 / math.sqrt(d), oracle.head_map(hq, hkv))
+    tol = TOL[dtype]
+    for name, got in (("O", o), ("LSE", lse), ("dQ", dq), ("dK", dk), ("dV", dv)):
+        check(name, host(got), ref[name.lower()], tol)
+
+
+def _phase_b_run(desc, t, cu, p, calls):
+    """Run Phase B as the given microbatches (lists of suffix indices); return gK, gV."""
+    hkv, d = t["k_p"].shape[1], t["k_p"].shape[2]
+    gk = torch.zeros(p, hkv, d, dtype=torch.float32, device="cuda")
+    gv = torch.zeros_like(gk)
+    for idx in calls:
+        rows = torch.cat([torch.arange(cu[i], cu[i + 1]) for i in idx]).cuda()
+        sub_cu = np.concatenate([[0], np.cumsum([cu[i + 1] - cu[i] for i in idx])]).astype(np.int32)
+        q, k, v, do = (t[n].index_select(0, rows).contiguous() for n in ("q_s", "k_s", "v_s", "do_s"))
+        o, lse = G.suffix_fwd(desc, t["k_p"], t["v_p"], sub_cu, q, k, v)
+        G.suffix_bwd(desc, t["k_p"], t["v_p"], sub_cu, q, k, v, o, lse, do, gk, gv)
+    torch.cuda.synchronize()
+    return gk, gv
+
+
+# Across microbatch splits only rounding differs.  In bf16 a different split
+# moves a suffix's keys onto different 64-key block boundaries, which changes
+# the running softmax maximum at which P is rounded to bf16 (and the bf16 O
+# that D is built from), so splits agree to the size of the bf16 parity error,
+# not bitwise.  In fp32 only the fp32 summation order differs.
+SPLIT_TOL = {"bf16": 5e-3, "f32": 1e-5}
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_determinism_and_split_invariance(dtype):
+    hq, hkv, p, lens = 8, 2, 520, [60, 130, 1, 200, 64, 90]
+    d = 128
+    g = random_small_group(31, hq, hkv, d, p, lens, dtype)
+    cu = g["cu_seqlens"]
+    desc = _desc(hq, hkv, d, dtype)
+    t = {k: dev(g[k], dtype) for k in ("k_p", "v_p", "q_s", "k_s", "v_s", "do_s")}
+    whole = [list(range(len(lens)))]
+    gk1, gv1 = _phase_b_run(desc, t, cu, p, whole)
+    gk2, gv2 = _phase_b_run(desc, t, cu, p, whole)
+    assert torch.equal(gk1, gk2) and torch.equal(gv1, gv2), "re-run is not bitwise identical"
+    ref = oracle.suffix_attention(g["k_p"], g["v_p"], g["q_s"], g["k_s"], g["v_s"], g["do_s"], cu,
+                                  1.0 / math.sqrt(d), oracle.head_map(hq, hkv))
+    check("gK whole vs oracle", host(gk1), ref["gk"], TOL[dtype])
+    for split in ([[0], [1], [2], [3], [4], [5]], [[5, 3], [0, 2, 1], [4]]):
+        gks, gvs = _phase_b_run(desc, t, cu, p, split)
+        gks2, _ = _phase_b_run(desc, t, cu, p, split)
+        assert torch.equal(gks, gks2), "re-run of a split is not bitwise identical"
+        check(f"gK split {split}", host(gks), host(gk1), SPLIT_TOL[dtype])
+        check(f"gV split {split}", host(gvs), host(gv1), SPLIT_TOL[dtype])
+        check(f"gK split {split} vs oracle", host(gks), ref["gk"], TOL[dtype])
+
+
+def test_no_cross_suffix_leakage():
+    hq, hkv, d, p, lens = 4, 2, 128, 64, [70, 50, 90]
+    g = random_small_group(37, hq, hkv, d, p, lens, "bf16")
+    cu = g["cu_seqlens"]
+    desc = _desc(hq, hkv, d, "bf16")
+    t = {k: dev(g[k], "bf16") for k in ("k_p", "v_p", "q_s", "k_s", "v_s", "do_s")}
+
+    def run(k_s):
+        o, lse = G.suffix_fwd(desc, t["k_p"], t["v_p"], cu, t["q_s"], k_s, t["v_s"])
+        gk = torch.zeros(p, hkv, d, dtype=torch.float32, device="cuda")
+        dq, _, _ = G.suffix_bwd(desc, t["k_p"], t["v_p"], cu, t["q_s"], k_s, t["v_s"], o, lse,
+                                t["do_s"], gk, torch.zeros_like(gk))
+        return o, dq
+
+    o1, dq1 = run(t["k_s"])
+    k2 = t["k_s"].clone()
+    k2[cu[1]:cu[2]] += 1.0
+    o2, dq2 = run(k2)
+    torch.cuda.synchronize()
+    for a, b in ((0, 1), (2, 3)):
+        sl = slice(int(cu[a]), int(cu[b]))
+        assert torch.equal(o1[sl], o2[sl]) and torch.equal(dq1[sl], dq2[sl])
+    assert not torch.equal(o1[cu[1]:cu[2]], o2[cu[1]:cu[2]])
+
+
+def test_empty_call_is_noop():
+    desc = _desc(4, 2, 128, "bf16")
+    kp = torch.zeros(16, 2, 128, dtype=torch.bfloat16, device="cuda")
+    empty_q = torch.zeros(0, 4, 128, dtype=torch.bfloat16, device="cuda")
+    empty_k = torch.zeros(0, 2, 128, dtype=torch.bfloat16, device="cuda")
+    gk = torch.full((16, 2, 128), 3.0, device="cuda")
+    o, lse = G.suffix_fwd(desc, kp, kp, np.array([0, 0], np.int32), empty_q, empty_k, empty_k)
+    G.suffix_bwd(desc, kp, kp, np.array([0, 0], np.int32), empty_q, empty_k, empty_k, o, lse,
+                 empty_q, gk, gk.clone())
+    torch.cuda.synchronize()
+    assert o.shape[0] == 0 and torch.all(gk == 3.0)
