@@ -59,6 +59,11 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
                           "`python shared_prefix_attention_pf_amd/build.py`")
+    # torch ships its own HIP runtime under the same soname as ROCm's.  Loading
+    # torch first makes libpf.so bind to that runtime; loading libpf.so first
+    # would put a second HIP runtime in the process, which then sees no device
+    # and rejects every launch against memory torch allocated.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     T, D, P = _Tensor, ctypes.POINTER(_Desc), ctypes.c_void_p
     i32, sz, fp = ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p
