@@ -33,6 +33,9 @@ def common_flags():
         f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
         "-I", INCLUDE, "-I", CSRC,
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # MFMA builtins produce VGPR results (they feed VALU code); the long-lived
+        # accumulators are placed in AGPRs explicitly by the kernels
+        "-mllvm", "-amdgpu-mfma-vgpr-form=1",
         "-Wall", "-Wno-unused-function",
     ]
 

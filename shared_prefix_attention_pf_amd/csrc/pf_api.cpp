@@ -72,6 +72,7 @@ pf_status check_desc(const pf_attn_desc* desc, Desc* out) {
       return fail(PF_ERR_INVALID_ARG, "KV head %d is read by more than %d query heads", g, group);
     out->heads.qhead[g * group + fill[g]++] = (int16_t)h;
   }
+  out->heads.n = hq;
   return PF_OK;
 }
 
@@ -149,8 +150,9 @@ pf_status check_stream_ws(void* ws, size_t ws_bytes, size_t need) {
 // ------------------------------------------------------------- workspace
 
 struct WsLayout {
-  size_t kend = 0, bmax = 0, bmin = 0, dsum = 0, gk_part = 0, gv_part = 0, total = 0;
-  int32_t n_chunks = 1;
+  size_t kend = 0, bmax = 0, bmin = 0, qhead = 0, dsum = 0, gk_part = 0, gv_part = 0, total = 0;
+  size_t dk_part = 0, dv_part = 0;
+  int32_t n_chunks = 1, n_chunks_own = 1;
 };
 
 WsLayout layout(int32_t op, const Desc& d, int32_t n_ext, int32_t rows) {
@@ -160,6 +162,7 @@ WsLayout layout(int32_t op, const Desc& d, int32_t n_ext, int32_t rows) {
   w.kend = off; off += align_up((size_t)rows * 4);
   w.bmax = off; off += align_up(nb * 4);
   w.bmin = off; off += align_up(nb * 4);
+  w.qhead = off; off += align_up((size_t)d.hq * 4);
   const bool bwd = op == PF_OP_SUFFIX_BWD || op == PF_OP_PREFIX_BWD || op == PF_OP_TREE_BWD;
   if (bwd) {
     w.dsum = off;
@@ -173,6 +176,14 @@ WsLayout layout(int32_t op, const Desc& d, int32_t n_ext, int32_t rows) {
       w.gv_part = off; off += align_up(part);
     }
   }
+  if (bwd) {
+    w.n_chunks_own = pf::own_chunks(op, rows, d.hq, d.hkv, d.d, d.dtype);
+    if (w.n_chunks_own > 1) {
+      const size_t part = (size_t)w.n_chunks_own * rows * d.hkv * d.d * 4;
+      w.dk_part = off; off += align_up(part);
+      w.dv_part = off; off += align_up(part);
+    }
+  }
   w.total = rows > 0 ? off : 0;
   return w;
 }
@@ -183,7 +194,16 @@ pf::RowInfo row_info(void* ws, const WsLayout& w) {
   ri.kend = (int32_t*)(b + w.kend);
   ri.bmax = (int32_t*)(b + w.bmax);
   ri.bmin = (int32_t*)(b + w.bmin);
+  ri.qhead = (int32_t*)(b + w.qhead);
   return ri;
+}
+
+void set_own_parts(pf::AttnArgs& a, void* ws, const WsLayout& w) {
+  a.n_chunks_own = w.n_chunks_own;
+  if (w.n_chunks_own > 1) {
+    a.dk_part = (float*)((char*)ws + w.dk_part);
+    a.dv_part = (float*)((char*)ws + w.dv_part);
+  }
 }
 
 pf::AttnArgs base_args(const Desc& d, int32_t rows) {
@@ -195,8 +215,8 @@ pf::AttnArgs base_args(const Desc& d, int32_t rows) {
   a.group = d.group;
   a.scale = d.scale;
   a.scale_log2 = d.scale * 1.4426950408889634f;
-  a.heads = d.heads;
   a.n_chunks = 1;
+  a.n_chunks_own = 1;
   return a;
 }
 
@@ -249,7 +269,7 @@ pf::SegTable tree_segments(int32_t n, const int32_t* node_off, const int32_t* su
 // ------------------------------------------------------------- launches
 
 pf_status run_fwd(const Desc& d, const pf::AttnArgs& a, const pf::SegTable& seg, hipStream_t st) {
-  hipError_t e = pf::launch_prep(seg, a.ri, st);
+  hipError_t e = pf::launch_prep(seg, d.heads, a.ri, st);
   if (e != hipSuccess) return hip_fail(e, "prep");
   e = d.dtype == PF_BF16 ? pf::launch_fwd_bf16(a, d.d, st) : pf::launch_fwd_f32(a, d.d, st);
   if (e != hipSuccess) return hip_fail(e, "forward");
@@ -257,7 +277,7 @@ pf_status run_fwd(const Desc& d, const pf::AttnArgs& a, const pf::SegTable& seg,
 }
 
 pf_status run_bwd(const Desc& d, const pf::AttnArgs& a, const pf::SegTable& seg, hipStream_t st) {
-  hipError_t e = pf::launch_prep(seg, a.ri, st);
+  hipError_t e = pf::launch_prep(seg, d.heads, a.ri, st);
   if (e != hipSuccess) return hip_fail(e, "prep");
   e = d.dtype == PF_BF16 ? pf::launch_bwd_dq_bf16(a, d.d, st) : pf::launch_bwd_dq_f32(a, d.d, st);
   if (e != hipSuccess) return hip_fail(e, "dq");
@@ -268,6 +288,14 @@ pf_status run_bwd(const Desc& d, const pf::AttnArgs& a, const pf::SegTable& seg,
     e = pf::launch_reduce_partials(a.gk_part, a.gk_acc, a.n_chunks, n, st);
     if (e == hipSuccess) e = pf::launch_reduce_partials(a.gv_part, a.gv_acc, a.n_chunks, n, st);
     if (e != hipSuccess) return hip_fail(e, "reduce");
+  }
+  if (a.n_chunks_own > 1) {
+    e = pf::launch_finish_own(a.dk_part, a.n_chunks_own, a.gk_init, a.dk_own, a.rows, d.hkv, d.d,
+                              a.dko_st, a.dko_sh, a.dkv_f32, st);
+    if (e == hipSuccess)
+      e = pf::launch_finish_own(a.dv_part, a.n_chunks_own, a.gv_init, a.dv_own, a.rows, d.hkv,
+                                d.d, a.dvo_st, a.dvo_sh, a.dkv_f32, st);
+    if (e != hipSuccess) return hip_fail(e, "finish");
   }
   return PF_OK;
 }
@@ -286,16 +314,33 @@ void launch_hook(const char* kernel, hipStream_t stream, int end) {
   if (h) h(kernel, (void*)stream, end, g_hook_user);
 }
 
+// Chunk counts aim for >= 512 workgroups (two rounds over 256 CUs) while each
+// chunk keeps at least 32 query steps of 32 rows.
 int32_t ext_chunks(int32_t n_ext, int32_t rows, int32_t hq, int32_t hkv, int32_t head_dim,
                    int32_t dtype) {
   (void)head_dim;
   if (dtype != PF_BF16 || n_ext <= 0 || rows <= 0) return 1;
-  // aim for >= 512 workgroups of prefix keys (two per CU on 256 CUs), while
-  // each chunk keeps at least 64 query steps of 32 rows
-  const int64_t wgs = (int64_t)((n_ext + 127) / 128) * hkv;
+  const int kb = dkv_keys_per_workgroup_bf16();
+  const int64_t wgs = (int64_t)((n_ext + kb - 1) / kb) * hkv;
   const int64_t steps = (int64_t)((rows + 31) / 32) * (hq / hkv);
   int32_t nc = 1;
-  while (nc < 8 && wgs * nc < 512 && steps / (2 * nc) >= 64) nc *= 2;
+  while (nc < 8 && wgs * nc < 512 && steps / (2 * nc) >= 32) nc *= 2;
+  return nc;
+}
+
+// Own keys: a causal prefix (Phase C) or a tree has key blocks whose query
+// ranges average about half the rows; Phase-B suffix keys only see their own
+// suffix and stay unsplit.
+int32_t own_chunks(int32_t op, int32_t rows, int32_t hq, int32_t hkv, int32_t head_dim,
+                   int32_t dtype) {
+  (void)head_dim;
+  if (dtype != PF_BF16 || rows <= 0) return 1;
+  if (op != PF_OP_PREFIX_BWD && op != PF_OP_TREE_BWD) return 1;
+  const int kb = dkv_keys_per_workgroup_bf16();
+  const int64_t wgs = (int64_t)((rows + kb - 1) / kb) * hkv;
+  const int64_t steps = (int64_t)((rows / 2 + 31) / 32) * (hq / hkv);
+  int32_t nc = 1;
+  while (nc < 8 && wgs * nc < 512 && steps / (2 * nc) >= 32) nc *= 2;
   return nc;
 }
 
@@ -444,6 +489,7 @@ pf_status pf_suffix_attn_bwd_accum(const pf_attn_desc* desc, int32_t prefix_len,
     a.gv_part = (float*)((char*)workspace + w.gv_part);
   }
   a.dsum = (float*)((char*)workspace + w.dsum);
+  set_own_parts(a, workspace, w);
   a.ri = row_info(workspace, w);
   return run_bwd(d, a, flat_segments(n_suffix, cu_seqlens), (hipStream_t)stream);
 }
@@ -505,6 +551,7 @@ pf_status pf_prefix_bwd_inject(const pf_attn_desc* desc, int32_t prefix_len, pf_
   a.gv_init = gv_acc;
   a.lse = const_cast<float*>(lse_p);
   a.dsum = (float*)((char*)workspace + w.dsum);
+  set_own_parts(a, workspace, w);
   a.ri = row_info(workspace, w);
   return run_bwd(d, a, causal_segment(prefix_len), st);
 }
@@ -567,6 +614,7 @@ pf_status pf_tree_attn_bwd(const pf_attn_desc* desc, int32_t n_nodes, const int3
   a.dkv_f32 = d.dtype == PF_F32;
   a.lse = const_cast<float*>(lse);
   a.dsum = (float*)((char*)workspace + w.dsum);
+  set_own_parts(a, workspace, w);
   a.ri = row_info(workspace, w);
   return run_bwd(d, a, tree_segments(n_nodes, node_off, send), (hipStream_t)stream);
 }

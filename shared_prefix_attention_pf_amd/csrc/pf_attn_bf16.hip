@@ -5,28 +5,37 @@
 //                   suffix forward over the cached prefix (read in place),
 //                   Phase A (causal prefix) and the tree forward.
 //   bwd_dq_kernel   Q-stationary backward: D = rowsum(dO * O) and dQ.
-//   bwd_dkv_kernel  KV-stationary backward: dK, dV of one key block summed over
-//                   every query row and every query head of its KV head.  For
-//                   the prefix ("external") keys of Phase B that sum is the
-//                   group's prefix-side gradient gK/gV (PrefixFlow §3.3, §4.1),
-//                   added to the fp32 accumulator by the one workgroup that
-//                   owns the block (or written as a per-chunk partial and
-//                   reduced in fixed order): no atomics, no races.
+//   bwd_dkv_kernel  KV-stationary backward: dK, dV of a key block summed over
+//                   the query rows of its range and every query head of its KV
+//                   head.  For the prefix ("external") keys of Phase B that sum
+//                   is the group's prefix-side gradient gK/gV (PrefixFlow §3.3,
+//                   §4.1), added to the fp32 accumulator by the one workgroup
+//                   that owns the block, or written as a per-chunk partial and
+//                   reduced in a fixed order: no atomics, no races.
 //
-// Matrix-core layout.  All contractions use v_mfma_f32_32x32x16_bf16:
-//   A (32 x 16): lane l holds A[l % 32][8 (l / 32) + i], i = 0..7
-//   B (16 x 32): lane l holds B[8 (l / 32) + i][l % 32]
-//   C (32 x 32): lane l holds C[8 (i / 4) + 4 (l / 32) + (i % 4)][l % 32], i = 0..15
-// The forward and dQ kernels compute S^T = K Q^T, so a lane owns one query
-// (column) and the softmax statistics are per lane.  A C tile of P^T (or
-// dS^T) is reused directly as the B operand of the next product: its 16
+// Matrix cores: every product is v_mfma_f32_32x32x16_bf16,
+//   A (32 x 16): lane l holds A[l % 32][8 (l / 32) + e], e = 0..7
+//   B (16 x 32): lane l holds B[8 (l / 32) + e][l % 32]
+//   C (32 x 32): lane l holds C[8 (i / 4) + 4 (l / 32) + i % 4][l % 32], i = 0..15
+// A C tile is reused directly as the B operand of the next product: its 16
 // values per lane are two 8-value k-steps whose contraction index runs over
-// keys {16s + 8(i/4) + 4(l/32) + i%4}.  The matching A operands (V^T, K^T) are
-// staged in LDS with keys permuted the same way inside every 16-key group
-// (offsets 4..7 and 8..11 swapped), so each A fragment is one 16-byte read.
-// The dK/dV kernel computes S = Q K^T (a lane owns one key) and reuses P and
-// dS as B operands the same way, with Q^T and dO^T staged permuted in LDS.
+// rows {16 s + 8 (e / 4) + 4 (l / 32) + e % 4}.  The matching A operand is read
+// from a row-major tile with the gfx950 transposing LDS read
+// (ds_read_b64_tr_b16), whose per-lane row addresses implement that order, so
+// no tile is ever stored transposed.
+//
+// LDS tiles hold rows of 128 bf16 (256 B) without padding; the 16-byte chunk
+// c of row r is stored at chunk c ^ swz(r).  swz spreads 16 consecutive rows
+// read at one chunk (the 16-byte fragment reads) and 4 consecutive rows read
+// across 4 chunks (the transposing reads) over all 64 banks.
+//
+// Each wave owns 64 rows of its stationary operand (queries in the forward
+// and dQ kernels, keys in the dK/dV kernel), so every fragment read from LDS
+// feeds two MFMAs and LDS traffic stays near half of its bandwidth at full
+// MFMA rate.
 #include <math.h>
+
+#include <type_traits>
 
 #include "pf_internal.h"
 
@@ -37,17 +46,36 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_t;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kD = 128;           // head_dim of this kernel family
-constexpr int kDP = kD + 8;       // LDS row pitch (elements) of [row][d] tiles
-constexpr int kThreads = 256;     // 4 waves
-constexpr int kRowsPerWg = 256;   // query rows (token x head) per Q-stationary workgroup
+constexpr int kD = 128;            // head_dim of this kernel family
+constexpr int kThreads = 256;      // 4 waves
+constexpr int kRowB = 2 * kD;      // bytes of one LDS tile row
+constexpr int kRowsPerWg = 256;    // query rows (token x head) per Q-stationary workgroup
+constexpr float kRescale = 8.0f;   // lazy rescale threshold (log2 units)
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+
+// Accumulating product with the accumulator held in AGPRs (acc += A B).  The
+// compiler keeps MFMA results it feeds to VALU code in VGPRs; the long-lived
+// accumulators of the PV, dQ and dK/dV products go to the AGPR file through
+// this form so the two files together hold a wave's working set.  Back-to-back
+// accumulation into the same registers needs no wait states; VALU reads of an
+// accumulator after its last product are separated by acc_fence().
+__device__ __forceinline__ void mfma_acc(f32x16& acc, bf16x8 a, bf16x8 b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+// wait states between the last accumulating product and VALU reads of it
+__device__ __forceinline__ void acc_fence() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
 
 __device__ __forceinline__ f32x16 zero16() {
   f32x16 z;
@@ -57,9 +85,6 @@ __device__ __forceinline__ f32x16 zero16() {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// position of key offset o (0..15) inside a permuted 16-key group
-__device__ __forceinline__ int perm16(int o) { return (o & ~12) | ((o & 4) << 1) | ((o & 8) >> 1); }
 
 __device__ __forceinline__ bf16x8 load8(const __bf16* p) { return *(const bf16x8*)p; }
 
@@ -77,6 +102,67 @@ __device__ __forceinline__ bf16x8 pack_half(const f32x16& c, int half) {
   for (int i = 0; i < 8; ++i) r[i] = (__bf16)c[8 * half + i];
   return r;
 }
+
+// ---------------------------------------------------------------------------
+// Swizzled LDS tiles.  Every kernel keeps its tiles in one __shared__ byte
+// array at compile-time offsets; a fragment read is one per-lane offset from
+// the Frag table plus an immediate (tile, buffer, row block).
+__device__ __forceinline__ uint32_t swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// byte offset of element (r, col) of a tile
+__device__ __forceinline__ uint32_t toff(int r, int col) {
+  return (uint32_t)r * kRowB + ((((uint32_t)col >> 3) ^ swz(r)) << 4) + (((uint32_t)col & 7) << 1);
+}
+
+// Per-lane offsets of the two fragment shapes (swz depends on the row mod 16
+// only, so whole 16-row blocks are immediates):
+//   row8[ds]    16-byte fragment (row l % 32, columns 16 ds + 8 (l / 32) ..+7):
+//               the A/B operand layout along the contraction over head_dim;
+//               add 32 rows (8192 B) per further 32-row tile.
+//   tr[dt][hi]  transposing read for the A operand (32 m x 16 k) from a
+//               row-major [k][m] tile, m-tile dt (columns 32 dt ..), rows
+//               4 (l / 32) + (l % 16) / 4 + 8 hi; add 4096 B per 16-row k-step.
+//               Element e of the fragment is tile[16 s + 8 (e / 4) + 4 (l / 32)
+//               + e % 4][32 dt + l % 32], the contraction order of a C tile
+//               reused as a B operand: within each 16-lane group the
+//               transposing read hands lane i element (i & 3) of the 8 bytes
+//               addressed by lane 4 k + (i >> 2), for k = 0..3.
+struct Frag {
+  uint32_t row8[kD / 16];
+  uint32_t tr[kD / 32][2];
+};
+
+__device__ __forceinline__ void frag_init(Frag& f, int lane) {
+  const int col = lane & 31, h = lane >> 5, i = lane & 15;
+#pragma unroll
+  for (int ds = 0; ds < kD / 16; ++ds) f.row8[ds] = toff(col, ds * 16 + 8 * h);
+  const int r0 = 4 * h + (i >> 2);
+  const int c0 = 16 * ((lane >> 4) & 1) + 4 * (i & 3);
+#pragma unroll
+  for (int dt = 0; dt < kD / 32; ++dt) {
+    f.tr[dt][0] = toff(r0, dt * 32 + c0);
+    f.tr[dt][1] = toff(r0 + 8, dt * 32 + c0);
+  }
+}
+
+__device__ __forceinline__ bf16x8 ld_row8(const lds_t* p) { return *(const lds_bf16x8*)p; }
+
+__device__ __forceinline__ bf16x8 ld_tr(const lds_t* lo, const lds_t* hi) {
+  const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)lo);
+  const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)hi);
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ void st16(lds_t* p, u32x4 v) { *(lds_u32x4*)p = v; }
+
+__device__ __forceinline__ u32x4 load16(const __bf16* p) { return *(const u32x4*)p; }
+__device__ __forceinline__ u32x4 zero_u4() { return u32x4{0u, 0u, 0u, 0u}; }
+
+// Staging offset of thread t: chunk (t & 15) of row t / 16 (+ 16 rows =
+// + 4096 B per further pass of 256 threads).
+__device__ __forceinline__ uint32_t stage_off(int t) { return toff(t >> 4, (t & 15) * 8); }
+
+template <int B> using Buf = std::integral_constant<int, B>;
 
 // Workgroup -> (KV head, item) with XCD awareness: workgroups are dispatched
 // round-robin over the 8 XCDs, so when Hkv is a multiple of 8 every XCD gets
@@ -109,7 +195,7 @@ __device__ __forceinline__ QCol qcol(const AttnArgs& a, int g, int t0, int tq, i
   const int j = r / tq;
   c.tok = t0 + (r - j * tq);
   c.valid = (j < a.group) && (c.tok < a.rows);
-  c.head = c.valid ? a.heads.qhead[g * a.group + j] : 0;
+  c.head = c.valid ? a.ri.qhead[g * a.group + j] : 0;
   if (!c.valid) c.tok = 0;
   return c;
 }
@@ -163,21 +249,54 @@ struct KeyWalk {
   }
 };
 
-// ---------------------------------------------------------------------------
-// Forward.
-//
-// LDS per stage: K [BN][kDP] and V^T [kD][BN + 8] (keys permuted), kend [BN].
+// Key/value block staging for the Q-stationary kernels: BN rows of K and V
+// (128 bf16 each) from global memory through registers into swizzled LDS.
 template <int BN>
-struct FwdSmem {
-  __bf16 k[2][BN][kDP];
-  __bf16 vt[2][kD][BN + 8];
-  int32_t kend[2][BN];
+struct KvStage {
+  static constexpr int kPer = BN * 16 / kThreads;   // 16-byte chunks per thread per tensor
+  u32x4 kreg[kPer], vreg[kPer];
+  int kendreg;
+
+  __device__ void issue(const AttnArgs& a, int g, bool ext, int k0, int tid) {
+    const int klim = ext ? a.n_ext : a.rows;
+    const __bf16* kb = (const __bf16*)(ext ? a.k_ext : a.k_own);
+    const __bf16* vb = (const __bf16*)(ext ? a.v_ext : a.v_own);
+    const int64_t kst = ext ? a.kx_st : a.ko_st, ksh = ext ? a.kx_sh : a.ko_sh;
+    const int64_t vst = ext ? a.vx_st : a.vo_st, vsh = ext ? a.vx_sh : a.vo_sh;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int c = tid + kThreads * i;
+      const int kk = k0 + (c >> 4), ch = c & 15;
+      const bool ok = kk < klim;
+      kreg[i] = ok ? load16(kb + (int64_t)kk * kst + (int64_t)g * ksh + ch * 8) : zero_u4();
+      vreg[i] = ok ? load16(vb + (int64_t)kk * vst + (int64_t)g * vsh + ch * 8) : zero_u4();
+    }
+    if (!ext && tid < BN) {
+      const int kk = k0 + tid;
+      kendreg = (kk < a.rows) ? a.ri.kend[kk] : -1;
+    }
+  }
+  __device__ void stash(lds_t* kt, lds_t* vt, int32_t* kend, bool ext, int tid, uint32_t so) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      st16(kt + so + i * 16 * kRowB, kreg[i]);
+      st16(vt + so + i * 16 * kRowB, vreg[i]);
+    }
+    if (!ext && tid < BN) kend[tid] = kendreg;
+  }
 };
 
-template <int BN>
-__global__ __launch_bounds__(kThreads) void fwd_kernel(AttnArgs a) {
-  static_assert(BN == 64, "staging below assumes 64-key blocks");
-  __shared__ FwdSmem<BN> sm;
+// ---------------------------------------------------------------------------
+// Forward.
+constexpr int kFwdBN = 64;
+constexpr int kFwdTile = kFwdBN * kRowB;            // one K or V block
+constexpr int kFwdK = 0, kFwdV = 2 * kFwdTile;      // two K buffers, then two V buffers
+
+__global__ __launch_bounds__(kThreads, 1) void fwd_kernel(AttnArgs a) {
+  constexpr int BN = kFwdBN;
+  __shared__ __attribute__((aligned(16))) char smem[4 * kFwdTile];
+  __shared__ int32_t kend_s[2][BN];
+  lds_t* const sb = (lds_t*)smem;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int col = lane & 31, h32 = lane >> 5;
@@ -211,59 +330,12 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(AttnArgs a) {
   walk.bmin = a.ri.bmin;
   walk.rows = a.rows;
 
-  // staging registers: K rows (4 x 16 B per thread) and V (4 keys x 8 d)
-  uint4 kreg[4], vreg[4];
-  int kendreg = 0;
-  const int v_kg = tid & 15, v_dc = tid >> 4;   // V: keys 4 v_kg..+3, d 8 v_dc..+7
-
-  auto issue = [&](int blk) {
-    const bool ext = blk < walk.n_ext_blocks;
-    const int k0 = (ext ? blk : blk - walk.n_ext_blocks) * BN;
-    const int klim = ext ? a.n_ext : a.rows;
-    const __bf16* kb = (const __bf16*)(ext ? a.k_ext : a.k_own);
-    const __bf16* vb = (const __bf16*)(ext ? a.v_ext : a.v_own);
-    const int64_t kst = ext ? a.kx_st : a.ko_st, ksh = ext ? a.kx_sh : a.ko_sh;
-    const int64_t vst = ext ? a.vx_st : a.vo_st, vsh = ext ? a.vx_sh : a.vo_sh;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + kThreads * i;
-      const int key = c >> 4, dch = c & 15;
-      const int kk = k0 + key;
-      kreg[i] = (kk < klim) ? *(const uint4*)(kb + (int64_t)kk * kst + (int64_t)g * ksh + dch * 8)
-                            : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int kk = k0 + 4 * v_kg + r;
-      vreg[r] = (kk < klim) ? *(const uint4*)(vb + (int64_t)kk * vst + (int64_t)g * vsh + v_dc * 8)
-                            : make_uint4(0, 0, 0, 0);
-    }
-    if (!ext && tid < BN) {
-      const int kk = k0 + tid;
-      kendreg = (kk < a.rows) ? a.ri.kend[kk] : -1;
-    }
-  };
-  auto stash = [&](int buf, int blk) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + kThreads * i;
-      *(uint4*)&sm.k[buf][c >> 4][(c & 15) * 8] = kreg[i];
-    }
-    // transpose V: for each of the 8 d values, 4 consecutive keys
-    const __bf16* v16[4] = {(const __bf16*)&vreg[0], (const __bf16*)&vreg[1],
-                            (const __bf16*)&vreg[2], (const __bf16*)&vreg[3]};
-    const int kpos = (4 * v_kg & ~15) + perm16((4 * v_kg) & 15);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      bf16x4 w;
-      w[0] = v16[0][e]; w[1] = v16[1][e]; w[2] = v16[2][e]; w[3] = v16[3][e];
-      *(bf16x4*)&sm.vt[buf][v_dc * 8 + e][kpos] = w;
-    }
-    if (blk >= walk.n_ext_blocks && tid < BN) sm.kend[buf][tid] = kendreg;
-  };
-
+  Frag f;
+  frag_init(f, lane);
+  const uint32_t so = stage_off(tid);
+  KvStage<BN> st;
   const float c = a.scale_log2;
-  float mrow[2] = {-INFINITY, -INFINITY};
+  float mrow[2] = {-INFINITY, -INFINITY};   // running max (log2 units) in use
   float lrow[2] = {0.f, 0.f};
   f32x16 acc[kD / 32][2];
 #pragma unroll
@@ -271,19 +343,15 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(AttnArgs a) {
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) acc[dt][nt] = zero16();
 
-  int blk = walk.next(0);
-  if (blk >= 0) {
-    issue(blk);
-    stash(0, blk);
-  }
-  __syncthreads();
-  int buf = 0;
-  while (blk >= 0) {
-    const int nxt = walk.next(blk + 1);
-    if (nxt >= 0) issue(nxt);
+  auto blk_k0 = [&](int b) { return (b < walk.n_ext_blocks ? b : b - walk.n_ext_blocks) * BN; };
 
+  // one key block held in buffer B; stages block nxt into the other buffer
+  auto block = [&](auto bc, int blk, int nxt) {
+    constexpr int B = decltype(bc)::value;
+    const lds_t* kt_s = sb + kFwdK + B * kFwdTile;
+    const lds_t* vt_s = sb + kFwdV + B * kFwdTile;
     const bool ext = blk < walk.n_ext_blocks;
-    const int k0 = (ext ? blk : blk - walk.n_ext_blocks) * BN;
+    const int k0 = blk_k0(blk);
     const bool msk = walk.masked(blk, a.n_ext);
 
     // S^T = K Q^T for BN keys x 64 queries
@@ -296,7 +364,7 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(AttnArgs a) {
     for (int ds = 0; ds < kD / 16; ++ds) {
 #pragma unroll
       for (int kt = 0; kt < BN / 32; ++kt) {
-        const bf16x8 af = load8(&sm.k[buf][kt * 32 + col][ds * 16 + 8 * h32]);
+        const bf16x8 af = ld_row8(kt_s + kt * 32 * kRowB + f.row8[ds]);
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) s[kt][nt] = mfma(af, qf[nt][ds], s[kt][nt]);
       }
@@ -311,7 +379,7 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(AttnArgs a) {
           const int kk = k0 + kl;
           bool vis0 = kk < klim, vis1 = kk < klim;
           if (!ext) {
-            const int ke = sm.kend[buf][kl];
+            const int ke = kend_s[B][kl];
             vis0 = vis0 && kk <= qc[0].tok && qc[0].tok < ke;
             vis1 = vis1 && kk <= qc[1].tok && qc[1].tok < ke;
           }
@@ -319,20 +387,39 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(AttnArgs a) {
           if (!vis1) s[kt][1][i] = -INFINITY;
         }
     }
-    // online softmax (log2 domain), per query column
-    bf16x8 pb[2][BN / 16];
+    // online softmax (log2 domain), per query column, with lazy rescaling:
+    // the running maximum in use only moves when a block exceeds it by more
+    // than kRescale, so probabilities stay below 2^kRescale
+    float mx[2];
+    bool grow = false;
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      float mx = -INFINITY;
+      float m = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < BN / 32; ++kt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][nt][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(mrow[nt], mx * c);
-      const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-      const float alpha = fast_exp2(mrow[nt] - muse);
-      mrow[nt] = mnew;
+        for (int i = 0; i < 16; ++i) m = fmaxf(m, s[kt][nt][i]);
+      m = fmaxf(m, __shfl_xor(m, 32)) * c;
+      mx[nt] = m;
+      grow = grow || (m > mrow[nt] + kRescale);
+    }
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      acc_fence();
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const float mnew = fmaxf(mrow[nt], mx[nt]);
+        const float alpha = (mnew > mrow[nt]) ? fast_exp2(mrow[nt] - mnew) : 1.f;
+        lrow[nt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < kD / 32; ++dt) acc[dt][nt] *= alpha;
+        mrow[nt] = mnew;
+      }
+      acc_fence();
+    }
+    bf16x8 pb[2][BN / 16];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const float muse = (mrow[nt] == -INFINITY) ? 0.f : mrow[nt];
       float lsum = 0.f;
 #pragma unroll
       for (int kt = 0; kt < BN / 32; ++kt) {
@@ -345,27 +432,46 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(AttnArgs a) {
         pb[nt][2 * kt] = pack_half(s[kt][nt], 0);
         pb[nt][2 * kt + 1] = pack_half(s[kt][nt], 1);
       }
-      lrow[nt] = lrow[nt] * alpha + lsum;
-#pragma unroll
-      for (int dt = 0; dt < kD / 32; ++dt) acc[dt][nt] *= alpha;
+      lrow[nt] += lsum;
     }
     // O^T += V^T P^T
 #pragma unroll
     for (int dt = 0; dt < kD / 32; ++dt) {
 #pragma unroll
       for (int ks = 0; ks < BN / 16; ++ks) {
-        const bf16x8 af = load8(&sm.vt[buf][dt * 32 + col][ks * 16 + 8 * h32]);
+        const lds_t* vb = vt_s + ks * 16 * kRowB;
+        const bf16x8 af = ld_tr(vb + f.tr[dt][0], vb + f.tr[dt][1]);
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) acc[dt][nt] = mfma(af, pb[nt][ks], acc[dt][nt]);
+        for (int nt = 0; nt < 2; ++nt) mfma_acc(acc[dt][nt], af, pb[nt][ks]);
       }
     }
-    if (nxt >= 0) stash(buf ^ 1, nxt);
+    if (nxt >= 0)
+      st.stash(sb + kFwdK + (1 - B) * kFwdTile, sb + kFwdV + (1 - B) * kFwdTile, kend_s[1 - B],
+               nxt < walk.n_ext_blocks, tid, so);
     __syncthreads();
-    buf ^= 1;
+  };
+
+  int blk = walk.next(0);
+  if (blk >= 0) {
+    const bool ext = blk < walk.n_ext_blocks;
+    st.issue(a, g, ext, blk_k0(blk), tid);
+    st.stash(sb + kFwdK, sb + kFwdV, kend_s[0], ext, tid, so);
+  }
+  __syncthreads();
+  while (blk >= 0) {
+    int nxt = walk.next(blk + 1);
+    if (nxt >= 0) st.issue(a, g, nxt < walk.n_ext_blocks, blk_k0(nxt), tid);
+    block(Buf<0>(), blk, nxt);
+    blk = nxt;
+    if (blk < 0) break;
+    nxt = walk.next(blk + 1);
+    if (nxt >= 0) st.issue(a, g, nxt < walk.n_ext_blocks, blk_k0(nxt), tid);
+    block(Buf<1>(), blk, nxt);
     blk = nxt;
   }
 
   // finalize: O = acc / l, LSE = (m + log2 l) ln 2
+  acc_fence();
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     const float l = lrow[nt] + __shfl_xor(lrow[nt], 32);
@@ -389,20 +495,15 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(AttnArgs a) {
 
 // ---------------------------------------------------------------------------
 // Backward, Q-stationary: D and dQ.
-//
-// LDS per stage: K [BN][kDP], V [BN][kDP], K^T [kD][BN + 8] (keys permuted).
-template <int BN>
-struct DqSmem {
-  __bf16 k[2][BN][kDP];
-  __bf16 v[2][BN][kDP];
-  __bf16 kt[2][kD][BN + 8];
-  int32_t kend[2][BN];
-};
+constexpr int kDqBN = 32;
+constexpr int kDqTile = kDqBN * kRowB;
+constexpr int kDqK = 0, kDqV = 2 * kDqTile;
 
-template <int BN>
-__global__ __launch_bounds__(kThreads) void bwd_dq_kernel(AttnArgs a) {
-  static_assert(BN == 32, "staging below assumes 32-key blocks");
-  __shared__ DqSmem<BN> sm;
+__global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(AttnArgs a) {
+  constexpr int BN = kDqBN;
+  __shared__ __attribute__((aligned(16))) char smem[4 * kDqTile];
+  __shared__ int32_t kend_s[2][BN];
+  lds_t* const sb = (lds_t*)smem;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int col = lane & 31, h32 = lane >> 5;
@@ -449,54 +550,10 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(AttnArgs a) {
   walk.bmin = a.ri.bmin;
   walk.rows = a.rows;
 
-  // staging: K and V rows (2 x 16 B each per thread); K^T from the K registers
-  uint4 kreg[2], vreg[2];
-  int kendreg = 0;
-  auto issue = [&](int blk) {
-    const bool ext = blk < walk.n_ext_blocks;
-    const int k0 = (ext ? blk : blk - walk.n_ext_blocks) * BN;
-    const int klim = ext ? a.n_ext : a.rows;
-    const __bf16* kb = (const __bf16*)(ext ? a.k_ext : a.k_own);
-    const __bf16* vb = (const __bf16*)(ext ? a.v_ext : a.v_own);
-    const int64_t kst = ext ? a.kx_st : a.ko_st, ksh = ext ? a.kx_sh : a.ko_sh;
-    const int64_t vst = ext ? a.vx_st : a.vo_st, vsh = ext ? a.vx_sh : a.vo_sh;
-    // thread -> (key = 4 * (tid & 7) + i, d chunk = tid >> 3), i = 0..1 pairs of
-    // consecutive keys (0/1 or 2/3) so the transposed store writes 4 keys at once
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int key = 4 * (tid & 7) + 2 * (tid >> 7) + i;   // tid >> 7 in {0, 1}
-      const int dch = (tid >> 3) & 15;
-      const int kk = k0 + key;
-      kreg[i] = (kk < klim) ? *(const uint4*)(kb + (int64_t)kk * kst + (int64_t)g * ksh + dch * 8)
-                            : make_uint4(0, 0, 0, 0);
-      vreg[i] = (kk < klim) ? *(const uint4*)(vb + (int64_t)kk * vst + (int64_t)g * vsh + dch * 8)
-                            : make_uint4(0, 0, 0, 0);
-    }
-    if (!ext && tid < BN) {
-      const int kk = k0 + tid;
-      kendreg = (kk < a.rows) ? a.ri.kend[kk] : -1;
-    }
-  };
-  auto stash = [&](int buf, int blk) {
-    const int kg = tid & 7, half = tid >> 7, dch = (tid >> 3) & 15;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int key = 4 * kg + 2 * half + i;
-      *(uint4*)&sm.k[buf][key][dch * 8] = kreg[i];
-      *(uint4*)&sm.v[buf][key][dch * 8] = vreg[i];
-    }
-    // K^T: 2 consecutive keys per d value (keys 4 kg + 2 half + {0, 1})
-    const __bf16* k16[2] = {(const __bf16*)&kreg[0], (const __bf16*)&kreg[1]};
-    const int o = 4 * kg + 2 * half;
-    const int kpos = (o & ~15) + perm16(o & 15);    // o & 3 in {0, 2}: stays contiguous
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      __bf16 w[2] = {k16[0][e], k16[1][e]};
-      *(uint32_t*)&sm.kt[buf][dch * 8 + e][kpos] = *(uint32_t*)w;
-    }
-    if (blk >= walk.n_ext_blocks && tid < BN) sm.kend[buf][tid] = kendreg;
-  };
-
+  Frag f;
+  frag_init(f, lane);
+  const uint32_t so = stage_off(tid);
+  KvStage<BN> st;
   const float c = a.scale_log2;
   f32x16 acc[kD / 32][2];
 #pragma unroll
@@ -504,26 +561,23 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(AttnArgs a) {
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) acc[dt][nt] = zero16();
 
-  int blk = walk.next(0);
-  if (blk >= 0) {
-    issue(blk);
-    stash(0, blk);
-  }
-  __syncthreads();
-  int buf = 0;
-  while (blk >= 0) {
-    const int nxt = walk.next(blk + 1);
-    if (nxt >= 0) issue(nxt);
+  auto blk_k0 = [&](int b) { return (b < walk.n_ext_blocks ? b : b - walk.n_ext_blocks) * BN; };
+
+  auto block = [&](auto bc, int blk, int nxt) {
+    constexpr int B = decltype(bc)::value;
+    const lds_t* kt_s = sb + kDqK + B * kDqTile;
+    const lds_t* vt_s = sb + kDqV + B * kDqTile;
     const bool ext = blk < walk.n_ext_blocks;
-    const int k0 = (ext ? blk : blk - walk.n_ext_blocks) * BN;
+    const int k0 = blk_k0(blk);
     const bool msk = walk.masked(blk, a.n_ext);
 
+    // S^T = K Q^T and dP^T = V dO^T: 32 keys x 64 queries
     f32x16 s[2], dp[2];
     s[0] = zero16(); s[1] = zero16(); dp[0] = zero16(); dp[1] = zero16();
 #pragma unroll
     for (int ds = 0; ds < kD / 16; ++ds) {
-      const bf16x8 ka = load8(&sm.k[buf][col][ds * 16 + 8 * h32]);
-      const bf16x8 va = load8(&sm.v[buf][col][ds * 16 + 8 * h32]);
+      const bf16x8 ka = ld_row8(kt_s + f.row8[ds]);
+      const bf16x8 va = ld_row8(vt_s + f.row8[ds]);
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         s[nt] = mfma(ka, qf[nt][ds], s[nt]);
@@ -540,7 +594,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(AttnArgs a) {
           const int kl = 8 * (i >> 2) + 4 * h32 + (i & 3);
           const int kk = k0 + kl;
           bool vis = kk < (ext ? a.n_ext : a.rows);
-          if (!ext) vis = vis && kk <= qc[nt].tok && qc[nt].tok < sm.kend[buf][kl];
+          if (!ext) vis = vis && kk <= qc[nt].tok && qc[nt].tok < kend_s[B][kl];
           if (!vis) p = 0.f;
         }
         s[nt][i] = p * (dp[nt][i] - dsum[nt]);
@@ -553,17 +607,38 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(AttnArgs a) {
     for (int dt = 0; dt < kD / 32; ++dt) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 af = load8(&sm.kt[buf][dt * 32 + col][ks * 16 + 8 * h32]);
+        const lds_t* kb = kt_s + ks * 16 * kRowB;
+        const bf16x8 af = ld_tr(kb + f.tr[dt][0], kb + f.tr[dt][1]);
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) acc[dt][nt] = mfma(af, dsb[nt][ks], acc[dt][nt]);
+        for (int nt = 0; nt < 2; ++nt) mfma_acc(acc[dt][nt], af, dsb[nt][ks]);
       }
     }
-    if (nxt >= 0) stash(buf ^ 1, nxt);
+    if (nxt >= 0)
+      st.stash(sb + kDqK + (1 - B) * kDqTile, sb + kDqV + (1 - B) * kDqTile, kend_s[1 - B],
+               nxt < walk.n_ext_blocks, tid, so);
     __syncthreads();
-    buf ^= 1;
+  };
+
+  int blk = walk.next(0);
+  if (blk >= 0) {
+    const bool ext = blk < walk.n_ext_blocks;
+    st.issue(a, g, ext, blk_k0(blk), tid);
+    st.stash(sb + kDqK, sb + kDqV, kend_s[0], ext, tid, so);
+  }
+  __syncthreads();
+  while (blk >= 0) {
+    int nxt = walk.next(blk + 1);
+    if (nxt >= 0) st.issue(a, g, nxt < walk.n_ext_blocks, blk_k0(nxt), tid);
+    block(Buf<0>(), blk, nxt);
+    blk = nxt;
+    if (blk < 0) break;
+    nxt = walk.next(blk + 1);
+    if (nxt >= 0) st.issue(a, g, nxt < walk.n_ext_blocks, blk_k0(nxt), tid);
+    block(Buf<1>(), blk, nxt);
     blk = nxt;
   }
 
+  acc_fence();
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     if (!qc[nt].valid) continue;
@@ -583,49 +658,53 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(AttnArgs a) {
 // ---------------------------------------------------------------------------
 // Backward, KV-stationary: dK, dV.
 //
-// A workgroup owns 128 keys (32 per wave) of one KV head and walks query
-// steps of 32 tokens x one query head, over every head of the group.
-// External key blocks walk all rows (split into n_chunks contiguous ranges of
-// the (query tile, head) index space); own key blocks walk the rows that can
-// see them: [k0, max kend).
+// A workgroup owns 256 keys of one KV head (64 per wave, as two 32-key column
+// tiles) and walks query steps of 32 tokens x one query head over every head
+// of the group.  The query range of a key block is [0, rows) for external
+// keys and [k0, max kend) for own keys; it is split into chunks of the
+// (query tile, head) index space when the grid needs more workgroups, and each
+// chunk writes an fp32 partial that a fixed-order reduce sums.  K fragments
+// stay in registers; the workgroup's V rows stay in LDS.
 constexpr int kQStep = 32;
-constexpr int kKeysPerWg = 128;
-constexpr int kQTP = kQStep + 8;   // LDS pitch of the transposed [d][query] tiles
+constexpr int kKeysPerWave = 64;
+constexpr int kKeysPerWg = 4 * kKeysPerWave;
+constexpr int kStepTile = kQStep * kRowB;
+constexpr int kDkvV = 0;                                  // V rows of the workgroup
+constexpr int kDkvQ = kKeysPerWg * kRowB;                 // two Q step buffers
+constexpr int kDkvO = kDkvQ + 2 * kStepTile;              // two dO step buffers
+constexpr int kDkvBytes = kDkvO + 2 * kStepTile;
 
-struct DkvSmem {
-  __bf16 q[2][kQStep][kDP];
-  __bf16 dO[2][kQStep][kDP];
-  __bf16 qt[2][kD][kQTP];
-  __bf16 dOt[2][kD][kQTP];
-  float lse2[2][kQStep];
-  float dsum[2][kQStep];
-};
-
-__global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(AttnArgs a) {
-  __shared__ DkvSmem sm;
+__global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[kDkvBytes];
+  __shared__ __attribute__((aligned(16))) float lse_s[2][kQStep];
+  __shared__ __attribute__((aligned(16))) float dsum_s[2][kQStep];
+  lds_t* const sb = (lds_t*)smem;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int col = lane & 31, h32 = lane >> 5;
 
   const int n_ext_kb = (a.n_ext + kKeysPerWg - 1) / kKeysPerWg;
   const int n_own_kb = (a.rows + kKeysPerWg - 1) / kKeysPerWg;
-  const int items = n_ext_kb * a.n_chunks + n_own_kb;   // per KV head
+  const int items = n_ext_kb * a.n_chunks + n_own_kb * a.n_chunks_own;   // per KV head
   int g, item;
   map_block(blockIdx.x, a.hkv, items, g, item);
   if (g >= a.hkv) return;
 
   const bool ext = item < n_ext_kb * a.n_chunks;
-  int kb, chunk = 0;
+  int kb, chunk, nch;
   if (ext) {
     kb = item / a.n_chunks;
     chunk = item - kb * a.n_chunks;
+    nch = a.n_chunks;
   } else {
-    kb = item - n_ext_kb * a.n_chunks;
+    const int oi = item - n_ext_kb * a.n_chunks;
+    kb = oi / a.n_chunks_own;
+    chunk = oi - kb * a.n_chunks_own;
+    nch = a.n_chunks_own;
   }
   const int k0 = kb * kKeysPerWg;
   const int klim = ext ? a.n_ext : a.rows;
-  const int kk = k0 + wave * 32 + col;   // this lane's key
-  const bool kvalid = kk < klim;
+  const int kw0 = k0 + wave * kKeysPerWave;      // this wave's first key
 
   // query range (tokens) and the (tile, head) index range of this workgroup
   int qlo, qhi;
@@ -643,48 +722,79 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(AttnArgs a) {
   const int qt_hi = (qhi > qlo) ? (qhi + kQStep - 1) / kQStep : qt_lo;
   const int n_it = (qt_hi - qt_lo) * a.group;
   int it_lo = 0, it_hi = n_it;
-  if (ext && a.n_chunks > 1) {
-    const int per = (n_it + a.n_chunks - 1) / a.n_chunks;
+  if (nch > 1) {
+    const int per = (n_it + nch - 1) / nch;
     it_lo = min(n_it, chunk * per);
     it_hi = min(n_it, it_lo + per);
   }
 
-  // stationary K^T and V^T fragments (B operands of Q K^T and dO V^T)
-  bf16x8 kf[kD / 16], vf[kD / 16];
+  const uint32_t so = stage_off(tid);
+  // V rows of the workgroup into LDS; K fragments (B operand of Q K^T) of the
+  // wave's two 32-key tiles into registers; visibility bounds of the keys
+  bf16x8 kf[2][kD / 16];
+  int kend_k[2];
+  bool kvalid[2];
+  int wave_qlo = 0x7fffffff, wave_kend_min = 0x7fffffff, wave_kend_max = -1;
   {
     const __bf16* kbase = (const __bf16*)(ext ? a.k_ext : a.k_own);
     const __bf16* vbase = (const __bf16*)(ext ? a.v_ext : a.v_own);
     const int64_t kst = ext ? a.kx_st : a.ko_st, ksh = ext ? a.kx_sh : a.ko_sh;
     const int64_t vst = ext ? a.vx_st : a.vo_st, vsh = ext ? a.vx_sh : a.vo_sh;
-    const __bf16* kp = kbase + (int64_t)kk * kst + (int64_t)g * ksh + 8 * h32;
-    const __bf16* vp = vbase + (int64_t)kk * vst + (int64_t)g * vsh + 8 * h32;
+#pragma unroll 4
+    for (int i = 0; i < kKeysPerWg / 16; ++i) {
+      const int kk = k0 + 16 * i + (tid >> 4);
+      const u32x4 v = kk < klim ? load16(vbase + (int64_t)kk * vst + (int64_t)g * vsh + (tid & 15) * 8)
+                                : zero_u4();
+      st16(sb + kDkvV + so + i * 16 * kRowB, v);
+    }
 #pragma unroll
-    for (int ds = 0; ds < kD / 16; ++ds) {
-      kf[ds] = kvalid ? load8(kp + ds * 16) : zero8();
-      vf[ds] = kvalid ? load8(vp + ds * 16) : zero8();
+    for (int kt = 0; kt < 2; ++kt) {
+      const int kk = kw0 + kt * 32 + col;
+      kvalid[kt] = kk < klim;
+      const __bf16* kp = kbase + (int64_t)kk * kst + (int64_t)g * ksh + 8 * h32;
+#pragma unroll
+      for (int ds = 0; ds < kD / 16; ++ds) kf[kt][ds] = kvalid[kt] ? load8(kp + ds * 16) : zero8();
+      kend_k[kt] = (!ext && kvalid[kt]) ? a.ri.kend[kk] : (ext ? 0x7fffffff : -1);
+      if (kvalid[kt]) {
+        wave_qlo = min(wave_qlo, kk);
+        wave_kend_min = min(wave_kend_min, kend_k[kt]);
+        wave_kend_max = max(wave_kend_max, kend_k[kt]);
+      }
     }
   }
-  const int kend_k = (!ext && kvalid) ? a.ri.kend[kk] : 0;
+  // wave-wide bounds: the wave's keys are read by tokens in [wave_qlo, wave_kend_max)
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    wave_qlo = min(wave_qlo, __shfl_xor(wave_qlo, off));
+    wave_kend_min = min(wave_kend_min, __shfl_xor(wave_kend_min, off));
+    wave_kend_max = max(wave_kend_max, __shfl_xor(wave_kend_max, off));
+  }
+  const int wave_khi = min(kw0 + kKeysPerWave, klim) - 1;   // last valid key of the wave
+
+  Frag f;
+  frag_init(f, lane);
+  uint32_t vrow[kD / 16];   // this wave's V fragments: rows 64 wave + l % 32 (+ 32 per tile)
+#pragma unroll
+  for (int ds = 0; ds < kD / 16; ++ds) vrow[ds] = f.row8[ds] + wave * kKeysPerWave * kRowB;
 
   // staging of one query step: Q and dO rows (32 tokens x 128 d each)
-  uint4 qreg[2], dreg[2];
+  u32x4 qreg[2], dreg[2];
   float lreg = 0.f, dsreg = 0.f;
-  // thread -> token 4 * (tid & 7) + 2 * (tid >> 7) + i, d chunk (tid >> 3) & 15
   auto issue = [&](int it) {
     const int qt = qt_lo + it / a.group;
     const int j = it % a.group;
-    const int head = a.heads.qhead[g * a.group + j];
-    const int dch = (tid >> 3) & 15;
+    const int head = a.ri.qhead[g * a.group + j];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int tok = qt * kQStep + 4 * (tid & 7) + 2 * (tid >> 7) + i;
+      const int tok = qt * kQStep + 16 * i + (tid >> 4);
+      const int ch = tid & 15;
       const bool ok = tok < a.rows;
-      qreg[i] = ok ? *(const uint4*)((const __bf16*)a.q + (int64_t)tok * a.q_st +
-                                     (int64_t)head * a.q_sh + dch * 8)
-                   : make_uint4(0, 0, 0, 0);
-      dreg[i] = ok ? *(const uint4*)((const __bf16*)a.dout + (int64_t)tok * a.do_st +
-                                     (int64_t)head * a.do_sh + dch * 8)
-                   : make_uint4(0, 0, 0, 0);
+      qreg[i] = ok ? load16((const __bf16*)a.q + (int64_t)tok * a.q_st + (int64_t)head * a.q_sh +
+                            ch * 8)
+                   : zero_u4();
+      dreg[i] = ok ? load16((const __bf16*)a.dout + (int64_t)tok * a.do_st +
+                            (int64_t)head * a.do_sh + ch * 8)
+                   : zero_u4();
     }
     if (tid < kQStep) {
       const int tok = qt * kQStep + tid;
@@ -698,120 +808,164 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(AttnArgs a) {
       }
     }
   };
-  auto stash = [&](int buf) {
-    const int kg = tid & 7, half = tid >> 7, dch = (tid >> 3) & 15;
+  auto stash = [&](auto bc) {
+    constexpr int B = decltype(bc)::value;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int t = 4 * kg + 2 * half + i;
-      *(uint4*)&sm.q[buf][t][dch * 8] = qreg[i];
-      *(uint4*)&sm.dO[buf][t][dch * 8] = dreg[i];
-    }
-    const __bf16* q16[2] = {(const __bf16*)&qreg[0], (const __bf16*)&qreg[1]};
-    const __bf16* d16[2] = {(const __bf16*)&dreg[0], (const __bf16*)&dreg[1]};
-    const int o = 4 * kg + 2 * half;
-    const int tpos = (o & ~15) + perm16(o & 15);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      __bf16 w[2] = {q16[0][e], q16[1][e]};
-      __bf16 x[2] = {d16[0][e], d16[1][e]};
-      *(uint32_t*)&sm.qt[buf][dch * 8 + e][tpos] = *(uint32_t*)w;
-      *(uint32_t*)&sm.dOt[buf][dch * 8 + e][tpos] = *(uint32_t*)x;
+      st16(sb + kDkvQ + B * kStepTile + so + i * 16 * kRowB, qreg[i]);
+      st16(sb + kDkvO + B * kStepTile + so + i * 16 * kRowB, dreg[i]);
     }
     if (tid < kQStep) {
-      sm.lse2[buf][tid] = lreg;
-      sm.dsum[buf][tid] = dsreg;
+      lse_s[B][tid] = lreg;
+      dsum_s[B][tid] = dsreg;
     }
   };
 
   const float c = a.scale_log2;
-  f32x16 dk[kD / 32], dv[kD / 32];
+  f32x16 dk[kD / 32][2], dv[kD / 32][2];
 #pragma unroll
-  for (int dt = 0; dt < kD / 32; ++dt) {
-    dk[dt] = zero16();
-    dv[dt] = zero16();
-  }
+  for (int dt = 0; dt < kD / 32; ++dt)
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      dk[dt][kt] = zero16();
+      dv[dt][kt] = zero16();
+    }
+
+  // one query step held in buffer B; stages step it + 1 into the other buffer
+  auto step = [&](auto bc, int it) {
+    constexpr int B = decltype(bc)::value;
+    const bool more = it + 1 < it_hi;
+    if (more) issue(it + 1);
+    const int qt = qt_lo + it / a.group;
+    const int tq0 = qt * kQStep;
+    // skip steps none of the wave's keys is visible to (wave-uniform)
+    const bool live = ext || (tq0 + kQStep - 1 >= wave_qlo && tq0 < wave_kend_max);
+    if (live) {
+      const lds_t* q_s = sb + kDkvQ + B * kStepTile;
+      const lds_t* d_s = sb + kDkvO + B * kStepTile;
+      // S = Q K^T and dP = dO V^T: 32 queries x the wave's 64 keys
+      f32x16 s[2], dp[2];
+      s[0] = zero16(); s[1] = zero16(); dp[0] = zero16(); dp[1] = zero16();
+#pragma unroll
+      for (int ds = 0; ds < kD / 16; ++ds) {
+        const bf16x8 qa = ld_row8(q_s + f.row8[ds]);
+        const bf16x8 da = ld_row8(d_s + f.row8[ds]);
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          const bf16x8 vb = ld_row8(sb + kDkvV + kt * 32 * kRowB + vrow[ds]);
+          s[kt] = mfma(qa, kf[kt][ds], s[kt]);
+          dp[kt] = mfma(da, vb, dp[kt]);
+        }
+      }
+      // P and dS; the C rows are queries 8 (i/4) + 4 h32 + i%4
+      const bool need_mask =
+          !ext && !(tq0 >= wave_khi && tq0 + kQStep - 1 < wave_kend_min);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int qr = 8 * jj + 4 * h32;
+        const f32x4 l4 = *(const f32x4*)&lse_s[B][qr];
+        const f32x4 d4 = *(const f32x4*)&dsum_s[B][qr];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = 4 * jj + r;
+            float p = fast_exp2(fmaf(s[kt][i], c, -l4[r]));
+            if (need_mask) {
+              const int tq = tq0 + qr + r;
+              const int kk = kw0 + kt * 32 + col;
+              if (!(kk <= tq && tq < kend_k[kt])) p = 0.f;
+            }
+            if (!kvalid[kt]) p = 0.f;
+            s[kt][i] = p;
+            dp[kt][i] = p * (dp[kt][i] - d4[r]);
+          }
+      }
+      bf16x8 pb[2][2], db[2][2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        pb[kt][0] = pack_half(s[kt], 0);
+        pb[kt][1] = pack_half(s[kt], 1);
+        db[kt][0] = pack_half(dp[kt], 0);
+        db[kt][1] = pack_half(dp[kt], 1);
+      }
+      // dV^T += dO^T P ; dK^T += Q^T dS
+#pragma unroll
+      for (int dt = 0; dt < kD / 32; ++dt) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const lds_t* ob = d_s + hf * 16 * kRowB;
+          const lds_t* qb = q_s + hf * 16 * kRowB;
+          const bf16x8 oa = ld_tr(ob + f.tr[dt][0], ob + f.tr[dt][1]);
+          const bf16x8 qa = ld_tr(qb + f.tr[dt][0], qb + f.tr[dt][1]);
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt) {
+            mfma_acc(dv[dt][kt], oa, pb[kt][hf]);
+            mfma_acc(dk[dt][kt], qa, db[kt][hf]);
+          }
+        }
+      }
+    }
+    if (more) stash(Buf<1 - B>());
+    __syncthreads();
+  };
 
   if (it_lo < it_hi) {
     issue(it_lo);
-    stash(0);
+    stash(Buf<0>());
   }
   __syncthreads();
-  int buf = 0;
-  for (int it = it_lo; it < it_hi; ++it) {
-    if (it + 1 < it_hi) issue(it + 1);
-    const int qt = qt_lo + it / a.group;
-    const int tq0 = qt * kQStep;
-
-    // S = Q K^T and dP = dO V^T: 32 queries x this wave's 32 keys
-    f32x16 s = zero16(), dp = zero16();
-#pragma unroll
-    for (int ds = 0; ds < kD / 16; ++ds) {
-      const bf16x8 qa = load8(&sm.q[buf][col][ds * 16 + 8 * h32]);
-      const bf16x8 da = load8(&sm.dO[buf][col][ds * 16 + 8 * h32]);
-      s = mfma(qa, kf[ds], s);
-      dp = mfma(da, vf[ds], dp);
-    }
-    // P and dS; the C rows are queries 8 (i/4) + 4 h32 + i%4
-    const bool need_mask = !ext && !(tq0 + kQStep - 1 < kend_k && tq0 >= k0 + kKeysPerWg);
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int qr = 8 * jj + 4 * h32;
-      const f32x4 l4 = *(const f32x4*)&sm.lse2[buf][qr];
-      const f32x4 d4 = *(const f32x4*)&sm.dsum[buf][qr];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 4 * jj + r;
-        float p = fast_exp2(fmaf(s[i], c, -l4[r]));
-        if (need_mask) {
-          const int tq = tq0 + qr + r;
-          if (!(kk <= tq && tq < kend_k)) p = 0.f;
-        }
-        if (!kvalid) p = 0.f;
-        s[i] = p;
-        dp[i] = p * (dp[i] - d4[r]);
-      }
-    }
-    const bf16x8 pb0 = pack_half(s, 0), pb1 = pack_half(s, 1);
-    const bf16x8 db0 = pack_half(dp, 0), db1 = pack_half(dp, 1);
-    // dV^T += dO^T P ; dK^T += Q^T dS
-#pragma unroll
-    for (int dt = 0; dt < kD / 32; ++dt) {
-      const bf16x8 oa0 = load8(&sm.dOt[buf][dt * 32 + col][8 * h32]);
-      const bf16x8 oa1 = load8(&sm.dOt[buf][dt * 32 + col][16 + 8 * h32]);
-      const bf16x8 qa0 = load8(&sm.qt[buf][dt * 32 + col][8 * h32]);
-      const bf16x8 qa1 = load8(&sm.qt[buf][dt * 32 + col][16 + 8 * h32]);
-      dv[dt] = mfma(oa0, pb0, dv[dt]);
-      dv[dt] = mfma(oa1, pb1, dv[dt]);
-      dk[dt] = mfma(qa0, db0, dk[dt]);
-      dk[dt] = mfma(qa1, db1, dk[dt]);
-    }
-    if (it + 1 < it_hi) stash(buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
+  for (int it = it_lo; it < it_hi; it += 2) {
+    step(Buf<0>(), it);
+    if (it + 1 < it_hi) step(Buf<1>(), it + 1);
   }
 
-  if (!kvalid) return;
-  // lane holds key kk, d = 32 dt + 8 j + 4 h32 + r
-  if (ext) {
+  // lane holds key kw0 + 32 kt + col, d = 32 dt + 8 j + 4 h32 + r
+  acc_fence();
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    if (!kvalid[kt]) continue;
+    const int kk = kw0 + kt * 32 + col;
     const int64_t base = ((int64_t)kk * a.hkv + g) * kD;
-    if (a.n_chunks == 1) {
+    if (ext) {
+      if (nch == 1) {
 #pragma unroll
-      for (int dt = 0; dt < kD / 32; ++dt)
+        for (int dt = 0; dt < kD / 32; ++dt)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int d = dt * 32 + 8 * j + 4 * h32;
-          f32x4 gk = *(f32x4*)(a.gk_acc + base + d);
-          f32x4 gv = *(f32x4*)(a.gv_acc + base + d);
+          for (int j = 0; j < 4; ++j) {
+            const int d = dt * 32 + 8 * j + 4 * h32;
+            f32x4 gk = *(f32x4*)(a.gk_acc + base + d);
+            f32x4 gv = *(f32x4*)(a.gv_acc + base + d);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            gk[r] += dk[dt][4 * j + r] * a.scale;
-            gv[r] += dv[dt][4 * j + r];
+            for (int r = 0; r < 4; ++r) {
+              gk[r] += dk[dt][kt][4 * j + r] * a.scale;
+              gv[r] += dv[dt][kt][4 * j + r];
+            }
+            *(f32x4*)(a.gk_acc + base + d) = gk;
+            *(f32x4*)(a.gv_acc + base + d) = gv;
           }
-          *(f32x4*)(a.gk_acc + base + d) = gk;
-          *(f32x4*)(a.gv_acc + base + d) = gv;
-        }
-    } else {
-      const int64_t pbase = (int64_t)chunk * a.n_ext * a.hkv * kD + base;
+      } else {
+        const int64_t pbase = (int64_t)chunk * a.n_ext * a.hkv * kD + base;
+#pragma unroll
+        for (int dt = 0; dt < kD / 32; ++dt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int d = dt * 32 + 8 * j + 4 * h32;
+            f32x4 gk, gv;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              gk[r] = dk[dt][kt][4 * j + r] * a.scale;
+              gv[r] = dv[dt][kt][4 * j + r];
+            }
+            *(f32x4*)(a.gk_part + pbase + d) = gk;
+            *(f32x4*)(a.gv_part + pbase + d) = gv;
+          }
+      }
+      continue;
+    }
+    if (nch > 1) {
+      // own keys split over query chunks: fp32 partials, finished by a reduce
+      const int64_t pbase = (int64_t)chunk * a.rows * a.hkv * kD + base;
 #pragma unroll
       for (int dt = 0; dt < kD / 32; ++dt)
 #pragma unroll
@@ -820,49 +974,48 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(AttnArgs a) {
           f32x4 gk, gv;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            gk[r] = dk[dt][4 * j + r] * a.scale;
-            gv[r] = dv[dt][4 * j + r];
+            gk[r] = dk[dt][kt][4 * j + r] * a.scale;
+            gv[r] = dv[dt][kt][4 * j + r];
           }
-          *(f32x4*)(a.gk_part + pbase + d) = gk;
-          *(f32x4*)(a.gv_part + pbase + d) = gv;
+          *(f32x4*)(a.dk_part + pbase + d) = gk;
+          *(f32x4*)(a.dv_part + pbase + d) = gv;
         }
+      continue;
     }
-    return;
-  }
-  const int64_t ibase = ((int64_t)kk * a.hkv + g) * kD;
 #pragma unroll
-  for (int dt = 0; dt < kD / 32; ++dt)
+    for (int dt = 0; dt < kD / 32; ++dt)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int d = dt * 32 + 8 * j + 4 * h32;
-      f32x4 vk, vv;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        vk[r] = dk[dt][4 * j + r] * a.scale;
-        vv[r] = dv[dt][4 * j + r];
-      }
-      if (a.gk_init) {
-        const f32x4 ik = *(const f32x4*)(a.gk_init + ibase + d);
-        const f32x4 iv = *(const f32x4*)(a.gv_init + ibase + d);
-        vk += ik;
-        vv += iv;
-      }
-      const int64_t ko = (int64_t)kk * a.dko_st + (int64_t)g * a.dko_sh + d;
-      const int64_t vo = (int64_t)kk * a.dvo_st + (int64_t)g * a.dvo_sh + d;
-      if (a.dkv_f32) {
-        *(f32x4*)((float*)a.dk_own + ko) = vk;
-        *(f32x4*)((float*)a.dv_own + vo) = vv;
-      } else {
-        bf16x4 wk, wv;
+      for (int j = 0; j < 4; ++j) {
+        const int d = dt * 32 + 8 * j + 4 * h32;
+        f32x4 vk, vv;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          wk[r] = (__bf16)vk[r];
-          wv[r] = (__bf16)vv[r];
+          vk[r] = dk[dt][kt][4 * j + r] * a.scale;
+          vv[r] = dv[dt][kt][4 * j + r];
         }
-        *(bf16x4*)((__bf16*)a.dk_own + ko) = wk;
-        *(bf16x4*)((__bf16*)a.dv_own + vo) = wv;
+        if (a.gk_init) {
+          const f32x4 ik = *(const f32x4*)(a.gk_init + base + d);
+          const f32x4 iv = *(const f32x4*)(a.gv_init + base + d);
+          vk += ik;
+          vv += iv;
+        }
+        const int64_t ko = (int64_t)kk * a.dko_st + (int64_t)g * a.dko_sh + d;
+        const int64_t vo = (int64_t)kk * a.dvo_st + (int64_t)g * a.dvo_sh + d;
+        if (a.dkv_f32) {
+          *(f32x4*)((float*)a.dk_own + ko) = vk;
+          *(f32x4*)((float*)a.dv_own + vo) = vv;
+        } else {
+          bf16x4 wk, wv;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            wk[r] = (__bf16)vk[r];
+            wv[r] = (__bf16)vv[r];
+          }
+          *(bf16x4*)((__bf16*)a.dk_own + ko) = wk;
+          *(bf16x4*)((__bf16*)a.dv_own + vo) = wv;
+        }
       }
-    }
+  }
 }
 
 // grid size: per-KV-head items, padded so the XCD mapping covers every item
@@ -878,7 +1031,7 @@ hipError_t launch_fwd_bf16(const AttnArgs& a, int32_t head_dim, hipStream_t stre
   if (a.rows <= 0) return hipSuccess;
   const int tq = kRowsPerWg / a.group;
   const int n_qt = (a.rows + tq - 1) / tq;
-  PF_LAUNCH("pf_fwd_bf16", fwd_kernel<64>, dim3(grid_for(a.hkv, n_qt)), dim3(kThreads), stream, a);
+  PF_LAUNCH("pf_fwd_bf16", fwd_kernel, dim3(grid_for(a.hkv, n_qt)), dim3(kThreads), stream, a);
   return hipGetLastError();
 }
 
@@ -887,7 +1040,7 @@ hipError_t launch_bwd_dq_bf16(const AttnArgs& a, int32_t head_dim, hipStream_t s
   if (a.rows <= 0) return hipSuccess;
   const int tq = kRowsPerWg / a.group;
   const int n_qt = (a.rows + tq - 1) / tq;
-  PF_LAUNCH("pf_bwd_dq_bf16", bwd_dq_kernel<32>, dim3(grid_for(a.hkv, n_qt)), dim3(kThreads),
+  PF_LAUNCH("pf_bwd_dq_bf16", bwd_dq_kernel, dim3(grid_for(a.hkv, n_qt)), dim3(kThreads),
             stream, a);
   return hipGetLastError();
 }
@@ -896,10 +1049,13 @@ hipError_t launch_bwd_dkv_bf16(const AttnArgs& a, int32_t head_dim, hipStream_t 
   if (head_dim != kD) return hipErrorInvalidValue;
   const int n_ext_kb = (a.n_ext + kKeysPerWg - 1) / kKeysPerWg;
   const int n_own_kb = (a.rows + kKeysPerWg - 1) / kKeysPerWg;
-  const int items = n_ext_kb * a.n_chunks + n_own_kb;
+  const int items = n_ext_kb * a.n_chunks + n_own_kb * a.n_chunks_own;
   if (items <= 0) return hipSuccess;
-  PF_LAUNCH("pf_bwd_dkv_bf16", bwd_dkv_kernel, dim3(grid_for(a.hkv, items)), dim3(kThreads), stream, a);
+  PF_LAUNCH("pf_bwd_dkv_bf16", bwd_dkv_kernel, dim3(grid_for(a.hkv, items)), dim3(kThreads),
+            stream, a);
   return hipGetLastError();
 }
+
+int32_t dkv_keys_per_workgroup_bf16() { return kKeysPerWg; }
 
 }  // namespace pf

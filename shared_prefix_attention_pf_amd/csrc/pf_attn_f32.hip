@@ -29,7 +29,7 @@ __global__ __launch_bounds__(kT) void fwd_f32_kernel(AttnArgs a) {
   // KV head of this query head: position of `head` in the grouped table
   int kvh = 0;
   for (int i = 0; i < a.hq; ++i)
-    if (a.heads.qhead[i] == head) kvh = i / a.group;
+    if (a.ri.qhead[i] == head) kvh = i / a.group;
   const int t0 = blockIdx.x * kT;
   const int tok = t0 + threadIdx.x;
   const bool valid = tok < a.rows;
@@ -96,7 +96,7 @@ __global__ __launch_bounds__(kT) void dq_f32_kernel(AttnArgs a) {
   const int head = blockIdx.y;
   int kvh = 0;
   for (int i = 0; i < a.hq; ++i)
-    if (a.heads.qhead[i] == head) kvh = i / a.group;
+    if (a.ri.qhead[i] == head) kvh = i / a.group;
   const int t0 = blockIdx.x * kT;
   const int tok = t0 + threadIdx.x;
   const bool valid = tok < a.rows;
@@ -198,7 +198,7 @@ __global__ __launch_bounds__(kT) void dkv_f32_kernel(AttnArgs a) {
     qhi = min(m, a.rows);
   }
   for (int j = 0; j < a.group; ++j) {
-    const int head = a.heads.qhead[g * a.group + j];
+    const int head = a.ri.qhead[g * a.group + j];
     for (int t0 = qlo; t0 < qhi; t0 += kT) {
       __syncthreads();
       for (int e = threadIdx.x; e < kT * D; e += kT) {

@@ -37,16 +37,19 @@ struct SegTable {
   int32_t vis_end[PF_MAX_SEGMENTS];
 };
 
-// Per-row visibility data in the workspace.
+// Per-row visibility data and the head table, in the workspace.
 struct RowInfo {
   int32_t* kend;      // [rows]
   int32_t* bmax;      // [ceil(rows/32)]: max kend over each 32-key block
   int32_t* bmin;      // [ceil(rows/32)]: min kend over the valid keys of the block
+  int32_t* qhead;     // [Hq]: qhead[g * G + j] is the j-th query head of KV head g
 };
 
-// Query heads grouped by the KV head they read: qhead[g * G + j] is the j-th
-// query head of KV head g.
+// Query heads grouped by the KV head they read (host side; the prep kernel
+// copies it into RowInfo::qhead so attention kernels index device memory,
+// not their argument block).
 struct HeadTable {
+  int32_t n;
   int16_t qhead[PF_MAX_HEADS];
 };
 
@@ -76,12 +79,15 @@ struct AttnArgs {
   float* gk_acc; float* gv_acc;           // accumulators (RMW when n_chunks == 1)
   float* gk_part; float* gv_part;         // partials [n_chunks, n_ext, Hkv, d]
   int32_t n_chunks;                       // query chunks per external key block
+  // own-key gradient partials when own key blocks are split over query
+  // chunks: fp32 [n_chunks_own, rows, Hkv, d], finished by launch_finish_own
+  float* dk_part; float* dv_part;
+  int32_t n_chunks_own;
   RowInfo ri;
   int32_t rows;
   int32_t hq, hkv, group;                 // group = Hq / Hkv
   float scale;                            // softmax scale
   float scale_log2;                       // scale * log2(e)
-  HeadTable heads;
 };
 
 // Calls the caller's launch hook (if any) around one kernel launch.
@@ -95,11 +101,14 @@ void launch_hook(const char* kernel, hipStream_t stream, int end);
   } while (0)
 
 // Launchers (return hipSuccess or the launch error).
-hipError_t launch_prep(const SegTable& seg, RowInfo ri, hipStream_t stream);
+hipError_t launch_prep(const SegTable& seg, const HeadTable& heads, RowInfo ri, hipStream_t stream);
 hipError_t launch_reduce_partials(const float* part, float* acc, int32_t n_chunks, int64_t n,
                                   hipStream_t stream);
 hipError_t launch_fill_zero(void* dst, int64_t rows, int32_t heads, int32_t d, int64_t st,
                             int64_t sh, int32_t elem_bytes, hipStream_t stream);
+hipError_t launch_finish_own(const float* part, int32_t n_chunks, const float* init, void* dst,
+                             int64_t rows, int32_t heads, int32_t d, int64_t st, int64_t sh,
+                             int32_t dst_f32, hipStream_t stream);
 hipError_t launch_convert_acc(const float* src, void* dst, int64_t rows, int32_t heads, int32_t d,
                               int64_t st, int64_t sh, int32_t dst_f32, hipStream_t stream);
 
@@ -112,9 +121,13 @@ hipError_t launch_bwd_dq_f32(const AttnArgs& a, int32_t head_dim, hipStream_t st
 hipError_t launch_bwd_dkv_f32(const AttnArgs& a, int32_t head_dim, hipStream_t stream);
 
 // Number of query chunks the KV-stationary backward splits the external
-// (prefix) keys into.  A function of the shapes only, so results do not
-// depend on the device.
+// (prefix) key blocks and the own key blocks into.  Functions of the shapes
+// only, so results do not depend on the device.
 int32_t ext_chunks(int32_t n_ext, int32_t rows, int32_t hq, int32_t hkv, int32_t head_dim,
                    int32_t dtype);
+int32_t own_chunks(int32_t op, int32_t rows, int32_t hq, int32_t hkv, int32_t head_dim,
+                   int32_t dtype);
+// keys per workgroup of the bf16 KV-stationary kernel
+int32_t dkv_keys_per_workgroup_bf16();
 
 }  // namespace pf

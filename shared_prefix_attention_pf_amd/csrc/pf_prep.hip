@@ -4,14 +4,17 @@
 //     pairwise order (contention-free and run-to-run deterministic; this is
 //     the per-suffix accumulation of PrefixFlow §3.1 "Savings over the
 //     baseline", an element-wise O(|P| d) add);
+//   - own-key finish: dK/dV of own keys = init + sum of per-chunk partials,
+//     in the same fixed order, converted to the output dtype;
 //   - zero fill and fp32 -> output conversion for Phase C with no upstream.
 #include "pf_internal.h"
 
 namespace pf {
 
-__global__ __launch_bounds__(256) void prep_kernel(SegTable seg, RowInfo ri) {
+__global__ __launch_bounds__(256) void prep_kernel(SegTable seg, HeadTable heads, RowInfo ri) {
   const int rows = seg.start[seg.n];
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t < heads.n) ri.qhead[t] = heads.qhead[t];
   int kend = -1;          // rows past the end: ignored by both summaries
   if (t < rows) {
     // segment of row t: the last i with start[i] <= t (empty segments skipped)
@@ -37,11 +40,12 @@ __global__ __launch_bounds__(256) void prep_kernel(SegTable seg, RowInfo ri) {
   }
 }
 
-hipError_t launch_prep(const SegTable& seg, RowInfo ri, hipStream_t stream) {
+hipError_t launch_prep(const SegTable& seg, const HeadTable& heads, RowInfo ri,
+                       hipStream_t stream) {
   const int rows = seg.start[seg.n];
   if (rows <= 0) return hipSuccess;
-  const int blocks = (rows + 255) / 256;
-  PF_LAUNCH("pf_prep", prep_kernel, dim3(blocks), dim3(256), stream, seg, ri);
+  const int blocks = (max(rows, heads.n) + 255) / 256;
+  PF_LAUNCH("pf_prep", prep_kernel, dim3(blocks), dim3(256), stream, seg, heads, ri);
   return hipGetLastError();
 }
 
@@ -83,6 +87,52 @@ hipError_t launch_reduce_partials(const float* part, float* acc, int32_t n_chunk
   int64_t blocks = (n4 + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   PF_LAUNCH("pf_reduce", reduce_partials_kernel, dim3((unsigned)blocks), dim3(256), stream, (const float4*)part, (float4*)acc, (int)n_chunks, n4);
+  return hipGetLastError();
+}
+
+// dst[r, h, :] = convert(init[r, h, :] + sum_c part[c, r, h, :]); part and
+// init are contiguous [rows, heads, d] fp32, dst is strided.
+__global__ __launch_bounds__(256) void finish_own_kernel(const float4* __restrict__ part, int nc,
+                                                         const float4* __restrict__ init,
+                                                         char* dst, int64_t rows, int heads,
+                                                         int d, int64_t st, int64_t sh,
+                                                         int dst_f32) {
+  const int per = d / 4;
+  const int64_t n4 = rows * heads * per;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+    float4 v;
+    if (nc <= 2) v = tree_sum<2>(part, n4, i, nc);
+    else if (nc <= 4) v = tree_sum<4>(part, n4, i, nc);
+    else v = tree_sum<8>(part, n4, i, nc);
+    if (init) {
+      const float4 w = init[i];
+      v.x = w.x + v.x; v.y = w.y + v.y; v.z = w.z + v.z; v.w = w.w + v.w;
+    }
+    const int c = (int)(i % per);
+    const int64_t rh = i / per;
+    const int h = (int)(rh % heads);
+    const int64_t r = rh / heads;
+    const int64_t off = r * st + (int64_t)h * sh + c * 4;   // elements
+    if (dst_f32) {
+      *(float4*)((float*)dst + off) = v;
+    } else {
+      __bf16* o = (__bf16*)dst + off;
+      o[0] = (__bf16)v.x; o[1] = (__bf16)v.y; o[2] = (__bf16)v.z; o[3] = (__bf16)v.w;
+    }
+  }
+}
+
+hipError_t launch_finish_own(const float* part, int32_t n_chunks, const float* init, void* dst,
+                             int64_t rows, int32_t heads, int32_t d, int64_t st, int64_t sh,
+                             int32_t dst_f32, hipStream_t stream) {
+  if (rows <= 0) return hipSuccess;
+  const int64_t total = rows * heads * (d / 4);
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  PF_LAUNCH("pf_finish_own", finish_own_kernel, dim3((unsigned)blocks), dim3(256), stream,
+            (const float4*)part, (int)n_chunks, (const float4*)init, (char*)dst, rows, (int)heads,
+            (int)d, st, sh, (int)dst_f32);
   return hipGetLastError();
 }
 
