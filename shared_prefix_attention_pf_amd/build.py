@@ -40,9 +40,30 @@ def common_flags():
     ]
 
 
+def check_wait_states(cc: str, tmp: str, verbose: bool = False) -> None:
+    """Generate the gfx950 assembly of the bf16 kernels and check that no
+    instruction touches an inline-asm MFMA's destination within its latency
+    (see asm_check.py).  Raises on a violation."""
+    sys.path.insert(0, PKG)
+    import asm_check  # noqa: E402  (module beside this file)
+    src = os.path.join(CSRC, "pf_attn_bf16.hip")
+    asm = os.path.join(tmp, "pf_attn_bf16.s")
+    cmd = [cc] + common_flags() + ["--cuda-device-only", "-S", src, "-o", asm]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    with open(asm) as fh:
+        bad = asm_check.check(fh.readlines())
+    if bad:
+        for no, msg in bad[:20]:
+            print(f"pf_attn_bf16.s:{no}: {msg}", file=sys.stderr)
+        raise RuntimeError(f"{len(bad)} MFMA wait-state violation(s) in the bf16 kernels")
+
+
 def build(verbose: bool = False, resource_usage: bool = False) -> str:
     cc = hipcc()
     with tempfile.TemporaryDirectory(prefix="pf_build_") as tmp:
+        check_wait_states(cc, tmp, verbose)
         objs = []
         for src in SOURCES:
             obj = os.path.join(tmp, src + ".o")

@@ -67,15 +67,39 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
 // Accumulating product with the accumulator held in AGPRs (acc += A B).  The
 // compiler keeps MFMA results it feeds to VALU code in VGPRs; the long-lived
 // accumulators of the PV, dQ and dK/dV products go to the AGPR file through
-// this form so the two files together hold a wave's working set.  Back-to-back
-// accumulation into the same registers needs no wait states; VALU reads of an
-// accumulator after its last product are separated by acc_fence().
+// this form so the two files together hold a wave's working set.
+// The compiler inserts wait states around builtin MFMAs but not around asm:
+//   - operands written by VALU code (packed P or dS fragments, fragments
+//     assembled from two transposing reads) need 2 wait states before an
+//     MFMA reads them; every asm product carries them itself (s_nop 1);
+//   - back-to-back accumulation into the same registers needs none;
+//   - accumulators pass through fence_acc() between the last product and
+//     VALU reads of them, and between VALU writes (rescaling) and the next
+//     product;
+//   - nothing else may touch an accumulator within a product's latency.  The
+//     compiler only moves AGPR values when it runs short of registers, so
+//     the kernels stay below the register files' size, and the build checks
+//     the generated assembly for any such access (asm_check.py).
 __device__ __forceinline__ void mfma_acc(f32x16& acc, bf16x8 a, bf16x8 b) {
-  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
-// wait states between the last accumulating product and VALU reads of it
-__device__ __forceinline__ void acc_fence() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+__device__ __forceinline__ void fence_acc(f32x16 (&x)[4][2]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+               : "+a"(x[0][0]), "+a"(x[0][1]), "+a"(x[1][0]), "+a"(x[1][1]), "+a"(x[2][0]),
+                 "+a"(x[2][1]), "+a"(x[3][0]), "+a"(x[3][1]));
+}
+
+__device__ __forceinline__ void fence_acc(f32x16 (&x)[4][2], f32x16 (&y)[4][2]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+               : "+a"(x[0][0]), "+a"(x[0][1]), "+a"(x[1][0]), "+a"(x[1][1]), "+a"(x[2][0]),
+                 "+a"(x[2][1]), "+a"(x[3][0]), "+a"(x[3][1]), "+a"(y[0][0]), "+a"(y[0][1]),
+                 "+a"(y[1][0]), "+a"(y[1][1]), "+a"(y[2][0]), "+a"(y[2][1]), "+a"(y[3][0]),
+                 "+a"(y[3][1]));
+}
+
+// keep a stationary fragment in the AGPR file; MFMAs read it from there
+__device__ __forceinline__ void pin_agpr(bf16x8& x) { asm("" : "+a"(x)); }
 
 __device__ __forceinline__ f32x16 zero16() {
   f32x16 z;
@@ -145,6 +169,24 @@ __device__ __forceinline__ void frag_init(Frag& f, int lane) {
   }
 }
 
+// The same offsets derived from three registers: row8[ds] = row8[0] ^ 32 ds
+// and tr[dt][hi] = tr[0][hi] ^ 64 dt, because the terms differ only in chunk
+// bits that the swizzle XORs.  fresh() hides the bases from loop-invariant
+// hoisting, so a kernel short of registers recomputes each offset with one
+// XOR instead of holding sixteen.
+struct FragC {
+  uint32_t row8_0;
+  uint32_t tr0[2];
+  __device__ void init(const Frag& f) {
+    row8_0 = f.row8[0];
+    tr0[0] = f.tr[0][0];
+    tr0[1] = f.tr[0][1];
+  }
+  __device__ void fresh() { asm volatile("" : "+v"(row8_0), "+v"(tr0[0]), "+v"(tr0[1])); }
+  __device__ uint32_t row8(int ds) const { return row8_0 ^ (uint32_t)(ds << 5); }
+  __device__ uint32_t tr(int dt, int hi) const { return tr0[hi] ^ (uint32_t)(dt << 6); }
+};
+
 __device__ __forceinline__ bf16x8 ld_row8(const lds_t* p) { return *(const lds_bf16x8*)p; }
 
 __device__ __forceinline__ bf16x8 ld_tr(const lds_t* lo, const lds_t* hi) {
@@ -158,11 +200,52 @@ __device__ __forceinline__ void st16(lds_t* p, u32x4 v) { *(lds_u32x4*)p = v; }
 __device__ __forceinline__ u32x4 load16(const __bf16* p) { return *(const u32x4*)p; }
 __device__ __forceinline__ u32x4 zero_u4() { return u32x4{0u, 0u, 0u, 0u}; }
 
-// Staging offset of thread t: chunk (t & 15) of row t / 16 (+ 16 rows =
-// + 4096 B per further pass of 256 threads).
-__device__ __forceinline__ uint32_t stage_off(int t) { return toff(t >> 4, (t & 15) * 8); }
 
 template <int B> using Buf = std::integral_constant<int, B>;
+
+// f(integral_constant<I>) for I in [I0, N): loop indices that must be
+// compile-time constants (asm operand selection)
+template <int I0, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I0 < N) {
+    f(std::integral_constant<int, I0>());
+    static_for<I0 + 1, N>(f);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Direct global -> LDS staging (buffer loads with the LDS destination).  A
+// buffer resource covers one block of rows; reads past its end return zero,
+// so ragged tails need no masking of the load.  Each wave moves four 256-byte
+// rows per instruction, lane l landing at byte 16 l of them: lane l of wave w
+// fetches the logical chunk (l & 15) ^ swz(r) of row r = 4 w + l / 16 (plus 16
+// rows per further pass), which puts every chunk at its swizzled position.
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, int nvalid,
+                                                           uint32_t st_b) {
+  const uint32_t bytes = nvalid > 0 ? (uint32_t)(nvalid - 1) * st_b + kRowB : 0u;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ uint32_t dma_lane_off(int wave, int lane, uint32_t st_b) {
+  const int r = 4 * wave + (lane >> 4);
+  return (uint32_t)r * st_b + ((((uint32_t)lane & 15) ^ swz(r)) << 4);
+}
+
+// ROWS rows (a multiple of 16) into `tile`, issued by every wave of the group
+template <int ROWS>
+__device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t res, uint32_t lane_off,
+                                         uint32_t st_b, lds_t* tile, int wave) {
+#pragma unroll
+  for (int i = 0; i < ROWS / 16; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(res, (lds_void*)(tile + (16 * i + 4 * wave) * kRowB),
+                                             16, lane_off, i * 16 * st_b, 0, 0);
+}
+
+// completes this wave's staging loads (a barrier then publishes them)
+__device__ __forceinline__ void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Workgroup -> (KV head, item) with XCD awareness: workgroups are dispatched
 // round-robin over the 8 XCDs, so when Hkv is a multiple of 8 every XCD gets
@@ -249,45 +332,75 @@ struct KeyWalk {
   }
 };
 
-// Key/value block staging for the Q-stationary kernels: BN rows of K and V
-// (128 bf16 each) from global memory through registers into swizzled LDS.
+// The key blocks a Q-stationary tile visits, in order (see KeyWalk), with the
+// uniform addresses of their K and V rows.
 template <int BN>
-struct KvStage {
-  static constexpr int kPer = BN * 16 / kThreads;   // 16-byte chunks per thread per tensor
-  u32x4 kreg[kPer], vreg[kPer];
-  int kendreg;
-
-  __device__ void issue(const AttnArgs& a, int g, bool ext, int k0, int tid) {
-    const int klim = ext ? a.n_ext : a.rows;
-    const __bf16* kb = (const __bf16*)(ext ? a.k_ext : a.k_own);
-    const __bf16* vb = (const __bf16*)(ext ? a.v_ext : a.v_own);
-    const int64_t kst = ext ? a.kx_st : a.ko_st, ksh = ext ? a.kx_sh : a.ko_sh;
-    const int64_t vst = ext ? a.vx_st : a.vo_st, vsh = ext ? a.vx_sh : a.vo_sh;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int c = tid + kThreads * i;
-      const int kk = k0 + (c >> 4), ch = c & 15;
-      const bool ok = kk < klim;
-      kreg[i] = ok ? load16(kb + (int64_t)kk * kst + (int64_t)g * ksh + ch * 8) : zero_u4();
-      vreg[i] = ok ? load16(vb + (int64_t)kk * vst + (int64_t)g * vsh + ch * 8) : zero_u4();
-    }
-    if (!ext && tid < BN) {
-      const int kk = k0 + tid;
-      kendreg = (kk < a.rows) ? a.ri.kend[kk] : -1;
-    }
+struct BlockSrc {
+  const AttnArgs* a;
+  int g;
+  int n_ext_blocks;
+  __device__ bool ext(int b) const { return b < n_ext_blocks; }
+  __device__ int k0(int b) const { return (ext(b) ? b : b - n_ext_blocks) * BN; }
+  __device__ int nvalid(int b) const { return (ext(b) ? a->n_ext : a->rows) - k0(b); }
+  __device__ const __bf16* kbase(int b) const {
+    return ext(b) ? (const __bf16*)a->k_ext + (int64_t)k0(b) * a->kx_st + (int64_t)g * a->kx_sh
+                  : (const __bf16*)a->k_own + (int64_t)k0(b) * a->ko_st + (int64_t)g * a->ko_sh;
   }
-  __device__ void stash(lds_t* kt, lds_t* vt, int32_t* kend, bool ext, int tid, uint32_t so) {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      st16(kt + so + i * 16 * kRowB, kreg[i]);
-      st16(vt + so + i * 16 * kRowB, vreg[i]);
-    }
-    if (!ext && tid < BN) kend[tid] = kendreg;
+  __device__ const __bf16* vbase(int b) const {
+    return ext(b) ? (const __bf16*)a->v_ext + (int64_t)k0(b) * a->vx_st + (int64_t)g * a->vx_sh
+                  : (const __bf16*)a->v_own + (int64_t)k0(b) * a->vo_st + (int64_t)g * a->vo_sh;
+  }
+  __device__ int64_t kst(int b) const { return ext(b) ? a->kx_st : a->ko_st; }
+  __device__ int64_t vst(int b) const { return ext(b) ? a->vx_st : a->vo_st; }
+  // stage the K or V rows of block b into an LDS tile (rows past the end read 0)
+  __device__ void dma_k(int b, lds_t* tile, int wave, int lane) const {
+    const uint32_t st_b = 2u * (uint32_t)kst(b);
+    dma_rows<BN>(row_rsrc(kbase(b), nvalid(b), st_b), dma_lane_off(wave, lane, st_b), st_b, tile,
+                 wave);
+  }
+  __device__ void dma_v(int b, lds_t* tile, int wave, int lane) const {
+    const uint32_t st_b = 2u * (uint32_t)vst(b);
+    dma_rows<BN>(row_rsrc(vbase(b), nvalid(b), st_b), dma_lane_off(wave, lane, st_b), st_b, tile,
+                 wave);
   }
 };
 
+// kend of the own keys of block b (thread tid < BN holds key k0 + tid)
+template <int BN>
+__device__ __forceinline__ int load_kend(const AttnArgs& a, const BlockSrc<BN>& src, int b, int tid) {
+  if (src.ext(b) || tid >= BN) return -1;
+  const int kk = src.k0(b) + tid;
+  return kk < a.rows ? a.ri.kend[kk] : -1;
+}
+
+// Mask of an S^T tile set (BN keys x two query columns, C layout: rows are
+// keys): invisible entries become -inf.  Branch-free per element.
+template <int BN>
+__device__ __forceinline__ void mask_st(f32x16 (&s)[BN / 32][2], bool ext, int k0, int klim,
+                                        const int32_t* kend, int tok0, int tok1, int h32) {
+#pragma unroll
+  for (int kt = 0; kt < BN / 32; ++kt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int kl = kt * 32 + 8 * (i >> 2) + 4 * h32 + (i & 3);
+      const int kk = k0 + kl;
+      const int ke = ext ? 0x7fffffff : kend[kl];
+      const bool in = kk < klim;
+      const bool v0 = in && (ext || (kk <= tok0 && tok0 < ke));
+      const bool v1 = in && (ext || (kk <= tok1 && tok1 < ke));
+      s[kt][0][i] = v0 ? s[kt][0][i] : -INFINITY;
+      s[kt][1][i] = v1 ? s[kt][1][i] : -INFINITY;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Forward.
+//
+// Software-pipelined over key blocks: while the softmax of block j runs on
+// the VALU, the MFMAs compute S^T of block j + 1; then O^T += V_j^T P_j^T.
+// K runs one block ahead of V, so K blocks j + 2 and V blocks j + 1 are staged
+// during iteration j into the buffers freed by iteration j - 1, with one
+// barrier per block.
 constexpr int kFwdBN = 64;
 constexpr int kFwdTile = kFwdBN * kRowB;            // one K or V block
 constexpr int kFwdK = 0, kFwdV = 2 * kFwdTile;      // two K buffers, then two V buffers
@@ -298,7 +411,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(AttnArgs a) {
   __shared__ int32_t kend_s[2][BN];
   lds_t* const sb = (lds_t*)smem;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int col = lane & 31, h32 = lane >> 5;
   const int tq = kRowsPerWg / a.group;
   const int n_qt = (a.rows + tq - 1) / tq;
@@ -310,7 +423,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(AttnArgs a) {
   const int t0 = qt * tq;
   const int t1 = min(t0 + tq, a.rows);
 
-  // this lane's two query columns and their Q fragments (B operand of K Q^T)
+  // this lane's two query columns and their Q fragments (B operand of K Q^T,
+  // kept in AGPRs)
   QCol qc[2];
   bf16x8 qf[2][kD / 16];
 #pragma unroll
@@ -319,7 +433,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(AttnArgs a) {
     const __bf16* qp = (const __bf16*)a.q + (int64_t)qc[nt].tok * a.q_st +
                        (int64_t)qc[nt].head * a.q_sh + 8 * h32;
 #pragma unroll
-    for (int ds = 0; ds < kD / 16; ++ds) qf[nt][ds] = qc[nt].valid ? load8(qp + ds * 16) : zero8();
+    for (int ds = 0; ds < kD / 16; ++ds) {
+      qf[nt][ds] = qc[nt].valid ? load8(qp + ds * 16) : zero8();
+      pin_agpr(qf[nt][ds]);
+    }
   }
 
   KeyWalk<BN> walk;
@@ -329,11 +446,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(AttnArgs a) {
   walk.bmax = a.ri.bmax;
   walk.bmin = a.ri.bmin;
   walk.rows = a.rows;
+  BlockSrc<BN> src{&a, g, walk.n_ext_blocks};
 
   Frag f;
   frag_init(f, lane);
-  const uint32_t so = stage_off(tid);
-  KvStage<BN> st;
+  int kendreg = -1;
   const float c = a.scale_log2;
   float mrow[2] = {-INFINITY, -INFINITY};   // running max (log2 units) in use
   float lrow[2] = {0.f, 0.f};
@@ -342,20 +459,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(AttnArgs a) {
   for (int dt = 0; dt < kD / 32; ++dt)
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) acc[dt][nt] = zero16();
+  fence_acc(acc);
 
-  auto blk_k0 = [&](int b) { return (b < walk.n_ext_blocks ? b : b - walk.n_ext_blocks) * BN; };
-
-  // one key block held in buffer B; stages block nxt into the other buffer
-  auto block = [&](auto bc, int blk, int nxt) {
-    constexpr int B = decltype(bc)::value;
-    const lds_t* kt_s = sb + kFwdK + B * kFwdTile;
-    const lds_t* vt_s = sb + kFwdV + B * kFwdTile;
-    const bool ext = blk < walk.n_ext_blocks;
-    const int k0 = blk_k0(blk);
-    const bool msk = walk.masked(blk, a.n_ext);
-
-    // S^T = K Q^T for BN keys x 64 queries
-    f32x16 s[BN / 32][2];
+  auto s_tile = [&](const lds_t* kt_s, f32x16 (&s)[BN / 32][2]) {
 #pragma unroll
     for (int kt = 0; kt < BN / 32; ++kt)
 #pragma unroll
@@ -369,27 +475,50 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(AttnArgs a) {
         for (int nt = 0; nt < 2; ++nt) s[kt][nt] = mfma(af, qf[nt][ds], s[kt][nt]);
       }
     }
-    if (msk) {
-      const int klim = ext ? a.n_ext : a.rows;
-#pragma unroll
-      for (int kt = 0; kt < BN / 32; ++kt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int kl = kt * 32 + 8 * (i >> 2) + 4 * h32 + (i & 3);
-          const int kk = k0 + kl;
-          bool vis0 = kk < klim, vis1 = kk < klim;
-          if (!ext) {
-            const int ke = kend_s[B][kl];
-            vis0 = vis0 && kk <= qc[0].tok && qc[0].tok < ke;
-            vis1 = vis1 && kk <= qc[1].tok && qc[1].tok < ke;
-          }
-          if (!vis0) s[kt][0][i] = -INFINITY;
-          if (!vis1) s[kt][1][i] = -INFINITY;
-        }
+  };
+  auto mask_if = [&](f32x16 (&s)[BN / 32][2], int b, const int32_t* kend) {
+    if (walk.masked(b, a.n_ext))
+      mask_st<BN>(s, src.ext(b), src.k0(b), src.ext(b) ? a.n_ext : a.rows, kend, qc[0].tok,
+                  qc[1].tok, h32);
+  };
+
+  // prologue: K blocks 0 and 1, V block 0; S of block 0
+  const int b0 = walk.next(0);
+  const int b1 = b0 >= 0 ? walk.next(b0 + 1) : -1;
+  f32x16 s_cur[BN / 32][2];
+  if (b0 >= 0) {
+    src.dma_k(b0, sb + kFwdK, wave, lane);
+    src.dma_v(b0, sb + kFwdV, wave, lane);
+    kendreg = load_kend<BN>(a, src, b0, tid);
+    if (tid < BN) kend_s[0][tid] = kendreg;
+    if (b1 >= 0) {
+      src.dma_k(b1, sb + kFwdK + kFwdTile, wave, lane);
+      kendreg = load_kend<BN>(a, src, b1, tid);
+      if (tid < BN) kend_s[1][tid] = kendreg;
     }
-    // online softmax (log2 domain), per query column, with lazy rescaling:
-    // the running maximum in use only moves when a block exceeds it by more
-    // than kRescale, so probabilities stay below 2^kRescale
+  }
+  dma_wait();
+  __syncthreads();
+  if (b0 >= 0) {
+    s_tile(sb + kFwdK, s_cur);
+    mask_if(s_cur, b0, kend_s[0]);
+  }
+  __syncthreads();   // K buffer 0 and kend_s[0] are restaged by the first iteration
+
+  // iteration for block cur in buffers B (its V) with block nx1 in K buffer
+  // 1 - B; stages K of nx2 into K buffer B and V of nx1 into V buffer 1 - B
+  auto iter = [&](auto bc, int cur, int nx1, int nx2) {
+    constexpr int B = decltype(bc)::value;
+    (void)cur;
+    if (nx2 >= 0) {
+      src.dma_k(nx2, sb + kFwdK + B * kFwdTile, wave, lane);
+      kendreg = load_kend<BN>(a, src, nx2, tid);
+    }
+    if (nx1 >= 0) src.dma_v(nx1, sb + kFwdV + (1 - B) * kFwdTile, wave, lane);
+
+    // online softmax (log2 domain) of block cur, per query column, with lazy
+    // rescaling: the running maximum in use only moves when a block exceeds
+    // it by more than kRescale, so probabilities stay below 2^kRescale
     float mx[2];
     bool grow = false;
 #pragma unroll
@@ -398,13 +527,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(AttnArgs a) {
 #pragma unroll
       for (int kt = 0; kt < BN / 32; ++kt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) m = fmaxf(m, s[kt][nt][i]);
+        for (int i = 0; i < 16; ++i) m = fmaxf(m, s_cur[kt][nt][i]);
       m = fmaxf(m, __shfl_xor(m, 32)) * c;
       mx[nt] = m;
       grow = grow || (m > mrow[nt] + kRescale);
     }
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-      acc_fence();
+      fence_acc(acc);
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         const float mnew = fmaxf(mrow[nt], mx[nt]);
@@ -414,8 +543,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(AttnArgs a) {
         for (int dt = 0; dt < kD / 32; ++dt) acc[dt][nt] *= alpha;
         mrow[nt] = mnew;
       }
-      acc_fence();
+      fence_acc(acc);
     }
+
+    // S^T of the next block (MFMA) while P of this block is formed (VALU)
+    f32x16 s_nxt[BN / 32][2];
+    s_tile(sb + kFwdK + (1 - B) * kFwdTile, s_nxt);
     bf16x8 pb[2][BN / 16];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
@@ -425,53 +558,52 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(AttnArgs a) {
       for (int kt = 0; kt < BN / 32; ++kt) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float p = fast_exp2(fmaf(s[kt][nt][i], c, -muse));
-          s[kt][nt][i] = p;
+          const float p = fast_exp2(fmaf(s_cur[kt][nt][i], c, -muse));
+          s_cur[kt][nt][i] = p;
           lsum += p;
         }
-        pb[nt][2 * kt] = pack_half(s[kt][nt], 0);
-        pb[nt][2 * kt + 1] = pack_half(s[kt][nt], 1);
+        pb[nt][2 * kt] = pack_half(s_cur[kt][nt], 0);
+        pb[nt][2 * kt + 1] = pack_half(s_cur[kt][nt], 1);
       }
       lrow[nt] += lsum;
     }
     // O^T += V^T P^T
-#pragma unroll
-    for (int dt = 0; dt < kD / 32; ++dt) {
+    const lds_t* vt_s = sb + kFwdV + B * kFwdTile;
+    static_for<0, kD / 32>([&](auto dtc) {
+      constexpr int dt = decltype(dtc)::value;
 #pragma unroll
       for (int ks = 0; ks < BN / 16; ++ks) {
         const lds_t* vb = vt_s + ks * 16 * kRowB;
         const bf16x8 af = ld_tr(vb + f.tr[dt][0], vb + f.tr[dt][1]);
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) mfma_acc(acc[dt][nt], af, pb[nt][ks]);
+        mfma_acc(acc[dt][0], af, pb[0][ks]);
+        mfma_acc(acc[dt][1], af, pb[1][ks]);
       }
-    }
-    if (nxt >= 0)
-      st.stash(sb + kFwdK + (1 - B) * kFwdTile, sb + kFwdV + (1 - B) * kFwdTile, kend_s[1 - B],
-               nxt < walk.n_ext_blocks, tid, so);
+    });
+    if (nx1 >= 0) mask_if(s_nxt, nx1, kend_s[1 - B]);
+#pragma unroll
+    for (int kt = 0; kt < BN / 32; ++kt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) s_cur[kt][nt] = s_nxt[kt][nt];
+    if (nx2 >= 0 && tid < BN) kend_s[B][tid] = kendreg;
+    dma_wait();
     __syncthreads();
   };
 
-  int blk = walk.next(0);
-  if (blk >= 0) {
-    const bool ext = blk < walk.n_ext_blocks;
-    st.issue(a, g, ext, blk_k0(blk), tid);
-    st.stash(sb + kFwdK, sb + kFwdV, kend_s[0], ext, tid, so);
-  }
-  __syncthreads();
-  while (blk >= 0) {
-    int nxt = walk.next(blk + 1);
-    if (nxt >= 0) st.issue(a, g, nxt < walk.n_ext_blocks, blk_k0(nxt), tid);
-    block(Buf<0>(), blk, nxt);
-    blk = nxt;
-    if (blk < 0) break;
-    nxt = walk.next(blk + 1);
-    if (nxt >= 0) st.issue(a, g, nxt < walk.n_ext_blocks, blk_k0(nxt), tid);
-    block(Buf<1>(), blk, nxt);
-    blk = nxt;
+  int cur = b0, nx1 = b1;
+  while (cur >= 0) {
+    int nx2 = nx1 >= 0 ? walk.next(nx1 + 1) : -1;
+    iter(Buf<0>(), cur, nx1, nx2);
+    cur = nx1;
+    nx1 = nx2;
+    if (cur < 0) break;
+    nx2 = nx1 >= 0 ? walk.next(nx1 + 1) : -1;
+    iter(Buf<1>(), cur, nx1, nx2);
+    cur = nx1;
+    nx1 = nx2;
   }
 
   // finalize: O = acc / l, LSE = (m + log2 l) ln 2
-  acc_fence();
+  fence_acc(acc);
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     const float l = lrow[nt] + __shfl_xor(lrow[nt], 32);
@@ -495,17 +627,22 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(AttnArgs a) {
 
 // ---------------------------------------------------------------------------
 // Backward, Q-stationary: D and dQ.
+//
+// Software-pipelined like the forward: the MFMAs compute S^T and dP^T of key
+// block j + 1 while dS of block j is formed, then dQ^T += K_j^T dS_j^T.  Both
+// K and V of block j + 1 are needed one iteration ahead, and K of block j is
+// read again by the dQ product, so blocks rotate through three buffers.
 constexpr int kDqBN = 32;
 constexpr int kDqTile = kDqBN * kRowB;
-constexpr int kDqK = 0, kDqV = 2 * kDqTile;
+constexpr int kDqK = 0, kDqV = 3 * kDqTile;         // three K buffers, then three V buffers
 
 __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(AttnArgs a) {
   constexpr int BN = kDqBN;
-  __shared__ __attribute__((aligned(16))) char smem[4 * kDqTile];
-  __shared__ int32_t kend_s[2][BN];
+  __shared__ __attribute__((aligned(16))) char smem[6 * kDqTile];
+  __shared__ int32_t kend_s[3][BN];
   lds_t* const sb = (lds_t*)smem;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int col = lane & 31, h32 = lane >> 5;
   const int tq = kRowsPerWg / a.group;
   const int n_qt = (a.rows + tq - 1) / tq;
@@ -534,6 +671,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(AttnArgs a) {
       const bf16x8 ov = qc[nt].valid ? load8((const __bf16*)a.o + oo + ds * 16) : zero8();
 #pragma unroll
       for (int e = 0; e < 8; ++e) dot = fmaf((float)df[nt][ds][e], (float)ov[e], dot);
+      pin_agpr(qf[nt][ds]);
+      pin_agpr(df[nt][ds]);
     }
     dot += __shfl_xor(dot, 32);
     dsum[nt] = dot;
@@ -549,30 +688,21 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(AttnArgs a) {
   walk.bmax = a.ri.bmax;
   walk.bmin = a.ri.bmin;
   walk.rows = a.rows;
+  BlockSrc<BN> src{&a, g, walk.n_ext_blocks};
 
   Frag f;
   frag_init(f, lane);
-  const uint32_t so = stage_off(tid);
-  KvStage<BN> st;
+  int kendreg = -1;
   const float c = a.scale_log2;
   f32x16 acc[kD / 32][2];
 #pragma unroll
   for (int dt = 0; dt < kD / 32; ++dt)
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) acc[dt][nt] = zero16();
+  fence_acc(acc);
 
-  auto blk_k0 = [&](int b) { return (b < walk.n_ext_blocks ? b : b - walk.n_ext_blocks) * BN; };
-
-  auto block = [&](auto bc, int blk, int nxt) {
-    constexpr int B = decltype(bc)::value;
-    const lds_t* kt_s = sb + kDqK + B * kDqTile;
-    const lds_t* vt_s = sb + kDqV + B * kDqTile;
-    const bool ext = blk < walk.n_ext_blocks;
-    const int k0 = blk_k0(blk);
-    const bool msk = walk.masked(blk, a.n_ext);
-
-    // S^T = K Q^T and dP^T = V dO^T: 32 keys x 64 queries
-    f32x16 s[2], dp[2];
+  // S^T = K Q^T and dP^T = V dO^T: 32 keys x 64 queries
+  auto sdp_tile = [&](const lds_t* kt_s, const lds_t* vt_s, f32x16 (&s)[2], f32x16 (&dp)[2]) {
     s[0] = zero16(); s[1] = zero16(); dp[0] = zero16(); dp[1] = zero16();
 #pragma unroll
     for (int ds = 0; ds < kD / 16; ++ds) {
@@ -584,61 +714,132 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(AttnArgs a) {
         dp[nt] = mfma(va, df[nt][ds], dp[nt]);
       }
     }
-    bf16x8 dsb[2][2];
+  };
+  // invisible entries of block b's S^T get -inf (so P^T = 0)
+  auto mask_if = [&](f32x16 (&s)[2], int b, const int32_t* kend) {
+    if (!walk.masked(b, a.n_ext)) return;
+    const bool ext = src.ext(b);
+    const int k0 = src.k0(b);
+    const int klim = ext ? a.n_ext : a.rows;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kl = 8 * (i >> 2) + 4 * h32 + (i & 3);
+        const int kk = k0 + kl;
+        const int ke = ext ? 0x7fffffff : kend[kl];
+        const bool vis = kk < klim && (ext || (kk <= qc[nt].tok && qc[nt].tok < ke));
+        s[nt][i] = vis ? s[nt][i] : -INFINITY;
+      }
+  };
+  // dS^T = P^T * (dP^T - D), with P^T = exp2(S^T c - LSE log2 e)
+  auto ds_tile = [&](f32x16 (&s)[2], const f32x16 (&dp)[2], bf16x8 (&dsb)[2][2]) {
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float p = fast_exp2(fmaf(s[nt][i], c, -lse2[nt]));
-        if (msk) {
-          const int kl = 8 * (i >> 2) + 4 * h32 + (i & 3);
-          const int kk = k0 + kl;
-          bool vis = kk < (ext ? a.n_ext : a.rows);
-          if (!ext) vis = vis && kk <= qc[nt].tok && qc[nt].tok < kend_s[B][kl];
-          if (!vis) p = 0.f;
-        }
+        const float p = fast_exp2(fmaf(s[nt][i], c, -lse2[nt]));
         s[nt][i] = p * (dp[nt][i] - dsum[nt]);
       }
       dsb[nt][0] = pack_half(s[nt], 0);
       dsb[nt][1] = pack_half(s[nt], 1);
     }
-    // dQ^T += K^T dS^T
+  };
+
+  // prologue: blocks 0 and 1 staged; S, dP of block 0
+  const int b0 = walk.next(0);
+  const int b1 = b0 >= 0 ? walk.next(b0 + 1) : -1;
+  f32x16 sA[2], dpA[2], sB[2], dpB[2];
+  if (b0 >= 0) {
+    src.dma_k(b0, sb + kDqK, wave, lane);
+    src.dma_v(b0, sb + kDqV, wave, lane);
+    kendreg = load_kend<BN>(a, src, b0, tid);
+    if (tid < BN) kend_s[0][tid] = kendreg;
+    if (b1 >= 0) {
+      src.dma_k(b1, sb + kDqK + kDqTile, wave, lane);
+      src.dma_v(b1, sb + kDqV + kDqTile, wave, lane);
+      kendreg = load_kend<BN>(a, src, b1, tid);
+      if (tid < BN) kend_s[1][tid] = kendreg;
+    }
+  }
+  dma_wait();
+  __syncthreads();
+  if (b0 >= 0) {
+    sdp_tile(sb + kDqK, sb + kDqV, sA, dpA);
+    mask_if(sA, b0, kend_s[0]);
+  }
+
+  // iteration for block cur in buffer B, nx1 in buffer (B + 1) % 3; stages
+  // nx2 into buffer (B + 2) % 3, last read by the previous iteration.  The
+  // current block's S/dP are in (sc, dpc); the next block's go to (sn, dpn).
+  auto iter = [&](auto bc, f32x16 (&sc)[2], f32x16 (&dpc)[2], f32x16 (&sn)[2],
+                  f32x16 (&dpn)[2], int nx1, int nx2) {
+    constexpr int B = decltype(bc)::value;
+    constexpr int B1 = (B + 1) % 3, B2 = (B + 2) % 3;
+    if (nx2 >= 0) {
+      src.dma_k(nx2, sb + kDqK + B2 * kDqTile, wave, lane);
+      src.dma_v(nx2, sb + kDqV + B2 * kDqTile, wave, lane);
+      kendreg = load_kend<BN>(a, src, nx2, tid);
+    }
+    // S^T, dP^T of the next block (MFMA) while dS^T of this block is formed
+    sdp_tile(sb + kDqK + B1 * kDqTile, sb + kDqV + B1 * kDqTile, sn, dpn);
+    bf16x8 dsb[2][2];
+    ds_tile(sc, dpc, dsb);
+    // interleave: LDS fragment reads run four MFMA pairs ahead
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-    for (int dt = 0; dt < kD / 32; ++dt) {
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // two MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // five VALU
+      if (i < 12) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+    }
+    // dQ^T += K^T dS^T
+    const lds_t* kt_s = sb + kDqK + B * kDqTile;
+    static_for<0, kD / 32>([&](auto dtc) {
+      constexpr int dt = decltype(dtc)::value;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const lds_t* kb = kt_s + ks * 16 * kRowB;
         const bf16x8 af = ld_tr(kb + f.tr[dt][0], kb + f.tr[dt][1]);
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) mfma_acc(acc[dt][nt], af, dsb[nt][ks]);
+        mfma_acc(acc[dt][0], af, dsb[0][ks]);
+        mfma_acc(acc[dt][1], af, dsb[1][ks]);
       }
-    }
-    if (nxt >= 0)
-      st.stash(sb + kDqK + (1 - B) * kDqTile, sb + kDqV + (1 - B) * kDqTile, kend_s[1 - B],
-               nxt < walk.n_ext_blocks, tid, so);
+    });
+    if (nx1 >= 0) mask_if(sn, nx1, kend_s[B1]);
+    if (nx2 >= 0 && tid < BN) kend_s[B2][tid] = kendreg;
+    dma_wait();
     __syncthreads();
   };
 
-  int blk = walk.next(0);
-  if (blk >= 0) {
-    const bool ext = blk < walk.n_ext_blocks;
-    st.issue(a, g, ext, blk_k0(blk), tid);
-    st.stash(sb + kDqK, sb + kDqV, kend_s[0], ext, tid, so);
-  }
-  __syncthreads();
-  while (blk >= 0) {
-    int nxt = walk.next(blk + 1);
-    if (nxt >= 0) st.issue(a, g, nxt < walk.n_ext_blocks, blk_k0(nxt), tid);
-    block(Buf<0>(), blk, nxt);
-    blk = nxt;
-    if (blk < 0) break;
-    nxt = walk.next(blk + 1);
-    if (nxt >= 0) st.issue(a, g, nxt < walk.n_ext_blocks, blk_k0(nxt), tid);
-    block(Buf<1>(), blk, nxt);
-    blk = nxt;
+  // blocks rotate through 3 LDS buffers and 2 register sets: unroll by 6
+  int cur = b0, nx1 = b1;
+  while (cur >= 0) {
+    int nx2 = nx1 >= 0 ? walk.next(nx1 + 1) : -1;
+    iter(Buf<0>(), sA, dpA, sB, dpB, nx1, nx2);
+    cur = nx1; nx1 = nx2;
+    if (cur < 0) break;
+    nx2 = nx1 >= 0 ? walk.next(nx1 + 1) : -1;
+    iter(Buf<1>(), sB, dpB, sA, dpA, nx1, nx2);
+    cur = nx1; nx1 = nx2;
+    if (cur < 0) break;
+    nx2 = nx1 >= 0 ? walk.next(nx1 + 1) : -1;
+    iter(Buf<2>(), sA, dpA, sB, dpB, nx1, nx2);
+    cur = nx1; nx1 = nx2;
+    if (cur < 0) break;
+    nx2 = nx1 >= 0 ? walk.next(nx1 + 1) : -1;
+    iter(Buf<0>(), sB, dpB, sA, dpA, nx1, nx2);
+    cur = nx1; nx1 = nx2;
+    if (cur < 0) break;
+    nx2 = nx1 >= 0 ? walk.next(nx1 + 1) : -1;
+    iter(Buf<1>(), sA, dpA, sB, dpB, nx1, nx2);
+    cur = nx1; nx1 = nx2;
+    if (cur < 0) break;
+    nx2 = nx1 >= 0 ? walk.next(nx1 + 1) : -1;
+    iter(Buf<2>(), sB, dpB, sA, dpA, nx1, nx2);
+    cur = nx1; nx1 = nx2;
   }
 
-  acc_fence();
+  fence_acc(acc);
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     if (!qc[nt].valid) continue;
@@ -669,18 +870,18 @@ constexpr int kQStep = 32;
 constexpr int kKeysPerWave = 64;
 constexpr int kKeysPerWg = 4 * kKeysPerWave;
 constexpr int kStepTile = kQStep * kRowB;
-constexpr int kDkvV = 0;                                  // V rows of the workgroup
-constexpr int kDkvQ = kKeysPerWg * kRowB;                 // two Q step buffers
-constexpr int kDkvO = kDkvQ + 2 * kStepTile;              // two dO step buffers
-constexpr int kDkvBytes = kDkvO + 2 * kStepTile;
+constexpr int kDkvQ = 0;                                  // three Q step buffers
+constexpr int kDkvO = 3 * kStepTile;                      // three dO step buffers
+constexpr int kDkvV = 6 * kStepTile;                      // V rows of the workgroup
+constexpr int kDkvBytes = kDkvV + kKeysPerWg * kRowB;
 
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[kDkvBytes];
-  __shared__ __attribute__((aligned(16))) float lse_s[2][kQStep];
-  __shared__ __attribute__((aligned(16))) float dsum_s[2][kQStep];
+  __shared__ __attribute__((aligned(16))) float lse_s[3][kQStep];
+  __shared__ __attribute__((aligned(16))) float dsum_s[3][kQStep];
   lds_t* const sb = (lds_t*)smem;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int col = lane & 31, h32 = lane >> 5;
 
   const int n_ext_kb = (a.n_ext + kKeysPerWg - 1) / kKeysPerWg;
@@ -728,9 +929,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(AttnArgs a) {
     it_hi = min(n_it, it_lo + per);
   }
 
-  const uint32_t so = stage_off(tid);
   // V rows of the workgroup into LDS; K fragments (B operand of Q K^T) of the
-  // wave's two 32-key tiles into registers; visibility bounds of the keys
+  // wave's two 32-key tiles into registers; visibility bounds of the keys.
+  // Keys past the end get zero K/V; their (discarded) gradients are the only
+  // values they influence, so they need no mask.
   bf16x8 kf[2][kD / 16];
   int kend_k[2];
   bool kvalid[2];
@@ -740,12 +942,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(AttnArgs a) {
     const __bf16* vbase = (const __bf16*)(ext ? a.v_ext : a.v_own);
     const int64_t kst = ext ? a.kx_st : a.ko_st, ksh = ext ? a.kx_sh : a.ko_sh;
     const int64_t vst = ext ? a.vx_st : a.vo_st, vsh = ext ? a.vx_sh : a.vo_sh;
-#pragma unroll 4
-    for (int i = 0; i < kKeysPerWg / 16; ++i) {
-      const int kk = k0 + 16 * i + (tid >> 4);
-      const u32x4 v = kk < klim ? load16(vbase + (int64_t)kk * vst + (int64_t)g * vsh + (tid & 15) * 8)
-                                : zero_u4();
-      st16(sb + kDkvV + so + i * 16 * kRowB, v);
+    {
+      const uint32_t st_b = 2u * (uint32_t)vst;
+      dma_rows<kKeysPerWg>(row_rsrc(vbase + (int64_t)k0 * vst + (int64_t)g * vsh, klim - k0, st_b),
+                           dma_lane_off(wave, lane, st_b), st_b, sb + kDkvV, wave);
     }
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
@@ -771,33 +971,36 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(AttnArgs a) {
   }
   const int wave_khi = min(kw0 + kKeysPerWave, klim) - 1;   // last valid key of the wave
 
-  Frag f;
-  frag_init(f, lane);
-  uint32_t vrow[kD / 16];   // this wave's V fragments: rows 64 wave + l % 32 (+ 32 per tile)
-#pragma unroll
-  for (int ds = 0; ds < kD / 16; ++ds) vrow[ds] = f.row8[ds] + wave * kKeysPerWave * kRowB;
+  FragC f;
+  {
+    Frag ff;
+    frag_init(ff, lane);
+    f.init(ff);
+  }
+  // this wave's V fragments: rows 64 wave + l % 32 (+ 32 per tile); the base
+  // is a multiple of 256 bytes, so the XOR form applies to it as well
+  uint32_t vrow0 = kDkvV + wave * kKeysPerWave * kRowB + f.row8_0;
 
-  // staging of one query step: Q and dO rows (32 tokens x 128 d each)
-  u32x4 qreg[2], dreg[2];
+  // staging of one query step: Q and dO rows (32 tokens x 128 d each) by
+  // DMA into Q/dO buffer B, LSE and D through registers; the step's (query
+  // tile, head) advances incrementally
   float lreg = 0.f, dsreg = 0.f;
-  auto issue = [&](int it) {
-    const int qt = qt_lo + it / a.group;
-    const int j = it % a.group;
-    const int head = a.ri.qhead[g * a.group + j];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int tok = qt * kQStep + 16 * i + (tid >> 4);
-      const int ch = tid & 15;
-      const bool ok = tok < a.rows;
-      qreg[i] = ok ? load16((const __bf16*)a.q + (int64_t)tok * a.q_st + (int64_t)head * a.q_sh +
-                            ch * 8)
-                   : zero_u4();
-      dreg[i] = ok ? load16((const __bf16*)a.dout + (int64_t)tok * a.do_st +
-                            (int64_t)head * a.do_sh + ch * 8)
-                   : zero_u4();
-    }
+  int iss_qt = qt_lo + it_lo / a.group, iss_j = it_lo % a.group;
+  const uint32_t q_st_b = 2u * (uint32_t)a.q_st, do_st_b = 2u * (uint32_t)a.do_st;
+  const uint32_t q_loff = dma_lane_off(wave, lane, q_st_b);
+  const uint32_t do_loff = dma_lane_off(wave, lane, do_st_b);
+  auto issue = [&](auto bc) {
+    constexpr int B = decltype(bc)::value;
+    const int head = a.ri.qhead[g * a.group + iss_j];
+    const int tbase = iss_qt * kQStep;
+    const __bf16* qb = (const __bf16*)a.q + (int64_t)tbase * a.q_st + (int64_t)head * a.q_sh;
+    const __bf16* db = (const __bf16*)a.dout + (int64_t)tbase * a.do_st + (int64_t)head * a.do_sh;
+    dma_rows<kQStep>(row_rsrc(qb, a.rows - tbase, q_st_b), q_loff, q_st_b,
+                     sb + kDkvQ + B * kStepTile, wave);
+    dma_rows<kQStep>(row_rsrc(db, a.rows - tbase, do_st_b), do_loff, do_st_b,
+                     sb + kDkvO + B * kStepTile, wave);
     if (tid < kQStep) {
-      const int tok = qt * kQStep + tid;
+      const int tok = tbase + tid;
       if (tok < a.rows) {
         const float l = a.lse[(int64_t)head * a.rows + tok];
         lreg = (l == -INFINITY) ? INFINITY : l * kLog2e;
@@ -807,14 +1010,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(AttnArgs a) {
         dsreg = 0.f;
       }
     }
+    if (++iss_j == a.group) {
+      iss_j = 0;
+      ++iss_qt;
+    }
   };
   auto stash = [&](auto bc) {
     constexpr int B = decltype(bc)::value;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      st16(sb + kDkvQ + B * kStepTile + so + i * 16 * kRowB, qreg[i]);
-      st16(sb + kDkvO + B * kStepTile + so + i * 16 * kRowB, dreg[i]);
-    }
     if (tid < kQStep) {
       lse_s[B][tid] = lreg;
       dsum_s[B][tid] = dsreg;
@@ -830,192 +1032,183 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(AttnArgs a) {
       dk[dt][kt] = zero16();
       dv[dt][kt] = zero16();
     }
+  fence_acc(dk, dv);
 
-  // one query step held in buffer B; stages step it + 1 into the other buffer
+  // P and dS element e = (kt, i) of the step in buffer B (C rows are queries
+  // 8 (i/4) + 4 h32 + i%4), packing each finished half into pb / db
+  auto pds_elem = [&](auto bc, auto ec, bool masked, int t0, f32x16 (&s)[2], f32x16 (&dp)[2],
+                      f32x4& l4, f32x4& d4, bf16x8 (&pb)[2][2], bf16x8 (&db)[2][2]) {
+    constexpr int B = decltype(bc)::value;
+    constexpr int e = decltype(ec)::value;
+    constexpr int kt = e >> 4, i = e & 15, jj = i >> 2, r = i & 3;
+    if constexpr (r == 0) {
+      l4 = *(const f32x4*)&lse_s[B][8 * jj + 4 * h32];
+      d4 = *(const f32x4*)&dsum_s[B][8 * jj + 4 * h32];
+    }
+    float p = fast_exp2(fmaf(s[kt][i], c, -l4[r]));
+    if (masked) {
+      const int tq = t0 + 8 * jj + 4 * h32 + r;
+      const int kk = kw0 + kt * 32 + col;
+      p = (kk <= tq && tq < kend_k[kt]) ? p : 0.f;
+    }
+    s[kt][i] = p;
+    dp[kt][i] = p * (dp[kt][i] - d4[r]);
+    if constexpr ((i & 7) == 7) {
+      pb[kt][i >> 3] = pack_half(s[kt], i >> 3);
+      db[kt][i >> 3] = pack_half(dp[kt], i >> 3);
+    }
+  };
+
+  // dV^T += dO^T P ; dK^T += Q^T dS for the step in buffer B, after P and dS
+  // are formed.  (Overlapping the two would need the VGPRs of a second set of
+  // P/dS fragments, which this wave does not have beside its K fragments.)
+  auto step_bwd = [&](auto bc, bool masked, int t0, f32x16 (&s)[2], f32x16 (&dp)[2]) {
+    constexpr int B = decltype(bc)::value;
+    const lds_t* q_s = sb + kDkvQ + B * kStepTile;
+    const lds_t* d_s = sb + kDkvO + B * kStepTile;
+    bf16x8 pb[2][2], db[2][2];
+    f32x4 l4, d4;
+    static_for<0, 32>([&](auto ec) {
+      pds_elem(bc, ec, masked, t0, s, dp, l4, d4, pb, db);
+    });
+    bf16x8 oa = ld_tr(d_s + f.tr(0, 0), d_s + f.tr(0, 1));
+    bf16x8 qa = ld_tr(q_s + f.tr(0, 0), q_s + f.tr(0, 1));
+    static_for<0, 8>([&](auto prc) {           // pr = (hf, dt)
+      constexpr int pr = decltype(prc)::value;
+      constexpr int hf = pr >> 2, dt = pr & 3;
+      constexpr int hn = (pr + 1) >> 2, dn = (pr + 1) & 3;
+      bf16x8 oan, qan;
+      if constexpr (pr + 1 < 8) {
+        const lds_t* ob = d_s + hn * 16 * kRowB;
+        const lds_t* qb = q_s + hn * 16 * kRowB;
+        oan = ld_tr(ob + f.tr(dn, 0), ob + f.tr(dn, 1));
+        qan = ld_tr(qb + f.tr(dn, 0), qb + f.tr(dn, 1));
+      }
+      mfma_acc(dv[dt][0], oa, pb[0][hf]);
+      mfma_acc(dv[dt][1], oa, pb[1][hf]);
+      mfma_acc(dk[dt][0], qa, db[0][hf]);
+      mfma_acc(dk[dt][1], qa, db[1][hf]);
+      if constexpr (pr + 1 < 8) {
+        oa = oan;
+        qa = qan;
+      }
+    });
+  };
+
+  // one query step in Q/dO buffer B: S, dP by MFMA, then P, dS and the dV/dK
+  // products; stages the next step into buffer B + 1
   auto step = [&](auto bc, int it) {
     constexpr int B = decltype(bc)::value;
+    constexpr int BN = (B + 1) % 3;
     const bool more = it + 1 < it_hi;
-    if (more) issue(it + 1);
-    const int qt = qt_lo + it / a.group;
-    const int tq0 = qt * kQStep;
+    if (more) issue(Buf<BN>());
+    f.fresh();
+    asm volatile("" : "+v"(vrow0));
+    const int t0 = (qt_lo + it / a.group) * kQStep;
     // skip steps none of the wave's keys is visible to (wave-uniform)
-    const bool live = ext || (tq0 + kQStep - 1 >= wave_qlo && tq0 < wave_kend_max);
+    const bool live = ext || (t0 + kQStep - 1 >= wave_qlo && t0 < wave_kend_max);
     if (live) {
+      f32x16 s[2], dp[2];
       const lds_t* q_s = sb + kDkvQ + B * kStepTile;
       const lds_t* d_s = sb + kDkvO + B * kStepTile;
       // S = Q K^T and dP = dO V^T: 32 queries x the wave's 64 keys
-      f32x16 s[2], dp[2];
       s[0] = zero16(); s[1] = zero16(); dp[0] = zero16(); dp[1] = zero16();
 #pragma unroll
       for (int ds = 0; ds < kD / 16; ++ds) {
-        const bf16x8 qa = ld_row8(q_s + f.row8[ds]);
-        const bf16x8 da = ld_row8(d_s + f.row8[ds]);
+        const bf16x8 qa = ld_row8(q_s + f.row8(ds));
+        const bf16x8 da = ld_row8(d_s + f.row8(ds));
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
-          const bf16x8 vb = ld_row8(sb + kDkvV + kt * 32 * kRowB + vrow[ds]);
+          const bf16x8 vb = ld_row8(sb + kt * 32 * kRowB + (vrow0 ^ (uint32_t)(ds << 5)));
           s[kt] = mfma(qa, kf[kt][ds], s[kt]);
           dp[kt] = mfma(da, vb, dp[kt]);
         }
       }
-      // P and dS; the C rows are queries 8 (i/4) + 4 h32 + i%4
-      const bool need_mask =
-          !ext && !(tq0 >= wave_khi && tq0 + kQStep - 1 < wave_kend_min);
+      // keep the fragment loads one d-step ahead of their products
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int qr = 8 * jj + 4 * h32;
-        const f32x4 l4 = *(const f32x4*)&lse_s[B][qr];
-        const f32x4 d4 = *(const f32x4*)&dsum_s[B][qr];
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int i = 4 * jj + r;
-            float p = fast_exp2(fmaf(s[kt][i], c, -l4[r]));
-            if (need_mask) {
-              const int tq = tq0 + qr + r;
-              const int kk = kw0 + kt * 32 + col;
-              if (!(kk <= tq && tq < kend_k[kt])) p = 0.f;
-            }
-            if (!kvalid[kt]) p = 0.f;
-            s[kt][i] = p;
-            dp[kt][i] = p * (dp[kt][i] - d4[r]);
-          }
+      for (int ds = 0; ds < kD / 16; ++ds) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        if (ds + 2 < kD / 16) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
       }
-      bf16x8 pb[2][2], db[2][2];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        pb[kt][0] = pack_half(s[kt], 0);
-        pb[kt][1] = pack_half(s[kt], 1);
-        db[kt][0] = pack_half(dp[kt], 0);
-        db[kt][1] = pack_half(dp[kt], 1);
-      }
-      // dV^T += dO^T P ; dK^T += Q^T dS
-#pragma unroll
-      for (int dt = 0; dt < kD / 32; ++dt) {
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const lds_t* ob = d_s + hf * 16 * kRowB;
-          const lds_t* qb = q_s + hf * 16 * kRowB;
-          const bf16x8 oa = ld_tr(ob + f.tr[dt][0], ob + f.tr[dt][1]);
-          const bf16x8 qa = ld_tr(qb + f.tr[dt][0], qb + f.tr[dt][1]);
-#pragma unroll
-          for (int kt = 0; kt < 2; ++kt) {
-            mfma_acc(dv[dt][kt], oa, pb[kt][hf]);
-            mfma_acc(dk[dt][kt], qa, db[kt][hf]);
-          }
-        }
-      }
+      const bool need_mask = !ext && !(t0 >= wave_khi && t0 + kQStep - 1 < wave_kend_min);
+      step_bwd(bc, need_mask, t0, s, dp);
     }
-    if (more) stash(Buf<1 - B>());
+    if (more) stash(Buf<BN>());
+    dma_wait();
     __syncthreads();
   };
 
   if (it_lo < it_hi) {
-    issue(it_lo);
+    issue(Buf<0>());
     stash(Buf<0>());
   }
+  dma_wait();
   __syncthreads();
-  for (int it = it_lo; it < it_hi; it += 2) {
+  for (int it = it_lo; it < it_hi; it += 3) {
     step(Buf<0>(), it);
     if (it + 1 < it_hi) step(Buf<1>(), it + 1);
+    if (it + 2 < it_hi) step(Buf<2>(), it + 2);
   }
-
-  // lane holds key kw0 + 32 kt + col, d = 32 dt + 8 j + 4 h32 + r
-  acc_fence();
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
-    if (!kvalid[kt]) continue;
+  // lane holds key kw0 + 32 kt + col, d = 32 dt + 8 j + 4 h32 + r.  One
+  // (key tile, d tile) at a time, so the epilogue reads 32 accumulators at once.
+  fence_acc(dk, dv);
+  // destination: 0 add into gK/gV, 1 external partial, 2 own partial, 3 own output
+  const int mode = ext ? (nch == 1 ? 0 : 1) : (nch > 1 ? 2 : 3);
+  static_for<0, 2>([&](auto ktc) {
+    constexpr int kt = decltype(ktc)::value;
     const int kk = kw0 + kt * 32 + col;
     const int64_t base = ((int64_t)kk * a.hkv + g) * kD;
-    if (ext) {
-      if (nch == 1) {
-#pragma unroll
-        for (int dt = 0; dt < kD / 32; ++dt)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int d = dt * 32 + 8 * j + 4 * h32;
-            f32x4 gk = *(f32x4*)(a.gk_acc + base + d);
-            f32x4 gv = *(f32x4*)(a.gv_acc + base + d);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              gk[r] += dk[dt][kt][4 * j + r] * a.scale;
-              gv[r] += dv[dt][kt][4 * j + r];
-            }
-            *(f32x4*)(a.gk_acc + base + d) = gk;
-            *(f32x4*)(a.gv_acc + base + d) = gv;
-          }
-      } else {
-        const int64_t pbase = (int64_t)chunk * a.n_ext * a.hkv * kD + base;
-#pragma unroll
-        for (int dt = 0; dt < kD / 32; ++dt)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int d = dt * 32 + 8 * j + 4 * h32;
-            f32x4 gk, gv;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              gk[r] = dk[dt][kt][4 * j + r] * a.scale;
-              gv[r] = dv[dt][kt][4 * j + r];
-            }
-            *(f32x4*)(a.gk_part + pbase + d) = gk;
-            *(f32x4*)(a.gv_part + pbase + d) = gv;
-          }
-      }
-      continue;
-    }
-    if (nch > 1) {
-      // own keys split over query chunks: fp32 partials, finished by a reduce
-      const int64_t pbase = (int64_t)chunk * a.rows * a.hkv * kD + base;
-#pragma unroll
-      for (int dt = 0; dt < kD / 32; ++dt)
+    static_for<0, kD / 32>([&](auto dtc) {
+      constexpr int dt = decltype(dtc)::value;
+      if (kvalid[kt]) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int d = dt * 32 + 8 * j + 4 * h32;
-          f32x4 gk, gv;
+          f32x4 vk, vv;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            gk[r] = dk[dt][kt][4 * j + r] * a.scale;
-            gv[r] = dv[dt][kt][4 * j + r];
+            vk[r] = dk[dt][kt][4 * j + r] * a.scale;
+            vv[r] = dv[dt][kt][4 * j + r];
           }
-          *(f32x4*)(a.dk_part + pbase + d) = gk;
-          *(f32x4*)(a.dv_part + pbase + d) = gv;
-        }
-      continue;
-    }
+          if (mode == 0) {
+            *(f32x4*)(a.gk_acc + base + d) += vk;
+            *(f32x4*)(a.gv_acc + base + d) += vv;
+          } else if (mode == 1) {
+            const int64_t pb = (int64_t)chunk * a.n_ext * a.hkv * kD + base;
+            *(f32x4*)(a.gk_part + pb + d) = vk;
+            *(f32x4*)(a.gv_part + pb + d) = vv;
+          } else if (mode == 2) {
+            // own keys split over query chunks: fp32 partials, finished by a reduce
+            const int64_t pb = (int64_t)chunk * a.rows * a.hkv * kD + base;
+            *(f32x4*)(a.dk_part + pb + d) = vk;
+            *(f32x4*)(a.dv_part + pb + d) = vv;
+          } else {
+            if (a.gk_init) {
+              vk += *(const f32x4*)(a.gk_init + base + d);
+              vv += *(const f32x4*)(a.gv_init + base + d);
+            }
+            const int64_t ko = (int64_t)kk * a.dko_st + (int64_t)g * a.dko_sh + d;
+            const int64_t vo = (int64_t)kk * a.dvo_st + (int64_t)g * a.dvo_sh + d;
+            if (a.dkv_f32) {
+              *(f32x4*)((float*)a.dk_own + ko) = vk;
+              *(f32x4*)((float*)a.dv_own + vo) = vv;
+            } else {
+              bf16x4 wk, wv;
 #pragma unroll
-    for (int dt = 0; dt < kD / 32; ++dt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int d = dt * 32 + 8 * j + 4 * h32;
-        f32x4 vk, vv;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          vk[r] = dk[dt][kt][4 * j + r] * a.scale;
-          vv[r] = dv[dt][kt][4 * j + r];
-        }
-        if (a.gk_init) {
-          const f32x4 ik = *(const f32x4*)(a.gk_init + base + d);
-          const f32x4 iv = *(const f32x4*)(a.gv_init + base + d);
-          vk += ik;
-          vv += iv;
-        }
-        const int64_t ko = (int64_t)kk * a.dko_st + (int64_t)g * a.dko_sh + d;
-        const int64_t vo = (int64_t)kk * a.dvo_st + (int64_t)g * a.dvo_sh + d;
-        if (a.dkv_f32) {
-          *(f32x4*)((float*)a.dk_own + ko) = vk;
-          *(f32x4*)((float*)a.dv_own + vo) = vv;
-        } else {
-          bf16x4 wk, wv;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            wk[r] = (__bf16)vk[r];
-            wv[r] = (__bf16)vv[r];
+              for (int r = 0; r < 4; ++r) {
+                wk[r] = (__bf16)vk[r];
+                wv[r] = (__bf16)vv[r];
+              }
+              *(bf16x4*)((__bf16*)a.dk_own + ko) = wk;
+              *(bf16x4*)((__bf16*)a.dv_own + vo) = wv;
+            }
           }
-          *(bf16x4*)((__bf16*)a.dk_own + ko) = wk;
-          *(bf16x4*)((__bf16*)a.dv_own + vo) = wv;
         }
       }
-  }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  });
 }
 
 // grid size: per-KV-head items, padded so the XCD mapping covers every item
