@@ -875,34 +875,18 @@ constexpr int kDkvO = 3 * kStepTile;                      // three dO step buffe
 constexpr int kDkvV = 6 * kStepTile;                      // V rows of the workgroup
 constexpr int kDkvBytes = kDkvV + kKeysPerWg * kRowB;
 
-__global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[kDkvBytes];
-  __shared__ __attribute__((aligned(16))) float lse_s[3][kQStep];
-  __shared__ __attribute__((aligned(16))) float dsum_s[3][kQStep];
+// One workgroup's key block: external (prefix) keys, which every query row
+// sees unmasked, or own keys; the two are separate instantiations so the
+// external path carries no masking code.
+template <bool EXT>
+__device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int chunk, int nch,
+                                          char* smem, float (&lse_s)[3][kQStep],
+                                          float (&dsum_s)[3][kQStep]) {
+  constexpr bool ext = EXT;
   lds_t* const sb = (lds_t*)smem;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int col = lane & 31, h32 = lane >> 5;
-
-  const int n_ext_kb = (a.n_ext + kKeysPerWg - 1) / kKeysPerWg;
-  const int n_own_kb = (a.rows + kKeysPerWg - 1) / kKeysPerWg;
-  const int items = n_ext_kb * a.n_chunks + n_own_kb * a.n_chunks_own;   // per KV head
-  int g, item;
-  map_block(blockIdx.x, a.hkv, items, g, item);
-  if (g >= a.hkv) return;
-
-  const bool ext = item < n_ext_kb * a.n_chunks;
-  int kb, chunk, nch;
-  if (ext) {
-    kb = item / a.n_chunks;
-    chunk = item - kb * a.n_chunks;
-    nch = a.n_chunks;
-  } else {
-    const int oi = item - n_ext_kb * a.n_chunks;
-    kb = oi / a.n_chunks_own;
-    chunk = oi - kb * a.n_chunks_own;
-    nch = a.n_chunks_own;
-  }
   const int k0 = kb * kKeysPerWg;
   const int klim = ext ? a.n_ext : a.rows;
   const int kw0 = k0 + wave * kKeysPerWave;      // this wave's first key
@@ -991,7 +975,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(AttnArgs a) {
   const uint32_t do_loff = dma_lane_off(wave, lane, do_st_b);
   auto issue = [&](auto bc) {
     constexpr int B = decltype(bc)::value;
-    const int head = a.ri.qhead[g * a.group + iss_j];
+    const int head = __builtin_amdgcn_readfirstlane(a.ri.qhead[g * a.group + iss_j]);
     const int tbase = iss_qt * kQStep;
     const __bf16* qb = (const __bf16*)a.q + (int64_t)tbase * a.q_st + (int64_t)head * a.q_sh;
     const __bf16* db = (const __bf16*)a.dout + (int64_t)tbase * a.do_st + (int64_t)head * a.do_sh;
@@ -1036,10 +1020,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(AttnArgs a) {
 
   // P and dS element e = (kt, i) of the step in buffer B (C rows are queries
   // 8 (i/4) + 4 h32 + i%4), packing each finished half into pb / db
-  auto pds_elem = [&](auto bc, auto ec, bool masked, int t0, f32x16 (&s)[2], f32x16 (&dp)[2],
+  auto pds_elem = [&](auto bc, auto ec, auto maskc, int t0, f32x16 (&s)[2], f32x16 (&dp)[2],
                       f32x4& l4, f32x4& d4, bf16x8 (&pb)[2][2], bf16x8 (&db)[2][2]) {
     constexpr int B = decltype(bc)::value;
     constexpr int e = decltype(ec)::value;
+    const bool masked = maskc;
     constexpr int kt = e >> 4, i = e & 15, jj = i >> 2, r = i & 3;
     if constexpr (r == 0) {
       l4 = *(const f32x4*)&lse_s[B][8 * jj + 4 * h32];
@@ -1062,36 +1047,32 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(AttnArgs a) {
   // dV^T += dO^T P ; dK^T += Q^T dS for the step in buffer B, after P and dS
   // are formed.  (Overlapping the two would need the VGPRs of a second set of
   // P/dS fragments, which this wave does not have beside its K fragments.)
-  auto step_bwd = [&](auto bc, bool masked, int t0, f32x16 (&s)[2], f32x16 (&dp)[2]) {
+  auto step_bwd = [&](auto bc, auto maskc, int t0, f32x16 (&s)[2], f32x16 (&dp)[2]) {
     constexpr int B = decltype(bc)::value;
     const lds_t* q_s = sb + kDkvQ + B * kStepTile;
     const lds_t* d_s = sb + kDkvO + B * kStepTile;
     bf16x8 pb[2][2], db[2][2];
     f32x4 l4, d4;
-    static_for<0, 32>([&](auto ec) {
-      pds_elem(bc, ec, masked, t0, s, dp, l4, d4, pb, db);
-    });
-    bf16x8 oa = ld_tr(d_s + f.tr(0, 0), d_s + f.tr(0, 1));
-    bf16x8 qa = ld_tr(q_s + f.tr(0, 0), q_s + f.tr(0, 1));
-    static_for<0, 8>([&](auto prc) {           // pr = (hf, dt)
+    static_for<0, 32>([&](auto ec) { pds_elem(bc, ec, maskc, t0, s, dp, l4, d4, pb, db); });
+    // transposed dO / Q fragments of pair pr = (hf, dt) in slot pr & 1,
+    // fetched one pair ahead
+    bf16x8 oa[2], qa[2];
+    oa[0] = ld_tr(d_s + f.tr(0, 0), d_s + f.tr(0, 1));
+    qa[0] = ld_tr(q_s + f.tr(0, 0), q_s + f.tr(0, 1));
+    static_for<0, 8>([&](auto prc) {
       constexpr int pr = decltype(prc)::value;
-      constexpr int hf = pr >> 2, dt = pr & 3;
-      constexpr int hn = (pr + 1) >> 2, dn = (pr + 1) & 3;
-      bf16x8 oan, qan;
+      constexpr int hf = pr >> 2, dt = pr & 3, sl = pr & 1;
       if constexpr (pr + 1 < 8) {
+        constexpr int hn = (pr + 1) >> 2, dn = (pr + 1) & 3;
         const lds_t* ob = d_s + hn * 16 * kRowB;
         const lds_t* qb = q_s + hn * 16 * kRowB;
-        oan = ld_tr(ob + f.tr(dn, 0), ob + f.tr(dn, 1));
-        qan = ld_tr(qb + f.tr(dn, 0), qb + f.tr(dn, 1));
+        oa[sl ^ 1] = ld_tr(ob + f.tr(dn, 0), ob + f.tr(dn, 1));
+        qa[sl ^ 1] = ld_tr(qb + f.tr(dn, 0), qb + f.tr(dn, 1));
       }
-      mfma_acc(dv[dt][0], oa, pb[0][hf]);
-      mfma_acc(dv[dt][1], oa, pb[1][hf]);
-      mfma_acc(dk[dt][0], qa, db[0][hf]);
-      mfma_acc(dk[dt][1], qa, db[1][hf]);
-      if constexpr (pr + 1 < 8) {
-        oa = oan;
-        qa = qan;
-      }
+      mfma_acc(dv[dt][0], oa[sl], pb[0][hf]);
+      mfma_acc(dv[dt][1], oa[sl], pb[1][hf]);
+      mfma_acc(dk[dt][0], qa[sl], db[0][hf]);
+      mfma_acc(dk[dt][1], qa[sl], db[1][hf]);
     });
   };
 
@@ -1209,6 +1190,26 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(AttnArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     });
   });
+}
+
+__global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[kDkvBytes];
+  __shared__ __attribute__((aligned(16))) float lse_s[3][kQStep];
+  __shared__ __attribute__((aligned(16))) float dsum_s[3][kQStep];
+  const int n_ext_kb = (a.n_ext + kKeysPerWg - 1) / kKeysPerWg;
+  const int n_own_kb = (a.rows + kKeysPerWg - 1) / kKeysPerWg;
+  const int items = n_ext_kb * a.n_chunks + n_own_kb * a.n_chunks_own;   // per KV head
+  int g, item;
+  map_block(blockIdx.x, a.hkv, items, g, item);
+  if (g >= a.hkv) return;
+  if (item < n_ext_kb * a.n_chunks) {
+    const int kb = item / a.n_chunks;
+    dkv_block<true>(a, g, kb, item - kb * a.n_chunks, a.n_chunks, smem, lse_s, dsum_s);
+  } else {
+    const int oi = item - n_ext_kb * a.n_chunks;
+    const int kb = oi / a.n_chunks_own;
+    dkv_block<false>(a, g, kb, oi - kb * a.n_chunks_own, a.n_chunks_own, smem, lse_s, dsum_s);
+  }
 }
 
 // grid size: per-KV-head items, padded so the XCD mapping covers every item
