@@ -18,7 +18,7 @@
  *   Trees    pf_tree_attn_fwd/bwd      compact rollout-tree rows under an
  *                                      ancestor mask ("HARTS: A Prefix-Sharing
  *                                      Training System for Agentic RL with
- *                                      Hybrid-Attention Models", §2.1, §2.2, §3).
+ *                                      Hybrid-Attention Models", §2.1, §2.2, §3.4).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -176,7 +176,7 @@ pf_status pf_tree_attn_fwd(const pf_attn_desc* desc, int32_t n_nodes, const int3
                            pf_tensor o, float* lse, void* workspace, size_t workspace_bytes,
                            void* stream);
 
-/* Tree backward (HARTS §3: the backward of a gather of ancestor K/V sums the
+/* Tree backward (HARTS §3.4: the backward of a gather of ancestor K/V sums the
  * gradients into the shared compact rows).  dK/dV of a row sum over every
  * descendant row that reads it, and over the query heads of its KV head.
  *   o, lse from pf_tree_attn_fwd; dout [C, Hq, d]    in

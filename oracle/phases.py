@@ -25,7 +25,7 @@ agree.
 Trees (HARTS §2.1, §2.2 and §3): `tree_attention_direct` applies the ancestor
 mask to the compact rows; `tree_attention_expanded` runs causal attention on
 every root-to-leaf trajectory and sums the per-occurrence gradients back into
-the shared compact rows (HARTS §3: gather backward sums into the shared
+the shared compact rows (HARTS §3.4: gather backward sums into the shared
 compact activations).
 
 Test infrastructure only.
