@@ -19,6 +19,7 @@ import argparse
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -41,6 +42,19 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample (0 disables)")
     ap.add_argument("--json-out", default=None)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after the timed steps, run a plain elementwise copy of this many MiB "
+                         "(3 launches); its HBM counter readings scale the attention kernels' ones")
+    ap.add_argument("--traffic-summary", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT_MD"),
+                    default=None,
+                    help="no GPU work: turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
+                         "this script into the traffic summary that later runs report")
+    ap.add_argument("--stats-summary", nargs=2, metavar=("STATS_CSV", "OUT_MD"), default=None,
+                    help="no GPU work: turn a rocprofv3 --kernel-trace --stats csv of this script "
+                         "into a kernel-time summary")
+    ap.add_argument("--pmc-command", default="",
+                    help="with --traffic-summary / --stats-summary: the profiling commands, "
+                         "recorded in the summary")
     return ap.parse_args()
 
 
@@ -98,7 +112,7 @@ class KernelTimer:
         return {k: {"launches": n, "avg_ms": tot / n, "total_ms": tot} for k, (n, tot) in out.items()}
 
 
-def run_gpu(cfg, data, steps, warmup):
+def run_gpu(cfg, data, steps, warmup, copy_mib=0):
     import torch
 
     import shared_prefix_attention_pf_amd as pf
@@ -220,9 +234,149 @@ def run_gpu(cfg, data, steps, warmup):
     finally:
         pf.pf_set_launch_hook(None)
     res["kernels"] = timer.summary()
+    if copy_mib > 0:
+        copy_probe(torch, copy_mib)
     res["device"] = torch.cuda.get_device_name(0)
     res["cus"] = torch.cuda.get_device_properties(0).multi_processor_count
     return res
+
+
+# ---------------------------------------------------------------- HBM traffic from counters
+
+# launch-hook label -> substring of the kernel symbol in rocprofv3 output
+KERNEL_SYMBOL = {"pf_fwd_bf16": "fwd_kernel", "pf_bwd_dq_bf16": "bwd_dq_kernel",
+                 "pf_bwd_dkv_bf16": "bwd_dkv_kernel", "pf_fwd_f32": "fwd_f32_kernel",
+                 "pf_bwd_dq_f32": "dq_f32_kernel", "pf_bwd_dkv_f32": "dkv_f32_kernel"}
+COPY_SYMBOL = "neg_kernel"       # the elementwise copy run by --copy-probe-mib
+
+
+def kernel_source_hash():
+    """sha256 over the library's kernel and launch sources: a stored traffic
+    figure only applies to the kernels it was measured on."""
+    import hashlib
+    h = hashlib.sha256()
+    cdir = os.path.join(ROOT, "shared_prefix_attention_pf_amd", "csrc")
+    for name in sorted(os.listdir(cdir)):
+        if name.endswith((".hip", ".cpp", ".h")):
+            with open(os.path.join(cdir, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def traffic_path(cid):
+    return os.path.join(ROOT, "profiles", f"hbm_traffic_config{cid}.md")
+
+
+def copy_probe(torch, mib):
+    """A plain elementwise copy (dst = -src) of `mib` MiB of fp32, launched 3
+    times: reads exactly mib MiB and writes mib MiB per launch."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def _counter_means(run_dir, counter):
+    """{kernel symbol: mean of `counter` per dispatch} from a rocprofv3 csv run."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {run_dir}")
+    per = {}
+    for fn in files:
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                key = (fn, r["Dispatch_Id"])
+                per.setdefault(r["Kernel_Name"], {}).setdefault(key, 0.0)
+                per[r["Kernel_Name"]][key] += float(r["Counter_Value"])
+    return {k: (sum(v.values()) / len(v), len(v)) for k, v in per.items()}
+
+
+def _pick(means, sub):
+    hits = [(k, v) for k, v in means.items() if sub in k]
+    if not hits:
+        return None
+    tot = sum(v[0] * v[1] for _, v in hits)
+    n = sum(v[1] for _, v in hits)
+    return tot / n, n
+
+
+def traffic_summary(fetch_dir, write_dir, out_md, cid, copy_mib, command):
+    """Writes the per-launch HBM read/write bytes of every attention kernel,
+    each counter scaled by the ratio of known to counted bytes of the copy."""
+    fetch = _counter_means(fetch_dir, "FETCH_SIZE")
+    write = _counter_means(write_dir, "WRITE_SIZE")
+    known_kib = copy_mib * 1024.0
+    cf, cw = _pick(fetch, COPY_SYMBOL), _pick(write, COPY_SYMBOL)
+    if cf is None or cw is None:
+        raise SystemExit("the copy probe's dispatches are missing from the counter runs")
+    f_fac, w_fac = known_kib / cf[0], known_kib / cw[0]
+    lines = [f"# HBM traffic per launch, config {cid} (rocprofv3 FETCH_SIZE / WRITE_SIZE)", "",
+             "Commands (run from the repository root on one MI355X):", "", "```", command.strip(),
+             "```", "",
+             f"Copy probe: `dst = -src` over {copy_mib} MiB of fp32 (reads and writes exactly "
+             f"{copy_mib} MiB per launch).", "",
+             f"- copy FETCH_SIZE {cf[0]:.1f} KiB per launch -> fetch scale {f_fac:.4f}",
+             f"- copy WRITE_SIZE {cw[0]:.1f} KiB per launch -> write scale {w_fac:.4f}", "",
+             "| label | kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | "
+             "read bytes (scaled) | write bytes (scaled) |", "|---|---|---|---|---|---|---|"]
+    for label, sym in KERNEL_SYMBOL.items():
+        fk, wk = _pick(fetch, sym), _pick(write, sym)
+        if fk is None or wk is None:
+            continue
+        rb, wb = fk[0] * 1024 * f_fac, wk[0] * 1024 * w_fac
+        lines.append(f"| {label} | {sym} | {fk[1]} | {fk[0]:.1f} | {wk[0]:.1f} | {rb:.6g} | {wb:.6g} |")
+    lines += ["", f"kernel sources sha256: `{kernel_source_hash()}`", ""]
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
+
+def stats_summary(stats_csv, out_md, cid, command):
+    """Kernel-time table from rocprofv3's kernel_stats.csv."""
+    import csv
+    rows = list(csv.DictReader(open(stats_csv)))
+    lines = [f"# Kernel times, config {cid} (rocprofv3 --kernel-trace --stats)", "",
+             "Command (run from the repository root on one MI355X):", "", "```", command.strip(),
+             "```", "", "| kernel | calls | total (us) | average (us) | min (us) | max (us) | share |",
+             "|---|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"]
+        m = re.search(r"\w*kernel\w*", name)
+        short = m.group(0) if m else name[:60]
+        fn = re.search(r"\w+Functor", name)
+        if fn:
+            short += f" ({fn.group(0)})"
+        lines.append(f"| {short} | {r['Calls']} | {float(r['TotalDurationNs']) / 1e3:.1f} | "
+                     f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+                     f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
+    lines += ["", f"kernel sources sha256: `{kernel_source_hash()}`", ""]
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
+
+def load_traffic(cid, label):
+    """HBM bytes per launch of `label` from the stored counter summary, or None
+    when there is none or the kernel sources changed since it was taken."""
+    path = traffic_path(cid)
+    if not os.path.exists(path):
+        return None, "no counter summary"
+    text = open(path).read()
+    if f"`{kernel_source_hash()}`" not in text:
+        return None, "kernel sources changed since the counters were taken"
+    for ln in text.splitlines():
+        cells = [c.strip() for c in ln.strip().strip("|").split("|")]
+        if len(cells) == 7 and cells[0] == label:
+            return float(cells[5]) + float(cells[6]), os.path.relpath(path, ROOT)
+    return None, f"{label} missing from the counter summary"
 
 
 # ---------------------------------------------------------------- CPU oracle baseline
@@ -281,12 +435,19 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path runs on one GPU; see the sharding notes in DESIGN.md)", file=sys.stderr)
         sys.exit(2)
+    if args.stats_summary:
+        stats_summary(args.stats_summary[0], args.stats_summary[1], args.config, args.pmc_command)
+        return
+    if args.traffic_summary:
+        fdir, wdir, out_md = args.traffic_summary
+        traffic_summary(fdir, wdir, out_md, args.config, args.copy_probe_mib, args.pmc_command)
+        return
     from workloads import generate, get_config
     cfg = get_config(args.config)
     print(f"[bench] generating config {cfg.cid} ({cfg.name})", flush=True)
     data = generate(cfg)
     print("[bench] running GPU steps", flush=True)
-    gres = run_gpu(cfg, data, args.steps, args.warmup)
+    gres = run_gpu(cfg, data, args.steps, args.warmup, args.copy_probe_mib)
     d, hq = cfg.head_dim, cfg.num_q_heads
     if cfg.is_tree:
         pairs_b = tree_pairs(data["node_off"], data["parent"])
@@ -321,9 +482,12 @@ def main():
         flops_per_launch = per_pair[dom] * d * pairs_step * hq / launches_per_step
         achieved = flops_per_launch / (kn["avg_ms"] * 1e-3) / 1e12
         peak = PEAK_BF16_TFLOPS if "bf16" in dom else PEAK_F32_TFLOPS
+        traffic, traffic_src = load_traffic(cfg.cid, dom)
         roofline = {"bound": "mfma" if "bf16" in dom else "alu", "kernel": dom,
                     "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                    "frac": round(achieved / peak, 4), "traffic": None,
+                    "frac": round(achieved / peak, 4),
+                    "traffic": None if traffic is None else round(traffic),
+                    "traffic_unit": "bytes per launch", "traffic_source": traffic_src,
                     "avg_launch_ms": round(kn["avg_ms"], 4),
                     "algorithmic_flops_per_launch": flops_per_launch}
     else:
