@@ -283,6 +283,13 @@ __device__ __forceinline__ QCol qcol(const AttnArgs& a, int g, int t0, int tq, i
   return c;
 }
 
+// Uniform reads of tables the kernel never writes (key-block summaries) as
+// scalar loads: through the constant address space the compiler may use the
+// scalar cache, so reading them does not wait on the vector memory counter
+// that the staging loads use.
+typedef __attribute__((address_space(4))) const int32_t const_i32;
+__device__ __forceinline__ int ld_uniform(const int32_t* p, int i) { return ((const_i32*)p)[i]; }
+
 // Iteration over key blocks of a Q-stationary tile: external blocks first,
 // then own blocks that hold at least one key visible to some query of the
 // tile (bmax > t0), stopping at the tile's last token.
@@ -299,7 +306,7 @@ struct KeyWalk {
 #pragma unroll
     for (int s = 0; s < BN / kKeyBlockSummary; ++s) {
       const int b = kb * (BN / kKeyBlockSummary) + s;
-      if (b * kKeyBlockSummary < rows) m = max(m, bmax[b]);
+      if (b * kKeyBlockSummary < rows) m = max(m, ld_uniform(bmax, b));
     }
     return m;
   }
@@ -308,7 +315,7 @@ struct KeyWalk {
 #pragma unroll
     for (int s = 0; s < BN / kKeyBlockSummary; ++s) {
       const int b = kb * (BN / kKeyBlockSummary) + s;
-      if (b * kKeyBlockSummary < rows) m = min(m, bmin[b]);
+      if (b * kKeyBlockSummary < rows) m = min(m, ld_uniform(bmin, b));
     }
     return m;
   }
@@ -374,41 +381,89 @@ __device__ __forceinline__ int load_kend(const AttnArgs& a, const BlockSrc<BN>& 
 }
 
 // Mask of an S^T tile set (BN keys x two query columns, C layout: rows are
-// keys): invisible entries become -inf.  Branch-free per element.
+// keys): invisible entries become -inf.  Branch-free per element; the kend
+// values are read four keys at a time, one group after another, so the mask
+// holds few registers beside the tiles.
 template <int BN>
 __device__ __forceinline__ void mask_st(f32x16 (&s)[BN / 32][2], bool ext, int k0, int klim,
                                         const int32_t* kend, int tok0, int tok1, int h32) {
 #pragma unroll
   for (int kt = 0; kt < BN / 32; ++kt)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int kl = kt * 32 + 8 * (i >> 2) + 4 * h32 + (i & 3);
-      const int kk = k0 + kl;
-      const int ke = ext ? 0x7fffffff : kend[kl];
-      const bool in = kk < klim;
-      const bool v0 = in && (ext || (kk <= tok0 && tok0 < ke));
-      const bool v1 = in && (ext || (kk <= tok1 && tok1 < ke));
-      s[kt][0][i] = v0 ? s[kt][0][i] : -INFINITY;
-      s[kt][1][i] = v1 ? s[kt][1][i] : -INFINITY;
+    for (int jj = 0; jj < 4; ++jj) {
+      const int kl0 = kt * 32 + 8 * jj + 4 * h32;
+      int ke4[4];
+      if (!ext) {
+        const int4 v = *(const int4*)&kend[kl0];
+        ke4[0] = v.x; ke4[1] = v.y; ke4[2] = v.z; ke4[3] = v.w;
+      } else {
+        ke4[0] = ke4[1] = ke4[2] = ke4[3] = 0x7fffffff;
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 4 * jj + r;
+        const int kk = k0 + kl0 + r;
+        const bool in = kk < klim;
+        const bool v0 = in && kk <= tok0 && tok0 < ke4[r];
+        const bool v1 = in && kk <= tok1 && tok1 < ke4[r];
+        s[kt][0][i] = v0 || (ext && in) ? s[kt][0][i] : -INFINITY;
+        s[kt][1][i] = v1 || (ext && in) ? s[kt][1][i] : -INFINITY;
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
 }
 
 // ---------------------------------------------------------------------------
 // Forward.
 //
-// Software-pipelined over key blocks: while the softmax of block j runs on
-// the VALU, the MFMAs compute S^T of block j + 1; then O^T += V_j^T P_j^T.
-// K runs one block ahead of V, so K blocks j + 2 and V blocks j + 1 are staged
-// during iteration j into the buffers freed by iteration j - 1, with one
-// barrier per block.
+// Each key block j (64 keys) runs in two matrix-core phases:
+//   A  S^T of block j + 1 (K Q^T) on the matrix cores while the VALU finishes
+//      P_j = exp2(S_j c - m), packs it to bf16 and adds its row sums;
+//   B  O^T += V_j^T P_j^T on the matrix cores while the VALU takes the row
+//      maxima of S_{j+1}, moves the running maxima (lazy rescale) and starts
+//      the exponentials of P_{j+1}.
+// K and V rotate through three LDS buffers each: iteration j stages K of
+// block j + 3 and V of block j + 2, so every staging load has a whole
+// iteration to land before the wait that precedes its use.  One barrier per
+// block.  Two register sets for S alternate with the buffers (unrolled x6).
 constexpr int kFwdBN = 64;
 constexpr int kFwdTile = kFwdBN * kRowB;            // one K or V block
-constexpr int kFwdK = 0, kFwdV = 2 * kFwdTile;      // two K buffers, then two V buffers
+constexpr int kFwdK = 0, kFwdV = 3 * kFwdTile;      // three K buffers, then three V buffers
+constexpr int kFwdDma = kFwdBN / 16;                // staging loads per wave per tile
+constexpr int kFwdExpB = 1;                         // key tiles of P exponentiated in phase B
+
+// max(x[l], x[l ^ 32]) in every lane, without LDS
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// waits for all but the `n` most recent staging loads of this wave
+template <int N>
+__device__ __forceinline__ void dma_wait_n() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// workgroup barrier for LDS hand-offs: this wave's LDS accesses complete,
+// then all waves meet.  Unlike __syncthreads() it does not wait for global
+// memory operations, so staging loads issued ahead stay in flight (their
+// own waits are explicit).  The memory clobber keeps the compiler from
+// moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(AttnArgs a) {
   constexpr int BN = kFwdBN;
-  __shared__ __attribute__((aligned(16))) char smem[4 * kFwdTile];
-  __shared__ int32_t kend_s[2][BN];
+  __shared__ __attribute__((aligned(16))) char smem[6 * kFwdTile];
+  __shared__ __attribute__((aligned(16))) int32_t kend_s[3][BN];
   lds_t* const sb = (lds_t*)smem;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -433,11 +488,16 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(AttnArgs a) {
     const __bf16* qp = (const __bf16*)a.q + (int64_t)qc[nt].tok * a.q_st +
                        (int64_t)qc[nt].head * a.q_sh + 8 * h32;
 #pragma unroll
+    for (int ds = 0; ds < kD / 16; ++ds) qf[nt][ds] = load8(qp + ds * 16);   // row 0 if invalid
+  }
+  // all loads in flight before the first use
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
     for (int ds = 0; ds < kD / 16; ++ds) {
-      qf[nt][ds] = qc[nt].valid ? load8(qp + ds * 16) : zero8();
+      if (!qc[nt].valid) qf[nt][ds] = zero8();
       pin_agpr(qf[nt][ds]);
     }
-  }
 
   KeyWalk<BN> walk;
   walk.n_ext_blocks = (a.n_ext + BN - 1) / BN;
@@ -448,12 +508,15 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(AttnArgs a) {
   walk.rows = a.rows;
   BlockSrc<BN> src{&a, g, walk.n_ext_blocks};
 
-  Frag f;
-  frag_init(f, lane);
-  int kendreg = -1;
+  FragC f;
+  {
+    Frag ff;
+    frag_init(ff, lane);
+    f.init(ff);
+  }
   const float c = a.scale_log2;
   float mrow[2] = {-INFINITY, -INFINITY};   // running max (log2 units) in use
-  float lrow[2] = {0.f, 0.f};
+  float lrow[2] = {0.f, 0.f};               // this lane's share of the row sums
   f32x16 acc[kD / 32][2];
 #pragma unroll
   for (int dt = 0; dt < kD / 32; ++dt)
@@ -461,6 +524,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(AttnArgs a) {
     for (int nt = 0; nt < 2; ++nt) acc[dt][nt] = zero16();
   fence_acc(acc);
 
+  // S^T tile of the K block in `kt_s`: 64 keys x this wave's 64 queries
   auto s_tile = [&](const lds_t* kt_s, f32x16 (&s)[BN / 32][2]) {
 #pragma unroll
     for (int kt = 0; kt < BN / 32; ++kt)
@@ -470,143 +534,266 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(AttnArgs a) {
     for (int ds = 0; ds < kD / 16; ++ds) {
 #pragma unroll
       for (int kt = 0; kt < BN / 32; ++kt) {
-        const bf16x8 af = ld_row8(kt_s + kt * 32 * kRowB + f.row8[ds]);
+        const bf16x8 af = ld_row8(kt_s + kt * 32 * kRowB + f.row8(ds));
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) s[kt][nt] = mfma(af, qf[nt][ds], s[kt][nt]);
       }
     }
   };
-  auto mask_if = [&](f32x16 (&s)[BN / 32][2], int b, const int32_t* kend) {
-    if (walk.masked(b, a.n_ext))
-      mask_st<BN>(s, src.ext(b), src.k0(b), src.ext(b) ? a.n_ext : a.rows, kend, qc[0].tok,
-                  qc[1].tok, h32);
+  // key blocks in walk order, with whether they need an element mask (found
+  // when the block is first reached, so the mask test reads no memory later)
+  struct Blk {
+    int id;
+    bool masked;
   };
-
-  // prologue: K blocks 0 and 1, V block 0; S of block 0
-  const int b0 = walk.next(0);
-  const int b1 = b0 >= 0 ? walk.next(b0 + 1) : -1;
-  f32x16 s_cur[BN / 32][2];
-  if (b0 >= 0) {
-    src.dma_k(b0, sb + kFwdK, wave, lane);
-    src.dma_v(b0, sb + kFwdV, wave, lane);
-    kendreg = load_kend<BN>(a, src, b0, tid);
-    if (tid < BN) kend_s[0][tid] = kendreg;
-    if (b1 >= 0) {
-      src.dma_k(b1, sb + kFwdK + kFwdTile, wave, lane);
-      kendreg = load_kend<BN>(a, src, b1, tid);
-      if (tid < BN) kend_s[1][tid] = kendreg;
-    }
-  }
-  dma_wait();
-  __syncthreads();
-  if (b0 >= 0) {
-    s_tile(sb + kFwdK, s_cur);
-    mask_if(s_cur, b0, kend_s[0]);
-  }
-  __syncthreads();   // K buffer 0 and kend_s[0] are restaged by the first iteration
-
-  // iteration for block cur in buffers B (its V) with block nx1 in K buffer
-  // 1 - B; stages K of nx2 into K buffer B and V of nx1 into V buffer 1 - B
-  auto iter = [&](auto bc, int cur, int nx1, int nx2) {
-    constexpr int B = decltype(bc)::value;
-    (void)cur;
-    if (nx2 >= 0) {
-      src.dma_k(nx2, sb + kFwdK + B * kFwdTile, wave, lane);
-      kendreg = load_kend<BN>(a, src, nx2, tid);
-    }
-    if (nx1 >= 0) src.dma_v(nx1, sb + kFwdV + (1 - B) * kFwdTile, wave, lane);
-
-    // online softmax (log2 domain) of block cur, per query column, with lazy
-    // rescaling: the running maximum in use only moves when a block exceeds
-    // it by more than kRescale, so probabilities stay below 2^kRescale
-    float mx[2];
-    bool grow = false;
+  auto blk = [&](int b) { return Blk{b, b >= 0 && walk.masked(b, a.n_ext)}; };
+  auto nxt = [&](Blk b) { return blk(b.id >= 0 ? walk.next(b.id + 1) : -1); };
+  auto mask_if = [&](f32x16 (&s)[BN / 32][2], Blk b, const int32_t* kend) {
+    if (b.masked)
+      mask_st<BN>(s, src.ext(b.id), src.k0(b.id), src.ext(b.id) ? a.n_ext : a.rows, kend,
+                  qc[0].tok, qc[1].tok, h32);
+  };
+  // row maxima of S (valid when `live`), the lazy move of the running maxima
+  // (only when a block exceeds them by more than kRescale, so probabilities
+  // stay below 2^kRescale), and exp2 of the first kFwdExpB key tiles.
+  // Returns the factors the accumulators must be scaled by.
+  auto softmax_head = [&](f32x16 (&s)[BN / 32][2], bool live, float (&alpha)[2]) {
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       float m = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < BN / 32; ++kt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) m = fmaxf(m, s_cur[kt][nt][i]);
-      m = fmaxf(m, __shfl_xor(m, 32)) * c;
-      mx[nt] = m;
-      grow = grow || (m > mrow[nt] + kRescale);
+        for (int i = 0; i < 16; ++i) m = fmaxf(m, s[kt][nt][i]);
+      const float mh = max_halves(m) * c;
+      m = live ? mh : -INFINITY;
+      const bool grow = m > mrow[nt] + kRescale;
+      const float mnew = grow ? m : mrow[nt];
+      alpha[nt] = fast_exp2(grow ? mrow[nt] - mnew : 0.f);
+      lrow[nt] *= alpha[nt];
+      mrow[nt] = mnew;
+      const float muse = (mnew == -INFINITY) ? 0.f : mnew;
+#pragma unroll
+      for (int kt = 0; kt < kFwdExpB; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[kt][nt][i] = fast_exp2(fmaf(s[kt][nt][i], c, -muse));
     }
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+  };
+  auto rescale = [&](const float (&alpha)[2]) {
+    if (__builtin_amdgcn_ballot_w64(alpha[0] != 1.f || alpha[1] != 1.f) != 0) {
       fence_acc(acc);
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const float mnew = fmaxf(mrow[nt], mx[nt]);
-        const float alpha = (mnew > mrow[nt]) ? fast_exp2(mrow[nt] - mnew) : 1.f;
-        lrow[nt] *= alpha;
+      for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-        for (int dt = 0; dt < kD / 32; ++dt) acc[dt][nt] *= alpha;
-        mrow[nt] = mnew;
-      }
+        for (int dt = 0; dt < kD / 32; ++dt) acc[dt][nt] *= alpha[nt];
       fence_acc(acc);
     }
+  };
+  auto stage_k = [&](int b, int buf) {
+    src.dma_k(b, sb + kFwdK + buf * kFwdTile, wave, lane);
+  };
+  auto stage_v = [&](int b, int buf) {
+    src.dma_v(b, sb + kFwdV + buf * kFwdTile, wave, lane);
+  };
+  // visibility ends of an own block's keys into kend_s[buf], by one staging
+  // load of wave 0 (keys past the end read 0: invisible)
+  auto stage_kend = [&](int b, int buf) {
+    if (src.ext(b) || wave != 0) return;
+    const int k0 = src.k0(b);
+    const __amdgpu_buffer_rsrc_t res = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.ri.kend + k0), (short)0, 4 * (a.rows - k0), 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(res, (lds_void*)&kend_s[buf][0], 4, 4 * lane, 0, 0,
+                                             0);
+  };
 
-    // S^T of the next block (MFMA) while P of this block is formed (VALU)
-    f32x16 s_nxt[BN / 32][2];
-    s_tile(sb + kFwdK + (1 - B) * kFwdTile, s_nxt);
-    bf16x8 pb[2][BN / 16];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const float muse = (mrow[nt] == -INFINITY) ? 0.f : mrow[nt];
-      float lsum = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < BN / 32; ++kt) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = fast_exp2(fmaf(s_cur[kt][nt][i], c, -muse));
-          s_cur[kt][nt][i] = p;
-          lsum += p;
-        }
-        pb[nt][2 * kt] = pack_half(s_cur[kt][nt], 0);
-        pb[nt][2 * kt + 1] = pack_half(s_cur[kt][nt], 1);
-      }
-      lrow[nt] += lsum;
+  // prologue: K and V of blocks 0 and 1, K of block 2; S of block 0
+  const Blk b0 = blk(walk.next(0));
+  const Blk b1 = nxt(b0);
+  const Blk b2 = nxt(b1);
+  if (b0.id >= 0) {
+    stage_kend(b0.id, 0);
+    if (b1.id >= 0) stage_kend(b1.id, 1);
+    if (b2.id >= 0) stage_kend(b2.id, 2);
+    stage_k(b0.id, 0);
+    stage_v(b0.id, 0);
+    if (b1.id >= 0) {
+      stage_k(b1.id, 1);
+      stage_v(b1.id, 1);
     }
-    // O^T += V^T P^T
-    const lds_t* vt_s = sb + kFwdV + B * kFwdTile;
-    static_for<0, kD / 32>([&](auto dtc) {
-      constexpr int dt = decltype(dtc)::value;
+    if (b2.id >= 0) stage_k(b2.id, 2);
+  }
+  dma_wait();
+  __syncthreads();
+  f32x16 sA[BN / 32][2], sB[BN / 32][2];
+  if (b0.id >= 0) {
+    s_tile(sb + kFwdK, sA);
+    mask_if(sA, b0, kend_s[0]);
+    float alpha[2];
+    softmax_head(sA, true, alpha);
+  }
+
+  // iteration j: block j's S in sc (maxima applied, first tiles
+  // exponentiated), its V in V buffer B, K of block j + 1 (n1) in K buffer
+  // B + 1.  Stages K of n3 into K buffer B and V of n2 into V buffer B + 2.
+  auto iter = [&](auto bc, f32x16 (&sc)[BN / 32][2], f32x16 (&sn)[BN / 32][2], Blk n1, Blk n2,
+                  Blk n3) {
+    constexpr int B = decltype(bc)::value;
+    constexpr int B1 = (B + 1) % 3, B2 = (B + 2) % 3;
+    f.fresh();
+    // wave 0 stages n3's kend before the tiles, so the waits below (which
+    // leave this iteration's tile loads in flight) cover it
+    if (n3.id >= 0) stage_kend(n3.id, B);
+    if (n3.id >= 0) stage_k(n3.id, B);
+    if (n2.id >= 0) stage_v(n2.id, B2);
+
+    // phase A: S^T of block j + 1 while P_j is completed and packed.  Eight
+    // steps, one per 16-wide slice of head_dim: each issues the K fragments
+    // of the next step, its four products and one eighth of the P work; the
+    // scheduling fences keep that order, so every fragment read has four
+    // products' time to land.
+    const lds_t* kt_s = sb + kFwdK + B1 * kFwdTile;
+    bf16x8 kfr[2][BN / 32];
+    auto ldk = [&](int ds, bf16x8 (&dst)[BN / 32]) {
 #pragma unroll
-      for (int ks = 0; ks < BN / 16; ++ks) {
-        const lds_t* vb = vt_s + ks * 16 * kRowB;
-        const bf16x8 af = ld_tr(vb + f.tr[dt][0], vb + f.tr[dt][1]);
-        mfma_acc(acc[dt][0], af, pb[0][ks]);
-        mfma_acc(acc[dt][1], af, pb[1][ks]);
-      }
-    });
-    if (nx1 >= 0) mask_if(s_nxt, nx1, kend_s[1 - B]);
+      for (int kt = 0; kt < BN / 32; ++kt) dst[kt] = ld_row8(kt_s + kt * 32 * kRowB + f.row8(ds));
+    };
 #pragma unroll
     for (int kt = 0; kt < BN / 32; ++kt)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) s_cur[kt][nt] = s_nxt[kt][nt];
-    if (nx2 >= 0 && tid < BN) kend_s[B][tid] = kendreg;
-    dma_wait();
-    __syncthreads();
+      for (int nt = 0; nt < 2; ++nt) sn[kt][nt] = zero16();
+    bf16x8 pb[2][BN / 16];
+    float ls[2] = {0.f, 0.f};
+    const float muse0 = (mrow[0] == -INFINITY) ? 0.f : mrow[0];
+    const float muse1 = (mrow[1] == -INFINITY) ? 0.f : mrow[1];
+    ldk(0, kfr[0]);
+    static_for<0, kD / 16>([&](auto dsc) {
+      constexpr int ds = decltype(dsc)::value;
+      if constexpr (ds + 1 < kD / 16) ldk(ds + 1, kfr[(ds + 1) & 1]);
+#pragma unroll
+      for (int kt = 0; kt < BN / 32; ++kt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) sn[kt][nt] = mfma(kfr[ds & 1][kt], qf[nt][ds], sn[kt][nt]);
+      // P slice ds: query column nt, key tile kt, half h (8 values)
+      constexpr int nt = ds >> 2, kt = (ds >> 1) & 1, h = ds & 1;
+      const float muse = nt ? muse1 : muse0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float p = sc[kt][nt][8 * h + e];
+        if (kt >= kFwdExpB) p = fast_exp2(fmaf(p, c, -muse));
+        sc[kt][nt][8 * h + e] = p;
+        ls[nt] += p;
+      }
+      pb[nt][2 * kt + h] = pack_half(sc[kt][nt], h);
+      // the slice is formed here, not sunk towards its use in phase B
+      asm volatile("" : "+v"(pb[nt][2 * kt + h]), "+v"(ls[nt]));
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    lrow[0] += ls[0];
+    lrow[1] += ls[1];
+    mask_if(sn, n1, kend_s[B1]);
+
+    // phase B: O^T += V_j^T P_j^T while the maxima of S_{j+1} are taken and
+    // its first exponentials formed.  Sixteen steps, one per V fragment
+    // (fetched two steps ahead), each with two products and a sixteenth of
+    // that VALU work.
+    const lds_t* vt_s = sb + kFwdV + B * kFwdTile;
+    auto ldv = [&](int fi) {
+      const int dt = fi >> 2, ks = fi & 3;
+      const lds_t* vb = vt_s + ks * 16 * kRowB;
+      return ld_tr(vb + f.tr(dt, 0), vb + f.tr(dt, 1));
+    };
+    bf16x8 vfr[3];
+    vfr[0] = ldv(0);
+    vfr[1] = ldv(1);
+    float mx[2] = {-INFINITY, -INFINITY};
+    float alpha[2] = {1.f, 1.f};
+    float musen[2] = {0.f, 0.f};
+    const bool live = n1.id >= 0;
+    static_for<0, kD / 32 * BN / 16>([&](auto fic) {
+      constexpr int fi = decltype(fic)::value;
+      constexpr int dt = fi >> 2, ks = fi & 3;
+      if constexpr (fi + 2 < kD / 32 * BN / 16) vfr[(fi + 2) % 3] = ldv(fi + 2);
+      mfma_acc(acc[dt][0], vfr[fi % 3], pb[0][ks]);
+      mfma_acc(acc[dt][1], vfr[fi % 3], pb[1][ks]);
+      if constexpr (fi < 8) {
+        // maxima: step fi covers column fi / 4, key tile (fi / 2) & 1, half fi & 1
+        constexpr int nt = fi >> 2, kt = (fi >> 1) & 1, h = fi & 1;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mx[nt] = fmaxf(mx[nt], sn[kt][nt][8 * h + e]);
+        asm volatile("" : "+v"(mx[nt]));
+      } else if constexpr (fi == 8) {
+        // lazy move of the running maxima: only when a block exceeds them by
+        // more than kRescale, so probabilities stay below 2^kRescale
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          const float mh = max_halves(mx[nt]) * c;
+          const float m = live ? mh : -INFINITY;
+          const bool grow = m > mrow[nt] + kRescale;
+          const float mnew = grow ? m : mrow[nt];
+          alpha[nt] = fast_exp2(grow ? mrow[nt] - mnew : 0.f);
+          lrow[nt] *= alpha[nt];
+          mrow[nt] = mnew;
+          musen[nt] = (mnew == -INFINITY) ? 0.f : mnew;
+        }
+        asm volatile("" : "+v"(musen[0]), "+v"(musen[1]), "+v"(lrow[0]), "+v"(lrow[1]));
+      } else {
+        // exponentials of the first kFwdExpB key tiles, 32 kFwdExpB values
+        // over steps 9..15
+        constexpr int n_e = 32 * kFwdExpB, per = (n_e + 6) / 7;
+        constexpr int e0 = (fi - 9) * per;
+#pragma unroll
+        for (int e = e0; e < e0 + per && e < n_e; ++e) {
+          const int nt = e & 1, kt = e >> 5, i = (e >> 1) & 15;
+          sn[kt][nt][i] = fast_exp2(fmaf(sn[kt][nt][i], c, -musen[nt]));
+          asm volatile("" : "+v"(sn[kt][nt][i]));
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    rescale(alpha);
+
+    if (n3.id >= 0) {
+      dma_wait_n<2 * kFwdDma>();
+    } else if (n2.id >= 0) {
+      dma_wait_n<kFwdDma>();
+    } else {
+      dma_wait();
+    }
+    lds_barrier();
   };
 
-  int cur = b0, nx1 = b1;
-  while (cur >= 0) {
-    int nx2 = nx1 >= 0 ? walk.next(nx1 + 1) : -1;
-    iter(Buf<0>(), cur, nx1, nx2);
-    cur = nx1;
-    nx1 = nx2;
-    if (cur < 0) break;
-    nx2 = nx1 >= 0 ? walk.next(nx1 + 1) : -1;
-    iter(Buf<1>(), cur, nx1, nx2);
-    cur = nx1;
-    nx1 = nx2;
+  Blk cur = b0, n1 = b1, n2 = b2;
+  while (cur.id >= 0) {
+    Blk n3 = nxt(n2);
+    iter(Buf<0>(), sA, sB, n1, n2, n3);
+    cur = n1; n1 = n2; n2 = n3;
+    if (cur.id < 0) break;
+    n3 = nxt(n2);
+    iter(Buf<1>(), sB, sA, n1, n2, n3);
+    cur = n1; n1 = n2; n2 = n3;
+    if (cur.id < 0) break;
+    n3 = nxt(n2);
+    iter(Buf<2>(), sA, sB, n1, n2, n3);
+    cur = n1; n1 = n2; n2 = n3;
+    if (cur.id < 0) break;
+    n3 = nxt(n2);
+    iter(Buf<0>(), sB, sA, n1, n2, n3);
+    cur = n1; n1 = n2; n2 = n3;
+    if (cur.id < 0) break;
+    n3 = nxt(n2);
+    iter(Buf<1>(), sA, sB, n1, n2, n3);
+    cur = n1; n1 = n2; n2 = n3;
+    if (cur.id < 0) break;
+    n3 = nxt(n2);
+    iter(Buf<2>(), sB, sA, n1, n2, n3);
+    cur = n1; n1 = n2; n2 = n3;
   }
 
   // finalize: O = acc / l, LSE = (m + log2 l) ln 2
   fence_acc(acc);
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
-    const float l = lrow[nt] + __shfl_xor(lrow[nt], 32);
+    const float l = sum_halves(lrow[nt]);
     const float inv = (l > 0.f) ? 1.f / l : 0.f;
     if (!qc[nt].valid) continue;
     __bf16* op = (__bf16*)a.out + (int64_t)qc[nt].tok * a.out_st + (int64_t)qc[nt].head * a.out_sh;
@@ -639,7 +826,7 @@ constexpr int kDqK = 0, kDqV = 3 * kDqTile;         // three K buffers, then thr
 __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(AttnArgs a) {
   constexpr int BN = kDqBN;
   __shared__ __attribute__((aligned(16))) char smem[6 * kDqTile];
-  __shared__ int32_t kend_s[3][BN];
+  __shared__ __attribute__((aligned(16))) int32_t kend_s[3][BN];
   lds_t* const sb = (lds_t*)smem;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
