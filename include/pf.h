@@ -24,7 +24,10 @@
  * ---------------------------------------
  *  - Tensors of rows are [tokens, heads, head_dim] with head_dim contiguous,
  *    described by pf_tensor (element strides).  Device pointers, 16-byte
- *    aligned; strides multiples of 8 elements (bf16) or 4 (fp32).
+ *    aligned; strides multiples of 8 elements (bf16) or 4 (fp32).  One
+ *    tensor's rows (rows x stride_tok elements) must span less than 2 GiB
+ *    (PF_ERR_UNSUPPORTED otherwise): the kernels address a head's rows
+ *    through 32-bit buffer offsets.
  *  - LSE arrays are fp32 [num_q_heads, rows], contiguous, natural log.
  *  - gK/gV accumulators are fp32 [prefix_len, num_kv_heads, head_dim],
  *    contiguous.

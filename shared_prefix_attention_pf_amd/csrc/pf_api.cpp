@@ -91,6 +91,9 @@ pf_status check_tensor(const char* name, const pf_tensor& t, int64_t rows, int h
   if (rows > 1 && t.stride_tok < (int64_t)(heads - 1) * t.stride_head + d.d)
     return fail(PF_ERR_INVALID_ARG, "%s.stride_tok (%lld) makes rows overlap", name,
                 (long long)t.stride_tok);
+  // the bf16 kernels address one head's rows through 32-bit buffer offsets
+  if (rows * t.stride_tok * (int64_t)elem_bytes(dtype) >= ((int64_t)1 << 31))
+    return fail(PF_ERR_UNSUPPORTED, "%s spans 2 GiB or more along the token axis", name);
   return PF_OK;
 }
 

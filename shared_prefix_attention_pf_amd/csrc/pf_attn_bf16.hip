@@ -339,36 +339,57 @@ struct KeyWalk {
   }
 };
 
-// The key blocks a Q-stationary tile visits, in order (see KeyWalk), with the
-// uniform addresses of their K and V rows.
+// The rows of one KV head in a key source (the cached prefix or the call's
+// own rows) as one buffer resource over all of them: a block is selected by
+// the scalar offset, which the hardware range check includes, so rows past
+// the last one read zero.  Built once per workgroup; staging a block is then
+// scalar arithmetic plus the loads.
+struct RowSrc {
+  __amdgpu_buffer_rsrc_t res;
+  uint32_t st_b;       // bytes per row
+  uint32_t lane_off;   // this lane's byte offset within a 4-row pass
+  __device__ void init(const void* base, int nrows, int64_t st_elems, int wave, int lane) {
+    st_b = 2u * (uint32_t)st_elems;
+    res = row_rsrc(base, nrows, st_b);
+    lane_off = dma_lane_off(wave, lane, st_b);
+  }
+  // rows [r0, r0 + ROWS) into `tile`, issued by every wave of the group
+  template <int ROWS>
+  __device__ void stage(int r0, lds_t* tile, int wave) const {
+#pragma unroll
+    for (int i = 0; i < ROWS / 16; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(res, (lds_void*)(tile + (16 * i + 4 * wave) * kRowB),
+                                               16, lane_off, (uint32_t)(r0 + 16 * i) * st_b, 0, 0);
+  }
+};
+
+// The key blocks a Q-stationary tile visits, in order (see KeyWalk): block b
+// < n_ext_blocks is prefix block b, later ones are own blocks.
 template <int BN>
 struct BlockSrc {
-  const AttnArgs* a;
-  int g;
   int n_ext_blocks;
+  RowSrc kx, vx, ko, vo;
+  __device__ void init(const AttnArgs& a, int g, int n_ext_blk, int wave, int lane) {
+    n_ext_blocks = n_ext_blk;
+    kx.init((const __bf16*)a.k_ext + (int64_t)g * a.kx_sh, a.n_ext, a.kx_st, wave, lane);
+    vx.init((const __bf16*)a.v_ext + (int64_t)g * a.vx_sh, a.n_ext, a.vx_st, wave, lane);
+    ko.init((const __bf16*)a.k_own + (int64_t)g * a.ko_sh, a.rows, a.ko_st, wave, lane);
+    vo.init((const __bf16*)a.v_own + (int64_t)g * a.vo_sh, a.rows, a.vo_st, wave, lane);
+  }
   __device__ bool ext(int b) const { return b < n_ext_blocks; }
   __device__ int k0(int b) const { return (ext(b) ? b : b - n_ext_blocks) * BN; }
-  __device__ int nvalid(int b) const { return (ext(b) ? a->n_ext : a->rows) - k0(b); }
-  __device__ const __bf16* kbase(int b) const {
-    return ext(b) ? (const __bf16*)a->k_ext + (int64_t)k0(b) * a->kx_st + (int64_t)g * a->kx_sh
-                  : (const __bf16*)a->k_own + (int64_t)k0(b) * a->ko_st + (int64_t)g * a->ko_sh;
-  }
-  __device__ const __bf16* vbase(int b) const {
-    return ext(b) ? (const __bf16*)a->v_ext + (int64_t)k0(b) * a->vx_st + (int64_t)g * a->vx_sh
-                  : (const __bf16*)a->v_own + (int64_t)k0(b) * a->vo_st + (int64_t)g * a->vo_sh;
-  }
-  __device__ int64_t kst(int b) const { return ext(b) ? a->kx_st : a->ko_st; }
-  __device__ int64_t vst(int b) const { return ext(b) ? a->vx_st : a->vo_st; }
   // stage the K or V rows of block b into an LDS tile (rows past the end read 0)
-  __device__ void dma_k(int b, lds_t* tile, int wave, int lane) const {
-    const uint32_t st_b = 2u * (uint32_t)kst(b);
-    dma_rows<BN>(row_rsrc(kbase(b), nvalid(b), st_b), dma_lane_off(wave, lane, st_b), st_b, tile,
-                 wave);
+  __device__ void dma_k(int b, lds_t* tile, int wave, int /*lane*/) const {
+    if (ext(b))
+      kx.stage<BN>(k0(b), tile, wave);
+    else
+      ko.stage<BN>(k0(b), tile, wave);
   }
-  __device__ void dma_v(int b, lds_t* tile, int wave, int lane) const {
-    const uint32_t st_b = 2u * (uint32_t)vst(b);
-    dma_rows<BN>(row_rsrc(vbase(b), nvalid(b), st_b), dma_lane_off(wave, lane, st_b), st_b, tile,
-                 wave);
+  __device__ void dma_v(int b, lds_t* tile, int wave, int /*lane*/) const {
+    if (ext(b))
+      vx.stage<BN>(k0(b), tile, wave);
+    else
+      vo.stage<BN>(k0(b), tile, wave);
   }
 };
 
@@ -506,7 +527,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(AttnArgs a) {
   walk.bmax = a.ri.bmax;
   walk.bmin = a.ri.bmin;
   walk.rows = a.rows;
-  BlockSrc<BN> src{&a, g, walk.n_ext_blocks};
+  BlockSrc<BN> src;
+  src.init(a, g, walk.n_ext_blocks, wave, lane);
 
   FragC f;
   {
@@ -875,7 +897,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(AttnArgs a) {
   walk.bmax = a.ri.bmax;
   walk.bmin = a.ri.bmin;
   walk.rows = a.rows;
-  BlockSrc<BN> src{&a, g, walk.n_ext_blocks};
+  BlockSrc<BN> src;
+  src.init(a, g, walk.n_ext_blocks, wave, lane);
 
   Frag f;
   frag_init(f, lane);
