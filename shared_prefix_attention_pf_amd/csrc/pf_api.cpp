@@ -153,7 +153,8 @@ pf_status check_stream_ws(void* ws, size_t ws_bytes, size_t need) {
 // ------------------------------------------------------------- workspace
 
 struct WsLayout {
-  size_t kend = 0, bmax = 0, bmin = 0, qhead = 0, dsum = 0, gk_part = 0, gv_part = 0, total = 0;
+  size_t kend = 0, bmax = 0, bmin = 0, qhead = 0, dsum = 0, lse2 = 0, gk_part = 0, gv_part = 0;
+  size_t total = 0;
   size_t dk_part = 0, dv_part = 0;
   int32_t n_chunks = 1, n_chunks_own = 1;
 };
@@ -169,6 +170,8 @@ WsLayout layout(int32_t op, const Desc& d, int32_t n_ext, int32_t rows) {
   const bool bwd = op == PF_OP_SUFFIX_BWD || op == PF_OP_PREFIX_BWD || op == PF_OP_TREE_BWD;
   if (bwd) {
     w.dsum = off;
+    off += align_up((size_t)d.hq * rows * 4);
+    w.lse2 = off;
     off += align_up((size_t)d.hq * rows * 4);
   }
   if (op == PF_OP_SUFFIX_BWD) {
@@ -492,6 +495,7 @@ pf_status pf_suffix_attn_bwd_accum(const pf_attn_desc* desc, int32_t prefix_len,
     a.gv_part = (float*)((char*)workspace + w.gv_part);
   }
   a.dsum = (float*)((char*)workspace + w.dsum);
+  a.lse2 = (float*)((char*)workspace + w.lse2);
   set_own_parts(a, workspace, w);
   a.ri = row_info(workspace, w);
   return run_bwd(d, a, flat_segments(n_suffix, cu_seqlens), (hipStream_t)stream);
@@ -554,6 +558,7 @@ pf_status pf_prefix_bwd_inject(const pf_attn_desc* desc, int32_t prefix_len, pf_
   a.gv_init = gv_acc;
   a.lse = const_cast<float*>(lse_p);
   a.dsum = (float*)((char*)workspace + w.dsum);
+  a.lse2 = (float*)((char*)workspace + w.lse2);
   set_own_parts(a, workspace, w);
   a.ri = row_info(workspace, w);
   return run_bwd(d, a, causal_segment(prefix_len), st);
@@ -617,6 +622,7 @@ pf_status pf_tree_attn_bwd(const pf_attn_desc* desc, int32_t n_nodes, const int3
   a.dkv_f32 = d.dtype == PF_F32;
   a.lse = const_cast<float*>(lse);
   a.dsum = (float*)((char*)workspace + w.dsum);
+  a.lse2 = (float*)((char*)workspace + w.lse2);
   set_own_parts(a, workspace, w);
   a.ri = row_info(workspace, w);
   return run_bwd(d, a, tree_segments(n_nodes, node_off, send), (hipStream_t)stream);

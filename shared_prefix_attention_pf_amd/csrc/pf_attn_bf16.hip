@@ -51,6 +51,7 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -887,7 +888,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(AttnArgs a) {
     dsum[nt] = dot;
     float l = qc[nt].valid ? a.lse[(int64_t)qc[nt].head * a.rows + qc[nt].tok] : 0.f;
     lse2[nt] = (l == -INFINITY) ? INFINITY : l * kLog2e;
-    if (qc[nt].valid && h32 == 0) a.dsum[(int64_t)qc[nt].head * a.rows + qc[nt].tok] = dot;
+    if (qc[nt].valid && h32 == 0) {
+      a.dsum[(int64_t)qc[nt].head * a.rows + qc[nt].tok] = dot;
+      a.lse2[(int64_t)qc[nt].head * a.rows + qc[nt].tok] = lse2[nt];
+    }
   }
 
   KeyWalk<BN> walk;
@@ -1076,22 +1080,41 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(AttnArgs a) {
 // (query tile, head) index space when the grid needs more workgroups, and each
 // chunk writes an fp32 partial that a fixed-order reduce sums.  K fragments
 // stay in registers; the workgroup's V rows stay in LDS.
+//
+// Per step t the work is S = Q K^T, dP = dO V^T (matrix cores), P =
+// exp2(S c - LSE log2 e), dS = P (dP - D) (VALU), dV^T += dO^T P and dK^T +=
+// Q^T dS (matrix cores).  The steps are software-pipelined so the VALU work
+// of one step runs beside the products of another:
+//   M1  S of step t + 1        with  dS of step t (first half)
+//   M2a dV from step t         with  dS of step t (second half)
+//   M2b dK from step t         with  P of step t + 1 (first half)
+//   M3  dP of step t + 1       with  P of step t + 1 (second half)
+// dS reads P back from its packed bf16 form, so one set of S/dP registers
+// serves every step.  Q/dO tiles and the steps' LSE (log2 units) and D rotate
+// through four LDS buffers; step t + 3 is staged during step t, one staging
+// load per M1 product pair.
 constexpr int kQStep = 32;
 constexpr int kKeysPerWave = 64;
 constexpr int kKeysPerWg = 4 * kKeysPerWave;
 constexpr int kStepTile = kQStep * kRowB;
-constexpr int kDkvQ = 0;                                  // three Q step buffers
-constexpr int kDkvO = 3 * kStepTile;                      // three dO step buffers
-constexpr int kDkvV = 6 * kStepTile;                      // V rows of the workgroup
-constexpr int kDkvBytes = kDkvV + kKeysPerWg * kRowB;
+constexpr int kDkvBufs = 4;
+constexpr int kDkvQ = 0;                                  // Q step buffers
+constexpr int kDkvO = kDkvBufs * kStepTile;               // dO step buffers
+constexpr int kDkvV = 2 * kDkvBufs * kStepTile;           // V rows of the workgroup
+constexpr int kDkvL = kDkvV + kKeysPerWg * kRowB;         // per buffer: 64 LSE values (log2)
+constexpr int kDkvD = kDkvL + kDkvBufs * 256;             // per buffer: 64 D values
+constexpr int kDkvBytes = kDkvD + kDkvBufs * 256;
+constexpr int kDkvDma = 2 * (kQStep / 16) + 2;            // staging loads per wave per step
+
+// value k of a packed bf16 fragment, as fp32
+__device__ __forceinline__ float unpack_bf16(const bf16x8& v, int k) { return (float)v[k]; }
 
 // One workgroup's key block: external (prefix) keys, which every query row
 // sees unmasked, or own keys; the two are separate instantiations so the
 // external path carries no masking code.
 template <bool EXT>
 __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int chunk, int nch,
-                                          char* smem, float (&lse_s)[3][kQStep],
-                                          float (&dsum_s)[3][kQStep]) {
+                                          char* smem) {
   constexpr bool ext = EXT;
   lds_t* const sb = (lds_t*)smem;
   const int tid = threadIdx.x;
@@ -1110,7 +1133,7 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
     qlo = k0;
     int m = -1;
     for (int b = k0 / kKeyBlockSummary; b * kKeyBlockSummary < min(k0 + kKeysPerWg, a.rows); ++b)
-      m = max(m, a.ri.bmax[b]);
+      m = max(m, ld_uniform(a.ri.bmax, b));
     qhi = min(m, a.rows);
   }
   const int qt_lo = qlo / kQStep;
@@ -1130,7 +1153,7 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
   bf16x8 kf[2][kD / 16];
   int kend_k[2];
   bool kvalid[2];
-  int wave_qlo = 0x7fffffff, wave_kend_min = 0x7fffffff, wave_kend_max = -1;
+  int wave_kend_min = 0x7fffffff;
   {
     const __bf16* kbase = (const __bf16*)(ext ? a.k_ext : a.k_own);
     const __bf16* vbase = (const __bf16*)(ext ? a.v_ext : a.v_own);
@@ -1145,24 +1168,21 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
     for (int kt = 0; kt < 2; ++kt) {
       const int kk = kw0 + kt * 32 + col;
       kvalid[kt] = kk < klim;
-      const __bf16* kp = kbase + (int64_t)kk * kst + (int64_t)g * ksh + 8 * h32;
+      const __bf16* kp = kbase + (int64_t)(kvalid[kt] ? kk : 0) * kst + (int64_t)g * ksh + 8 * h32;
 #pragma unroll
-      for (int ds = 0; ds < kD / 16; ++ds) kf[kt][ds] = kvalid[kt] ? load8(kp + ds * 16) : zero8();
+      for (int ds = 0; ds < kD / 16; ++ds) kf[kt][ds] = load8(kp + ds * 16);
       kend_k[kt] = (!ext && kvalid[kt]) ? a.ri.kend[kk] : (ext ? 0x7fffffff : -1);
-      if (kvalid[kt]) {
-        wave_qlo = min(wave_qlo, kk);
-        wave_kend_min = min(wave_kend_min, kend_k[kt]);
-        wave_kend_max = max(wave_kend_max, kend_k[kt]);
-      }
+      if (kvalid[kt]) wave_kend_min = min(wave_kend_min, kend_k[kt]);
     }
-  }
-  // wave-wide bounds: the wave's keys are read by tokens in [wave_qlo, wave_kend_max)
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    wave_qlo = min(wave_qlo, __shfl_xor(wave_qlo, off));
-    wave_kend_min = min(wave_kend_min, __shfl_xor(wave_kend_min, off));
-    wave_kend_max = max(wave_kend_max, __shfl_xor(wave_kend_max, off));
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int ds = 0; ds < kD / 16; ++ds)
+        if (!kvalid[kt]) kf[kt][ds] = zero8();
   }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1)
+    wave_kend_min = min(wave_kend_min, __shfl_xor(wave_kend_min, off));
   const int wave_khi = min(kw0 + kKeysPerWave, klim) - 1;   // last valid key of the wave
 
   FragC f;
@@ -1175,46 +1195,65 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
   // is a multiple of 256 bytes, so the XOR form applies to it as well
   uint32_t vrow0 = kDkvV + wave * kKeysPerWave * kRowB + f.row8_0;
 
-  // staging of one query step: Q and dO rows (32 tokens x 128 d each) by
-  // DMA into Q/dO buffer B, LSE and D through registers; the step's (query
-  // tile, head) advances incrementally
-  float lreg = 0.f, dsreg = 0.f;
-  int iss_qt = qt_lo + it_lo / a.group, iss_j = it_lo % a.group;
+  // staging sources: Q and dO rows of every query head (a step selects one
+  // head and 32 tokens by the scalar offset; rows past the end read zero),
+  // and the steps' LSE (log2) and D values, 64 per step (the 32 of the step
+  // and 32 that are not used), every wave loading the same values
   const uint32_t q_st_b = 2u * (uint32_t)a.q_st, do_st_b = 2u * (uint32_t)a.do_st;
+  const uint32_t q_bytes = (uint32_t)(((int64_t)(a.rows - 1) * a.q_st + (int64_t)(a.hq - 1) * a.q_sh) * 2 + kRowB);
+  const uint32_t do_bytes = (uint32_t)(((int64_t)(a.rows - 1) * a.do_st + (int64_t)(a.hq - 1) * a.do_sh) * 2 + kRowB);
+  const uint32_t l_bytes = (uint32_t)a.hq * (uint32_t)a.rows * 4u;
+  const __amdgpu_buffer_rsrc_t q_res = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.q), (short)0, (int)q_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t do_res = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.dout), (short)0, (int)do_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t l_res = __builtin_amdgcn_make_buffer_rsrc((void*)a.lse2, (short)0, (int)l_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t d_res = __builtin_amdgcn_make_buffer_rsrc((void*)a.dsum, (short)0, (int)l_bytes, 0x00020000);
   const uint32_t q_loff = dma_lane_off(wave, lane, q_st_b);
   const uint32_t do_loff = dma_lane_off(wave, lane, do_st_b);
-  auto issue = [&](auto bc) {
-    constexpr int B = decltype(bc)::value;
-    const int head = __builtin_amdgcn_readfirstlane(a.ri.qhead[g * a.group + iss_j]);
-    const int tbase = iss_qt * kQStep;
-    const __bf16* qb = (const __bf16*)a.q + (int64_t)tbase * a.q_st + (int64_t)head * a.q_sh;
-    const __bf16* db = (const __bf16*)a.dout + (int64_t)tbase * a.do_st + (int64_t)head * a.do_sh;
-    dma_rows<kQStep>(row_rsrc(qb, a.rows - tbase, q_st_b), q_loff, q_st_b,
-                     sb + kDkvQ + B * kStepTile, wave);
-    dma_rows<kQStep>(row_rsrc(db, a.rows - tbase, do_st_b), do_loff, do_st_b,
-                     sb + kDkvO + B * kStepTile, wave);
-    if (tid < kQStep) {
-      const int tok = tbase + tid;
-      if (tok < a.rows) {
-        const float l = a.lse[(int64_t)head * a.rows + tok];
-        lreg = (l == -INFINITY) ? INFINITY : l * kLog2e;
-        dsreg = a.dsum[(int64_t)head * a.rows + tok];
-      } else {
-        lreg = INFINITY;   // exp2(s - inf) = 0: padded rows contribute nothing
-        dsreg = 0.f;
-      }
+
+  // the step the next staging call loads (steps past it_hi read zeros)
+  int iss_it = it_lo, iss_qt = qt_lo + it_lo / a.group, iss_j = it_lo % a.group;
+  uint32_t st_q = 0, st_do = 0, st_l = 0;   // scalar offsets of the step being staged
+  auto stage_begin = [&]() {
+    if (iss_it < it_hi) {
+      const int head = ld_uniform(a.ri.qhead, g * a.group + iss_j);
+      const int tbase = iss_qt * kQStep;
+      st_q = (uint32_t)(((int64_t)tbase * a.q_st + (int64_t)head * a.q_sh) * 2);
+      st_do = (uint32_t)(((int64_t)tbase * a.do_st + (int64_t)head * a.do_sh) * 2);
+      st_l = ((uint32_t)head * (uint32_t)a.rows + (uint32_t)tbase) * 4u;
+    } else {
+      st_q = q_bytes;
+      st_do = do_bytes;
+      st_l = l_bytes;
     }
+    ++iss_it;
     if (++iss_j == a.group) {
       iss_j = 0;
       ++iss_qt;
     }
   };
-  auto stash = [&](auto bc) {
+  // staging load k (0..kDkvDma-1) of the current step into buffer B
+  auto stage_load = [&](auto bc, int k) {
     constexpr int B = decltype(bc)::value;
-    if (tid < kQStep) {
-      lse_s[B][tid] = lreg;
-      dsum_s[B][tid] = dsreg;
+    if (k < 2) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          q_res, (lds_void*)(sb + kDkvQ + B * kStepTile + (16 * k + 4 * wave) * kRowB), 16, q_loff,
+          st_q + 16u * (uint32_t)k * q_st_b, 0, 0);
+    } else if (k < 4) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          do_res, (lds_void*)(sb + kDkvO + B * kStepTile + (16 * (k - 2) + 4 * wave) * kRowB), 16,
+          do_loff, st_do + 16u * (uint32_t)(k - 2) * do_st_b, 0, 0);
+    } else if (k == 4) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(l_res, (lds_void*)(sb + kDkvL + B * 256), 4,
+                                               4 * lane, st_l, 0, 0);
+    } else {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(d_res, (lds_void*)(sb + kDkvD + B * 256), 4,
+                                               4 * lane, st_l, 0, 0);
     }
+  };
+  auto stage_all = [&](auto bc) {
+    stage_begin();
+#pragma unroll
+    for (int k = 0; k < kDkvDma; ++k) stage_load(bc, k);
   };
 
   const float c = a.scale_log2;
@@ -1228,119 +1267,211 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
     }
   fence_acc(dk, dv);
 
-  // P and dS element e = (kt, i) of the step in buffer B (C rows are queries
-  // 8 (i/4) + 4 h32 + i%4), packing each finished half into pb / db
-  auto pds_elem = [&](auto bc, auto ec, auto maskc, int t0, f32x16 (&s)[2], f32x16 (&dp)[2],
-                      f32x4& l4, f32x4& d4, bf16x8 (&pb)[2][2], bf16x8 (&db)[2][2]) {
-    constexpr int B = decltype(bc)::value;
+  // Per-lane elements of a step's 32 x 32 tiles (C layout): element (kt, i)
+  // is query row 8 (i / 4) + 4 h32 + i % 4 of the step, key kw0 + 32 kt + col.
+  f32x16 s[2], dp[2];          // S then P (fp32) / dP then dS of a step
+  bf16x8 pb[2][2], db[2][2];   // packed P and dS: [key tile][query half]
+  f32x4 l4, d4;
+
+  // P element e of the step whose LSE is in buffer BL (in place in s)
+  auto p_elem = [&](auto blc, auto ec) {
+    constexpr int BL = decltype(blc)::value;
     constexpr int e = decltype(ec)::value;
-    const bool masked = maskc;
     constexpr int kt = e >> 4, i = e & 15, jj = i >> 2, r = i & 3;
-    if constexpr (r == 0) {
-      l4 = *(const f32x4*)&lse_s[B][8 * jj + 4 * h32];
-      d4 = *(const f32x4*)&dsum_s[B][8 * jj + 4 * h32];
-    }
-    float p = fast_exp2(fmaf(s[kt][i], c, -l4[r]));
-    if (masked) {
-      const int tq = t0 + 8 * jj + 4 * h32 + r;
-      const int kk = kw0 + kt * 32 + col;
-      p = (kk <= tq && tq < kend_k[kt]) ? p : 0.f;
-    }
-    s[kt][i] = p;
-    dp[kt][i] = p * (dp[kt][i] - d4[r]);
+    if constexpr (r == 0) l4 = *(const lds_f32x4*)(sb + kDkvL + BL * 256 + 4 * (8 * jj + 4 * h32));
+    s[kt][i] = fast_exp2(fmaf(s[kt][i], c, -l4[r]));
+    // formed here, beside this step's products (not moved to its first use)
+    asm volatile("" : "+v"(s[kt][i]));
     if constexpr ((i & 7) == 7) {
       pb[kt][i >> 3] = pack_half(s[kt], i >> 3);
-      db[kt][i >> 3] = pack_half(dp[kt], i >> 3);
+      asm volatile("" : "+v"(pb[kt][i >> 3]));
     }
   };
-
-  // dV^T += dO^T P ; dK^T += Q^T dS for the step in buffer B, after P and dS
-  // are formed.  (Overlapping the two would need the VGPRs of a second set of
-  // P/dS fragments, which this wave does not have beside its K fragments.)
-  auto step_bwd = [&](auto bc, auto maskc, int t0, f32x16 (&s)[2], f32x16 (&dp)[2]) {
-    constexpr int B = decltype(bc)::value;
-    const lds_t* q_s = sb + kDkvQ + B * kStepTile;
-    const lds_t* d_s = sb + kDkvO + B * kStepTile;
-    bf16x8 pb[2][2], db[2][2];
-    f32x4 l4, d4;
-    static_for<0, 32>([&](auto ec) { pds_elem(bc, ec, maskc, t0, s, dp, l4, d4, pb, db); });
-    // transposed dO / Q fragments of pair pr = (hf, dt) in slot pr & 1,
-    // fetched one pair ahead
-    bf16x8 oa[2], qa[2];
-    oa[0] = ld_tr(d_s + f.tr(0, 0), d_s + f.tr(0, 1));
-    qa[0] = ld_tr(q_s + f.tr(0, 0), q_s + f.tr(0, 1));
-    static_for<0, 8>([&](auto prc) {
-      constexpr int pr = decltype(prc)::value;
-      constexpr int hf = pr >> 2, dt = pr & 3, sl = pr & 1;
-      if constexpr (pr + 1 < 8) {
-        constexpr int hn = (pr + 1) >> 2, dn = (pr + 1) & 3;
-        const lds_t* ob = d_s + hn * 16 * kRowB;
-        const lds_t* qb = q_s + hn * 16 * kRowB;
-        oa[sl ^ 1] = ld_tr(ob + f.tr(dn, 0), ob + f.tr(dn, 1));
-        qa[sl ^ 1] = ld_tr(qb + f.tr(dn, 0), qb + f.tr(dn, 1));
+  // dS element e of the step whose D is in buffer BD (in place in dp)
+  auto ds_elem = [&](auto bdc, auto ec) {
+    constexpr int BD = decltype(bdc)::value;
+    constexpr int e = decltype(ec)::value;
+    constexpr int kt = e >> 4, i = e & 15, jj = i >> 2, r = i & 3;
+    if constexpr (r == 0) d4 = *(const lds_f32x4*)(sb + kDkvD + BD * 256 + 4 * (8 * jj + 4 * h32));
+    dp[kt][i] = unpack_bf16(pb[kt][i >> 3], i & 7) * (dp[kt][i] - d4[r]);
+    asm volatile("" : "+v"(dp[kt][i]));
+    if constexpr ((i & 7) == 7) {
+      db[kt][i >> 3] = pack_half(dp[kt], i >> 3);
+      asm volatile("" : "+v"(db[kt][i >> 3]));
+    }
+  };
+  // invisible entries of a step's S (own keys) become -inf
+  auto mask_s = [&](int t0) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int kk = kw0 + kt * 32 + col;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int tq = t0 + 8 * (i >> 2) + 4 * h32 + (i & 3);
+        const bool vis = kk <= tq && tq < kend_k[kt];
+        s[kt][i] = vis ? s[kt][i] : -INFINITY;
       }
-      mfma_acc(dv[dt][0], oa[sl], pb[0][hf]);
-      mfma_acc(dv[dt][1], oa[sl], pb[1][hf]);
-      mfma_acc(dk[dt][0], qa[sl], db[0][hf]);
-      mfma_acc(dk[dt][1], qa[sl], db[1][hf]);
+    }
+  };
+  auto step_needs_mask = [&](int t0) {
+    return !ext && !(t0 >= wave_khi && t0 + kQStep - 1 < wave_kend_min);
+  };
+
+  // M1: S of the step in buffer BQ (Q fragments one d-step ahead), with the
+  // first half of the dS work of buffer BD and the staging of buffer BS
+  auto m1 = [&](auto bqc, auto bdc, auto bsc) {
+    constexpr int BQ = decltype(bqc)::value;
+    const lds_t* q_s = sb + kDkvQ + BQ * kStepTile;
+    bf16x8 qa[2];
+    qa[0] = ld_row8(q_s + f.row8(0));
+    s[0] = zero16();
+    s[1] = zero16();
+    static_for<0, kD / 16>([&](auto dsc) {
+      constexpr int ds = decltype(dsc)::value;
+      if constexpr (ds + 1 < kD / 16) qa[(ds + 1) & 1] = ld_row8(q_s + f.row8(ds + 1));
+      s[0] = mfma(qa[ds & 1], kf[0][ds], s[0]);
+      s[1] = mfma(qa[ds & 1], kf[1][ds], s[1]);
+      ds_elem(bdc, std::integral_constant<int, 2 * ds>());
+      ds_elem(bdc, std::integral_constant<int, 2 * ds + 1>());
+      if constexpr (ds < kDkvDma) stage_load(bsc, ds);
+      __builtin_amdgcn_sched_barrier(0);
     });
   };
-
-  // one query step in Q/dO buffer B: S, dP by MFMA, then P, dS and the dV/dK
-  // products; stages the next step into buffer B + 1
-  auto step = [&](auto bc, int it) {
+  // M2a: dV^T += dO^T P of buffer B (transposed dO fragments two ahead), with
+  // the second half of the dS work
+  auto m2a = [&](auto bc) {
     constexpr int B = decltype(bc)::value;
-    constexpr int BN = (B + 1) % 3;
-    const bool more = it + 1 < it_hi;
-    if (more) issue(Buf<BN>());
-    f.fresh();
-    asm volatile("" : "+v"(vrow0));
-    const int t0 = (qt_lo + it / a.group) * kQStep;
-    // skip steps none of the wave's keys is visible to (wave-uniform)
-    const bool live = ext || (t0 + kQStep - 1 >= wave_qlo && t0 < wave_kend_max);
-    if (live) {
-      f32x16 s[2], dp[2];
-      const lds_t* q_s = sb + kDkvQ + B * kStepTile;
-      const lds_t* d_s = sb + kDkvO + B * kStepTile;
-      // S = Q K^T and dP = dO V^T: 32 queries x the wave's 64 keys
-      s[0] = zero16(); s[1] = zero16(); dp[0] = zero16(); dp[1] = zero16();
+    const lds_t* d_s = sb + kDkvO + B * kStepTile;
+    auto ldo = [&](int pr) {
+      const lds_t* ob = d_s + (pr >> 2) * 16 * kRowB;
+      return ld_tr(ob + f.tr(pr & 3, 0), ob + f.tr(pr & 3, 1));
+    };
+    bf16x8 oa[3];
+    oa[0] = ldo(0);
+    oa[1] = ldo(1);
+    static_for<0, 8>([&](auto prc) {
+      constexpr int pr = decltype(prc)::value;
+      constexpr int hf = pr >> 2, dt = pr & 3;
+      if constexpr (pr + 2 < 8) oa[(pr + 2) % 3] = ldo(pr + 2);
+      mfma_acc(dv[dt][0], oa[pr % 3], pb[0][hf]);
+      mfma_acc(dv[dt][1], oa[pr % 3], pb[1][hf]);
+      ds_elem(bc, std::integral_constant<int, 16 + 2 * pr>());
+      ds_elem(bc, std::integral_constant<int, 17 + 2 * pr>());
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+  // M2b: dK^T += Q^T dS of buffer B, with the first half of the P work of
+  // buffer BL
+  auto m2b = [&](auto bc, auto blc) {
+    constexpr int B = decltype(bc)::value;
+    const lds_t* q_s = sb + kDkvQ + B * kStepTile;
+    auto ldq = [&](int pr) {
+      const lds_t* qb = q_s + (pr >> 2) * 16 * kRowB;
+      return ld_tr(qb + f.tr(pr & 3, 0), qb + f.tr(pr & 3, 1));
+    };
+    bf16x8 qa[3];
+    qa[0] = ldq(0);
+    qa[1] = ldq(1);
+    static_for<0, 8>([&](auto prc) {
+      constexpr int pr = decltype(prc)::value;
+      constexpr int hf = pr >> 2, dt = pr & 3;
+      if constexpr (pr + 2 < 8) qa[(pr + 2) % 3] = ldq(pr + 2);
+      mfma_acc(dk[dt][0], qa[pr % 3], db[0][hf]);
+      mfma_acc(dk[dt][1], qa[pr % 3], db[1][hf]);
+      p_elem(blc, std::integral_constant<int, 2 * pr>());
+      p_elem(blc, std::integral_constant<int, 2 * pr + 1>());
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+  // M3: dP of the step in buffer BQ (dO and V fragments one d-step ahead),
+  // with the second half of the P work
+  auto m3 = [&](auto bqc) {
+    constexpr int BQ = decltype(bqc)::value;
+    const lds_t* d_s = sb + kDkvO + BQ * kStepTile;
+    bf16x8 da[2], vb[2][2];
+    auto ld = [&](int ds, int sl) {
+      da[sl] = ld_row8(d_s + f.row8(ds));
 #pragma unroll
-      for (int ds = 0; ds < kD / 16; ++ds) {
-        const bf16x8 qa = ld_row8(q_s + f.row8(ds));
-        const bf16x8 da = ld_row8(d_s + f.row8(ds));
+      for (int kt = 0; kt < 2; ++kt)
+        vb[sl][kt] = ld_row8(sb + kt * 32 * kRowB + (vrow0 ^ (uint32_t)(ds << 5)));
+    };
+    ld(0, 0);
+    dp[0] = zero16();
+    dp[1] = zero16();
+    static_for<0, kD / 16>([&](auto dsc) {
+      constexpr int ds = decltype(dsc)::value;
+      if constexpr (ds + 1 < kD / 16) ld(ds + 1, (ds + 1) & 1);
+      dp[0] = mfma(da[ds & 1], vb[ds & 1][0], dp[0]);
+      dp[1] = mfma(da[ds & 1], vb[ds & 1][1], dp[1]);
+      p_elem(bqc, std::integral_constant<int, 16 + 2 * ds>());
+      p_elem(bqc, std::integral_constant<int, 17 + 2 * ds>());
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+  // S, P and dP of the step in buffer BQ without overlap (pipeline fill)
+  auto fill = [&](auto bqc, int t0) {
+    constexpr int BQ = decltype(bqc)::value;
+    const lds_t* q_s = sb + kDkvQ + BQ * kStepTile;
+    s[0] = zero16();
+    s[1] = zero16();
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          const bf16x8 vb = ld_row8(sb + kt * 32 * kRowB + (vrow0 ^ (uint32_t)(ds << 5)));
-          s[kt] = mfma(qa, kf[kt][ds], s[kt]);
-          dp[kt] = mfma(da, vb, dp[kt]);
-        }
-      }
-      // keep the fragment loads one d-step ahead of their products
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-      for (int ds = 0; ds < kD / 16; ++ds) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-        if (ds + 2 < kD / 16) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-      }
-      const bool need_mask = !ext && !(t0 >= wave_khi && t0 + kQStep - 1 < wave_kend_min);
-      step_bwd(bc, need_mask, t0, s, dp);
+    for (int ds = 0; ds < kD / 16; ++ds) {
+      const bf16x8 qa = ld_row8(q_s + f.row8(ds));
+      s[0] = mfma(qa, kf[0][ds], s[0]);
+      s[1] = mfma(qa, kf[1][ds], s[1]);
     }
-    if (more) stash(Buf<BN>());
-    dma_wait();
-    __syncthreads();
+    if (step_needs_mask(t0)) mask_s(t0);
+    static_for<0, 16>([&](auto ec) { p_elem(bqc, ec); });
+    m3(bqc);
   };
 
   if (it_lo < it_hi) {
-    issue(Buf<0>());
-    stash(Buf<0>());
+    stage_all(Buf<0>());
+    stage_all(Buf<1>());
+    stage_all(Buf<2>());
   }
   dma_wait();
   __syncthreads();
-  for (int it = it_lo; it < it_hi; it += 3) {
-    step(Buf<0>(), it);
-    if (it + 1 < it_hi) step(Buf<1>(), it + 1);
-    if (it + 2 < it_hi) step(Buf<2>(), it + 2);
+  if (it_lo < it_hi) {
+    // query tile of step t + 1, advanced per step
+    int nqt = qt_lo + it_lo / a.group, nj = it_lo % a.group;
+    fill(Buf<0>(), nqt * kQStep);
+    auto advance = [&]() {
+      if (++nj == a.group) {
+        nj = 0;
+        ++nqt;
+      }
+    };
+    advance();
+    // step t in buffer B: step t + 1 in B + 1, staging of step t + 3 into B + 3
+    auto iter = [&](auto bc) {
+      constexpr int B = decltype(bc)::value;
+      constexpr int B1 = (B + 1) % kDkvBufs, B3 = (B + 3) % kDkvBufs;
+      f.fresh();
+      asm volatile("" : "+v"(vrow0));
+      stage_begin();
+      m1(Buf<B1>(), bc, Buf<B3>());
+      m2a(bc);
+      const int t0n = nqt * kQStep;
+      if (step_needs_mask(t0n)) mask_s(t0n);
+      m2b(bc, Buf<B1>());
+      m3(Buf<B1>());
+      advance();
+      dma_wait_n<kDkvDma>();
+      lds_barrier();
+    };
+    for (int it = it_lo; it < it_hi; it += kDkvBufs) {
+      iter(Buf<0>());
+      if (it + 1 >= it_hi) break;
+      iter(Buf<1>());
+      if (it + 2 >= it_hi) break;
+      iter(Buf<2>());
+      if (it + 3 >= it_hi) break;
+      iter(Buf<3>());
+    }
   }
+  dma_wait();
+
   // lane holds key kw0 + 32 kt + col, d = 32 dt + 8 j + 4 h32 + r.  One
   // (key tile, d tile) at a time, so the epilogue reads 32 accumulators at once.
   fence_acc(dk, dv);
@@ -1404,8 +1535,6 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
 
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[kDkvBytes];
-  __shared__ __attribute__((aligned(16))) float lse_s[3][kQStep];
-  __shared__ __attribute__((aligned(16))) float dsum_s[3][kQStep];
   const int n_ext_kb = (a.n_ext + kKeysPerWg - 1) / kKeysPerWg;
   const int n_own_kb = (a.rows + kKeysPerWg - 1) / kKeysPerWg;
   const int items = n_ext_kb * a.n_chunks + n_own_kb * a.n_chunks_own;   // per KV head
@@ -1414,11 +1543,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(AttnArgs a) {
   if (g >= a.hkv) return;
   if (item < n_ext_kb * a.n_chunks) {
     const int kb = item / a.n_chunks;
-    dkv_block<true>(a, g, kb, item - kb * a.n_chunks, a.n_chunks, smem, lse_s, dsum_s);
+    dkv_block<true>(a, g, kb, item - kb * a.n_chunks, a.n_chunks, smem);
   } else {
     const int oi = item - n_ext_kb * a.n_chunks;
     const int kb = oi / a.n_chunks_own;
-    dkv_block<false>(a, g, kb, oi - kb * a.n_chunks_own, a.n_chunks_own, smem, lse_s, dsum_s);
+    dkv_block<false>(a, g, kb, oi - kb * a.n_chunks_own, a.n_chunks_own, smem);
   }
 }
 

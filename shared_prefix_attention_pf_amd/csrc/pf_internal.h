@@ -62,6 +62,8 @@ struct AttnArgs {
   void* out; int64_t out_st, out_sh;      // O (forward) or dQ (backward)
   float* lse;                             // [Hq, rows]
   float* dsum;                            // [Hq, rows] D = rowsum(dO * O), workspace
+  float* lse2;                            // [Hq, rows] LSE log2(e) (+inf for rows that see no key),
+                                          //   written by the dQ pass for the dK/dV pass, workspace
   // external keys (every query row sees all of them), [n_ext, Hkv, d]
   const void* k_ext; int64_t kx_st, kx_sh;
   const void* v_ext; int64_t vx_st, vx_sh;
