@@ -92,13 +92,24 @@ def check(lines):
     return bad
 
 
+def check_no_stack(lines):
+    """Kernels must keep everything in registers: a private segment means an
+    array was placed in scratch memory (a slow path inside the loops)."""
+    bad = []
+    for no, raw in enumerate(lines, 1):
+        m = re.match(r"\s*\.private_segment_fixed_size:\s+(\d+)", raw)
+        if m and int(m.group(1)) != 0:
+            bad.append((no, f"kernel uses {m.group(1)} bytes of scratch memory"))
+    return bad
+
+
 def main(argv):
     if len(argv) != 2:
         print(__doc__)
         return 2
     with open(argv[1]) as fh:
         lines = fh.readlines()
-    bad = check(lines)
+    bad = check(lines) + check_no_stack(lines)
     for no, msg in bad[:50]:
         print(f"{argv[1]}:{no}: {msg}")
     if bad:

@@ -53,7 +53,9 @@ def check_wait_states(cc: str, tmp: str, verbose: bool = False) -> None:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     with open(asm) as fh:
-        bad = asm_check.check(fh.readlines())
+        lines = fh.readlines()
+    bad = asm_check.check(lines)
+    bad += asm_check.check_no_stack(lines)
     if bad:
         for no, msg in bad[:20]:
             print(f"pf_attn_bf16.s:{no}: {msg}", file=sys.stderr)

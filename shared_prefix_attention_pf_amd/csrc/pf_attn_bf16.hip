@@ -838,18 +838,25 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(AttnArgs a) {
 // ---------------------------------------------------------------------------
 // Backward, Q-stationary: D and dQ.
 //
-// Software-pipelined like the forward: the MFMAs compute S^T and dP^T of key
-// block j + 1 while dS of block j is formed, then dQ^T += K_j^T dS_j^T.  Both
-// K and V of block j + 1 are needed one iteration ahead, and K of block j is
-// read again by the dQ product, so blocks rotate through three buffers.
+// Per key block j (32 keys): S^T = K Q^T and dP^T = V dO^T (matrix cores),
+// dS^T = P^T (dP^T - D) with P^T = exp2(S^T c - LSE log2 e) (VALU), and
+// dQ^T += K^T dS^T (matrix cores).  Software-pipelined in two phases:
+//   A  S^T, dP^T of block j + 1   with  dS of block j (first 22 values)
+//   B  dQ from block j - 1        with  dS of block j (last 10 values)
+// so the dQ product trails one block and both phases carry VALU work.  K/V
+// blocks rotate through five LDS buffers (block j - 1 is still read by phase
+// B while block j + 3 is staged); the buffer of a block is a runtime index.
 constexpr int kDqBN = 32;
 constexpr int kDqTile = kDqBN * kRowB;
-constexpr int kDqK = 0, kDqV = 3 * kDqTile;         // three K buffers, then three V buffers
+constexpr int kDqBufs = 5;
+constexpr int kDqK = 0, kDqV = kDqBufs * kDqTile;   // five K buffers, then five V buffers
+constexpr int kDqDma = 2 * (kDqBN / 16);            // staging loads per wave per block
+constexpr int kDqSplit = 22;                        // dS values formed in phase A
 
 __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(AttnArgs a) {
   constexpr int BN = kDqBN;
-  __shared__ __attribute__((aligned(16))) char smem[6 * kDqTile];
-  __shared__ __attribute__((aligned(16))) int32_t kend_s[3][BN];
+  __shared__ __attribute__((aligned(16))) char smem[2 * kDqBufs * kDqTile];
+  __shared__ __attribute__((aligned(16))) int32_t kend_s[kDqBufs][BN];
   lds_t* const sb = (lds_t*)smem;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -864,6 +871,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(AttnArgs a) {
   const int t0 = qt * tq;
   const int t1 = min(t0 + tq, a.rows);
 
+  // stationary Q and dO fragments (AGPRs), D = rowsum(dO * O) and LSE (log2)
+  // per query column; D and LSE (log2) are also written for the dK/dV pass
   QCol qc[2];
   bf16x8 qf[2][kD / 16], df[2][kD / 16];
   float lse2[2], dsum[2];
@@ -872,27 +881,43 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(AttnArgs a) {
     qc[nt] = qcol(a, g, t0, tq, wave * 64 + nt * 32 + col);
     const int64_t qo = (int64_t)qc[nt].tok * a.q_st + (int64_t)qc[nt].head * a.q_sh + 8 * h32;
     const int64_t doo = (int64_t)qc[nt].tok * a.do_st + (int64_t)qc[nt].head * a.do_sh + 8 * h32;
+#pragma unroll
+    for (int ds = 0; ds < kD / 16; ++ds) {
+      qf[nt][ds] = load8((const __bf16*)a.q + qo + ds * 16);          // row 0 if invalid
+      df[nt][ds] = load8((const __bf16*)a.dout + doo + ds * 16);
+    }
+  }
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
     const int64_t oo = (int64_t)qc[nt].tok * a.o_st + (int64_t)qc[nt].head * a.o_sh + 8 * h32;
     float dot = 0.f;
 #pragma unroll
     for (int ds = 0; ds < kD / 16; ++ds) {
-      qf[nt][ds] = qc[nt].valid ? load8((const __bf16*)a.q + qo + ds * 16) : zero8();
-      df[nt][ds] = qc[nt].valid ? load8((const __bf16*)a.dout + doo + ds * 16) : zero8();
-      const bf16x8 ov = qc[nt].valid ? load8((const __bf16*)a.o + oo + ds * 16) : zero8();
+      const bf16x8 ov = load8((const __bf16*)a.o + oo + ds * 16);
 #pragma unroll
       for (int e = 0; e < 8; ++e) dot = fmaf((float)df[nt][ds][e], (float)ov[e], dot);
-      pin_agpr(qf[nt][ds]);
-      pin_agpr(df[nt][ds]);
     }
-    dot += __shfl_xor(dot, 32);
+    dot = sum_halves(dot);
+    if (!qc[nt].valid) dot = 0.f;
     dsum[nt] = dot;
-    float l = qc[nt].valid ? a.lse[(int64_t)qc[nt].head * a.rows + qc[nt].tok] : 0.f;
+    const float l = qc[nt].valid ? a.lse[(int64_t)qc[nt].head * a.rows + qc[nt].tok] : 0.f;
     lse2[nt] = (l == -INFINITY) ? INFINITY : l * kLog2e;
     if (qc[nt].valid && h32 == 0) {
       a.dsum[(int64_t)qc[nt].head * a.rows + qc[nt].tok] = dot;
       a.lse2[(int64_t)qc[nt].head * a.rows + qc[nt].tok] = lse2[nt];
     }
   }
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int ds = 0; ds < kD / 16; ++ds) {
+      if (!qc[nt].valid) {
+        qf[nt][ds] = zero8();
+        df[nt][ds] = zero8();
+      }
+      pin_agpr(qf[nt][ds]);
+      pin_agpr(df[nt][ds]);
+    }
 
   KeyWalk<BN> walk;
   walk.n_ext_blocks = (a.n_ext + BN - 1) / BN;
@@ -904,9 +929,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(AttnArgs a) {
   BlockSrc<BN> src;
   src.init(a, g, walk.n_ext_blocks, wave, lane);
 
-  Frag f;
-  frag_init(f, lane);
-  int kendreg = -1;
+  FragC f;
+  {
+    Frag ff;
+    frag_init(ff, lane);
+    f.init(ff);
+  }
   const float c = a.scale_log2;
   f32x16 acc[kD / 32][2];
 #pragma unroll
@@ -915,142 +943,186 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(AttnArgs a) {
     for (int nt = 0; nt < 2; ++nt) acc[dt][nt] = zero16();
   fence_acc(acc);
 
-  // S^T = K Q^T and dP^T = V dO^T: 32 keys x 64 queries
-  auto sdp_tile = [&](const lds_t* kt_s, const lds_t* vt_s, f32x16 (&s)[2], f32x16 (&dp)[2]) {
-    s[0] = zero16(); s[1] = zero16(); dp[0] = zero16(); dp[1] = zero16();
-#pragma unroll
-    for (int ds = 0; ds < kD / 16; ++ds) {
-      const bf16x8 ka = ld_row8(kt_s + f.row8[ds]);
-      const bf16x8 va = ld_row8(vt_s + f.row8[ds]);
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        s[nt] = mfma(ka, qf[nt][ds], s[nt]);
-        dp[nt] = mfma(va, df[nt][ds], dp[nt]);
+  struct Blk {
+    int id;
+    bool masked;
+  };
+  auto blk = [&](int b) { return Blk{b, b >= 0 && walk.masked(b, a.n_ext)}; };
+  auto nxt = [&](Blk b) { return blk(b.id >= 0 ? walk.next(b.id + 1) : -1); };
+  // K and V of block b into buffer buf (a block that does not exist reads
+  // zeros: its rows are past the end of the resource)
+  auto stage = [&](Blk b, int buf) {
+    lds_t* kt_s = sb + kDqK + buf * kDqTile;
+    lds_t* vt_s = sb + kDqV + buf * kDqTile;
+    if (b.id >= 0) {
+      src.dma_k(b.id, kt_s, wave, lane);
+      src.dma_v(b.id, vt_s, wave, lane);
+      if (!src.ext(b.id) && wave == 0) {
+        const int k0 = src.k0(b.id);
+        const __amdgpu_buffer_rsrc_t res = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(a.ri.kend + k0), (short)0, 4 * (a.rows - k0), 0x00020000);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(res, (lds_void*)&kend_s[buf][0], 4, 4 * lane, 0,
+                                                 0, 0);
       }
+    } else {
+      src.kx.stage<BN>(a.n_ext + BN, kt_s, wave);
+      src.vx.stage<BN>(a.n_ext + BN, vt_s, wave);
     }
   };
-  // invisible entries of block b's S^T get -inf (so P^T = 0)
-  auto mask_if = [&](f32x16 (&s)[2], int b, const int32_t* kend) {
-    if (!walk.masked(b, a.n_ext)) return;
-    const bool ext = src.ext(b);
-    const int k0 = src.k0(b);
-    const int klim = ext ? a.n_ext : a.rows;
+
+  // per-lane elements: (nt, i) is query column nt, key 8 (i / 4) + 4 h32 + i % 4
+  f32x16 sA[1][2], dpA[2], sB[1][2], dpB[2];   // S^T as one key tile for mask_st
+  bf16x8 dsA[2][2], dsB[2][2];    // packed dS^T [column][key half]
+  // S^T, dP^T of the block in buffer buf into (s, dp); fragments one d-step
+  // ahead; `work(ds)` is VALU work placed beside d-step ds
+  auto sdp = [&](int buf, f32x16 (&s)[1][2], f32x16 (&dp)[2], auto&& work) {
+    const uint32_t kb = f.row8_0 + kDqK + buf * kDqTile;
+    const uint32_t vb = f.row8_0 + kDqV + buf * kDqTile;
+    bf16x8 ka[2], va[2];
+    ka[0] = ld_row8(sb + kb);
+    va[0] = ld_row8(sb + vb);
+    s[0][0] = zero16(); s[0][1] = zero16(); dp[0] = zero16(); dp[1] = zero16();
+    static_for<0, kD / 16>([&](auto dsc) {
+      constexpr int ds = decltype(dsc)::value;
+      if constexpr (ds + 1 < kD / 16) {
+        ka[(ds + 1) & 1] = ld_row8(sb + (kb ^ (uint32_t)((ds + 1) << 5)));
+        va[(ds + 1) & 1] = ld_row8(sb + (vb ^ (uint32_t)((ds + 1) << 5)));
+      }
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        s[0][nt] = mfma(ka[ds & 1], qf[nt][ds], s[0][nt]);
+        dp[nt] = mfma(va[ds & 1], df[nt][ds], dp[nt]);
+      }
+      work(dsc);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+  // dS value e (0..31) of (s, dp) into ds; e = 16 nt + i
+  auto ds_elem = [&](f32x16 (&s)[1][2], f32x16 (&dp)[2], bf16x8 (&dsb)[2][2], auto ec) {
+    constexpr int e = decltype(ec)::value;
+    constexpr int nt = e >> 4, i = e & 15;
+    const float p = fast_exp2(fmaf(s[0][nt][i], c, -lse2[nt]));
+    s[0][nt][i] = p * (dp[nt][i] - dsum[nt]);
+    asm volatile("" : "+v"(s[0][nt][i]));
+    if constexpr ((i & 7) == 7) {
+      dsb[nt][i >> 3] = pack_half(s[0][nt], i >> 3);
+      asm volatile("" : "+v"(dsb[nt][i >> 3]));
+    }
+  };
+  // dQ^T += K^T dS^T for the block whose K is in buffer buf (transposed K
+  // fragments two ahead), with `work(k)` beside product pair k
+  auto dq_prod = [&](int buf, const bf16x8 (&dsb)[2][2], auto&& work) {
+    const uint32_t t0b = f.tr0[0] + kDqK + buf * kDqTile;
+    const uint32_t t1b = f.tr0[1] + kDqK + buf * kDqTile;
+    auto ldk = [&](int k) {
+      const int dt = k >> 1, ks = k & 1;
+      const uint32_t o = ks * 16 * kRowB;
+      return ld_tr(sb + (t0b ^ (uint32_t)(dt << 6)) + o, sb + (t1b ^ (uint32_t)(dt << 6)) + o);
+    };
+    bf16x8 kfr[3];
+    kfr[0] = ldk(0);
+    kfr[1] = ldk(1);
+    static_for<0, 2 * kD / 32>([&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      constexpr int dt = k >> 1, ks = k & 1;
+      if constexpr (k + 2 < 2 * kD / 32) kfr[(k + 2) % 3] = ldk(k + 2);
+      mfma_acc(acc[dt][0], kfr[k % 3], dsb[0][ks]);
+      mfma_acc(acc[dt][1], kfr[k % 3], dsb[1][ks]);
+      work(kc);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
+  // prologue: blocks 0..2 staged into buffers 0..2, zeros into buffer 4 (the
+  // "block -1" whose dQ product the first iteration runs, with dS = 0)
+  const Blk b0 = blk(walk.next(0));
+  const Blk b1 = nxt(b0);
+  const Blk b2 = nxt(b1);
+  stage(b0, 0);
+  stage(b1, 1);
+  stage(b2, 2);
+  stage(Blk{-1, false}, kDqBufs - 1);
+  dma_wait();
+  __syncthreads();
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int k = 0; k < 2; ++k) dsB[nt][k] = zero8();
+  if (b0.id >= 0) {
+    sdp(0, sA, dpA, [&](auto) {});
+    if (b0.masked)
+      mask_st<BN>(sA, src.ext(b0.id), src.k0(b0.id),
+                  src.ext(b0.id) ? a.n_ext : a.rows, kend_s[0], qc[0].tok, qc[1].tok, h32);
+  }
+
+  // iteration for block j in buffer bj with (sc, dpc) = its S^T, dP^T and
+  // (sn, dpn) receiving block j + 1's; dsp holds dS of block j - 1 (buffer
+  // bp), dsc receives block j's.  Stages block j + 3.
+  auto iter = [&](f32x16 (&sc)[1][2], f32x16 (&dpc)[2], f32x16 (&sn)[1][2], f32x16 (&dpn)[2],
+                  bf16x8 (&dsc)[2][2], const bf16x8 (&dsp)[2][2], int bj, Blk n1, Blk n3) {
+    const int b1i = bj + 1 == kDqBufs ? 0 : bj + 1;
+    const int b3i = bj + 3 >= kDqBufs ? bj + 3 - kDqBufs : bj + 3;
+    const int bpi = bj == 0 ? kDqBufs - 1 : bj - 1;
+    f.fresh();
+    stage(n3, b3i);
+    // phase A
+    sdp(b1i, sn, dpn, [&](auto dsc_) {
+      constexpr int ds = decltype(dsc_)::value;
+      static_for<0, 3>([&](auto uc) {
+        constexpr int e = 3 * ds + decltype(uc)::value;
+        if constexpr (e < kDqSplit) ds_elem(sc, dpc, dsc, std::integral_constant<int, e>());
+      });
+    });
+    if (n1.masked)
+      mask_st<BN>(sn, src.ext(n1.id), src.k0(n1.id),
+                  src.ext(n1.id) ? a.n_ext : a.rows, kend_s[b1i], qc[0].tok, qc[1].tok, h32);
+    // phase B
+    dq_prod(bpi, dsp, [&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      static_for<0, 2>([&](auto uc) {
+        constexpr int e = kDqSplit + 2 * k + decltype(uc)::value;
+        if constexpr (e < 32) ds_elem(sc, dpc, dsc, std::integral_constant<int, e>());
+      });
+    });
+    // every iteration stages kDqDma tile loads per wave (zeros for a block
+    // that does not exist), and wave 0 one kend load for an own block; at
+    // most kDqDma outstanding means every load of earlier iterations landed
+    dma_wait_n<kDqDma>();
+    lds_barrier();
+  };
+
+  Blk cur = b0, n1 = b1, n2 = b2;
+  int bj = 0, last = 0;
+  bool last_in_a = true;   // whether the last block's dS went to dsA
+  while (cur.id >= 0) {
+    Blk n3 = nxt(n2);
+    iter(sA, dpA, sB, dpB, dsA, dsB, bj, n1, n3);
+    last = bj;
+    last_in_a = true;
+    bj = bj + 1 == kDqBufs ? 0 : bj + 1;
+    cur = n1; n1 = n2; n2 = n3;
+    if (cur.id < 0) break;
+    n3 = nxt(n2);
+    iter(sB, dpB, sA, dpA, dsB, dsA, bj, n1, n3);
+    last = bj;
+    last_in_a = false;
+    bj = bj + 1 == kDqBufs ? 0 : bj + 1;
+    cur = n1; n1 = n2; n2 = n3;
+  }
+  // the dQ product of the last block (one call site: the accumulators must
+  // not be merged from two paths, which would copy them right after a product)
+  if (b0.id >= 0) {
+    bf16x8 dsl[2][2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int kl = 8 * (i >> 2) + 4 * h32 + (i & 3);
-        const int kk = k0 + kl;
-        const int ke = ext ? 0x7fffffff : kend[kl];
-        const bool vis = kk < klim && (ext || (kk <= qc[nt].tok && qc[nt].tok < ke));
-        s[nt][i] = vis ? s[nt][i] : -INFINITY;
+      for (int k = 0; k < 2; ++k) {
+        // select values, not array addresses (which would put both arrays in memory)
+        bf16x8 xa = dsA[nt][k], xb = dsB[nt][k];
+        asm volatile("" : "+v"(xa), "+v"(xb));
+        dsl[nt][k] = last_in_a ? xa : xb;
       }
-  };
-  // dS^T = P^T * (dP^T - D), with P^T = exp2(S^T c - LSE log2 e)
-  auto ds_tile = [&](f32x16 (&s)[2], const f32x16 (&dp)[2], bf16x8 (&dsb)[2][2]) {
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = fast_exp2(fmaf(s[nt][i], c, -lse2[nt]));
-        s[nt][i] = p * (dp[nt][i] - dsum[nt]);
-      }
-      dsb[nt][0] = pack_half(s[nt], 0);
-      dsb[nt][1] = pack_half(s[nt], 1);
-    }
-  };
-
-  // prologue: blocks 0 and 1 staged; S, dP of block 0
-  const int b0 = walk.next(0);
-  const int b1 = b0 >= 0 ? walk.next(b0 + 1) : -1;
-  f32x16 sA[2], dpA[2], sB[2], dpB[2];
-  if (b0 >= 0) {
-    src.dma_k(b0, sb + kDqK, wave, lane);
-    src.dma_v(b0, sb + kDqV, wave, lane);
-    kendreg = load_kend<BN>(a, src, b0, tid);
-    if (tid < BN) kend_s[0][tid] = kendreg;
-    if (b1 >= 0) {
-      src.dma_k(b1, sb + kDqK + kDqTile, wave, lane);
-      src.dma_v(b1, sb + kDqV + kDqTile, wave, lane);
-      kendreg = load_kend<BN>(a, src, b1, tid);
-      if (tid < BN) kend_s[1][tid] = kendreg;
-    }
-  }
-  dma_wait();
-  __syncthreads();
-  if (b0 >= 0) {
-    sdp_tile(sb + kDqK, sb + kDqV, sA, dpA);
-    mask_if(sA, b0, kend_s[0]);
-  }
-
-  // iteration for block cur in buffer B, nx1 in buffer (B + 1) % 3; stages
-  // nx2 into buffer (B + 2) % 3, last read by the previous iteration.  The
-  // current block's S/dP are in (sc, dpc); the next block's go to (sn, dpn).
-  auto iter = [&](auto bc, f32x16 (&sc)[2], f32x16 (&dpc)[2], f32x16 (&sn)[2],
-                  f32x16 (&dpn)[2], int nx1, int nx2) {
-    constexpr int B = decltype(bc)::value;
-    constexpr int B1 = (B + 1) % 3, B2 = (B + 2) % 3;
-    if (nx2 >= 0) {
-      src.dma_k(nx2, sb + kDqK + B2 * kDqTile, wave, lane);
-      src.dma_v(nx2, sb + kDqV + B2 * kDqTile, wave, lane);
-      kendreg = load_kend<BN>(a, src, nx2, tid);
-    }
-    // S^T, dP^T of the next block (MFMA) while dS^T of this block is formed
-    sdp_tile(sb + kDqK + B1 * kDqTile, sb + kDqV + B1 * kDqTile, sn, dpn);
-    bf16x8 dsb[2][2];
-    ds_tile(sc, dpc, dsb);
-    // interleave: LDS fragment reads run four MFMA pairs ahead
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // two MFMAs
-      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // five VALU
-      if (i < 12) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
-    }
-    // dQ^T += K^T dS^T
-    const lds_t* kt_s = sb + kDqK + B * kDqTile;
-    static_for<0, kD / 32>([&](auto dtc) {
-      constexpr int dt = decltype(dtc)::value;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const lds_t* kb = kt_s + ks * 16 * kRowB;
-        const bf16x8 af = ld_tr(kb + f.tr[dt][0], kb + f.tr[dt][1]);
-        mfma_acc(acc[dt][0], af, dsb[0][ks]);
-        mfma_acc(acc[dt][1], af, dsb[1][ks]);
-      }
-    });
-    if (nx1 >= 0) mask_if(sn, nx1, kend_s[B1]);
-    if (nx2 >= 0 && tid < BN) kend_s[B2][tid] = kendreg;
-    dma_wait();
-    __syncthreads();
-  };
-
-  // blocks rotate through 3 LDS buffers and 2 register sets: unroll by 6
-  int cur = b0, nx1 = b1;
-  while (cur >= 0) {
-    int nx2 = nx1 >= 0 ? walk.next(nx1 + 1) : -1;
-    iter(Buf<0>(), sA, dpA, sB, dpB, nx1, nx2);
-    cur = nx1; nx1 = nx2;
-    if (cur < 0) break;
-    nx2 = nx1 >= 0 ? walk.next(nx1 + 1) : -1;
-    iter(Buf<1>(), sB, dpB, sA, dpA, nx1, nx2);
-    cur = nx1; nx1 = nx2;
-    if (cur < 0) break;
-    nx2 = nx1 >= 0 ? walk.next(nx1 + 1) : -1;
-    iter(Buf<2>(), sA, dpA, sB, dpB, nx1, nx2);
-    cur = nx1; nx1 = nx2;
-    if (cur < 0) break;
-    nx2 = nx1 >= 0 ? walk.next(nx1 + 1) : -1;
-    iter(Buf<0>(), sB, dpB, sA, dpA, nx1, nx2);
-    cur = nx1; nx1 = nx2;
-    if (cur < 0) break;
-    nx2 = nx1 >= 0 ? walk.next(nx1 + 1) : -1;
-    iter(Buf<1>(), sA, dpA, sB, dpB, nx1, nx2);
-    cur = nx1; nx1 = nx2;
-    if (cur < 0) break;
-    nx2 = nx1 >= 0 ? walk.next(nx1 + 1) : -1;
-    iter(Buf<2>(), sB, dpB, sA, dpA, nx1, nx2);
-    cur = nx1; nx1 = nx2;
+    dq_prod(last, dsl, [&](auto) {});
   }
 
   fence_acc(acc);
