@@ -1,0 +1,206 @@
+"""GPU parity at the full measured sizes.
+
+The GPU runs each workload exactly as the benchmark times it: the 32/8-head
+group at P = 4096 with all 8 suffixes in one Phase-B call (config 2), the
+64-suffix group at P = 8192 in 8 microbatch calls (config 4), the RAG-shaped
+varlen group at P = 16384 in 4 calls (config 3) and the 12288-row rollout tree
+(config 5).  The fp64 oracle then recomputes whole KV-head groups (every
+query head that reads the chosen KV head, every row) and each output slice is
+compared normwise against it (2e-2, the bf16 bar).  Heads are independent, so
+a KV-head group is an exact sub-problem of the full call.
+
+Invariants checked at full size, where the oracle cannot cover every head:
+the prefix-side gradient of a call is the same whichever microbatch split
+produced it (up to fp32 summation order), and the outputs are finite.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_util import TOL, check, dev, host
+from workloads import generate, get_config
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import shared_prefix_attention_pf_amd as pf
+    from shared_prefix_attention_pf_amd import group as G
+
+
+def _heads_of(cfg, g):
+    gs = cfg.group_size
+    return slice(g * gs, (g + 1) * gs)
+
+
+def _phase_b(cfg, data, desc, calls):
+    """Phase B as `calls` consecutive calls (lists of (first, last) suffixes),
+    accumulating gK/gV.  Returns per-row outputs and the accumulators."""
+    p, cu = cfg.prefix_len, data["cu_seqlens"]
+    t = {k: dev(data[k], cfg.dtype) for k in ("k_p", "v_p", "q_s", "k_s", "v_s", "do_s")}
+    rows = int(cu[-1])
+    out = {"o": torch.empty_like(t["q_s"]), "dq": torch.empty_like(t["q_s"]),
+           "dk": torch.empty_like(t["k_s"]), "dv": torch.empty_like(t["v_s"]),
+           "lse": torch.empty(cfg.num_q_heads, rows, device="cuda")}
+    gk = torch.zeros(p, cfg.num_kv_heads, cfg.head_dim, device="cuda")
+    gv = torch.zeros_like(gk)
+    for a, b in calls:
+        r0, r1 = int(cu[a]), int(cu[b])
+        sub = (cu[a:b + 1] - cu[a]).astype(np.int32)
+        sl = slice(r0, r1)
+        o, lse = G.suffix_fwd(desc, t["k_p"], t["v_p"], sub, t["q_s"][sl], t["k_s"][sl],
+                              t["v_s"][sl])
+        dq, dk, dv = G.suffix_bwd(desc, t["k_p"], t["v_p"], sub, t["q_s"][sl], t["k_s"][sl],
+                                  t["v_s"][sl], o, lse, t["do_s"][sl], gk, gv)
+        out["o"][sl], out["lse"][:, sl] = o, lse
+        out["dq"][sl], out["dk"][sl], out["dv"][sl] = dq, dk, dv
+    torch.cuda.synchronize()
+    res = {k: host(v) for k, v in out.items()}
+    res["gk"], res["gv"] = host(gk), host(gv)
+    return res
+
+
+def _check_phase_b_group(cfg, data, res, g):
+    hs = _heads_of(cfg, g)
+    scale = 1.0 / math.sqrt(cfg.head_dim)
+    hmap = np.zeros(cfg.group_size, dtype=np.int64)
+    print(f"  oracle Phase B, KV head {g}", flush=True)
+    ref = oracle.suffix_attention(data["k_p"][:, g:g + 1], data["v_p"][:, g:g + 1],
+                                  data["q_s"][:, hs], data["k_s"][:, g:g + 1],
+                                  data["v_s"][:, g:g + 1], data["do_s"][:, hs],
+                                  data["cu_seqlens"], scale, hmap)
+    tol = TOL[cfg.dtype]
+    check(f"O_S[g{g}]", res["o"][:, hs], ref["o_s"], tol)
+    check(f"LSE_S[g{g}]", res["lse"][hs], ref["lse_s"], tol)
+    check(f"dQ_S[g{g}]", res["dq"][:, hs], ref["dq_s"], tol)
+    check(f"dK_S[g{g}]", res["dk"][:, g:g + 1], ref["dk_s"], tol)
+    check(f"dV_S[g{g}]", res["dv"][:, g:g + 1], ref["dv_s"], tol)
+    check(f"gK[g{g}]", res["gk"][:, g:g + 1], ref["gk"], tol)
+    check(f"gV[g{g}]", res["gv"][:, g:g + 1], ref["gv"], tol)
+    return ref
+
+
+def _desc(cfg):
+    return pf.AttnDesc(cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, pf.PF_BF16)
+
+
+def test_config2_all_phases_full_size():
+    """Phase A, one Phase-B call over all 8 suffixes, Phase C with the
+    accumulated gK/gV injected: the benchmark's step at config 2."""
+    cfg = get_config(2)
+    print(f"\ngenerating config {cfg.cid}", flush=True)
+    data = generate(cfg)
+    desc = _desc(cfg)
+    n = cfg.n_suffix
+    res = _phase_b(cfg, data, desc, [(0, n)])
+    # Phase A and Phase C on the GPU, C with the GPU's accumulators
+    q_p, k_p, v_p, do_p = (dev(data[k], cfg.dtype) for k in ("q_p", "k_p", "v_p", "do_p"))
+    o_p, lse_p = G.prefix_fwd(desc, q_p, k_p, v_p)
+    gk = torch.from_numpy(res["gk"].astype(np.float32)).cuda()
+    gv = torch.from_numpy(res["gv"].astype(np.float32)).cuda()
+    dq_p, dk_p, dv_p = G.prefix_bwd(desc, q_p, k_p, v_p, o_p, lse_p, do_p, gk, gv)
+    torch.cuda.synchronize()
+    o_p, lse_p, dq_p, dk_p, dv_p = (host(x) for x in (o_p, lse_p, dq_p, dk_p, dv_p))
+    for x in (res["o"], res["dq"], res["dk"], res["dv"], res["gk"], o_p, dq_p, dk_p, dv_p):
+        assert np.all(np.isfinite(x))
+    scale = 1.0 / math.sqrt(cfg.head_dim)
+    hmap = np.zeros(cfg.group_size, dtype=np.int64)
+    tol = TOL[cfg.dtype]
+    for g in (0, 5):
+        ref_b = _check_phase_b_group(cfg, data, res, g)
+        hs = _heads_of(cfg, g)
+        print(f"  oracle Phase A/C, KV head {g}", flush=True)
+        ro, rl = oracle.prefix_forward(data["q_p"][:, hs], data["k_p"][:, g:g + 1],
+                                       data["v_p"][:, g:g + 1], scale, hmap)
+        check(f"O_P[g{g}]", o_p[:, hs], ro, tol)
+        check(f"LSE_P[g{g}]", lse_p[hs], rl, tol)
+        rdq, rdk, rdv = oracle.prefix_backward_inject(
+            data["q_p"][:, hs], data["k_p"][:, g:g + 1], data["v_p"][:, g:g + 1],
+            data["do_p"][:, hs], ref_b["gk"], ref_b["gv"], scale, hmap)
+        check(f"dQ_P[g{g}]", dq_p[:, hs], rdq, tol)
+        check(f"dK_P[g{g}]", dk_p[:, g:g + 1], rdk, tol)
+        check(f"dV_P[g{g}]", dv_p[:, g:g + 1], rdv, tol)
+
+
+def test_config4_microbatches_full_size():
+    """Phase B of 64 suffixes at P = 8192 as 8 calls of 8 (the benchmark's
+    split): oracle on one KV-head group, and the accumulated gK/gV of a
+    different split (2 calls of 32) agree to fp32 summation order."""
+    cfg = get_config(4)
+    print(f"\ngenerating config {cfg.cid}", flush=True)
+    data = generate(cfg)
+    desc = _desc(cfg)
+    calls = [tuple(int(x) for x in mb) for mb in data["microbatches"]]
+    res = _phase_b(cfg, data, desc, calls)
+    _check_phase_b_group(cfg, data, res, 3)
+    res2 = _phase_b(cfg, data, desc, [(0, 32), (32, 64)])
+    for name in ("gk", "gv"):
+        rel = np.abs(res2[name] - res[name]).max() / np.abs(res[name]).max()
+        print(f"  {name}: split 8x8 vs 2x32 max rel diff {rel:.2e}", flush=True)
+        assert rel < 1e-5
+    for name in ("o", "dq", "dk", "dv"):
+        assert np.array_equal(res[name], res2[name]), f"{name} depends on the split"
+
+
+def test_config3_varlen_full_size():
+    """Phase B of the RAG-shaped group (P = 16384, 16 varlen suffixes, 4
+    calls).  The oracle recomputes two whole suffixes (the shortest and the
+    longest) for one KV-head group: their rows' O, LSE, dQ and their own
+    keys' dK, dV depend only on their own trajectories."""
+    cfg = get_config(3)
+    print(f"\ngenerating config {cfg.cid}", flush=True)
+    data = generate(cfg, include_prefix_q=False)
+    desc = _desc(cfg)
+    calls = [tuple(int(x) for x in mb) for mb in data["microbatches"]]
+    res = _phase_b(cfg, data, desc, calls)
+    cu = data["cu_seqlens"]
+    lens = np.diff(cu)
+    g = 6
+    hs = _heads_of(cfg, g)
+    scale = 1.0 / math.sqrt(cfg.head_dim)
+    hmap = np.zeros(cfg.group_size, dtype=np.int64)
+    tol = TOL[cfg.dtype]
+    for i in (int(np.argmin(lens)), int(np.argmax(lens))):
+        a, b = int(cu[i]), int(cu[i + 1])
+        print(f"  oracle suffix {i} ({b - a} rows), KV head {g}", flush=True)
+        sub = np.asarray([0, b - a], dtype=np.int32)
+        ref = oracle.suffix_attention(data["k_p"][:, g:g + 1], data["v_p"][:, g:g + 1],
+                                      data["q_s"][a:b, hs], data["k_s"][a:b, g:g + 1],
+                                      data["v_s"][a:b, g:g + 1], data["do_s"][a:b, hs], sub,
+                                      scale, hmap)
+        check(f"O_S[s{i}]", res["o"][a:b, hs], ref["o_s"], tol)
+        check(f"LSE_S[s{i}]", res["lse"][hs, a:b], ref["lse_s"], tol)
+        check(f"dQ_S[s{i}]", res["dq"][a:b, hs], ref["dq_s"], tol)
+        check(f"dK_S[s{i}]", res["dk"][a:b, g:g + 1], ref["dk_s"], tol)
+        check(f"dV_S[s{i}]", res["dv"][a:b, g:g + 1], ref["dv_s"], tol)
+
+
+def test_config5_tree_full_size():
+    """The 12288-row rollout tree, forward and backward in one call each:
+    oracle (ancestor mask over the compact rows) on one KV-head group."""
+    cfg = get_config(5)
+    print(f"\ngenerating config {cfg.cid}", flush=True)
+    data = generate(cfg)
+    desc = _desc(cfg)
+    node_off, parent = data["node_off"], data["parent"]
+    q, k, v, do = (dev(data[n], cfg.dtype) for n in ("q", "k", "v", "do"))
+    o, lse = G.tree_fwd(desc, node_off, parent, q, k, v)
+    dq, dk, dv = G.tree_bwd(desc, node_off, parent, q, k, v, o, lse, do)
+    torch.cuda.synchronize()
+    o, lse, dq, dk, dv = (host(x) for x in (o, lse, dq, dk, dv))
+    g = 2
+    hs = _heads_of(cfg, g)
+    scale = 1.0 / math.sqrt(cfg.head_dim)
+    hmap = np.zeros(cfg.group_size, dtype=np.int64)
+    print(f"  oracle tree, KV head {g}", flush=True)
+    ref = oracle.tree_attention_direct(data["q"][:, hs], data["k"][:, g:g + 1],
+                                       data["v"][:, g:g + 1], data["do"][:, hs], node_off, parent,
+                                       scale, hmap)
+    tol = TOL[cfg.dtype]
+    check("O", o[:, hs], ref["o"], tol)
+    check("LSE", lse[hs], ref["lse"], tol)
+    check("dQ", dq[:, hs], ref["dq"], tol)
+    check("dK", dk[:, g:g + 1], ref["dk"], tol)
+    check("dV", dv[:, g:g + 1], ref["dv"], tol)
