@@ -23,7 +23,7 @@ PF_F32, PF_BF16 = 0, 1
 PF_MAX_SEGMENTS = 256
 
 EXPORTED = (
-    "pf_workspace_size", "pf_prefix_fwd", "pf_suffix_attn_fwd", "pf_suffix_attn_bwd_accum",
+    "pf_workspace_size", "pf_workspace_size_min", "pf_prefix_fwd", "pf_suffix_attn_fwd", "pf_suffix_attn_bwd_accum",
     "pf_prefix_bwd_inject", "pf_tree_attn_fwd", "pf_tree_attn_bwd", "pf_tree_subtree_end",
     "pf_status_string", "pf_last_error", "pf_abi_version", "pf_set_launch_hook",
 )
@@ -70,6 +70,7 @@ def _load():
     ip = ctypes.POINTER(ctypes.c_int32)
     sigs = {
         "pf_workspace_size": (sz, [i32, D, i32, i32]),
+        "pf_workspace_size_min": (sz, [i32, D, i32, i32]),
         "pf_prefix_fwd": (i32, [D, i32, T, T, T, T, fp, P, sz, P]),
         "pf_suffix_attn_fwd": (i32, [D, i32, T, T, i32, ip, T, T, T, T, fp, P, sz, P]),
         "pf_suffix_attn_bwd_accum": (i32, [D, i32, T, T, i32, ip, T, T, T, T, fp, T, T, T, T,
@@ -171,6 +172,11 @@ def pf_abi_version() -> int:
 def pf_workspace_size(op: int, desc: AttnDesc, prefix_len: int, rows: int) -> int:
     d, _keep = desc._c()
     return int(_lib.pf_workspace_size(op, ctypes.byref(d), prefix_len, rows))
+
+
+def pf_workspace_size_min(op: int, desc: AttnDesc, prefix_len: int, rows: int) -> int:
+    d, _keep = desc._c()
+    return int(_lib.pf_workspace_size_min(op, ctypes.byref(d), prefix_len, rows))
 
 
 def pf_tree_subtree_end(node_off, parent) -> np.ndarray:

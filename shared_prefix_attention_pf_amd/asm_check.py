@@ -92,6 +92,25 @@ def check(lines):
     return bad
 
 
+def check_m0(lines):
+    """M0 is set by the inline-asm staging loads right before they use it;
+    any other instruction touching M0 could see or clobber that value."""
+    bad = []
+    in_asm = False
+    for no, raw in enumerate(lines, 1):
+        st = raw.strip()
+        if st.startswith(";;#ASMSTART"):
+            in_asm = True
+            continue
+        if st.startswith(";;#ASMEND"):
+            in_asm = False
+            continue
+        code = st.split(";")[0]
+        if not in_asm and re.search(r"\bm0\b", code):
+            bad.append((no, f"'{code.strip()}' uses M0 outside an inline-asm staging load"))
+    return bad
+
+
 def check_no_stack(lines):
     """Kernels must keep everything in registers: a private segment means an
     array was placed in scratch memory (a slow path inside the loops)."""
@@ -109,7 +128,7 @@ def main(argv):
         return 2
     with open(argv[1]) as fh:
         lines = fh.readlines()
-    bad = check(lines) + check_no_stack(lines)
+    bad = check(lines) + check_no_stack(lines) + check_m0(lines)
     for no, msg in bad[:50]:
         print(f"{argv[1]}:{no}: {msg}")
     if bad:

@@ -56,6 +56,7 @@ def check_wait_states(cc: str, tmp: str, verbose: bool = False) -> None:
         lines = fh.readlines()
     bad = asm_check.check(lines)
     bad += asm_check.check_no_stack(lines)
+    bad += asm_check.check_m0(lines)
     if bad:
         for no, msg in bad[:20]:
             print(f"pf_attn_bf16.s:{no}: {msg}", file=sys.stderr)

@@ -157,9 +157,22 @@ struct WsLayout {
   size_t total = 0;
   size_t dk_part = 0, dv_part = 0;
   int32_t n_chunks = 1, n_chunks_own = 1;
+  // Phase-B dS buffer of the external keys and the fp32 dQ part they give
+  bool use_ds = false;
+  size_t ds_ext = 0, dq_part = 0;
+  int32_t ds_keys = 0, ds_rows = 0;
 };
 
-WsLayout layout(int32_t op, const Desc& d, int32_t n_ext, int32_t rows) {
+// Phase B keeps dS^T of the external keys when the workspace allows it: the
+// buffer holds Hq x ceil256(P) x ceil256(rows) bf16 values (one head's share
+// must stay below 2 GiB for 32-bit buffer offsets).
+bool ds_eligible(int32_t op, const Desc& d, int32_t n_ext, int32_t rows) {
+  if (op != PF_OP_SUFFIX_BWD || d.dtype != PF_BF16 || n_ext <= 0 || rows <= 0) return false;
+  const int64_t keys = (n_ext + 255) / 256 * 256, r = ((int64_t)rows + 255) / 256 * 256;
+  return keys * r * 2 < ((int64_t)1 << 31);
+}
+
+WsLayout layout(int32_t op, const Desc& d, int32_t n_ext, int32_t rows, bool want_ds = false) {
   WsLayout w;
   size_t off = 0;
   const size_t nb = (size_t)((rows + 31) / 32);
@@ -189,6 +202,15 @@ WsLayout layout(int32_t op, const Desc& d, int32_t n_ext, int32_t rows) {
       w.dk_part = off; off += align_up(part);
       w.dv_part = off; off += align_up(part);
     }
+  }
+  if (want_ds && ds_eligible(op, d, n_ext, rows)) {
+    w.use_ds = true;
+    w.ds_keys = (n_ext + 255) / 256 * 256;
+    w.ds_rows = (rows + 255) / 256 * 256;
+    w.ds_ext = off;
+    off += align_up((size_t)d.hq * w.ds_keys * w.ds_rows * 2);
+    w.dq_part = off;
+    off += align_up((size_t)rows * d.hq * d.d * 4);
   }
   w.total = rows > 0 ? off : 0;
   return w;
@@ -285,10 +307,23 @@ pf_status run_fwd(const Desc& d, const pf::AttnArgs& a, const pf::SegTable& seg,
 pf_status run_bwd(const Desc& d, const pf::AttnArgs& a, const pf::SegTable& seg, hipStream_t st) {
   hipError_t e = pf::launch_prep(seg, d.heads, a.ri, st);
   if (e != hipSuccess) return hip_fail(e, "prep");
-  e = d.dtype == PF_BF16 ? pf::launch_bwd_dq_bf16(a, d.d, st) : pf::launch_bwd_dq_f32(a, d.d, st);
-  if (e != hipSuccess) return hip_fail(e, "dq");
-  e = d.dtype == PF_BF16 ? pf::launch_bwd_dkv_bf16(a, d.d, st) : pf::launch_bwd_dkv_f32(a, d.d, st);
-  if (e != hipSuccess) return hip_fail(e, "dkv");
+  if (a.ds_ext) {
+    // D and LSE first; the dK/dV pass stores dS^T of the external keys, the
+    // external part of dQ is read from it, then the dQ pass adds the own keys
+    e = pf::launch_dsum_bf16(a, st);
+    if (e != hipSuccess) return hip_fail(e, "dsum");
+    e = pf::launch_bwd_dkv_bf16(a, d.d, st);
+    if (e != hipSuccess) return hip_fail(e, "dkv");
+    e = pf::launch_bwd_dq_ext_bf16(a, d.d, st);
+    if (e != hipSuccess) return hip_fail(e, "dq_ext");
+    e = pf::launch_bwd_dq_bf16(a, d.d, st);
+    if (e != hipSuccess) return hip_fail(e, "dq");
+  } else {
+    e = d.dtype == PF_BF16 ? pf::launch_bwd_dq_bf16(a, d.d, st) : pf::launch_bwd_dq_f32(a, d.d, st);
+    if (e != hipSuccess) return hip_fail(e, "dq");
+    e = d.dtype == PF_BF16 ? pf::launch_bwd_dkv_bf16(a, d.d, st) : pf::launch_bwd_dkv_f32(a, d.d, st);
+    if (e != hipSuccess) return hip_fail(e, "dkv");
+  }
   if (a.n_chunks > 1 && a.n_ext > 0) {
     const int64_t n = (int64_t)a.n_ext * d.hkv * d.d;
     e = pf::launch_reduce_partials(a.gk_part, a.gk_acc, a.n_chunks, n, st);
@@ -380,7 +415,17 @@ size_t pf_workspace_size(int32_t op, const pf_attn_desc* desc, int32_t prefix_le
   if (op == PF_OP_PREFIX_FWD || op == PF_OP_PREFIX_BWD) rows = prefix_len;
   const int32_t n_ext = (op == PF_OP_SUFFIX_FWD || op == PF_OP_SUFFIX_BWD) ? prefix_len : 0;
   if (op < PF_OP_PREFIX_FWD || op > PF_OP_TREE_BWD) return 0;
-  return layout(op, d, n_ext, rows).total;
+  return layout(op, d, n_ext, rows, true).total;
+}
+
+size_t pf_workspace_size_min(int32_t op, const pf_attn_desc* desc, int32_t prefix_len,
+                             int32_t rows) {
+  Desc d;
+  if (check_desc(desc, &d) != PF_OK || rows < 0 || prefix_len < 0) return 0;
+  if (op == PF_OP_PREFIX_FWD || op == PF_OP_PREFIX_BWD) rows = prefix_len;
+  const int32_t n_ext = (op == PF_OP_SUFFIX_FWD || op == PF_OP_SUFFIX_BWD) ? prefix_len : 0;
+  if (op < PF_OP_PREFIX_FWD || op > PF_OP_TREE_BWD) return 0;
+  return layout(op, d, n_ext, rows, false).total;
 }
 
 pf_status pf_tree_subtree_end(int32_t n_nodes, const int32_t* node_off, const int32_t* parent,
@@ -474,8 +519,10 @@ pf_status pf_suffix_attn_bwd_accum(const pf_attn_desc* desc, int32_t prefix_len,
     if ((s = check_ptr("gk_acc", gk_acc, 16)) != PF_OK) return s;
     if ((s = check_ptr("gv_acc", gv_acc, 16)) != PF_OK) return s;
   }
-  const WsLayout w = layout(PF_OP_SUFFIX_BWD, d, prefix_len, rows);
-  if ((s = check_stream_ws(workspace, workspace_bytes, w.total)) != PF_OK) return s;
+  const WsLayout w_min = layout(PF_OP_SUFFIX_BWD, d, prefix_len, rows, false);
+  if ((s = check_stream_ws(workspace, workspace_bytes, w_min.total)) != PF_OK) return s;
+  const WsLayout w_ds = layout(PF_OP_SUFFIX_BWD, d, prefix_len, rows, true);
+  const WsLayout& w = (w_ds.use_ds && workspace_bytes >= w_ds.total) ? w_ds : w_min;
   if (rows == 0) return PF_OK;
   pf::AttnArgs a = base_args(d, rows);
   set_q(a, q_s);
@@ -496,6 +543,12 @@ pf_status pf_suffix_attn_bwd_accum(const pf_attn_desc* desc, int32_t prefix_len,
   }
   a.dsum = (float*)((char*)workspace + w.dsum);
   a.lse2 = (float*)((char*)workspace + w.lse2);
+  if (w.use_ds) {
+    a.ds_ext = (__bf16*)((char*)workspace + w.ds_ext);
+    a.ds_keys = w.ds_keys;
+    a.ds_rows = w.ds_rows;
+    a.dq_part = (float*)((char*)workspace + w.dq_part);
+  }
   set_own_parts(a, workspace, w);
   a.ri = row_info(workspace, w);
   return run_bwd(d, a, flat_segments(n_suffix, cu_seqlens), (hipStream_t)stream);

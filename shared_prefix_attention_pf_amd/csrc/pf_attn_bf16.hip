@@ -221,13 +221,47 @@ __device__ __forceinline__ void static_for(F&& f) {
 // rows per instruction, lane l landing at byte 16 l of them: lane l of wave w
 // fetches the logical chunk (l & 15) ^ swz(r) of row r = 4 w + l / 16 (plus 16
 // rows per further pass), which puts every chunk at its swizzled position.
+//
+// The loads are issued from inline asm.  The compiler treats a staging load
+// as a write to any LDS address, so it would wait for every staging load in
+// flight before the next LDS read, which defeats staging ahead; here every
+// wait is explicit (dma_wait*).  The statement sets M0 (the LDS base of the
+// load) itself; the build checks that no other instruction reads or writes
+// M0.  Resources are plain SGPR quads: base, stride 0, size in bytes, and
+// the raw-buffer format word.
 typedef __attribute__((address_space(3))) void lds_void;
+typedef u32x4 Rsrc;
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, int nvalid,
-                                                           uint32_t st_b) {
-  const uint32_t bytes = nvalid > 0 ? (uint32_t)(nvalid - 1) * st_b + kRowB : 0u;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           0x00020000);
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t p = (uint64_t)(uintptr_t)base;
+  Rsrc r;
+  r[0] = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32) & 0xffffu);
+  r[2] = __builtin_amdgcn_readfirstlane(bytes);
+  r[3] = 0x00020000u;
+  return r;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const lds_t* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
+}
+
+// 16 bytes per lane into dst + 16 lane
+__device__ __forceinline__ void lds_dma16(Rsrc r, const lds_t* dst, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(lds_addr(dst)), "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(soff))
+               : "memory");
+}
+
+// 4 bytes per lane into dst + 4 lane
+__device__ __forceinline__ void lds_dma4(Rsrc r, const lds_t* dst, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :: "s"(lds_addr(dst)), "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(soff))
+               : "memory");
+}
+
+__device__ __forceinline__ Rsrc row_rsrc(const void* base, int nvalid, uint32_t st_b) {
+  return make_rsrc(base, nvalid > 0 ? (uint32_t)(nvalid - 1) * st_b + kRowB : 0u);
 }
 
 __device__ __forceinline__ uint32_t dma_lane_off(int wave, int lane, uint32_t st_b) {
@@ -237,12 +271,11 @@ __device__ __forceinline__ uint32_t dma_lane_off(int wave, int lane, uint32_t st
 
 // ROWS rows (a multiple of 16) into `tile`, issued by every wave of the group
 template <int ROWS>
-__device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t res, uint32_t lane_off,
-                                         uint32_t st_b, lds_t* tile, int wave) {
+__device__ __forceinline__ void dma_rows(Rsrc res, uint32_t lane_off, uint32_t st_b, lds_t* tile,
+                                         int wave) {
 #pragma unroll
   for (int i = 0; i < ROWS / 16; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(res, (lds_void*)(tile + (16 * i + 4 * wave) * kRowB),
-                                             16, lane_off, i * 16 * st_b, 0, 0);
+    lds_dma16(res, tile + (16 * i + 4 * wave) * kRowB, lane_off, i * 16 * st_b);
 }
 
 // completes this wave's staging loads (a barrier then publishes them)
@@ -346,7 +379,7 @@ struct KeyWalk {
 // the last one read zero.  Built once per workgroup; staging a block is then
 // scalar arithmetic plus the loads.
 struct RowSrc {
-  __amdgpu_buffer_rsrc_t res;
+  Rsrc res;
   uint32_t st_b;       // bytes per row
   uint32_t lane_off;   // this lane's byte offset within a 4-row pass
   __device__ void init(const void* base, int nrows, int64_t st_elems, int wave, int lane) {
@@ -359,8 +392,7 @@ struct RowSrc {
   __device__ void stage(int r0, lds_t* tile, int wave) const {
 #pragma unroll
     for (int i = 0; i < ROWS / 16; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(res, (lds_void*)(tile + (16 * i + 4 * wave) * kRowB),
-                                               16, lane_off, (uint32_t)(r0 + 16 * i) * st_b, 0, 0);
+      lds_dma16(res, tile + (16 * i + 4 * wave) * kRowB, lane_off, (uint32_t)(r0 + 16 * i) * st_b);
   }
 };
 
@@ -623,10 +655,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(AttnArgs a) {
   auto stage_kend = [&](int b, int buf) {
     if (src.ext(b) || wave != 0) return;
     const int k0 = src.k0(b);
-    const __amdgpu_buffer_rsrc_t res = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(a.ri.kend + k0), (short)0, 4 * (a.rows - k0), 0x00020000);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(res, (lds_void*)&kend_s[buf][0], 4, 4 * lane, 0, 0,
-                                             0);
+    lds_dma4(make_rsrc(a.ri.kend + k0, 4u * (uint32_t)(a.rows - k0)), (const lds_t*)&kend_s[buf][0],
+             4u * lane, 0u);
   };
 
   // prologue: K and V of blocks 0 and 1, K of block 2; S of block 0
@@ -887,24 +917,34 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(AttnArgs a) {
       df[nt][ds] = load8((const __bf16*)a.dout + doo + ds * 16);
     }
   }
+  if (a.dq_part) {
+    // D and LSE (log2) were formed by the pre-pass
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int64_t oo = (int64_t)qc[nt].tok * a.o_st + (int64_t)qc[nt].head * a.o_sh + 8 * h32;
-    float dot = 0.f;
-#pragma unroll
-    for (int ds = 0; ds < kD / 16; ++ds) {
-      const bf16x8 ov = load8((const __bf16*)a.o + oo + ds * 16);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) dot = fmaf((float)df[nt][ds][e], (float)ov[e], dot);
+    for (int nt = 0; nt < 2; ++nt) {
+      const int64_t ix = (int64_t)qc[nt].head * a.rows + qc[nt].tok;
+      dsum[nt] = qc[nt].valid ? a.dsum[ix] : 0.f;
+      lse2[nt] = qc[nt].valid ? a.lse2[ix] : INFINITY;
     }
-    dot = sum_halves(dot);
-    if (!qc[nt].valid) dot = 0.f;
-    dsum[nt] = dot;
-    const float l = qc[nt].valid ? a.lse[(int64_t)qc[nt].head * a.rows + qc[nt].tok] : 0.f;
-    lse2[nt] = (l == -INFINITY) ? INFINITY : l * kLog2e;
-    if (qc[nt].valid && h32 == 0) {
-      a.dsum[(int64_t)qc[nt].head * a.rows + qc[nt].tok] = dot;
-      a.lse2[(int64_t)qc[nt].head * a.rows + qc[nt].tok] = lse2[nt];
+  } else {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int64_t oo = (int64_t)qc[nt].tok * a.o_st + (int64_t)qc[nt].head * a.o_sh + 8 * h32;
+      float dot = 0.f;
+#pragma unroll
+      for (int ds = 0; ds < kD / 16; ++ds) {
+        const bf16x8 ov = load8((const __bf16*)a.o + oo + ds * 16);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dot = fmaf((float)df[nt][ds][e], (float)ov[e], dot);
+      }
+      dot = sum_halves(dot);
+      if (!qc[nt].valid) dot = 0.f;
+      dsum[nt] = dot;
+      const float l = qc[nt].valid ? a.lse[(int64_t)qc[nt].head * a.rows + qc[nt].tok] : 0.f;
+      lse2[nt] = (l == -INFINITY) ? INFINITY : l * kLog2e;
+      if (qc[nt].valid && h32 == 0) {
+        a.dsum[(int64_t)qc[nt].head * a.rows + qc[nt].tok] = dot;
+        a.lse2[(int64_t)qc[nt].head * a.rows + qc[nt].tok] = lse2[nt];
+      }
     }
   }
 #pragma unroll
@@ -959,10 +999,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(AttnArgs a) {
       src.dma_v(b.id, vt_s, wave, lane);
       if (!src.ext(b.id) && wave == 0) {
         const int k0 = src.k0(b.id);
-        const __amdgpu_buffer_rsrc_t res = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(a.ri.kend + k0), (short)0, 4 * (a.rows - k0), 0x00020000);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(res, (lds_void*)&kend_s[buf][0], 4, 4 * lane, 0,
-                                                 0, 0);
+        lds_dma4(make_rsrc(a.ri.kend + k0, 4u * (uint32_t)(a.rows - k0)),
+                 (const lds_t*)&kend_s[buf][0], 4u * lane, 0u);
       }
     } else {
       src.kx.stage<BN>(a.n_ext + BN, kt_s, wave);
@@ -1035,7 +1073,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(AttnArgs a) {
 
   // prologue: blocks 0..2 staged into buffers 0..2, zeros into buffer 4 (the
   // "block -1" whose dQ product the first iteration runs, with dS = 0)
-  const Blk b0 = blk(walk.next(0));
+  // with a dS buffer the external keys' part of dQ is already in dq_part
+  const Blk b0 = blk(walk.next(a.dq_part ? walk.n_ext_blocks : 0));
   const Blk b1 = nxt(b0);
   const Blk b2 = nxt(b1);
   stage(b0, 0);
@@ -1130,14 +1169,166 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(AttnArgs a) {
   for (int nt = 0; nt < 2; ++nt) {
     if (!qc[nt].valid) continue;
     __bf16* op = (__bf16*)a.out + (int64_t)qc[nt].tok * a.out_st + (int64_t)qc[nt].head * a.out_sh;
+    const float* pp = a.dq_part ? a.dq_part + ((int64_t)qc[nt].tok * a.hq + qc[nt].head) * kD : nullptr;
 #pragma unroll
     for (int dt = 0; dt < kD / 32; ++dt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
+        const f32x4 pv = pp ? *(const f32x4*)(pp + dt * 32 + 8 * j + 4 * h32) : f32x4{0.f, 0.f, 0.f, 0.f};
         bf16x4 w;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) w[r] = (__bf16)(acc[dt][nt][4 * j + r] * a.scale);
+        for (int r = 0; r < 4; ++r) w[r] = (__bf16)((acc[dt][nt][4 * j + r] + pv[r]) * a.scale);
         *(bf16x4*)(op + dt * 32 + 8 * j + 4 * h32) = w;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Backward, dQ from the stored dS^T of the external keys (Phase B).
+//
+// dQ^T [d x q] += K^T [d x k] dS^T [k x q] over the external keys, with both
+// operands read from memory: the K rows of the KV head and the dS^T rows the
+// dK/dV pass stored (so S and dP are not computed a second time).  A
+// workgroup owns 256 tokens of one query head, 64 per wave as two 32-column
+// tiles; per block of 32 keys it stages K (32 x 256 B) and dS^T (32 keys x
+// 256 tokens, as two 128-token tiles) and each wave runs 16 products.  Two
+// workgroups share a CU (72 KiB of LDS each), so more staging is in flight.  The
+// result is fp32 and unscaled; the dQ pass adds the own keys' part to it.
+// Within each 32-token group the dS^T columns are in the dK/dV pass's register
+// order: column p holds row 16 (p / 16) + 8 ((p % 8) / 4) + 4 ((p / 8) % 2) + p % 4.
+constexpr int kDsStep = 32;                       // query rows per stored dS^T step
+constexpr int kDxBN = 32;
+constexpr int kDxTok = 256;
+constexpr int kDxTile = kDxBN * kRowB;
+constexpr int kDxBufBytes = 3 * kDxTile;          // K tile, then two dS^T tiles
+constexpr int kDxBufs = 3;
+constexpr int kDxDma = 3 * (kDxBN / 16);          // staging loads per wave per block
+
+__device__ __forceinline__ int ds_col_row(int p) {
+  return 16 * (p >> 4) + 8 * ((p & 7) >> 2) + 4 * ((p >> 3) & 1) + (p & 3);
+}
+
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq_ext_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[kDxBufs * kDxBufBytes];
+  lds_t* const sb = (lds_t*)smem;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int col = lane & 31, h32 = lane >> 5;
+  const int n_tt = (a.rows + kDxTok - 1) / kDxTok;
+  int g, item;
+  map_block(blockIdx.x, a.hkv, a.group * n_tt, g, item);
+  if (g >= a.hkv) return;
+  const int j = item / n_tt, tt = item - j * n_tt;
+  const int head = ld_uniform(a.ri.qhead, g * a.group + j);
+  const int t0 = tt * kDxTok;
+  const int n_blk = (a.n_ext + kDxBN - 1) / kDxBN;
+
+  // staging sources: K rows of KV head g, and dS^T of this head for the
+  // tile's 8 steps of 32 tokens (64 bytes per key and step, keys contiguous
+  // within a step).  LDS dS^T tile d (0, 1) is [64 keys][128 tokens] with
+  // 256-byte rows: logical chunk c of row r is positions 8 (c % 4) .. of step
+  // 4 d + c / 4.  Each lane's chunk and row within a staging pass are fixed,
+  // so its offset is fixed; the key block and the pass move the scalar offset.
+  RowSrc ksrc;
+  ksrc.init((const __bf16*)a.k_ext + (int64_t)g * a.kx_sh, a.n_ext, a.kx_st, wave, lane);
+  const int64_t n_steps = a.ds_rows / kDsStep;
+  const __bf16* dbase = a.ds_ext + ((int64_t)head * n_steps + t0 / kDsStep) * a.ds_keys * kDsStep;
+  const Rsrc dres = make_rsrc(dbase, 8u * (uint32_t)a.ds_keys * kDsStep * 2u);
+  uint32_t d_loff;
+  {
+    const int r = 4 * wave + (lane >> 4);
+    const int lc = (lane & 15) ^ (int)swz(r);
+    d_loff = (uint32_t)(((lc >> 2) * a.ds_keys + r) * kDsStep + 8 * (lc & 3)) * 2u;
+  }
+  auto stage = [&](int b, int buf) {
+    lds_t* base = sb + buf * kDxBufBytes;
+    const int k0 = b < n_blk ? b * kDxBN : a.ds_keys;   // past the end: not consumed
+    ksrc.stage<kDxBN>(k0, base, wave);
+#pragma unroll
+    for (int d = 0; d < 2; ++d)
+#pragma unroll
+      for (int i = 0; i < kDxBN / 16; ++i)
+        lds_dma16(dres, base + (1 + d) * kDxTile + (16 * i + 4 * wave) * kRowB, d_loff,
+                  (uint32_t)((4 * d * a.ds_keys + k0 + 16 * i) * kDsStep * 2));
+  };
+
+  FragC f;
+  {
+    Frag ff;
+    frag_init(ff, lane);
+    f.init(ff);
+  }
+  f32x16 acc[kD / 32][2];
+#pragma unroll
+  for (int dt = 0; dt < kD / 32; ++dt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) acc[dt][nt] = zero16();
+  fence_acc(acc);
+
+  // this wave's dS^T tile and its two column tiles in it
+  const int dtile = 1 + (wave >> 1);
+  const int ct0 = 2 * (wave & 1);
+  stage(0, 0);
+  stage(1, 1);
+  dma_wait();
+  __syncthreads();
+  for (int b = 0; b < n_blk; ++b) {
+    const int buf = b % kDxBufs;
+    const int nbuf = (b + 2) % kDxBufs;
+    f.fresh();
+    stage(b + 2, nbuf);
+    const lds_t* kt_s = sb + buf * kDxBufBytes;
+    const lds_t* ds_s = kt_s + dtile * kDxTile;
+    // per 16-key slice: two dS^T fragments (B, one per column tile) and four
+    // K^T fragments (A, one per d tile), fetched one slice ahead
+    auto ldb = [&](int ks, int nt) {
+      const lds_t* p = ds_s + ks * 16 * kRowB;
+      return ld_tr(p + f.tr(ct0 + nt, 0), p + f.tr(ct0 + nt, 1));
+    };
+    auto lda = [&](int ks, int dt) {
+      const lds_t* p = kt_s + ks * 16 * kRowB;
+      return ld_tr(p + f.tr(dt, 0), p + f.tr(dt, 1));
+    };
+    bf16x8 bf[2][2], af[2][kD / 32];
+    bf[0][0] = ldb(0, 0);
+    bf[0][1] = ldb(0, 1);
+#pragma unroll
+    for (int dt = 0; dt < kD / 32; ++dt) af[0][dt] = lda(0, dt);
+    static_for<0, kDxBN / 16>([&](auto ksc) {
+      constexpr int ks = decltype(ksc)::value;
+      constexpr int cs = ks & 1, ns = cs ^ 1;
+      if constexpr (ks + 1 < kDxBN / 16) {
+        bf[ns][0] = ldb(ks + 1, 0);
+        bf[ns][1] = ldb(ks + 1, 1);
+#pragma unroll
+        for (int dt = 0; dt < kD / 32; ++dt) af[ns][dt] = lda(ks + 1, dt);
+      }
+      static_for<0, kD / 32>([&](auto dtc) {
+        constexpr int dt = decltype(dtc)::value;
+        mfma_acc(acc[dt][0], af[cs][dt], bf[cs][0]);
+        mfma_acc(acc[dt][1], af[cs][dt], bf[cs][1]);
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    dma_wait_n<kDxDma>();
+    lds_barrier();
+  }
+  dma_wait();
+
+  fence_acc(acc);
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int tok = t0 + 128 * (wave >> 1) + 32 * (ct0 + nt) + ds_col_row(col);
+    if (tok >= a.rows) continue;
+    float* op = a.dq_part + ((int64_t)tok * a.hq + head) * kD;
+#pragma unroll
+    for (int dt = 0; dt < kD / 32; ++dt)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        f32x4 w;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) w[r] = acc[dt][nt][4 * jj + r];
+        *(f32x4*)(op + dt * 32 + 8 * jj + 4 * h32) = w;
       }
   }
 }
@@ -1166,6 +1357,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(AttnArgs a) {
 // through four LDS buffers; step t + 3 is staged during step t, one staging
 // load per M1 product pair.
 constexpr int kQStep = 32;
+static_assert(kQStep == kDsStep, "the dS^T store and the dQ pass share the step");
 constexpr int kKeysPerWave = 64;
 constexpr int kKeysPerWg = 4 * kKeysPerWave;
 constexpr int kStepTile = kQStep * kRowB;
@@ -1275,10 +1467,10 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
   const uint32_t q_bytes = (uint32_t)(((int64_t)(a.rows - 1) * a.q_st + (int64_t)(a.hq - 1) * a.q_sh) * 2 + kRowB);
   const uint32_t do_bytes = (uint32_t)(((int64_t)(a.rows - 1) * a.do_st + (int64_t)(a.hq - 1) * a.do_sh) * 2 + kRowB);
   const uint32_t l_bytes = (uint32_t)a.hq * (uint32_t)a.rows * 4u;
-  const __amdgpu_buffer_rsrc_t q_res = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.q), (short)0, (int)q_bytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t do_res = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.dout), (short)0, (int)do_bytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t l_res = __builtin_amdgcn_make_buffer_rsrc((void*)a.lse2, (short)0, (int)l_bytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t d_res = __builtin_amdgcn_make_buffer_rsrc((void*)a.dsum, (short)0, (int)l_bytes, 0x00020000);
+  const Rsrc q_res = make_rsrc(a.q, q_bytes);
+  const Rsrc do_res = make_rsrc(a.dout, do_bytes);
+  const Rsrc l_res = make_rsrc(a.lse2, l_bytes);
+  const Rsrc d_res = make_rsrc(a.dsum, l_bytes);
   const uint32_t q_loff = dma_lane_off(wave, lane, q_st_b);
   const uint32_t do_loff = dma_lane_off(wave, lane, do_st_b);
 
@@ -1307,19 +1499,15 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
   auto stage_load = [&](auto bc, int k) {
     constexpr int B = decltype(bc)::value;
     if (k < 2) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          q_res, (lds_void*)(sb + kDkvQ + B * kStepTile + (16 * k + 4 * wave) * kRowB), 16, q_loff,
-          st_q + 16u * (uint32_t)k * q_st_b, 0, 0);
+      lds_dma16(q_res, sb + kDkvQ + B * kStepTile + (16 * k + 4 * wave) * kRowB, q_loff,
+                st_q + 16u * (uint32_t)k * q_st_b);
     } else if (k < 4) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          do_res, (lds_void*)(sb + kDkvO + B * kStepTile + (16 * (k - 2) + 4 * wave) * kRowB), 16,
-          do_loff, st_do + 16u * (uint32_t)(k - 2) * do_st_b, 0, 0);
+      lds_dma16(do_res, sb + kDkvO + B * kStepTile + (16 * (k - 2) + 4 * wave) * kRowB, do_loff,
+                st_do + 16u * (uint32_t)(k - 2) * do_st_b);
     } else if (k == 4) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(l_res, (lds_void*)(sb + kDkvL + B * 256), 4,
-                                               4 * lane, st_l, 0, 0);
+      lds_dma4(l_res, sb + kDkvL + B * 256, 4u * lane, st_l);
     } else {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(d_res, (lds_void*)(sb + kDkvD + B * 256), 4,
-                                               4 * lane, st_l, 0, 0);
+      lds_dma4(d_res, sb + kDkvD + B * 256, 4u * lane, st_l);
     }
   };
   auto stage_all = [&](auto bc) {
@@ -1434,7 +1622,7 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
   };
   // M2b: dK^T += Q^T dS of buffer B, with the first half of the P work of
   // buffer BL
-  auto m2b = [&](auto bc, auto blc) {
+  auto m2b = [&](auto bc, auto blc, __bf16* ds_dst) {
     constexpr int B = decltype(bc)::value;
     const lds_t* q_s = sb + kDkvQ + B * kStepTile;
     auto ldq = [&](int pr) {
@@ -1452,6 +1640,11 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
       mfma_acc(dk[dt][1], qa[pr % 3], db[1][hf]);
       p_elem(blc, std::integral_constant<int, 2 * pr>());
       p_elem(blc, std::integral_constant<int, 2 * pr + 1>());
+      if constexpr (EXT && pr < 4) {
+        // dS^T of this step for the dQ pass: key tile pr / 2, query half pr % 2
+        if (ds_dst)
+          *(bf16x8*)(ds_dst + (pr >> 1) * 32 * kQStep + 16 * (pr & 1)) = db[pr >> 1][pr & 1];
+      }
       __builtin_amdgcn_sched_barrier(0);
     });
   };
@@ -1507,6 +1700,7 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
   if (it_lo < it_hi) {
     // query tile of step t + 1, advanced per step
     int nqt = qt_lo + it_lo / a.group, nj = it_lo % a.group;
+    int cqt = nqt, cj = nj;   // step t
     fill(Buf<0>(), nqt * kQStep);
     auto advance = [&]() {
       if (++nj == a.group) {
@@ -1526,10 +1720,27 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
       m2a(bc);
       const int t0n = nqt * kQStep;
       if (step_needs_mask(t0n)) mask_s(t0n);
-      m2b(bc, Buf<B1>());
+      // this lane's dS^T destination for step t: key kw0 + col (+32 per key
+      // tile), positions 8 h32 .. 8 h32 + 7 of each 16-position half of the
+      // step's 32 values (64 contiguous bytes per key and step)
+      __bf16* ds_dst = nullptr;
+      if (EXT && a.ds_ext) {
+        const int head = ld_uniform(a.ri.qhead, g * a.group + cj);
+        const int64_t n_steps = a.ds_rows / kQStep;
+        ds_dst = a.ds_ext + (((int64_t)head * n_steps + cqt) * a.ds_keys + kw0 + col) * kQStep +
+                 8 * h32;
+      }
+      m2b(bc, Buf<B1>(), ds_dst);
       m3(Buf<B1>());
+      cqt = nqt;
+      cj = nj;
       advance();
-      dma_wait_n<kDkvDma>();
+      // the vector memory counter also counts the dS^T stores issued after
+      // this iteration's staging loads: leave both in flight
+      if (ds_dst)
+        dma_wait_n<kDkvDma + 4>();
+      else
+        dma_wait_n<kDkvDma>();
       lds_barrier();
     };
     for (int it = it_lo; it < it_hi; it += kDkvBufs) {
@@ -1658,6 +1869,15 @@ hipError_t launch_bwd_dkv_bf16(const AttnArgs& a, int32_t head_dim, hipStream_t 
   if (items <= 0) return hipSuccess;
   PF_LAUNCH("pf_bwd_dkv_bf16", bwd_dkv_kernel, dim3(grid_for(a.hkv, items)), dim3(kThreads),
             stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq_ext_bf16(const AttnArgs& a, int32_t head_dim, hipStream_t stream) {
+  if (head_dim != kD) return hipErrorInvalidValue;
+  if (a.rows <= 0 || a.n_ext <= 0) return hipSuccess;
+  const int n_tt = (a.rows + kDxTok - 1) / kDxTok;
+  PF_LAUNCH("pf_bwd_dq_ext_bf16", bwd_dq_ext_kernel, dim3(grid_for(a.hkv, a.group * n_tt)),
+            dim3(kThreads), stream, a);
   return hipGetLastError();
 }
 

@@ -85,6 +85,13 @@ struct AttnArgs {
   // chunks: fp32 [n_chunks_own, rows, Hkv, d], finished by launch_finish_own
   float* dk_part; float* dv_part;
   int32_t n_chunks_own;
+  // Phase B with a dS buffer: the dK/dV pass stores dS^T of the external
+  // keys (bf16 [Hq, ds_keys, ds_rows]; within each 32-row group the rows are
+  // in the order the dK/dV pass holds them, see kernels), a separate pass
+  // forms their part of dQ into dq_part (fp32 [rows, Hq, d], unscaled) and
+  // the dQ pass then covers own keys only and adds dq_part.
+  __bf16* ds_ext; int32_t ds_keys, ds_rows;
+  float* dq_part;
   RowInfo ri;
   int32_t rows;
   int32_t hq, hkv, group;                 // group = Hq / Hkv
@@ -104,6 +111,9 @@ void launch_hook(const char* kernel, hipStream_t stream, int end);
 
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_prep(const SegTable& seg, const HeadTable& heads, RowInfo ri, hipStream_t stream);
+// D = rowsum(dO * O) and LSE log2(e) (+inf for rows that see no key) of every
+// (row, query head), into a.dsum / a.lse2 (bf16 inputs).
+hipError_t launch_dsum_bf16(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_reduce_partials(const float* part, float* acc, int32_t n_chunks, int64_t n,
                                   hipStream_t stream);
 hipError_t launch_fill_zero(void* dst, int64_t rows, int32_t heads, int32_t d, int64_t st,
@@ -117,6 +127,7 @@ hipError_t launch_convert_acc(const float* src, void* dst, int64_t rows, int32_t
 hipError_t launch_fwd_bf16(const AttnArgs& a, int32_t head_dim, hipStream_t stream);
 hipError_t launch_bwd_dq_bf16(const AttnArgs& a, int32_t head_dim, hipStream_t stream);
 hipError_t launch_bwd_dkv_bf16(const AttnArgs& a, int32_t head_dim, hipStream_t stream);
+hipError_t launch_bwd_dq_ext_bf16(const AttnArgs& a, int32_t head_dim, hipStream_t stream);
 
 hipError_t launch_fwd_f32(const AttnArgs& a, int32_t head_dim, hipStream_t stream);
 hipError_t launch_bwd_dq_f32(const AttnArgs& a, int32_t head_dim, hipStream_t stream);

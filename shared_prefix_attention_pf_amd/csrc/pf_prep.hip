@@ -6,7 +6,10 @@
 //     baseline", an element-wise O(|P| d) add);
 //   - own-key finish: dK/dV of own keys = init + sum of per-chunk partials,
 //     in the same fixed order, converted to the output dtype;
+//   - D = rowsum(dO * O) and LSE in log2 units for the backward passes;
 //   - zero fill and fp32 -> output conversion for Phase C with no upstream.
+#include <math.h>
+
 #include "pf_internal.h"
 
 namespace pf {
@@ -46,6 +49,36 @@ hipError_t launch_prep(const SegTable& seg, const HeadTable& heads, RowInfo ri,
   if (rows <= 0) return hipSuccess;
   const int blocks = (max(rows, heads.n) + 255) / 256;
   PF_LAUNCH("pf_prep", prep_kernel, dim3(blocks), dim3(256), stream, seg, heads, ri);
+  return hipGetLastError();
+}
+
+// D and LSE (log2) per (row, query head): 16 lanes per pair, each lane
+// reading 8 head_dim values of dO and O (head_dim 128).
+__global__ __launch_bounds__(256) void dsum_kernel(AttnArgs a) {
+  typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+  const int64_t pair = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int sub = threadIdx.x & 15;
+  const int64_t n = (int64_t)a.rows * a.hq;
+  const int64_t pc = pair < n ? pair : n - 1;
+  const int h = (int)(pc / a.rows), t = (int)(pc - (int64_t)h * a.rows);
+  const bf16x8 dv = *(const bf16x8*)((const __bf16*)a.dout + (int64_t)t * a.do_st + (int64_t)h * a.do_sh + 8 * sub);
+  const bf16x8 ov = *(const bf16x8*)((const __bf16*)a.o + (int64_t)t * a.o_st + (int64_t)h * a.o_sh + 8 * sub);
+  float dot = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) dot = fmaf((float)dv[e], (float)ov[e], dot);
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 16);
+  if (sub == 0 && pair < n) {
+    const float l = a.lse[(int64_t)h * a.rows + t];
+    a.dsum[(int64_t)h * a.rows + t] = dot;
+    a.lse2[(int64_t)h * a.rows + t] = (l == -INFINITY) ? INFINITY : l * 1.4426950408889634f;
+  }
+}
+
+hipError_t launch_dsum_bf16(const AttnArgs& a, hipStream_t stream) {
+  const int64_t n = (int64_t)a.rows * a.hq;
+  if (n <= 0) return hipSuccess;
+  PF_LAUNCH("pf_dsum", dsum_kernel, dim3((unsigned)((n + 15) / 16)), dim3(256), stream, a);
   return hipGetLastError();
 }
 

@@ -67,6 +67,48 @@ def test_suffix_phase_b(case):
         check("gV", host(gv), ref["gv"], tol)
 
 
+@pytest.mark.parametrize("case", [SUFFIX_CASES[0], SUFFIX_CASES[2]],
+                         ids=lambda c: f"{c[3]}-h{c[0]}x{c[1]}-P{c[4]}-{c[5]}")
+def test_suffix_phase_b_min_workspace(case):
+    """The backward with the smallest workspace (no dS buffer: dQ recomputes
+    S and dP) against the oracle, and against the dS-buffer path."""
+    hq, hkv, d, dtype, p, lens, qmap = case
+    print(f"\ncase {case}", flush=True)
+    g = random_small_group(17, hq, hkv, d, p, lens, dtype)
+    cu = g["cu_seqlens"]
+    rows = int(cu[-1])
+    desc = _desc(hq, hkv, d, dtype, qmap)
+    scale = 1.0 / math.sqrt(d)
+    t = {k: dev(g[k], dtype) for k in ("k_p", "v_p", "q_s", "k_s", "v_s", "do_s")}
+    o_s, lse_s = G.suffix_fwd(desc, t["k_p"], t["v_p"], cu, t["q_s"], t["k_s"], t["v_s"])
+    n_min = pf.pf_workspace_size_min(pf.PF_OP_SUFFIX_BWD, desc, p, rows)
+    n_full = pf.pf_workspace_size(pf.PF_OP_SUFFIX_BWD, desc, p, rows)
+    assert n_full > n_min
+    outs = []
+    for n_ws in (n_min, n_full):
+        ws = torch.empty(n_ws, dtype=torch.uint8, device="cuda")
+        gk = torch.zeros(p, hkv, d, dtype=torch.float32, device="cuda")
+        gv = torch.zeros_like(gk)
+        dq, dk, dv = G.suffix_bwd(desc, t["k_p"], t["v_p"], cu, t["q_s"], t["k_s"], t["v_s"],
+                                  o_s, lse_s, t["do_s"], gk, gv, ws=ws)
+        torch.cuda.synchronize()
+        outs.append({"dq": host(dq), "dk": host(dk), "dv": host(dv), "gk": host(gk),
+                     "gv": host(gv)})
+    hmap = oracle.head_map(hq, hkv, qmap)
+    ref = oracle.suffix_attention(g["k_p"], g["v_p"], g["q_s"], g["k_s"], g["v_s"], g["do_s"], cu,
+                                  scale, hmap)
+    tol = TOL[dtype]
+    mn = outs[0]
+    check("dQ_S (min ws)", mn["dq"], ref["dq_s"], tol)
+    check("dK_S (min ws)", mn["dk"], ref["dk_s"], tol)
+    check("dV_S (min ws)", mn["dv"], ref["dv_s"], tol)
+    check("gK (min ws)", mn["gk"], ref["gk"], tol)
+    check("gV (min ws)", mn["gv"], ref["gv"], tol)
+    # the two paths differ only in rounding (dS rounded to bf16 either way)
+    for k in ("dq", "dk", "dv", "gk", "gv"):
+        check(f"{k}: min ws vs dS buffer", mn[k], outs[1][k], tol)
+
+
 PREFIX_CASES = [
     (8, 2, 128, "bf16", 300, True),
     (4, 4, 128, "bf16", 64, True),
