@@ -108,13 +108,12 @@ typedef struct {
 size_t pf_workspace_size(int32_t op, const pf_attn_desc* desc, int32_t prefix_len, int32_t rows);
 
 /* The smallest workspace `op` accepts (same arguments).  For PF_OP_SUFFIX_BWD
- * with bf16 and prefix_len > 0, pf_workspace_size() adds a buffer for dS of
- * the prefix keys (num_q_heads x ceil256(prefix_len) x ceil256(rows) bf16
- * plus an fp32 [rows, num_q_heads, head_dim] dQ part): with it the backward
- * reads dS back for dQ instead of recomputing S and dP.  A workspace of at
- * least this size but smaller than pf_workspace_size() runs the recompute
- * path.  Results agree to rounding; each path is deterministic.  Other ops:
- * equal to pf_workspace_size(). */
+ * with bf16, pf_workspace_size() adds a buffer for dS (num_q_heads x
+ * (ceil256(prefix_len) + ceil256(rows)) x ceil256(rows) bf16 values): with it
+ * the backward stores dS once and forms dQ from it instead of recomputing S
+ * and dP.  A workspace of at least this size but smaller than
+ * pf_workspace_size() runs the recompute path.  Results agree to rounding;
+ * each path is deterministic.  Other ops: equal to pf_workspace_size(). */
 size_t pf_workspace_size_min(int32_t op, const pf_attn_desc* desc, int32_t prefix_len,
                              int32_t rows);
 

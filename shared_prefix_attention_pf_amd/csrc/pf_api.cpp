@@ -157,18 +157,19 @@ struct WsLayout {
   size_t total = 0;
   size_t dk_part = 0, dv_part = 0;
   int32_t n_chunks = 1, n_chunks_own = 1;
-  // Phase-B dS buffer of the external keys and the fp32 dQ part they give
+  // Phase-B dS buffer (external keys, then own keys)
   bool use_ds = false;
-  size_t ds_ext = 0, dq_part = 0;
-  int32_t ds_keys = 0, ds_rows = 0;
+  size_t ds_ext = 0;
+  int32_t ds_keys = 0, ds_rows = 0, ds_own0 = 0;
 };
 
-// Phase B keeps dS^T of the external keys when the workspace allows it: the
-// buffer holds Hq x ceil256(P) x ceil256(rows) bf16 values (one head's share
-// must stay below 2 GiB for 32-bit buffer offsets).
+// Phase B keeps dS^T when the workspace allows it: the buffer holds
+// Hq x (ceil256(P) + ceil256(rows)) keys x ceil256(rows) rows of bf16 (one
+// head's share must stay below 2 GiB for 32-bit buffer offsets).
 bool ds_eligible(int32_t op, const Desc& d, int32_t n_ext, int32_t rows) {
-  if (op != PF_OP_SUFFIX_BWD || d.dtype != PF_BF16 || n_ext <= 0 || rows <= 0) return false;
-  const int64_t keys = (n_ext + 255) / 256 * 256, r = ((int64_t)rows + 255) / 256 * 256;
+  if (op != PF_OP_SUFFIX_BWD || d.dtype != PF_BF16 || rows <= 0) return false;
+  const int64_t r = ((int64_t)rows + 255) / 256 * 256;
+  const int64_t keys = ((int64_t)n_ext + 255) / 256 * 256 + r;
   return keys * r * 2 < ((int64_t)1 << 31);
 }
 
@@ -205,12 +206,11 @@ WsLayout layout(int32_t op, const Desc& d, int32_t n_ext, int32_t rows, bool wan
   }
   if (want_ds && ds_eligible(op, d, n_ext, rows)) {
     w.use_ds = true;
-    w.ds_keys = (n_ext + 255) / 256 * 256;
     w.ds_rows = (rows + 255) / 256 * 256;
+    w.ds_own0 = (n_ext + 255) / 256 * 256;
+    w.ds_keys = w.ds_own0 + w.ds_rows;
     w.ds_ext = off;
     off += align_up((size_t)d.hq * w.ds_keys * w.ds_rows * 2);
-    w.dq_part = off;
-    off += align_up((size_t)rows * d.hq * d.d * 4);
   }
   w.total = rows > 0 ? off : 0;
   return w;
@@ -308,16 +308,13 @@ pf_status run_bwd(const Desc& d, const pf::AttnArgs& a, const pf::SegTable& seg,
   hipError_t e = pf::launch_prep(seg, d.heads, a.ri, st);
   if (e != hipSuccess) return hip_fail(e, "prep");
   if (a.ds_ext) {
-    // D and LSE first; the dK/dV pass stores dS^T of the external keys, the
-    // external part of dQ is read from it, then the dQ pass adds the own keys
+    // D and LSE first; the dK/dV pass stores dS^T, then dQ is read from it
     e = pf::launch_dsum_bf16(a, st);
     if (e != hipSuccess) return hip_fail(e, "dsum");
     e = pf::launch_bwd_dkv_bf16(a, d.d, st);
     if (e != hipSuccess) return hip_fail(e, "dkv");
-    e = pf::launch_bwd_dq_ext_bf16(a, d.d, st);
-    if (e != hipSuccess) return hip_fail(e, "dq_ext");
-    e = pf::launch_bwd_dq_bf16(a, d.d, st);
-    if (e != hipSuccess) return hip_fail(e, "dq");
+    e = pf::launch_bwd_dq_ds_bf16(a, d.d, st);
+    if (e != hipSuccess) return hip_fail(e, "dq_ds");
   } else {
     e = d.dtype == PF_BF16 ? pf::launch_bwd_dq_bf16(a, d.d, st) : pf::launch_bwd_dq_f32(a, d.d, st);
     if (e != hipSuccess) return hip_fail(e, "dq");
@@ -547,7 +544,7 @@ pf_status pf_suffix_attn_bwd_accum(const pf_attn_desc* desc, int32_t prefix_len,
     a.ds_ext = (__bf16*)((char*)workspace + w.ds_ext);
     a.ds_keys = w.ds_keys;
     a.ds_rows = w.ds_rows;
-    a.dq_part = (float*)((char*)workspace + w.dq_part);
+    a.ds_own0 = w.ds_own0;
   }
   set_own_parts(a, workspace, w);
   a.ri = row_info(workspace, w);

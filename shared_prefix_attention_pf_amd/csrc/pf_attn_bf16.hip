@@ -917,15 +917,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(AttnArgs a) {
       df[nt][ds] = load8((const __bf16*)a.dout + doo + ds * 16);
     }
   }
-  if (a.dq_part) {
-    // D and LSE (log2) were formed by the pre-pass
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int64_t ix = (int64_t)qc[nt].head * a.rows + qc[nt].tok;
-      dsum[nt] = qc[nt].valid ? a.dsum[ix] : 0.f;
-      lse2[nt] = qc[nt].valid ? a.lse2[ix] : INFINITY;
-    }
-  } else {
+  {
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       const int64_t oo = (int64_t)qc[nt].tok * a.o_st + (int64_t)qc[nt].head * a.o_sh + 8 * h32;
@@ -1073,8 +1065,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(AttnArgs a) {
 
   // prologue: blocks 0..2 staged into buffers 0..2, zeros into buffer 4 (the
   // "block -1" whose dQ product the first iteration runs, with dS = 0)
-  // with a dS buffer the external keys' part of dQ is already in dq_part
-  const Blk b0 = blk(walk.next(a.dq_part ? walk.n_ext_blocks : 0));
+  const Blk b0 = blk(walk.next(0));
   const Blk b1 = nxt(b0);
   const Blk b2 = nxt(b1);
   stage(b0, 0);
@@ -1169,33 +1160,37 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(AttnArgs a) {
   for (int nt = 0; nt < 2; ++nt) {
     if (!qc[nt].valid) continue;
     __bf16* op = (__bf16*)a.out + (int64_t)qc[nt].tok * a.out_st + (int64_t)qc[nt].head * a.out_sh;
-    const float* pp = a.dq_part ? a.dq_part + ((int64_t)qc[nt].tok * a.hq + qc[nt].head) * kD : nullptr;
 #pragma unroll
     for (int dt = 0; dt < kD / 32; ++dt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const f32x4 pv = pp ? *(const f32x4*)(pp + dt * 32 + 8 * j + 4 * h32) : f32x4{0.f, 0.f, 0.f, 0.f};
         bf16x4 w;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) w[r] = (__bf16)((acc[dt][nt][4 * j + r] + pv[r]) * a.scale);
+        for (int r = 0; r < 4; ++r) w[r] = (__bf16)(acc[dt][nt][4 * j + r] * a.scale);
         *(bf16x4*)(op + dt * 32 + 8 * j + 4 * h32) = w;
       }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Backward, dQ from the stored dS^T of the external keys (Phase B).
+// Backward, dQ from the stored dS^T (Phase B).
 //
-// dQ^T [d x q] += K^T [d x k] dS^T [k x q] over the external keys, with both
-// operands read from memory: the K rows of the KV head and the dS^T rows the
-// dK/dV pass stored (so S and dP are not computed a second time).  A
-// workgroup owns 256 tokens of one query head, 64 per wave as two 32-column
-// tiles; per block of 32 keys it stages K (32 x 256 B) and dS^T (32 keys x
-// 256 tokens, as two 128-token tiles) and each wave runs 16 products.  Two
-// workgroups share a CU (72 KiB of LDS each), so more staging is in flight.  The
-// result is fp32 and unscaled; the dQ pass adds the own keys' part to it.
-// Within each 32-token group the dS^T columns are in the dK/dV pass's register
-// order: column p holds row 16 (p / 16) + 8 ((p % 8) / 4) + 4 ((p / 8) % 2) + p % 4.
+// dQ^T [d x q] = s K^T [d x k] dS^T [k x q] over every key a query sees, with
+// both operands read from memory: the K rows and the dS^T the dK/dV pass
+// stored (so S and dP are not computed a second time).  A workgroup owns 256
+// tokens of one query head, 64 per wave as two 32-column tiles, and walks the
+// external key blocks and the own key blocks its tokens can see (32 keys
+// each); per block it stages K (32 x 256 B) and dS^T (32 keys x 256 tokens, as
+// two 128-token tiles) and each wave runs 16 products.  Two workgroups share a
+// CU (72 KiB of LDS each).
+//
+// dS^T is stored as [query head][32-key block][32-row step][key][32 values],
+// so a block's eight steps of one workgroup are 16 contiguous KiB.  Within a
+// step the 32 values are in the dK/dV pass's register order: value p is row
+// 16 (p / 16) + 8 ((p % 8) / 4) + 4 ((p / 8) % 2) + p % 4 of the step.  The
+// dK/dV pass writes an own key block's steps from its 256-key workgroup block
+// on to its last visible row; other steps of that block hold no values and
+// are read as zero here.
 constexpr int kDsStep = 32;                       // query rows per stored dS^T step
 constexpr int kDxBN = 32;
 constexpr int kDxTok = 256;
@@ -1208,7 +1203,8 @@ __device__ __forceinline__ int ds_col_row(int p) {
   return 16 * (p >> 4) + 8 * ((p & 7) >> 2) + 4 * ((p >> 3) & 1) + (p & 3);
 }
 
-__global__ __launch_bounds__(kThreads, 2) void bwd_dq_ext_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq_ds_kernel(AttnArgs a) {
+  constexpr int BN = kDxBN;
   __shared__ __attribute__((aligned(16))) char smem[kDxBufs * kDxBufBytes];
   lds_t* const sb = (lds_t*)smem;
   const int tid = threadIdx.x;
@@ -1221,35 +1217,64 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_ext_kernel(AttnArgs a) {
   const int j = item / n_tt, tt = item - j * n_tt;
   const int head = ld_uniform(a.ri.qhead, g * a.group + j);
   const int t0 = tt * kDxTok;
-  const int n_blk = (a.n_ext + kDxBN - 1) / kDxBN;
 
-  // staging sources: K rows of KV head g, and dS^T of this head for the
-  // tile's 8 steps of 32 tokens (64 bytes per key and step, keys contiguous
-  // within a step).  LDS dS^T tile d (0, 1) is [64 keys][128 tokens] with
-  // 256-byte rows: logical chunk c of row r is positions 8 (c % 4) .. of step
-  // 4 d + c / 4.  Each lane's chunk and row within a staging pass are fixed,
-  // so its offset is fixed; the key block and the pass move the scalar offset.
-  RowSrc ksrc;
-  ksrc.init((const __bf16*)a.k_ext + (int64_t)g * a.kx_sh, a.n_ext, a.kx_st, wave, lane);
-  const int64_t n_steps = a.ds_rows / kDsStep;
-  const __bf16* dbase = a.ds_ext + ((int64_t)head * n_steps + t0 / kDsStep) * a.ds_keys * kDsStep;
-  const Rsrc dres = make_rsrc(dbase, 8u * (uint32_t)a.ds_keys * kDsStep * 2u);
+  KeyWalk<BN> walk;
+  walk.n_ext_blocks = (a.n_ext + BN - 1) / BN;
+  walk.t0 = t0;
+  walk.t1 = min(t0 + kDxTok, a.rows);
+  walk.bmax = a.ri.bmax;
+  walk.bmin = a.ri.bmin;
+  walk.rows = a.rows;
+  BlockSrc<BN> src;
+  src.init(a, g, walk.n_ext_blocks, wave, lane);
+
+  // dS^T of this head for the tile's 8 steps.  LDS dS^T tile d (0, 1) is [32
+  // keys][128 tokens] with 256-byte rows: logical chunk c of row r is values
+  // 8 (c % 4) .. of step 4 d + c / 4.  Each lane's chunk and row within a
+  // staging pass are fixed, so its offset is fixed; the key block and the
+  // pass move the scalar offset.
+  const int n_steps = a.ds_rows / kDsStep, nkb = a.ds_keys / 32, s0 = t0 / kDsStep;
+  const __bf16* dbase = a.ds_ext + ((int64_t)head * nkb * n_steps + s0) * 32 * kDsStep;
+  const Rsrc dres = make_rsrc(dbase, (uint32_t)(nkb * n_steps - s0) * 32u * kDsStep * 2u);
   uint32_t d_loff;
   {
     const int r = 4 * wave + (lane >> 4);
     const int lc = (lane & 15) ^ (int)swz(r);
-    d_loff = (uint32_t)(((lc >> 2) * a.ds_keys + r) * kDsStep + 8 * (lc & 3)) * 2u;
+    d_loff = (uint32_t)(((lc >> 2) * 32 + r) * kDsStep + 8 * (lc & 3)) * 2u;
   }
+  // key block b of the walk -> its 32-key block in the dS^T store
+  auto ds_block = [&](int b) {
+    return src.ext(b) ? b : a.ds_own0 / 32 + (b - walk.n_ext_blocks);
+  };
   auto stage = [&](int b, int buf) {
     lds_t* base = sb + buf * kDxBufBytes;
-    const int k0 = b < n_blk ? b * kDxBN : a.ds_keys;   // past the end: not consumed
-    ksrc.stage<kDxBN>(k0, base, wave);
+    int kbs = nkb;                       // no block: zeros (not consumed)
+    if (b >= 0) {
+      src.dma_k(b, base, wave, lane);
+      kbs = ds_block(b);
+    }
 #pragma unroll
     for (int d = 0; d < 2; ++d)
 #pragma unroll
-      for (int i = 0; i < kDxBN / 16; ++i)
+      for (int i = 0; i < BN / 16; ++i)
         lds_dma16(dres, base + (1 + d) * kDxTile + (16 * i + 4 * wave) * kRowB, d_loff,
-                  (uint32_t)((4 * d * a.ds_keys + k0 + 16 * i) * kDsStep * 2));
+                  (uint32_t)(((kbs * n_steps + 4 * d) * 32 + 16 * i) * kDsStep * 2));
+    if (b < 0) {
+      // keep the per-wave load count uniform: K rows past the end
+      src.kx.stage<BN>(a.n_ext + BN, base, wave);
+    }
+  };
+  // steps of own block b the dK/dV pass wrote: from its 256-key workgroup
+  // block's first row to the last row any of those keys is visible to
+  auto own_steps = [&](int b, int& lo, int& hi) {
+    const int kb = b - walk.n_ext_blocks;
+    const int k0 = (kb * BN) / 256 * 256;
+    int m = -1;
+    for (int q = k0 / kKeyBlockSummary; q * kKeyBlockSummary < min(k0 + 256, a.rows); ++q)
+      m = max(m, ld_uniform(a.ri.bmax, q));
+    const int qhi = min(m, a.rows);
+    lo = k0 / kDsStep;
+    hi = qhi > k0 ? (qhi + kDsStep - 1) / kDsStep : lo;
   };
 
   FragC f;
@@ -1265,25 +1290,38 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_ext_kernel(AttnArgs a) {
     for (int nt = 0; nt < 2; ++nt) acc[dt][nt] = zero16();
   fence_acc(acc);
 
-  // this wave's dS^T tile and its two column tiles in it
+  // this wave's dS^T tile, its two column tiles in it and their steps
   const int dtile = 1 + (wave >> 1);
   const int ct0 = 2 * (wave & 1);
-  stage(0, 0);
-  stage(1, 1);
+  const int step0 = s0 + 4 * (wave >> 1) + ct0;
+  const int b0 = walk.next(0);
+  const int b1 = b0 >= 0 ? walk.next(b0 + 1) : -1;
+  stage(b0, 0);
+  stage(b1, 1);
   dma_wait();
   __syncthreads();
-  for (int b = 0; b < n_blk; ++b) {
-    const int buf = b % kDxBufs;
-    const int nbuf = (b + 2) % kDxBufs;
+  int cur = b0, n1 = b1, buf = 0;
+  while (cur >= 0) {
+    const int n2 = n1 >= 0 ? walk.next(n1 + 1) : -1;
+    const int nbuf = buf == 0 ? 2 : buf - 1;   // (buf + 2) % 3
     f.fresh();
-    stage(b + 2, nbuf);
+    stage(n2, nbuf);
+    // column tiles of steps this block holds no values for read as zero
+    bool live0 = true, live1 = true;
+    if (!src.ext(cur)) {
+      int lo, hi;
+      own_steps(cur, lo, hi);
+      live0 = step0 >= lo && step0 < hi;
+      live1 = step0 + 1 >= lo && step0 + 1 < hi;
+    }
     const lds_t* kt_s = sb + buf * kDxBufBytes;
     const lds_t* ds_s = kt_s + dtile * kDxTile;
     // per 16-key slice: two dS^T fragments (B, one per column tile) and four
     // K^T fragments (A, one per d tile), fetched one slice ahead
     auto ldb = [&](int ks, int nt) {
       const lds_t* p = ds_s + ks * 16 * kRowB;
-      return ld_tr(p + f.tr(ct0 + nt, 0), p + f.tr(ct0 + nt, 1));
+      const bf16x8 v = ld_tr(p + f.tr(ct0 + nt, 0), p + f.tr(ct0 + nt, 1));
+      return (nt ? live1 : live0) ? v : zero8();
     };
     auto lda = [&](int ks, int dt) {
       const lds_t* p = kt_s + ks * 16 * kRowB;
@@ -1294,10 +1332,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_ext_kernel(AttnArgs a) {
     bf[0][1] = ldb(0, 1);
 #pragma unroll
     for (int dt = 0; dt < kD / 32; ++dt) af[0][dt] = lda(0, dt);
-    static_for<0, kDxBN / 16>([&](auto ksc) {
+    static_for<0, BN / 16>([&](auto ksc) {
       constexpr int ks = decltype(ksc)::value;
       constexpr int cs = ks & 1, ns = cs ^ 1;
-      if constexpr (ks + 1 < kDxBN / 16) {
+      if constexpr (ks + 1 < BN / 16) {
         bf[ns][0] = ldb(ks + 1, 0);
         bf[ns][1] = ldb(ks + 1, 1);
 #pragma unroll
@@ -1312,6 +1350,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_ext_kernel(AttnArgs a) {
     });
     dma_wait_n<kDxDma>();
     lds_barrier();
+    cur = n1;
+    n1 = n2;
+    buf = buf == 2 ? 0 : buf + 1;
   }
   dma_wait();
 
@@ -1320,15 +1361,15 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_ext_kernel(AttnArgs a) {
   for (int nt = 0; nt < 2; ++nt) {
     const int tok = t0 + 128 * (wave >> 1) + 32 * (ct0 + nt) + ds_col_row(col);
     if (tok >= a.rows) continue;
-    float* op = a.dq_part + ((int64_t)tok * a.hq + head) * kD;
+    __bf16* op = (__bf16*)a.out + (int64_t)tok * a.out_st + (int64_t)head * a.out_sh;
 #pragma unroll
     for (int dt = 0; dt < kD / 32; ++dt)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        f32x4 w;
+        bf16x4 w;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) w[r] = acc[dt][nt][4 * jj + r];
-        *(f32x4*)(op + dt * 32 + 8 * jj + 4 * h32) = w;
+        for (int r = 0; r < 4; ++r) w[r] = (__bf16)(acc[dt][nt][4 * jj + r] * a.scale);
+        *(bf16x4*)(op + dt * 32 + 8 * jj + 4 * h32) = w;
       }
   }
 }
@@ -1640,10 +1681,11 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
       mfma_acc(dk[dt][1], qa[pr % 3], db[1][hf]);
       p_elem(blc, std::integral_constant<int, 2 * pr>());
       p_elem(blc, std::integral_constant<int, 2 * pr + 1>());
-      if constexpr (EXT && pr < 4) {
+      if constexpr (pr < 4) {
         // dS^T of this step for the dQ pass: key tile pr / 2, query half pr % 2
         if (ds_dst)
-          *(bf16x8*)(ds_dst + (pr >> 1) * 32 * kQStep + 16 * (pr & 1)) = db[pr >> 1][pr & 1];
+          *(bf16x8*)(ds_dst + (int64_t)(pr >> 1) * (a.ds_rows / kQStep) * 32 * kQStep +
+                     16 * (pr & 1)) = db[pr >> 1][pr & 1];
       }
       __builtin_amdgcn_sched_barrier(0);
     });
@@ -1720,14 +1762,15 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
       m2a(bc);
       const int t0n = nqt * kQStep;
       if (step_needs_mask(t0n)) mask_s(t0n);
-      // this lane's dS^T destination for step t: key kw0 + col (+32 per key
-      // tile), positions 8 h32 .. 8 h32 + 7 of each 16-position half of the
-      // step's 32 values (64 contiguous bytes per key and step)
+      // this lane's dS^T destination for step t: key kw0 + col (the next key
+      // tile is the next 32-key block), positions 8 h32 .. 8 h32 + 7 of each
+      // 16-position half of the step's 32 values
       __bf16* ds_dst = nullptr;
-      if (EXT && a.ds_ext) {
+      if (a.ds_ext) {
         const int head = ld_uniform(a.ri.qhead, g * a.group + cj);
-        const int64_t n_steps = a.ds_rows / kQStep;
-        ds_dst = a.ds_ext + (((int64_t)head * n_steps + cqt) * a.ds_keys + kw0 + col) * kQStep +
+        const int64_t n_steps = a.ds_rows / kQStep, nkb = a.ds_keys / 32;
+        const int kbs = ((EXT ? 0 : a.ds_own0) + kw0) / 32;
+        ds_dst = a.ds_ext + ((((int64_t)head * nkb + kbs) * n_steps + cqt) * 32 + col) * kQStep +
                  8 * h32;
       }
       m2b(bc, Buf<B1>(), ds_dst);
@@ -1872,11 +1915,11 @@ hipError_t launch_bwd_dkv_bf16(const AttnArgs& a, int32_t head_dim, hipStream_t 
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dq_ext_bf16(const AttnArgs& a, int32_t head_dim, hipStream_t stream) {
+hipError_t launch_bwd_dq_ds_bf16(const AttnArgs& a, int32_t head_dim, hipStream_t stream) {
   if (head_dim != kD) return hipErrorInvalidValue;
-  if (a.rows <= 0 || a.n_ext <= 0) return hipSuccess;
+  if (a.rows <= 0) return hipSuccess;
   const int n_tt = (a.rows + kDxTok - 1) / kDxTok;
-  PF_LAUNCH("pf_bwd_dq_ext_bf16", bwd_dq_ext_kernel, dim3(grid_for(a.hkv, a.group * n_tt)),
+  PF_LAUNCH("pf_bwd_dq_ds_bf16", bwd_dq_ds_kernel, dim3(grid_for(a.hkv, a.group * n_tt)),
             dim3(kThreads), stream, a);
   return hipGetLastError();
 }

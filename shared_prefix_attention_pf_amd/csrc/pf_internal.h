@@ -85,13 +85,11 @@ struct AttnArgs {
   // chunks: fp32 [n_chunks_own, rows, Hkv, d], finished by launch_finish_own
   float* dk_part; float* dv_part;
   int32_t n_chunks_own;
-  // Phase B with a dS buffer: the dK/dV pass stores dS^T of the external
-  // keys (bf16 [Hq, ds_keys, ds_rows]; within each 32-row group the rows are
-  // in the order the dK/dV pass holds them, see kernels), a separate pass
-  // forms their part of dQ into dq_part (fp32 [rows, Hq, d], unscaled) and
-  // the dQ pass then covers own keys only and adds dq_part.
-  __bf16* ds_ext; int32_t ds_keys, ds_rows;
-  float* dq_part;
+  // Phase B with a dS buffer: the dK/dV pass stores dS^T of every key block
+  // it processes (bf16; external keys at key indices [0, ds_own0), own keys
+  // from ds_own0; ds_keys keys and ds_rows rows in all, layout in the
+  // kernels) and dQ is then formed from it instead of by recomputing S, dP.
+  __bf16* ds_ext; int32_t ds_keys, ds_rows, ds_own0;
   RowInfo ri;
   int32_t rows;
   int32_t hq, hkv, group;                 // group = Hq / Hkv
@@ -127,7 +125,7 @@ hipError_t launch_convert_acc(const float* src, void* dst, int64_t rows, int32_t
 hipError_t launch_fwd_bf16(const AttnArgs& a, int32_t head_dim, hipStream_t stream);
 hipError_t launch_bwd_dq_bf16(const AttnArgs& a, int32_t head_dim, hipStream_t stream);
 hipError_t launch_bwd_dkv_bf16(const AttnArgs& a, int32_t head_dim, hipStream_t stream);
-hipError_t launch_bwd_dq_ext_bf16(const AttnArgs& a, int32_t head_dim, hipStream_t stream);
+hipError_t launch_bwd_dq_ds_bf16(const AttnArgs& a, int32_t head_dim, hipStream_t stream);
 
 hipError_t launch_fwd_f32(const AttnArgs& a, int32_t head_dim, hipStream_t stream);
 hipError_t launch_bwd_dq_f32(const AttnArgs& a, int32_t head_dim, hipStream_t stream);
