@@ -87,8 +87,9 @@ class KernelTimer:
     def __init__(self, torch):
         self.torch = torch
         self.open = {}
-        self.spans = []          # (label, start_event, end_event)
+        self.spans = []          # (label, phase, start_event, end_event)
         self.streams = {}
+        self.phase = None        # set by the step before each phase's calls
 
     def __call__(self, label, stream, end):
         torch = self.torch
@@ -100,16 +101,19 @@ class KernelTimer:
         if end == 0:
             self.open[(label, stream)] = ev
         else:
-            self.spans.append((label, self.open.pop((label, stream)), ev))
+            self.spans.append((label, self.phase, self.open.pop((label, stream)), ev))
 
     def summary(self):
         out = {}
-        for label, a, b in self.spans:
+        for label, phase, a, b in self.spans:
             ms = a.elapsed_time(b)
-            t = out.setdefault(label, [0, 0.0])
-            t[0] += 1
-            t[1] += ms
-        return {k: {"launches": n, "avg_ms": tot / n, "total_ms": tot} for k, (n, tot) in out.items()}
+            t = out.setdefault(label, {"launches": 0, "total_ms": 0.0, "phases": {}})
+            t["launches"] += 1
+            t["total_ms"] += ms
+            t["phases"][phase] = t["phases"].get(phase, 0) + 1
+        for t in out.values():
+            t["avg_ms"] = t["total_ms"] / t["launches"]
+        return out
 
 
 def run_gpu(cfg, data, steps, warmup, copy_mib=0):
@@ -127,6 +131,7 @@ def run_gpu(cfg, data, steps, warmup, copy_mib=0):
 
     stream = torch.cuda.current_stream()
     res = {}
+    timer = KernelTimer(torch)
     if cfg.is_tree:
         node_off, parent = data["node_off"], data["parent"]
         q, k, v, do = (to_dev(data[n]) for n in ("q", "k", "v", "do"))
@@ -140,6 +145,7 @@ def run_gpu(cfg, data, steps, warmup, copy_mib=0):
                            dtype=torch.uint8, device=dev)
 
         def step(ev=None):
+            timer.phase = "tree"
             if ev:
                 ev[0].record(stream)
             pf.pf_tree_attn_fwd(desc, node_off, parent, q, k, v, o, lse, ws_f)
@@ -183,17 +189,20 @@ def run_gpu(cfg, data, steps, warmup, copy_mib=0):
         def step(ev=None):
             gk.zero_()
             gv.zero_()
+            timer.phase = "A"
             if ev:
                 ev[0].record(stream)
             pf.pf_prefix_fwd(desc, p, q_p, k_p, v_p, o_p, lse_p, ws)
             if ev:
                 ev[1].record(stream)
+            timer.phase = "B"
             for m in mbs:
                 pf.pf_suffix_attn_fwd(desc, p, k_p, v_p, m["cu"], m["q"], m["k"], m["v"], m["o"],
                                       m["lse"], ws)
                 pf.pf_suffix_attn_bwd_accum(desc, p, k_p, v_p, m["cu"], m["q"], m["k"], m["v"],
                                             m["o"], m["lse"], m["do"], m["dq"], m["dk"], m["dv"],
                                             gk, gv, ws)
+            timer.phase = "C"
             if ev:
                 ev[2].record(stream)
             pf.pf_prefix_bwd_inject(desc, p, q_p, k_p, v_p, o_p, lse_p, do_p, gk, gv, dq_p, dk_p,
@@ -206,13 +215,18 @@ def run_gpu(cfg, data, steps, warmup, copy_mib=0):
         step()
     torch.cuda.synchronize()
 
-    # timed region: K steps, per-phase events inside each step
+    # timed region: K steps, per-phase events inside each step; the launch hook
+    # records HIP events around every kernel on the stream it is launched on
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
-    t0 = time.perf_counter()
-    for i in range(steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    pf.pf_set_launch_hook(timer)
+    try:
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step(evs[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    finally:
+        pf.pf_set_launch_hook(None)
     phase_ms = {}
     if cfg.is_tree:
         phase_ms["tree"] = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
@@ -223,16 +237,6 @@ def run_gpu(cfg, data, steps, warmup, copy_mib=0):
     res["wall_ms_per_step"] = wall * 1e3 / steps
     res["phase_ms"] = phase_ms
 
-    # per-kernel durations: the same steps again with the launch hook recording
-    # HIP events around every kernel on the stream it is launched on
-    timer = KernelTimer(torch)
-    pf.pf_set_launch_hook(timer)
-    try:
-        for _ in range(steps):
-            step()
-        torch.cuda.synchronize()
-    finally:
-        pf.pf_set_launch_hook(None)
     res["kernels"] = timer.summary()
     if copy_mib > 0:
         copy_probe(torch, copy_mib)
@@ -245,8 +249,10 @@ def run_gpu(cfg, data, steps, warmup, copy_mib=0):
 
 # launch-hook label -> substring of the kernel symbol in rocprofv3 output
 KERNEL_SYMBOL = {"pf_fwd_bf16": "fwd_kernel", "pf_bwd_dq_bf16": "bwd_dq_kernel",
-                 "pf_bwd_dkv_bf16": "bwd_dkv_kernel", "pf_fwd_f32": "fwd_f32_kernel",
-                 "pf_bwd_dq_f32": "dq_f32_kernel", "pf_bwd_dkv_f32": "dkv_f32_kernel"}
+                 "pf_bwd_dq_ds_bf16": "bwd_dq_ds_kernel", "pf_bwd_dkv_bf16": "bwd_dkv_kernel",
+                 "pf_fwd_f32": "fwd_f32_kernel", "pf_bwd_dq_f32": "dq_f32_kernel",
+                 "pf_bwd_dkv_f32": "dkv_f32_kernel", "pf_dsum": "dsum_kernel",
+                 "pf_reduce": "reduce_partials_kernel", "pf_finish_own": "finish_own_kernel"}
 COPY_SYMBOL = "neg_kernel"       # the elementwise copy run by --copy-probe-mib
 
 
@@ -469,17 +475,23 @@ def main():
     # roofline of the kernel with the largest total time
     kern = gres["kernels"]
     dom = max(kern, key=lambda k: kern[k]["total_ms"])
-    # algorithmic FLOPs per launch of each kernel (per visible pair per query head):
-    # forward 4d; dQ kernel 2d (dQ = dS K); dK/dV kernel 6d (dV, dP, dK)
-    per_pair = {"pf_fwd_bf16": 4, "pf_bwd_dq_bf16": 2, "pf_bwd_dkv_bf16": 6,
-                "pf_fwd_f32": 4, "pf_bwd_dq_f32": 2, "pf_bwd_dkv_f32": 6}
+    # algorithmic FLOPs of each matrix kernel per visible (query, key) pair per
+    # query head: forward 4d (S = QK^T, O = PV); dQ kernels 2d (dQ = dS K; the
+    # recompute of S and dP is not counted); dK/dV kernel 6d (dV, dP, dK)
+    per_pair = {"pf_fwd_bf16": 4, "pf_bwd_dq_bf16": 2, "pf_bwd_dq_ds_bf16": 2,
+                "pf_bwd_dkv_bf16": 6, "pf_fwd_f32": 4, "pf_bwd_dq_f32": 2,
+                "pf_bwd_dkv_f32": 6}
+    # a kernel launched in a phase covers every visible pair of that phase
+    phase_pairs = {"A": pairs_a, "B": pairs_b, "C": pairs_a, "tree": pairs_b}
+    for label, kn in kern.items():
+        if label not in per_pair:
+            continue
+        flops = sum(per_pair[label] * d * hq * phase_pairs[ph] for ph in kn["phases"]) * args.steps
+        kn["algorithmic_flops_per_launch"] = flops / kn["launches"]
+        kn["tflops"] = flops / (kn["total_ms"] * 1e-3) / 1e12
     if dom in per_pair:
         kn = kern[dom]
-        launches_per_step = kn["launches"] / args.steps
-        # total algorithmic pairs this kernel processes per step: Phase B pairs
-        # plus the prefix pairs of Phase A (fwd) or Phase C (bwd)
-        pairs_step = pairs_b + pairs_a
-        flops_per_launch = per_pair[dom] * d * pairs_step * hq / launches_per_step
+        flops_per_launch = kn["algorithmic_flops_per_launch"]
         achieved = flops_per_launch / (kn["avg_ms"] * 1e-3) / 1e12
         peak = PEAK_BF16_TFLOPS if "bf16" in dom else PEAK_F32_TFLOPS
         traffic, traffic_src = load_traffic(cfg.cid, dom)
