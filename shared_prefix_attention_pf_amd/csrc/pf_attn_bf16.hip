@@ -1184,10 +1184,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(AttnArgs a) {
 // two 128-token tiles) and each wave runs 16 products.  Two workgroups share a
 // CU (72 KiB of LDS each).
 //
-// dS^T is stored as [query head][32-key block][32-row step][key][32 values],
-// so a block's eight steps of one workgroup are 16 contiguous KiB.  Within a
-// step the 32 values are in the dK/dV pass's register order: value p is row
-// 16 (p / 16) + 8 ((p % 8) / 4) + 4 ((p / 8) % 2) + p % 4 of the step.  The
+// dS^T is stored as [query head][32-key block][32-row step][half][key][16
+// values], so a block's eight steps of one workgroup are 16 contiguous KiB and
+// each dK/dV store instruction writes one contiguous KiB (a half of 32 keys).
+// The 32 values of a (step, key) are in the dK/dV pass's register order: value
+// p is row 16 (p / 16) + 8 ((p % 8) / 4) + 4 ((p / 8) % 2) + p % 4 of the step,
+// and half h holds values 16 h .. 16 h + 15.  The
 // dK/dV pass writes an own key block's steps from its 256-key workgroup block
 // on to its last visible row; other steps of that block hold no values and
 // are read as zero here.
@@ -1240,7 +1242,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_ds_kernel(AttnArgs a) {
   {
     const int r = 4 * wave + (lane >> 4);
     const int lc = (lane & 15) ^ (int)swz(r);
-    d_loff = (uint32_t)(((lc >> 2) * 32 + r) * kDsStep + 8 * (lc & 3)) * 2u;
+    d_loff = (uint32_t)((lc >> 2) * 32 * kDsStep + ((lc & 3) >> 1) * 16 * 32 + r * 16 +
+                        8 * (lc & 1)) * 2u;
   }
   // key block b of the walk -> its 32-key block in the dS^T store
   auto ds_block = [&](int b) {
@@ -1258,7 +1261,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_ds_kernel(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < BN / 16; ++i)
         lds_dma16(dres, base + (1 + d) * kDxTile + (16 * i + 4 * wave) * kRowB, d_loff,
-                  (uint32_t)(((kbs * n_steps + 4 * d) * 32 + 16 * i) * kDsStep * 2));
+                  (uint32_t)(((kbs * n_steps + 4 * d) * 32 * kDsStep + 16 * i * 16) * 2));
     if (b < 0) {
       // keep the per-wave load count uniform: K rows past the end
       src.kx.stage<BN>(a.n_ext + BN, base, wave);
@@ -1388,13 +1391,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_ds_kernel(AttnArgs a) {
 // Per step t the work is S = Q K^T, dP = dO V^T (matrix cores), P =
 // exp2(S c - LSE log2 e), dS = P (dP - D) (VALU), dV^T += dO^T P and dK^T +=
 // Q^T dS (matrix cores).  The steps are software-pipelined so the VALU work
-// of one step runs beside the products of another:
-//   M1  S of step t + 1        with  dS of step t (first half)
-//   M2a dV from step t         with  dS of step t (second half)
-//   M2b dK from step t         with  P of step t + 1 (first half)
-//   M3  dP of step t + 1       with  P of step t + 1 (second half)
-// dS reads P back from its packed bf16 form, so one set of S/dP registers
-// serves every step.  Q/dO tiles and the steps' LSE (log2 units) and D rotate
+// of one step runs beside the products of another (the four runs of MFMA
+// pairs described at `step` below).  dS reads P back from its packed bf16
+// form, so one set of S/dP registers serves every step.  Q/dO tiles and the steps' LSE (log2 units) and D rotate
 // through four LDS buffers; step t + 3 is staged during step t, one staging
 // load per M1 product pair.
 constexpr int kQStep = 32;
@@ -1572,15 +1571,27 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
   // is query row 8 (i / 4) + 4 h32 + i % 4 of the step, key kw0 + 32 kt + col.
   f32x16 s[2], dp[2];          // S then P (fp32) / dP then dS of a step
   bf16x8 pb[2][2], db[2][2];   // packed P and dS: [key tile][query half]
-  f32x4 l4, d4;
 
-  // P element e of the step whose LSE is in buffer BL (in place in s)
+  // LSE (log2) and D of one 4-row group of a step (rows 8 (k & 3) + 4 h32 + r
+  // of group k = 0..7, the same rows for both key tiles), double-buffered: each
+  // group's values are read from LDS while the group before it is in use
+  f32x4 lg[2], dg[2];
+  auto ld_l = [&](auto blc, auto kc) {
+    constexpr int BL = decltype(blc)::value, k = decltype(kc)::value;
+    lg[k & 1] = *(const lds_f32x4*)(sb + kDkvL + BL * 256 + 4 * (8 * (k & 3) + 4 * h32));
+  };
+  auto ld_d = [&](auto bdc, auto kc) {
+    constexpr int BD = decltype(bdc)::value, k = decltype(kc)::value;
+    dg[k & 1] = *(const lds_f32x4*)(sb + kDkvD + BD * 256 + 4 * (8 * (k & 3) + 4 * h32));
+  };
+
+  // P element e of the step whose LSE is in buffer BL (in place in s); group
+  // 0's LSE must have been read (ld_l) beforehand
   auto p_elem = [&](auto blc, auto ec) {
-    constexpr int BL = decltype(blc)::value;
     constexpr int e = decltype(ec)::value;
-    constexpr int kt = e >> 4, i = e & 15, jj = i >> 2, r = i & 3;
-    if constexpr (r == 0) l4 = *(const lds_f32x4*)(sb + kDkvL + BL * 256 + 4 * (8 * jj + 4 * h32));
-    s[kt][i] = fast_exp2(fmaf(s[kt][i], c, -l4[r]));
+    constexpr int kt = e >> 4, i = e & 15, k = e >> 2, r = i & 3;
+    if constexpr (r == 0 && k + 1 < 8) ld_l(blc, std::integral_constant<int, k + 1>());
+    s[kt][i] = fast_exp2(fmaf(s[kt][i], c, -lg[k & 1][r]));
     // formed here, beside this step's products (not moved to its first use)
     asm volatile("" : "+v"(s[kt][i]));
     if constexpr ((i & 7) == 7) {
@@ -1588,13 +1599,13 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
       asm volatile("" : "+v"(pb[kt][i >> 3]));
     }
   };
-  // dS element e of the step whose D is in buffer BD (in place in dp)
+  // dS element e of the step whose D is in buffer BD (in place in dp); group
+  // 0's D must have been read (ld_d) beforehand
   auto ds_elem = [&](auto bdc, auto ec) {
-    constexpr int BD = decltype(bdc)::value;
     constexpr int e = decltype(ec)::value;
-    constexpr int kt = e >> 4, i = e & 15, jj = i >> 2, r = i & 3;
-    if constexpr (r == 0) d4 = *(const lds_f32x4*)(sb + kDkvD + BD * 256 + 4 * (8 * jj + 4 * h32));
-    dp[kt][i] = unpack_bf16(pb[kt][i >> 3], i & 7) * (dp[kt][i] - d4[r]);
+    constexpr int kt = e >> 4, i = e & 15, k = e >> 2, r = i & 3;
+    if constexpr (r == 0 && k + 1 < 8) ld_d(bdc, std::integral_constant<int, k + 1>());
+    dp[kt][i] = unpack_bf16(pb[kt][i >> 3], i & 7) * (dp[kt][i] - dg[k & 1][r]);
     asm volatile("" : "+v"(dp[kt][i]));
     if constexpr ((i & 7) == 7) {
       db[kt][i >> 3] = pack_half(dp[kt], i >> 3);
@@ -1618,118 +1629,110 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
     return !ext && !(t0 >= wave_khi && t0 + kQStep - 1 < wave_kend_min);
   };
 
-  // M1: S of the step in buffer BQ (Q fragments one d-step ahead), with the
-  // first half of the dS work of buffer BD and the staging of buffer BS
-  auto m1 = [&](auto bqc, auto bdc, auto bsc) {
-    constexpr int BQ = decltype(bqc)::value;
-    const lds_t* q_s = sb + kDkvQ + BQ * kStepTile;
-    bf16x8 qa[2];
-    qa[0] = ld_row8(q_s + f.row8(0));
-    s[0] = zero16();
-    s[1] = zero16();
-    static_for<0, kD / 16>([&](auto dsc) {
-      constexpr int ds = decltype(dsc)::value;
-      if constexpr (ds + 1 < kD / 16) qa[(ds + 1) & 1] = ld_row8(q_s + f.row8(ds + 1));
-      s[0] = mfma(qa[ds & 1], kf[0][ds], s[0]);
-      s[1] = mfma(qa[ds & 1], kf[1][ds], s[1]);
-      ds_elem(bdc, std::integral_constant<int, 2 * ds>());
-      ds_elem(bdc, std::integral_constant<int, 2 * ds + 1>());
-      if constexpr (ds < kDkvDma) stage_load(bsc, ds);
-      __builtin_amdgcn_sched_barrier(0);
-    });
+  // One step t (buffer B; step t + 1 in B + 1) is 32 MFMA pairs in four runs
+  // of 8, each run paired with VALU work of another step:
+  //   pairs  0-7   S of step t + 1        with  dS of step t (first half)
+  //   pairs  8-15  dV^T += dO^T P, step t  with  dS of step t (second half)
+  //   pairs 16-23  dK^T += Q^T dS, step t  with  P of step t + 1 (first half)
+  //   pairs 24-31  dP of step t + 1        with  P of step t + 1 (second half)
+  // Every pair's A fragment (and the two V fragments of a dP pair) is read
+  // from LDS two pairs ahead through a three-slot ring, across the runs.
+  bf16x8 fr[3], vr[3][2];
+  auto frag = [&](auto bc, auto pc) {
+    constexpr int B = decltype(bc)::value, B1 = (B + 1) % kDkvBufs;
+    constexpr int p = decltype(pc)::value, run = p >> 3, idx = p & 7, sl = p % 3;
+    if constexpr (run == 0) {
+      fr[sl] = ld_row8(sb + kDkvQ + B1 * kStepTile + f.row8(idx));
+    } else if constexpr (run == 1 || run == 2) {
+      const lds_t* t = sb + (run == 1 ? kDkvO : kDkvQ) + B * kStepTile + (idx >> 2) * 16 * kRowB;
+      fr[sl] = ld_tr(t + f.tr(idx & 3, 0), t + f.tr(idx & 3, 1));
+    } else {
+      fr[sl] = ld_row8(sb + kDkvO + B1 * kStepTile + f.row8(idx));
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+        vr[sl][kt] = ld_row8(sb + kt * 32 * kRowB + (vrow0 ^ (uint32_t)(idx << 5)));
+    }
   };
-  // M2a: dV^T += dO^T P of buffer B (transposed dO fragments two ahead), with
-  // the second half of the dS work
-  auto m2a = [&](auto bc) {
+  auto step = [&](auto bc, __bf16* ds_dst, int t0n) {
     constexpr int B = decltype(bc)::value;
-    const lds_t* d_s = sb + kDkvO + B * kStepTile;
-    auto ldo = [&](int pr) {
-      const lds_t* ob = d_s + (pr >> 2) * 16 * kRowB;
-      return ld_tr(ob + f.tr(pr & 3, 0), ob + f.tr(pr & 3, 1));
-    };
-    bf16x8 oa[3];
-    oa[0] = ldo(0);
-    oa[1] = ldo(1);
-    static_for<0, 8>([&](auto prc) {
-      constexpr int pr = decltype(prc)::value;
-      constexpr int hf = pr >> 2, dt = pr & 3;
-      if constexpr (pr + 2 < 8) oa[(pr + 2) % 3] = ldo(pr + 2);
-      mfma_acc(dv[dt][0], oa[pr % 3], pb[0][hf]);
-      mfma_acc(dv[dt][1], oa[pr % 3], pb[1][hf]);
-      ds_elem(bc, std::integral_constant<int, 16 + 2 * pr>());
-      ds_elem(bc, std::integral_constant<int, 17 + 2 * pr>());
-      __builtin_amdgcn_sched_barrier(0);
-    });
-  };
-  // M2b: dK^T += Q^T dS of buffer B, with the first half of the P work of
-  // buffer BL
-  auto m2b = [&](auto bc, auto blc, __bf16* ds_dst) {
-    constexpr int B = decltype(bc)::value;
-    const lds_t* q_s = sb + kDkvQ + B * kStepTile;
-    auto ldq = [&](int pr) {
-      const lds_t* qb = q_s + (pr >> 2) * 16 * kRowB;
-      return ld_tr(qb + f.tr(pr & 3, 0), qb + f.tr(pr & 3, 1));
-    };
-    bf16x8 qa[3];
-    qa[0] = ldq(0);
-    qa[1] = ldq(1);
-    static_for<0, 8>([&](auto prc) {
-      constexpr int pr = decltype(prc)::value;
-      constexpr int hf = pr >> 2, dt = pr & 3;
-      if constexpr (pr + 2 < 8) qa[(pr + 2) % 3] = ldq(pr + 2);
-      mfma_acc(dk[dt][0], qa[pr % 3], db[0][hf]);
-      mfma_acc(dk[dt][1], qa[pr % 3], db[1][hf]);
-      p_elem(blc, std::integral_constant<int, 2 * pr>());
-      p_elem(blc, std::integral_constant<int, 2 * pr + 1>());
-      if constexpr (pr < 4) {
-        // dS^T of this step for the dQ pass: key tile pr / 2, query half pr % 2
-        if (ds_dst)
-          *(bf16x8*)(ds_dst + (int64_t)(pr >> 1) * (a.ds_rows / kQStep) * 32 * kQStep +
-                     16 * (pr & 1)) = db[pr >> 1][pr & 1];
+    constexpr int B1 = (B + 1) % kDkvBufs, B3 = (B + 3) % kDkvBufs;
+    frag(bc, std::integral_constant<int, 0>());
+    frag(bc, std::integral_constant<int, 1>());
+    static_for<0, 32>([&](auto pc) {
+      constexpr int p = decltype(pc)::value, run = p >> 3, idx = p & 7, sl = p % 3;
+      constexpr int hf = idx >> 2, dt = idx & 3;
+      if constexpr (p + 2 < 32) frag(bc, std::integral_constant<int, p + 2>());
+      if constexpr (run == 0) {
+        if constexpr (idx == 0) {
+          s[0] = zero16();
+          s[1] = zero16();
+        }
+        s[0] = mfma(fr[sl], kf[0][idx], s[0]);
+        s[1] = mfma(fr[sl], kf[1][idx], s[1]);
+        ds_elem(bc, std::integral_constant<int, 2 * idx>());
+        ds_elem(bc, std::integral_constant<int, 2 * idx + 1>());
+        if constexpr (idx < kDkvDma) stage_load(Buf<B3>(), idx);
+      } else if constexpr (run == 1) {
+        mfma_acc(dv[dt][0], fr[sl], pb[0][hf]);
+        mfma_acc(dv[dt][1], fr[sl], pb[1][hf]);
+        ds_elem(bc, std::integral_constant<int, 16 + 2 * idx>());
+        ds_elem(bc, std::integral_constant<int, 17 + 2 * idx>());
+        // group 0 of the LSE of step t + 1 (lg[0] is free from here)
+        if constexpr (idx == 4) ld_l(Buf<B1>(), std::integral_constant<int, 0>());
+      } else if constexpr (run == 2) {
+        mfma_acc(dk[dt][0], fr[sl], db[0][hf]);
+        mfma_acc(dk[dt][1], fr[sl], db[1][hf]);
+        if constexpr (idx == 0) {
+          if (step_needs_mask(t0n)) mask_s(t0n);
+        }
+        p_elem(Buf<B1>(), std::integral_constant<int, 2 * idx>());
+        p_elem(Buf<B1>(), std::integral_constant<int, 2 * idx + 1>());
+        if constexpr (idx < 4) {
+          // dS^T of this step for the dQ pass: key tile idx / 2, query half idx % 2
+          if (ds_dst)
+            *(bf16x8*)(ds_dst + (int64_t)(idx >> 1) * (a.ds_rows / kQStep) * 32 * kQStep +
+                       16 * 32 * (idx & 1)) = db[idx >> 1][idx & 1];
+        }
+        // group 0 of the D of step t + 1, read by the next step's dS (dg[0] is
+        // free from here)
+        if constexpr (idx == 4) ld_d(Buf<B1>(), std::integral_constant<int, 0>());
+      } else {
+        if constexpr (idx == 0) {
+          dp[0] = zero16();
+          dp[1] = zero16();
+        }
+        dp[0] = mfma(fr[sl], vr[sl][0], dp[0]);
+        dp[1] = mfma(fr[sl], vr[sl][1], dp[1]);
+        p_elem(Buf<B1>(), std::integral_constant<int, 16 + 2 * idx>());
+        p_elem(Buf<B1>(), std::integral_constant<int, 17 + 2 * idx>());
       }
       __builtin_amdgcn_sched_barrier(0);
     });
   };
-  // M3: dP of the step in buffer BQ (dO and V fragments one d-step ahead),
-  // with the second half of the P work
-  auto m3 = [&](auto bqc) {
-    constexpr int BQ = decltype(bqc)::value;
-    const lds_t* d_s = sb + kDkvO + BQ * kStepTile;
-    bf16x8 da[2], vb[2][2];
-    auto ld = [&](int ds, int sl) {
-      da[sl] = ld_row8(d_s + f.row8(ds));
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-        vb[sl][kt] = ld_row8(sb + kt * 32 * kRowB + (vrow0 ^ (uint32_t)(ds << 5)));
-    };
-    ld(0, 0);
-    dp[0] = zero16();
-    dp[1] = zero16();
-    static_for<0, kD / 16>([&](auto dsc) {
-      constexpr int ds = decltype(dsc)::value;
-      if constexpr (ds + 1 < kD / 16) ld(ds + 1, (ds + 1) & 1);
-      dp[0] = mfma(da[ds & 1], vb[ds & 1][0], dp[0]);
-      dp[1] = mfma(da[ds & 1], vb[ds & 1][1], dp[1]);
-      p_elem(bqc, std::integral_constant<int, 16 + 2 * ds>());
-      p_elem(bqc, std::integral_constant<int, 17 + 2 * ds>());
-      __builtin_amdgcn_sched_barrier(0);
-    });
-  };
-  // S, P and dP of the step in buffer BQ without overlap (pipeline fill)
+  // S, P and dP of the step in buffer BQ without overlap (pipeline fill); it
+  // leaves group 0 of that step's D read for the first step's dS
   auto fill = [&](auto bqc, int t0) {
     constexpr int BQ = decltype(bqc)::value;
     const lds_t* q_s = sb + kDkvQ + BQ * kStepTile;
+    const lds_t* d_s = sb + kDkvO + BQ * kStepTile;
+    ld_l(bqc, std::integral_constant<int, 0>());
     s[0] = zero16();
     s[1] = zero16();
+    dp[0] = zero16();
+    dp[1] = zero16();
 #pragma unroll
     for (int ds = 0; ds < kD / 16; ++ds) {
       const bf16x8 qa = ld_row8(q_s + f.row8(ds));
       s[0] = mfma(qa, kf[0][ds], s[0]);
       s[1] = mfma(qa, kf[1][ds], s[1]);
+      const bf16x8 da = ld_row8(d_s + f.row8(ds));
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+        dp[kt] = mfma(da, ld_row8(sb + kt * 32 * kRowB + (vrow0 ^ (uint32_t)(ds << 5))), dp[kt]);
     }
     if (step_needs_mask(t0)) mask_s(t0);
-    static_for<0, 16>([&](auto ec) { p_elem(bqc, ec); });
-    m3(bqc);
+    static_for<0, 32>([&](auto ec) { p_elem(bqc, ec); });
+    ld_d(bqc, std::integral_constant<int, 0>());
   };
 
   if (it_lo < it_hi) {
@@ -1753,15 +1756,9 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
     advance();
     // step t in buffer B: step t + 1 in B + 1, staging of step t + 3 into B + 3
     auto iter = [&](auto bc) {
-      constexpr int B = decltype(bc)::value;
-      constexpr int B1 = (B + 1) % kDkvBufs, B3 = (B + 3) % kDkvBufs;
       f.fresh();
       asm volatile("" : "+v"(vrow0));
       stage_begin();
-      m1(Buf<B1>(), bc, Buf<B3>());
-      m2a(bc);
-      const int t0n = nqt * kQStep;
-      if (step_needs_mask(t0n)) mask_s(t0n);
       // this lane's dS^T destination for step t: key kw0 + col (the next key
       // tile is the next 32-key block), positions 8 h32 .. 8 h32 + 7 of each
       // 16-position half of the step's 32 values
@@ -1770,11 +1767,10 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
         const int head = ld_uniform(a.ri.qhead, g * a.group + cj);
         const int64_t n_steps = a.ds_rows / kQStep, nkb = a.ds_keys / 32;
         const int kbs = ((EXT ? 0 : a.ds_own0) + kw0) / 32;
-        ds_dst = a.ds_ext + ((((int64_t)head * nkb + kbs) * n_steps + cqt) * 32 + col) * kQStep +
+        ds_dst = a.ds_ext + (((int64_t)head * nkb + kbs) * n_steps + cqt) * 32 * kQStep + 16 * col +
                  8 * h32;
       }
-      m2b(bc, Buf<B1>(), ds_dst);
-      m3(Buf<B1>());
+      step(bc, ds_dst, nqt * kQStep);
       cqt = nqt;
       cj = nj;
       advance();
