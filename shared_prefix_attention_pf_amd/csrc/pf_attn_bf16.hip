@@ -1199,7 +1199,7 @@ constexpr int kDxTok = 256;
 constexpr int kDxTile = kDxBN * kRowB;
 constexpr int kDxBufBytes = 3 * kDxTile;          // K tile, then two dS^T tiles
 constexpr int kDxBufs = 3;
-constexpr int kDxDma = 3 * (kDxBN / 16);          // staging loads per wave per block
+constexpr int kDxDma = 3 * (kDxBN / 16);          // K staging + dS^T loads per wave per block
 
 __device__ __forceinline__ int ds_col_row(int p) {
   return 16 * (p >> 4) + 8 * ((p & 7) >> 2) + 4 * ((p >> 3) & 1) + (p & 3);
@@ -1237,7 +1237,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_ds_kernel(AttnArgs a) {
   // pass move the scalar offset.
   const int n_steps = a.ds_rows / kDsStep, nkb = a.ds_keys / 32, s0 = t0 / kDsStep;
   const __bf16* dbase = a.ds_ext + ((int64_t)head * nkb * n_steps + s0) * 32 * kDsStep;
-  const Rsrc dres = make_rsrc(dbase, (uint32_t)(nkb * n_steps - s0) * 32u * kDsStep * 2u);
+  const __amdgpu_buffer_rsrc_t dres = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)dbase, (short)0, (nkb * n_steps - s0) * 32 * kDsStep * 2, 0x00020000);
   uint32_t d_loff;
   {
     const int r = 4 * wave + (lane >> 4);
@@ -1249,23 +1250,37 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_ds_kernel(AttnArgs a) {
   auto ds_block = [&](int b) {
     return src.ext(b) ? b : a.ds_own0 / 32 + (b - walk.n_ext_blocks);
   };
-  auto stage = [&](int b, int buf) {
+  // Block b's K rows go to LDS buffer `buf` by staging loads; its dS^T goes
+  // through registers (plain loads, two blocks ahead in one of two register
+  // stages) and is written to the buffer one block later, so the staging
+  // path carries only K (mostly L2 hits) and the dS^T stream, the HBM-bound
+  // part, has two blocks of time to arrive.
+  u32x4 dsr[2][2][BN / 16];   // [register stage][dS^T tile][16-key pass]
+  auto stage = [&](int b, int buf, u32x4 (&r)[2][BN / 16]) {
     lds_t* base = sb + buf * kDxBufBytes;
-    int kbs = nkb;                       // no block: zeros (not consumed)
     if (b >= 0) {
       src.dma_k(b, base, wave, lane);
-      kbs = ds_block(b);
+    } else {
+      // keep the per-wave load count uniform: K rows past the end
+      src.kx.stage<BN>(a.n_ext + BN, base, wave);
     }
+    // past the last block: offsets past the resource, which read zero (the
+    // values are never used; every block issues the same loads)
+    const int kbs = b >= 0 ? ds_block(b) : nkb;
 #pragma unroll
     for (int d = 0; d < 2; ++d)
 #pragma unroll
       for (int i = 0; i < BN / 16; ++i)
-        lds_dma16(dres, base + (1 + d) * kDxTile + (16 * i + 4 * wave) * kRowB, d_loff,
-                  (uint32_t)(((kbs * n_steps + 4 * d) * 32 * kDsStep + 16 * i * 16) * 2));
-    if (b < 0) {
-      // keep the per-wave load count uniform: K rows past the end
-      src.kx.stage<BN>(a.n_ext + BN, base, wave);
-    }
+        r[d][i] = __builtin_amdgcn_raw_buffer_load_b128(
+            dres, (int)d_loff, ((kbs * n_steps + 4 * d) * 32 * kDsStep + 16 * i * 16) * 2, 0);
+  };
+  auto commit = [&](int buf, const u32x4 (&r)[2][BN / 16]) {
+    lds_t* base = sb + buf * kDxBufBytes;
+#pragma unroll
+    for (int d = 0; d < 2; ++d)
+#pragma unroll
+      for (int i = 0; i < BN / 16; ++i)
+        st16(base + (1 + d) * kDxTile + (16 * i + 4 * wave) * kRowB + 16 * lane, r[d][i]);
   };
   // steps of own block b the dK/dV pass wrote: from its 256-key workgroup
   // block's first row to the last row any of those keys is visible to
@@ -1297,18 +1312,21 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_ds_kernel(AttnArgs a) {
   const int dtile = 1 + (wave >> 1);
   const int ct0 = 2 * (wave & 1);
   const int step0 = s0 + 4 * (wave >> 1) + ct0;
-  const int b0 = walk.next(0);
-  const int b1 = b0 >= 0 ? walk.next(b0 + 1) : -1;
-  stage(b0, 0);
-  stage(b1, 1);
+  // cur is the block in buffer `buf`, n1 the next (its dS^T in register
+  // stage RS ^ 1), n2 the one after (staged during this block into stage RS)
+  int cur = walk.next(0);
+  int n1 = cur >= 0 ? walk.next(cur + 1) : -1;
+  stage(cur, 0, dsr[0]);
+  stage(n1, 1, dsr[1]);
   dma_wait();
+  commit(0, dsr[0]);
   __syncthreads();
-  int cur = b0, n1 = b1, buf = 0;
-  while (cur >= 0) {
+  int buf = 0;
+  auto block = [&](auto rsc) {
+    constexpr int RS = decltype(rsc)::value;
     const int n2 = n1 >= 0 ? walk.next(n1 + 1) : -1;
-    const int nbuf = buf == 0 ? 2 : buf - 1;   // (buf + 2) % 3
     f.fresh();
-    stage(n2, nbuf);
+    stage(n2, buf == 0 ? 2 : buf - 1, dsr[RS]);
     // column tiles of steps this block holds no values for read as zero
     bool live0 = true, live1 = true;
     if (!src.ext(cur)) {
@@ -1351,11 +1369,19 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_ds_kernel(AttnArgs a) {
       });
       __builtin_amdgcn_sched_barrier(0);
     });
+    // the next block's K and dS^T have landed (this block's loads stay in
+    // flight): its dS^T goes to its buffer
     dma_wait_n<kDxDma>();
+    commit(buf == 2 ? 0 : buf + 1, dsr[RS ^ 1]);
     lds_barrier();
     cur = n1;
     n1 = n2;
     buf = buf == 2 ? 0 : buf + 1;
+  };
+  while (cur >= 0) {
+    block(std::integral_constant<int, 0>());
+    if (cur < 0) break;
+    block(std::integral_constant<int, 1>());
   }
   dma_wait();
 
