@@ -305,17 +305,19 @@ pf_status run_fwd(const Desc& d, const pf::AttnArgs& a, const pf::SegTable& seg,
 }
 
 pf_status run_bwd(const Desc& d, const pf::AttnArgs& a, const pf::SegTable& seg, hipStream_t st) {
-  hipError_t e = pf::launch_prep(seg, d.heads, a.ri, st);
-  if (e != hipSuccess) return hip_fail(e, "prep");
+  hipError_t e;
   if (a.ds_ext) {
-    // D and LSE first; the dK/dV pass stores dS^T, then dQ is read from it
-    e = pf::launch_dsum_bf16(a, st);
-    if (e != hipSuccess) return hip_fail(e, "dsum");
+    // prep with D and LSE first; the dK/dV pass stores dS^T, then dQ is read
+    // from it
+    e = pf::launch_prep_dsum_bf16(seg, d.heads, a, st);
+    if (e != hipSuccess) return hip_fail(e, "prep");
     e = pf::launch_bwd_dkv_bf16(a, d.d, st);
     if (e != hipSuccess) return hip_fail(e, "dkv");
     e = pf::launch_bwd_dq_ds_bf16(a, d.d, st);
     if (e != hipSuccess) return hip_fail(e, "dq_ds");
   } else {
+    e = pf::launch_prep(seg, d.heads, a.ri, st);
+    if (e != hipSuccess) return hip_fail(e, "prep");
     e = d.dtype == PF_BF16 ? pf::launch_bwd_dq_bf16(a, d.d, st) : pf::launch_bwd_dq_f32(a, d.d, st);
     if (e != hipSuccess) return hip_fail(e, "dq");
     e = d.dtype == PF_BF16 ? pf::launch_bwd_dkv_bf16(a, d.d, st) : pf::launch_bwd_dkv_f32(a, d.d, st);
@@ -323,16 +325,15 @@ pf_status run_bwd(const Desc& d, const pf::AttnArgs& a, const pf::SegTable& seg,
   }
   if (a.n_chunks > 1 && a.n_ext > 0) {
     const int64_t n = (int64_t)a.n_ext * d.hkv * d.d;
-    e = pf::launch_reduce_partials(a.gk_part, a.gk_acc, a.n_chunks, n, st);
-    if (e == hipSuccess) e = pf::launch_reduce_partials(a.gv_part, a.gv_acc, a.n_chunks, n, st);
+    e = pf::launch_reduce_partials(a.gk_part, a.gk_acc, a.gv_part, a.gv_acc, a.n_chunks, n, st);
     if (e != hipSuccess) return hip_fail(e, "reduce");
   }
   if (a.n_chunks_own > 1) {
-    e = pf::launch_finish_own(a.dk_part, a.n_chunks_own, a.gk_init, a.dk_own, a.rows, d.hkv, d.d,
-                              a.dko_st, a.dko_sh, a.dkv_f32, st);
-    if (e == hipSuccess)
-      e = pf::launch_finish_own(a.dv_part, a.n_chunks_own, a.gv_init, a.dv_own, a.rows, d.hkv,
-                                d.d, a.dvo_st, a.dvo_sh, a.dkv_f32, st);
+    const pf::OwnFinish fk{(const float4*)a.dk_part, (const float4*)a.gk_init, (char*)a.dk_own,
+                           a.dko_st, a.dko_sh};
+    const pf::OwnFinish fv{(const float4*)a.dv_part, (const float4*)a.gv_init, (char*)a.dv_own,
+                           a.dvo_st, a.dvo_sh};
+    e = pf::launch_finish_own(fk, fv, a.n_chunks_own, a.rows, d.hkv, d.d, a.dkv_f32, st);
     if (e != hipSuccess) return hip_fail(e, "finish");
   }
   return PF_OK;

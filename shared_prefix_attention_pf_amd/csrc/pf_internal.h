@@ -109,16 +109,28 @@ void launch_hook(const char* kernel, hipStream_t stream, int end);
 
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_prep(const SegTable& seg, const HeadTable& heads, RowInfo ri, hipStream_t stream);
-// D = rowsum(dO * O) and LSE log2(e) (+inf for rows that see no key) of every
-// (row, query head), into a.dsum / a.lse2 (bf16 inputs).
-hipError_t launch_dsum_bf16(const AttnArgs& a, hipStream_t stream);
-hipError_t launch_reduce_partials(const float* part, float* acc, int32_t n_chunks, int64_t n,
-                                  hipStream_t stream);
+// launch_prep's work and, in the same launch, D = rowsum(dO * O) and LSE
+// log2(e) (+inf for rows that see no key) of every (row, query head) into
+// a.dsum / a.lse2 (bf16 inputs).
+hipError_t launch_prep_dsum_bf16(const SegTable& seg, const HeadTable& heads, const AttnArgs& a,
+                                 hipStream_t stream);
+// acc_k += sum of the n_chunks partials part_k[c] (fixed pairwise order), and
+// the same for the V arrays, in one launch; n elements per array
+hipError_t launch_reduce_partials(const float* part_k, float* acc_k, const float* part_v,
+                                  float* acc_v, int32_t n_chunks, int64_t n, hipStream_t stream);
 hipError_t launch_fill_zero(void* dst, int64_t rows, int32_t heads, int32_t d, int64_t st,
                             int64_t sh, int32_t elem_bytes, hipStream_t stream);
-hipError_t launch_finish_own(const float* part, int32_t n_chunks, const float* init, void* dst,
-                             int64_t rows, int32_t heads, int32_t d, int64_t st, int64_t sh,
-                             int32_t dst_f32, hipStream_t stream);
+// One own-key gradient (dK or dV) to finish: dst = convert(init + sum of the
+// chunk partials); part and init are contiguous [rows, heads, d] fp32 (init
+// may be null), dst is strided (elements).
+struct OwnFinish {
+  const float4* part;
+  const float4* init;
+  char* dst;
+  int64_t st, sh;
+};
+hipError_t launch_finish_own(OwnFinish fk, OwnFinish fv, int32_t n_chunks, int64_t rows,
+                             int32_t heads, int32_t d, int32_t dst_f32, hipStream_t stream);
 hipError_t launch_convert_acc(const float* src, void* dst, int64_t rows, int32_t heads, int32_t d,
                               int64_t st, int64_t sh, int32_t dst_f32, hipStream_t stream);
 

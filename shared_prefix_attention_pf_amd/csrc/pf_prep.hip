@@ -14,9 +14,11 @@
 
 namespace pf {
 
-__global__ __launch_bounds__(256) void prep_kernel(SegTable seg, HeadTable heads, RowInfo ri) {
+// thread t of the prep grid (block `blk`)
+__device__ __forceinline__ void prep_body(const SegTable& seg, const HeadTable& heads,
+                                          const RowInfo& ri, int blk) {
   const int rows = seg.start[seg.n];
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  const int t = blk * blockDim.x + threadIdx.x;
   if (t < heads.n) ri.qhead[t] = heads.qhead[t];
   int kend = -1;          // rows past the end: ignored by both summaries
   if (t < rows) {
@@ -43,20 +45,29 @@ __global__ __launch_bounds__(256) void prep_kernel(SegTable seg, HeadTable heads
   }
 }
 
+__global__ __launch_bounds__(256) void prep_kernel(SegTable seg, HeadTable heads, RowInfo ri) {
+  prep_body(seg, heads, ri, blockIdx.x);
+}
+
+static int prep_blocks(const SegTable& seg, const HeadTable& heads) {
+  return (max(seg.start[seg.n], heads.n) + 255) / 256;
+}
+
 hipError_t launch_prep(const SegTable& seg, const HeadTable& heads, RowInfo ri,
                        hipStream_t stream) {
   const int rows = seg.start[seg.n];
   if (rows <= 0) return hipSuccess;
-  const int blocks = (max(rows, heads.n) + 255) / 256;
-  PF_LAUNCH("pf_prep", prep_kernel, dim3(blocks), dim3(256), stream, seg, heads, ri);
+  PF_LAUNCH("pf_prep", prep_kernel, dim3(prep_blocks(seg, heads)), dim3(256), stream, seg, heads,
+            ri);
   return hipGetLastError();
 }
 
 // D and LSE (log2) per (row, query head): 16 lanes per pair, each lane
-// reading 8 head_dim values of dO and O (head_dim 128).
-__global__ __launch_bounds__(256) void dsum_kernel(AttnArgs a) {
+// reading 8 head_dim values of dO and O (head_dim 128); block `blk` covers
+// 16 pairs.
+__device__ __forceinline__ void dsum_body(const AttnArgs& a, int blk) {
   typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-  const int64_t pair = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int64_t pair = (int64_t)blk * 16 + (threadIdx.x >> 4);
   const int sub = threadIdx.x & 15;
   const int64_t n = (int64_t)a.rows * a.hq;
   const int64_t pc = pair < n ? pair : n - 1;
@@ -75,10 +86,23 @@ __global__ __launch_bounds__(256) void dsum_kernel(AttnArgs a) {
   }
 }
 
-hipError_t launch_dsum_bf16(const AttnArgs& a, hipStream_t stream) {
+// the prep grid followed by the D/LSE grid, in one launch (neither reads
+// what the other writes)
+__global__ __launch_bounds__(256) void prep_dsum_kernel(SegTable seg, HeadTable heads, RowInfo ri,
+                                                        AttnArgs a, int n_prep) {
+  if ((int)blockIdx.x < n_prep)
+    prep_body(seg, heads, ri, blockIdx.x);
+  else
+    dsum_body(a, blockIdx.x - n_prep);
+}
+
+hipError_t launch_prep_dsum_bf16(const SegTable& seg, const HeadTable& heads, const AttnArgs& a,
+                                 hipStream_t stream) {
   const int64_t n = (int64_t)a.rows * a.hq;
   if (n <= 0) return hipSuccess;
-  PF_LAUNCH("pf_dsum", dsum_kernel, dim3((unsigned)((n + 15) / 16)), dim3(256), stream, a);
+  const int np = prep_blocks(seg, heads);
+  PF_LAUNCH("pf_prep_dsum", prep_dsum_kernel, dim3((unsigned)(np + (n + 15) / 16)), dim3(256),
+            stream, seg, heads, a.ri, a, np);
   return hipGetLastError();
 }
 
@@ -98,9 +122,14 @@ __device__ inline float4 tree_sum(const float4* part, int64_t n4, int64_t i, int
   return v[0];
 }
 
-__global__ __launch_bounds__(256) void reduce_partials_kernel(const float4* __restrict__ part,
-                                                              float4* __restrict__ acc,
+// blockIdx.y selects the K (0) or V (1) pair of arrays
+__global__ __launch_bounds__(256) void reduce_partials_kernel(const float4* __restrict__ part_k,
+                                                              float4* __restrict__ acc_k,
+                                                              const float4* __restrict__ part_v,
+                                                              float4* __restrict__ acc_v,
                                                               int nc, int64_t n4) {
+  const float4* __restrict__ part = blockIdx.y ? part_v : part_k;
+  float4* __restrict__ acc = blockIdx.y ? acc_v : acc_k;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
     float4 s;
@@ -113,23 +142,29 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(const float4* __re
   }
 }
 
-hipError_t launch_reduce_partials(const float* part, float* acc, int32_t n_chunks, int64_t n,
-                                  hipStream_t stream) {
+hipError_t launch_reduce_partials(const float* part_k, float* acc_k, const float* part_v,
+                                  float* acc_v, int32_t n_chunks, int64_t n, hipStream_t stream) {
   if (n <= 0) return hipSuccess;
   const int64_t n4 = n / 4;  // n is a multiple of head_dim (>= 64)
   int64_t blocks = (n4 + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
-  PF_LAUNCH("pf_reduce", reduce_partials_kernel, dim3((unsigned)blocks), dim3(256), stream, (const float4*)part, (float4*)acc, (int)n_chunks, n4);
+  if (blocks > 2048) blocks = 2048;
+  PF_LAUNCH("pf_reduce", reduce_partials_kernel, dim3((unsigned)blocks, 2), dim3(256), stream,
+            (const float4*)part_k, (float4*)acc_k, (const float4*)part_v, (float4*)acc_v,
+            (int)n_chunks, n4);
   return hipGetLastError();
 }
 
 // dst[r, h, :] = convert(init[r, h, :] + sum_c part[c, r, h, :]); part and
 // init are contiguous [rows, heads, d] fp32, dst is strided.
-__global__ __launch_bounds__(256) void finish_own_kernel(const float4* __restrict__ part, int nc,
-                                                         const float4* __restrict__ init,
-                                                         char* dst, int64_t rows, int heads,
-                                                         int d, int64_t st, int64_t sh,
+// blockIdx.y selects dK (0) or dV (1)
+__global__ __launch_bounds__(256) void finish_own_kernel(OwnFinish fk, OwnFinish fv, int nc,
+                                                         int64_t rows, int heads, int d,
                                                          int dst_f32) {
+  const OwnFinish& fo = blockIdx.y ? fv : fk;
+  const float4* __restrict__ part = fo.part;
+  const float4* __restrict__ init = fo.init;
+  char* dst = fo.dst;
+  const int64_t st = fo.st, sh = fo.sh;
   const int per = d / 4;
   const int64_t n4 = rows * heads * per;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -156,16 +191,14 @@ __global__ __launch_bounds__(256) void finish_own_kernel(const float4* __restric
   }
 }
 
-hipError_t launch_finish_own(const float* part, int32_t n_chunks, const float* init, void* dst,
-                             int64_t rows, int32_t heads, int32_t d, int64_t st, int64_t sh,
-                             int32_t dst_f32, hipStream_t stream) {
+hipError_t launch_finish_own(OwnFinish fk, OwnFinish fv, int32_t n_chunks, int64_t rows,
+                             int32_t heads, int32_t d, int32_t dst_f32, hipStream_t stream) {
   if (rows <= 0) return hipSuccess;
   const int64_t total = rows * heads * (d / 4);
   int64_t blocks = (total + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
-  PF_LAUNCH("pf_finish_own", finish_own_kernel, dim3((unsigned)blocks), dim3(256), stream,
-            (const float4*)part, (int)n_chunks, (const float4*)init, (char*)dst, rows, (int)heads,
-            (int)d, st, sh, (int)dst_f32);
+  if (blocks > 2048) blocks = 2048;
+  PF_LAUNCH("pf_finish_own", finish_own_kernel, dim3((unsigned)blocks, 2), dim3(256), stream, fk,
+            fv, (int)n_chunks, rows, (int)heads, (int)d, (int)dst_f32);
   return hipGetLastError();
 }
 
