@@ -197,7 +197,7 @@ WsLayout layout(int32_t op, const Desc& d, int32_t n_ext, int32_t rows, bool wan
     }
   }
   if (bwd) {
-    w.n_chunks_own = pf::own_chunks(op, rows, d.hq, d.hkv, d.d, d.dtype);
+    w.n_chunks_own = pf::own_chunks(op, n_ext, rows, d.hq, d.hkv, d.d, d.dtype);
     if (w.n_chunks_own > 1) {
       const size_t part = (size_t)w.n_chunks_own * rows * d.hkv * d.d * 4;
       w.dk_part = off; off += align_up(part);
@@ -306,12 +306,17 @@ pf_status run_fwd(const Desc& d, const pf::AttnArgs& a, const pf::SegTable& seg,
 
 pf_status run_bwd(const Desc& d, const pf::AttnArgs& a, const pf::SegTable& seg, hipStream_t st) {
   hipError_t e;
+  // longest-first order of the KV-stationary items (a host-side plan; no
+  // device work)
+  pf::ItemOrder ord;
+  ord.n = 0;
+  if (d.dtype == PF_BF16) pf::dkv_item_order(a, seg, ord);
   if (a.ds_ext) {
     // prep with D and LSE first; the dK/dV pass stores dS^T, then dQ is read
     // from it
     e = pf::launch_prep_dsum_bf16(seg, d.heads, a, st);
     if (e != hipSuccess) return hip_fail(e, "prep");
-    e = pf::launch_bwd_dkv_bf16(a, d.d, st);
+    e = pf::launch_bwd_dkv_bf16(a, ord, d.d, st);
     if (e != hipSuccess) return hip_fail(e, "dkv");
     e = pf::launch_bwd_dq_ds_bf16(a, d.d, st);
     if (e != hipSuccess) return hip_fail(e, "dq_ds");
@@ -320,7 +325,7 @@ pf_status run_bwd(const Desc& d, const pf::AttnArgs& a, const pf::SegTable& seg,
     if (e != hipSuccess) return hip_fail(e, "prep");
     e = d.dtype == PF_BF16 ? pf::launch_bwd_dq_bf16(a, d.d, st) : pf::launch_bwd_dq_f32(a, d.d, st);
     if (e != hipSuccess) return hip_fail(e, "dq");
-    e = d.dtype == PF_BF16 ? pf::launch_bwd_dkv_bf16(a, d.d, st) : pf::launch_bwd_dkv_f32(a, d.d, st);
+    e = d.dtype == PF_BF16 ? pf::launch_bwd_dkv_bf16(a, ord, d.d, st) : pf::launch_bwd_dkv_f32(a, d.d, st);
     if (e != hipSuccess) return hip_fail(e, "dkv");
   }
   if (a.n_chunks > 1 && a.n_ext > 0) {
@@ -368,12 +373,16 @@ int32_t ext_chunks(int32_t n_ext, int32_t rows, int32_t hq, int32_t hkv, int32_t
 }
 
 // Own keys: a causal prefix (Phase C) or a tree has key blocks whose query
-// ranges average about half the rows; Phase-B suffix keys only see their own
-// suffix and stay unsplit.
-int32_t own_chunks(int32_t op, int32_t rows, int32_t hq, int32_t hkv, int32_t head_dim,
-                   int32_t dtype) {
+// ranges average about half the rows, split like the external blocks.  In
+// Phase B a suffix key block sees at most its own suffix, a fraction of what
+// an external block sees; after the external items fill every CU the own
+// items form the tail of the launch, so with a prefix they are halved to
+// shorten that tail (their partials are summed by the finishing pass).
+int32_t own_chunks(int32_t op, int32_t n_ext, int32_t rows, int32_t hq, int32_t hkv,
+                   int32_t head_dim, int32_t dtype) {
   (void)head_dim;
   if (dtype != PF_BF16 || rows <= 0) return 1;
+  if (op == PF_OP_SUFFIX_BWD) return (n_ext > 0 && rows >= 512) ? 2 : 1;
   if (op != PF_OP_PREFIX_BWD && op != PF_OP_TREE_BWD) return 1;
   const int kb = dkv_keys_per_workgroup_bf16();
   const int64_t wgs = (int64_t)((rows + kb - 1) / kb) * hkv;

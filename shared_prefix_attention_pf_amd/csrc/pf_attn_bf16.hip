@@ -35,6 +35,7 @@
 // MFMA rate.
 #include <math.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "pf_internal.h"
@@ -1881,7 +1882,7 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
   });
 }
 
-__global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(AttnArgs a, ItemOrder ord) {
   __shared__ __attribute__((aligned(16))) char smem[kDkvBytes];
   const int n_ext_kb = (a.n_ext + kKeysPerWg - 1) / kKeysPerWg;
   const int n_own_kb = (a.rows + kKeysPerWg - 1) / kKeysPerWg;
@@ -1889,6 +1890,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(AttnArgs a) {
   int g, item;
   map_block(blockIdx.x, a.hkv, items, g, item);
   if (g >= a.hkv) return;
+  if (ord.n == items) item = ord.item[item];
   if (item < n_ext_kb * a.n_chunks) {
     const int kb = item / a.n_chunks;
     dkv_block<true>(a, g, kb, item - kb * a.n_chunks, a.n_chunks, smem);
@@ -1926,14 +1928,60 @@ hipError_t launch_bwd_dq_bf16(const AttnArgs& a, int32_t head_dim, hipStream_t s
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dkv_bf16(const AttnArgs& a, int32_t head_dim, hipStream_t stream) {
+// Query steps of item (key block kb, chunk c of nch) as dkv_block counts them,
+// with the own keys' visibility ends taken from the segment table.
+static int dkv_item_steps(const AttnArgs& a, const SegTable& seg, bool ext, int kb, int c, int nch) {
+  int n_it;
+  if (ext) {
+    n_it = (a.rows + kQStep - 1) / kQStep * a.group;
+  } else {
+    const int k0 = kb * kKeysPerWg, k1 = std::min(k0 + kKeysPerWg, a.rows);
+    int m = -1;
+    for (int i = 0; i < seg.n; ++i)
+      if (seg.start[i] < k1 && seg.start[i + 1] > k0) m = std::max(m, seg.vis_end[i]);
+    const int qhi = std::min(m, a.rows);
+    const int qt_lo = k0 / kQStep;
+    const int qt_hi = (qhi > k0) ? (qhi + kQStep - 1) / kQStep : qt_lo;
+    n_it = (qt_hi - qt_lo) * a.group;
+  }
+  if (nch <= 1) return n_it;
+  const int per = (n_it + nch - 1) / nch;
+  const int lo = std::min(n_it, c * per);
+  return std::min(n_it, lo + per) - lo;
+}
+
+void dkv_item_order(const AttnArgs& a, const SegTable& seg, ItemOrder& ord) {
+  ord.n = 0;
+  const int n_ext_kb = (a.n_ext + kKeysPerWg - 1) / kKeysPerWg;
+  const int n_own_kb = (a.rows + kKeysPerWg - 1) / kKeysPerWg;
+  const int n_ext_items = n_ext_kb * a.n_chunks;
+  const int items = n_ext_items + n_own_kb * a.n_chunks_own;
+  if (items <= 0 || items > kMaxOrderedItems) return;
+  // cost = query steps plus a fixed start-up (K/V loads, pipeline fill and
+  // drain, the result write) of about four steps
+  int cost[kMaxOrderedItems];
+  for (int i = 0; i < items; ++i) {
+    const bool ext = i < n_ext_items;
+    const int j = ext ? i : i - n_ext_items;
+    const int nch = ext ? a.n_chunks : a.n_chunks_own;
+    cost[i] = 4 + dkv_item_steps(a, seg, ext, j / nch, j % nch, nch);
+  }
+  for (int i = 0; i < items; ++i) ord.item[i] = (uint16_t)i;
+  std::stable_sort(ord.item, ord.item + items,
+                   [&](uint16_t x, uint16_t y) { return cost[x] > cost[y]; });
+  ord.n = items;
+}
+
+hipError_t launch_bwd_dkv_bf16(const AttnArgs& a, const ItemOrder& ord, int32_t head_dim,
+                               hipStream_t stream) {
   if (head_dim != kD) return hipErrorInvalidValue;
   const int n_ext_kb = (a.n_ext + kKeysPerWg - 1) / kKeysPerWg;
   const int n_own_kb = (a.rows + kKeysPerWg - 1) / kKeysPerWg;
   const int items = n_ext_kb * a.n_chunks + n_own_kb * a.n_chunks_own;
   if (items <= 0) return hipSuccess;
+  if (ord.n != 0 && ord.n != items) return hipErrorInvalidValue;
   PF_LAUNCH("pf_bwd_dkv_bf16", bwd_dkv_kernel, dim3(grid_for(a.hkv, items)), dim3(kThreads),
-            stream, a);
+            stream, a, ord);
   return hipGetLastError();
 }
 

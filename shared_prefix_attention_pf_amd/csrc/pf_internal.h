@@ -136,7 +136,22 @@ hipError_t launch_convert_acc(const float* src, void* dst, int64_t rows, int32_t
 
 hipError_t launch_fwd_bf16(const AttnArgs& a, int32_t head_dim, hipStream_t stream);
 hipError_t launch_bwd_dq_bf16(const AttnArgs& a, int32_t head_dim, hipStream_t stream);
-hipError_t launch_bwd_dkv_bf16(const AttnArgs& a, int32_t head_dim, hipStream_t stream);
+// Order in which the KV-stationary backward's workgroups of one KV head take
+// their items (key block x query chunk): item[i] is the item of the i-th
+// workgroup.  Workgroups are dispatched in index order to whichever CU frees
+// up first, so items sorted longest first make that a longest-first list
+// schedule; n == 0 keeps the natural order (external blocks, then own).
+constexpr int kMaxOrderedItems = 512;
+struct ItemOrder {
+  int32_t n;
+  uint16_t item[kMaxOrderedItems];
+};
+// Fills `ord` for the bf16 KV-stationary backward of `a`; the own-key query
+// ranges come from the segment table (the same visibility ends the prep
+// kernel writes).  Host only; leaves n = 0 when the items do not fit.
+void dkv_item_order(const AttnArgs& a, const SegTable& seg, ItemOrder& ord);
+hipError_t launch_bwd_dkv_bf16(const AttnArgs& a, const ItemOrder& ord, int32_t head_dim,
+                               hipStream_t stream);
 hipError_t launch_bwd_dq_ds_bf16(const AttnArgs& a, int32_t head_dim, hipStream_t stream);
 
 hipError_t launch_fwd_f32(const AttnArgs& a, int32_t head_dim, hipStream_t stream);
@@ -148,8 +163,8 @@ hipError_t launch_bwd_dkv_f32(const AttnArgs& a, int32_t head_dim, hipStream_t s
 // only, so results do not depend on the device.
 int32_t ext_chunks(int32_t n_ext, int32_t rows, int32_t hq, int32_t hkv, int32_t head_dim,
                    int32_t dtype);
-int32_t own_chunks(int32_t op, int32_t rows, int32_t hq, int32_t hkv, int32_t head_dim,
-                   int32_t dtype);
+int32_t own_chunks(int32_t op, int32_t n_ext, int32_t rows, int32_t hq, int32_t hkv,
+                   int32_t head_dim, int32_t dtype);
 // keys per workgroup of the bf16 KV-stationary kernel
 int32_t dkv_keys_per_workgroup_bf16();
 
