@@ -163,11 +163,13 @@ struct WsLayout {
   int32_t ds_keys = 0, ds_rows = 0, ds_own0 = 0;
 };
 
-// Phase B keeps dS^T when the workspace allows it: the buffer holds
-// Hq x (ceil256(P) + ceil256(rows)) keys x ceil256(rows) rows of bf16 (one
-// head's share must stay below 2 GiB for 32-bit buffer offsets).
+// A bf16 backward keeps dS^T when the workspace allows it (Phase B, Phase C
+// and trees): the buffer holds Hq x (ceil256(n_ext) + ceil256(rows)) keys x
+// ceil256(rows) rows of bf16, of which only the visible tiles are written and
+// read (one head's share must stay below 2 GiB for 32-bit buffer offsets).
 bool ds_eligible(int32_t op, const Desc& d, int32_t n_ext, int32_t rows) {
-  if (op != PF_OP_SUFFIX_BWD || d.dtype != PF_BF16 || rows <= 0) return false;
+  if (op != PF_OP_SUFFIX_BWD && op != PF_OP_PREFIX_BWD && op != PF_OP_TREE_BWD) return false;
+  if (d.dtype != PF_BF16 || rows <= 0) return false;
   const int64_t r = ((int64_t)rows + 255) / 256 * 256;
   const int64_t keys = ((int64_t)n_ext + 255) / 256 * 256 + r;
   return keys * r * 2 < ((int64_t)1 << 31);
@@ -224,6 +226,23 @@ pf::RowInfo row_info(void* ws, const WsLayout& w) {
   ri.bmin = (int32_t*)(b + w.bmin);
   ri.qhead = (int32_t*)(b + w.qhead);
   return ri;
+}
+
+// the dS^T buffer of a layout that has one
+void set_ds(pf::AttnArgs& a, void* ws, const WsLayout& w) {
+  if (!w.use_ds) return;
+  a.ds_ext = (__bf16*)((char*)ws + w.ds_ext);
+  a.ds_keys = w.ds_keys;
+  a.ds_rows = w.ds_rows;
+  a.ds_own0 = w.ds_own0;
+}
+
+// the full layout (with the dS^T buffer) when the workspace holds it, else
+// the minimal one; `w_min` has already been checked against the workspace
+WsLayout pick_layout(int32_t op, const Desc& d, int32_t n_ext, int32_t rows, size_t ws_bytes,
+                     const WsLayout& w_min) {
+  const WsLayout w_ds = layout(op, d, n_ext, rows, true);
+  return (w_ds.use_ds && ws_bytes >= w_ds.total) ? w_ds : w_min;
 }
 
 void set_own_parts(pf::AttnArgs& a, void* ws, const WsLayout& w) {
@@ -528,8 +547,7 @@ pf_status pf_suffix_attn_bwd_accum(const pf_attn_desc* desc, int32_t prefix_len,
   }
   const WsLayout w_min = layout(PF_OP_SUFFIX_BWD, d, prefix_len, rows, false);
   if ((s = check_stream_ws(workspace, workspace_bytes, w_min.total)) != PF_OK) return s;
-  const WsLayout w_ds = layout(PF_OP_SUFFIX_BWD, d, prefix_len, rows, true);
-  const WsLayout& w = (w_ds.use_ds && workspace_bytes >= w_ds.total) ? w_ds : w_min;
+  const WsLayout w = pick_layout(PF_OP_SUFFIX_BWD, d, prefix_len, rows, workspace_bytes, w_min);
   if (rows == 0) return PF_OK;
   pf::AttnArgs a = base_args(d, rows);
   set_q(a, q_s);
@@ -550,12 +568,7 @@ pf_status pf_suffix_attn_bwd_accum(const pf_attn_desc* desc, int32_t prefix_len,
   }
   a.dsum = (float*)((char*)workspace + w.dsum);
   a.lse2 = (float*)((char*)workspace + w.lse2);
-  if (w.use_ds) {
-    a.ds_ext = (__bf16*)((char*)workspace + w.ds_ext);
-    a.ds_keys = w.ds_keys;
-    a.ds_rows = w.ds_rows;
-    a.ds_own0 = w.ds_own0;
-  }
+  set_ds(a, workspace, w);
   set_own_parts(a, workspace, w);
   a.ri = row_info(workspace, w);
   return run_bwd(d, a, flat_segments(n_suffix, cu_seqlens), (hipStream_t)stream);
@@ -588,8 +601,10 @@ pf_status pf_prefix_bwd_inject(const pf_attn_desc* desc, int32_t prefix_len, pf_
     if ((s = check_ptr("gk_acc", gk_acc, 16)) != PF_OK) return s;
     if ((s = check_ptr("gv_acc", gv_acc, 16)) != PF_OK) return s;
   }
-  const WsLayout w = layout(PF_OP_PREFIX_BWD, d, 0, prefix_len);
-  if (has_do && (s = check_stream_ws(workspace, workspace_bytes, w.total)) != PF_OK) return s;
+  const WsLayout w_min = layout(PF_OP_PREFIX_BWD, d, 0, prefix_len);
+  if (has_do && (s = check_stream_ws(workspace, workspace_bytes, w_min.total)) != PF_OK) return s;
+  const WsLayout w = has_do ? pick_layout(PF_OP_PREFIX_BWD, d, 0, prefix_len, workspace_bytes, w_min)
+                            : w_min;
   if (prefix_len == 0) return PF_OK;
   hipStream_t st = (hipStream_t)stream;
   if (!has_do) {
@@ -619,6 +634,7 @@ pf_status pf_prefix_bwd_inject(const pf_attn_desc* desc, int32_t prefix_len, pf_
   a.lse = const_cast<float*>(lse_p);
   a.dsum = (float*)((char*)workspace + w.dsum);
   a.lse2 = (float*)((char*)workspace + w.lse2);
+  set_ds(a, workspace, w);
   set_own_parts(a, workspace, w);
   a.ri = row_info(workspace, w);
   return run_bwd(d, a, causal_segment(prefix_len), st);
@@ -669,9 +685,10 @@ pf_status pf_tree_attn_bwd(const pf_attn_desc* desc, int32_t n_nodes, const int3
   if ((s = check_tensor("dk", dk, rows, d.hkv, d, d.dtype)) != PF_OK) return s;
   if ((s = check_tensor("dv", dv, rows, d.hkv, d, d.dtype)) != PF_OK) return s;
   if (rows > 0 && (s = check_ptr("lse", lse, 4)) != PF_OK) return s;
-  const WsLayout w = layout(PF_OP_TREE_BWD, d, 0, rows);
-  if ((s = check_stream_ws(workspace, workspace_bytes, w.total)) != PF_OK) return s;
+  const WsLayout w_min = layout(PF_OP_TREE_BWD, d, 0, rows);
+  if ((s = check_stream_ws(workspace, workspace_bytes, w_min.total)) != PF_OK) return s;
   if (rows == 0) return PF_OK;
+  const WsLayout w = pick_layout(PF_OP_TREE_BWD, d, 0, rows, workspace_bytes, w_min);
   pf::AttnArgs a = base_args(d, rows);
   set_q(a, q);
   set_o(a, o);
@@ -683,6 +700,7 @@ pf_status pf_tree_attn_bwd(const pf_attn_desc* desc, int32_t n_nodes, const int3
   a.lse = const_cast<float*>(lse);
   a.dsum = (float*)((char*)workspace + w.dsum);
   a.lse2 = (float*)((char*)workspace + w.lse2);
+  set_ds(a, workspace, w);
   set_own_parts(a, workspace, w);
   a.ri = row_info(workspace, w);
   return run_bwd(d, a, tree_segments(n_nodes, node_off, send), (hipStream_t)stream);

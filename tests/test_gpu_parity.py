@@ -174,6 +174,60 @@ def test_tree(seed, hq, hkv, dtype):
         check(name, host(got), ref[name.lower()], tol)
 
 
+def test_phase_c_and_tree_min_workspace():
+    """Phase C and the tree backward with the smallest workspace (dQ recomputes
+    S and dP) and with the full one (dQ from the stored dS), each against the
+    oracle and against each other."""
+    hq, hkv, d, p = 8, 2, 128, 300
+    g = random_small_group(23, hq, hkv, d, p, [1], "bf16")
+    desc = _desc(hq, hkv, d, "bf16")
+    scale = 1.0 / math.sqrt(d)
+    hmap = oracle.head_map(hq, hkv)
+    rng = np.random.default_rng(5)
+    gk_np = rng.standard_normal((p, hkv, d)).astype(np.float32)
+    gv_np = rng.standard_normal((p, hkv, d)).astype(np.float32)
+    t = {k: dev(g[k], "bf16") for k in ("q_p", "k_p", "v_p", "do_p")}
+    o_p, lse_p = G.prefix_fwd(desc, t["q_p"], t["k_p"], t["v_p"])
+    gk, gv = torch.from_numpy(gk_np).cuda(), torch.from_numpy(gv_np).cuda()
+    n_min = pf.pf_workspace_size_min(pf.PF_OP_PREFIX_BWD, desc, p, p)
+    n_full = pf.pf_workspace_size(pf.PF_OP_PREFIX_BWD, desc, p, p)
+    assert n_full > n_min
+    outs = []
+    for n_ws in (n_min, n_full):
+        ws = torch.empty(n_ws, dtype=torch.uint8, device="cuda")
+        outs.append([host(x) for x in G.prefix_bwd(desc, t["q_p"], t["k_p"], t["v_p"], o_p, lse_p,
+                                                   t["do_p"], gk, gv, ws=ws)])
+    torch.cuda.synchronize()
+    ref = oracle.prefix_backward_inject(g["q_p"], g["k_p"], g["v_p"], g["do_p"], gk_np, gv_np,
+                                        scale, hmap)
+    for name, mn, full, r in zip(("dQ_P", "dK_P", "dV_P"), outs[0], outs[1], ref):
+        check(f"{name} (min ws)", mn, r, TOL["bf16"])
+        check(f"{name} (dS buffer)", full, r, TOL["bf16"])
+        check(f"{name}: min ws vs dS buffer", mn, full, TOL["bf16"])
+
+    node_off, parent = random_tree(4, 9, max_len=90, min_len=0)
+    print(f"\ntree node_off {node_off.tolist()} parent {parent.tolist()}", flush=True)
+    rows = int(node_off[-1])
+    tg = random_tree_group(4, node_off, hq, hkv, d, "bf16")
+    tt = {k: dev(tg[k], "bf16") for k in ("q", "k", "v", "do")}
+    o, lse = G.tree_fwd(desc, node_off, parent, tt["q"], tt["k"], tt["v"])
+    n_min = pf.pf_workspace_size_min(pf.PF_OP_TREE_BWD, desc, 0, rows)
+    n_full = pf.pf_workspace_size(pf.PF_OP_TREE_BWD, desc, 0, rows)
+    assert n_full > n_min
+    outs = []
+    for n_ws in (n_min, n_full):
+        ws = torch.empty(n_ws, dtype=torch.uint8, device="cuda")
+        outs.append([host(x) for x in G.tree_bwd(desc, node_off, parent, tt["q"], tt["k"],
+                                                 tt["v"], o, lse, tt["do"], ws=ws)])
+    torch.cuda.synchronize()
+    ref = oracle.tree_attention_direct(tg["q"], tg["k"], tg["v"], tg["do"], node_off, parent,
+                                       scale, hmap)
+    for name, mn, full in zip(("dq", "dk", "dv"), outs[0], outs[1]):
+        check(f"tree {name} (min ws)", mn, ref[name], TOL["bf16"])
+        check(f"tree {name} (dS buffer)", full, ref[name], TOL["bf16"])
+        check(f"tree {name}: min ws vs dS buffer", mn, full, TOL["bf16"])
+
+
 def _phase_b_run(desc, t, cu, p, calls):
     """Run Phase B as the given microbatches (lists of suffix indices); return gK, gV."""
     hkv, d = t["k_p"].shape[1], t["k_p"].shape[2]
