@@ -252,7 +252,7 @@ KERNEL_SYMBOL = {"pf_fwd_bf16": "fwd_kernel", "pf_bwd_dq_bf16": "bwd_dq_kernel",
                  "pf_bwd_dq_ds_bf16": "bwd_dq_ds_kernel", "pf_bwd_dkv_bf16": "bwd_dkv_kernel",
                  "pf_fwd_f32": "fwd_f32_kernel", "pf_bwd_dq_f32": "dq_f32_kernel",
                  "pf_bwd_dkv_f32": "dkv_f32_kernel", "pf_prep_dsum": "prep_dsum_kernel",
-                 "pf_reduce": "reduce_partials_kernel", "pf_finish_own": "finish_own_kernel"}
+                 "pf_partials": "partial_sums_kernel"}
 COPY_SYMBOL = "neg_kernel"       # the elementwise copy run by --copy-probe-mib
 
 

@@ -193,7 +193,7 @@ WsLayout layout(int32_t op, const Desc& d, int32_t n_ext, int32_t rows, bool wan
   if (op == PF_OP_SUFFIX_BWD) {
     w.n_chunks = pf::ext_chunks(n_ext, rows, d.hq, d.hkv, d.d, d.dtype);
     if (w.n_chunks > 1) {
-      const size_t part = (size_t)w.n_chunks * n_ext * d.hkv * d.d * 4;
+      const size_t part = (size_t)(w.n_chunks - 1) * n_ext * d.hkv * d.d * 4;
       w.gk_part = off; off += align_up(part);
       w.gv_part = off; off += align_up(part);
     }
@@ -347,18 +347,34 @@ pf_status run_bwd(const Desc& d, const pf::AttnArgs& a, const pf::SegTable& seg,
     e = d.dtype == PF_BF16 ? pf::launch_bwd_dkv_bf16(a, ord, d.d, st) : pf::launch_bwd_dkv_f32(a, d.d, st);
     if (e != hipSuccess) return hip_fail(e, "dkv");
   }
-  if (a.n_chunks > 1 && a.n_ext > 0) {
-    const int64_t n = (int64_t)a.n_ext * d.hkv * d.d;
-    e = pf::launch_reduce_partials(a.gk_part, a.gk_acc, a.gv_part, a.gv_acc, a.n_chunks, n, st);
-    if (e != hipSuccess) return hip_fail(e, "reduce");
-  }
-  if (a.n_chunks_own > 1) {
-    const pf::OwnFinish fk{(const float4*)a.dk_part, (const float4*)a.gk_init, (char*)a.dk_own,
-                           a.dko_st, a.dko_sh};
-    const pf::OwnFinish fv{(const float4*)a.dv_part, (const float4*)a.gv_init, (char*)a.dv_own,
-                           a.dvo_st, a.dvo_sh};
-    e = pf::launch_finish_own(fk, fv, a.n_chunks_own, a.rows, d.hkv, d.d, a.dkv_f32, st);
-    if (e != hipSuccess) return hip_fail(e, "finish");
+  // the split blocks' partials: gK/gV += later chunks, own dK/dV = init +
+  // chunks, in one launch
+  const bool ext_parts = a.n_chunks > 1 && a.n_ext > 0;
+  const bool own_parts = a.n_chunks_own > 1;
+  if (ext_parts || own_parts) {
+    pf::PartialSums ps;
+    memset(&ps, 0, sizeof(ps));
+    if (ext_parts) {
+      ps.ext_planes = a.n_chunks - 1;
+      ps.ext_n4 = (int64_t)a.n_ext * d.hkv * d.d / 4;
+      ps.part_k = (const float4*)a.gk_part;
+      ps.part_v = (const float4*)a.gv_part;
+      ps.acc_k = (float4*)a.gk_acc;
+      ps.acc_v = (float4*)a.gv_acc;
+    }
+    if (own_parts) {
+      ps.own_planes = a.n_chunks_own;
+      ps.fk = pf::OwnFinish{(const float4*)a.dk_part, (const float4*)a.gk_init, (char*)a.dk_own,
+                            a.dko_st, a.dko_sh};
+      ps.fv = pf::OwnFinish{(const float4*)a.dv_part, (const float4*)a.gv_init, (char*)a.dv_own,
+                            a.dvo_st, a.dvo_sh};
+      ps.rows = a.rows;
+      ps.heads = d.hkv;
+      ps.d = d.d;
+      ps.dst_f32 = a.dkv_f32;
+    }
+    e = pf::launch_partial_sums(ps, st);
+    if (e != hipSuccess) return hip_fail(e, "partials");
   }
   return PF_OK;
 }

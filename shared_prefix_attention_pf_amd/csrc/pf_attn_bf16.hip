@@ -1824,8 +1824,12 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
   // lane holds key kw0 + 32 kt + col, d = 32 dt + 8 j + 4 h32 + r.  One
   // (key tile, d tile) at a time, so the epilogue reads 32 accumulators at once.
   fence_acc(dk, dv);
-  // destination: 0 add into gK/gV, 1 external partial, 2 own partial, 3 own output
-  const int mode = ext ? (nch == 1 ? 0 : 1) : (nch > 1 ? 2 : 3);
+  // destination: 0 add into gK/gV, 1 external partial, 2 own partial, 3 own output.
+  // The first query chunk of a split external block adds into gK/gV itself
+  // (no other workgroup touches those elements during the launch); chunks
+  // 1.. write partial planes 0.. that the finishing pass adds afterwards, so
+  // every element is acc + c0 + (c1 + c2 + ...), a fixed order.
+  const int mode = ext ? ((nch == 1 || chunk == 0) ? 0 : 1) : (nch > 1 ? 2 : 3);
   static_for<0, 2>([&](auto ktc) {
     constexpr int kt = decltype(ktc)::value;
     const int kk = kw0 + kt * 32 + col;
@@ -1846,7 +1850,7 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
             *(f32x4*)(a.gk_acc + base + d) += vk;
             *(f32x4*)(a.gv_acc + base + d) += vv;
           } else if (mode == 1) {
-            const int64_t pb = (int64_t)chunk * a.n_ext * a.hkv * kD + base;
+            const int64_t pb = (int64_t)(chunk - 1) * a.n_ext * a.hkv * kD + base;
             *(f32x4*)(a.gk_part + pb + d) = vk;
             *(f32x4*)(a.gv_part + pb + d) = vv;
           } else if (mode == 2) {

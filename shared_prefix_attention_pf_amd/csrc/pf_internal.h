@@ -79,10 +79,10 @@ struct AttnArgs {
   const float* gv_init;                   //   and dV before the rounding (Phase C)
   // external-key gradient destination: fp32 [n_ext, Hkv, d]
   float* gk_acc; float* gv_acc;           // accumulators (RMW when n_chunks == 1)
-  float* gk_part; float* gv_part;         // partials [n_chunks, n_ext, Hkv, d]
+  float* gk_part; float* gv_part;         // partials of chunks 1.. [n_chunks - 1, n_ext, Hkv, d]
   int32_t n_chunks;                       // query chunks per external key block
   // own-key gradient partials when own key blocks are split over query
-  // chunks: fp32 [n_chunks_own, rows, Hkv, d], finished by launch_finish_own
+  // chunks: fp32 [n_chunks_own, rows, Hkv, d], finished by launch_partial_sums
   float* dk_part; float* dv_part;
   int32_t n_chunks_own;
   // Phase B with a dS buffer: the dK/dV pass stores dS^T of every key block
@@ -114,10 +114,6 @@ hipError_t launch_prep(const SegTable& seg, const HeadTable& heads, RowInfo ri, 
 // a.dsum / a.lse2 (bf16 inputs).
 hipError_t launch_prep_dsum_bf16(const SegTable& seg, const HeadTable& heads, const AttnArgs& a,
                                  hipStream_t stream);
-// acc_k += sum of the n_chunks partials part_k[c] (fixed pairwise order), and
-// the same for the V arrays, in one launch; n elements per array
-hipError_t launch_reduce_partials(const float* part_k, float* acc_k, const float* part_v,
-                                  float* acc_v, int32_t n_chunks, int64_t n, hipStream_t stream);
 hipError_t launch_fill_zero(void* dst, int64_t rows, int32_t heads, int32_t d, int64_t st,
                             int64_t sh, int32_t elem_bytes, hipStream_t stream);
 // One own-key gradient (dK or dV) to finish: dst = convert(init + sum of the
@@ -129,8 +125,25 @@ struct OwnFinish {
   char* dst;
   int64_t st, sh;
 };
-hipError_t launch_finish_own(OwnFinish fk, OwnFinish fv, int32_t n_chunks, int64_t rows,
-                             int32_t heads, int32_t d, int32_t dst_f32, hipStream_t stream);
+// The split key blocks' partials of one backward call, summed in a fixed
+// pairwise order ((p0 + p1) + (p2 + p3)) + ...:
+//   external: acc += sum of ext_planes planes (the first chunk already added
+//             itself), K and V, ext_n4 float4 each;
+//   own:      dst = convert(init + sum of own_planes planes), dK and dV.
+// A part with zero planes is skipped; both run in one launch.
+struct PartialSums {
+  int32_t ext_planes;
+  int64_t ext_n4;
+  const float4* part_k;
+  const float4* part_v;
+  float4* acc_k;
+  float4* acc_v;
+  int32_t own_planes;
+  OwnFinish fk, fv;
+  int64_t rows;
+  int32_t heads, d, dst_f32;
+};
+hipError_t launch_partial_sums(const PartialSums& ps, hipStream_t stream);
 hipError_t launch_convert_acc(const float* src, void* dst, int64_t rows, int32_t heads, int32_t d,
                               int64_t st, int64_t sh, int32_t dst_f32, hipStream_t stream);
 

@@ -1,11 +1,11 @@
 // Small device kernels around the attention kernels:
 //   - prep: per-row kend[] and its 32-key block min/max from the segment table;
-//   - reduce: gK/gV accumulator += sum of per-chunk partials, in a fixed
-//     pairwise order (contention-free and run-to-run deterministic; this is
-//     the per-suffix accumulation of PrefixFlow §3.1 "Savings over the
-//     baseline", an element-wise O(|P| d) add);
-//   - own-key finish: dK/dV of own keys = init + sum of per-chunk partials,
-//     in the same fixed order, converted to the output dtype;
+//   - partial sums, one launch: gK/gV accumulator += the later query chunks'
+//     partials of split prefix key blocks, in a fixed pairwise order
+//     (contention-free and run-to-run deterministic; this is the per-suffix
+//     accumulation of PrefixFlow §3.1 "Savings over the baseline", an
+//     element-wise O(|P| d) add), and dK/dV of split own key blocks = init +
+//     sum of their partials, converted to the output dtype;
 //   - D = rowsum(dO * O) and LSE in log2 units for the backward passes;
 //   - zero fill and fp32 -> output conversion for Phase C with no upstream.
 #include <math.h>
@@ -106,7 +106,7 @@ hipError_t launch_prep_dsum_bf16(const SegTable& seg, const HeadTable& heads, co
   return hipGetLastError();
 }
 
-// acc[i] += (((p0 + p1) + (p2 + p3)) + ...)  over n_chunks partials of n floats.
+// (((p0 + p1) + (p2 + p3)) + ...) over nc partial planes of n4 float4 each (planes past nc are zero).
 template <int NC>
 __device__ inline float4 tree_sum(const float4* part, int64_t n4, int64_t i, int nc) {
   float4 v[NC];
@@ -122,52 +122,37 @@ __device__ inline float4 tree_sum(const float4* part, int64_t n4, int64_t i, int
   return v[0];
 }
 
-// blockIdx.y selects the K (0) or V (1) pair of arrays
-__global__ __launch_bounds__(256) void reduce_partials_kernel(const float4* __restrict__ part_k,
-                                                              float4* __restrict__ acc_k,
-                                                              const float4* __restrict__ part_v,
-                                                              float4* __restrict__ acc_v,
-                                                              int nc, int64_t n4) {
-  const float4* __restrict__ part = blockIdx.y ? part_v : part_k;
-  float4* __restrict__ acc = blockIdx.y ? acc_v : acc_k;
+// Sums of the split key blocks' partial planes (PartialSums).  blockIdx.y +
+// y0 selects the array: 0 / 1 external K / V (acc += planes), 2 / 3 own dK /
+// dV (dst = convert(init + planes)).
+__global__ __launch_bounds__(256) void partial_sums_kernel(PartialSums ps, int y0) {
+  const int y = (int)blockIdx.y + y0;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
-    float4 s;
-    if (nc <= 2) s = tree_sum<2>(part, n4, i, nc);
-    else if (nc <= 4) s = tree_sum<4>(part, n4, i, nc);
-    else s = tree_sum<8>(part, n4, i, nc);
-    float4 a = acc[i];
-    a.x += s.x; a.y += s.y; a.z += s.z; a.w += s.w;
-    acc[i] = a;
+  if (y < 2) {
+    const float4* __restrict__ part = y ? ps.part_v : ps.part_k;
+    float4* __restrict__ acc = y ? ps.acc_v : ps.acc_k;
+    const int nc = ps.ext_planes;
+    const int64_t n4 = ps.ext_n4;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+      float4 s;
+      if (nc == 1) s = part[i];
+      else if (nc <= 2) s = tree_sum<2>(part, n4, i, nc);
+      else if (nc <= 4) s = tree_sum<4>(part, n4, i, nc);
+      else s = tree_sum<8>(part, n4, i, nc);
+      float4 a = acc[i];
+      a.x += s.x; a.y += s.y; a.z += s.z; a.w += s.w;
+      acc[i] = a;
+    }
+    return;
   }
-}
-
-hipError_t launch_reduce_partials(const float* part_k, float* acc_k, const float* part_v,
-                                  float* acc_v, int32_t n_chunks, int64_t n, hipStream_t stream) {
-  if (n <= 0) return hipSuccess;
-  const int64_t n4 = n / 4;  // n is a multiple of head_dim (>= 64)
-  int64_t blocks = (n4 + 255) / 256;
-  if (blocks > 2048) blocks = 2048;
-  PF_LAUNCH("pf_reduce", reduce_partials_kernel, dim3((unsigned)blocks, 2), dim3(256), stream,
-            (const float4*)part_k, (float4*)acc_k, (const float4*)part_v, (float4*)acc_v,
-            (int)n_chunks, n4);
-  return hipGetLastError();
-}
-
-// dst[r, h, :] = convert(init[r, h, :] + sum_c part[c, r, h, :]); part and
-// init are contiguous [rows, heads, d] fp32, dst is strided.
-// blockIdx.y selects dK (0) or dV (1)
-__global__ __launch_bounds__(256) void finish_own_kernel(OwnFinish fk, OwnFinish fv, int nc,
-                                                         int64_t rows, int heads, int d,
-                                                         int dst_f32) {
-  const OwnFinish& fo = blockIdx.y ? fv : fk;
+  const OwnFinish& fo = (y == 3) ? ps.fv : ps.fk;
   const float4* __restrict__ part = fo.part;
   const float4* __restrict__ init = fo.init;
   char* dst = fo.dst;
   const int64_t st = fo.st, sh = fo.sh;
-  const int per = d / 4;
-  const int64_t n4 = rows * heads * per;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int nc = ps.own_planes, heads = ps.heads;
+  const int per = ps.d / 4;
+  const int64_t n4 = ps.rows * heads * per;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
     float4 v;
     if (nc <= 2) v = tree_sum<2>(part, n4, i, nc);
@@ -182,7 +167,7 @@ __global__ __launch_bounds__(256) void finish_own_kernel(OwnFinish fk, OwnFinish
     const int h = (int)(rh % heads);
     const int64_t r = rh / heads;
     const int64_t off = r * st + (int64_t)h * sh + c * 4;   // elements
-    if (dst_f32) {
+    if (ps.dst_f32) {
       *(float4*)((float*)dst + off) = v;
     } else {
       __bf16* o = (__bf16*)dst + off;
@@ -191,14 +176,18 @@ __global__ __launch_bounds__(256) void finish_own_kernel(OwnFinish fk, OwnFinish
   }
 }
 
-hipError_t launch_finish_own(OwnFinish fk, OwnFinish fv, int32_t n_chunks, int64_t rows,
-                             int32_t heads, int32_t d, int32_t dst_f32, hipStream_t stream) {
-  if (rows <= 0) return hipSuccess;
-  const int64_t total = rows * heads * (d / 4);
-  int64_t blocks = (total + 255) / 256;
+hipError_t launch_partial_sums(const PartialSums& ps, hipStream_t stream) {
+  const bool ext = ps.ext_planes > 0 && ps.ext_n4 > 0;
+  const bool own = ps.own_planes > 1 && ps.rows > 0;
+  if (!ext && !own) return hipSuccess;
+  const int64_t own_n4 = own ? ps.rows * ps.heads * (ps.d / 4) : 0;
+  const int64_t n4 = ext && ps.ext_n4 > own_n4 ? ps.ext_n4 : own_n4;
+  int64_t blocks = (n4 + 255) / 256;
   if (blocks > 2048) blocks = 2048;
-  PF_LAUNCH("pf_finish_own", finish_own_kernel, dim3((unsigned)blocks, 2), dim3(256), stream, fk,
-            fv, (int)n_chunks, rows, (int)heads, (int)d, (int)dst_f32);
+  const int y0 = ext ? 0 : 2;
+  const int ny = (ext ? 2 : 0) + (own ? 2 : 0);
+  PF_LAUNCH("pf_partials", partial_sums_kernel, dim3((unsigned)blocks, (unsigned)ny), dim3(256),
+            stream, ps, y0);
   return hipGetLastError();
 }
 
