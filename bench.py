@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--stats-summary", nargs=2, metavar=("STATS_CSV", "OUT_MD"), default=None,
                     help="no GPU work: turn a rocprofv3 --kernel-trace --stats csv of this script "
                          "into a kernel-time summary")
+    ap.add_argument("--counter-summary", nargs="+", metavar="RUN_DIR_OR_OUT_MD", default=None,
+                    help="no GPU work: turn rocprofv3 --pmc runs of SQ_ counters (their output "
+                         "directories, then the output file) into a per-kernel counter summary")
     ap.add_argument("--pmc-command", default="",
                     help="with --traffic-summary / --stats-summary: the profiling commands, "
                          "recorded in the summary")
@@ -369,6 +372,74 @@ def stats_summary(stats_csv, out_md, cid, command):
     print("\n".join(lines))
 
 
+# phases a single-call group step launches each kernel in (full workspace)
+PHASES_OF = {"fwd_kernel": ("A", "B"), "bwd_dkv_kernel": ("B", "C"),
+             "bwd_dq_ds_kernel": ("B", "C"), "prep_dsum_kernel": ("B", "C"),
+             "partial_sums_kernel": ("B", "C")}
+
+
+def counter_summary(run_dirs, out_md, cid, command):
+    """Per-kernel SQ counter table (last dispatch of each kernel and phase) from
+    rocprofv3 --pmc runs of one bench step, with the derived shares of the
+    shader clock: MFMA busy, and per wave the time issuing or waiting."""
+    import csv
+    import glob
+    per = {}        # (kernel, k-th dispatch of it) -> {counter: value}
+    for d in run_dirs:
+        for fn in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            disp = {}
+            for r in csv.DictReader(open(fn)):
+                m = re.search(r"(\w+_kernel)", r["Kernel_Name"])
+                if not m or m.group(1) not in KERNEL_SYMBOL.values():
+                    continue
+                did = int(r["Dispatch_Id"])
+                disp.setdefault(did, [m.group(1), {}])
+                c = disp[did][1]
+                c[r["Counter_Name"]] = c.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            seen = {}
+            for did in sorted(disp):
+                k, c = disp[did]
+                seen.setdefault(k, []).append(c)
+            for k, lst in seen.items():
+                # one step of a single-call group launches each kernel once in
+                # each phase that uses it, in phase order; keep the last step's
+                phases = PHASES_OF.get(k, ("B",))
+                for ph, c in zip(phases, lst[-len(phases):]):
+                    per.setdefault((k, ph), {}).update(c)
+    names = ["SQ_CYCLES", "SQ_BUSY_CU_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA",
+             "SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_WAVE_CYCLES", "SQ_WAIT_ANY",
+             "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY", "SQ_VALU_MFMA_COEXEC_CYCLES"]
+    lines = [f"# SQ counters per kernel, config {cid} (rocprofv3 --pmc)", "",
+             "Commands (run from the repository root on one MI355X):", "", "```", command.strip(),
+             "```", "",
+             "Raw counters are summed over the chip. Derived: clock = SQ_CYCLES / 32 shader "
+             "engines / kernel time; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs / "
+             "(SQ_CYCLES / 32); wave shares = SQ_ACTIVE_INST_ANY, SQ_WAIT_ANY (at an "
+             "s_waitcnt) and SQ_WAIT_INST_ANY (instruction not yet issuable) over "
+             "SQ_WAVE_CYCLES.", "",
+             "| kernel (phase) | " + " | ".join(names) +
+             " | VALU / MFMA | MFMA busy | issuing | at s_waitcnt | waiting to issue |",
+             "|---" * (len(names) + 6) + "|"]
+    for (k, ph), c in sorted(per.items()):
+        vals = [c.get(n) for n in names]
+        cyc = c.get("SQ_CYCLES")
+        mf = c.get("SQ_VALU_MFMA_BUSY_CYCLES")
+        wc = c.get("SQ_WAVE_CYCLES")
+
+        def share(x):
+            return f"{100 * x / wc:.0f}%" if x is not None and wc else "-"
+        busy = f"{100 * mf / 1024 / (cyc / 32):.0f}%" if mf is not None and cyc else "-"
+        vpm = (f"{(c['SQ_INSTS_VALU'] - c['SQ_INSTS_MFMA']) / c['SQ_INSTS_MFMA']:.2f}"
+               if c.get("SQ_INSTS_MFMA") and c.get("SQ_INSTS_VALU") is not None else "-")
+        lines.append(f"| {k} ({ph}) | " + " | ".join("-" if v is None else f"{v:.4g}" for v in vals)
+                     + f" | {vpm} | {busy} | {share(c.get('SQ_ACTIVE_INST_ANY'))} | "
+                     f"{share(c.get('SQ_WAIT_ANY'))} | {share(c.get('SQ_WAIT_INST_ANY'))} |")
+    lines += ["", f"kernel sources sha256: `{kernel_source_hash()}`", ""]
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def load_traffic(cid, label):
     """HBM bytes per launch of `label` from the stored counter summary, or None
     when there is none or the kernel sources changed since it was taken."""
@@ -439,10 +510,15 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path runs on one GPU; see the sharding notes in DESIGN.md)", file=sys.stderr)
+              "(the path runs on one GPU: heads, groups or suffixes would shard across GPUs, "
+              "none of which is built here)", file=sys.stderr)
         sys.exit(2)
     if args.stats_summary:
         stats_summary(args.stats_summary[0], args.stats_summary[1], args.config, args.pmc_command)
+        return
+    if args.counter_summary:
+        counter_summary(args.counter_summary[:-1], args.counter_summary[-1], args.config,
+                        args.pmc_command)
         return
     if args.traffic_summary:
         fdir, wdir, out_md = args.traffic_summary

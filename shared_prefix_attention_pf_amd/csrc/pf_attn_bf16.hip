@@ -1217,7 +1217,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_ds_kernel(AttnArgs a) {
   int g, item;
   map_block(blockIdx.x, a.hkv, a.group * n_tt, g, item);
   if (g >= a.hkv) return;
-  const int j = item / n_tt, tt = item - j * n_tt;
+  // later token tiles first: under a causal or tree mask they see the most keys
+  const int j = item / n_tt, tt = n_tt - 1 - (item - j * n_tt);
   const int head = ld_uniform(a.ri.qhead, g * a.group + j);
   const int t0 = tt * kDxTok;
 
