@@ -284,13 +284,20 @@ __device__ __forceinline__ void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" :
 
 // Workgroup -> (KV head, item) with XCD awareness: workgroups are dispatched
 // round-robin over the 8 XCDs, so when Hkv is a multiple of 8 every XCD gets
-// the items of its own KV heads (their K/V or Q/dO stay in that XCD's L2).
+// the items of its own KV heads (their K/V or Q/dO stay in that XCD's L2),
+// and when Hkv divides 8 every KV head gets 8 / Hkv XCDs of its own.  Padding
+// workgroups of the second form get g = Hkv (the kernels return at once).
 __device__ __forceinline__ void map_block(int bid, int hkv, int items, int& g, int& item) {
   if ((hkv & 7) == 0) {
     const int xcd = bid & 7, pos = bid >> 3;
     const int hh = pos / items;
     item = pos - hh * items;
     g = xcd + 8 * hh;
+  } else if ((8 % hkv) == 0) {
+    const int xpg = 8 / hkv, xcd = bid & 7;
+    g = xcd / xpg;
+    item = (bid >> 3) * xpg + (xcd - g * xpg);
+    if (item >= items) g = hkv;
   } else {
     g = bid / items;
     item = bid - g * items;
@@ -1909,6 +1916,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(AttnArgs a, ItemOr
 // grid size: per-KV-head items, padded so the XCD mapping covers every item
 int grid_for(int hkv, int items) {
   if ((hkv & 7) == 0) return 8 * ((hkv / 8) * items);
+  if ((8 % hkv) == 0) {
+    const int xpg = 8 / hkv;
+    return 8 * ((items + xpg - 1) / xpg);
+  }
   return hkv * items;
 }
 
