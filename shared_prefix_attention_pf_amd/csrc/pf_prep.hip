@@ -63,26 +63,41 @@ hipError_t launch_prep(const SegTable& seg, const HeadTable& heads, RowInfo ri,
 }
 
 // D and LSE (log2) per (row, query head): 16 lanes per pair, each lane
-// reading 8 head_dim values of dO and O (head_dim 128); block `blk` covers
-// 16 pairs.
+// reading 8 head_dim values of dO and O (head_dim 128); a 16-lane group
+// covers kDsumPairs consecutive pairs, all of whose loads are issued before
+// the first product so that enough bytes are in flight to stream from HBM;
+// block `blk` covers 16 kDsumPairs pairs.
+constexpr int kDsumPairs = 4;
 __device__ __forceinline__ void dsum_body(const AttnArgs& a, int blk) {
   typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-  const int64_t pair = (int64_t)blk * 16 + (threadIdx.x >> 4);
   const int sub = threadIdx.x & 15;
   const int64_t n = (int64_t)a.rows * a.hq;
-  const int64_t pc = pair < n ? pair : n - 1;
-  const int h = (int)(pc / a.rows), t = (int)(pc - (int64_t)h * a.rows);
-  const bf16x8 dv = *(const bf16x8*)((const __bf16*)a.dout + (int64_t)t * a.do_st + (int64_t)h * a.do_sh + 8 * sub);
-  const bf16x8 ov = *(const bf16x8*)((const __bf16*)a.o + (int64_t)t * a.o_st + (int64_t)h * a.o_sh + 8 * sub);
-  float dot = 0.f;
+  const int64_t p0 = ((int64_t)blk * 16 + (threadIdx.x >> 4)) * kDsumPairs;
+  bf16x8 dv[kDsumPairs], ov[kDsumPairs];
+  int hh[kDsumPairs], tt[kDsumPairs];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) dot = fmaf((float)dv[e], (float)ov[e], dot);
+  for (int u = 0; u < kDsumPairs; ++u) {
+    const int64_t pc = p0 + u < n ? p0 + u : n - 1;
+    hh[u] = (int)(pc / a.rows);
+    tt[u] = (int)(pc - (int64_t)hh[u] * a.rows);
+    dv[u] = *(const bf16x8*)((const __bf16*)a.dout + (int64_t)tt[u] * a.do_st +
+                             (int64_t)hh[u] * a.do_sh + 8 * sub);
+    ov[u] = *(const bf16x8*)((const __bf16*)a.o + (int64_t)tt[u] * a.o_st +
+                             (int64_t)hh[u] * a.o_sh + 8 * sub);
+  }
 #pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 16);
-  if (sub == 0 && pair < n) {
-    const float l = a.lse[(int64_t)h * a.rows + t];
-    a.dsum[(int64_t)h * a.rows + t] = dot;
-    a.lse2[(int64_t)h * a.rows + t] = (l == -INFINITY) ? INFINITY : l * 1.4426950408889634f;
+  for (int u = 0; u < kDsumPairs; ++u) {
+    float dot = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dot = fmaf((float)dv[u][e], (float)ov[u][e], dot);
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 16);
+    if (sub == 0 && p0 + u < n) {
+      const int64_t i = (int64_t)hh[u] * a.rows + tt[u];
+      const float l = a.lse[i];
+      a.dsum[i] = dot;
+      a.lse2[i] = (l == -INFINITY) ? INFINITY : l * 1.4426950408889634f;
+    }
   }
 }
 
@@ -101,7 +116,9 @@ hipError_t launch_prep_dsum_bf16(const SegTable& seg, const HeadTable& heads, co
   const int64_t n = (int64_t)a.rows * a.hq;
   if (n <= 0) return hipSuccess;
   const int np = prep_blocks(seg, heads);
-  PF_LAUNCH("pf_prep_dsum", prep_dsum_kernel, dim3((unsigned)(np + (n + 15) / 16)), dim3(256),
+  const int64_t per_blk = 16 * kDsumPairs;
+  PF_LAUNCH("pf_prep_dsum", prep_dsum_kernel, dim3((unsigned)(np + (n + per_blk - 1) / per_blk)),
+            dim3(256),
             stream, seg, heads, a.ri, a, np);
   return hipGetLastError();
 }
