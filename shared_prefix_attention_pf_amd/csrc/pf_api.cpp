@@ -323,6 +323,33 @@ pf_status run_fwd(const Desc& d, const pf::AttnArgs& a, const pf::SegTable& seg,
   return PF_OK;
 }
 
+// the split key blocks' partial sums of a backward call (empty when no block
+// is split)
+pf::PartialSums partial_sums_of(const Desc& d, const pf::AttnArgs& a) {
+  pf::PartialSums ps;
+  memset(&ps, 0, sizeof(ps));
+  if (a.n_chunks > 1 && a.n_ext > 0) {
+    ps.ext_planes = a.n_chunks - 1;
+    ps.ext_n4 = (int64_t)a.n_ext * d.hkv * d.d / 4;
+    ps.part_k = (const float4*)a.gk_part;
+    ps.part_v = (const float4*)a.gv_part;
+    ps.acc_k = (float4*)a.gk_acc;
+    ps.acc_v = (float4*)a.gv_acc;
+  }
+  if (a.n_chunks_own > 1) {
+    ps.own_planes = a.n_chunks_own;
+    ps.fk = pf::OwnFinish{(const float4*)a.dk_part, (const float4*)a.gk_init, (char*)a.dk_own,
+                          a.dko_st, a.dko_sh};
+    ps.fv = pf::OwnFinish{(const float4*)a.dv_part, (const float4*)a.gv_init, (char*)a.dv_own,
+                          a.dvo_st, a.dvo_sh};
+    ps.rows = a.rows;
+    ps.heads = d.hkv;
+    ps.d = d.d;
+    ps.dst_f32 = a.dkv_f32;
+  }
+  return ps;
+}
+
 pf_status run_bwd(const Desc& d, const pf::AttnArgs& a, const pf::SegTable& seg, hipStream_t st) {
   hipError_t e;
   // longest-first order of the KV-stationary items (a host-side plan; no
@@ -330,52 +357,28 @@ pf_status run_bwd(const Desc& d, const pf::AttnArgs& a, const pf::SegTable& seg,
   pf::ItemOrder ord;
   ord.n = 0;
   if (d.dtype == PF_BF16) pf::dkv_item_order(a, seg, ord);
+  const pf::PartialSums ps = partial_sums_of(d, a);
   if (a.ds_ext) {
     // prep with D and LSE first; the dK/dV pass stores dS^T, then dQ is read
-    // from it
+    // from it, with the split blocks' partial sums in the same launch
     e = pf::launch_prep_dsum_bf16(seg, d.heads, a, st);
     if (e != hipSuccess) return hip_fail(e, "prep");
     e = pf::launch_bwd_dkv_bf16(a, ord, d.d, st);
     if (e != hipSuccess) return hip_fail(e, "dkv");
-    e = pf::launch_bwd_dq_ds_bf16(a, d.d, st);
+    e = pf::launch_bwd_dq_ds_bf16(a, ps, d.d, st);
     if (e != hipSuccess) return hip_fail(e, "dq_ds");
-  } else {
-    e = pf::launch_prep(seg, d.heads, a.ri, st);
-    if (e != hipSuccess) return hip_fail(e, "prep");
-    e = d.dtype == PF_BF16 ? pf::launch_bwd_dq_bf16(a, d.d, st) : pf::launch_bwd_dq_f32(a, d.d, st);
-    if (e != hipSuccess) return hip_fail(e, "dq");
-    e = d.dtype == PF_BF16 ? pf::launch_bwd_dkv_bf16(a, ord, d.d, st) : pf::launch_bwd_dkv_f32(a, d.d, st);
-    if (e != hipSuccess) return hip_fail(e, "dkv");
+    return PF_OK;
   }
+  e = pf::launch_prep(seg, d.heads, a.ri, st);
+  if (e != hipSuccess) return hip_fail(e, "prep");
+  e = d.dtype == PF_BF16 ? pf::launch_bwd_dq_bf16(a, d.d, st) : pf::launch_bwd_dq_f32(a, d.d, st);
+  if (e != hipSuccess) return hip_fail(e, "dq");
+  e = d.dtype == PF_BF16 ? pf::launch_bwd_dkv_bf16(a, ord, d.d, st) : pf::launch_bwd_dkv_f32(a, d.d, st);
+  if (e != hipSuccess) return hip_fail(e, "dkv");
   // the split blocks' partials: gK/gV += later chunks, own dK/dV = init +
   // chunks, in one launch
-  const bool ext_parts = a.n_chunks > 1 && a.n_ext > 0;
-  const bool own_parts = a.n_chunks_own > 1;
-  if (ext_parts || own_parts) {
-    pf::PartialSums ps;
-    memset(&ps, 0, sizeof(ps));
-    if (ext_parts) {
-      ps.ext_planes = a.n_chunks - 1;
-      ps.ext_n4 = (int64_t)a.n_ext * d.hkv * d.d / 4;
-      ps.part_k = (const float4*)a.gk_part;
-      ps.part_v = (const float4*)a.gv_part;
-      ps.acc_k = (float4*)a.gk_acc;
-      ps.acc_v = (float4*)a.gv_acc;
-    }
-    if (own_parts) {
-      ps.own_planes = a.n_chunks_own;
-      ps.fk = pf::OwnFinish{(const float4*)a.dk_part, (const float4*)a.gk_init, (char*)a.dk_own,
-                            a.dko_st, a.dko_sh};
-      ps.fv = pf::OwnFinish{(const float4*)a.dv_part, (const float4*)a.gv_init, (char*)a.dv_own,
-                            a.dvo_st, a.dvo_sh};
-      ps.rows = a.rows;
-      ps.heads = d.hkv;
-      ps.d = d.d;
-      ps.dst_f32 = a.dkv_f32;
-    }
-    e = pf::launch_partial_sums(ps, st);
-    if (e != hipSuccess) return hip_fail(e, "partials");
-  }
+  e = pf::launch_partial_sums(ps, st);
+  if (e != hipSuccess) return hip_fail(e, "partials");
   return PF_OK;
 }
 

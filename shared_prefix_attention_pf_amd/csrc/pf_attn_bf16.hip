@@ -39,6 +39,7 @@
 #include <type_traits>
 
 #include "pf_internal.h"
+#include "pf_partials.h"
 
 namespace pf {
 namespace {
@@ -1213,7 +1214,16 @@ __device__ __forceinline__ int ds_col_row(int p) {
   return 16 * (p >> 4) + 8 * ((p & 7) >> 2) + 4 * ((p >> 3) & 1) + (p & 3);
 }
 
-__global__ __launch_bounds__(kThreads, 2) void bwd_dq_ds_kernel(AttnArgs a) {
+// The dQ pass's grid (n_dq workgroups) is followed by the split key blocks'
+// partial sums (PartialSums, nbx blocks per array from array y0 on): the two
+// read disjoint data, and one launch saves the gap between two.
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq_ds_kernel(AttnArgs a, PartialSums ps,
+                                                                int n_dq, int ps_nbx, int ps_y0) {
+  if ((int)blockIdx.x >= n_dq) {
+    const int pb = (int)blockIdx.x - n_dq;
+    partial_sums_block(ps, ps_y0 + pb / ps_nbx, pb % ps_nbx, ps_nbx);
+    return;
+  }
   constexpr int BN = kDxBN;
   __shared__ __attribute__((aligned(16))) char smem[kDxBufs * kDxBufBytes];
   lds_t* const sb = (lds_t*)smem;
@@ -2001,12 +2011,16 @@ hipError_t launch_bwd_dkv_bf16(const AttnArgs& a, const ItemOrder& ord, int32_t 
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dq_ds_bf16(const AttnArgs& a, int32_t head_dim, hipStream_t stream) {
+hipError_t launch_bwd_dq_ds_bf16(const AttnArgs& a, const PartialSums& ps, int32_t head_dim,
+                                 hipStream_t stream) {
   if (head_dim != kD) return hipErrorInvalidValue;
-  if (a.rows <= 0) return hipSuccess;
+  if (a.rows <= 0) return launch_partial_sums(ps, stream);
   const int n_tt = (a.rows + kDxTok - 1) / kDxTok;
-  PF_LAUNCH("pf_bwd_dq_ds_bf16", bwd_dq_ds_kernel, dim3(grid_for(a.hkv, a.group * n_tt)),
-            dim3(kThreads), stream, a);
+  const int n_dq = grid_for(a.hkv, a.group * n_tt);
+  int nbx, ny, y0;
+  partial_sums_grid(ps, nbx, ny, y0);
+  PF_LAUNCH("pf_bwd_dq_ds_bf16", bwd_dq_ds_kernel, dim3(n_dq + nbx * ny), dim3(kThreads), stream,
+            a, ps, n_dq, nbx > 0 ? nbx : 1, y0);
   return hipGetLastError();
 }
 

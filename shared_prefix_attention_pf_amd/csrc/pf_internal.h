@@ -144,6 +144,10 @@ struct PartialSums {
   int32_t heads, d, dst_f32;
 };
 hipError_t launch_partial_sums(const PartialSums& ps, hipStream_t stream);
+// the dQ-from-dS pass, followed in the same launch by the partial sums `ps`
+// (which may be empty)
+hipError_t launch_bwd_dq_ds_bf16(const AttnArgs& a, const PartialSums& ps, int32_t head_dim,
+                                 hipStream_t stream);
 hipError_t launch_convert_acc(const float* src, void* dst, int64_t rows, int32_t heads, int32_t d,
                               int64_t st, int64_t sh, int32_t dst_f32, hipStream_t stream);
 
@@ -165,7 +169,7 @@ struct ItemOrder {
 void dkv_item_order(const AttnArgs& a, const SegTable& seg, ItemOrder& ord);
 hipError_t launch_bwd_dkv_bf16(const AttnArgs& a, const ItemOrder& ord, int32_t head_dim,
                                hipStream_t stream);
-hipError_t launch_bwd_dq_ds_bf16(const AttnArgs& a, int32_t head_dim, hipStream_t stream);
+
 
 hipError_t launch_fwd_f32(const AttnArgs& a, int32_t head_dim, hipStream_t stream);
 hipError_t launch_bwd_dq_f32(const AttnArgs& a, int32_t head_dim, hipStream_t stream);
