@@ -33,6 +33,10 @@ SUFFIX_CASES = [
     (6, 2, 128, "bf16", 70, [50, 90], None),
     (4, 2, 128, "bf16", 0, [100, 30], None),
     (4, 2, 128, "bf16", 96, [40, 41], [1, 0, 0, 1]),
+    # KV head counts that are neither a divisor nor a multiple of 8 (head-major
+    # block order) and a multiple of 8 with two heads per XCD
+    (6, 3, 128, "bf16", 130, [70, 33], None),
+    (16, 16, 128, "bf16", 64, [40, 90], None),
     (2, 2, 64, "f32", 256, [64, 64, 64, 64], None),
     (4, 2, 128, "f32", 100, [3, 70, 0], None),
 ]
