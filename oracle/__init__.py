@@ -10,8 +10,10 @@ Pins (checked by `tests/test_oracle_*.py`, none of which compares the oracle
 with itself): finite differences, torch CPU fp64 autograd and SDPA (math
 path), closed forms (Q = 0, single visible key), the full-trajectory row
 identity, prefix-gradient superposition via a packed-graph formulation,
-GQA = MHA with repeated K/V, tree expanded-vs-direct, and the reductions of
-trees to flat groups and causal chains.
+GQA = MHA with repeated K/V, tree expanded-vs-direct, the reductions of
+trees to flat groups and causal chains, and tree windows over a prefix
+against per-trajectory flat Phase B (expansion with a split upstream), a
+chain tree as one flat suffix, and P = 0 as a plain tree.
 
 Sources (page titles and sections):
   * PrefixFlow: Training-Time KV Caching for Schedule-Level Prefix Reuse in
@@ -21,7 +23,8 @@ Sources (page titles and sections):
   * HARTS: A Prefix-Sharing Training System for Agentic RL with
     Hybrid-Attention Models — §2.1 (rollout trees, compact rows), §2.2
     (full attention reads ancestor K/V through a tree mask), §3 (gather
-    backward sums into shared rows).
+    backward sums into shared rows; producer / consumer sharing windows,
+    consumer gradients accumulated before one producer backward).
 """
 from .attention import attention_backward, attention_forward, head_map
 from .masks import causal_mask, suffix_rows_mask, tree_ancestor_mask, tree_node_of_row
@@ -33,6 +36,7 @@ from .phases import (
     tree_attention_direct,
     tree_attention_expanded,
     tree_trajectories,
+    tree_window_attention,
 )
 
 __all__ = [
@@ -50,4 +54,5 @@ __all__ = [
     "tree_attention_direct",
     "tree_attention_expanded",
     "tree_trajectories",
+    "tree_window_attention",
 ]

@@ -206,3 +206,34 @@ def tree_attention_expanded(q, k, v, do, node_off, parent, scale, hmap,
         np.add.at(dv, rows, dvt)
     return {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv,
             "forward_spread": spread}
+
+
+def tree_window_attention(k_p, v_p, q, k, v, do, node_off, parent, scale, hmap,
+                          dtype=np.float64, backward=True) -> Dict[str, np.ndarray]:
+    """One sharing window of rollout trees over a cached prefix (HARTS §3.4,
+    "Window-scoped reuse and backward": a producer forward caches the ancestor
+    K/V once; the consumers of a window run only their uncached tokens, and
+    their backward passes accumulate the gradients at that interface before
+    the one producer backward).
+
+    The window's compact rows (DFS preorder, node_off / parent as for trees)
+    all sit after the P prefix positions of every trajectory they belong to,
+    so a row sees every prefix key and, through the ancestor mask, its own
+    node up to itself and every ancestor node (HARTS §2.2).  Full attention
+    over [prefix ; window rows] with that mask gives o, lse of the window rows;
+    the backward under upstream [0_P ; dO] gives dq, dk, dv of the window rows
+    and, in the prefix rows of dK, dV, this window's gk, gv.
+    """
+    p = k_p.shape[0]
+    c = q.shape[0]
+    tvis = tree_ancestor_mask(node_off, parent)
+    vis = np.concatenate([np.ones((c, p), dtype=bool), tvis], axis=1)      # [C, P + C]
+    k_all = np.concatenate([k_p, k], axis=0)
+    v_all = np.concatenate([v_p, v], axis=0)
+    o, lse = attention_forward(q, k_all, v_all, vis, scale, hmap, dtype)
+    out = {"o": o, "lse": lse}
+    if backward:
+        dq, dk_all, dv_all = attention_backward(q, k_all, v_all, do, vis, scale, hmap, dtype)
+        out.update(dq=dq, dk=dk_all[p:], dv=dv_all[p:], gk=dk_all[:p], gv=dv_all[:p])
+    return out
+

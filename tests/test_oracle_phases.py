@@ -28,6 +28,7 @@ from oracle import (
     tree_attention_direct,
     tree_attention_expanded,
     tree_trajectories,
+    tree_window_attention,
 )
 from workloads.gen import random_small_group, random_tree, random_tree_group, tree_layout
 
@@ -268,3 +269,88 @@ def test_config5_tree_layout():
     assert sum(len(t) for t in trajs) == 86016
     end = _subtree_end(node_off, parent)
     assert end[0] == 12288 and end[1] == 4096 + 1024 + 4 * 256
+
+
+def _window(seed, p, n_nodes=7, max_len=6, hq=4, hkv=2, d=8):
+    node_off, parent = random_tree(seed, n_nodes, max_len=max_len, min_len=1)
+    g = random_tree_group(seed, node_off, hq, hkv, d)
+    rng = np.random.default_rng(seed + 77)
+    g["k_p"] = rng.standard_normal((p, hkv, d))
+    g["v_p"] = rng.standard_normal((p, hkv, d))
+    return node_off, parent, {k: np.asarray(v, dtype=np.float64) for k, v in g.items()}
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_tree_window_equals_flat_phase_b_per_trajectory(seed):
+    """A window of trees over a prefix, by expansion: every root-to-leaf
+    trajectory is one flat Phase-B suffix [P || path] (suffix_attention, the
+    flat-suffix mask), with each compact row's upstream split at random over
+    the trajectories that contain it.  Forward rows must agree with the
+    compact result wherever they occur; compact dQ/dK/dV are the sums over
+    occurrences, and gK/gV the sum over trajectories (linearity in dO)."""
+    p = 6
+    node_off, parent, g = _window(seed, p)
+    hmap = head_map(4, 2)
+    ref = tree_window_attention(g["k_p"], g["v_p"], g["q"], g["k"], g["v"], g["do"], node_off,
+                                parent, 0.4, hmap)
+    trajs = tree_trajectories(node_off, parent)
+    c = int(node_off[-1])
+    occ = np.zeros(c, dtype=np.int64)
+    for rows in trajs:
+        occ[rows] += 1
+    rng = np.random.default_rng(seed + 5)
+    left = np.ones(c)
+    seen = np.zeros(c, dtype=np.int64)
+    dq = np.zeros_like(g["q"])
+    dk = np.zeros_like(g["k"])
+    dv = np.zeros_like(g["v"])
+    gk = np.zeros_like(g["k_p"])
+    gv = np.zeros_like(g["v_p"])
+    for rows in trajs:
+        seen[rows] += 1
+        w = np.where(seen[rows] == occ[rows], left[rows], rng.uniform(0, 1, len(rows)) * left[rows])
+        left[rows] -= w
+        r = suffix_attention(g["k_p"], g["v_p"], g["q"][rows], g["k"][rows], g["v"][rows],
+                             g["do"][rows] * w[:, None, None], np.asarray([0, len(rows)]), 0.4,
+                             hmap)
+        np.testing.assert_allclose(r["o_s"], ref["o"][rows], atol=1e-12)
+        np.testing.assert_allclose(r["lse_s"], ref["lse"][:, rows], atol=1e-12)
+        np.add.at(dq, rows, r["dq_s"])
+        np.add.at(dk, rows, r["dk_s"])
+        np.add.at(dv, rows, r["dv_s"])
+        gk += r["gk"]
+        gv += r["gv"]
+    np.testing.assert_allclose(left, 0.0, atol=1e-12)
+    for name, got in (("dq", dq), ("dk", dk), ("dv", dv), ("gk", gk), ("gv", gv)):
+        np.testing.assert_allclose(got, ref[name], atol=1e-11, err_msg=name)
+
+
+def test_tree_window_chain_is_one_flat_suffix():
+    """A chain of nodes is one trajectory: the window equals Phase B with one suffix."""
+    p = 5
+    node_off = np.asarray([0, 2, 5, 6, 9], dtype=np.int32)
+    parent = np.asarray([-1, 0, 1, 2], dtype=np.int32)
+    g = random_tree_group(3, node_off, 4, 2, 8)
+    g = {k: np.asarray(v, dtype=np.float64) for k, v in g.items()}
+    rng = np.random.default_rng(9)
+    k_p, v_p = rng.standard_normal((p, 2, 8)), rng.standard_normal((p, 2, 8))
+    hmap = head_map(4, 2)
+    a = tree_window_attention(k_p, v_p, g["q"], g["k"], g["v"], g["do"], node_off, parent, 0.5,
+                              hmap)
+    b = suffix_attention(k_p, v_p, g["q"], g["k"], g["v"], g["do"], np.asarray([0, 9]), 0.5, hmap)
+    for x, y in (("o", "o_s"), ("lse", "lse_s"), ("dq", "dq_s"), ("dk", "dk_s"), ("dv", "dv_s"),
+                 ("gk", "gk"), ("gv", "gv")):
+        np.testing.assert_allclose(a[x], b[y], atol=1e-12, err_msg=x)
+
+
+def test_tree_window_without_prefix_is_a_tree():
+    node_off, parent, g = _window(4, 0)
+    hmap = head_map(4, 2)
+    a = tree_window_attention(g["k_p"], g["v_p"], g["q"], g["k"], g["v"], g["do"], node_off,
+                              parent, 0.3, hmap)
+    b = tree_attention_expanded(g["q"], g["k"], g["v"], g["do"], node_off, parent, 0.3, hmap,
+                                rng=np.random.default_rng(4))
+    for key in ("o", "lse", "dq", "dk", "dv"):
+        np.testing.assert_allclose(a[key], b[key], atol=1e-12, err_msg=key)
+    assert a["gk"].shape[0] == 0
+
