@@ -19,6 +19,10 @@
  *                                      ancestor mask ("HARTS: A Prefix-Sharing
  *                                      Training System for Agentic RL with
  *                                      Hybrid-Attention Models", §2.1, §2.2, §3.4).
+ *   Windows  pf_tree_suffix_attn_fwd,  a window of rollout trees over a cached
+ *            pf_tree_suffix_attn_bwd_accum  prefix, with the prefix-side
+ *                                      gradients accumulated (HARTS §3.4,
+ *                                      window-scoped reuse and backward).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -80,7 +84,9 @@ typedef enum {
   PF_OP_SUFFIX_BWD = 2,
   PF_OP_PREFIX_BWD = 3,
   PF_OP_TREE_FWD = 4,
-  PF_OP_TREE_BWD = 5
+  PF_OP_TREE_BWD = 5,
+  PF_OP_TREE_SUFFIX_FWD = 6,
+  PF_OP_TREE_SUFFIX_BWD = 7
 } pf_op;
 
 /* Attention head configuration of one layer (the caller's local head shard). */
@@ -104,16 +110,17 @@ typedef struct {
 
 /* Bytes of device workspace `op` needs.  rows = prefix_len for the prefix
  * ops, the total packed suffix rows for the suffix ops and the compact rows
- * for the tree ops.  Pure host arithmetic; never fails (0 for bad args). */
+ * for the tree and tree-window ops.  Pure host arithmetic; never fails (0 for bad args). */
 size_t pf_workspace_size(int32_t op, const pf_attn_desc* desc, int32_t prefix_len, int32_t rows);
 
-/* The smallest workspace `op` accepts (same arguments).  For PF_OP_SUFFIX_BWD
- * with bf16, pf_workspace_size() adds a buffer for dS (num_q_heads x
- * (ceil256(prefix_len) + ceil256(rows)) x ceil256(rows) bf16 values): with it
- * the backward stores dS once and forms dQ from it instead of recomputing S
- * and dP.  A workspace of at least this size but smaller than
- * pf_workspace_size() runs the recompute path.  Results agree to rounding;
- * each path is deterministic.  Other ops: equal to pf_workspace_size(). */
+/* The smallest workspace `op` accepts (same arguments).  For the bf16
+ * backward ops, pf_workspace_size() adds a buffer for dS (num_q_heads x
+ * (ceil256(prefix_len) + ceil256(rows)) x ceil256(rows) bf16 values; prefix_len
+ * counts as 0 for Phase C and trees): with it the backward stores dS once and
+ * forms dQ from it instead of recomputing S and dP.  A workspace of at least
+ * this size but smaller than pf_workspace_size() runs the recompute path.
+ * Results agree to rounding; each path is deterministic.  Forward ops: equal
+ * to pf_workspace_size(). */
 size_t pf_workspace_size_min(int32_t op, const pf_attn_desc* desc, int32_t prefix_len,
                              int32_t rows);
 
@@ -199,6 +206,42 @@ pf_status pf_tree_attn_bwd(const pf_attn_desc* desc, int32_t n_nodes, const int3
                            pf_tensor o, const float* lse, pf_tensor dout, pf_tensor dq,
                            pf_tensor dk, pf_tensor dv, void* workspace, size_t workspace_bytes,
                            void* stream);
+
+/* A sharing window of rollout trees over a cached prefix ("HARTS", §3.4,
+ * window-scoped reuse and backward: a producer forward caches the ancestor
+ * K/V once; the consumers of a window run only their uncached tokens, and
+ * their backward passes accumulate the gradients at that interface before
+ * the one producer backward).  The window's rows are compact tree rows as for
+ * pf_tree_attn_fwd (DFS preorder, node_off, parent); every row also sees all
+ * prefix_len cached prefix rows, which precede the tree root in every
+ * trajectory.  The prefix K/V are read in place.  A chain of nodes is one
+ * Phase-B suffix; a window per call, several calls adding into one gK/gV,
+ * then pf_prefix_bwd_inject is the producer backward.
+ *   k_p, v_p [P, Hkv, d]                  in  (the cached prefix; P >= 0)
+ *   node_off host [n_nodes + 1], parent host [n_nodes]   in
+ *   q [C, Hq, d], k, v [C, Hkv, d]        in  (C = node_off[n_nodes])
+ *   o [C, Hq, d], lse [Hq, C] fp32        out                            */
+pf_status pf_tree_suffix_attn_fwd(const pf_attn_desc* desc, int32_t prefix_len, pf_tensor k_p,
+                                  pf_tensor v_p, int32_t n_nodes, const int32_t* node_off,
+                                  const int32_t* parent, pf_tensor q, pf_tensor k, pf_tensor v,
+                                  pf_tensor o, float* lse, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/* Backward of a tree window over a cached prefix: dQ of the window rows, dK/dV
+ * of the window rows (summed over the descendant rows and query heads that
+ * read them), and the window's prefix-side gradients ADDED into gK/gV.
+ *   (forward arguments as above), o, lse from pf_tree_suffix_attn_fwd,
+ *   dout [C, Hq, d]                       in
+ *   dq [C, Hq, d], dk, dv [C, Hkv, d]     out (overwritten)
+ *   gk_acc, gv_acc fp32 [P, Hkv, d]       in/out: added into, as in
+ *                                         pf_suffix_attn_bwd_accum          */
+pf_status pf_tree_suffix_attn_bwd_accum(const pf_attn_desc* desc, int32_t prefix_len,
+                                        pf_tensor k_p, pf_tensor v_p, int32_t n_nodes,
+                                        const int32_t* node_off, const int32_t* parent,
+                                        pf_tensor q, pf_tensor k, pf_tensor v, pf_tensor o,
+                                        const float* lse, pf_tensor dout, pf_tensor dq,
+                                        pf_tensor dk, pf_tensor dv, float* gk_acc, float* gv_acc,
+                                        void* workspace, size_t workspace_bytes, void* stream);
 
 /* Host-only helper: the end row of each node's subtree (exclusive), the
  * bound of the rows that can read that node's keys.  Validates the tree.

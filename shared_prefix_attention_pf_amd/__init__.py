@@ -19,12 +19,13 @@ LIB_PATH = os.path.join(_PKG, "libpf.so")
 PF_OK, PF_ERR_INVALID_ARG, PF_ERR_UNSUPPORTED, PF_ERR_WORKSPACE, PF_ERR_HIP = range(5)
 PF_F32, PF_BF16 = 0, 1
 (PF_OP_PREFIX_FWD, PF_OP_SUFFIX_FWD, PF_OP_SUFFIX_BWD, PF_OP_PREFIX_BWD, PF_OP_TREE_FWD,
- PF_OP_TREE_BWD) = range(6)
+ PF_OP_TREE_BWD, PF_OP_TREE_SUFFIX_FWD, PF_OP_TREE_SUFFIX_BWD) = range(8)
 PF_MAX_SEGMENTS = 256
 
 EXPORTED = (
     "pf_workspace_size", "pf_workspace_size_min", "pf_prefix_fwd", "pf_suffix_attn_fwd", "pf_suffix_attn_bwd_accum",
-    "pf_prefix_bwd_inject", "pf_tree_attn_fwd", "pf_tree_attn_bwd", "pf_tree_subtree_end",
+    "pf_prefix_bwd_inject", "pf_tree_attn_fwd", "pf_tree_attn_bwd", "pf_tree_suffix_attn_fwd",
+    "pf_tree_suffix_attn_bwd_accum", "pf_tree_subtree_end",
     "pf_status_string", "pf_last_error", "pf_abi_version", "pf_set_launch_hook",
 )
 
@@ -79,6 +80,9 @@ def _load():
                                        P]),
         "pf_tree_attn_fwd": (i32, [D, i32, ip, ip, T, T, T, T, fp, P, sz, P]),
         "pf_tree_attn_bwd": (i32, [D, i32, ip, ip, T, T, T, T, fp, T, T, T, T, P, sz, P]),
+        "pf_tree_suffix_attn_fwd": (i32, [D, i32, T, T, i32, ip, ip, T, T, T, T, fp, P, sz, P]),
+        "pf_tree_suffix_attn_bwd_accum": (i32, [D, i32, T, T, i32, ip, ip, T, T, T, T, fp, T, T, T,
+                                                T, fp, fp, P, sz, P]),
         "pf_tree_subtree_end": (i32, [i32, ip, ip, ip]),
         "pf_status_string": (ctypes.c_char_p, [i32]),
         "pf_last_error": (ctypes.c_char_p, []),
@@ -244,6 +248,29 @@ def pf_tree_attn_bwd(desc, node_off, parent, q, k, v, o, lse, dout, dq, dk, dv, 
     _check(_lib.pf_tree_attn_bwd(ctypes.byref(d), len(pa), no_p, pa_p, _t(q), _t(k), _t(v), _t(o),
                                  _p(lse), _t(dout), _t(dq), _t(dk), _t(dv), ws, nws,
                                  _stream(stream)))
+
+
+def pf_tree_suffix_attn_fwd(desc, prefix_len, k_p, v_p, node_off, parent, q, k, v, o, lse,
+                            workspace, stream=None):
+    d, _keep = desc._c()
+    no, no_p = _ints(node_off)
+    pa, pa_p = _ints(parent)
+    ws, nws = _ws(workspace)
+    _check(_lib.pf_tree_suffix_attn_fwd(ctypes.byref(d), prefix_len, _t(k_p), _t(v_p), len(pa),
+                                        no_p, pa_p, _t(q), _t(k), _t(v), _t(o), _p(lse), ws, nws,
+                                        _stream(stream)))
+
+
+def pf_tree_suffix_attn_bwd_accum(desc, prefix_len, k_p, v_p, node_off, parent, q, k, v, o, lse,
+                                  dout, dq, dk, dv, gk_acc, gv_acc, workspace, stream=None):
+    d, _keep = desc._c()
+    no, no_p = _ints(node_off)
+    pa, pa_p = _ints(parent)
+    ws, nws = _ws(workspace)
+    _check(_lib.pf_tree_suffix_attn_bwd_accum(
+        ctypes.byref(d), prefix_len, _t(k_p), _t(v_p), len(pa), no_p, pa_p, _t(q), _t(k), _t(v),
+        _t(o), _p(lse), _t(dout), _t(dq), _t(dk), _t(dv), _p(gk_acc), _p(gv_acc), ws, nws,
+        _stream(stream)))
 
 
 __all__ = [name for name in EXPORTED] + ["AttnDesc", "PFError", "PF_BF16", "PF_F32", "LIB_PATH"]

@@ -168,7 +168,9 @@ struct WsLayout {
 // ceil256(rows) rows of bf16, of which only the visible tiles are written and
 // read (one head's share must stay below 2 GiB for 32-bit buffer offsets).
 bool ds_eligible(int32_t op, const Desc& d, int32_t n_ext, int32_t rows) {
-  if (op != PF_OP_SUFFIX_BWD && op != PF_OP_PREFIX_BWD && op != PF_OP_TREE_BWD) return false;
+  if (op != PF_OP_SUFFIX_BWD && op != PF_OP_PREFIX_BWD && op != PF_OP_TREE_BWD &&
+      op != PF_OP_TREE_SUFFIX_BWD)
+    return false;
   if (d.dtype != PF_BF16 || rows <= 0) return false;
   const int64_t r = ((int64_t)rows + 255) / 256 * 256;
   const int64_t keys = ((int64_t)n_ext + 255) / 256 * 256 + r;
@@ -183,14 +185,15 @@ WsLayout layout(int32_t op, const Desc& d, int32_t n_ext, int32_t rows, bool wan
   w.bmax = off; off += align_up(nb * 4);
   w.bmin = off; off += align_up(nb * 4);
   w.qhead = off; off += align_up((size_t)d.hq * 4);
-  const bool bwd = op == PF_OP_SUFFIX_BWD || op == PF_OP_PREFIX_BWD || op == PF_OP_TREE_BWD;
+  const bool bwd = op == PF_OP_SUFFIX_BWD || op == PF_OP_PREFIX_BWD || op == PF_OP_TREE_BWD ||
+                   op == PF_OP_TREE_SUFFIX_BWD;
   if (bwd) {
     w.dsum = off;
     off += align_up((size_t)d.hq * rows * 4);
     w.lse2 = off;
     off += align_up((size_t)d.hq * rows * 4);
   }
-  if (op == PF_OP_SUFFIX_BWD) {
+  if (op == PF_OP_SUFFIX_BWD || op == PF_OP_TREE_SUFFIX_BWD) {
     w.n_chunks = pf::ext_chunks(n_ext, rows, d.hq, d.hkv, d.d, d.dtype);
     if (w.n_chunks > 1) {
       const size_t part = (size_t)(w.n_chunks - 1) * n_ext * d.hkv * d.d * 4;
@@ -424,7 +427,7 @@ int32_t own_chunks(int32_t op, int32_t n_ext, int32_t rows, int32_t hq, int32_t 
   (void)head_dim;
   if (dtype != PF_BF16 || rows <= 0) return 1;
   if (op == PF_OP_SUFFIX_BWD) return (n_ext > 0 && rows >= 512) ? 2 : 1;
-  if (op != PF_OP_PREFIX_BWD && op != PF_OP_TREE_BWD) return 1;
+  if (op != PF_OP_PREFIX_BWD && op != PF_OP_TREE_BWD && op != PF_OP_TREE_SUFFIX_BWD) return 1;
   const int kb = dkv_keys_per_workgroup_bf16();
   const int64_t wgs = (int64_t)((rows + kb - 1) / kb) * hkv;
   const int64_t steps = (int64_t)((rows / 2 + 31) / 32) * (hq / hkv);
@@ -461,8 +464,11 @@ size_t pf_workspace_size(int32_t op, const pf_attn_desc* desc, int32_t prefix_le
   Desc d;
   if (check_desc(desc, &d) != PF_OK || rows < 0 || prefix_len < 0) return 0;
   if (op == PF_OP_PREFIX_FWD || op == PF_OP_PREFIX_BWD) rows = prefix_len;
-  const int32_t n_ext = (op == PF_OP_SUFFIX_FWD || op == PF_OP_SUFFIX_BWD) ? prefix_len : 0;
-  if (op < PF_OP_PREFIX_FWD || op > PF_OP_TREE_BWD) return 0;
+  const int32_t n_ext = (op == PF_OP_SUFFIX_FWD || op == PF_OP_SUFFIX_BWD ||
+                         op == PF_OP_TREE_SUFFIX_FWD || op == PF_OP_TREE_SUFFIX_BWD)
+                            ? prefix_len
+                            : 0;
+  if (op < PF_OP_PREFIX_FWD || op > PF_OP_TREE_SUFFIX_BWD) return 0;
   return layout(op, d, n_ext, rows, true).total;
 }
 
@@ -471,8 +477,11 @@ size_t pf_workspace_size_min(int32_t op, const pf_attn_desc* desc, int32_t prefi
   Desc d;
   if (check_desc(desc, &d) != PF_OK || rows < 0 || prefix_len < 0) return 0;
   if (op == PF_OP_PREFIX_FWD || op == PF_OP_PREFIX_BWD) rows = prefix_len;
-  const int32_t n_ext = (op == PF_OP_SUFFIX_FWD || op == PF_OP_SUFFIX_BWD) ? prefix_len : 0;
-  if (op < PF_OP_PREFIX_FWD || op > PF_OP_TREE_BWD) return 0;
+  const int32_t n_ext = (op == PF_OP_SUFFIX_FWD || op == PF_OP_SUFFIX_BWD ||
+                         op == PF_OP_TREE_SUFFIX_FWD || op == PF_OP_TREE_SUFFIX_BWD)
+                            ? prefix_len
+                            : 0;
+  if (op < PF_OP_PREFIX_FWD || op > PF_OP_TREE_SUFFIX_BWD) return 0;
   return layout(op, d, n_ext, rows, false).total;
 }
 
@@ -510,16 +519,18 @@ pf_status pf_prefix_fwd(const pf_attn_desc* desc, int32_t prefix_len, pf_tensor 
   return run_fwd(d, a, causal_segment(prefix_len), (hipStream_t)stream);
 }
 
-pf_status pf_suffix_attn_fwd(const pf_attn_desc* desc, int32_t prefix_len, pf_tensor k_p,
-                             pf_tensor v_p, int32_t n_suffix, const int32_t* cu_seqlens,
-                             pf_tensor q_s, pf_tensor k_s, pf_tensor v_s, pf_tensor o_s,
-                             float* lse_s, void* workspace, size_t workspace_bytes, void* stream) {
-  Desc d;
-  pf_status s = check_desc(desc, &d);
-  if (s != PF_OK) return s;
-  if (prefix_len < 0) return fail(PF_ERR_INVALID_ARG, "prefix_len is negative");
-  int32_t rows = 0;
-  if ((s = check_cu(n_suffix, cu_seqlens, &rows)) != PF_OK) return s;
+}  // extern "C"
+
+namespace {
+
+// Phase B forward over a cached prefix for rows whose own-key visibility is
+// the segment table `seg` (flat suffixes or a tree window); `rows` and the
+// structure are already validated.
+pf_status suffix_fwd_impl(int32_t op, const Desc& d, int32_t prefix_len, pf_tensor k_p,
+                          pf_tensor v_p, int32_t rows, const pf::SegTable& seg, pf_tensor q_s,
+                          pf_tensor k_s, pf_tensor v_s, pf_tensor o_s, float* lse_s,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  pf_status s;
   if ((s = check_tensor("k_p", k_p, prefix_len, d.hkv, d, d.dtype)) != PF_OK) return s;
   if ((s = check_tensor("v_p", v_p, prefix_len, d.hkv, d, d.dtype)) != PF_OK) return s;
   if ((s = check_tensor("q_s", q_s, rows, d.hq, d, d.dtype)) != PF_OK) return s;
@@ -527,7 +538,7 @@ pf_status pf_suffix_attn_fwd(const pf_attn_desc* desc, int32_t prefix_len, pf_te
   if ((s = check_tensor("v_s", v_s, rows, d.hkv, d, d.dtype)) != PF_OK) return s;
   if ((s = check_tensor("o_s", o_s, rows, d.hq, d, d.dtype)) != PF_OK) return s;
   if (rows > 0 && (s = check_ptr("lse_s", lse_s, 4)) != PF_OK) return s;
-  const WsLayout w = layout(PF_OP_SUFFIX_FWD, d, prefix_len, rows);
+  const WsLayout w = layout(op, d, prefix_len, rows);
   if ((s = check_stream_ws(workspace, workspace_bytes, w.total)) != PF_OK) return s;
   if (rows == 0) return PF_OK;
   pf::AttnArgs a = base_args(d, rows);
@@ -537,21 +548,17 @@ pf_status pf_suffix_attn_fwd(const pf_attn_desc* desc, int32_t prefix_len, pf_te
   set_own(a, k_s, v_s);
   a.lse = lse_s;
   a.ri = row_info(workspace, w);
-  return run_fwd(d, a, flat_segments(n_suffix, cu_seqlens), (hipStream_t)stream);
+  return run_fwd(d, a, seg, (hipStream_t)stream);
 }
 
-pf_status pf_suffix_attn_bwd_accum(const pf_attn_desc* desc, int32_t prefix_len, pf_tensor k_p,
-                                   pf_tensor v_p, int32_t n_suffix, const int32_t* cu_seqlens,
-                                   pf_tensor q_s, pf_tensor k_s, pf_tensor v_s, pf_tensor o_s,
-                                   const float* lse_s, pf_tensor do_s, pf_tensor dq_s,
-                                   pf_tensor dk_s, pf_tensor dv_s, float* gk_acc, float* gv_acc,
-                                   void* workspace, size_t workspace_bytes, void* stream) {
-  Desc d;
-  pf_status s = check_desc(desc, &d);
-  if (s != PF_OK) return s;
-  if (prefix_len < 0) return fail(PF_ERR_INVALID_ARG, "prefix_len is negative");
-  int32_t rows = 0;
-  if ((s = check_cu(n_suffix, cu_seqlens, &rows)) != PF_OK) return s;
+// Phase B backward with gK/gV accumulation, for the same two row structures.
+pf_status suffix_bwd_impl(int32_t op, const Desc& d, int32_t prefix_len, pf_tensor k_p,
+                          pf_tensor v_p, int32_t rows, const pf::SegTable& seg, pf_tensor q_s,
+                          pf_tensor k_s, pf_tensor v_s, pf_tensor o_s, const float* lse_s,
+                          pf_tensor do_s, pf_tensor dq_s, pf_tensor dk_s, pf_tensor dv_s,
+                          float* gk_acc, float* gv_acc, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  pf_status s;
   if ((s = check_tensor("k_p", k_p, prefix_len, d.hkv, d, d.dtype)) != PF_OK) return s;
   if ((s = check_tensor("v_p", v_p, prefix_len, d.hkv, d, d.dtype)) != PF_OK) return s;
   if ((s = check_tensor("q_s", q_s, rows, d.hq, d, d.dtype)) != PF_OK) return s;
@@ -567,9 +574,9 @@ pf_status pf_suffix_attn_bwd_accum(const pf_attn_desc* desc, int32_t prefix_len,
     if ((s = check_ptr("gk_acc", gk_acc, 16)) != PF_OK) return s;
     if ((s = check_ptr("gv_acc", gv_acc, 16)) != PF_OK) return s;
   }
-  const WsLayout w_min = layout(PF_OP_SUFFIX_BWD, d, prefix_len, rows, false);
+  const WsLayout w_min = layout(op, d, prefix_len, rows, false);
   if ((s = check_stream_ws(workspace, workspace_bytes, w_min.total)) != PF_OK) return s;
-  const WsLayout w = pick_layout(PF_OP_SUFFIX_BWD, d, prefix_len, rows, workspace_bytes, w_min);
+  const WsLayout w = pick_layout(op, d, prefix_len, rows, workspace_bytes, w_min);
   if (rows == 0) return PF_OK;
   pf::AttnArgs a = base_args(d, rows);
   set_q(a, q_s);
@@ -593,7 +600,77 @@ pf_status pf_suffix_attn_bwd_accum(const pf_attn_desc* desc, int32_t prefix_len,
   set_ds(a, workspace, w);
   set_own_parts(a, workspace, w);
   a.ri = row_info(workspace, w);
-  return run_bwd(d, a, flat_segments(n_suffix, cu_seqlens), (hipStream_t)stream);
+  return run_bwd(d, a, seg, (hipStream_t)stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+pf_status pf_suffix_attn_fwd(const pf_attn_desc* desc, int32_t prefix_len, pf_tensor k_p,
+                             pf_tensor v_p, int32_t n_suffix, const int32_t* cu_seqlens,
+                             pf_tensor q_s, pf_tensor k_s, pf_tensor v_s, pf_tensor o_s,
+                             float* lse_s, void* workspace, size_t workspace_bytes, void* stream) {
+  Desc d;
+  pf_status s = check_desc(desc, &d);
+  if (s != PF_OK) return s;
+  if (prefix_len < 0) return fail(PF_ERR_INVALID_ARG, "prefix_len is negative");
+  int32_t rows = 0;
+  if ((s = check_cu(n_suffix, cu_seqlens, &rows)) != PF_OK) return s;
+  return suffix_fwd_impl(PF_OP_SUFFIX_FWD, d, prefix_len, k_p, v_p, rows,
+                         flat_segments(n_suffix, cu_seqlens), q_s, k_s, v_s, o_s, lse_s,
+                         workspace, workspace_bytes, stream);
+}
+
+pf_status pf_suffix_attn_bwd_accum(const pf_attn_desc* desc, int32_t prefix_len, pf_tensor k_p,
+                                   pf_tensor v_p, int32_t n_suffix, const int32_t* cu_seqlens,
+                                   pf_tensor q_s, pf_tensor k_s, pf_tensor v_s, pf_tensor o_s,
+                                   const float* lse_s, pf_tensor do_s, pf_tensor dq_s,
+                                   pf_tensor dk_s, pf_tensor dv_s, float* gk_acc, float* gv_acc,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  Desc d;
+  pf_status s = check_desc(desc, &d);
+  if (s != PF_OK) return s;
+  if (prefix_len < 0) return fail(PF_ERR_INVALID_ARG, "prefix_len is negative");
+  int32_t rows = 0;
+  if ((s = check_cu(n_suffix, cu_seqlens, &rows)) != PF_OK) return s;
+  return suffix_bwd_impl(PF_OP_SUFFIX_BWD, d, prefix_len, k_p, v_p, rows,
+                         flat_segments(n_suffix, cu_seqlens), q_s, k_s, v_s, o_s, lse_s, do_s,
+                         dq_s, dk_s, dv_s, gk_acc, gv_acc, workspace, workspace_bytes, stream);
+}
+
+pf_status pf_tree_suffix_attn_fwd(const pf_attn_desc* desc, int32_t prefix_len, pf_tensor k_p,
+                                  pf_tensor v_p, int32_t n_nodes, const int32_t* node_off,
+                                  const int32_t* parent, pf_tensor q, pf_tensor k, pf_tensor v,
+                                  pf_tensor o, float* lse, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  Desc d;
+  pf_status s = check_desc(desc, &d);
+  if (s != PF_OK) return s;
+  if (prefix_len < 0) return fail(PF_ERR_INVALID_ARG, "prefix_len is negative");
+  int32_t send[PF_MAX_SEGMENTS];
+  if ((s = check_tree(n_nodes, node_off, parent, send)) != PF_OK) return s;
+  return suffix_fwd_impl(PF_OP_TREE_SUFFIX_FWD, d, prefix_len, k_p, v_p, node_off[n_nodes],
+                         tree_segments(n_nodes, node_off, send), q, k, v, o, lse, workspace,
+                         workspace_bytes, stream);
+}
+
+pf_status pf_tree_suffix_attn_bwd_accum(const pf_attn_desc* desc, int32_t prefix_len,
+                                        pf_tensor k_p, pf_tensor v_p, int32_t n_nodes,
+                                        const int32_t* node_off, const int32_t* parent,
+                                        pf_tensor q, pf_tensor k, pf_tensor v, pf_tensor o,
+                                        const float* lse, pf_tensor dout, pf_tensor dq,
+                                        pf_tensor dk, pf_tensor dv, float* gk_acc, float* gv_acc,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+  Desc d;
+  pf_status s = check_desc(desc, &d);
+  if (s != PF_OK) return s;
+  if (prefix_len < 0) return fail(PF_ERR_INVALID_ARG, "prefix_len is negative");
+  int32_t send[PF_MAX_SEGMENTS];
+  if ((s = check_tree(n_nodes, node_off, parent, send)) != PF_OK) return s;
+  return suffix_bwd_impl(PF_OP_TREE_SUFFIX_BWD, d, prefix_len, k_p, v_p, node_off[n_nodes],
+                         tree_segments(n_nodes, node_off, send), q, k, v, o, lse, dout, dq, dk,
+                         dv, gk_acc, gv_acc, workspace, workspace_bytes, stream);
 }
 
 pf_status pf_prefix_bwd_inject(const pf_attn_desc* desc, int32_t prefix_len, pf_tensor q_p,

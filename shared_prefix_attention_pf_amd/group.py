@@ -17,6 +17,8 @@ from . import (
     PF_OP_SUFFIX_FWD,
     PF_OP_TREE_BWD,
     PF_OP_TREE_FWD,
+    PF_OP_TREE_SUFFIX_BWD,
+    PF_OP_TREE_SUFFIX_FWD,
     AttnDesc,
     pf_prefix_bwd_inject,
     pf_prefix_fwd,
@@ -24,6 +26,8 @@ from . import (
     pf_suffix_attn_fwd,
     pf_tree_attn_bwd,
     pf_tree_attn_fwd,
+    pf_tree_suffix_attn_bwd_accum,
+    pf_tree_suffix_attn_fwd,
     pf_workspace_size,
 )
 
@@ -109,3 +113,28 @@ def tree_bwd(desc, node_off, parent, q, k, v, o, lse, dout, ws=None, stream=None
         ws = workspace(PF_OP_TREE_BWD, desc, 0, rows, q.device)
     pf_tree_attn_bwd(desc, node_off, parent, q, k, v, o, lse, dout, dq, dk, dv, ws, stream)
     return dq, dk, dv
+
+
+def tree_suffix_fwd(desc, k_p, v_p, node_off, parent, q, k, v, ws=None, stream=None):
+    rows = int(node_off[-1])
+    o = torch.empty_like(q)
+    lse = torch.empty(desc.num_q_heads, rows, dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = workspace(PF_OP_TREE_SUFFIX_FWD, desc, k_p.shape[0], rows, q.device)
+    pf_tree_suffix_attn_fwd(desc, k_p.shape[0], k_p, v_p, node_off, parent, q, k, v, o, lse, ws,
+                            stream)
+    return o, lse
+
+
+def tree_suffix_bwd(desc, k_p, v_p, node_off, parent, q, k, v, o, lse, dout, gk_acc, gv_acc,
+                    ws=None, stream=None):
+    rows = int(node_off[-1])
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    if ws is None:
+        ws = workspace(PF_OP_TREE_SUFFIX_BWD, desc, k_p.shape[0], rows, q.device)
+    pf_tree_suffix_attn_bwd_accum(desc, k_p.shape[0], k_p, v_p, node_off, parent, q, k, v, o, lse,
+                                  dout, dq, dk, dv, gk_acc, gv_acc, ws, stream)
+    return dq, dk, dv
+

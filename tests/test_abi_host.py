@@ -149,3 +149,31 @@ def test_prefix_bwd_rejects_bad_dkv_dtype():
                                       ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), t, kv, kv, 7,
                                       ctypes.c_void_p(FAKE), 1 << 30, ctypes.c_void_p(0))
     assert st == pf.PF_ERR_INVALID_ARG
+
+
+def test_tree_window_entry_points_validate_on_the_host():
+    """The tree-window calls reject a bad tree or a short workspace before any
+    launch, and size their workspace like a suffix call over the same rows."""
+    d, _keep = _desc()
+    p32 = ctypes.POINTER(ctypes.c_int32)
+
+    def fwd(node_off, parent, ws_bytes=1 << 30):
+        no = np.asarray(node_off, dtype=np.int32)
+        pa = np.asarray(parent, dtype=np.int32)
+        rows = int(no[-1])
+        q, kv, kp = _t(heads=32), _t(), _t()
+        return pf._lib.pf_tree_suffix_attn_fwd(ctypes.byref(d), 64, kp, kp, len(pa),
+                                               no.ctypes.data_as(p32), pa.ctypes.data_as(p32), q,
+                                               kv, kv, q, ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE),
+                                               ws_bytes, ctypes.c_void_p(0)), rows
+    assert fwd([0, 4, 6], [0, 0])[0] == pf.PF_ERR_INVALID_ARG
+    assert fwd([0, 4, 6, 7], [-1, 2, 0])[0] == pf.PF_ERR_INVALID_ARG
+    desc = pf.AttnDesc(32, 8, 128)
+    rows = 6
+    need = pf.pf_workspace_size(pf.PF_OP_TREE_SUFFIX_FWD, desc, 64, rows)
+    assert need == pf.pf_workspace_size(pf.PF_OP_SUFFIX_FWD, desc, 64, rows) > 0
+    assert fwd([0, 4, 6], [-1, 0], ws_bytes=need - 1)[0] == pf.PF_ERR_WORKSPACE
+    full = pf.pf_workspace_size(pf.PF_OP_TREE_SUFFIX_BWD, desc, 4096, 2048)
+    least = pf.pf_workspace_size_min(pf.PF_OP_TREE_SUFFIX_BWD, desc, 4096, 2048)
+    assert full > least > 0
+

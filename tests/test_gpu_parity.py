@@ -232,6 +232,72 @@ def test_phase_c_and_tree_min_workspace():
         check(f"tree {name}: min ws vs dS buffer", mn, full, TOL["bf16"])
 
 
+@pytest.mark.parametrize("dtype,p", [("bf16", 300), ("bf16", 0), ("f32", 70)])
+def test_tree_windows_over_a_prefix(dtype, p):
+    """Two sharing windows of irregular rollout trees over one cached prefix:
+    each window's outputs against the oracle, the prefix-side gradients
+    accumulated over both windows, then the producer backward (Phase C with
+    the accumulated gK/gV injected).  The first window's backward also runs
+    with the smallest workspace (recompute dQ path)."""
+    hq, hkv = 8, 2
+    d = 128 if dtype == "bf16" else 64
+    print(f"\ntree windows {dtype} P={p}", flush=True)
+    g = random_small_group(41, hq, hkv, d, p, [1], dtype)
+    desc = _desc(hq, hkv, d, dtype)
+    scale = 1.0 / math.sqrt(d)
+    hmap = oracle.head_map(hq, hkv)
+    tol = TOL[dtype]
+    t = {k: dev(g[k], dtype) for k in ("q_p", "k_p", "v_p", "do_p")}
+    gk = torch.zeros(p, hkv, d, dtype=torch.float32, device="cuda")
+    gv = torch.zeros_like(gk)
+    gk_ref = np.zeros((p, hkv, d))
+    gv_ref = np.zeros((p, hkv, d))
+    for w, (seed, n_nodes, max_len) in enumerate(((5, 9, 90), (6, 12, 40))):
+        node_off, parent = random_tree(seed, n_nodes, max_len=max_len, min_len=0)
+        rows = int(node_off[-1])
+        print(f"  window {w}: node_off {node_off.tolist()} parent {parent.tolist()}", flush=True)
+        tg = random_tree_group(seed, node_off, hq, hkv, d, dtype)
+        tt = {k: dev(tg[k], dtype) for k in ("q", "k", "v", "do")}
+        o, lse = G.tree_suffix_fwd(desc, t["k_p"], t["v_p"], node_off, parent, tt["q"], tt["k"],
+                                   tt["v"])
+        if w == 0:
+            n_min = pf.pf_workspace_size_min(pf.PF_OP_TREE_SUFFIX_BWD, desc, p, rows)
+            ws = torch.empty(n_min, dtype=torch.uint8, device="cuda")
+            gk0 = torch.zeros_like(gk)
+            gv0 = torch.zeros_like(gv)
+            mn = G.tree_suffix_bwd(desc, t["k_p"], t["v_p"], node_off, parent, tt["q"], tt["k"],
+                                   tt["v"], o, lse, tt["do"], gk0, gv0, ws=ws)
+        dq, dk, dv = G.tree_suffix_bwd(desc, t["k_p"], t["v_p"], node_off, parent, tt["q"],
+                                       tt["k"], tt["v"], o, lse, tt["do"], gk, gv)
+        torch.cuda.synchronize()
+        ref = oracle.tree_window_attention(g["k_p"], g["v_p"], tg["q"], tg["k"], tg["v"],
+                                           tg["do"], node_off, parent, scale, hmap)
+        gk_ref += ref["gk"]
+        gv_ref += ref["gv"]
+        for name, got in (("O", o), ("LSE", lse), ("dQ", dq), ("dK", dk), ("dV", dv)):
+            check(f"window {w} {name}", host(got), ref[name.lower()], tol)
+        if w == 0:
+            for name, got in zip(("dQ", "dK", "dV"), mn):
+                check(f"window 0 {name} (min ws)", host(got), ref[name.lower()], tol)
+            if p > 0:
+                check("window 0 gK (min ws)", host(gk0), ref["gk"], tol)
+        if p > 0:
+            check(f"gK after window {w}", host(gk), gk_ref, tol)
+            check(f"gV after window {w}", host(gv), gv_ref, tol)
+    if p == 0:
+        return
+    # the producer backward with both windows' gradients injected
+    o_p, lse_p = G.prefix_fwd(desc, t["q_p"], t["k_p"], t["v_p"])
+    dq_p, dk_p, dv_p = G.prefix_bwd(desc, t["q_p"], t["k_p"], t["v_p"], o_p, lse_p, t["do_p"], gk,
+                                    gv)
+    torch.cuda.synchronize()
+    rdq, rdk, rdv = oracle.prefix_backward_inject(g["q_p"], g["k_p"], g["v_p"], g["do_p"], gk_ref,
+                                                  gv_ref, scale, hmap)
+    check("producer dQ_P", host(dq_p), rdq, tol)
+    check("producer dK_P", host(dk_p), rdk, tol)
+    check("producer dV_P", host(dv_p), rdv, tol)
+
+
 def _phase_b_run(desc, t, cu, p, calls):
     """Run Phase B as the given microbatches (lists of suffix indices); return gK, gV."""
     hkv, d = t["k_p"].shape[1], t["k_p"].shape[2]
