@@ -38,7 +38,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2, help="workload (1..5); 2 is the headline")
+    ap.add_argument("--config", type=int, default=2,
+                    help="workload (1..6; 6 is tree windows over a cached prefix); 2 is the headline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample (0 disables)")
     ap.add_argument("--json-out", default=None)
@@ -80,6 +81,12 @@ def tree_pairs(node_off, parent):
         ln = int(node_off[v + 1] - node_off[v])
         total += ln * int(depth_rows[v]) + ln * (ln + 1) // 2
     return total
+
+
+def window_pairs(p, node_off, parent):
+    """Visible pairs per query head of a tree window over a P-row prefix: every
+    row sees the whole prefix, plus its tree pairs."""
+    return int(node_off[-1]) * p + tree_pairs(node_off, parent)
 
 
 # ---------------------------------------------------------------- GPU side
@@ -135,7 +142,53 @@ def run_gpu(cfg, data, steps, warmup, copy_mib=0):
     stream = torch.cuda.current_stream()
     res = {}
     timer = KernelTimer(torch)
-    if cfg.is_tree:
+    if cfg.is_windows:
+        p = cfg.prefix_len
+        q_p, k_p, v_p, do_p = (to_dev(data[n]) for n in ("q_p", "k_p", "v_p", "do_p"))
+        o_p = torch.empty_like(q_p)
+        lse_p = torch.empty(cfg.num_q_heads, p, device=dev)
+        dq_p, dk_p, dv_p = torch.empty_like(q_p), torch.empty_like(k_p), torch.empty_like(v_p)
+        gk = torch.empty(p, cfg.num_kv_heads, cfg.head_dim, device=dev)
+        gv = torch.empty_like(gk)
+        wins = []
+        for wd in data["windows"]:
+            w = {n: to_dev(wd[n]) for n in ("q", "k", "v", "do")}
+            c = w["q"].shape[0]
+            w.update(node_off=wd["node_off"], parent=wd["parent"], o=torch.empty_like(w["q"]),
+                     lse=torch.empty(cfg.num_q_heads, c, device=dev), dq=torch.empty_like(w["q"]),
+                     dk=torch.empty_like(w["k"]), dv=torch.empty_like(w["v"]))
+            wins.append(w)
+        max_c = max(int(wd["node_off"][-1]) for wd in data["windows"])
+        ws_bytes = max(pf.pf_workspace_size(op, desc, p, max_c) for op in
+                       (pf.PF_OP_TREE_SUFFIX_FWD, pf.PF_OP_TREE_SUFFIX_BWD))
+        ws_bytes = max(ws_bytes, pf.pf_workspace_size(pf.PF_OP_PREFIX_BWD, desc, p, p))
+        ws = torch.empty(max(16, ws_bytes), dtype=torch.uint8, device=dev)
+
+        def step(ev=None):
+            gk.zero_()
+            gv.zero_()
+            timer.phase = "A"
+            if ev:
+                ev[0].record(stream)
+            pf.pf_prefix_fwd(desc, p, q_p, k_p, v_p, o_p, lse_p, ws)
+            if ev:
+                ev[1].record(stream)
+            timer.phase = "B"
+            for w in wins:
+                pf.pf_tree_suffix_attn_fwd(desc, p, k_p, v_p, w["node_off"], w["parent"], w["q"],
+                                           w["k"], w["v"], w["o"], w["lse"], ws)
+                pf.pf_tree_suffix_attn_bwd_accum(desc, p, k_p, v_p, w["node_off"], w["parent"],
+                                                 w["q"], w["k"], w["v"], w["o"], w["lse"],
+                                                 w["do"], w["dq"], w["dk"], w["dv"], gk, gv, ws)
+            timer.phase = "C"
+            if ev:
+                ev[2].record(stream)
+            pf.pf_prefix_bwd_inject(desc, p, q_p, k_p, v_p, o_p, lse_p, do_p, gk, gv, dq_p, dk_p,
+                                    dv_p, pdt, ws)
+            if ev:
+                ev[3].record(stream)
+        phase_names = ("A", "B", "C")
+    elif cfg.is_tree:
         node_off, parent = data["node_off"], data["parent"]
         q, k, v, do = (to_dev(data[n]) for n in ("q", "k", "v", "do"))
         c = q.shape[0]
@@ -477,7 +530,16 @@ def cpu_baseline(cfg, data, target_s):
     for kvh in range(cfg.num_kv_heads):
         heads = slice(kvh * g, (kvh + 1) * g)
         t0 = time.perf_counter()
-        if cfg.is_tree:
+        if cfg.is_windows:
+            pairs = 0
+            for w in data["windows"]:
+                oracle.tree_window_attention(data["k_p"][:, kvh:kvh + 1],
+                                             data["v_p"][:, kvh:kvh + 1], w["q"][:, heads],
+                                             w["k"][:, kvh:kvh + 1], w["v"][:, kvh:kvh + 1],
+                                             w["do"][:, heads], w["node_off"], w["parent"], scale,
+                                             hmap, dtype=np.float32)
+                pairs += window_pairs(cfg.prefix_len, w["node_off"], w["parent"])
+        elif cfg.is_tree:
             oracle.tree_attention_direct(data["q"][:, heads], data["k"][:, kvh:kvh + 1],
                                          data["v"][:, kvh:kvh + 1], data["do"][:, heads],
                                          data["node_off"], data["parent"], scale, hmap,
@@ -494,7 +556,8 @@ def cpu_baseline(cfg, data, target_s):
         done_groups += 1
         if elapsed >= target_s:
             break
-    what = "tree fwd+bwd" if cfg.is_tree else "Phase B fwd+bwd"
+    what = ("tree fwd+bwd" if cfg.is_tree else
+            "tree-window fwd+bwd" if cfg.is_windows else "Phase B fwd+bwd")
     return {
         "value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads),
         "kind": "oracle",
@@ -531,7 +594,16 @@ def main():
     print("[bench] running GPU steps", flush=True)
     gres = run_gpu(cfg, data, args.steps, args.warmup, args.copy_probe_mib)
     d, hq = cfg.head_dim, cfg.num_q_heads
-    if cfg.is_tree:
+    if cfg.is_windows:
+        from oracle import tree_trajectories
+        p = cfg.prefix_len
+        pairs_b = sum(window_pairs(p, w["node_off"], w["parent"]) for w in data["windows"])
+        pairs_a = p * (p + 1) // 2
+        compact = p + sum(int(w["node_off"][-1]) for w in data["windows"])
+        expanded = int(sum(p + len(t) for w in data["windows"]
+                           for t in tree_trajectories(w["node_off"], w["parent"])))
+        b_ms = gres["phase_ms"]["B"]
+    elif cfg.is_tree:
         pairs_b = tree_pairs(data["node_off"], data["parent"])
         pairs_a = 0
         compact = int(data["node_off"][-1])
@@ -605,9 +677,12 @@ def main():
             "workload": f"config {cfg.cid}: {cfg.name}",
             "num_q_heads": hq, "num_kv_heads": cfg.num_kv_heads, "head_dim": d,
             "prefix_len": cfg.prefix_len,
-            "suffix_lens": (None if cfg.is_tree else
+            "suffix_lens": (None if cfg.is_tree or cfg.is_windows else
                             np.diff(data["cu_seqlens"]).astype(int).tolist()),
-            "microbatches": None if cfg.is_tree else len(data["microbatches"]),
+            "microbatches": (len(data["windows"]) if cfg.is_windows else
+                             None if cfg.is_tree else len(data["microbatches"])),
+            "window_rows": ([int(w["node_off"][-1]) for w in data["windows"]]
+                            if cfg.is_windows else None),
             "parallelism": "single GPU",
         },
         "pct_of_bf16_peak": round(100.0 * value / peak, 2),

@@ -1,10 +1,12 @@
-"""The five synthetic group shapes the path is tested and measured on.
+"""The synthetic group shapes the path is tested and measured on (five groups,
+and a sixth workload of tree windows over a cached prefix).
 
 Shapes follow the workloads the PrefixFlow page trains on (flat GRPO groups
 [P || S_i], PrefixFlow §2.1; long-prefix RAG groups, §5.2 Claim 2.1; the
 large-N prefix-ratio sweep, §5.4 Claim 3) and the rollout trees of the HARTS
-page (§2.1, compact representation).  Inputs are synthetic N(0,1) draws; no
-dataset item is reproduced.
+page (§2.1, compact representation; §3.4, sharing windows whose consumers
+read a producer's cached ancestor K/V).  Inputs are synthetic N(0,1) draws;
+no dataset item is reproduced.
 """
 from dataclasses import dataclass, field
 from typing import List, Optional, Tuple
@@ -26,12 +28,20 @@ class Config:
     microbatches: int = 1      # Phase B calls; microbatch k takes suffixes in index order
     # tree config: fan-out per level and node length per level (root first)
     tree_levels: Optional[Tuple[Tuple[int, int], ...]] = None
+    # tree windows over the prefix: windows, nodes per window, node length range
+    windows: int = 0
+    window_nodes: int = 0
+    node_len_range: Optional[Tuple[int, int]] = None
     seed: int = 0
     note: str = ""
 
     @property
     def is_tree(self) -> bool:
         return self.tree_levels is not None
+
+    @property
+    def is_windows(self) -> bool:
+        return self.windows > 0
 
     @property
     def group_size(self) -> int:
@@ -54,6 +64,11 @@ CONFIGS: List[Config] = [
            tree_levels=((1, 4096), (4, 1024), (4, 256)), seed=5,
            note="DFS-preorder compact rows: root 4096, 4 children of 1024, 4 leaves of 256 each; "
                 "12288 compact rows, 16 trajectories"),
+    Config(6, "windows-bf16-p4096-4x24-irregular", "bf16", 32, 8, 128, 4096, windows=4,
+           window_nodes=24, node_len_range=(32, 256), seed=6,
+           note="the next row after the five groups: 4 sharing windows over one cached 4096-row "
+                "prefix, each an irregular tree of 24 nodes (each node's parent uniform over the "
+                "earlier nodes, lengths uniform on [32, 256]), one call per window"),
 ]
 
 

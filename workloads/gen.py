@@ -80,10 +80,36 @@ def generate(cfg: Config, include_prefix_q: bool = True) -> Dict[str, np.ndarray
     cu_seqlens [N+1] (int32, over the packed suffix rows) and `microbatches`,
     a list of (first_suffix, last_suffix_exclusive).
     Tree groups: q, k, v, do [C, H, d]; node_off [n+1]; parent [n].
+    Tree windows: q_p, k_p, v_p, do_p of the prefix and `windows`, a list of
+    dicts with node_off, parent, q, k, v, do per window.
     """
     rng = np.random.Generator(np.random.PCG64(cfg.seed))
     hq, hkv, d = cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim
     out: Dict[str, np.ndarray] = {}
+    if cfg.is_windows:
+        # the cached prefix, then each window's tree (from its own seed,
+        # 100 seed + w) and rows
+        p = cfg.prefix_len
+        if include_prefix_q:
+            out["q_p"] = _normal(rng, (p, hq, d), cfg.dtype)
+        else:
+            _normal(rng, (p, hq, d), cfg.dtype)
+        out["k_p"] = _normal(rng, (p, hkv, d), cfg.dtype)
+        out["v_p"] = _normal(rng, (p, hkv, d), cfg.dtype)
+        out["do_p"] = _normal(rng, (p, hq, d), cfg.dtype)
+        lo, hi = cfg.node_len_range
+        wins = []
+        for w in range(cfg.windows):
+            node_off, parent = random_tree(100 * cfg.seed + w, cfg.window_nodes, max_len=hi,
+                                           min_len=lo)
+            c = int(node_off[-1])
+            wins.append({"node_off": node_off, "parent": parent,
+                         "q": _normal(rng, (c, hq, d), cfg.dtype),
+                         "k": _normal(rng, (c, hkv, d), cfg.dtype),
+                         "v": _normal(rng, (c, hkv, d), cfg.dtype),
+                         "do": _normal(rng, (c, hq, d), cfg.dtype)})
+        out["windows"] = wins
+        return out
     if cfg.is_tree:
         node_off, parent = tree_layout(cfg.tree_levels)
         c = int(node_off[-1])
