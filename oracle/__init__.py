@@ -13,7 +13,9 @@ identity, prefix-gradient superposition via a packed-graph formulation,
 GQA = MHA with repeated K/V, tree expanded-vs-direct, the reductions of
 trees to flat groups and causal chains, and tree windows over a prefix
 against per-trajectory flat Phase B (expansion with a split upstream), a
-chain tree as one flat suffix, and P = 0 as a plain tree.
+chain tree as one flat suffix, and P = 0 as a plain tree; compact
+log-probabilities against torch log_softmax and autograd on the expanded
+per-position logits, and scipy's logsumexp.
 
 Sources (page titles and sections):
   * PrefixFlow: Training-Time KV Caching for Schedule-Level Prefix Reuse in
@@ -24,9 +26,11 @@ Sources (page titles and sections):
     Hybrid-Attention Models — §2.1 (rollout trees, compact rows), §2.2
     (full attention reads ancestor K/V through a tree mask), §3 (gather
     backward sums into shared rows; producer / consumer sharing windows,
-    consumer gradients accumulated before one producer backward).
+    consumer gradients accumulated before one producer backward), §3.5
+    (compact log-probability recovery).
 """
 from .attention import attention_backward, attention_forward, head_map
+from .logprob import compact_logprob, positions_by_row, row_logsumexp
 from .masks import causal_mask, suffix_rows_mask, tree_ancestor_mask, tree_node_of_row
 from .phases import (
     prefix_backward_inject,
@@ -40,6 +44,9 @@ from .phases import (
 )
 
 __all__ = [
+    "compact_logprob",
+    "positions_by_row",
+    "row_logsumexp",
     "attention_backward",
     "attention_forward",
     "head_map",
