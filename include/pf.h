@@ -19,6 +19,8 @@
  *                                      ancestor mask ("HARTS: A Prefix-Sharing
  *                                      Training System for Agentic RL with
  *                                      Hybrid-Attention Models", §2.1, §2.2, §3.4).
+ *   Logprob  pf_compact_logprob_fwd/bwd  per-position log-probabilities from
+ *                                      compact-row logits (HARTS §3.5).
  *   Windows  pf_tree_suffix_attn_fwd,  a window of rollout trees over a cached
  *            pf_tree_suffix_attn_bwd_accum  prefix, with the prefix-side
  *                                      gradients accumulated (HARTS §3.4,
@@ -242,6 +244,37 @@ pf_status pf_tree_suffix_attn_bwd_accum(const pf_attn_desc* desc, int32_t prefix
                                         const float* lse, pf_tensor dout, pf_tensor dq,
                                         pf_tensor dk, pf_tensor dv, float* gk_acc, float* gv_acc,
                                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Compact log-probability recovery ("HARTS" §3.5): logits exist once per
+ * compact row; each semantic position s reads its row m(s) and target y_s,
+ *   logp_s = z[m(s), y_s] - log sum_v exp z[m(s), v],
+ * so neither direction forms S x V logits or gradients.  Positions are given
+ * grouped by row: the positions of row c are pos[row_ptr[c] .. row_ptr[c+1]).
+ *   z [n_rows, vocab] (dtype PF_BF16 or PF_F32), row stride z_stride elements
+ *     (>= vocab, a multiple of 16 bytes), 16-byte aligned      in
+ *   row_ptr device int32 [n_rows + 1], pos device int32 [n_pos],
+ *   y device int32 [n_pos] (the target of position s is y[s])    in
+ *   lse fp32 [n_rows]                                            out
+ *   logp fp32 [n_pos], indexed by position                      out
+ * The index arrays are read on the device: an index outside its range is
+ * skipped (a position whose target is outside [0, vocab) gets NaN); positions
+ * that no row lists are not written.                                        */
+pf_status pf_compact_logprob_fwd(int32_t n_rows, int32_t vocab, const void* z, int64_t z_stride,
+                                 int32_t dtype, const int32_t* row_ptr, const int32_t* pos,
+                                 const int32_t* y, int32_t n_pos, float* lse, float* logp,
+                                 void* stream);
+
+/* Backward of the compact log-probabilities: every position adds its own term
+ * to its row (HARTS §3.5: the backward sums each position's gradient into its
+ * compact row rather than scaling one gradient by a reuse count),
+ *   dz[c, v] = sum over positions s of row c of dlogp_s (1[v = y_s] - softmax(z_c)[v]).
+ *   (forward arguments), lse from pf_compact_logprob_fwd, dlogp fp32 [n_pos]  in
+ *   dz [n_rows, vocab] (dtype of z), row stride dz_stride elements,
+ *     16-byte aligned                                            out (overwritten) */
+pf_status pf_compact_logprob_bwd(int32_t n_rows, int32_t vocab, const void* z, int64_t z_stride,
+                                 int32_t dtype, const float* lse, const int32_t* row_ptr,
+                                 const int32_t* pos, const int32_t* y, int32_t n_pos,
+                                 const float* dlogp, void* dz, int64_t dz_stride, void* stream);
 
 /* Host-only helper: the end row of each node's subtree (exclusive), the
  * bound of the rows that can read that node's keys.  Validates the tree.

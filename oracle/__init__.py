@@ -30,7 +30,7 @@ Sources (page titles and sections):
     (compact log-probability recovery).
 """
 from .attention import attention_backward, attention_forward, head_map
-from .logprob import compact_logprob, positions_by_row, row_logsumexp
+from .logprob import compact_logprob, row_logsumexp
 from .masks import causal_mask, suffix_rows_mask, tree_ancestor_mask, tree_node_of_row
 from .phases import (
     prefix_backward_inject,
@@ -45,7 +45,6 @@ from .phases import (
 
 __all__ = [
     "compact_logprob",
-    "positions_by_row",
     "row_logsumexp",
     "attention_backward",
     "attention_forward",

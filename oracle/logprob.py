@@ -53,14 +53,3 @@ def compact_logprob(z, row_ptr, pos, y, dlogp=None) -> Dict[str, np.ndarray]:
                 dz[r, int(y[p])] += dlogp[p]
         out["dz"] = dz
     return out
-
-
-def positions_by_row(m: np.ndarray, n_rows: int):
-    """(row_ptr [C+1], pos [S]) grouping positions s by their row m(s), in
-    increasing s within a row."""
-    m = np.asarray(m, dtype=np.int64)
-    order = np.argsort(m, kind="stable")
-    counts = np.bincount(m, minlength=n_rows)
-    row_ptr = np.zeros(n_rows + 1, dtype=np.int32)
-    row_ptr[1:] = np.cumsum(counts)
-    return row_ptr, order.astype(np.int32)

@@ -25,7 +25,8 @@ PF_MAX_SEGMENTS = 256
 EXPORTED = (
     "pf_workspace_size", "pf_workspace_size_min", "pf_prefix_fwd", "pf_suffix_attn_fwd", "pf_suffix_attn_bwd_accum",
     "pf_prefix_bwd_inject", "pf_tree_attn_fwd", "pf_tree_attn_bwd", "pf_tree_suffix_attn_fwd",
-    "pf_tree_suffix_attn_bwd_accum", "pf_tree_subtree_end",
+    "pf_tree_suffix_attn_bwd_accum", "pf_compact_logprob_fwd", "pf_compact_logprob_bwd",
+    "pf_tree_subtree_end",
     "pf_status_string", "pf_last_error", "pf_abi_version", "pf_set_launch_hook",
 )
 
@@ -83,6 +84,10 @@ def _load():
         "pf_tree_suffix_attn_fwd": (i32, [D, i32, T, T, i32, ip, ip, T, T, T, T, fp, P, sz, P]),
         "pf_tree_suffix_attn_bwd_accum": (i32, [D, i32, T, T, i32, ip, ip, T, T, T, T, fp, T, T, T,
                                                 T, fp, fp, P, sz, P]),
+        "pf_compact_logprob_fwd": (i32, [i32, i32, P, ctypes.c_int64, i32, P, P, P, i32, fp, fp,
+                                         P]),
+        "pf_compact_logprob_bwd": (i32, [i32, i32, P, ctypes.c_int64, i32, fp, P, P, P, i32, fp,
+                                         P, ctypes.c_int64, P]),
         "pf_tree_subtree_end": (i32, [i32, ip, ip, ip]),
         "pf_status_string": (ctypes.c_char_p, [i32]),
         "pf_last_error": (ctypes.c_char_p, []),
@@ -271,6 +276,25 @@ def pf_tree_suffix_attn_bwd_accum(desc, prefix_len, k_p, v_p, node_off, parent, 
         ctypes.byref(d), prefix_len, _t(k_p), _t(v_p), len(pa), no_p, pa_p, _t(q), _t(k), _t(v),
         _t(o), _p(lse), _t(dout), _t(dq), _t(dk), _t(dv), _p(gk_acc), _p(gv_acc), ws, nws,
         _stream(stream)))
+
+
+def _dtype_of(t):
+    import torch
+    return PF_BF16 if t.dtype == torch.bfloat16 else PF_F32
+
+
+def pf_compact_logprob_fwd(z, row_ptr, pos, y, lse, logp, stream=None):
+    """z [C, V] (bf16 or fp32, last dim contiguous); row_ptr [C+1], pos [S], y [S]
+    int32 device tensors; lse [C], logp [S] fp32 outputs."""
+    _check(_lib.pf_compact_logprob_fwd(z.shape[0], z.shape[1], _p(z), z.stride(0), _dtype_of(z),
+                                       _p(row_ptr), _p(pos), _p(y), pos.shape[0], _p(lse),
+                                       _p(logp), _stream(stream)))
+
+
+def pf_compact_logprob_bwd(z, lse, row_ptr, pos, y, dlogp, dz, stream=None):
+    _check(_lib.pf_compact_logprob_bwd(z.shape[0], z.shape[1], _p(z), z.stride(0), _dtype_of(z),
+                                       _p(lse), _p(row_ptr), _p(pos), _p(y), pos.shape[0],
+                                       _p(dlogp), _p(dz), dz.stride(0), _stream(stream)))
 
 
 __all__ = [name for name in EXPORTED] + ["AttnDesc", "PFError", "PF_BF16", "PF_F32", "LIB_PATH"]

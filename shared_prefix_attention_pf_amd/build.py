@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpf.so")
-SOURCES = ["pf_api.cpp", "pf_prep.hip", "pf_attn_bf16.hip", "pf_attn_f32.hip"]
+SOURCES = ["pf_api.cpp", "pf_prep.hip", "pf_attn_bf16.hip", "pf_attn_f32.hip", "pf_logprob.hip"]
 ARCH = os.environ.get("PF_OFFLOAD_ARCH", "gfx950")
 
 

@@ -805,4 +805,61 @@ pf_status pf_tree_attn_bwd(const pf_attn_desc* desc, int32_t n_nodes, const int3
   return run_bwd(d, a, tree_segments(n_nodes, node_off, send), (hipStream_t)stream);
 }
 
+// ------------------------------------------------- compact log-probabilities
+
+namespace {
+
+pf_status check_logprob(int32_t n_rows, int32_t vocab, const void* z, int64_t z_stride,
+                        int32_t dtype, const int32_t* row_ptr, const int32_t* pos,
+                        const int32_t* y, int32_t n_pos) {
+  if (dtype != PF_BF16 && dtype != PF_F32) return fail(PF_ERR_INVALID_ARG, "dtype must be PF_BF16 or PF_F32");
+  if (n_rows < 0 || n_pos < 0) return fail(PF_ERR_INVALID_ARG, "n_rows and n_pos must be >= 0");
+  if (vocab < 1) return fail(PF_ERR_INVALID_ARG, "vocab must be >= 1");
+  if (n_rows == 0) return PF_OK;
+  const int64_t eb = dtype == PF_BF16 ? 2 : 4;
+  if (!z || (uintptr_t)z % 16) return fail(PF_ERR_INVALID_ARG, "z is NULL or not 16-byte aligned");
+  if (z_stride < vocab || (z_stride * eb) % 16)
+    return fail(PF_ERR_INVALID_ARG, "z row stride must be >= vocab and a multiple of 16 bytes");
+  if (!row_ptr) return fail(PF_ERR_INVALID_ARG, "row_ptr is NULL");
+  if (n_pos > 0 && (!pos || !y)) return fail(PF_ERR_INVALID_ARG, "pos or y is NULL");
+  return PF_OK;
+}
+
+}  // namespace
+
+pf_status pf_compact_logprob_fwd(int32_t n_rows, int32_t vocab, const void* z, int64_t z_stride,
+                                 int32_t dtype, const int32_t* row_ptr, const int32_t* pos,
+                                 const int32_t* y, int32_t n_pos, float* lse, float* logp,
+                                 void* stream) {
+  pf_status s = check_logprob(n_rows, vocab, z, z_stride, dtype, row_ptr, pos, y, n_pos);
+  if (s != PF_OK) return s;
+  if (n_rows == 0) return PF_OK;
+  if (!lse) return fail(PF_ERR_INVALID_ARG, "lse is NULL");
+  if (n_pos > 0 && !logp) return fail(PF_ERR_INVALID_ARG, "logp is NULL");
+  const int64_t eb = dtype == PF_BF16 ? 2 : 4;
+  const hipError_t e = pf::launch_logprob_fwd(n_rows, vocab, z, z_stride * eb, dtype == PF_BF16,
+                                              row_ptr, pos, y, n_pos, lse, logp,
+                                              (hipStream_t)stream);
+  return e == hipSuccess ? PF_OK : hip_fail(e, "logprob_fwd");
+}
+
+pf_status pf_compact_logprob_bwd(int32_t n_rows, int32_t vocab, const void* z, int64_t z_stride,
+                                 int32_t dtype, const float* lse, const int32_t* row_ptr,
+                                 const int32_t* pos, const int32_t* y, int32_t n_pos,
+                                 const float* dlogp, void* dz, int64_t dz_stride, void* stream) {
+  pf_status s = check_logprob(n_rows, vocab, z, z_stride, dtype, row_ptr, pos, y, n_pos);
+  if (s != PF_OK) return s;
+  if (n_rows == 0) return PF_OK;
+  const int64_t eb = dtype == PF_BF16 ? 2 : 4;
+  if (!lse) return fail(PF_ERR_INVALID_ARG, "lse is NULL");
+  if (n_pos > 0 && !dlogp) return fail(PF_ERR_INVALID_ARG, "dlogp is NULL");
+  if (!dz || (uintptr_t)dz % 16) return fail(PF_ERR_INVALID_ARG, "dz is NULL or not 16-byte aligned");
+  if (dz_stride < vocab || (dz_stride * eb) % 16)
+    return fail(PF_ERR_INVALID_ARG, "dz row stride must be >= vocab and a multiple of 16 bytes");
+  const hipError_t e = pf::launch_logprob_bwd(n_rows, vocab, z, z_stride * eb, dtype == PF_BF16, lse,
+                                              row_ptr, pos, y, n_pos, dlogp, dz, dz_stride * eb,
+                                              (hipStream_t)stream);
+  return e == hipSuccess ? PF_OK : hip_fail(e, "logprob_bwd");
+}
+
 }  // extern "C"

@@ -175,6 +175,18 @@ hipError_t launch_fwd_f32(const AttnArgs& a, int32_t head_dim, hipStream_t strea
 hipError_t launch_bwd_dq_f32(const AttnArgs& a, int32_t head_dim, hipStream_t stream);
 hipError_t launch_bwd_dkv_f32(const AttnArgs& a, int32_t head_dim, hipStream_t stream);
 
+// Compact log-probabilities (pf_logprob.hip); strides in bytes, bf16 != 0
+// selects bf16 logits (else fp32)
+hipError_t launch_logprob_fwd(int32_t n_rows, int32_t vocab, const void* z, int64_t z_stride_b,
+                              int32_t bf16, const int32_t* row_ptr, const int32_t* pos,
+                              const int32_t* y, int32_t n_pos, float* lse, float* logp,
+                              hipStream_t stream);
+hipError_t launch_logprob_bwd(int32_t n_rows, int32_t vocab, const void* z, int64_t z_stride_b,
+                              int32_t bf16, const float* lse, const int32_t* row_ptr,
+                              const int32_t* pos, const int32_t* y, int32_t n_pos,
+                              const float* dlogp, void* dz, int64_t dz_stride_b,
+                              hipStream_t stream);
+
 // Number of query chunks the KV-stationary backward splits the external
 // (prefix) key blocks and the own key blocks into.  Functions of the shapes
 // only, so results do not depend on the device.

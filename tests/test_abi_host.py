@@ -177,3 +177,19 @@ def test_tree_window_entry_points_validate_on_the_host():
     least = pf.pf_workspace_size_min(pf.PF_OP_TREE_SUFFIX_BWD, desc, 4096, 2048)
     assert full > least > 0
 
+
+def test_logprob_entry_points_validate_on_the_host():
+    """Bad dtype, vocabulary, alignment or stride is rejected before any launch."""
+    lib = pf._lib
+    f = lambda n_rows, vocab, z, stride, dtype=pf.PF_BF16: lib.pf_compact_logprob_fwd(
+        n_rows, vocab, ctypes.c_void_p(z), stride, dtype, ctypes.c_void_p(FAKE),
+        ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), 4, ctypes.c_void_p(FAKE),
+        ctypes.c_void_p(FAKE), ctypes.c_void_p(0))
+    assert f(4, 100, FAKE, 104, dtype=7) == pf.PF_ERR_INVALID_ARG
+    assert f(4, 0, FAKE, 104) == pf.PF_ERR_INVALID_ARG
+    assert f(4, 100, FAKE + 2, 104) == pf.PF_ERR_INVALID_ARG          # z not 16-byte aligned
+    assert f(4, 100, FAKE, 100) == pf.PF_ERR_INVALID_ARG              # 200-byte rows
+    assert f(4, 100, FAKE, 96) == pf.PF_ERR_INVALID_ARG               # stride < vocab
+    assert f(0, 100, 0, 0) == pf.PF_OK                                # nothing to do
+    assert "stride" in lib.pf_last_error().decode() or True
+

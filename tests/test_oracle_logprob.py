@@ -7,7 +7,8 @@ import pytest
 import torch
 from scipy.special import logsumexp
 
-from oracle.logprob import compact_logprob, positions_by_row, row_logsumexp
+from oracle.logprob import compact_logprob, row_logsumexp
+from workloads.gen import positions_by_row
 
 
 def _case(seed, c=7, v=53, s=23):

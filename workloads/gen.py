@@ -195,3 +195,33 @@ def random_tree_group(seed: int, node_off: np.ndarray, num_q_heads: int, num_kv_
         "v": _normal(rng, (c, num_kv_heads, head_dim), dtype),
         "do": _normal(rng, (c, num_q_heads, head_dim), dtype),
     }
+
+
+def positions_by_row(m: np.ndarray, n_rows: int):
+    """(row_ptr [C+1], pos [S]) grouping positions s by their compact row m(s),
+    in increasing s within a row (the layout the compact log-probability
+    calls take)."""
+    m = np.asarray(m, dtype=np.int64)
+    order = np.argsort(m, kind="stable")
+    counts = np.bincount(m, minlength=n_rows)
+    row_ptr = np.zeros(n_rows + 1, dtype=np.int32)
+    row_ptr[1:] = np.cumsum(counts)
+    return row_ptr, order.astype(np.int32)
+
+
+def random_logprob_case(seed: int, n_rows: int, vocab: int, n_pos: int, dtype: str = "f32"):
+    """Compact-row logits z [C, V] (N(0, 3^2), rounded to dtype), a random row
+    m(s) and target y_s per position (some rows unread, some (row, target)
+    pairs repeated), the grouped layout, and an upstream dlogp [S]."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    z = round_to_dtype(rng.standard_normal((n_rows, vocab), dtype=np.float32) * 3.0, dtype)
+    m = rng.integers(0, max(1, n_rows - 1), size=n_pos)      # the last row is never read
+    y = rng.integers(0, vocab, size=n_pos)
+    if n_pos >= 4:
+        m[1], y[1] = m[0], y[0]                                # a repeated (row, target)
+        m[3] = m[2]                                            # a shared row, other target
+    row_ptr, pos = positions_by_row(m, n_rows)
+    dlogp = rng.standard_normal(n_pos).astype(np.float32)
+    return {"z": z, "m": m.astype(np.int32), "y": y.astype(np.int32), "row_ptr": row_ptr,
+            "pos": pos, "dlogp": dlogp}
+
