@@ -39,7 +39,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2,
-                    help="workload (1..6; 6 is tree windows over a cached prefix); 2 is the headline")
+                    help="workload (1..7; 6 is tree windows over a cached prefix, 7 compact "
+                         "log-probabilities); 2 is the headline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample (0 disables)")
     ap.add_argument("--json-out", default=None)
@@ -569,6 +570,99 @@ def cpu_baseline(cfg, data, target_s):
     }
 
 
+def run_logprob(cfg, data, args):
+    """Compact log-probabilities (forward + backward) of one tree's compact rows:
+    HBM-bound, so the line reports GB/s against the 8 TB/s HBM peak."""
+    import torch
+
+    import oracle
+    import shared_prefix_attention_pf_amd as pf
+
+    dev = torch.device("cuda:0")
+    c, v = int(data["node_off"][-1]), cfg.logprob_vocab
+    s_pos = len(data["m"])
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(cfg.seed)
+    z = (torch.randn(c, v, generator=gen, device=dev) * 3.0).to(torch.bfloat16)
+    ints = {k: torch.from_numpy(data[k]).to(dev) for k in ("row_ptr", "pos", "y")}
+    dl = torch.from_numpy(data["dlogp"]).to(dev)
+    lse = torch.empty(c, device=dev)
+    logp = torch.empty(s_pos, device=dev)
+    dz = torch.empty_like(z)
+    stream = torch.cuda.current_stream()
+    timer = KernelTimer(torch)
+
+    def step():
+        pf.pf_compact_logprob_fwd(z, ints["row_ptr"], ints["pos"], ints["y"], lse, logp)
+        pf.pf_compact_logprob_bwd(z, lse, ints["row_ptr"], ints["pos"], ints["y"], dl, dz)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    timer.phase = "logprob"
+    pf.pf_set_launch_hook(timer)
+    try:
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(args.steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    finally:
+        pf.pf_set_launch_hook(None)
+    ms = e0.elapsed_time(e1) / args.steps
+    eb = 2
+    # algorithmic bytes: the logits read once forward, read and dz written once
+    # backward, plus the per-position index, target and gradient arrays
+    per_pos = 4 * 4
+    fwd_bytes = c * v * eb + c * 4 + s_pos * per_pos + (c + 1) * 4
+    bwd_bytes = 2 * c * v * eb + c * 4 + s_pos * per_pos + (c + 1) * 4
+    value = (fwd_bytes + bwd_bytes) / (ms * 1e-3) / 1e9
+    kern = timer.summary()
+    dom = max(kern, key=lambda k: kern[k]["total_ms"])
+    dom_bytes = bwd_bytes if dom == "pf_logprob_bwd" else fwd_bytes
+    achieved = dom_bytes / (kern[dom]["avg_ms"] * 1e-3) / 1e9
+    cpu = None
+    if args.cpu_seconds > 0:
+        print("[bench] timing the CPU oracle", flush=True)
+        zs = z.float().cpu().numpy()
+        rp, ps, ys = data["row_ptr"], data["pos"], data["y"]
+        rows, t_cpu = 0, 0.0
+        while rows < c and t_cpu < args.cpu_seconds:
+            r1 = min(c, rows + 16)
+            sub_ptr = (rp[rows:r1 + 1] - rp[rows]).astype(np.int32)
+            sub_pos = ps[rp[rows]:rp[r1]]
+            t0 = time.perf_counter()
+            oracle.compact_logprob(zs[rows:r1], sub_ptr, sub_pos, ys, data["dlogp"])
+            t_cpu += time.perf_counter() - t0
+            rows = r1
+        sample_bytes = 3 * rows * v * eb
+        # numpy's elementwise exp and sums run on one thread
+        cpu = {"value": sample_bytes / t_cpu / 1e9, "unit": "GB/s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"compact log-prob fwd+bwd of {rows} of {c} rows (fp64 numpy; bytes "
+                         f"counted as bf16 logits read twice and dz written once), {t_cpu:.1f} s"}
+    out = {
+        "metric": "compact log-prob fwd+bwd HBM GB/s (algorithmic bytes)",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"config {cfg.cid}: {cfg.name}", "rows": c, "vocab": v,
+                   "positions": s_pos},
+        "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv)
+                        for kk, vv in kv.items()} for k, kv in kern.items()},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": None, "algorithmic_bytes_per_launch": dom_bytes,
+                     "avg_launch_ms": round(kern[dom]["avg_ms"], 4)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -591,6 +685,10 @@ def main():
     cfg = get_config(args.config)
     print(f"[bench] generating config {cfg.cid} ({cfg.name})", flush=True)
     data = generate(cfg)
+    if cfg.is_logprob:
+        print("[bench] running GPU steps", flush=True)
+        run_logprob(cfg, data, args)
+        return
     print("[bench] running GPU steps", flush=True)
     gres = run_gpu(cfg, data, args.steps, args.warmup, args.copy_probe_mib)
     d, hq = cfg.head_dim, cfg.num_q_heads

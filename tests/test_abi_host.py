@@ -191,5 +191,4 @@ def test_logprob_entry_points_validate_on_the_host():
     assert f(4, 100, FAKE, 100) == pf.PF_ERR_INVALID_ARG              # 200-byte rows
     assert f(4, 100, FAKE, 96) == pf.PF_ERR_INVALID_ARG               # stride < vocab
     assert f(0, 100, 0, 0) == pf.PF_OK                                # nothing to do
-    assert "stride" in lib.pf_last_error().decode() or True
 

@@ -32,6 +32,9 @@ class Config:
     windows: int = 0
     window_nodes: int = 0
     node_len_range: Optional[Tuple[int, int]] = None
+    # compact log-probabilities: vocabulary of the compact-row logits (the
+    # rows and positions are those of tree_levels)
+    logprob_vocab: int = 0
     seed: int = 0
     note: str = ""
 
@@ -42,6 +45,10 @@ class Config:
     @property
     def is_windows(self) -> bool:
         return self.windows > 0
+
+    @property
+    def is_logprob(self) -> bool:
+        return self.logprob_vocab > 0
 
     @property
     def group_size(self) -> int:
@@ -69,6 +76,11 @@ CONFIGS: List[Config] = [
            note="the next row after the five groups: 4 sharing windows over one cached 4096-row "
                 "prefix, each an irregular tree of 24 nodes (each node's parent uniform over the "
                 "earlier nodes, lengths uniform on [32, 256]), one call per window"),
+    Config(7, "logprob-bf16-tree5-v151936", "bf16", 16, 4, 128, 0,
+           tree_levels=((1, 4096), (4, 1024), (4, 256)), logprob_vocab=151936, seed=7,
+           note="compact log-probabilities of the config-5 tree: 12288 compact rows of bf16 "
+                "logits over a 151936-token vocabulary, 86016 trajectory positions mapped to "
+                "their rows, targets uniform; logits drawn on the device from the seed"),
 ]
 
 

@@ -110,6 +110,15 @@ def generate(cfg: Config, include_prefix_q: bool = True) -> Dict[str, np.ndarray
                          "do": _normal(rng, (c, hq, d), cfg.dtype)})
         out["windows"] = wins
         return out
+    if cfg.is_logprob:
+        # structure only; the C x V logits are drawn on the device by the caller
+        node_off, parent = tree_layout(cfg.tree_levels)
+        m = np.concatenate(tree_paths(node_off, parent)).astype(np.int32)
+        out["node_off"], out["parent"], out["m"] = node_off, parent, m
+        out["y"] = rng.integers(0, cfg.logprob_vocab, size=len(m)).astype(np.int32)
+        out["row_ptr"], out["pos"] = positions_by_row(m, int(node_off[-1]))
+        out["dlogp"] = rng.standard_normal(len(m)).astype(np.float32)
+        return out
     if cfg.is_tree:
         node_off, parent = tree_layout(cfg.tree_levels)
         c = int(node_off[-1])
@@ -224,4 +233,21 @@ def random_logprob_case(seed: int, n_rows: int, vocab: int, n_pos: int, dtype: s
     dlogp = rng.standard_normal(n_pos).astype(np.float32)
     return {"z": z, "m": m.astype(np.int32), "y": y.astype(np.int32), "row_ptr": row_ptr,
             "pos": pos, "dlogp": dlogp}
+
+
+def tree_paths(node_off: np.ndarray, parent: np.ndarray) -> List[np.ndarray]:
+    """Compact rows of every root-to-leaf trajectory of a DFS-preorder tree, in
+    leaf order: position t of a trajectory reads compact row path[t]."""
+    n = len(parent)
+    has_child = np.zeros(n, dtype=bool)
+    has_child[np.asarray(parent[1:], dtype=np.int64)] = True
+    paths = []
+    for leaf in np.flatnonzero(~has_child):
+        chain = []
+        u = int(leaf)
+        while u >= 0:
+            chain.append(u)
+            u = int(parent[u])
+        paths.append(np.concatenate([np.arange(node_off[u], node_off[u + 1]) for u in reversed(chain)]))
+    return paths
 
