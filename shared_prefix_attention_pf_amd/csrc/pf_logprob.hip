@@ -207,9 +207,22 @@ __global__ __launch_bounds__(kLpThreads) void logprob_bwd_kernel(LpArgs a) {
   }
   const float g = block_sum(part, red);
   const float lse2 = a.lse[c] * kLog2e;
-  // dense part: dz = -g softmax(z)
+  // dense part: dz = -g softmax(z), four vectors in flight per thread
   const int nvec = a.vocab / 8;
-  for (int i = threadIdx.x; i < nvec; i += kLpThreads) {
+  constexpr int U = 4;
+  int i = threadIdx.x;
+  for (; i + (U - 1) * kLpThreads < nvec; i += U * kLpThreads) {
+    float x[U][8];
+#pragma unroll
+    for (int u = 0; u < U; ++u) load8<BF16>(row, 8 * (i + u * kLpThreads), x[u]);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) x[u][k] = -g * fexp2(fmaf(x[u][k], kLog2e, -lse2));
+      store8<BF16>(drow, 8 * (i + u * kLpThreads), x[u]);
+    }
+  }
+  for (; i < nvec; i += kLpThreads) {
     float x[8];
     load8<BF16>(row, 8 * i, x);
 #pragma unroll
