@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--stats-summary", nargs=2, metavar=("STATS_CSV", "OUT_MD"), default=None,
                     help="no GPU work: turn a rocprofv3 --kernel-trace --stats csv of this script "
                          "into a kernel-time summary")
+    ap.add_argument("--offload", action="store_true",
+                    help="flat configs: measure the dormant-prefix offload instead (Q_P, O_P, "
+                         "LSE_P to pinned host memory during Phase B, prefetched before Phase C)")
     ap.add_argument("--counter-summary", nargs="+", metavar="RUN_DIR_OR_OUT_MD", default=None,
                     help="no GPU work: turn rocprofv3 --pmc runs of SQ_ counters (their output "
                          "directories, then the output file) into a per-kernel counter summary")
@@ -663,6 +666,117 @@ def run_logprob(cfg, data, args):
     print(json.dumps(out), flush=True)
 
 
+def run_offload(cfg, data, args):
+    """Dormant prefix offload at a flat config: copy rates each way, how much of
+    the device-to-host copy Phase B hides, and Phase B's peak HBM with the
+    dormant tensors resident or offloaded.  Prints one JSON line."""
+    import torch
+
+    import shared_prefix_attention_pf_amd as pf
+    from shared_prefix_attention_pf_amd import group as G
+    from shared_prefix_attention_pf_amd.offload import DormantPrefix
+
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    pdt = pf.PF_BF16 if cfg.dtype == "bf16" else pf.PF_F32
+    desc = pf.AttnDesc(cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, pdt)
+    t = {k: torch.from_numpy(np.ascontiguousarray(data[k])).to(tdt).to(dev)
+         for k in ("q_p", "k_p", "v_p", "do_p", "q_s", "k_s", "v_s", "do_s")}
+    cu = data["cu_seqlens"]
+    p = cfg.prefix_len
+    rows = int(cu[-1])
+    ws = G.workspace(pf.PF_OP_SUFFIX_BWD, desc, p, rows, dev)
+    gk = torch.zeros(p, cfg.num_kv_heads, cfg.head_dim, device=dev)
+    gv = torch.zeros_like(gk)
+    cs = torch.cuda.current_stream()
+
+    def phase_b():
+        o_s, lse_s = G.suffix_fwd(desc, t["k_p"], t["v_p"], cu, t["q_s"], t["k_s"], t["v_s"],
+                                  ws=ws)
+        G.suffix_bwd(desc, t["k_p"], t["v_p"], cu, t["q_s"], t["k_s"], t["v_s"], o_s, lse_s,
+                     t["do_s"], gk, gv, ws=ws)
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    res = {}
+    reps = max(3, args.steps)
+    for _ in range(args.warmup):
+        phase_b()
+    # Phase A's outputs; Phase B reads none of Q_P, O_P, LSE_P
+    o_p, lse_p = G.prefix_fwd(desc, t["q_p"], t["k_p"], t["v_p"])
+    dormant = {"q_p": t.pop("q_p"), "o_p": o_p, "lse_p": lse_p}
+    del o_p, lse_p
+    nbytes = sum(x.numel() * x.element_size() for x in dormant.values())
+
+    def steady_phase_b(key):
+        # peak HBM over `reps` Phase-B steps, from a synchronized start
+        torch.cuda.synchronize()
+        torch.empty(1, device=dev)  # lets the allocator retire stream-deferred frees
+        torch.cuda.reset_peak_memory_stats()
+        a, b = ev(), ev()
+        a.record(cs)
+        for _ in range(reps):
+            phase_b()
+        b.record(cs)
+        torch.cuda.synchronize()
+        res[f"phase_b_ms_{key}"] = a.elapsed_time(b) / reps
+        res[f"phase_b_peak_mib_{key}"] = torch.cuda.max_memory_allocated() / 2**20
+
+    # dormant tensors resident through Phase B
+    steady_phase_b("resident")
+    holder = DormantPrefix(dormant)
+    del dormant
+    # copy rates, each alone
+    torch.cuda.synchronize()
+    a, b = ev(), ev()
+    a.record(holder.copy_stream)
+    holder.offload()
+    b.record(holder.copy_stream)
+    torch.cuda.synchronize()
+    res["d2h_ms"] = a.elapsed_time(b)
+    a, b = ev(), ev()
+    a.record(holder.copy_stream)
+    holder.prefetch()
+    b.record(holder.copy_stream)
+    torch.cuda.synchronize()
+    res["h2d_ms"] = a.elapsed_time(b)
+    holder.get()
+    # one Phase B with the offload running beside it on the copy stream
+    torch.cuda.synchronize()
+    a, b, c0, c1 = ev(), ev(), ev(), ev()
+    c0.record(cs)
+    holder.offload(cs)
+    a.record(cs)
+    phase_b()
+    b.record(cs)
+    c1.record(holder.copy_stream)
+    torch.cuda.synchronize()
+    res["phase_b_ms_beside_d2h"] = a.elapsed_time(b)
+    res["d2h_done_ms_after_phase_b_start"] = c0.elapsed_time(c1)
+    # dormant tensors in host memory through Phase B
+    steady_phase_b("offloaded")
+    # Phase C's inputs come back
+    holder.prefetch()
+    holder.get()
+    torch.cuda.synchronize()
+    out = {
+        "metric": "dormant prefix offload across Phase B (host link)",
+        "config": {"workload": f"config {cfg.cid}: {cfg.name}"},
+        "dormant_bytes": nbytes,
+        "d2h_gbs": round(nbytes / (res["d2h_ms"] * 1e-3) / 1e9, 2),
+        "h2d_gbs": round(nbytes / (res["h2d_ms"] * 1e-3) / 1e9, 2),
+        "phase_b_time_ratio_beside_d2h": round(res["phase_b_ms_beside_d2h"] /
+                                               res["phase_b_ms_resident"], 4),
+        "d2h_hidden_by_phase_b": res["d2h_done_ms_after_phase_b_start"] <=
+                                 res["phase_b_ms_beside_d2h"],
+        "phase_b_peak_hbm_saved_mib": round(res["phase_b_peak_mib_resident"] -
+                                            res["phase_b_peak_mib_offloaded"], 2),
+        **{k: round(v, 4) for k, v in res.items()},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -688,6 +802,12 @@ def main():
     if cfg.is_logprob:
         print("[bench] running GPU steps", flush=True)
         run_logprob(cfg, data, args)
+        return
+    if args.offload:
+        if cfg.is_tree or cfg.is_windows:
+            raise SystemExit("--offload measures a flat group (configs 1-4)")
+        print("[bench] measuring the dormant-prefix offload", flush=True)
+        run_offload(cfg, data, args)
         return
     print("[bench] running GPU steps", flush=True)
     gres = run_gpu(cfg, data, args.steps, args.warmup, args.copy_probe_mib)
