@@ -125,8 +125,14 @@ class KernelTimer:
             t["launches"] += 1
             t["total_ms"] += ms
             t["phases"][phase] = t["phases"].get(phase, 0) + 1
+            t.setdefault("phase_total_ms", {})
+            t["phase_total_ms"][phase] = t["phase_total_ms"].get(phase, 0.0) + ms
         for t in out.values():
             t["avg_ms"] = t["total_ms"] / t["launches"]
+            # average launch time within each phase the kernel runs in
+            t["phase_avg_ms"] = {p: round(t["phase_total_ms"].pop(p) / n, 4)
+                                 for p, n in t["phases"].items()}
+            del t["phase_total_ms"]
         return out
 
 
