@@ -3,15 +3,22 @@
 The GPU runs each workload exactly as the benchmark times it: the 32/8-head
 group at P = 4096 with all 8 suffixes in one Phase-B call (config 2), the
 64-suffix group at P = 8192 in 8 microbatch calls (config 4), the RAG-shaped
-varlen group at P = 16384 in 4 calls (config 3) and the 12288-row rollout tree
-(config 5).  The fp64 oracle then recomputes whole KV-head groups (every
+varlen group at P = 16384 in 4 calls (config 3), the 12288-row rollout tree
+(config 5), four irregular tree windows over a 4096-row prefix with the
+producer backward (config 6), and the compact log-probabilities of the
+config-5 tree over a 151936-token vocabulary (config 7).  The fp64 oracle then recomputes whole KV-head groups (every
 query head that reads the chosen KV head, every row) and each output slice is
 compared normwise against it (2e-2, the bf16 bar).  Heads are independent, so
 a KV-head group is an exact sub-problem of the full call.
 
-Invariants checked at full size, where the oracle cannot cover every head:
-the prefix-side gradient of a call is the same whichever microbatch split
-produced it (up to fp32 summation order), and the outputs are finite.
+Invariants checked at full size, where the oracle cannot cover every head
+or row:
+- the prefix-side gradient of a call is the same whichever microbatch split
+  produced it (up to fp32 summation order);
+- the outputs are finite;
+- every compact row's log-sum-exp lies in [max z, max z + ln V];
+- every log-probability is at most 0;
+- every row of dz sums to zero.
 """
 import math
 
@@ -204,3 +211,115 @@ def test_config5_tree_full_size():
     check("dQ", dq[:, hs], ref["dq"], tol)
     check("dK", dk[:, g:g + 1], ref["dk"], tol)
     check("dV", dv[:, g:g + 1], ref["dv"], tol)
+
+
+def test_config6_tree_windows_full_size():
+    """Phase A, four irregular tree windows over the 4096-row prefix (each a
+    forward and a backward call adding into one gK/gV), then Phase C with that
+    gK/gV injected: the benchmark's step at config 6.  The oracle recomputes
+    one KV-head group through every window and both prefix phases."""
+    cfg = get_config(6)
+    print(f"\ngenerating config {cfg.cid}", flush=True)
+    data = generate(cfg)
+    desc = _desc(cfg)
+    p = cfg.prefix_len
+    q_p, k_p, v_p, do_p = (dev(data[k], cfg.dtype) for k in ("q_p", "k_p", "v_p", "do_p"))
+    o_p, lse_p = G.prefix_fwd(desc, q_p, k_p, v_p)
+    gk = torch.zeros(p, cfg.num_kv_heads, cfg.head_dim, device="cuda")
+    gv = torch.zeros_like(gk)
+    outs = []
+    for wd in data["windows"]:
+        q, k, v, do = (dev(wd[n], cfg.dtype) for n in ("q", "k", "v", "do"))
+        o, lse = G.tree_suffix_fwd(desc, k_p, v_p, wd["node_off"], wd["parent"], q, k, v)
+        dq, dk, dv = G.tree_suffix_bwd(desc, k_p, v_p, wd["node_off"], wd["parent"], q, k, v, o,
+                                       lse, do, gk, gv)
+        outs.append((o, lse, dq, dk, dv))
+    dq_p, dk_p, dv_p = G.prefix_bwd(desc, q_p, k_p, v_p, o_p, lse_p, do_p, gk, gv)
+    torch.cuda.synchronize()
+    outs = [tuple(host(x) for x in w) for w in outs]
+    o_p, lse_p, dq_p, dk_p, dv_p, gk, gv = (host(x) for x in (o_p, lse_p, dq_p, dk_p, dv_p, gk,
+                                                                gv))
+    for x in (o_p, dq_p, dk_p, dv_p, gk, gv):
+        assert np.all(np.isfinite(x))
+    g = 5
+    hs = _heads_of(cfg, g)
+    scale = 1.0 / math.sqrt(cfg.head_dim)
+    hmap = np.zeros(cfg.group_size, dtype=np.int64)
+    tol = TOL[cfg.dtype]
+    kp, vp = data["k_p"][:, g:g + 1], data["v_p"][:, g:g + 1]
+    ref_gk = np.zeros((p, 1, cfg.head_dim))
+    ref_gv = np.zeros_like(ref_gk)
+    for w, (wd, (o, lse, dq, dk, dv)) in enumerate(zip(data["windows"], outs)):
+        assert np.all(np.isfinite(dq)) and np.all(np.isfinite(dk))
+        print(f"  oracle window {w} ({int(wd['node_off'][-1])} rows), KV head {g}", flush=True)
+        ref = oracle.tree_window_attention(kp, vp, wd["q"][:, hs], wd["k"][:, g:g + 1],
+                                           wd["v"][:, g:g + 1], wd["do"][:, hs], wd["node_off"],
+                                           wd["parent"], scale, hmap)
+        check(f"O[w{w}]", o[:, hs], ref["o"], tol)
+        check(f"LSE[w{w}]", lse[hs], ref["lse"], tol)
+        check(f"dQ[w{w}]", dq[:, hs], ref["dq"], tol)
+        check(f"dK[w{w}]", dk[:, g:g + 1], ref["dk"], tol)
+        check(f"dV[w{w}]", dv[:, g:g + 1], ref["dv"], tol)
+        ref_gk += ref["gk"]
+        ref_gv += ref["gv"]
+    check("gK (4 windows)", gk[:, g:g + 1], ref_gk, tol)
+    check("gV (4 windows)", gv[:, g:g + 1], ref_gv, tol)
+    print(f"  oracle Phase A/C, KV head {g}", flush=True)
+    ro, rl = oracle.prefix_forward(data["q_p"][:, hs], kp, vp, scale, hmap)
+    check("O_P", o_p[:, hs], ro, tol)
+    check("LSE_P", lse_p[hs], rl, tol)
+    rdq, rdk, rdv = oracle.prefix_backward_inject(data["q_p"][:, hs], kp, vp, data["do_p"][:, hs],
+                                                  ref_gk, ref_gv, scale, hmap)
+    check("dQ_P", dq_p[:, hs], rdq, tol)
+    check("dK_P", dk_p[:, g:g + 1], rdk, tol)
+    check("dV_P", dv_p[:, g:g + 1], rdv, tol)
+
+
+def test_config7_compact_logprob_full_size():
+    """Compact log-probabilities of the config-5 tree's 12288 rows over a
+    151936-token vocabulary, logits drawn on the device from the seed as the
+    benchmark draws them.  The oracle recomputes sampled rows (the root, rows
+    of every tree level, the last row); properties hold for every row."""
+    cfg = get_config(7)
+    print(f"\ngenerating config {cfg.cid}", flush=True)
+    data = generate(cfg)
+    c, v = int(data["node_off"][-1]), cfg.logprob_vocab
+    s_pos = len(data["m"])
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(cfg.seed)
+    z = (torch.randn(c, v, generator=gen, device="cuda") * 3.0).to(torch.bfloat16)
+    ints = {k: torch.from_numpy(data[k]).cuda() for k in ("row_ptr", "pos", "y")}
+    lse = torch.empty(c, device="cuda")
+    logp = torch.full((s_pos,), 7.0, device="cuda")
+    dz = torch.empty_like(z)
+    pf.pf_compact_logprob_fwd(z, ints["row_ptr"], ints["pos"], ints["y"], lse, logp)
+    pf.pf_compact_logprob_bwd(z, lse, ints["row_ptr"], ints["pos"], ints["y"],
+                              torch.from_numpy(data["dlogp"]).cuda(), dz)
+    torch.cuda.synchronize()
+    # properties over every row and position
+    zmax = z.float().amax(dim=1)
+    assert torch.all(lse >= zmax - 1e-3).item()
+    assert torch.all(lse <= zmax + math.log(v) + 1e-3).item()
+    assert torch.all(logp <= 1e-3).item(), "a log-probability above 0 (or a position not written)"
+    dzf = dz.float()
+    row_sum = dzf.sum(dim=1).abs()
+    row_abs = dzf.abs().sum(dim=1)
+    worst = (row_sum / row_abs.clamp_min(1e-30)).max().item()
+    print(f"  max |sum dz| / sum |dz| over rows: {worst:.2e}", flush=True)
+    assert worst < 1e-2
+    # sampled rows against the oracle
+    node_off = data["node_off"]
+    rows = sorted({0, int(node_off[1]) - 1, int(node_off[1]), int(node_off[5]) - 1,
+                   int(node_off[5]) + 7, c // 2, c - 1})
+    rp, ps = data["row_ptr"], data["pos"]
+    tol = TOL["bf16"]
+    for r in rows:
+        zr = z[r:r + 1].float().cpu().double().numpy()
+        sub_ptr = np.asarray([0, rp[r + 1] - rp[r]], dtype=np.int32)
+        sub_pos = ps[rp[r]:rp[r + 1]]
+        ref = oracle.compact_logprob(zr, sub_ptr, sub_pos, data["y"], data["dlogp"])
+        print(f"  oracle row {r} ({len(sub_pos)} positions)", flush=True)
+        check(f"lse[{r}]", lse[r:r + 1].cpu().double().numpy(), ref["lse"], tol)
+        check(f"logp[row {r}]", logp[torch.from_numpy(sub_pos.astype(np.int64)).cuda()]
+              .cpu().double().numpy(), ref["logp"][sub_pos], tol)
+        check(f"dz[{r}]", dz[r:r + 1].float().cpu().double().numpy(), ref["dz"], tol)
