@@ -96,26 +96,57 @@ def window_pairs(p, node_off, parent):
 # ---------------------------------------------------------------- GPU side
 
 class KernelTimer:
-    """Launch-hook consumer: HIP events around every kernel, on its own stream."""
+    """Launch-hook consumer: HIP events around every kernel, on its own stream.
 
-    def __init__(self, torch):
+    Within one phase the step enqueues nothing but library calls, so the event
+    that ends one kernel also starts the next one on the same stream: one event
+    per launch boundary instead of two.  A kernel's time then includes the
+    launch gap before it, which errs on the long side.  Setting `phase` starts
+    fresh events, since the step records its own phase events in between.
+    `reserve` events are created (and recorded once) up front, so the timed
+    region only re-records existing events."""
+
+    def __init__(self, torch, reserve=0):
         self.torch = torch
         self.open = {}
         self.spans = []          # (label, phase, start_event, end_event)
         self.streams = {}
-        self.phase = None        # set by the step before each phase's calls
+        self.last_end = {}       # stream -> end event of the previous kernel, this phase
+        self._phase = None
+        self.pool = [torch.cuda.Event(enable_timing=True) for _ in range(reserve)]
+        for e in self.pool:
+            e.record()
+        if reserve:
+            torch.cuda.synchronize()
+
+    @property
+    def phase(self):
+        return self._phase
+
+    @phase.setter
+    def phase(self, name):
+        # set by the step before each phase's calls
+        self._phase = name
+        self.last_end = {}
+
+    def _record(self, s):
+        ev = self.pool.pop() if self.pool else self.torch.cuda.Event(enable_timing=True)
+        ev.record(s)
+        return ev
 
     def __call__(self, label, stream, end):
         torch = self.torch
         if stream not in self.streams:
             self.streams[stream] = torch.cuda.ExternalStream(stream) if stream else \
                 torch.cuda.default_stream()
-        ev = torch.cuda.Event(enable_timing=True)
-        ev.record(self.streams[stream])
+        s = self.streams[stream]
         if end == 0:
-            self.open[(label, stream)] = ev
+            ev = self.last_end.pop(stream, None)
+            self.open[(label, stream)] = ev if ev is not None else self._record(s)
         else:
+            ev = self._record(s)
             self.spans.append((label, self.phase, self.open.pop((label, stream)), ev))
+            self.last_end[stream] = ev
 
     def summary(self):
         out = {}
@@ -151,7 +182,7 @@ def run_gpu(cfg, data, steps, warmup, copy_mib=0):
 
     stream = torch.cuda.current_stream()
     res = {}
-    timer = KernelTimer(torch)
+    timer = KernelTimer(torch, reserve=64 * (steps + 1))
     if cfg.is_windows:
         p = cfg.prefix_len
         q_p, k_p, v_p, do_p = (to_dev(data[n]) for n in ("q_p", "k_p", "v_p", "do_p"))
@@ -599,7 +630,7 @@ def run_logprob(cfg, data, args):
     logp = torch.empty(s_pos, device=dev)
     dz = torch.empty_like(z)
     stream = torch.cuda.current_stream()
-    timer = KernelTimer(torch)
+    timer = KernelTimer(torch, reserve=4 * (args.steps + 1))
 
     def step():
         pf.pf_compact_logprob_fwd(z, ints["row_ptr"], ints["pos"], ints["y"], lse, logp)
