@@ -96,28 +96,57 @@ def window_pairs(p, node_off, parent):
 # ---------------------------------------------------------------- GPU side
 
 class KernelTimer:
-    """Kernel times from HIP events that the library passes to
-    hipExtLaunchKernel (pf_set_launch_events_hook): the runtime marks each
-    event pair at the kernel's own start and end, so timing adds no event
-    records between kernels.  The events are created (and recorded once)
-    before the timed region; `reserve` is the number of launches that can be
-    timed."""
+    """Launch-hook consumer: HIP events around every kernel, on its own stream.
 
-    def __init__(self, torch, reserve):
+    Within one phase the step enqueues nothing but library calls, so the event
+    that ends one kernel also starts the next one on the same stream: one event
+    per launch boundary instead of two.  A kernel's time then includes the
+    launch gap before it, which errs on the long side.  Setting `phase` starts
+    fresh events, since the step records its own phase events in between.
+    `reserve` events are created (and recorded once) up front, so the timed
+    region only re-records existing events."""
+
+    def __init__(self, torch, reserve=0):
         self.torch = torch
+        self.open = {}
         self.spans = []          # (label, phase, start_event, end_event)
-        self.phase = None        # set by the step before each phase's calls
-        self.pool = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reserve)]
+        self.streams = {}
+        self.last_end = {}       # stream -> end event of the previous kernel, this phase
+        self._phase = None
+        self.pool = [torch.cuda.Event(enable_timing=True) for _ in range(reserve)]
         for e in self.pool:
             e.record()
-        torch.cuda.synchronize()
+        if reserve:
+            torch.cuda.synchronize()
 
-    def events(self, label, stream):
-        if len(self.pool) < 2:
-            raise RuntimeError("kernel timer: more launches than reserved events")
-        a, b = self.pool.pop(), self.pool.pop()
-        self.spans.append((label, self.phase, a, b))
-        return a.cuda_event, b.cuda_event
+    @property
+    def phase(self):
+        return self._phase
+
+    @phase.setter
+    def phase(self, name):
+        # set by the step before each phase's calls
+        self._phase = name
+        self.last_end = {}
+
+    def _record(self, s):
+        ev = self.pool.pop() if self.pool else self.torch.cuda.Event(enable_timing=True)
+        ev.record(s)
+        return ev
+
+    def __call__(self, label, stream, end):
+        torch = self.torch
+        if stream not in self.streams:
+            self.streams[stream] = torch.cuda.ExternalStream(stream) if stream else \
+                torch.cuda.default_stream()
+        s = self.streams[stream]
+        if end == 0:
+            ev = self.last_end.pop(stream, None)
+            self.open[(label, stream)] = ev if ev is not None else self._record(s)
+        else:
+            ev = self._record(s)
+            self.spans.append((label, self.phase, self.open.pop((label, stream)), ev))
+            self.last_end[stream] = ev
 
     def summary(self):
         out = {}
@@ -283,10 +312,10 @@ def run_gpu(cfg, data, steps, warmup, copy_mib=0):
         step()
     torch.cuda.synchronize()
 
-    # timed region: K steps, per-phase events inside each step; every kernel
-    # is launched with a start/stop event pair from the timer's reserve
+    # timed region: K steps, per-phase events inside each step; the launch hook
+    # records HIP events around every kernel on the stream it is launched on
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
-    pf.pf_set_launch_events_hook(timer.events)
+    pf.pf_set_launch_hook(timer)
     try:
         t0 = time.perf_counter()
         for i in range(steps):
@@ -294,7 +323,7 @@ def run_gpu(cfg, data, steps, warmup, copy_mib=0):
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
     finally:
-        pf.pf_set_launch_events_hook(None)
+        pf.pf_set_launch_hook(None)
     phase_ms = {}
     if cfg.is_tree:
         phase_ms["tree"] = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
@@ -601,7 +630,7 @@ def run_logprob(cfg, data, args):
     logp = torch.empty(s_pos, device=dev)
     dz = torch.empty_like(z)
     stream = torch.cuda.current_stream()
-    timer = KernelTimer(torch, reserve=2 * (args.steps + 1))
+    timer = KernelTimer(torch, reserve=4 * (args.steps + 1))
 
     def step():
         pf.pf_compact_logprob_fwd(z, ints["row_ptr"], ints["pos"], ints["y"], lse, logp)
@@ -612,7 +641,7 @@ def run_logprob(cfg, data, args):
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     timer.phase = "logprob"
-    pf.pf_set_launch_events_hook(timer.events)
+    pf.pf_set_launch_hook(timer)
     try:
         t0 = time.perf_counter()
         e0.record(stream)
@@ -622,7 +651,7 @@ def run_logprob(cfg, data, args):
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
     finally:
-        pf.pf_set_launch_events_hook(None)
+        pf.pf_set_launch_hook(None)
     ms = e0.elapsed_time(e1) / args.steps
     eb = 2
     # algorithmic bytes: the logits read once forward, read and dz written once

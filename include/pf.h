@@ -290,21 +290,6 @@ pf_status pf_tree_subtree_end(int32_t n_nodes, const int32_t* node_off, const in
 typedef void (*pf_launch_hook)(const char* kernel, void* stream, int32_t end, void* user);
 void pf_set_launch_hook(pf_launch_hook hook, void* user);
 
-/* Profiling aid that adds no work between kernels.  When this hook is set,
- * the library calls it on the host right before enqueuing each kernel, with
- * the kernel label and its stream.  The hook may store two HIP events
- * (hipEvent_t, created with timing enabled and owned by the caller) in
- * *start_event and *stop_event and return 1.  The kernel is then launched
- * with hipExtLaunchKernel, so the runtime marks those events at the kernel's
- * own start and end, with no separate event records between kernels.
- * Returning 0 (or leaving either event NULL) launches the kernel normally.
- * An events hook takes precedence over pf_set_launch_hook for that launch.
- * NULL removes it.  It is process-wide; set it while no other thread
- * launches. */
-typedef int32_t (*pf_launch_events_hook)(const char* kernel, void* stream, void** start_event,
-                                         void** stop_event, void* user);
-void pf_set_launch_events_hook(pf_launch_events_hook hook, void* user);
-
 const char* pf_status_string(pf_status status);
 const char* pf_last_error(void);
 int32_t pf_abi_version(void);

@@ -28,7 +28,6 @@ EXPORTED = (
     "pf_tree_suffix_attn_bwd_accum", "pf_compact_logprob_fwd", "pf_compact_logprob_bwd",
     "pf_tree_subtree_end",
     "pf_status_string", "pf_last_error", "pf_abi_version", "pf_set_launch_hook",
-    "pf_set_launch_events_hook",
 )
 
 
@@ -56,9 +55,6 @@ class _Tensor(ctypes.Structure):
 # void (*)(const char* kernel, void* stream, int32_t end, void* user)
 LAUNCH_HOOK = ctypes.CFUNCTYPE(None, ctypes.c_char_p, ctypes.c_void_p, ctypes.c_int32,
                                ctypes.c_void_p)
-LAUNCH_EVENTS_HOOK = ctypes.CFUNCTYPE(ctypes.c_int32, ctypes.c_char_p, ctypes.c_void_p,
-                                      ctypes.POINTER(ctypes.c_void_p),
-                                      ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p)
 
 
 def _load():
@@ -97,7 +93,6 @@ def _load():
         "pf_last_error": (ctypes.c_char_p, []),
         "pf_abi_version": (i32, []),
         "pf_set_launch_hook": (None, [LAUNCH_HOOK, P]),
-        "pf_set_launch_events_hook": (None, [LAUNCH_EVENTS_HOOK, P]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -177,31 +172,6 @@ def pf_set_launch_hook(fn) -> None:
         return
     _hook_keepalive = LAUNCH_HOOK(lambda k, s, e, u: fn(k.decode(), s or 0, e))
     _lib.pf_set_launch_hook(_hook_keepalive, None)
-
-
-_events_keepalive = None
-
-
-def pf_set_launch_events_hook(fn) -> None:
-    """Install fn(kernel: str, stream: int) -> (start, stop) or None before every
-    kernel launch, or None to remove it.  start and stop are raw hipEvent_t
-    handles (ints) of events the caller created with timing enabled; the kernel
-    is launched so that they mark its own start and end."""
-    global _events_keepalive
-    if fn is None:
-        _events_keepalive = None
-        _lib.pf_set_launch_events_hook(LAUNCH_EVENTS_HOOK(), None)
-        return
-
-    def call(k, s, start, stop, u):
-        ev = fn(k.decode(), s or 0)
-        if not ev:
-            return 0
-        start[0], stop[0] = ev
-        return 1
-
-    _events_keepalive = LAUNCH_EVENTS_HOOK(call)
-    _lib.pf_set_launch_events_hook(_events_keepalive, None)
 
 
 def pf_abi_version() -> int:

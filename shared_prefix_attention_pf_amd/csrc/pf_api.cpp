@@ -392,24 +392,11 @@ namespace pf {
 namespace {
 pf_launch_hook g_hook = nullptr;
 void* g_hook_user = nullptr;
-pf_launch_events_hook g_ev_hook = nullptr;
-void* g_ev_user = nullptr;
 }  // namespace
 
 void launch_hook(const char* kernel, hipStream_t stream, int end) {
   const pf_launch_hook h = g_hook;
   if (h) h(kernel, (void*)stream, end, g_hook_user);
-}
-
-int launch_events(const char* kernel, hipStream_t stream, hipEvent_t* start, hipEvent_t* stop) {
-  const pf_launch_events_hook h = g_ev_hook;
-  if (!h) return 0;
-  void* e0 = nullptr;
-  void* e1 = nullptr;
-  if (h(kernel, (void*)stream, &e0, &e1, g_ev_user) == 0 || !e0 || !e1) return 0;
-  *start = (hipEvent_t)e0;
-  *stop = (hipEvent_t)e1;
-  return 1;
 }
 
 // External key blocks are split into query chunks until there is about one
@@ -458,11 +445,6 @@ int32_t pf_abi_version(void) { return PF_ABI_VERSION; }
 void pf_set_launch_hook(pf_launch_hook hook, void* user) {
   pf::g_hook_user = user;
   pf::g_hook = hook;
-}
-
-void pf_set_launch_events_hook(pf_launch_events_hook hook, void* user) {
-  pf::g_ev_user = user;
-  pf::g_ev_hook = hook;
 }
 
 const char* pf_last_error(void) { return g_last_error.c_str(); }

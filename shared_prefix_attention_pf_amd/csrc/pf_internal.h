@@ -19,7 +19,6 @@
 // segment table by the prep kernel.
 #pragma once
 
-#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -101,20 +100,11 @@ struct AttnArgs {
 // Calls the caller's launch hook (if any) around one kernel launch.
 void launch_hook(const char* kernel, hipStream_t stream, int end);
 
-// Events from pf_set_launch_events_hook for the next launch (1), or none (0).
-int launch_events(const char* kernel, hipStream_t stream, hipEvent_t* start, hipEvent_t* stop);
-
 #define PF_LAUNCH(label, kernel, grid, block, stream, ...)                    \
   do {                                                                        \
-    hipEvent_t pf_start_ = nullptr, pf_stop_ = nullptr;                       \
-    if (::pf::launch_events(label, stream, &pf_start_, &pf_stop_)) {          \
-      hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, pf_start_,        \
-                            pf_stop_, 0, __VA_ARGS__);                        \
-    } else {                                                                  \
-      ::pf::launch_hook(label, stream, 0);                                    \
-      hipLaunchKernelGGL(kernel, grid, block, 0, stream, __VA_ARGS__);        \
-      ::pf::launch_hook(label, stream, 1);                                    \
-    }                                                                         \
+    ::pf::launch_hook(label, stream, 0);                                      \
+    hipLaunchKernelGGL(kernel, grid, block, 0, stream, __VA_ARGS__);          \
+    ::pf::launch_hook(label, stream, 1);                                      \
   } while (0)
 
 // Launchers (return hipSuccess or the launch error).
