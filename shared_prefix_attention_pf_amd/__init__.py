@@ -21,6 +21,7 @@ PF_F32, PF_BF16 = 0, 1
 (PF_OP_PREFIX_FWD, PF_OP_SUFFIX_FWD, PF_OP_SUFFIX_BWD, PF_OP_PREFIX_BWD, PF_OP_TREE_FWD,
  PF_OP_TREE_BWD, PF_OP_TREE_SUFFIX_FWD, PF_OP_TREE_SUFFIX_BWD) = range(8)
 PF_MAX_SEGMENTS = 256
+PF_MAX_HEADS = 256
 
 EXPORTED = (
     "pf_workspace_size", "pf_workspace_size_min", "pf_prefix_fwd", "pf_suffix_attn_fwd", "pf_suffix_attn_bwd_accum",

@@ -62,7 +62,16 @@ def _suffix_fwd(desc_keep, cu, ws=FAKE, ws_bytes=1 << 30, q=None, kp=None, lse=F
                                       ctypes.c_void_p(0))
 
 
+def test_binding_constants_match_the_header():
+    src = open(os.path.join(ROOT, "include", "pf.h")).read()
+    defs = dict(re.findall(r"#define\s+(PF_MAX_[A-Z]+)\s+(\d+)", src))
+    assert int(defs["PF_MAX_SEGMENTS"]) == pf.PF_MAX_SEGMENTS
+    assert int(defs["PF_MAX_HEADS"]) == pf.PF_MAX_HEADS
+
+
 def test_rejects_bad_head_config():
+    h = pf.PF_MAX_HEADS + 1
+    assert _suffix_fwd(_desc(hq=h, hkv=h), [0, 4]) == pf.PF_ERR_UNSUPPORTED
     assert _suffix_fwd(_desc(hq=30, hkv=8), [0, 4]) == pf.PF_ERR_INVALID_ARG
     assert _suffix_fwd(_desc(hq=0, hkv=8), [0, 4]) == pf.PF_ERR_INVALID_ARG
     assert _suffix_fwd(_desc(d=96), [0, 4]) == pf.PF_ERR_UNSUPPORTED

@@ -44,6 +44,12 @@ SUFFIX_CASES = [
 
 @pytest.mark.parametrize("case", SUFFIX_CASES, ids=lambda c: f"{c[3]}-h{c[0]}x{c[1]}-P{c[4]}-{c[5]}")
 def test_suffix_phase_b(case):
+    _suffix_case(case)
+
+
+def _suffix_case(case):
+    """Phase B (forward, backward with gK/gV accumulation) of one case against
+    the oracle."""
     hq, hkv, d, dtype, p, lens, qmap = case
     print(f"\ncase {case}", flush=True)
     g = random_small_group(17, hq, hkv, d, p, lens, dtype)
@@ -124,6 +130,12 @@ PREFIX_CASES = [
 
 @pytest.mark.parametrize("case", PREFIX_CASES, ids=lambda c: f"{c[3]}-h{c[0]}x{c[1]}-P{c[4]}-do{c[5]}")
 def test_prefix_phases_a_and_c(case):
+    _prefix_case(case)
+
+
+def _prefix_case(case):
+    """Phase A and Phase C (with injected accumulators) of one case against the
+    oracle, with dK/dV in the input dtype and in fp32."""
     hq, hkv, d, dtype, p, with_do = case
     print(f"\ncase {case}", flush=True)
     g = random_small_group(23, hq, hkv, d, p, [1], dtype)
@@ -162,9 +174,32 @@ def test_prefix_phases_a_and_c(case):
 @pytest.mark.parametrize("seed,hq,hkv,dtype", [(0, 8, 2, "bf16"), (1, 4, 4, "bf16"),
                                                (2, 2, 1, "f32"), (3, 8, 2, "bf16")])
 def test_tree(seed, hq, hkv, dtype):
+    _tree_case(seed, hq, hkv, dtype, 9, 90)
+
+
+def test_maximum_sizes():
+    """The limits the boundary accepts: PF_MAX_SEGMENTS suffixes in one call
+    (ragged, a quarter of them empty) and a tree of PF_MAX_SEGMENTS nodes,
+    PF_MAX_HEADS query heads as 128 per KV head and as one per KV head."""
+    rng = np.random.Generator(np.random.PCG64(77))
+    lens = rng.integers(0, 10, size=pf.PF_MAX_SEGMENTS)
+    lens[rng.permutation(pf.PF_MAX_SEGMENTS)[:pf.PF_MAX_SEGMENTS // 4]] = 0
+    _suffix_case((4, 2, 128, "bf16", 100, lens.tolist(), None))
+    _tree_case(11, 4, 2, "bf16", pf.PF_MAX_SEGMENTS, 6)
+    for hkv in (2, pf.PF_MAX_HEADS):
+        _suffix_case((pf.PF_MAX_HEADS, hkv, 128, "bf16", 40, [30, 0, 17], None))
+        _prefix_case((pf.PF_MAX_HEADS, hkv, 128, "bf16", 45, True))
+
+
+def _tree_case(seed, hq, hkv, dtype, n_nodes, max_len):
+    """Tree forward and backward of a random tree against the oracle."""
     d = 128 if dtype == "bf16" else 64
-    node_off, parent = random_tree(seed, 9, max_len=90, min_len=0)
-    print(f"\ntree seed {seed}: node_off {node_off.tolist()} parent {parent.tolist()}", flush=True)
+    node_off, parent = random_tree(seed, n_nodes, max_len=max_len, min_len=0)
+    if n_nodes <= 16:
+        print(f"\ntree seed {seed}: node_off {node_off.tolist()} parent {parent.tolist()}",
+              flush=True)
+    else:
+        print(f"\ntree seed {seed}: {n_nodes} nodes, {int(node_off[-1])} rows", flush=True)
     g = random_tree_group(seed, node_off, hq, hkv, d, dtype)
     desc = _desc(hq, hkv, d, dtype)
     t = {k: dev(g[k], dtype) for k in ("q", "k", "v", "do")}
