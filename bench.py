@@ -349,7 +349,8 @@ KERNEL_SYMBOL = {"pf_fwd_bf16": "fwd_kernel", "pf_bwd_dq_bf16": "bwd_dq_kernel",
                  "pf_bwd_dq_ds_bf16": "bwd_dq_ds_kernel", "pf_bwd_dkv_bf16": "bwd_dkv_kernel",
                  "pf_fwd_f32": "fwd_f32_kernel", "pf_bwd_dq_f32": "dq_f32_kernel",
                  "pf_bwd_dkv_f32": "dkv_f32_kernel", "pf_prep_dsum": "prep_dsum_kernel",
-                 "pf_partials": "partial_sums_kernel"}
+                 "pf_partials": "partial_sums_kernel", "pf_logprob_fwd": "logprob_fwd_kernel",
+                 "pf_logprob_bwd": "logprob_bwd_kernel"}
 COPY_SYMBOL = "neg_kernel"       # the elementwise copy run by --copy-probe-mib
 
 
@@ -402,8 +403,13 @@ def _counter_means(run_dir, counter):
     return {k: (sum(v.values()) / len(v), len(v)) for k, v in per.items()}
 
 
-def _pick(means, sub):
-    hits = [(k, v) for k, v in means.items() if sub in k]
+def _pick(means, sub, whole=False):
+    """Mean counter value per dispatch over the kernels whose name contains
+    `sub` (as a whole identifier when `whole`: fwd_kernel must not match
+    logprob_fwd_kernel)."""
+    import re
+    pat = re.compile(r"(?<![A-Za-z0-9_])" + re.escape(sub) + r"(?![A-Za-z0-9_])")
+    hits = [(k, v) for k, v in means.items() if (pat.search(k) if whole else sub in k)]
     if not hits:
         return None
     tot = sum(v[0] * v[1] for _, v in hits)
@@ -431,7 +437,7 @@ def traffic_summary(fetch_dir, write_dir, out_md, cid, copy_mib, command):
              "| label | kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | "
              "read bytes (scaled) | write bytes (scaled) |", "|---|---|---|---|---|---|---|"]
     for label, sym in KERNEL_SYMBOL.items():
-        fk, wk = _pick(fetch, sym), _pick(write, sym)
+        fk, wk = _pick(fetch, sym, whole=True), _pick(write, sym, whole=True)
         if fk is None or wk is None:
             continue
         rb, wb = fk[0] * 1024 * f_fac, wk[0] * 1024 * w_fac
@@ -653,6 +659,8 @@ def run_logprob(cfg, data, args):
     finally:
         pf.pf_set_launch_hook(None)
     ms = e0.elapsed_time(e1) / args.steps
+    if args.copy_probe_mib > 0:
+        copy_probe(torch, args.copy_probe_mib)
     eb = 2
     # algorithmic bytes: the logits read once forward, read and dz written once
     # backward, plus the per-position index, target and gradient arrays
@@ -664,6 +672,7 @@ def run_logprob(cfg, data, args):
     dom = max(kern, key=lambda k: kern[k]["total_ms"])
     dom_bytes = bwd_bytes if dom == "pf_logprob_bwd" else fwd_bytes
     achieved = dom_bytes / (kern[dom]["avg_ms"] * 1e-3) / 1e9
+    traffic, traffic_src = load_traffic(cfg.cid, dom)
     cpu = None
     if args.cpu_seconds > 0:
         print("[bench] timing the CPU oracle", flush=True)
@@ -696,7 +705,8 @@ def run_logprob(cfg, data, args):
                         for kk, vv in kv.items()} for k, kv in kern.items()},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": None, "algorithmic_bytes_per_launch": dom_bytes,
+                     "traffic": traffic, "traffic_unit": "bytes per launch",
+                     "traffic_source": traffic_src, "algorithmic_bytes_per_launch": dom_bytes,
                      "avg_launch_ms": round(kern[dom]["avg_ms"], 4)},
         "cpu_baseline": cpu,
     }
