@@ -1,0 +1,45 @@
+"""The benchmark's work counts, which every reported TFLOP/s rests on, against
+brute-force counts of the oracle's visibility masks.
+
+A Phase-B suffix row j sees the P prefix keys and its own keys 0..j; a prefix
+row q sees keys 0..q; a tree row sees its own node up to itself and every
+ancestor node; a tree-window row also sees the whole prefix.  The benchmark
+prices a visible (query, key) pair per query head at 12 d FLOP (forward 4 d,
+backward 8 d)."""
+import numpy as np
+import pytest
+
+import bench
+from oracle import causal_mask, suffix_rows_mask, tree_ancestor_mask
+from workloads import get_config
+from workloads.gen import random_tree
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_flat_pairs_match_the_masks(seed):
+    rng = np.random.default_rng(seed)
+    p = int(rng.integers(0, 40))
+    lens = rng.integers(0, 25, size=int(rng.integers(1, 6)))
+    phase_b, prefix = bench.flat_pairs(p, lens)
+    assert phase_b == sum(int(suffix_rows_mask(p, int(s)).sum()) for s in lens)
+    assert prefix == int(causal_mask(p).sum())
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_tree_and_window_pairs_match_the_masks(seed):
+    node_off, parent = random_tree(seed, 9, max_len=12, min_len=0)
+    c = int(node_off[-1])
+    vis = tree_ancestor_mask(node_off, parent)
+    assert bench.tree_pairs(node_off, parent) == int(vis.sum())
+    p = 7 + seed
+    assert bench.window_pairs(p, node_off, parent) == c * p + int(vis.sum())
+
+
+def test_phase_b_work_at_the_headline_group():
+    """GQA 32/8, d 128, P 4096, 8 suffixes of 512: 570 490 880 visible pairs
+    over all query heads, 876.27 GFLOP of forward and backward."""
+    cfg = get_config(2)
+    pairs, _ = bench.flat_pairs(cfg.prefix_len, [cfg.suffix_len] * cfg.n_suffix)
+    assert pairs * cfg.num_q_heads == 570_490_880
+    flops = 12.0 * cfg.head_dim * pairs * cfg.num_q_heads
+    assert round(flops / 1e9, 2) == 876.27
