@@ -1,15 +1,21 @@
 """GPU parity at the full measured sizes.
 
-The GPU runs each workload exactly as the benchmark times it: the 32/8-head
-group at P = 4096 with all 8 suffixes in one Phase-B call (config 2), the
-64-suffix group at P = 8192 in 8 microbatch calls (config 4), the RAG-shaped
-varlen group at P = 16384 in 4 calls (config 3), the 12288-row rollout tree
-(config 5), four irregular tree windows over a 4096-row prefix with the
-producer backward (config 6), and the compact log-probabilities of the
-config-5 tree over a 151936-token vocabulary (config 7).  The fp64 oracle then recomputes whole KV-head groups (every
-query head that reads the chosen KV head, every row) and each output slice is
-compared normwise against it (2e-2, the bf16 bar).  Heads are independent, so
-a KV-head group is an exact sub-problem of the full call.
+The GPU runs each workload exactly as the benchmark times it:
+- the fp32 group of config 1;
+- the 32/8-head group at P = 4096 with all 8 suffixes in one Phase-B call
+  (config 2);
+- the RAG-shaped varlen group at P = 16384 in 4 calls (config 3);
+- the 64-suffix group at P = 8192 in 8 microbatch calls (config 4);
+- the 12288-row rollout tree (config 5);
+- four irregular tree windows over a 4096-row prefix with the producer
+  backward (config 6);
+- the compact log-probabilities of the config-5 tree over a 151936-token
+  vocabulary (config 7).
+
+The fp64 oracle then recomputes whole KV-head groups (every query head that
+reads the chosen KV head, every row), and each output slice is compared
+normwise against it: 2e-2, the bf16 bar, and 1e-4 for fp32.  Heads are
+independent, so a KV-head group is an exact sub-problem of the full call.
 
 Invariants checked at full size, where the oracle cannot cover every head
 or row:
@@ -91,6 +97,43 @@ def _check_phase_b_group(cfg, data, res, g):
 
 def _desc(cfg):
     return pf.AttnDesc(cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, pf.PF_BF16)
+
+
+def test_config1_fp32_all_phases():
+    """The fp32 group of config 1 (2 heads, d 64, P 256, 4 suffixes of 64) as
+    the benchmark generates it: Phase A, Phase B and Phase C with the
+    accumulated gK/gV, every head against the oracle at the fp32 bar."""
+    cfg = get_config(1)
+    print(f"\ngenerating config {cfg.cid}", flush=True)
+    data = generate(cfg)
+    desc = pf.AttnDesc(cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, pf.PF_F32)
+    res = _phase_b(cfg, data, desc, [(0, cfg.n_suffix)])
+    q_p, k_p, v_p, do_p = (dev(data[k], cfg.dtype) for k in ("q_p", "k_p", "v_p", "do_p"))
+    o_p, lse_p = G.prefix_fwd(desc, q_p, k_p, v_p)
+    gk = torch.from_numpy(res["gk"].astype(np.float32)).cuda()
+    gv = torch.from_numpy(res["gv"].astype(np.float32)).cuda()
+    dq_p, dk_p, dv_p = G.prefix_bwd(desc, q_p, k_p, v_p, o_p, lse_p, do_p, gk, gv)
+    torch.cuda.synchronize()
+    scale = 1.0 / math.sqrt(cfg.head_dim)
+    hmap = oracle.head_map(cfg.num_q_heads, cfg.num_kv_heads)
+    tol = TOL[cfg.dtype]
+    ref = oracle.suffix_attention(data["k_p"], data["v_p"], data["q_s"], data["k_s"], data["v_s"],
+                                  data["do_s"], data["cu_seqlens"], scale, hmap)
+    check("O_S", res["o"], ref["o_s"], tol)
+    check("LSE_S", res["lse"], ref["lse_s"], tol)
+    check("dQ_S", res["dq"], ref["dq_s"], tol)
+    check("dK_S", res["dk"], ref["dk_s"], tol)
+    check("dV_S", res["dv"], ref["dv_s"], tol)
+    check("gK", res["gk"], ref["gk"], tol)
+    check("gV", res["gv"], ref["gv"], tol)
+    ro, rl = oracle.prefix_forward(data["q_p"], data["k_p"], data["v_p"], scale, hmap)
+    check("O_P", host(o_p), ro, tol)
+    check("LSE_P", host(lse_p), rl, tol)
+    rdq, rdk, rdv = oracle.prefix_backward_inject(data["q_p"], data["k_p"], data["v_p"],
+                                                  data["do_p"], ref["gk"], ref["gv"], scale, hmap)
+    check("dQ_P", host(dq_p), rdq, tol)
+    check("dK_P", host(dk_p), rdk, tol)
+    check("dV_P", host(dv_p), rdv, tol)
 
 
 def test_config2_all_phases_full_size():
