@@ -493,7 +493,7 @@ constexpr int kFwdBN = 64;
 constexpr int kFwdTile = kFwdBN * kRowB;            // one K or V block
 constexpr int kFwdK = 0, kFwdV = 3 * kFwdTile;      // three K buffers, then three V buffers
 constexpr int kFwdDma = kFwdBN / 16;                // staging loads per wave per tile
-constexpr int kFwdExpB = 1;                         // key tiles of P exponentiated in phase B
+constexpr int kFwdExpB = 0;                         // key tiles of P exponentiated in phase B
 
 // max(x[l], x[l ^ 32]) in every lane, without LDS
 __device__ __forceinline__ float max_halves(float x) {
