@@ -10,12 +10,17 @@ workload a step is the tree forward and backward.
 Printed JSON (one line): `value` is the Phase-B forward+backward throughput
 in algorithmic TFLOP/s (12 * head_dim FLOPs per visible (query, key) pair
 per query head: 4 forward, 8 backward; the backward's recompute of the
-scores is not counted), with inputs resident in HBM.  `roofline` is for the
-kernel with the largest share of the step, timed with HIP events recorded
-on its own stream around each of its launches.  `cpu_baseline` is the CPU
-oracle (fp32 numpy) timed on a bounded sample of the same workload.
+scores is not counted), with inputs resident in HBM.  The timed steps record
+HIP events at the phase boundaries only.  `roofline` is for the kernel with
+the largest share of the step; its launch time comes from a separate pass
+over the same steps that records HIP events on the kernel's own stream
+around every launch (issued behind a queue of untimed steps, so the host's
+event bookkeeping never leaves the GPU idle).  `cpu_baseline` is the CPU
+oracle (fp32 numpy): dense attention over whole trajectories, timed on a
+bounded sample of the same workload.
 """
 import argparse
+import gc
 import json
 import math
 import os
@@ -106,17 +111,27 @@ class KernelTimer:
     `reserve` events are created (and recorded once) up front, so the timed
     region only re-records existing events."""
 
-    def __init__(self, torch, reserve=0):
+    def __init__(self, torch, reserve=0, streams=()):
         self.torch = torch
         self.open = {}
         self.spans = []          # (label, phase, start_event, end_event)
-        self.streams = {}
+        # streams the library is called on, wrapped before any launch so the
+        # hook creates no stream objects while kernels are being enqueued
+        self.streams = {s.cuda_stream: s for s in streams}
         self.last_end = {}       # stream -> end event of the previous kernel, this phase
         self._phase = None
-        self.pool = [torch.cuda.Event(enable_timing=True) for _ in range(reserve)]
+        self.reserve = reserve
+        self.pool = []
+        self.refill()
+
+    def refill(self):
+        """Drops recorded spans and makes `reserve` events ready for reuse."""
+        torch = self.torch
+        self.open, self.spans, self.last_end = {}, [], {}
+        self.pool = [torch.cuda.Event(enable_timing=True) for _ in range(self.reserve)]
         for e in self.pool:
             e.record()
-        if reserve:
+        if self.reserve:
             torch.cuda.synchronize()
 
     @property
@@ -182,7 +197,7 @@ def run_gpu(cfg, data, steps, warmup, copy_mib=0):
 
     stream = torch.cuda.current_stream()
     res = {}
-    timer = KernelTimer(torch, reserve=64 * (steps + 1))
+    timer = KernelTimer(torch, reserve=64 * (min(steps, 10) + 1), streams=(stream,))
     if cfg.is_windows:
         p = cfg.prefix_len
         q_p, k_p, v_p, do_p = (to_dev(data[n]) for n in ("q_p", "k_p", "v_p", "do_p"))
@@ -312,10 +327,20 @@ def run_gpu(cfg, data, steps, warmup, copy_mib=0):
         step()
     torch.cuda.synchronize()
 
-    # timed region: K steps, per-phase events inside each step; the launch hook
-    # records HIP events around every kernel on the stream it is launched on
+    def phases_of(evs):
+        n = len(evs)
+        if cfg.is_tree:
+            return {"tree": sum(e[0].elapsed_time(e[1]) for e in evs) / n}
+        return {"A": sum(e[0].elapsed_time(e[1]) for e in evs) / n,
+                "B": sum(e[1].elapsed_time(e[2]) for e in evs) / n,
+                "C": sum(e[2].elapsed_time(e[3]) for e in evs) / n}
+
+    # timed region: K steps with HIP events at the phase boundaries only (no
+    # per-kernel events: an event record between two kernels adds its own
+    # cost, and host-side bookkeeping per launch can leave the GPU idle)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
-    pf.pf_set_launch_hook(timer)
+    gc.collect()
+    gc.disable()
     try:
         t0 = time.perf_counter()
         for i in range(steps):
@@ -323,23 +348,58 @@ def run_gpu(cfg, data, steps, warmup, copy_mib=0):
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
     finally:
-        pf.pf_set_launch_hook(None)
-    phase_ms = {}
-    if cfg.is_tree:
-        phase_ms["tree"] = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
-    else:
-        phase_ms["A"] = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
-        phase_ms["B"] = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
-        phase_ms["C"] = sum(e[2].elapsed_time(e[3]) for e in evs) / steps
+        gc.enable()
+    phase_ms = phases_of(evs)
     res["wall_ms_per_step"] = wall * 1e3 / steps
     res["phase_ms"] = phase_ms
-
-    res["kernels"] = timer.summary()
+    res["steps_total_ms"] = evs[0][0].elapsed_time(evs[-1][3])
+    res["kernels"], res["kernel_pass"] = kernel_pass(torch, pf, timer, step, phases_of, phase_ms,
+                                                     min(steps, 10))
     if copy_mib > 0:
         copy_probe(torch, copy_mib)
     res["device"] = torch.cuda.get_device_name(0)
     res["cus"] = torch.cuda.get_device_properties(0).multi_processor_count
     return res
+
+
+def kernel_pass(torch, pf, timer, step, phases_of, timed_phase_ms, n_steps, lead=3, tries=2):
+    """Per-kernel launch times, from steps run after the timed region with the
+    launch hook recording HIP events around every kernel.  `lead` untimed steps
+    are queued first, so the GPU has several milliseconds of work ahead of the
+    host while the hook's bookkeeping runs.  The pass is repeated once if its
+    Phase-B (or tree) time is more than 5 % above the timed region's, and the
+    pass closer to the timed region is kept; both are reported."""
+    key = "tree" if "tree" in timed_phase_ms else "B"
+    best = None
+    passes = []
+    for _ in range(tries):
+        timer.refill()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_steps)]
+        torch.cuda.synchronize()
+        gc.collect()
+        gc.disable()
+        try:
+            for _ in range(lead):
+                step()
+            pf.pf_set_launch_hook(timer)
+            try:
+                for i in range(n_steps):
+                    step(evs[i])
+            finally:
+                pf.pf_set_launch_hook(None)
+            torch.cuda.synchronize()
+        finally:
+            gc.enable()
+        ph = phases_of(evs)
+        summ = timer.summary()
+        passes.append({k: round(v, 4) for k, v in ph.items()})
+        if best is None or ph[key] < best[0][key]:
+            best = (ph, summ)
+        if ph[key] <= 1.05 * timed_phase_ms[key]:
+            break
+    info = {"steps": n_steps, "lead_steps": lead, "passes_phase_ms": passes,
+            "kept_phase_ms": {k: round(v, 4) for k, v in best[0].items()}}
+    return best[1], info
 
 
 # ---------------------------------------------------------------- HBM traffic from counters
@@ -558,9 +618,19 @@ def load_traffic(cid, label):
 
 # ---------------------------------------------------------------- CPU oracle baseline
 
-def cpu_baseline(cfg, data, target_s):
-    """Time the oracle as it stands (fp32 numpy) on whole KV-head groups of the
-    workload until about target_s seconds of work; scale to TFLOP/s."""
+def cpu_baseline(cfg, data, target_s, group_flops, compact, expanded):
+    """The oracle as it stands (fp32 numpy, every core BLAS gets) on the dense
+    baseline the method replaces: every trajectory [P || S_i] of a flat group,
+    and every root-to-leaf trajectory of a tree, trained as an independent
+    causal sequence (forward and backward over its whole L x L score matrix;
+    `suffix_attention_full_rows`, `tree_attention_expanded`).  That yields the
+    group's Phase A, B and C results.  Tree windows use the oracle's
+    per-window dense attention over [prefix ; window rows].
+
+    Timed on whole KV-head groups until about target_s seconds; heads are
+    independent, so the whole group's time is the sample's scaled by
+    Hkv / groups done (exact in work).  `value` is the group's algorithmic
+    TFLOP (Phases A + B + C, or the tree) per second of oracle time."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -573,46 +643,54 @@ def cpu_baseline(cfg, data, target_s):
     d = cfg.head_dim
     scale = 1.0 / math.sqrt(d)
     hmap = np.zeros(g, dtype=np.int64)
-    done_groups, elapsed, flops = 0, 0.0, 0.0
+    done_groups, elapsed = 0, 0.0
     for kvh in range(cfg.num_kv_heads):
         heads = slice(kvh * g, (kvh + 1) * g)
+        kv = slice(kvh, kvh + 1)
         t0 = time.perf_counter()
         if cfg.is_windows:
-            pairs = 0
+            q_ph = data["q_p"][:, heads]
+            oracle.prefix_forward(q_ph, data["k_p"][:, kv], data["v_p"][:, kv], scale, hmap,
+                                  dtype=np.float32)
+            zero = np.zeros((cfg.prefix_len, 1, d), np.float32)
+            oracle.prefix_backward_inject(q_ph, data["k_p"][:, kv], data["v_p"][:, kv],
+                                          data["do_p"][:, heads], zero, zero, scale, hmap,
+                                          dtype=np.float32)
             for w in data["windows"]:
-                oracle.tree_window_attention(data["k_p"][:, kvh:kvh + 1],
-                                             data["v_p"][:, kvh:kvh + 1], w["q"][:, heads],
-                                             w["k"][:, kvh:kvh + 1], w["v"][:, kvh:kvh + 1],
+                oracle.tree_window_attention(data["k_p"][:, kv], data["v_p"][:, kv],
+                                             w["q"][:, heads], w["k"][:, kv], w["v"][:, kv],
                                              w["do"][:, heads], w["node_off"], w["parent"], scale,
                                              hmap, dtype=np.float32)
-                pairs += window_pairs(cfg.prefix_len, w["node_off"], w["parent"])
         elif cfg.is_tree:
-            oracle.tree_attention_direct(data["q"][:, heads], data["k"][:, kvh:kvh + 1],
-                                         data["v"][:, kvh:kvh + 1], data["do"][:, heads],
-                                         data["node_off"], data["parent"], scale, hmap,
-                                         dtype=np.float32)
-            pairs = tree_pairs(data["node_off"], data["parent"])
+            oracle.tree_attention_expanded(data["q"][:, heads], data["k"][:, kv],
+                                           data["v"][:, kv], data["do"][:, heads],
+                                           data["node_off"], data["parent"], scale, hmap,
+                                           dtype=np.float32)
         else:
-            oracle.suffix_attention(data["k_p"][:, kvh:kvh + 1], data["v_p"][:, kvh:kvh + 1],
-                                    data["q_s"][:, heads], data["k_s"][:, kvh:kvh + 1],
-                                    data["v_s"][:, kvh:kvh + 1], data["do_s"][:, heads],
-                                    data["cu_seqlens"], scale, hmap, dtype=np.float32)
-            pairs, _ = flat_pairs(cfg.prefix_len, np.diff(data["cu_seqlens"]))
+            oracle.suffix_attention_full_rows(data["q_p"][:, heads], data["k_p"][:, kv],
+                                              data["v_p"][:, kv], data["q_s"][:, heads],
+                                              data["k_s"][:, kv], data["v_s"][:, kv],
+                                              data["do_s"][:, heads], data["cu_seqlens"], scale,
+                                              hmap, dtype=np.float32)
         elapsed += time.perf_counter() - t0
-        flops += 12.0 * d * pairs * g
         done_groups += 1
         if elapsed >= target_s:
             break
-    what = ("tree fwd+bwd" if cfg.is_tree else
-            "tree-window fwd+bwd" if cfg.is_windows else "Phase B fwd+bwd")
+    full_s = elapsed * cfg.num_kv_heads / done_groups
+    what = ("dense fwd+bwd of every root-to-leaf trajectory" if cfg.is_tree else
+            "dense prefix fwd+bwd and every window over [prefix ; window rows]" if cfg.is_windows
+            else
+            "dense fwd+bwd of every trajectory [P || S_i], all rows")
     return {
-        "value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+        "value": group_flops / full_s / 1e12, "unit": "TFLOP/s", "cores": int(threads),
         "kind": "oracle",
         "sample": f"{what} of config {cfg.cid} on {done_groups} of {cfg.num_kv_heads} KV-head "
-                  f"groups ({done_groups * g} query heads), fp32 numpy, {elapsed:.1f} s",
+                  f"groups ({done_groups * g} query heads), fp32 numpy, {elapsed:.1f} s; value = "
+                  f"the group's algorithmic FLOPs / the group time scaled from the sample",
         "seconds": elapsed, "os_cpu_count": os.cpu_count(),
         "affinity_cpus": len(os.sched_getaffinity(0)), "blas": blas,
-        "full_workload_seconds_extrapolated": elapsed * cfg.num_kv_heads / done_groups,
+        "full_workload_seconds_extrapolated": full_s,
+        "group_tokens_per_s": {"compact": compact / full_s, "expanded": expanded / full_s},
     }
 
 
@@ -899,7 +977,8 @@ def main():
     for label, kn in kern.items():
         if label not in per_pair:
             continue
-        flops = sum(per_pair[label] * d * hq * phase_pairs[ph] for ph in kn["phases"]) * args.steps
+        flops = (sum(per_pair[label] * d * hq * phase_pairs[ph] for ph in kn["phases"]) *
+                 gres["kernel_pass"]["steps"])
         kn["algorithmic_flops_per_launch"] = flops / kn["launches"]
         kn["tflops"] = flops / (kn["total_ms"] * 1e-3) / 1e12
     if dom in per_pair:
@@ -919,10 +998,13 @@ def main():
         roofline = {"bound": "hbm", "kernel": dom, "achieved": None, "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": None, "traffic": None}
 
+    # the group's algorithmic work: Phase A forward (4d per pair), Phase B
+    # forward and backward (12d), Phase C backward (8d); or the tree (12d)
+    group_flops = flops_b + 12.0 * d * pairs_a * hq
     cpu = None
     if args.cpu_seconds > 0:
         print("[bench] timing the CPU oracle", flush=True)
-        cpu = cpu_baseline(cfg, data, args.cpu_seconds)
+        cpu = cpu_baseline(cfg, data, args.cpu_seconds, group_flops, compact, expanded)
 
     peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
     out = {
@@ -956,15 +1038,18 @@ def main():
         "group_tokens_per_s": {"compact": round(compact / (step_ms * 1e-3), 1),
                                "expanded": round(expanded / (step_ms * 1e-3), 1)},
         "wall_ms_per_step": round(gres["wall_ms_per_step"], 4),
+        "steps_total_ms_per_step": round(gres["steps_total_ms"] / args.steps, 4),
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv)
                         for kk, vv in v.items()} for k, v in kern.items()},
+        "kernel_pass": gres["kernel_pass"],
         "roofline": roofline,
         "cpu_baseline": cpu,
         "device": gres["device"], "compute_units": gres["cus"],
     }
+    out["group_tflops"] = round(group_flops / (step_ms * 1e-3) / 1e12, 3)
     if cpu:
-        # the oracle's rate on the same unit, and group tokens/s at that rate
-        ratio = value / cpu["value"] if cpu["value"] > 0 else None
+        # the same group on both sides: algorithmic TFLOP/s and group tokens/s
+        ratio = out["group_tflops"] / cpu["value"] if cpu["value"] > 0 else None
         out["gpu_over_oracle"] = round(ratio, 1) if ratio else None
     line = json.dumps(out)
     if args.json_out:

@@ -4,7 +4,8 @@ The GPU runs each workload exactly as the benchmark times it:
 - the fp32 group of config 1;
 - the 32/8-head group at P = 4096 with all 8 suffixes in one Phase-B call
   (config 2);
-- the RAG-shaped varlen group at P = 16384 in 4 calls (config 3);
+- the RAG-shaped varlen group at P = 16384: Phase A, Phase B in 4 calls
+  adding into one gK/gV, Phase C (config 3);
 - the 64-suffix group at P = 8192 in 8 microbatch calls (config 4);
 - the 12288-row rollout tree (config 5);
 - four irregular tree windows over a 4096-row prefix with the producer
@@ -34,6 +35,7 @@ import torch
 
 import oracle
 from tests.gpu_util import TOL, check, dev, host
+from tests.row_blocks import prefix_phases_by_row_blocks
 from workloads import generate, get_config
 
 pytestmark = pytest.mark.gpu
@@ -194,37 +196,58 @@ def test_config4_microbatches_full_size():
         assert np.array_equal(res[name], res2[name]), f"{name} depends on the split"
 
 
+@pytest.mark.timeout(1200)
 def test_config3_varlen_full_size():
-    """Phase B of the RAG-shaped group (P = 16384, 16 varlen suffixes, 4
-    calls).  The oracle recomputes two whole suffixes (the shortest and the
-    longest) for one KV-head group: their rows' O, LSE, dQ and their own
-    keys' dK, dV depend only on their own trajectories."""
+    """The RAG-shaped group as the benchmark runs it: Phase A at P = 16384,
+    Phase B of 16 varlen suffixes in 4 calls adding into one gK/gV, and
+    Phase C with that gK/gV injected (the full workspace, so the backward
+    stores dS: the largest dS buffer of any workload, Hq x P^2 bf16).  For one
+    KV-head group (its 4 query heads, every row) the fp64 oracle recomputes
+    every Phase-B output, the gK/gV accumulated over the 4 calls (against the
+    oracle over all 16 suffixes at once), and Phase A / Phase C, assembled from
+    the oracle over blocks of 2048 prefix rows (tests/row_blocks.py)."""
     cfg = get_config(3)
     print(f"\ngenerating config {cfg.cid}", flush=True)
-    data = generate(cfg, include_prefix_q=False)
+    data = generate(cfg)
     desc = _desc(cfg)
+    p = cfg.prefix_len
     calls = [tuple(int(x) for x in mb) for mb in data["microbatches"]]
+    assert len(calls) == 4
     res = _phase_b(cfg, data, desc, calls)
-    cu = data["cu_seqlens"]
-    lens = np.diff(cu)
+    q_p, k_p, v_p, do_p = (dev(data[k], cfg.dtype) for k in ("q_p", "k_p", "v_p", "do_p"))
+    o_p, lse_p = G.prefix_fwd(desc, q_p, k_p, v_p)
+    gk = torch.from_numpy(res["gk"].astype(np.float32)).cuda()
+    gv = torch.from_numpy(res["gv"].astype(np.float32)).cuda()
+    ws_c = G.workspace(pf.PF_OP_PREFIX_BWD, desc, p, p, "cuda")
+    assert ws_c.numel() > pf.pf_workspace_size_min(pf.PF_OP_PREFIX_BWD, desc, p, p)
+    dq_p, dk_p, dv_p = G.prefix_bwd(desc, q_p, k_p, v_p, o_p, lse_p, do_p, gk, gv, ws=ws_c)
+    torch.cuda.synchronize()
+    del ws_c, q_p, k_p, v_p, do_p, gk, gv
+    o_p, lse_p, dq_p, dk_p, dv_p = (host(x) for x in (o_p, lse_p, dq_p, dk_p, dv_p))
+    for x in (res["o"], res["dq"], res["dk"], res["dv"], res["gk"], res["gv"], o_p, lse_p, dq_p,
+              dk_p, dv_p):
+        assert np.all(np.isfinite(x))
     g = 6
     hs = _heads_of(cfg, g)
     scale = 1.0 / math.sqrt(cfg.head_dim)
     hmap = np.zeros(cfg.group_size, dtype=np.int64)
     tol = TOL[cfg.dtype]
-    for i in (int(np.argmin(lens)), int(np.argmax(lens))):
-        a, b = int(cu[i]), int(cu[i + 1])
-        print(f"  oracle suffix {i} ({b - a} rows), KV head {g}", flush=True)
-        sub = np.asarray([0, b - a], dtype=np.int32)
-        ref = oracle.suffix_attention(data["k_p"][:, g:g + 1], data["v_p"][:, g:g + 1],
-                                      data["q_s"][a:b, hs], data["k_s"][a:b, g:g + 1],
-                                      data["v_s"][a:b, g:g + 1], data["do_s"][a:b, hs], sub,
-                                      scale, hmap)
-        check(f"O_S[s{i}]", res["o"][a:b, hs], ref["o_s"], tol)
-        check(f"LSE_S[s{i}]", res["lse"][hs, a:b], ref["lse_s"], tol)
-        check(f"dQ_S[s{i}]", res["dq"][a:b, hs], ref["dq_s"], tol)
-        check(f"dK_S[s{i}]", res["dk"][a:b, g:g + 1], ref["dk_s"], tol)
-        check(f"dV_S[s{i}]", res["dv"][a:b, g:g + 1], ref["dv_s"], tol)
+    # every Phase-B output of the group, and gK/gV summed over all 16 suffixes
+    ref_b = _check_phase_b_group(cfg, data, res, g)
+    torch.cuda.empty_cache()
+
+    def progress(r0, r1):
+        print(f"  oracle prefix rows [{r0}, {r1}), KV head {g}", flush=True)
+
+    kp, vp = data["k_p"][:, g:g + 1], data["v_p"][:, g:g + 1]
+    ro, rl, rdq, rdk, rdv = prefix_phases_by_row_blocks(
+        data["q_p"][:, hs], kp, vp, data["do_p"][:, hs], ref_b["gk"], ref_b["gv"], scale, hmap,
+        2048, progress)
+    check(f"O_P[g{g}]", o_p[:, hs], ro, tol)
+    check(f"LSE_P[g{g}]", lse_p[hs], rl, tol)
+    check(f"dQ_P[g{g}]", dq_p[:, hs], rdq, tol)
+    check(f"dK_P[g{g}]", dk_p[:, g:g + 1], rdk, tol)
+    check(f"dV_P[g{g}]", dv_p[:, g:g + 1], rdv, tol)
 
 
 def test_config5_tree_full_size():
