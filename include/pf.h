@@ -42,7 +42,10 @@
  *    value, so no call reads host memory after it returns.
  *  - The caller allocates every device buffer, including the workspace,
  *    sized by pf_workspace_size().  The library allocates nothing, keeps no
- *    state between calls, never synchronises and never frees.
+ *    state between calls, never synchronises and never frees.  The one
+ *    exception is pf_suffix_attn_bwd_accum_noalloc, which takes no workspace:
+ *    it runs in a static device array of the library and remembers that
+ *    array's address per device.
  *  - All work is enqueued on `stream` (a hipStream_t; NULL = default stream)
  *    and is asynchronous: a return of PF_OK means "launched".
  *  - Every argument is validated before anything is launched.  On an error
@@ -168,6 +171,32 @@ pf_status pf_suffix_attn_bwd_accum(const pf_attn_desc* desc, int32_t prefix_len,
                                    pf_tensor do_s, pf_tensor dq_s, pf_tensor dk_s,
                                    pf_tensor dv_s, float* gk_acc, float* gv_acc,
                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* The Phase-B backward of pf_suffix_attn_bwd_accum for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops,
+ * harnesses that forbid allocation): same arguments and results, without
+ * the workspace.  It allocates nothing and calls no allocating routine; its
+ * device scratch is a static array of PF_NOALLOC_SCRATCH_BYTES in the
+ * library, one per GPU, held until the process ends, on the calling thread's
+ * current device (the stream must belong to that device).
+ *   Scratch need: about 4 x rows + 8 x Hq x rows bytes (the per-row
+ *   visibility tables, D and LSE); a call that needs more returns
+ *   PF_ERR_UNSUPPORTED with nothing launched.
+ *   It runs the recompute dQ path with every key block whole, so results
+ *   agree with pf_suffix_attn_bwd_accum to rounding (fp32 sums in another
+ *   order), and are bitwise identical run to run.
+ *   Every call on a GPU shares that GPU's scratch: calls that overlap in time
+ *   on one GPU (other streams, other threads) race and must be ordered by
+ *   the caller.  Nothing in the scratch needs to start at zero; each call
+ *   writes what it reads.                                                  */
+#define PF_NOALLOC_SCRATCH_BYTES (16u << 20)
+pf_status pf_suffix_attn_bwd_accum_noalloc(const pf_attn_desc* desc, int32_t prefix_len,
+                                           pf_tensor k_p, pf_tensor v_p, int32_t n_suffix,
+                                           const int32_t* cu_seqlens, pf_tensor q_s,
+                                           pf_tensor k_s, pf_tensor v_s, pf_tensor o_s,
+                                           const float* lse_s, pf_tensor do_s, pf_tensor dq_s,
+                                           pf_tensor dk_s, pf_tensor dv_s, float* gk_acc,
+                                           float* gv_acc, void* stream);
 
 /* Phase C (PrefixFlow §3.1 "Phase C: prefix backward", §4.1): the causal
  * prefix backward, with the accumulated gK/gV added in fp32 before the one

@@ -22,10 +22,11 @@ PF_F32, PF_BF16 = 0, 1
  PF_OP_TREE_BWD, PF_OP_TREE_SUFFIX_FWD, PF_OP_TREE_SUFFIX_BWD) = range(8)
 PF_MAX_SEGMENTS = 256
 PF_MAX_HEADS = 256
+PF_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 EXPORTED = (
     "pf_workspace_size", "pf_workspace_size_min", "pf_prefix_fwd", "pf_suffix_attn_fwd", "pf_suffix_attn_bwd_accum",
-    "pf_prefix_bwd_inject", "pf_tree_attn_fwd", "pf_tree_attn_bwd", "pf_tree_suffix_attn_fwd",
+    "pf_suffix_attn_bwd_accum_noalloc", "pf_prefix_bwd_inject", "pf_tree_attn_fwd", "pf_tree_attn_bwd", "pf_tree_suffix_attn_fwd",
     "pf_tree_suffix_attn_bwd_accum", "pf_compact_logprob_fwd", "pf_compact_logprob_bwd",
     "pf_tree_subtree_end",
     "pf_status_string", "pf_last_error", "pf_abi_version", "pf_set_launch_hook",
@@ -78,6 +79,8 @@ def _load():
         "pf_suffix_attn_fwd": (i32, [D, i32, T, T, i32, ip, T, T, T, T, fp, P, sz, P]),
         "pf_suffix_attn_bwd_accum": (i32, [D, i32, T, T, i32, ip, T, T, T, T, fp, T, T, T, T,
                                            fp, fp, P, sz, P]),
+        "pf_suffix_attn_bwd_accum_noalloc": (i32, [D, i32, T, T, i32, ip, T, T, T, T, fp, T, T,
+                                                   T, T, fp, fp, P]),
         "pf_prefix_bwd_inject": (i32, [D, i32, T, T, T, T, fp, T, fp, fp, T, T, T, i32, P, sz,
                                        P]),
         "pf_tree_attn_fwd": (i32, [D, i32, ip, ip, T, T, T, T, fp, P, sz, P]),
@@ -224,6 +227,17 @@ def pf_suffix_attn_bwd_accum(desc, prefix_len, k_p, v_p, cu_seqlens, q_s, k_s, v
         ctypes.byref(d), prefix_len, _t(k_p), _t(v_p), len(cu) - 1, cu_p, _t(q_s), _t(k_s),
         _t(v_s), _t(o_s), _p(lse_s), _t(do_s), _t(dq_s), _t(dk_s), _t(dv_s), _p(gk_acc),
         _p(gv_acc), ws, nws, _stream(stream)))
+
+
+def pf_suffix_attn_bwd_accum_noalloc(desc, prefix_len, k_p, v_p, cu_seqlens, q_s, k_s, v_s,
+                                     o_s, lse_s, do_s, dq_s, dk_s, dv_s, gk_acc, gv_acc,
+                                     stream=None):
+    d, _keep = desc._c()
+    cu, cu_p = _ints(cu_seqlens)
+    _check(_lib.pf_suffix_attn_bwd_accum_noalloc(
+        ctypes.byref(d), prefix_len, _t(k_p), _t(v_p), len(cu) - 1, cu_p, _t(q_s), _t(k_s),
+        _t(v_s), _t(o_s), _p(lse_s), _t(do_s), _t(dq_s), _t(dk_s), _t(dv_s), _p(gk_acc),
+        _p(gv_acc), _stream(stream)))
 
 
 def pf_prefix_bwd_inject(desc, prefix_len, q_p, k_p, v_p, o_p, lse_p, do_p, gk_acc, gv_acc,

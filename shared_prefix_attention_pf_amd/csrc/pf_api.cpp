@@ -7,6 +7,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "pf_internal.h"
@@ -150,6 +151,41 @@ pf_status check_stream_ws(void* ws, size_t ws_bytes, size_t need) {
   return PF_OK;
 }
 
+// ------------------------------------------------------------- static scratch
+
+// Device memory of pf_suffix_attn_bwd_accum_noalloc, which cannot take a
+// workspace from its caller.  Each GPU the library runs on holds one copy of
+// this array until the process ends.  In host code `scratch` names a host-side
+// stand-in, not device memory: the device address comes from
+// hipGetSymbolAddress, once per device, and only that address is used.
+constexpr size_t kScratchBytes = PF_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices];
+
+// The device address of `scratch` on the calling thread's current device.
+pf_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(PF_ERR_UNSUPPORTED, "device %d is beyond the %d devices the scratch tracks", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p || (uintptr_t)p % 256)
+      return fail(PF_ERR_HIP, "hipGetSymbolAddress(scratch) returned an unaligned address");
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return PF_OK;
+}
+
 // ------------------------------------------------------------- workspace
 
 struct WsLayout {
@@ -177,7 +213,8 @@ bool ds_eligible(int32_t op, const Desc& d, int32_t n_ext, int32_t rows) {
   return keys * r * 2 < ((int64_t)1 << 31);
 }
 
-WsLayout layout(int32_t op, const Desc& d, int32_t n_ext, int32_t rows, bool want_ds = false) {
+WsLayout layout(int32_t op, const Desc& d, int32_t n_ext, int32_t rows, bool want_ds = false,
+                bool split = true) {
   WsLayout w;
   size_t off = 0;
   const size_t nb = (size_t)((rows + 31) / 32);
@@ -193,7 +230,7 @@ WsLayout layout(int32_t op, const Desc& d, int32_t n_ext, int32_t rows, bool wan
     w.lse2 = off;
     off += align_up((size_t)d.hq * rows * 4);
   }
-  if (op == PF_OP_SUFFIX_BWD || op == PF_OP_TREE_SUFFIX_BWD) {
+  if (split && (op == PF_OP_SUFFIX_BWD || op == PF_OP_TREE_SUFFIX_BWD)) {
     w.n_chunks = pf::ext_chunks(n_ext, rows, d.hq, d.hkv, d.d, d.dtype);
     if (w.n_chunks > 1) {
       const size_t part = (size_t)(w.n_chunks - 1) * n_ext * d.hkv * d.d * 4;
@@ -201,7 +238,7 @@ WsLayout layout(int32_t op, const Desc& d, int32_t n_ext, int32_t rows, bool wan
       w.gv_part = off; off += align_up(part);
     }
   }
-  if (bwd) {
+  if (bwd && split) {
     w.n_chunks_own = pf::own_chunks(op, n_ext, rows, d.hq, d.hkv, d.d, d.dtype);
     if (w.n_chunks_own > 1) {
       const size_t part = (size_t)w.n_chunks_own * rows * d.hkv * d.d * 4;
@@ -552,12 +589,16 @@ pf_status suffix_fwd_impl(int32_t op, const Desc& d, int32_t prefix_len, pf_tens
 }
 
 // Phase B backward with gK/gV accumulation, for the same two row structures.
+// With use_scratch the call runs in this library's static device scratch
+// instead of a workspace argument (workspace and workspace_bytes are
+// ignored): the recompute dQ path with no key block split, so the scratch
+// holds only the per-row tables and D / LSE.
 pf_status suffix_bwd_impl(int32_t op, const Desc& d, int32_t prefix_len, pf_tensor k_p,
                           pf_tensor v_p, int32_t rows, const pf::SegTable& seg, pf_tensor q_s,
                           pf_tensor k_s, pf_tensor v_s, pf_tensor o_s, const float* lse_s,
                           pf_tensor do_s, pf_tensor dq_s, pf_tensor dk_s, pf_tensor dv_s,
                           float* gk_acc, float* gv_acc, void* workspace, size_t workspace_bytes,
-                          void* stream) {
+                          void* stream, bool use_scratch = false) {
   pf_status s;
   if ((s = check_tensor("k_p", k_p, prefix_len, d.hkv, d, d.dtype)) != PF_OK) return s;
   if ((s = check_tensor("v_p", v_p, prefix_len, d.hkv, d, d.dtype)) != PF_OK) return s;
@@ -574,9 +615,21 @@ pf_status suffix_bwd_impl(int32_t op, const Desc& d, int32_t prefix_len, pf_tens
     if ((s = check_ptr("gk_acc", gk_acc, 16)) != PF_OK) return s;
     if ((s = check_ptr("gv_acc", gv_acc, 16)) != PF_OK) return s;
   }
-  const WsLayout w_min = layout(op, d, prefix_len, rows, false);
-  if ((s = check_stream_ws(workspace, workspace_bytes, w_min.total)) != PF_OK) return s;
-  const WsLayout w = pick_layout(op, d, prefix_len, rows, workspace_bytes, w_min);
+  WsLayout w;
+  if (use_scratch) {
+    w = layout(op, d, prefix_len, rows, false, false);
+    if (w.total > kScratchBytes)
+      return fail(PF_ERR_UNSUPPORTED,
+                  "this call needs %zu bytes of scratch; the static scratch holds %zu "
+                  "(PF_NOALLOC_SCRATCH_BYTES)", w.total, kScratchBytes);
+    if (rows == 0) return PF_OK;
+    if ((s = scratch_of_current_device(&workspace)) != PF_OK) return s;
+    workspace_bytes = kScratchBytes;
+  } else {
+    const WsLayout w_min = layout(op, d, prefix_len, rows, false);
+    if ((s = check_stream_ws(workspace, workspace_bytes, w_min.total)) != PF_OK) return s;
+    w = pick_layout(op, d, prefix_len, rows, workspace_bytes, w_min);
+  }
   if (rows == 0) return PF_OK;
   pf::AttnArgs a = base_args(d, rows);
   set_q(a, q_s);
@@ -637,6 +690,24 @@ pf_status pf_suffix_attn_bwd_accum(const pf_attn_desc* desc, int32_t prefix_len,
   return suffix_bwd_impl(PF_OP_SUFFIX_BWD, d, prefix_len, k_p, v_p, rows,
                          flat_segments(n_suffix, cu_seqlens), q_s, k_s, v_s, o_s, lse_s, do_s,
                          dq_s, dk_s, dv_s, gk_acc, gv_acc, workspace, workspace_bytes, stream);
+}
+
+pf_status pf_suffix_attn_bwd_accum_noalloc(const pf_attn_desc* desc, int32_t prefix_len,
+                                           pf_tensor k_p, pf_tensor v_p, int32_t n_suffix,
+                                           const int32_t* cu_seqlens, pf_tensor q_s,
+                                           pf_tensor k_s, pf_tensor v_s, pf_tensor o_s,
+                                           const float* lse_s, pf_tensor do_s, pf_tensor dq_s,
+                                           pf_tensor dk_s, pf_tensor dv_s, float* gk_acc,
+                                           float* gv_acc, void* stream) {
+  Desc d;
+  pf_status s = check_desc(desc, &d);
+  if (s != PF_OK) return s;
+  if (prefix_len < 0) return fail(PF_ERR_INVALID_ARG, "prefix_len is negative");
+  int32_t rows = 0;
+  if ((s = check_cu(n_suffix, cu_seqlens, &rows)) != PF_OK) return s;
+  return suffix_bwd_impl(PF_OP_SUFFIX_BWD, d, prefix_len, k_p, v_p, rows,
+                         flat_segments(n_suffix, cu_seqlens), q_s, k_s, v_s, o_s, lse_s, do_s,
+                         dq_s, dk_s, dv_s, gk_acc, gv_acc, nullptr, 0, stream, true);
 }
 
 pf_status pf_tree_suffix_attn_fwd(const pf_attn_desc* desc, int32_t prefix_len, pf_tensor k_p,

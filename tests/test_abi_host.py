@@ -67,6 +67,8 @@ def test_binding_constants_match_the_header():
     defs = dict(re.findall(r"#define\s+(PF_MAX_[A-Z]+)\s+(\d+)", src))
     assert int(defs["PF_MAX_SEGMENTS"]) == pf.PF_MAX_SEGMENTS
     assert int(defs["PF_MAX_HEADS"]) == pf.PF_MAX_HEADS
+    m = re.search(r"#define\s+PF_NOALLOC_SCRATCH_BYTES\s+\((\d+)u\s*<<\s*(\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == pf.PF_NOALLOC_SCRATCH_BYTES
 
 
 def test_rejects_bad_head_config():
@@ -201,3 +203,22 @@ def test_logprob_entry_points_validate_on_the_host():
     assert f(4, 100, FAKE, 96) == pf.PF_ERR_INVALID_ARG               # stride < vocab
     assert f(0, 100, 0, 0) == pf.PF_OK                                # nothing to do
 
+
+
+def test_noalloc_rejects_a_call_beyond_its_scratch():
+    """The no-alloc backward checks its scratch need on the host: a call whose
+    per-row tables and D / LSE exceed the static scratch is refused with
+    PF_ERR_UNSUPPORTED before any HIP call (placeholder pointers are never
+    touched), and so is an invalid argument."""
+    d, _keep = _desc()
+    rows = 1 << 17        # 8 x 32 x 131072 bytes of D and LSE alone: past 16 MiB
+    cu = np.asarray([0, rows], dtype=np.int32)
+    cu_p = cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    q = _t(heads=32)
+    kv = _t(heads=8)
+    args = [ctypes.byref(d), 64, kv, kv, 1, cu_p, q, kv, kv, q, ctypes.c_void_p(FAKE), q, q, kv,
+            kv, ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), ctypes.c_void_p(0)]
+    assert pf._lib.pf_suffix_attn_bwd_accum_noalloc(*args) == pf.PF_ERR_UNSUPPORTED
+    assert b"scratch" in pf._lib.pf_last_error()
+    args[1] = -1
+    assert pf._lib.pf_suffix_attn_bwd_accum_noalloc(*args) == pf.PF_ERR_INVALID_ARG
