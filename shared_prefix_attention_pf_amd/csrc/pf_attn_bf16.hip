@@ -396,12 +396,15 @@ struct RowSrc {
     res = row_rsrc(base, nrows, st_b);
     lane_off = dma_lane_off(wave, lane, st_b);
   }
-  // rows [r0, r0 + ROWS) into `tile`, issued by every wave of the group
-  template <int ROWS>
+  // rows [r0, r0 + ROWS) into `tile`, issued by every one of the group's
+  // WAVES waves (each moves 4 rows per load)
+  template <int ROWS, int WAVES = 4>
   __device__ void stage(int r0, lds_t* tile, int wave) const {
+    static_assert(ROWS % (4 * WAVES) == 0, "rows per stage must cover every wave");
 #pragma unroll
-    for (int i = 0; i < ROWS / 16; ++i)
-      lds_dma16(res, tile + (16 * i + 4 * wave) * kRowB, lane_off, (uint32_t)(r0 + 16 * i) * st_b);
+    for (int i = 0; i < ROWS / (4 * WAVES); ++i)
+      lds_dma16(res, tile + (4 * WAVES * i + 4 * wave) * kRowB, lane_off,
+                (uint32_t)(r0 + 4 * WAVES * i) * st_b);
   }
 };
 
@@ -420,18 +423,21 @@ struct BlockSrc {
   }
   __device__ bool ext(int b) const { return b < n_ext_blocks; }
   __device__ int k0(int b) const { return (ext(b) ? b : b - n_ext_blocks) * BN; }
-  // stage the K or V rows of block b into an LDS tile (rows past the end read 0)
+  // stage the K or V rows of block b into an LDS tile (rows past the end
+  // read 0), issued by all WAVES waves of the group
+  template <int WAVES = 4>
   __device__ void dma_k(int b, lds_t* tile, int wave, int /*lane*/) const {
     if (ext(b))
-      kx.stage<BN>(k0(b), tile, wave);
+      kx.stage<BN, WAVES>(k0(b), tile, wave);
     else
-      ko.stage<BN>(k0(b), tile, wave);
+      ko.stage<BN, WAVES>(k0(b), tile, wave);
   }
+  template <int WAVES = 4>
   __device__ void dma_v(int b, lds_t* tile, int wave, int /*lane*/) const {
     if (ext(b))
-      vx.stage<BN>(k0(b), tile, wave);
+      vx.stage<BN, WAVES>(k0(b), tile, wave);
     else
-      vo.stage<BN>(k0(b), tile, wave);
+      vo.stage<BN, WAVES>(k0(b), tile, wave);
   }
 };
 
@@ -443,13 +449,14 @@ __device__ __forceinline__ int load_kend(const AttnArgs& a, const BlockSrc<BN>& 
   return kk < a.rows ? a.ri.kend[kk] : -1;
 }
 
-// Mask of an S^T tile set (BN keys x two query columns, C layout: rows are
+// Mask of an S^T tile set (BN keys x NT query columns, C layout: rows are
 // keys): invisible entries become -inf.  Branch-free per element; the kend
 // values are read four keys at a time, one group after another, so the mask
-// holds few registers beside the tiles.
-template <int BN>
-__device__ __forceinline__ void mask_st(f32x16 (&s)[BN / 32][2], bool ext, int k0, int klim,
-                                        const int32_t* kend, int tok0, int tok1, int h32) {
+// holds few registers beside the tiles.  tok[nt] is the lane's query token of
+// column tile nt.
+template <int BN, int NT>
+__device__ __forceinline__ void mask_st(f32x16 (&s)[BN / 32][NT], bool ext, int k0, int klim,
+                                        const int32_t* kend, const int (&tok)[NT], int h32) {
 #pragma unroll
   for (int kt = 0; kt < BN / 32; ++kt)
 #pragma unroll
@@ -462,15 +469,18 @@ __device__ __forceinline__ void mask_st(f32x16 (&s)[BN / 32][2], bool ext, int k
       } else {
         ke4[0] = ke4[1] = ke4[2] = ke4[3] = 0x7fffffff;
       }
+      // bitwise, not short-circuit, tests: one select per element, no branch
+      const int ext_i = ext ? 1 : 0;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 4 * jj + r;
         const int kk = k0 + kl0 + r;
-        const bool in = kk < klim;
-        const bool v0 = in && kk <= tok0 && tok0 < ke4[r];
-        const bool v1 = in && kk <= tok1 && tok1 < ke4[r];
-        s[kt][0][i] = v0 || (ext && in) ? s[kt][0][i] : -INFINITY;
-        s[kt][1][i] = v1 || (ext && in) ? s[kt][1][i] : -INFINITY;
+        const int in = kk < klim ? 1 : 0;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const int own = (kk <= tok[nt] ? 1 : 0) & (tok[nt] < ke4[r] ? 1 : 0);
+          s[kt][nt][i] = (in & (ext_i | own)) ? s[kt][nt][i] : -INFINITY;
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -479,12 +489,16 @@ __device__ __forceinline__ void mask_st(f32x16 (&s)[BN / 32][2], bool ext, int k
 // ---------------------------------------------------------------------------
 // Forward.
 //
-// Each key block j (64 keys) runs in two matrix-core phases:
+// A workgroup holds kRowsPerWg query rows; each wave holds NT column tiles of
+// 32 rows, so there are 8 / NT waves.  With NT = 1 (the build's choice) the
+// eight waves run two per SIMD: while one issues matrix-core products the
+// other's softmax arithmetic, LDS reads and waits proceed, which a single
+// wave per SIMD cannot overlap with its own products.  Each key block j (64
+// keys) runs in two matrix-core phases:
 //   A  S^T of block j + 1 (K Q^T) on the matrix cores while the VALU finishes
 //      P_j = exp2(S_j c - m), packs it to bf16 and adds its row sums;
 //   B  O^T += V_j^T P_j^T on the matrix cores while the VALU takes the row
-//      maxima of S_{j+1}, moves the running maxima (lazy rescale) and starts
-//      the exponentials of P_{j+1}.
+//      maxima of S_{j+1} and moves the running maxima (lazy rescale).
 // K and V rotate through three LDS buffers each: iteration j stages K of
 // block j + 3 and V of block j + 2, so every staging load has a whole
 // iteration to land before the wait that precedes its use.  One barrier per
@@ -492,8 +506,7 @@ __device__ __forceinline__ void mask_st(f32x16 (&s)[BN / 32][2], bool ext, int k
 constexpr int kFwdBN = 64;
 constexpr int kFwdTile = kFwdBN * kRowB;            // one K or V block
 constexpr int kFwdK = 0, kFwdV = 3 * kFwdTile;      // three K buffers, then three V buffers
-constexpr int kFwdDma = kFwdBN / 16;                // staging loads per wave per tile
-constexpr int kFwdExpB = 0;                         // key tiles of P exponentiated in phase B
+constexpr int kFwdNT = 1;                           // 32-row query tiles per wave
 
 // max(x[l], x[l ^ 32]) in every lane, without LDS
 __device__ __forceinline__ float max_halves(float x) {
@@ -523,8 +536,32 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-__global__ __launch_bounds__(kThreads, 1) void fwd_kernel(AttnArgs a) {
+// Register placement of the forward's accumulators.  With one wave per SIMD
+// (NT = 2) the wave has 512 registers and the long-lived O accumulators and Q
+// fragments go to the AGPR file through the asm product; with two waves per
+// SIMD (NT = 1) a wave has 256, and a kernel that uses any AGPR gets only half
+// of them as VGPRs, so everything stays in VGPRs and the builtin product
+// (whose hazards the compiler handles) is used.
+template <int NT>
+__device__ __forceinline__ void fence_acc_nt(f32x16 (&x)[kD / 32][NT]) {
+  if constexpr (NT == 2) fence_acc(x);
+}
+template <int NT>
+__device__ __forceinline__ void mfma_acc_nt(f32x16& acc, bf16x8 a, bf16x8 b) {
+  if constexpr (NT == 2)
+    mfma_acc(acc, a, b);
+  else
+    acc = mfma(a, b, acc);
+}
+
+template <int NT>
+__global__ __launch_bounds__(64 * 8 / NT, 1) void fwd_kernel(AttnArgs a) {
   constexpr int BN = kFwdBN;
+  constexpr int WAVES = 8 / NT;
+  constexpr int kDma = BN / (4 * WAVES);     // staging loads per wave per K or V tile
+  constexpr int VPS = 4 * NT;                // P (or maxima) values per lane per step
+  constexpr int KPD = NT == 1 ? 2 : 1;       // K fragment prefetch distance (steps)
+  constexpr int VPD = NT == 1 ? 3 : 2;       // V fragment prefetch distance (products)
   __shared__ __attribute__((aligned(16))) char smem[6 * kFwdTile];
   __shared__ __attribute__((aligned(16))) int32_t kend_s[3][BN];
   lds_t* const sb = (lds_t*)smem;
@@ -541,13 +578,15 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(AttnArgs a) {
   const int t0 = qt * tq;
   const int t1 = min(t0 + tq, a.rows);
 
-  // this lane's two query columns and their Q fragments (B operand of K Q^T,
+  // this lane's query columns and their Q fragments (B operand of K Q^T,
   // kept in AGPRs)
-  QCol qc[2];
-  bf16x8 qf[2][kD / 16];
+  QCol qc[NT];
+  int tok[NT];
+  bf16x8 qf[NT][kD / 16];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    qc[nt] = qcol(a, g, t0, tq, wave * 64 + nt * 32 + col);
+  for (int nt = 0; nt < NT; ++nt) {
+    qc[nt] = qcol(a, g, t0, tq, wave * 32 * NT + nt * 32 + col);
+    tok[nt] = qc[nt].tok;
     const __bf16* qp = (const __bf16*)a.q + (int64_t)qc[nt].tok * a.q_st +
                        (int64_t)qc[nt].head * a.q_sh + 8 * h32;
 #pragma unroll
@@ -555,11 +594,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(AttnArgs a) {
   }
   // all loads in flight before the first use
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt)
+  for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
     for (int ds = 0; ds < kD / 16; ++ds) {
       if (!qc[nt].valid) qf[nt][ds] = zero8();
-      pin_agpr(qf[nt][ds]);
+      if constexpr (NT == 2) pin_agpr(qf[nt][ds]);
     }
 
   KeyWalk<BN> walk;
@@ -579,28 +618,32 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(AttnArgs a) {
     f.init(ff);
   }
   const float c = a.scale_log2;
-  float mrow[2] = {-INFINITY, -INFINITY};   // running max (log2 units) in use
-  float lrow[2] = {0.f, 0.f};               // this lane's share of the row sums
-  f32x16 acc[kD / 32][2];
+  float mrow[NT], lrow[NT];                 // running max (log2 units) in use; row-sum share
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    mrow[nt] = -INFINITY;
+    lrow[nt] = 0.f;
+  }
+  f32x16 acc[kD / 32][NT];
 #pragma unroll
   for (int dt = 0; dt < kD / 32; ++dt)
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) acc[dt][nt] = zero16();
-  fence_acc(acc);
+    for (int nt = 0; nt < NT; ++nt) acc[dt][nt] = zero16();
+  fence_acc_nt<NT>(acc);
 
-  // S^T tile of the K block in `kt_s`: 64 keys x this wave's 64 queries
-  auto s_tile = [&](const lds_t* kt_s, f32x16 (&s)[BN / 32][2]) {
+  // S^T tile of the K block in `kt_s`: 64 keys x this wave's query columns
+  auto s_tile = [&](const lds_t* kt_s, f32x16 (&s)[BN / 32][NT]) {
 #pragma unroll
     for (int kt = 0; kt < BN / 32; ++kt)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) s[kt][nt] = zero16();
+      for (int nt = 0; nt < NT; ++nt) s[kt][nt] = zero16();
 #pragma unroll
     for (int ds = 0; ds < kD / 16; ++ds) {
 #pragma unroll
       for (int kt = 0; kt < BN / 32; ++kt) {
         const bf16x8 af = ld_row8(kt_s + kt * 32 * kRowB + f.row8(ds));
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) s[kt][nt] = mfma(af, qf[nt][ds], s[kt][nt]);
+        for (int nt = 0; nt < NT; ++nt) s[kt][nt] = mfma(af, qf[nt][ds], s[kt][nt]);
       }
     }
   };
@@ -612,52 +655,45 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(AttnArgs a) {
   };
   auto blk = [&](int b) { return Blk{b, b >= 0 && walk.masked(b, a.n_ext)}; };
   auto nxt = [&](Blk b) { return blk(b.id >= 0 ? walk.next(b.id + 1) : -1); };
-  auto mask_if = [&](f32x16 (&s)[BN / 32][2], Blk b, const int32_t* kend) {
+  auto mask_if = [&](f32x16 (&s)[BN / 32][NT], Blk b, const int32_t* kend) {
     if (b.masked)
-      mask_st<BN>(s, src.ext(b.id), src.k0(b.id), src.ext(b.id) ? a.n_ext : a.rows, kend,
-                  qc[0].tok, qc[1].tok, h32);
+      mask_st<BN, NT>(s, src.ext(b.id), src.k0(b.id), src.ext(b.id) ? a.n_ext : a.rows, kend,
+                      tok, h32);
   };
-  // row maxima of S (valid when `live`), the lazy move of the running maxima
-  // (only when a block exceeds them by more than kRescale, so probabilities
-  // stay below 2^kRescale), and exp2 of the first kFwdExpB key tiles.
-  // Returns the factors the accumulators must be scaled by.
-  auto softmax_head = [&](f32x16 (&s)[BN / 32][2], bool live, float (&alpha)[2]) {
+  // the lazy move of the running maxima to the block maxima mx (valid when
+  // `live`): only when a block exceeds them by more than kRescale, so
+  // probabilities stay below 2^kRescale.  Returns the factors the
+  // accumulators must be scaled by.
+  auto move_max = [&](const float (&mx)[NT], bool live, float (&alpha)[NT]) {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      float m = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < BN / 32; ++kt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) m = fmaxf(m, s[kt][nt][i]);
-      const float mh = max_halves(m) * c;
-      m = live ? mh : -INFINITY;
+    for (int nt = 0; nt < NT; ++nt) {
+      const float mh = max_halves(mx[nt]) * c;
+      const float m = live ? mh : -INFINITY;
       const bool grow = m > mrow[nt] + kRescale;
       const float mnew = grow ? m : mrow[nt];
       alpha[nt] = fast_exp2(grow ? mrow[nt] - mnew : 0.f);
       lrow[nt] *= alpha[nt];
       mrow[nt] = mnew;
-      const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-#pragma unroll
-      for (int kt = 0; kt < kFwdExpB; ++kt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s[kt][nt][i] = fast_exp2(fmaf(s[kt][nt][i], c, -muse));
     }
   };
-  auto rescale = [&](const float (&alpha)[2]) {
-    if (__builtin_amdgcn_ballot_w64(alpha[0] != 1.f || alpha[1] != 1.f) != 0) {
-      fence_acc(acc);
+  auto rescale = [&](const float (&alpha)[NT]) {
+    bool any = false;
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
+    for (int nt = 0; nt < NT; ++nt) any = any || alpha[nt] != 1.f;
+    if (__builtin_amdgcn_ballot_w64(any) != 0) {
+      fence_acc_nt<NT>(acc);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int dt = 0; dt < kD / 32; ++dt) acc[dt][nt] *= alpha[nt];
-      fence_acc(acc);
+      fence_acc_nt<NT>(acc);
     }
   };
   auto stage_k = [&](int b, int buf) {
-    src.dma_k(b, sb + kFwdK + buf * kFwdTile, wave, lane);
+    src.template dma_k<WAVES>(b, sb + kFwdK + buf * kFwdTile, wave, lane);
   };
   auto stage_v = [&](int b, int buf) {
-    src.dma_v(b, sb + kFwdV + buf * kFwdTile, wave, lane);
+    src.template dma_v<WAVES>(b, sb + kFwdV + buf * kFwdTile, wave, lane);
   };
   // visibility ends of an own block's keys into kend_s[buf], by one staging
   // load of wave 0 (keys past the end read 0: invisible)
@@ -686,18 +722,26 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(AttnArgs a) {
   }
   dma_wait();
   __syncthreads();
-  f32x16 sA[BN / 32][2], sB[BN / 32][2];
+  f32x16 sA[BN / 32][NT], sB[BN / 32][NT];
   if (b0.id >= 0) {
     s_tile(sb + kFwdK, sA);
     mask_if(sA, b0, kend_s[0]);
-    float alpha[2];
-    softmax_head(sA, true, alpha);
+    float mx[NT], alpha[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      mx[nt] = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < BN / 32; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx[nt] = fmaxf(mx[nt], sA[kt][nt][i]);
+    }
+    move_max(mx, true, alpha);
   }
 
-  // iteration j: block j's S in sc (maxima applied, first tiles
-  // exponentiated), its V in V buffer B, K of block j + 1 (n1) in K buffer
-  // B + 1.  Stages K of n3 into K buffer B and V of n2 into V buffer B + 2.
-  auto iter = [&](auto bc, f32x16 (&sc)[BN / 32][2], f32x16 (&sn)[BN / 32][2], Blk n1, Blk n2,
+  // iteration j: block j's S in sc (maxima applied), its V in V buffer B, K
+  // of block j + 1 (n1) in K buffer B + 1.  Stages K of n3 into K buffer B
+  // and V of n2 into V buffer B + 2.
+  auto iter = [&](auto bc, f32x16 (&sc)[BN / 32][NT], f32x16 (&sn)[BN / 32][NT], Blk n1, Blk n2,
                   Blk n3) {
     constexpr int B = decltype(bc)::value;
     constexpr int B1 = (B + 1) % 3, B2 = (B + 2) % 3;
@@ -710,11 +754,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(AttnArgs a) {
 
     // phase A: S^T of block j + 1 while P_j is completed and packed.  Eight
     // steps, one per 16-wide slice of head_dim: each issues the K fragments
-    // of the next step, its four products and one eighth of the P work; the
-    // scheduling fences keep that order, so every fragment read has four
-    // products' time to land.
+    // KPD steps ahead, its products and one eighth of the P work; the
+    // scheduling fences keep that order.
     const lds_t* kt_s = sb + kFwdK + B1 * kFwdTile;
-    bf16x8 kfr[2][BN / 32];
+    bf16x8 kfr[KPD + 1][BN / 32];
     auto ldk = [&](int ds, bf16x8 (&dst)[BN / 32]) {
 #pragma unroll
       for (int kt = 0; kt < BN / 32; ++kt) dst[kt] = ld_row8(kt_s + kt * 32 * kRowB + f.row8(ds));
@@ -722,102 +765,92 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(AttnArgs a) {
 #pragma unroll
     for (int kt = 0; kt < BN / 32; ++kt)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) sn[kt][nt] = zero16();
-    bf16x8 pb[2][BN / 16];
-    float ls[2] = {0.f, 0.f};
-    const float muse0 = (mrow[0] == -INFINITY) ? 0.f : mrow[0];
-    const float muse1 = (mrow[1] == -INFINITY) ? 0.f : mrow[1];
-    ldk(0, kfr[0]);
+      for (int nt = 0; nt < NT; ++nt) sn[kt][nt] = zero16();
+    bf16x8 pb[NT][BN / 16];
+    float ls[NT], muse[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      ls[nt] = 0.f;
+      muse[nt] = (mrow[nt] == -INFINITY) ? 0.f : mrow[nt];
+    }
+#pragma unroll
+    for (int d0 = 0; d0 < KPD; ++d0) ldk(d0, kfr[d0]);
     static_for<0, kD / 16>([&](auto dsc) {
       constexpr int ds = decltype(dsc)::value;
-      if constexpr (ds + 1 < kD / 16) ldk(ds + 1, kfr[(ds + 1) & 1]);
+      if constexpr (ds + KPD < kD / 16) ldk(ds + KPD, kfr[(ds + KPD) % (KPD + 1)]);
 #pragma unroll
       for (int kt = 0; kt < BN / 32; ++kt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) sn[kt][nt] = mfma(kfr[ds & 1][kt], qf[nt][ds], sn[kt][nt]);
-      // P slice ds: query column nt, key tile kt, half h (8 values)
-      constexpr int nt = ds >> 2, kt = (ds >> 1) & 1, h = ds & 1;
-      const float muse = nt ? muse1 : muse0;
+        for (int nt = 0; nt < NT; ++nt)
+          sn[kt][nt] = mfma(kfr[ds % (KPD + 1)][kt], qf[nt][ds], sn[kt][nt]);
+      // P values ds * VPS .. ds * VPS + VPS - 1 in (column, key tile, value) order
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float p = sc[kt][nt][8 * h + e];
-        if (kt >= kFwdExpB) p = fast_exp2(fmaf(p, c, -muse));
-        sc[kt][nt][8 * h + e] = p;
+      for (int e = 0; e < VPS; ++e) {
+        const int lin = ds * VPS + e, nt = lin >> 5, kt = (lin >> 4) & 1, i = lin & 15;
+        const float p = fast_exp2(fmaf(sc[kt][nt][i], c, -muse[nt]));
+        sc[kt][nt][i] = p;
         ls[nt] += p;
+        if ((i & 7) == 7) {
+          pb[nt][2 * kt + (i >> 3)] = pack_half(sc[kt][nt], i >> 3);
+          // the half is formed here, not sunk towards its use in phase B
+          asm volatile("" : "+v"(pb[nt][2 * kt + (i >> 3)]));
+        }
       }
-      pb[nt][2 * kt + h] = pack_half(sc[kt][nt], h);
-      // the slice is formed here, not sunk towards its use in phase B
-      asm volatile("" : "+v"(pb[nt][2 * kt + h]), "+v"(ls[nt]));
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) asm volatile("" : "+v"(ls[nt]));
       __builtin_amdgcn_sched_barrier(0);
     });
-    lrow[0] += ls[0];
-    lrow[1] += ls[1];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) lrow[nt] += ls[nt];
     mask_if(sn, n1, kend_s[B1]);
 
-    // phase B: O^T += V_j^T P_j^T while the maxima of S_{j+1} are taken and
-    // its first exponentials formed.  Sixteen steps, one per V fragment
-    // (fetched two steps ahead), each with two products and a sixteenth of
-    // that VALU work.
+    // phase B: O^T += V_j^T P_j^T while the maxima of S_{j+1} are taken.
+    // Sixteen steps, one per V fragment (fetched VPD steps ahead), each with
+    // NT products and a sixteenth of that VALU work.
     const lds_t* vt_s = sb + kFwdV + B * kFwdTile;
     auto ldv = [&](int fi) {
       const int dt = fi >> 2, ks = fi & 3;
       const lds_t* vb = vt_s + ks * 16 * kRowB;
       return ld_tr(vb + f.tr(dt, 0), vb + f.tr(dt, 1));
     };
-    bf16x8 vfr[3];
-    vfr[0] = ldv(0);
-    vfr[1] = ldv(1);
-    float mx[2] = {-INFINITY, -INFINITY};
-    float alpha[2] = {1.f, 1.f};
-    float musen[2] = {0.f, 0.f};
+    bf16x8 vfr[VPD + 1];
+#pragma unroll
+    for (int f0 = 0; f0 < VPD; ++f0) vfr[f0] = ldv(f0);
+    float mx[NT], alpha[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      mx[nt] = -INFINITY;
+      alpha[nt] = 1.f;
+    }
     const bool live = n1.id >= 0;
     static_for<0, kD / 32 * BN / 16>([&](auto fic) {
       constexpr int fi = decltype(fic)::value;
       constexpr int dt = fi >> 2, ks = fi & 3;
-      if constexpr (fi + 2 < kD / 32 * BN / 16) vfr[(fi + 2) % 3] = ldv(fi + 2);
-      mfma_acc(acc[dt][0], vfr[fi % 3], pb[0][ks]);
-      mfma_acc(acc[dt][1], vfr[fi % 3], pb[1][ks]);
+      if constexpr (fi + VPD < kD / 32 * BN / 16) vfr[(fi + VPD) % (VPD + 1)] = ldv(fi + VPD);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) mfma_acc_nt<NT>(acc[dt][nt], vfr[fi % (VPD + 1)], pb[nt][ks]);
       if constexpr (fi < 8) {
-        // maxima: step fi covers column fi / 4, key tile (fi / 2) & 1, half fi & 1
-        constexpr int nt = fi >> 2, kt = (fi >> 1) & 1, h = fi & 1;
+        // maxima: values fi * VPS .. in (column, key tile, value) order
 #pragma unroll
-        for (int e = 0; e < 8; ++e) mx[nt] = fmaxf(mx[nt], sn[kt][nt][8 * h + e]);
-        asm volatile("" : "+v"(mx[nt]));
+        for (int e = 0; e < VPS; ++e) {
+          const int lin = fi * VPS + e, nt = lin >> 5, kt = (lin >> 4) & 1, i = lin & 15;
+          mx[nt] = fmaxf(mx[nt], sn[kt][nt][i]);
+        }
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) asm volatile("" : "+v"(mx[nt]));
       } else if constexpr (fi == 8) {
-        // lazy move of the running maxima: only when a block exceeds them by
-        // more than kRescale, so probabilities stay below 2^kRescale
+        move_max(mx, live, alpha);
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          const float mh = max_halves(mx[nt]) * c;
-          const float m = live ? mh : -INFINITY;
-          const bool grow = m > mrow[nt] + kRescale;
-          const float mnew = grow ? m : mrow[nt];
-          alpha[nt] = fast_exp2(grow ? mrow[nt] - mnew : 0.f);
-          lrow[nt] *= alpha[nt];
-          mrow[nt] = mnew;
-          musen[nt] = (mnew == -INFINITY) ? 0.f : mnew;
-        }
-        asm volatile("" : "+v"(musen[0]), "+v"(musen[1]), "+v"(lrow[0]), "+v"(lrow[1]));
-      } else {
-        // exponentials of the first kFwdExpB key tiles, 32 kFwdExpB values
-        // over steps 9..15
-        constexpr int n_e = 32 * kFwdExpB, per = (n_e + 6) / 7;
-        constexpr int e0 = (fi - 9) * per;
-#pragma unroll
-        for (int e = e0; e < e0 + per && e < n_e; ++e) {
-          const int nt = e & 1, kt = e >> 5, i = (e >> 1) & 15;
-          sn[kt][nt][i] = fast_exp2(fmaf(sn[kt][nt][i], c, -musen[nt]));
-          asm volatile("" : "+v"(sn[kt][nt][i]));
-        }
+        for (int nt = 0; nt < NT; ++nt) asm volatile("" : "+v"(lrow[nt]), "+v"(mrow[nt]));
       }
       __builtin_amdgcn_sched_barrier(0);
     });
     rescale(alpha);
 
     if (n3.id >= 0) {
-      dma_wait_n<2 * kFwdDma>();
+      dma_wait_n<2 * kDma>();
     } else if (n2.id >= 0) {
-      dma_wait_n<kFwdDma>();
+      dma_wait_n<kDma>();
     } else {
       dma_wait();
     }
@@ -852,9 +885,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(AttnArgs a) {
   }
 
   // finalize: O = acc / l, LSE = (m + log2 l) ln 2
-  fence_acc(acc);
+  fence_acc_nt<NT>(acc);
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
+  for (int nt = 0; nt < NT; ++nt) {
     const float l = sum_halves(lrow[nt]);
     const float inv = (l > 0.f) ? 1.f / l : 0.f;
     if (!qc[nt].valid) continue;
@@ -960,6 +993,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(AttnArgs a) {
       pin_agpr(df[nt][ds]);
     }
 
+  const int toks[2] = {qc[0].tok, qc[1].tok};
   KeyWalk<BN> walk;
   walk.n_ext_blocks = (a.n_ext + BN - 1) / BN;
   walk.t0 = t0;
@@ -1090,8 +1124,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(AttnArgs a) {
   if (b0.id >= 0) {
     sdp(0, sA, dpA, [&](auto) {});
     if (b0.masked)
-      mask_st<BN>(sA, src.ext(b0.id), src.k0(b0.id),
-                  src.ext(b0.id) ? a.n_ext : a.rows, kend_s[0], qc[0].tok, qc[1].tok, h32);
+      mask_st<BN, 2>(sA, src.ext(b0.id), src.k0(b0.id),
+                     src.ext(b0.id) ? a.n_ext : a.rows, kend_s[0], toks, h32);
   }
 
   // iteration for block j in buffer bj with (sc, dpc) = its S^T, dP^T and
@@ -1113,8 +1147,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(AttnArgs a) {
       });
     });
     if (n1.masked)
-      mask_st<BN>(sn, src.ext(n1.id), src.k0(n1.id),
-                  src.ext(n1.id) ? a.n_ext : a.rows, kend_s[b1i], qc[0].tok, qc[1].tok, h32);
+      mask_st<BN, 2>(sn, src.ext(n1.id), src.k0(n1.id),
+                     src.ext(n1.id) ? a.n_ext : a.rows, kend_s[b1i], toks, h32);
     // phase B
     dq_prod(bpi, dsp, [&](auto kc) {
       constexpr int k = decltype(kc)::value;
@@ -1940,7 +1974,8 @@ hipError_t launch_fwd_bf16(const AttnArgs& a, int32_t head_dim, hipStream_t stre
   if (a.rows <= 0) return hipSuccess;
   const int tq = kRowsPerWg / a.group;
   const int n_qt = (a.rows + tq - 1) / tq;
-  PF_LAUNCH("pf_fwd_bf16", fwd_kernel, dim3(grid_for(a.hkv, n_qt)), dim3(kThreads), stream, a);
+  PF_LAUNCH("pf_fwd_bf16", fwd_kernel<kFwdNT>, dim3(grid_for(a.hkv, n_qt)),
+            dim3(64 * 8 / kFwdNT), stream, a);
   return hipGetLastError();
 }
 
