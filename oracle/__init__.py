@@ -13,7 +13,9 @@ identity, prefix-gradient superposition via a packed-graph formulation,
 GQA = MHA with repeated K/V, tree expanded-vs-direct, the reductions of
 trees to flat groups and causal chains, and tree windows over a prefix
 against per-trajectory flat Phase B (expansion with a split upstream), a
-chain tree as one flat suffix, and P = 0 as a plain tree; compact
+chain tree as one flat suffix, and P = 0 as a plain tree; a window over a
+producer tree's ancestor rows with the producer backward against direct
+attention over the combined tree; compact
 log-probabilities against torch log_softmax and autograd on the expanded
 per-position logits, and scipy's logsumexp.
 
@@ -39,8 +41,10 @@ from .phases import (
     suffix_attention_full_rows,
     tree_attention_direct,
     tree_attention_expanded,
+    tree_backward_inject,
     tree_trajectories,
     tree_window_attention,
+    tree_window_attention_ranges,
 )
 
 __all__ = [
@@ -61,4 +65,6 @@ __all__ = [
     "tree_attention_expanded",
     "tree_trajectories",
     "tree_window_attention",
+    "tree_window_attention_ranges",
+    "tree_backward_inject",
 ]

@@ -237,3 +237,43 @@ def tree_window_attention(k_p, v_p, q, k, v, do, node_off, parent, scale, hmap,
         out.update(dq=dq, dk=dk_all[p:], dv=dv_all[p:], gk=dk_all[:p], gv=dv_all[:p])
     return out
 
+
+
+def tree_window_attention_ranges(k_c, v_c, ranges, q, k, v, do, node_off, parent, scale, hmap,
+                                 dtype=np.float64, backward=True) -> Dict[str, np.ndarray]:
+    """A sharing window whose cached rows are row ranges of a producer's
+    compact rows (HARTS §3.4, "Window-scoped reuse and backward": the producer
+    caches ancestor K/V; each internal node of a rollout tree can carry such a
+    cache, so a consumer attached under node u reads the rows of u and of its
+    ancestors).
+
+    `ranges` lists (start, length) spans of k_c / v_c [C_prod, Hkv, d]; their
+    rows, concatenated in list order, precede the window's rows in every
+    window trajectory.  By the definition of the gather: gather those rows,
+    run `tree_window_attention` over them, and add the gathered rows'
+    gradients back into the producer rows they came from (the gather's
+    backward sums into the shared rows).  gk, gv are [C_prod, Hkv, d]."""
+    idx = [np.arange(int(s), int(s) + int(n)) for s, n in ranges]
+    rows = np.concatenate(idx) if idx else np.zeros(0, dtype=np.int64)
+    res = tree_window_attention(k_c[rows], v_c[rows], q, k, v, do, node_off, parent, scale, hmap,
+                                dtype, backward)
+    if backward:
+        gk = np.zeros(k_c.shape, dtype)
+        gv = np.zeros(v_c.shape, dtype)
+        np.add.at(gk, rows, res["gk"])
+        np.add.at(gv, rows, res["gv"])
+        res["gk"], res["gv"] = gk, gv
+    return res
+
+
+def tree_backward_inject(q, k, v, do, node_off, parent, gk_acc, gv_acc, scale, hmap,
+                         dtype=np.float64):
+    """The producer backward of a rollout tree whose rows were read by consumer
+    windows (HARTS §3.4: the consumers' interface gradients are accumulated
+    before the one producer backward): the tree backward under upstream dO,
+    with gK/gV added to the K/V gradients of the compact rows.
+    Returns (dQ, dK + gK_acc, dV + gV_acc)."""
+    if do is None:
+        do = np.zeros(q.shape, dtype)
+    r = tree_attention_direct(q, k, v, do, node_off, parent, scale, hmap, dtype)
+    return r["dq"], r["dk"] + gk_acc, r["dv"] + gv_acc

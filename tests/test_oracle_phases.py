@@ -27,10 +27,19 @@ from oracle import (
     tree_ancestor_mask,
     tree_attention_direct,
     tree_attention_expanded,
+    tree_backward_inject,
     tree_trajectories,
     tree_window_attention,
+    tree_window_attention_ranges,
 )
-from workloads.gen import random_small_group, random_tree, random_tree_group, tree_layout
+from workloads.gen import (
+    ancestor_row_ranges,
+    node_depths,
+    random_small_group,
+    random_tree,
+    random_tree_group,
+    tree_layout,
+)
 
 
 def _group(seed=0, hq=4, hkv=2, d=8, p=5, lens=(1, 2, 4), scale_q=1.0):
@@ -354,3 +363,49 @@ def test_tree_window_without_prefix_is_a_tree():
         np.testing.assert_allclose(a[key], b[key], atol=1e-12, err_msg=key)
     assert a["gk"].shape[0] == 0
 
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+def test_window_over_producer_ancestors_equals_combined_tree(seed):
+    """A consumer window attached under an internal node u of a producer tree,
+    reading the rows of u and its ancestors as its cached rows, then the
+    producer backward with the window's gK/gV injected, equals plain attention
+    over the combined tree in which the consumer's root is a child of u (the
+    ancestor mask over all compact rows, HARTS §2.2): the consumer rows'
+    outputs and gradients, and the producer rows' outputs and gradients."""
+    rng = np.random.default_rng(seed)
+    node_off_p, parent_p = random_tree(50 + seed, 7, max_len=5, min_len=1)
+    depth = node_depths(parent_p)
+    cand = [v for v in range(len(parent_p)) if depth[v] >= 1]
+    u = int(cand[seed % len(cand)])
+    ranges = ancestor_row_ranges(node_off_p, parent_p, u)
+    node_off_c, parent_c = random_tree(80 + seed, 5, max_len=4, min_len=1)
+    hq, hkv, d = 4, 2, 8
+    hmap = head_map(hq, hkv)
+    cp, cc = int(node_off_p[-1]), int(node_off_c[-1])
+    gp = {k: rng.standard_normal((cp, hq if k in ("q", "do") else hkv, d)) for k in "q k v do".split()}
+    gc = {k: rng.standard_normal((cc, hq if k in ("q", "do") else hkv, d)) for k in "q k v do".split()}
+    win = tree_window_attention_ranges(gp["k"], gp["v"], ranges, gc["q"], gc["k"], gc["v"],
+                                       gc["do"], node_off_c, parent_c, 0.35, hmap)
+    prod = tree_attention_direct(gp["q"], gp["k"], gp["v"], gp["do"], node_off_p, parent_p, 0.35,
+                                 hmap)
+    dq_p, dk_p, dv_p = tree_backward_inject(gp["q"], gp["k"], gp["v"], gp["do"], node_off_p,
+                                            parent_p, win["gk"], win["gv"], 0.35, hmap)
+    # the combined tree: producer nodes, then the consumer's, its root under u
+    n_p = len(parent_p)
+    parent = np.concatenate([parent_p, np.where(parent_c < 0, u, parent_c + n_p)]).astype(np.int32)
+    node_off = np.concatenate([node_off_p, node_off_c[1:] + cp]).astype(np.int32)
+    both = {k: np.concatenate([gp[k], gc[k]], axis=0) for k in gp}
+    full = tree_attention_direct(both["q"], both["k"], both["v"], both["do"], node_off, parent,
+                                 0.35, hmap)
+    for key in ("o", "dq", "dk", "dv"):
+        np.testing.assert_allclose(win[key], full[key][cp:], atol=1e-12, err_msg=key)
+    np.testing.assert_allclose(win["lse"], full["lse"][:, cp:], atol=1e-12)
+    np.testing.assert_allclose(prod["o"], full["o"][:cp], atol=1e-12)
+    for key, got in (("dq", dq_p), ("dk", dk_p), ("dv", dv_p)):
+        np.testing.assert_allclose(got, full[key][:cp], atol=1e-12, err_msg=key)
+    # rows outside the ranges receive no gradient from the window
+    used = np.zeros(cp, dtype=bool)
+    for s, n in ranges:
+        used[s:s + n] = True
+    assert np.all(win["gk"][~used] == 0) and np.abs(win["gk"][used]).max() > 0

@@ -251,3 +251,21 @@ def tree_paths(node_off: np.ndarray, parent: np.ndarray) -> List[np.ndarray]:
         paths.append(np.concatenate([np.arange(node_off[u], node_off[u + 1]) for u in reversed(chain)]))
     return paths
 
+
+
+def ancestor_row_ranges(node_off: np.ndarray, parent: np.ndarray, u: int):
+    """(start, length) of the compact rows of node u and of each of its
+    ancestors, root first: the rows a consumer window attached under u reads
+    (in trajectory order)."""
+    chain = []
+    while u >= 0:
+        chain.append(int(u))
+        u = int(parent[u])
+    return [(int(node_off[a]), int(node_off[a + 1] - node_off[a])) for a in reversed(chain)]
+
+
+def node_depths(parent: np.ndarray) -> np.ndarray:
+    d = np.zeros(len(parent), dtype=np.int64)
+    for v in range(1, len(parent)):
+        d[v] = d[parent[v]] + 1
+    return d
