@@ -24,7 +24,11 @@
  *   Windows  pf_tree_suffix_attn_fwd,  a window of rollout trees over a cached
  *            pf_tree_suffix_attn_bwd_accum  prefix, with the prefix-side
  *                                      gradients accumulated (HARTS §3.4,
- *                                      window-scoped reuse and backward).
+ *                                      window-scoped reuse and backward);
+ *            ..._ranges variants       the cached rows as row ranges of a
+ *                                      producer tree (its ancestor rows), and
+ *            pf_tree_attn_bwd_inject   the producer tree's backward with the
+ *                                      accumulated gradients injected.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -273,6 +277,63 @@ pf_status pf_tree_suffix_attn_bwd_accum(const pf_attn_desc* desc, int32_t prefix
                                         const float* lse, pf_tensor dout, pf_tensor dq,
                                         pf_tensor dk, pf_tensor dv, float* gk_acc, float* gv_acc,
                                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* A sharing window whose cached rows are row ranges of a producer's compact
+ * rows, read in place ("HARTS", §3.4, window-scoped reuse: each internal node
+ * of a rollout tree can carry the K/V cache of its ancestor rows, so a
+ * consumer window attached under node u reads the rows of u and of every
+ * ancestor of u, and its backward adds the interface gradients into exactly
+ * those rows before the one producer backward).  Same as
+ * pf_tree_suffix_attn_fwd, except that the cached rows are, in trajectory
+ * order, the ranges [range_start[i], range_start[i] + range_len[i]) of k_c
+ * and v_c instead of one prefix block; nothing is gathered or copied.
+ *   k_c, v_c [c_rows, Hkv, d]             in  (the producer's compact K/V)
+ *   n_ranges <= PF_MAX_SEGMENTS; range_start, range_len host [n_ranges]  in
+ *     (inside [0, c_rows); empty ranges are ignored)
+ *   (tree and window tensors as for pf_tree_suffix_attn_fwd)
+ * Workspace: pf_workspace_size(PF_OP_TREE_SUFFIX_FWD, desc, prefix_len, C)
+ * with prefix_len = pf_ranges_cached_keys(n_ranges, range_len).
+ * bf16 only (PF_ERR_UNSUPPORTED for fp32).                                  */
+pf_status pf_tree_suffix_attn_fwd_ranges(const pf_attn_desc* desc, int32_t c_rows, pf_tensor k_c,
+                                         pf_tensor v_c, int32_t n_ranges,
+                                         const int32_t* range_start, const int32_t* range_len,
+                                         int32_t n_nodes, const int32_t* node_off,
+                                         const int32_t* parent, pf_tensor q, pf_tensor k,
+                                         pf_tensor v, pf_tensor o, float* lse, void* workspace,
+                                         size_t workspace_bytes, void* stream);
+
+/* Backward of pf_tree_suffix_attn_fwd_ranges: dQ, dK, dV of the window rows
+ * (overwritten) and the window's gradients of the cached rows ADDED into
+ * rows of gk_acc, gv_acc fp32 [c_rows, Hkv, d]: cached row r of range i
+ * adds into row r, so windows under different nodes of one producer add into
+ * the shared ancestor rows.  Workspace as for the forward, with
+ * PF_OP_TREE_SUFFIX_BWD.                                                    */
+pf_status pf_tree_suffix_attn_bwd_accum_ranges(
+    const pf_attn_desc* desc, int32_t c_rows, pf_tensor k_c, pf_tensor v_c, int32_t n_ranges,
+    const int32_t* range_start, const int32_t* range_len, int32_t n_nodes,
+    const int32_t* node_off, const int32_t* parent, pf_tensor q, pf_tensor k, pf_tensor v,
+    pf_tensor o, const float* lse, pf_tensor dout, pf_tensor dq, pf_tensor dk, pf_tensor dv,
+    float* gk_acc, float* gv_acc, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The padded cached-key count of a ranges call: the sum over ranges of
+ * range_len rounded up to 32 (the prefix_len that sizes its workspace);
+ * -1 for invalid arguments.  Host arithmetic only.                          */
+int32_t pf_ranges_cached_keys(int32_t n_ranges, const int32_t* range_len);
+
+/* The producer backward of a rollout tree whose rows were read by consumer
+ * windows ("HARTS", §3.4: the consumers' interface gradients are accumulated
+ * before the one producer backward): pf_tree_attn_bwd with gk_acc, gv_acc
+ * fp32 [C, Hkv, d] added to the rows' K/V gradients in fp32 before the one
+ * rounding, as pf_prefix_bwd_inject does for a flat prefix.
+ *   dout.data == NULL means a zero upstream (dQ = 0, dK = gK, dV = gV)
+ *   dq [C, Hq, d] (desc dtype); dk, dv [C, Hkv, d] (dkv_dtype: PF_F32 or
+ *   the desc dtype)                                          out (overwritten) */
+pf_status pf_tree_attn_bwd_inject(const pf_attn_desc* desc, int32_t n_nodes,
+                                  const int32_t* node_off, const int32_t* parent, pf_tensor q,
+                                  pf_tensor k, pf_tensor v, pf_tensor o, const float* lse,
+                                  pf_tensor dout, const float* gk_acc, const float* gv_acc,
+                                  pf_tensor dq, pf_tensor dk, pf_tensor dv, int32_t dkv_dtype,
+                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /* Compact log-probability recovery ("HARTS" §3.5): logits exist once per
  * compact row; each semantic position s reads its row m(s) and target y_s,

@@ -27,7 +27,9 @@ PF_NOALLOC_SCRATCH_BYTES = 16 << 20
 EXPORTED = (
     "pf_workspace_size", "pf_workspace_size_min", "pf_prefix_fwd", "pf_suffix_attn_fwd", "pf_suffix_attn_bwd_accum",
     "pf_suffix_attn_bwd_accum_noalloc", "pf_prefix_bwd_inject", "pf_tree_attn_fwd", "pf_tree_attn_bwd", "pf_tree_suffix_attn_fwd",
-    "pf_tree_suffix_attn_bwd_accum", "pf_compact_logprob_fwd", "pf_compact_logprob_bwd",
+    "pf_tree_suffix_attn_bwd_accum", "pf_tree_suffix_attn_fwd_ranges",
+    "pf_tree_suffix_attn_bwd_accum_ranges", "pf_ranges_cached_keys", "pf_tree_attn_bwd_inject",
+    "pf_compact_logprob_fwd", "pf_compact_logprob_bwd",
     "pf_tree_subtree_end",
     "pf_status_string", "pf_last_error", "pf_abi_version", "pf_set_launch_hook",
 )
@@ -88,6 +90,13 @@ def _load():
         "pf_tree_suffix_attn_fwd": (i32, [D, i32, T, T, i32, ip, ip, T, T, T, T, fp, P, sz, P]),
         "pf_tree_suffix_attn_bwd_accum": (i32, [D, i32, T, T, i32, ip, ip, T, T, T, T, fp, T, T, T,
                                                 T, fp, fp, P, sz, P]),
+        "pf_tree_suffix_attn_fwd_ranges": (i32, [D, i32, T, T, i32, ip, ip, i32, ip, ip, T, T, T, T,
+                                                 fp, P, sz, P]),
+        "pf_tree_suffix_attn_bwd_accum_ranges": (i32, [D, i32, T, T, i32, ip, ip, i32, ip, ip, T, T,
+                                                       T, T, fp, T, T, T, T, fp, fp, P, sz, P]),
+        "pf_ranges_cached_keys": (i32, [i32, ip]),
+        "pf_tree_attn_bwd_inject": (i32, [D, i32, ip, ip, T, T, T, T, fp, T, fp, fp, T, T, T, i32,
+                                          P, sz, P]),
         "pf_compact_logprob_fwd": (i32, [i32, i32, P, ctypes.c_int64, i32, P, P, P, i32, fp, fp,
                                          P]),
         "pf_compact_logprob_bwd": (i32, [i32, i32, P, ctypes.c_int64, i32, fp, P, P, P, i32, fp,
@@ -291,6 +300,53 @@ def pf_tree_suffix_attn_bwd_accum(desc, prefix_len, k_p, v_p, node_off, parent, 
         ctypes.byref(d), prefix_len, _t(k_p), _t(v_p), len(pa), no_p, pa_p, _t(q), _t(k), _t(v),
         _t(o), _p(lse), _t(dout), _t(dq), _t(dk), _t(dv), _p(gk_acc), _p(gv_acc), ws, nws,
         _stream(stream)))
+
+
+def pf_ranges_cached_keys(range_len) -> int:
+    ln, ln_p = _ints(range_len)
+    n = int(_lib.pf_ranges_cached_keys(len(ln), ln_p))
+    if n < 0:
+        raise PFError(PF_ERR_INVALID_ARG, "invalid range lengths")
+    return n
+
+
+def pf_tree_suffix_attn_fwd_ranges(desc, k_c, v_c, range_start, range_len, node_off, parent, q, k,
+                                   v, o, lse, workspace, stream=None):
+    d, _keep = desc._c()
+    rs, rs_p = _ints(range_start)
+    rl, rl_p = _ints(range_len)
+    no, no_p = _ints(node_off)
+    pa, pa_p = _ints(parent)
+    ws, nws = _ws(workspace)
+    _check(_lib.pf_tree_suffix_attn_fwd_ranges(
+        ctypes.byref(d), k_c.shape[0], _t(k_c), _t(v_c), len(rs), rs_p, rl_p, len(pa), no_p, pa_p,
+        _t(q), _t(k), _t(v), _t(o), _p(lse), ws, nws, _stream(stream)))
+
+
+def pf_tree_suffix_attn_bwd_accum_ranges(desc, k_c, v_c, range_start, range_len, node_off, parent,
+                                         q, k, v, o, lse, dout, dq, dk, dv, gk_acc, gv_acc,
+                                         workspace, stream=None):
+    d, _keep = desc._c()
+    rs, rs_p = _ints(range_start)
+    rl, rl_p = _ints(range_len)
+    no, no_p = _ints(node_off)
+    pa, pa_p = _ints(parent)
+    ws, nws = _ws(workspace)
+    _check(_lib.pf_tree_suffix_attn_bwd_accum_ranges(
+        ctypes.byref(d), k_c.shape[0], _t(k_c), _t(v_c), len(rs), rs_p, rl_p, len(pa), no_p, pa_p,
+        _t(q), _t(k), _t(v), _t(o), _p(lse), _t(dout), _t(dq), _t(dk), _t(dv), _p(gk_acc),
+        _p(gv_acc), ws, nws, _stream(stream)))
+
+
+def pf_tree_attn_bwd_inject(desc, node_off, parent, q, k, v, o, lse, dout, gk_acc, gv_acc, dq, dk,
+                            dv, dkv_dtype, workspace, stream=None):
+    d, _keep = desc._c()
+    no, no_p = _ints(node_off)
+    pa, pa_p = _ints(parent)
+    ws, nws = _ws(workspace)
+    _check(_lib.pf_tree_attn_bwd_inject(
+        ctypes.byref(d), len(pa), no_p, pa_p, _t(q), _t(k), _t(v), _t(o), _p(lse), _t(dout),
+        _p(gk_acc), _p(gv_acc), _t(dq), _t(dk), _t(dv), dkv_dtype, ws, nws, _stream(stream)))
 
 
 def _dtype_of(t):

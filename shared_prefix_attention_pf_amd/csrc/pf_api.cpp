@@ -143,6 +143,34 @@ pf_status check_tree(int32_t n, const int32_t* node_off, const int32_t* parent, 
   return PF_OK;
 }
 
+// Row ranges of a producer tensor of c_rows rows as the external keys of a
+// window call: empty ranges are dropped, the rest padded to whole 32-key
+// tiles; *n_virtual is the padded key count (the prefix_len that sizes the
+// call's workspace).
+pf_status check_ranges(int32_t n, const int32_t* start, const int32_t* len, int32_t c_rows,
+                       pf::RangeTable* rt, int32_t* n_virtual) {
+  if (n < 0) return fail(PF_ERR_INVALID_ARG, "n_ranges is negative");
+  if (n > PF_MAX_SEGMENTS) return fail(PF_ERR_UNSUPPORTED, "more than %d cached row ranges", PF_MAX_SEGMENTS);
+  if (n > 0 && (!start || !len)) return fail(PF_ERR_INVALID_ARG, "range_start or range_len is NULL");
+  if (c_rows < 0) return fail(PF_ERR_INVALID_ARG, "c_rows is negative");
+  rt->n = 0;
+  rt->vt0[0] = 0;
+  for (int i = 0; i < n; ++i) {
+    if (start[i] < 0 || len[i] < 0 || (int64_t)start[i] + len[i] > c_rows)
+      return fail(PF_ERR_INVALID_ARG, "range %d = [%d, %d + %d) is outside the %d producer rows", i,
+                  start[i], start[i], len[i], c_rows);
+    if (len[i] == 0) continue;
+    const int j = rt->n++;
+    rt->start[j] = start[i];
+    rt->len[j] = len[i];
+    rt->vt0[j + 1] = rt->vt0[j] + (len[i] + 31) / 32;
+  }
+  const int64_t nv = 32 * (int64_t)rt->vt0[rt->n];
+  if (nv >= ((int64_t)1 << 30)) return fail(PF_ERR_UNSUPPORTED, "too many cached rows");
+  *n_virtual = (int32_t)nv;
+  return PF_OK;
+}
+
 pf_status check_stream_ws(void* ws, size_t ws_bytes, size_t need) {
   if (need == 0) return PF_OK;
   if (!ws) return fail(PF_ERR_WORKSPACE, "workspace is NULL but %zu bytes are needed", need);
@@ -190,6 +218,7 @@ pf_status scratch_of_current_device(void** out) {
 
 struct WsLayout {
   size_t kend = 0, bmax = 0, bmin = 0, qhead = 0, dsum = 0, lse2 = 0, gk_part = 0, gv_part = 0;
+  size_t ext_tiles = 0;   // window ops: (first row, valid rows) per 32 cached keys
   size_t total = 0;
   size_t dk_part = 0, dv_part = 0;
   int32_t n_chunks = 1, n_chunks_own = 1;
@@ -222,6 +251,10 @@ WsLayout layout(int32_t op, const Desc& d, int32_t n_ext, int32_t rows, bool wan
   w.bmax = off; off += align_up(nb * 4);
   w.bmin = off; off += align_up(nb * 4);
   w.qhead = off; off += align_up((size_t)d.hq * 4);
+  if (op == PF_OP_TREE_SUFFIX_FWD || op == PF_OP_TREE_SUFFIX_BWD) {
+    w.ext_tiles = off;
+    off += align_up((size_t)(n_ext + 31) / 32 * 8);
+  }
   const bool bwd = op == PF_OP_SUFFIX_BWD || op == PF_OP_PREFIX_BWD || op == PF_OP_TREE_BWD ||
                    op == PF_OP_TREE_SUFFIX_BWD;
   if (bwd) {
@@ -275,6 +308,14 @@ void set_ds(pf::AttnArgs& a, void* ws, const WsLayout& w) {
   a.ds_keys = w.ds_keys;
   a.ds_rows = w.ds_rows;
   a.ds_own0 = w.ds_own0;
+}
+
+// the tile table of a call whose external keys are row ranges
+void set_tiles(pf::AttnArgs& a, void* ws, const WsLayout& w, const pf::RangeTable* rt,
+               int32_t c_rows) {
+  if (!rt) return;
+  a.ext_tiles = (const int2*)((char*)ws + w.ext_tiles);
+  a.ext_rows = c_rows;
 }
 
 // the full layout (with the dS^T buffer) when the workspace holds it, else
@@ -355,7 +396,17 @@ pf::SegTable tree_segments(int32_t n, const int32_t* node_off, const int32_t* su
 
 // ------------------------------------------------------------- launches
 
-pf_status run_fwd(const Desc& d, const pf::AttnArgs& a, const pf::SegTable& seg, hipStream_t st) {
+// the tile table of a call whose external keys are row ranges (no-op otherwise)
+pf_status run_tiles(const pf::RangeTable* rt, const pf::AttnArgs& a, hipStream_t st) {
+  if (!rt || !a.ext_tiles) return PF_OK;
+  const hipError_t e = pf::launch_ext_tiles(*rt, const_cast<int2*>(a.ext_tiles), st);
+  return e == hipSuccess ? PF_OK : hip_fail(e, "ext_tiles");
+}
+
+pf_status run_fwd(const Desc& d, const pf::AttnArgs& a, const pf::SegTable& seg, hipStream_t st,
+                  const pf::RangeTable* rt = nullptr) {
+  pf_status s = run_tiles(rt, a, st);
+  if (s != PF_OK) return s;
   hipError_t e = pf::launch_prep(seg, d.heads, a.ri, st);
   if (e != hipSuccess) return hip_fail(e, "prep");
   e = d.dtype == PF_BF16 ? pf::launch_fwd_bf16(a, d.d, st) : pf::launch_fwd_f32(a, d.d, st);
@@ -375,6 +426,8 @@ pf::PartialSums partial_sums_of(const Desc& d, const pf::AttnArgs& a) {
     ps.part_v = (const float4*)a.gv_part;
     ps.acc_k = (float4*)a.gk_acc;
     ps.acc_v = (float4*)a.gv_acc;
+    ps.ext_tiles = a.ext_tiles;
+    ps.ext_row4 = d.hkv * d.d / 4;
   }
   if (a.n_chunks_own > 1) {
     ps.own_planes = a.n_chunks_own;
@@ -390,7 +443,10 @@ pf::PartialSums partial_sums_of(const Desc& d, const pf::AttnArgs& a) {
   return ps;
 }
 
-pf_status run_bwd(const Desc& d, const pf::AttnArgs& a, const pf::SegTable& seg, hipStream_t st) {
+pf_status run_bwd(const Desc& d, const pf::AttnArgs& a, const pf::SegTable& seg, hipStream_t st,
+                  const pf::RangeTable* rt = nullptr) {
+  const pf_status s = run_tiles(rt, a, st);
+  if (s != PF_OK) return s;
   hipError_t e;
   // longest-first order of the KV-stationary items (a host-side plan; no
   // device work)
@@ -563,13 +619,19 @@ namespace {
 // Phase B forward over a cached prefix for rows whose own-key visibility is
 // the segment table `seg` (flat suffixes or a tree window); `rows` and the
 // structure are already validated.
+// With `rt`, the external keys are the row ranges rt of k_p / v_p, which hold
+// c_rows rows, and prefix_len is the padded key count of check_ranges.
 pf_status suffix_fwd_impl(int32_t op, const Desc& d, int32_t prefix_len, pf_tensor k_p,
                           pf_tensor v_p, int32_t rows, const pf::SegTable& seg, pf_tensor q_s,
                           pf_tensor k_s, pf_tensor v_s, pf_tensor o_s, float* lse_s,
-                          void* workspace, size_t workspace_bytes, void* stream) {
+                          void* workspace, size_t workspace_bytes, void* stream,
+                          const pf::RangeTable* rt = nullptr, int32_t c_rows = 0) {
   pf_status s;
-  if ((s = check_tensor("k_p", k_p, prefix_len, d.hkv, d, d.dtype)) != PF_OK) return s;
-  if ((s = check_tensor("v_p", v_p, prefix_len, d.hkv, d, d.dtype)) != PF_OK) return s;
+  if (rt && d.dtype != PF_BF16)
+    return fail(PF_ERR_UNSUPPORTED, "cached row ranges need bf16 (the fp32 kernels read one span)");
+  const int32_t x_rows = rt ? c_rows : prefix_len;
+  if ((s = check_tensor("k_p", k_p, x_rows, d.hkv, d, d.dtype)) != PF_OK) return s;
+  if ((s = check_tensor("v_p", v_p, x_rows, d.hkv, d, d.dtype)) != PF_OK) return s;
   if ((s = check_tensor("q_s", q_s, rows, d.hq, d, d.dtype)) != PF_OK) return s;
   if ((s = check_tensor("k_s", k_s, rows, d.hkv, d, d.dtype)) != PF_OK) return s;
   if ((s = check_tensor("v_s", v_s, rows, d.hkv, d, d.dtype)) != PF_OK) return s;
@@ -582,10 +644,11 @@ pf_status suffix_fwd_impl(int32_t op, const Desc& d, int32_t prefix_len, pf_tens
   set_q(a, q_s);
   set_out(a, o_s);
   set_ext(a, k_p, v_p, prefix_len);
+  set_tiles(a, workspace, w, rt, c_rows);
   set_own(a, k_s, v_s);
   a.lse = lse_s;
   a.ri = row_info(workspace, w);
-  return run_fwd(d, a, seg, (hipStream_t)stream);
+  return run_fwd(d, a, seg, (hipStream_t)stream, rt);
 }
 
 // Phase B backward with gK/gV accumulation, for the same two row structures.
@@ -598,10 +661,14 @@ pf_status suffix_bwd_impl(int32_t op, const Desc& d, int32_t prefix_len, pf_tens
                           pf_tensor k_s, pf_tensor v_s, pf_tensor o_s, const float* lse_s,
                           pf_tensor do_s, pf_tensor dq_s, pf_tensor dk_s, pf_tensor dv_s,
                           float* gk_acc, float* gv_acc, void* workspace, size_t workspace_bytes,
-                          void* stream, bool use_scratch = false) {
+                          void* stream, bool use_scratch = false,
+                          const pf::RangeTable* rt = nullptr, int32_t c_rows = 0) {
   pf_status s;
-  if ((s = check_tensor("k_p", k_p, prefix_len, d.hkv, d, d.dtype)) != PF_OK) return s;
-  if ((s = check_tensor("v_p", v_p, prefix_len, d.hkv, d, d.dtype)) != PF_OK) return s;
+  if (rt && d.dtype != PF_BF16)
+    return fail(PF_ERR_UNSUPPORTED, "cached row ranges need bf16 (the fp32 kernels read one span)");
+  const int32_t x_rows = rt ? c_rows : prefix_len;
+  if ((s = check_tensor("k_p", k_p, x_rows, d.hkv, d, d.dtype)) != PF_OK) return s;
+  if ((s = check_tensor("v_p", v_p, x_rows, d.hkv, d, d.dtype)) != PF_OK) return s;
   if ((s = check_tensor("q_s", q_s, rows, d.hq, d, d.dtype)) != PF_OK) return s;
   if ((s = check_tensor("k_s", k_s, rows, d.hkv, d, d.dtype)) != PF_OK) return s;
   if ((s = check_tensor("v_s", v_s, rows, d.hkv, d, d.dtype)) != PF_OK) return s;
@@ -652,8 +719,9 @@ pf_status suffix_bwd_impl(int32_t op, const Desc& d, int32_t prefix_len, pf_tens
   a.lse2 = (float*)((char*)workspace + w.lse2);
   set_ds(a, workspace, w);
   set_own_parts(a, workspace, w);
+  set_tiles(a, workspace, w, rt, c_rows);
   a.ri = row_info(workspace, w);
-  return run_bwd(d, a, seg, (hipStream_t)stream);
+  return run_bwd(d, a, seg, (hipStream_t)stream, rt);
 }
 
 }  // namespace
@@ -742,6 +810,58 @@ pf_status pf_tree_suffix_attn_bwd_accum(const pf_attn_desc* desc, int32_t prefix
   return suffix_bwd_impl(PF_OP_TREE_SUFFIX_BWD, d, prefix_len, k_p, v_p, node_off[n_nodes],
                          tree_segments(n_nodes, node_off, send), q, k, v, o, lse, dout, dq, dk,
                          dv, gk_acc, gv_acc, workspace, workspace_bytes, stream);
+}
+
+pf_status pf_tree_suffix_attn_fwd_ranges(const pf_attn_desc* desc, int32_t c_rows, pf_tensor k_c,
+                                         pf_tensor v_c, int32_t n_ranges,
+                                         const int32_t* range_start, const int32_t* range_len,
+                                         int32_t n_nodes, const int32_t* node_off,
+                                         const int32_t* parent, pf_tensor q, pf_tensor k,
+                                         pf_tensor v, pf_tensor o, float* lse, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+  Desc d;
+  pf_status s = check_desc(desc, &d);
+  if (s != PF_OK) return s;
+  pf::RangeTable rt;
+  int32_t n_virtual = 0;
+  if ((s = check_ranges(n_ranges, range_start, range_len, c_rows, &rt, &n_virtual)) != PF_OK)
+    return s;
+  int32_t send[PF_MAX_SEGMENTS];
+  if ((s = check_tree(n_nodes, node_off, parent, send)) != PF_OK) return s;
+  return suffix_fwd_impl(PF_OP_TREE_SUFFIX_FWD, d, n_virtual, k_c, v_c, node_off[n_nodes],
+                         tree_segments(n_nodes, node_off, send), q, k, v, o, lse, workspace,
+                         workspace_bytes, stream, &rt, c_rows);
+}
+
+pf_status pf_tree_suffix_attn_bwd_accum_ranges(
+    const pf_attn_desc* desc, int32_t c_rows, pf_tensor k_c, pf_tensor v_c, int32_t n_ranges,
+    const int32_t* range_start, const int32_t* range_len, int32_t n_nodes,
+    const int32_t* node_off, const int32_t* parent, pf_tensor q, pf_tensor k, pf_tensor v,
+    pf_tensor o, const float* lse, pf_tensor dout, pf_tensor dq, pf_tensor dk, pf_tensor dv,
+    float* gk_acc, float* gv_acc, void* workspace, size_t workspace_bytes, void* stream) {
+  Desc d;
+  pf_status s = check_desc(desc, &d);
+  if (s != PF_OK) return s;
+  pf::RangeTable rt;
+  int32_t n_virtual = 0;
+  if ((s = check_ranges(n_ranges, range_start, range_len, c_rows, &rt, &n_virtual)) != PF_OK)
+    return s;
+  int32_t send[PF_MAX_SEGMENTS];
+  if ((s = check_tree(n_nodes, node_off, parent, send)) != PF_OK) return s;
+  return suffix_bwd_impl(PF_OP_TREE_SUFFIX_BWD, d, n_virtual, k_c, v_c, node_off[n_nodes],
+                         tree_segments(n_nodes, node_off, send), q, k, v, o, lse, dout, dq, dk,
+                         dv, gk_acc, gv_acc, workspace, workspace_bytes, stream, false, &rt,
+                         c_rows);
+}
+
+int32_t pf_ranges_cached_keys(int32_t n_ranges, const int32_t* range_len) {
+  if (n_ranges < 0 || n_ranges > PF_MAX_SEGMENTS || (n_ranges > 0 && !range_len)) return -1;
+  int64_t n = 0;
+  for (int i = 0; i < n_ranges; ++i) {
+    if (range_len[i] < 0) return -1;
+    n += (range_len[i] + 31) / 32 * 32;
+  }
+  return n < ((int64_t)1 << 30) ? (int32_t)n : -1;
 }
 
 pf_status pf_prefix_bwd_inject(const pf_attn_desc* desc, int32_t prefix_len, pf_tensor q_p,
@@ -836,28 +956,59 @@ pf_status pf_tree_attn_fwd(const pf_attn_desc* desc, int32_t n_nodes, const int3
   return run_fwd(d, a, tree_segments(n_nodes, node_off, send), (hipStream_t)stream);
 }
 
-pf_status pf_tree_attn_bwd(const pf_attn_desc* desc, int32_t n_nodes, const int32_t* node_off,
-                           const int32_t* parent, pf_tensor q, pf_tensor k, pf_tensor v, pf_tensor o,
-                           const float* lse, pf_tensor dout, pf_tensor dq, pf_tensor dk,
-                           pf_tensor dv, void* workspace, size_t workspace_bytes, void* stream) {
-  Desc d;
-  pf_status s = check_desc(desc, &d);
-  if (s != PF_OK) return s;
+}  // extern "C"
+
+namespace {
+
+// The tree backward; with gk_acc / gv_acc (fp32 [C, Hkv, d]) they are added
+// to dK / dV before the one rounding (the producer backward of HARTS §3.4),
+// in dkv_dtype.  A NULL dout.data with injection means a zero upstream.
+pf_status tree_bwd_impl(const Desc& d, int32_t n_nodes, const int32_t* node_off,
+                        const int32_t* parent, pf_tensor q, pf_tensor k, pf_tensor v, pf_tensor o,
+                        const float* lse, pf_tensor dout, const float* gk_acc,
+                        const float* gv_acc, pf_tensor dq, pf_tensor dk, pf_tensor dv,
+                        int32_t dkv_dtype, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  pf_status s;
   int32_t send[PF_MAX_SEGMENTS];
   if ((s = check_tree(n_nodes, node_off, parent, send)) != PF_OK) return s;
   const int32_t rows = node_off[n_nodes];
-  if ((s = check_tensor("q", q, rows, d.hq, d, d.dtype)) != PF_OK) return s;
-  if ((s = check_tensor("k", k, rows, d.hkv, d, d.dtype)) != PF_OK) return s;
-  if ((s = check_tensor("v", v, rows, d.hkv, d, d.dtype)) != PF_OK) return s;
-  if ((s = check_tensor("o", o, rows, d.hq, d, d.dtype)) != PF_OK) return s;
-  if ((s = check_tensor("dout", dout, rows, d.hq, d, d.dtype)) != PF_OK) return s;
+  const bool inject = gk_acc != nullptr || gv_acc != nullptr;
+  const bool has_do = dout.data != nullptr || !inject;
+  if (dkv_dtype != PF_F32 && dkv_dtype != d.dtype)
+    return fail(PF_ERR_INVALID_ARG, "dkv_dtype must be PF_F32 or the input dtype");
+  if (has_do) {
+    if ((s = check_tensor("q", q, rows, d.hq, d, d.dtype)) != PF_OK) return s;
+    if ((s = check_tensor("k", k, rows, d.hkv, d, d.dtype)) != PF_OK) return s;
+    if ((s = check_tensor("v", v, rows, d.hkv, d, d.dtype)) != PF_OK) return s;
+    if ((s = check_tensor("o", o, rows, d.hq, d, d.dtype)) != PF_OK) return s;
+    if ((s = check_tensor("dout", dout, rows, d.hq, d, d.dtype)) != PF_OK) return s;
+    if (rows > 0 && (s = check_ptr("lse", lse, 4)) != PF_OK) return s;
+  }
   if ((s = check_tensor("dq", dq, rows, d.hq, d, d.dtype)) != PF_OK) return s;
-  if ((s = check_tensor("dk", dk, rows, d.hkv, d, d.dtype)) != PF_OK) return s;
-  if ((s = check_tensor("dv", dv, rows, d.hkv, d, d.dtype)) != PF_OK) return s;
-  if (rows > 0 && (s = check_ptr("lse", lse, 4)) != PF_OK) return s;
+  if ((s = check_tensor("dk", dk, rows, d.hkv, d, dkv_dtype)) != PF_OK) return s;
+  if ((s = check_tensor("dv", dv, rows, d.hkv, d, dkv_dtype)) != PF_OK) return s;
+  if (inject && rows > 0) {
+    if ((s = check_ptr("gk_acc", gk_acc, 16)) != PF_OK) return s;
+    if ((s = check_ptr("gv_acc", gv_acc, 16)) != PF_OK) return s;
+  }
   const WsLayout w_min = layout(PF_OP_TREE_BWD, d, 0, rows);
-  if ((s = check_stream_ws(workspace, workspace_bytes, w_min.total)) != PF_OK) return s;
+  if (has_do && (s = check_stream_ws(workspace, workspace_bytes, w_min.total)) != PF_OK) return s;
   if (rows == 0) return PF_OK;
+  hipStream_t st = (hipStream_t)stream;
+  if (!has_do) {
+    // zero upstream: dQ = 0 and the K/V gradients are the accumulators
+    hipError_t e = pf::launch_fill_zero(dq.data, rows, d.hq, d.d, dq.stride_tok, dq.stride_head,
+                                        elem_bytes(d.dtype), st);
+    if (e == hipSuccess)
+      e = pf::launch_convert_acc(gk_acc, dk.data, rows, d.hkv, d.d, dk.stride_tok,
+                                 dk.stride_head, dkv_dtype == PF_F32, st);
+    if (e == hipSuccess)
+      e = pf::launch_convert_acc(gv_acc, dv.data, rows, d.hkv, d.d, dv.stride_tok,
+                                 dv.stride_head, dkv_dtype == PF_F32, st);
+    if (e != hipSuccess) return hip_fail(e, "inject");
+    return PF_OK;
+  }
   const WsLayout w = pick_layout(PF_OP_TREE_BWD, d, 0, rows, workspace_bytes, w_min);
   pf::AttnArgs a = base_args(d, rows);
   set_q(a, q);
@@ -866,14 +1017,45 @@ pf_status pf_tree_attn_bwd(const pf_attn_desc* desc, int32_t n_nodes, const int3
   set_out(a, dq);
   set_own(a, k, v);
   set_dkv(a, dk, dv);
-  a.dkv_f32 = d.dtype == PF_F32;
+  a.dkv_f32 = dkv_dtype == PF_F32;
+  a.gk_init = gk_acc;
+  a.gv_init = gv_acc;
   a.lse = const_cast<float*>(lse);
   a.dsum = (float*)((char*)workspace + w.dsum);
   a.lse2 = (float*)((char*)workspace + w.lse2);
   set_ds(a, workspace, w);
   set_own_parts(a, workspace, w);
   a.ri = row_info(workspace, w);
-  return run_bwd(d, a, tree_segments(n_nodes, node_off, send), (hipStream_t)stream);
+  return run_bwd(d, a, tree_segments(n_nodes, node_off, send), st);
+}
+
+}  // namespace
+
+extern "C" {
+
+pf_status pf_tree_attn_bwd(const pf_attn_desc* desc, int32_t n_nodes, const int32_t* node_off,
+                           const int32_t* parent, pf_tensor q, pf_tensor k, pf_tensor v, pf_tensor o,
+                           const float* lse, pf_tensor dout, pf_tensor dq, pf_tensor dk,
+                           pf_tensor dv, void* workspace, size_t workspace_bytes, void* stream) {
+  Desc d;
+  pf_status s = check_desc(desc, &d);
+  if (s != PF_OK) return s;
+  return tree_bwd_impl(d, n_nodes, node_off, parent, q, k, v, o, lse, dout, nullptr, nullptr, dq,
+                       dk, dv, d.dtype, workspace, workspace_bytes, stream);
+}
+
+pf_status pf_tree_attn_bwd_inject(const pf_attn_desc* desc, int32_t n_nodes,
+                                  const int32_t* node_off, const int32_t* parent, pf_tensor q,
+                                  pf_tensor k, pf_tensor v, pf_tensor o, const float* lse,
+                                  pf_tensor dout, const float* gk_acc, const float* gv_acc,
+                                  pf_tensor dq, pf_tensor dk, pf_tensor dv, int32_t dkv_dtype,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  Desc d;
+  pf_status s = check_desc(desc, &d);
+  if (s != PF_OK) return s;
+  if (!gk_acc || !gv_acc) return fail(PF_ERR_INVALID_ARG, "gk_acc or gv_acc is NULL");
+  return tree_bwd_impl(d, n_nodes, node_off, parent, q, k, v, o, lse, dout, gk_acc, gv_acc, dq,
+                       dk, dv, dkv_dtype, workspace, workspace_bytes, stream);
 }
 
 // ------------------------------------------------- compact log-probabilities

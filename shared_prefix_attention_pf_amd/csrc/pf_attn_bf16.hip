@@ -343,6 +343,7 @@ struct KeyWalk {
   const int32_t* bmax;
   const int32_t* bmin;
   int rows;
+  const int2* tiles;      // external keys as row ranges (padding needs a mask), or null
 
   __device__ int own_block_max(int kb) const {
     int m = -1;
@@ -373,7 +374,15 @@ struct KeyWalk {
   }
   // does the block need an element mask
   __device__ bool masked(int i, int n_ext) const {
-    if (i < n_ext_blocks) return (i + 1) * BN > n_ext;
+    if (i < n_ext_blocks) {
+      if ((i + 1) * BN > n_ext) return true;
+      if (!tiles) return false;
+      int m = 32;
+#pragma unroll
+      for (int kt = 0; kt < BN / 32; ++kt)
+        m = min(m, ld_uniform((const int32_t*)tiles, 2 * ((i * BN) / 32 + kt) + 1));
+      return m < 32;
+    }
     const int kb = i - n_ext_blocks;
     const int k0 = kb * BN;
     if (k0 + BN > rows) return true;
@@ -389,12 +398,37 @@ struct KeyWalk {
 // scalar arithmetic plus the loads.
 struct RowSrc {
   Rsrc res;
+  const char* base;    // row 0
+  int nrows;           // rows the resource covers
   uint32_t st_b;       // bytes per row
   uint32_t lane_off;   // this lane's byte offset within a 4-row pass
-  __device__ void init(const void* base, int nrows, int64_t st_elems, int wave, int lane) {
+  __device__ void init(const void* base_, int nrows_, int64_t st_elems, int wave, int lane) {
+    base = (const char*)base_;
+    nrows = nrows_;
     st_b = 2u * (uint32_t)st_elems;
-    res = row_rsrc(base, nrows, st_b);
+    res = row_rsrc(base_, nrows_, st_b);
     lane_off = dma_lane_off(wave, lane, st_b);
+  }
+  // the same for the virtual external keys [r0, r0 + ROWS) of a call whose
+  // external keys are row ranges (tile table `tiles`, n_ext virtual keys):
+  // each pass of 4 WAVES rows lies in one 32-key tile and is read from that
+  // tile's rows; padding and keys past n_ext read zero
+  template <int ROWS, int WAVES = 4>
+  __device__ void stage_tiled(const int2* tiles, int n_ext, int r0, lds_t* tile, int wave) const {
+    constexpr int RS = 4 * WAVES;
+    static_assert(32 % RS == 0 && ROWS % RS == 0, "a pass lies in one tile");
+#pragma unroll
+    for (int i = 0; i < ROWS / RS; ++i) {
+      const int vr = r0 + RS * i;
+      int first = 0, valid = 0;
+      if (vr < n_ext) {
+        first = ld_uniform((const int32_t*)tiles, 2 * (vr >> 5));
+        valid = ld_uniform((const int32_t*)tiles, 2 * (vr >> 5) + 1) - (vr & 31);
+        first += vr & 31;
+      }
+      lds_dma16(row_rsrc(base + (int64_t)first * st_b, valid, st_b),
+                tile + (RS * i + 4 * wave) * kRowB, lane_off, 0u);
+    }
   }
   // rows [r0, r0 + ROWS) into `tile`, issued by every one of the group's
   // WAVES waves (each moves 4 rows per load)
@@ -413,11 +447,16 @@ struct RowSrc {
 template <int BN>
 struct BlockSrc {
   int n_ext_blocks;
+  const int2* tiles;   // external keys as row ranges (or null)
+  int n_ext;
   RowSrc kx, vx, ko, vo;
   __device__ void init(const AttnArgs& a, int g, int n_ext_blk, int wave, int lane) {
     n_ext_blocks = n_ext_blk;
-    kx.init((const __bf16*)a.k_ext + (int64_t)g * a.kx_sh, a.n_ext, a.kx_st, wave, lane);
-    vx.init((const __bf16*)a.v_ext + (int64_t)g * a.vx_sh, a.n_ext, a.vx_st, wave, lane);
+    tiles = a.ext_tiles;
+    n_ext = a.n_ext;
+    const int xrows = a.ext_tiles ? a.ext_rows : a.n_ext;
+    kx.init((const __bf16*)a.k_ext + (int64_t)g * a.kx_sh, xrows, a.kx_st, wave, lane);
+    vx.init((const __bf16*)a.v_ext + (int64_t)g * a.vx_sh, xrows, a.vx_st, wave, lane);
     ko.init((const __bf16*)a.k_own + (int64_t)g * a.ko_sh, a.rows, a.ko_st, wave, lane);
     vo.init((const __bf16*)a.v_own + (int64_t)g * a.vo_sh, a.rows, a.vo_st, wave, lane);
   }
@@ -427,17 +466,36 @@ struct BlockSrc {
   // read 0), issued by all WAVES waves of the group
   template <int WAVES = 4>
   __device__ void dma_k(int b, lds_t* tile, int wave, int /*lane*/) const {
-    if (ext(b))
-      kx.stage<BN, WAVES>(k0(b), tile, wave);
-    else
+    if (ext(b)) {
+      if (tiles)
+        kx.stage_tiled<BN, WAVES>(tiles, n_ext, k0(b), tile, wave);
+      else
+        kx.stage<BN, WAVES>(k0(b), tile, wave);
+    } else {
       ko.stage<BN, WAVES>(k0(b), tile, wave);
+    }
   }
   template <int WAVES = 4>
   __device__ void dma_v(int b, lds_t* tile, int wave, int /*lane*/) const {
-    if (ext(b))
-      vx.stage<BN, WAVES>(k0(b), tile, wave);
-    else
+    if (ext(b)) {
+      if (tiles)
+        vx.stage_tiled<BN, WAVES>(tiles, n_ext, k0(b), tile, wave);
+      else
+        vx.stage<BN, WAVES>(k0(b), tile, wave);
+    } else {
       vo.stage<BN, WAVES>(k0(b), tile, wave);
+    }
+  }
+  // valid keys of the external 32-key tiles of block b (b external)
+  __device__ void ext_valid(int b, int (&v)[BN / 32]) const {
+#pragma unroll
+    for (int kt = 0; kt < BN / 32; ++kt) {
+      const int vk = b * BN + 32 * kt;
+      if (tiles)
+        v[kt] = vk < n_ext ? ld_uniform((const int32_t*)tiles, 2 * (vk >> 5) + 1) : 0;
+      else
+        v[kt] = min(32, max(0, n_ext - vk));
+    }
   }
 };
 
@@ -454,9 +512,12 @@ __device__ __forceinline__ int load_kend(const AttnArgs& a, const BlockSrc<BN>& 
 // values are read four keys at a time, one group after another, so the mask
 // holds few registers beside the tiles.  tok[nt] is the lane's query token of
 // column tile nt.
+// evalid[kt] is the number of valid keys of external key tile kt (padding of
+// row ranges, or the end of the external keys); own keys use klim.
 template <int BN, int NT>
 __device__ __forceinline__ void mask_st(f32x16 (&s)[BN / 32][NT], bool ext, int k0, int klim,
-                                        const int32_t* kend, const int (&tok)[NT], int h32) {
+                                        const int32_t* kend, const int (&tok)[NT], int h32,
+                                        const int (&evalid)[BN / 32]) {
 #pragma unroll
   for (int kt = 0; kt < BN / 32; ++kt)
 #pragma unroll
@@ -475,7 +536,7 @@ __device__ __forceinline__ void mask_st(f32x16 (&s)[BN / 32][NT], bool ext, int 
       for (int r = 0; r < 4; ++r) {
         const int i = 4 * jj + r;
         const int kk = k0 + kl0 + r;
-        const int in = kk < klim ? 1 : 0;
+        const int in = ext ? ((8 * jj + 4 * h32 + r) < evalid[kt] ? 1 : 0) : (kk < klim ? 1 : 0);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           const int own = (kk <= tok[nt] ? 1 : 0) & (tok[nt] < ke4[r] ? 1 : 0);
@@ -608,6 +669,7 @@ __global__ __launch_bounds__(64 * 8 / NT, 1) void fwd_kernel(AttnArgs a) {
   walk.bmax = a.ri.bmax;
   walk.bmin = a.ri.bmin;
   walk.rows = a.rows;
+  walk.tiles = a.ext_tiles;
   BlockSrc<BN> src;
   src.init(a, g, walk.n_ext_blocks, wave, lane);
 
@@ -656,9 +718,12 @@ __global__ __launch_bounds__(64 * 8 / NT, 1) void fwd_kernel(AttnArgs a) {
   auto blk = [&](int b) { return Blk{b, b >= 0 && walk.masked(b, a.n_ext)}; };
   auto nxt = [&](Blk b) { return blk(b.id >= 0 ? walk.next(b.id + 1) : -1); };
   auto mask_if = [&](f32x16 (&s)[BN / 32][NT], Blk b, const int32_t* kend) {
-    if (b.masked)
+    if (b.masked) {
+      int ev[BN / 32] = {};
+      if (src.ext(b.id)) src.ext_valid(b.id, ev);
       mask_st<BN, NT>(s, src.ext(b.id), src.k0(b.id), src.ext(b.id) ? a.n_ext : a.rows, kend,
-                      tok, h32);
+                      tok, h32, ev);
+    }
   };
   // the lazy move of the running maxima to the block maxima mx (valid when
   // `live`): only when a block exceeds them by more than kRescale, so
@@ -1001,6 +1066,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(AttnArgs a) {
   walk.bmax = a.ri.bmax;
   walk.bmin = a.ri.bmin;
   walk.rows = a.rows;
+  walk.tiles = a.ext_tiles;
   BlockSrc<BN> src;
   src.init(a, g, walk.n_ext_blocks, wave, lane);
 
@@ -1038,8 +1104,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(AttnArgs a) {
                  (const lds_t*)&kend_s[buf][0], 4u * lane, 0u);
       }
     } else {
-      src.kx.stage<BN>(a.n_ext + BN, kt_s, wave);
-      src.vx.stage<BN>(a.n_ext + BN, vt_s, wave);
+      src.kx.stage<BN>(src.kx.nrows + BN, kt_s, wave);   // past the end: zeros
+      src.vx.stage<BN>(src.vx.nrows + BN, vt_s, wave);
     }
   };
 
@@ -1123,9 +1189,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(AttnArgs a) {
     for (int k = 0; k < 2; ++k) dsB[nt][k] = zero8();
   if (b0.id >= 0) {
     sdp(0, sA, dpA, [&](auto) {});
-    if (b0.masked)
+    if (b0.masked) {
+      int ev[BN / 32] = {};
+      if (src.ext(b0.id)) src.ext_valid(b0.id, ev);
       mask_st<BN, 2>(sA, src.ext(b0.id), src.k0(b0.id),
-                     src.ext(b0.id) ? a.n_ext : a.rows, kend_s[0], toks, h32);
+                     src.ext(b0.id) ? a.n_ext : a.rows, kend_s[0], toks, h32, ev);
+    }
   }
 
   // iteration for block j in buffer bj with (sc, dpc) = its S^T, dP^T and
@@ -1146,9 +1215,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(AttnArgs a) {
         if constexpr (e < kDqSplit) ds_elem(sc, dpc, dsc, std::integral_constant<int, e>());
       });
     });
-    if (n1.masked)
+    if (n1.masked) {
+      int ev[BN / 32] = {};
+      if (src.ext(n1.id)) src.ext_valid(n1.id, ev);
       mask_st<BN, 2>(sn, src.ext(n1.id), src.k0(n1.id),
-                     src.ext(n1.id) ? a.n_ext : a.rows, kend_s[b1i], toks, h32);
+                     src.ext(n1.id) ? a.n_ext : a.rows, kend_s[b1i], toks, h32, ev);
+    }
     // phase B
     dq_prod(bpi, dsp, [&](auto kc) {
       constexpr int k = decltype(kc)::value;
@@ -1280,6 +1352,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_ds_kernel(AttnArgs a, Part
   walk.bmax = a.ri.bmax;
   walk.bmin = a.ri.bmin;
   walk.rows = a.rows;
+  walk.tiles = a.ext_tiles;
   BlockSrc<BN> src;
   src.init(a, g, walk.n_ext_blocks, wave, lane);
 
@@ -1315,7 +1388,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_ds_kernel(AttnArgs a, Part
       src.dma_k(b, base, wave, lane);
     } else {
       // keep the per-wave load count uniform: K rows past the end
-      src.kx.stage<BN>(a.n_ext + BN, base, wave);
+      src.kx.stage<BN>(src.kx.nrows + BN, base, wave);
     }
     // past the last block: offsets past the resource, which read zero (the
     // values are never used; every block issues the same loads)
@@ -1536,7 +1609,10 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
   bf16x8 kf[2][kD / 16];
   int kend_k[2];
   bool kvalid[2];
+  int krow[2];       // row of the lane's key in k/v (and gK/gV for external keys)
   int wave_kend_min = 0x7fffffff;
+  // external keys as row ranges of a larger tensor (tile table), or not
+  const int2* tiles = ext ? a.ext_tiles : nullptr;
   {
     const __bf16* kbase = (const __bf16*)(ext ? a.k_ext : a.k_own);
     const __bf16* vbase = (const __bf16*)(ext ? a.v_ext : a.v_own);
@@ -1544,14 +1620,37 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
     const int64_t vst = ext ? a.vx_st : a.vo_st, vsh = ext ? a.vx_sh : a.vo_sh;
     {
       const uint32_t st_b = 2u * (uint32_t)vst;
-      dma_rows<kKeysPerWg>(row_rsrc(vbase + (int64_t)k0 * vst + (int64_t)g * vsh, klim - k0, st_b),
-                           dma_lane_off(wave, lane, st_b), st_b, sb + kDkvV, wave);
+      const uint32_t loff = dma_lane_off(wave, lane, st_b);
+      if (tiles) {
+        // 16-row passes, each inside one 32-key tile and read from its rows
+        const __bf16* vg = vbase + (int64_t)g * vsh;
+#pragma unroll
+        for (int i = 0; i < kKeysPerWg / 16; ++i) {
+          const int vr = k0 + 16 * i;
+          int first = 0, valid = 0;
+          if (vr < klim) {
+            first = ld_uniform((const int32_t*)tiles, 2 * (vr >> 5)) + (vr & 31);
+            valid = ld_uniform((const int32_t*)tiles, 2 * (vr >> 5) + 1) - (vr & 31);
+          }
+          lds_dma16(row_rsrc(vg + (int64_t)first * vst, valid, st_b),
+                    sb + kDkvV + (16 * i + 4 * wave) * kRowB, loff, 0u);
+        }
+      } else {
+        dma_rows<kKeysPerWg>(row_rsrc(vbase + (int64_t)k0 * vst + (int64_t)g * vsh, klim - k0, st_b),
+                             loff, st_b, sb + kDkvV, wave);
+      }
     }
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       const int kk = kw0 + kt * 32 + col;
       kvalid[kt] = kk < klim;
-      const __bf16* kp = kbase + (int64_t)(kvalid[kt] ? kk : 0) * kst + (int64_t)g * ksh + 8 * h32;
+      krow[kt] = kk;
+      if (tiles && kvalid[kt]) {
+        const int vt = (kw0 + kt * 32) >> 5;
+        krow[kt] = ld_uniform((const int32_t*)tiles, 2 * vt) + col;
+        kvalid[kt] = col < ld_uniform((const int32_t*)tiles, 2 * vt + 1);
+      }
+      const __bf16* kp = kbase + (int64_t)(kvalid[kt] ? krow[kt] : 0) * kst + (int64_t)g * ksh + 8 * h32;
 #pragma unroll
       for (int ds = 0; ds < kD / 16; ++ds) kf[kt][ds] = load8(kp + ds * 16);
       kend_k[kt] = (!ext && kvalid[kt]) ? a.ri.kend[kk] : (ext ? 0x7fffffff : -1);
@@ -1885,7 +1984,8 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
   static_for<0, 2>([&](auto ktc) {
     constexpr int kt = decltype(ktc)::value;
     const int kk = kw0 + kt * 32 + col;
-    const int64_t base = ((int64_t)kk * a.hkv + g) * kD;
+    const int64_t base = ((int64_t)kk * a.hkv + g) * kD;         // partial planes: virtual keys
+    const int64_t abase = ((int64_t)krow[kt] * a.hkv + g) * kD;  // gK/gV: accumulator rows
     static_for<0, kD / 32>([&](auto dtc) {
       constexpr int dt = decltype(dtc)::value;
       if (kvalid[kt]) {
@@ -1899,8 +1999,8 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
             vv[r] = dv[dt][kt][4 * j + r];
           }
           if (mode == 0) {
-            *(f32x4*)(a.gk_acc + base + d) += vk;
-            *(f32x4*)(a.gv_acc + base + d) += vv;
+            *(f32x4*)(a.gk_acc + abase + d) += vk;
+            *(f32x4*)(a.gv_acc + abase + d) += vv;
           } else if (mode == 1) {
             const int64_t pb = (int64_t)(chunk - 1) * a.n_ext * a.hkv * kD + base;
             *(f32x4*)(a.gk_part + pb + d) = vk;

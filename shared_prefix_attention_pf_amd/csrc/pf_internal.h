@@ -37,6 +37,17 @@ struct SegTable {
   int32_t vis_end[PF_MAX_SEGMENTS];
 };
 
+// Row ranges of a larger K/V tensor that form the external keys of a call
+// (host side, by value to the tile kernel): range i is rows [start[i],
+// start[i] + len[i]), padded to a multiple of 32 virtual keys starting at
+// virtual tile vt0[i]; vt0[n] is the number of tiles.
+struct RangeTable {
+  int32_t n;
+  int32_t start[PF_MAX_SEGMENTS];
+  int32_t len[PF_MAX_SEGMENTS];
+  int32_t vt0[PF_MAX_SEGMENTS + 1];
+};
+
 // Per-row visibility data and the head table, in the workspace.
 struct RowInfo {
   int32_t* kend;      // [rows]
@@ -68,6 +79,14 @@ struct AttnArgs {
   const void* k_ext; int64_t kx_st, kx_sh;
   const void* v_ext; int64_t vx_st, vx_sh;
   int32_t n_ext;
+  // External keys read from row ranges of a larger tensor (the cached rows of
+  // a producer tree): ext_tiles[t] = (first row, valid rows) of virtual
+  // external keys [32 t, 32 t + 32), so external key 32 t + i (i < valid) is
+  // row first + i of k_ext / v_ext and of gk_acc / gv_acc; keys past `valid`
+  // are padding (read as zero, never visible, never written).  Null: external
+  // key e is row e.  n_ext then counts the padded virtual keys.
+  const int2* ext_tiles;
+  int32_t ext_rows;                       // rows of k_ext / v_ext (and gk_acc) with ext_tiles
   // own keys, indexed like the query rows, [rows, Hkv, d]
   const void* k_own; int64_t ko_st, ko_sh;
   const void* v_own; int64_t vo_st, vo_sh;
@@ -114,6 +133,8 @@ hipError_t launch_prep(const SegTable& seg, const HeadTable& heads, RowInfo ri, 
 // a.dsum / a.lse2 (bf16 inputs).
 hipError_t launch_prep_dsum_bf16(const SegTable& seg, const HeadTable& heads, const AttnArgs& a,
                                  hipStream_t stream);
+// ext_tiles[0 .. rt.vt0[rt.n]) from the range table
+hipError_t launch_ext_tiles(const RangeTable& rt, int2* tiles, hipStream_t stream);
 hipError_t launch_fill_zero(void* dst, int64_t rows, int32_t heads, int32_t d, int64_t st,
                             int64_t sh, int32_t elem_bytes, hipStream_t stream);
 // One own-key gradient (dK or dV) to finish: dst = convert(init + sum of the
@@ -134,6 +155,8 @@ struct OwnFinish {
 struct PartialSums {
   int32_t ext_planes;
   int64_t ext_n4;
+  const int2* ext_tiles;                  // virtual external rows -> accumulator rows (or null)
+  int32_t ext_row4;                       // float4 values per external row (Hkv d / 4)
   const float4* part_k;
   const float4* part_v;
   float4* acc_k;

@@ -39,9 +39,18 @@ __device__ inline void partial_sums_block(const PartialSums& ps, int y, int bx, 
       else if (nc <= 2) s = tree_sum<2>(part, n4, i, nc);
       else if (nc <= 4) s = tree_sum<4>(part, n4, i, nc);
       else s = tree_sum<8>(part, n4, i, nc);
-      float4 a = acc[i];
+      int64_t ai = i;
+      if (ps.ext_tiles) {
+        // virtual external row -> accumulator row; padding rows are skipped
+        const int64_t vr = i / ps.ext_row4;
+        const int2 t = ps.ext_tiles[vr >> 5];
+        const int loc = (int)(vr & 31);
+        if (loc >= t.y) continue;
+        ai = (int64_t)(t.x + loc) * ps.ext_row4 + (i - vr * ps.ext_row4);
+      }
+      float4 a = acc[ai];
       a.x += s.x; a.y += s.y; a.z += s.z; a.w += s.w;
-      acc[i] = a;
+      acc[ai] = a;
     }
     return;
   }

@@ -63,6 +63,28 @@ hipError_t launch_prep(const SegTable& seg, const HeadTable& heads, RowInfo ri,
   return hipGetLastError();
 }
 
+// One thread per virtual tile of 32 external keys: the range holding it (the
+// last i with vt0[i] <= t) and, from the tile's offset in that range, its
+// first row and valid rows.
+__global__ __launch_bounds__(256) void ext_tiles_kernel(RangeTable rt, int2* tiles) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= rt.vt0[rt.n]) return;
+  int lo = 0, hi = rt.n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (rt.vt0[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  const int off = 32 * (t - rt.vt0[lo]);
+  tiles[t] = make_int2(rt.start[lo] + off, min(32, rt.len[lo] - off));
+}
+
+hipError_t launch_ext_tiles(const RangeTable& rt, int2* tiles, hipStream_t stream) {
+  const int n = rt.vt0[rt.n];
+  if (n <= 0) return hipSuccess;
+  PF_LAUNCH("pf_ext_tiles", ext_tiles_kernel, dim3((n + 255) / 256), dim3(256), stream, rt, tiles);
+  return hipGetLastError();
+}
+
 // D and LSE (log2) per (row, query head): 16 lanes per pair, each lane
 // reading 8 head_dim values of dO and O (head_dim 128); a 16-lane group
 // covers kDsumPairs consecutive pairs, all of whose loads are issued before

@@ -26,8 +26,12 @@ from . import (
     pf_suffix_attn_fwd,
     pf_tree_attn_bwd,
     pf_tree_attn_fwd,
+    pf_ranges_cached_keys,
+    pf_tree_attn_bwd_inject,
     pf_tree_suffix_attn_bwd_accum,
+    pf_tree_suffix_attn_bwd_accum_ranges,
     pf_tree_suffix_attn_fwd,
+    pf_tree_suffix_attn_fwd_ranges,
     pf_workspace_size,
 )
 
@@ -138,3 +142,48 @@ def tree_suffix_bwd(desc, k_p, v_p, node_off, parent, q, k, v, o, lse, dout, gk_
                                   dout, dq, dk, dv, gk_acc, gv_acc, ws, stream)
     return dq, dk, dv
 
+
+
+def tree_suffix_fwd_ranges(desc, k_c, v_c, ranges, node_off, parent, q, k, v, ws=None,
+                           stream=None):
+    """ranges: (start, length) row spans of k_c / v_c, in trajectory order."""
+    starts = [int(s) for s, _ in ranges]
+    lens = [int(n) for _, n in ranges]
+    rows = int(node_off[-1])
+    o = torch.empty_like(q)
+    lse = torch.empty(desc.num_q_heads, rows, dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = workspace(PF_OP_TREE_SUFFIX_FWD, desc, pf_ranges_cached_keys(lens), rows, q.device)
+    pf_tree_suffix_attn_fwd_ranges(desc, k_c, v_c, starts, lens, node_off, parent, q, k, v, o, lse,
+                                   ws, stream)
+    return o, lse
+
+
+def tree_suffix_bwd_ranges(desc, k_c, v_c, ranges, node_off, parent, q, k, v, o, lse, dout, gk_acc,
+                           gv_acc, ws=None, stream=None):
+    starts = [int(s) for s, _ in ranges]
+    lens = [int(n) for _, n in ranges]
+    rows = int(node_off[-1])
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    if ws is None:
+        ws = workspace(PF_OP_TREE_SUFFIX_BWD, desc, pf_ranges_cached_keys(lens), rows, q.device)
+    pf_tree_suffix_attn_bwd_accum_ranges(desc, k_c, v_c, starts, lens, node_off, parent, q, k, v,
+                                         o, lse, dout, dq, dk, dv, gk_acc, gv_acc, ws, stream)
+    return dq, dk, dv
+
+
+def tree_bwd_inject(desc, node_off, parent, q, k, v, o, lse, dout, gk_acc, gv_acc, dkv_dtype=None,
+                    ws=None, stream=None):
+    rows = int(node_off[-1])
+    if dkv_dtype is None:
+        dkv_dtype = desc.dtype
+    dq = torch.empty_like(q)
+    dk = torch.empty(k.shape, dtype=TORCH_DTYPE[dkv_dtype], device=k.device)
+    dv = torch.empty(v.shape, dtype=TORCH_DTYPE[dkv_dtype], device=v.device)
+    if ws is None:
+        ws = workspace(PF_OP_TREE_BWD, desc, 0, rows, q.device)
+    pf_tree_attn_bwd_inject(desc, node_off, parent, q, k, v, o, lse, dout, gk_acc, gv_acc, dq, dk,
+                            dv, dkv_dtype, ws, stream)
+    return dq, dk, dv

@@ -182,7 +182,9 @@ def test_tree_window_entry_points_validate_on_the_host():
     desc = pf.AttnDesc(32, 8, 128)
     rows = 6
     need = pf.pf_workspace_size(pf.PF_OP_TREE_SUFFIX_FWD, desc, 64, rows)
-    assert need == pf.pf_workspace_size(pf.PF_OP_SUFFIX_FWD, desc, 64, rows) > 0
+    # a suffix call's workspace plus the table of cached-row tiles (8 B per 32
+    # keys, rounded to 256 B)
+    assert need == pf.pf_workspace_size(pf.PF_OP_SUFFIX_FWD, desc, 64, rows) + 256
     assert fwd([0, 4, 6], [-1, 0], ws_bytes=need - 1)[0] == pf.PF_ERR_WORKSPACE
     full = pf.pf_workspace_size(pf.PF_OP_TREE_SUFFIX_BWD, desc, 4096, 2048)
     least = pf.pf_workspace_size_min(pf.PF_OP_TREE_SUFFIX_BWD, desc, 4096, 2048)
@@ -222,3 +224,42 @@ def test_noalloc_rejects_a_call_beyond_its_scratch():
     assert b"scratch" in pf._lib.pf_last_error()
     args[1] = -1
     assert pf._lib.pf_suffix_attn_bwd_accum_noalloc(*args) == pf.PF_ERR_INVALID_ARG
+
+
+def test_ranges_entry_points_validate_on_the_host():
+    """The windows over producer row ranges reject a range outside the
+    producer, fp32 inputs and a short workspace before any launch; the
+    padded key count that sizes their workspace rounds each range to 32; the
+    injected tree backward needs both accumulators."""
+    assert pf.pf_ranges_cached_keys([100, 0, 32, 1]) == 128 + 0 + 32 + 32
+    assert pf.pf_ranges_cached_keys([]) == 0
+    p32 = ctypes.POINTER(ctypes.c_int32)
+
+    def call(starts, lens, c_rows=1000, dtype=pf.PF_BF16, ws_bytes=1 << 30):
+        d, _keep = _desc(dtype=dtype, d=128)
+        rs = np.asarray(starts, dtype=np.int32)
+        rl = np.asarray(lens, dtype=np.int32)
+        no = np.asarray([0, 4, 6], dtype=np.int32)
+        pa = np.asarray([-1, 0], dtype=np.int32)
+        q, kv = _t(heads=32), _t()
+        return pf._lib.pf_tree_suffix_attn_fwd_ranges(
+            ctypes.byref(d), c_rows, kv, kv, len(rs), rs.ctypes.data_as(p32),
+            rl.ctypes.data_as(p32), len(pa), no.ctypes.data_as(p32), pa.ctypes.data_as(p32), q,
+            kv, kv, q, ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), ws_bytes, ctypes.c_void_p(0))
+    assert call([990], [20]) == pf.PF_ERR_INVALID_ARG
+    assert call([-1], [5]) == pf.PF_ERR_INVALID_ARG
+    assert call([0], [-5]) == pf.PF_ERR_INVALID_ARG
+    assert call([0, 500], [100, 40], dtype=pf.PF_F32) == pf.PF_ERR_UNSUPPORTED
+    desc = pf.AttnDesc(32, 8, 128)
+    need = pf.pf_workspace_size(pf.PF_OP_TREE_SUFFIX_FWD, desc, pf.pf_ranges_cached_keys([100, 40]),
+                                6)
+    assert call([0, 500], [100, 40], ws_bytes=need - 1) == pf.PF_ERR_WORKSPACE
+    d, _keep = _desc()
+    no = np.asarray([0, 4, 6], dtype=np.int32)
+    pa = np.asarray([-1, 0], dtype=np.int32)
+    q, kv = _t(heads=32), _t()
+    st = pf._lib.pf_tree_attn_bwd_inject(
+        ctypes.byref(d), 2, no.ctypes.data_as(p32), pa.ctypes.data_as(p32), q, kv, kv, q,
+        ctypes.c_void_p(FAKE), q, None, ctypes.c_void_p(FAKE), q, kv, kv, pf.PF_BF16,
+        ctypes.c_void_p(FAKE), 1 << 30, ctypes.c_void_p(0))
+    assert st == pf.PF_ERR_INVALID_ARG

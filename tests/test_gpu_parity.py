@@ -12,7 +12,13 @@ import torch
 
 import oracle
 from tests.gpu_util import TOL, check, dev, host
-from workloads.gen import random_small_group, random_tree, random_tree_group
+from workloads.gen import (
+    ancestor_row_ranges,
+    node_depths,
+    random_small_group,
+    random_tree,
+    random_tree_group,
+)
 
 pytestmark = pytest.mark.gpu
 
@@ -416,3 +422,112 @@ def test_empty_call_is_noop():
                  empty_q, gk, gk.clone())
     torch.cuda.synchronize()
     assert o.shape[0] == 0 and torch.all(gk == 3.0)
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (16, 4)])
+def test_windows_under_producer_nodes(hq, hkv):
+    """Consumer windows attached under internal nodes of a producer rollout
+    tree, each reading the rows of its node and the node's ancestors in place
+    (row ranges of the producer's K/V, not 32-aligned), adding its gradients
+    into those producer rows; then the producer's tree backward with the
+    summed gradients injected.  Every output against the oracle (gather,
+    window attention, scatter-add; tree backward plus the injection).  The
+    first window's backward also runs with the smallest workspace (recompute
+    dQ), and one range [0, P) equals the window over a flat prefix."""
+    d, dtype = 128, "bf16"
+    desc = _desc(hq, hkv, d, dtype)
+    scale = 1.0 / math.sqrt(d)
+    hmap = oracle.head_map(hq, hkv)
+    tol = TOL[dtype]
+    node_off_p, parent_p = random_tree(28, 10, max_len=120, min_len=20)
+    depth = node_depths(parent_p)
+    assert depth[7] == 2 and 8 in np.flatnonzero(parent_p == 7)   # a depth-2 internal node
+    cp = int(node_off_p[-1])
+    gp = random_tree_group(28, node_off_p, hq, hkv, d, dtype)
+    tp = {k: dev(gp[k], dtype) for k in ("q", "k", "v", "do")}
+    print(f"\nproducer node_off {node_off_p.tolist()} parent {parent_p.tolist()}", flush=True)
+    o_p, lse_p = G.tree_fwd(desc, node_off_p, parent_p, tp["q"], tp["k"], tp["v"])
+    gk = torch.zeros(cp, hkv, d, dtype=torch.float32, device="cuda")
+    gv = torch.zeros_like(gk)
+    gk_ref = np.zeros((cp, hkv, d))
+    gv_ref = np.zeros((cp, hkv, d))
+    for w, (u, seed, n_nodes, max_len) in enumerate(((7, 60, 8, 70), (9, 61, 11, 40))):
+        ranges = ancestor_row_ranges(node_off_p, parent_p, u)
+        node_off, parent = random_tree(seed, n_nodes, max_len=max_len, min_len=1)
+        rows = int(node_off[-1])
+        print(f"  window {w} under node {u}: ranges {ranges}, {rows} rows", flush=True)
+        tg = random_tree_group(seed, node_off, hq, hkv, d, dtype)
+        tt = {k: dev(tg[k], dtype) for k in ("q", "k", "v", "do")}
+        o, lse = G.tree_suffix_fwd_ranges(desc, tp["k"], tp["v"], ranges, node_off, parent,
+                                          tt["q"], tt["k"], tt["v"])
+        if w == 0:
+            nk = pf.pf_ranges_cached_keys([n for _, n in ranges])
+            n_min = pf.pf_workspace_size_min(pf.PF_OP_TREE_SUFFIX_BWD, desc, nk, rows)
+            ws = torch.empty(n_min, dtype=torch.uint8, device="cuda")
+            gk0 = torch.zeros_like(gk)
+            gv0 = torch.zeros_like(gv)
+            mn = G.tree_suffix_bwd_ranges(desc, tp["k"], tp["v"], ranges, node_off, parent,
+                                          tt["q"], tt["k"], tt["v"], o, lse, tt["do"], gk0, gv0,
+                                          ws=ws)
+        dq, dk, dv = G.tree_suffix_bwd_ranges(desc, tp["k"], tp["v"], ranges, node_off, parent,
+                                              tt["q"], tt["k"], tt["v"], o, lse, tt["do"], gk, gv)
+        torch.cuda.synchronize()
+        ref = oracle.tree_window_attention_ranges(gp["k"], gp["v"], ranges, tg["q"], tg["k"],
+                                                  tg["v"], tg["do"], node_off, parent, scale, hmap)
+        gk_ref += ref["gk"]
+        gv_ref += ref["gv"]
+        for name, got in (("O", o), ("LSE", lse), ("dQ", dq), ("dK", dk), ("dV", dv)):
+            check(f"window {w} {name}", host(got), ref[name.lower()], tol)
+        if w == 0:
+            for name, got in zip(("dQ", "dK", "dV"), mn):
+                check(f"window 0 {name} (min ws)", host(got), ref[name.lower()], tol)
+            check("window 0 gK (min ws)", host(gk0), ref["gk"], tol)
+            check("window 0 gV (min ws)", host(gv0), ref["gv"], tol)
+            # rows outside the ranges are never written
+            used = np.zeros(cp, dtype=bool)
+            for s, n in ranges:
+                used[s:s + n] = True
+            assert np.all(host(gk)[~used] == 0) and np.all(host(gv)[~used] == 0)
+        check(f"gK after window {w}", host(gk), gk_ref, tol)
+        check(f"gV after window {w}", host(gv), gv_ref, tol)
+    # the producer backward with both windows' gradients injected
+    dq_p, dk_p, dv_p = G.tree_bwd_inject(desc, node_off_p, parent_p, tp["q"], tp["k"], tp["v"],
+                                         o_p, lse_p, tp["do"], gk, gv)
+    torch.cuda.synchronize()
+    rp = oracle.tree_attention_direct(gp["q"], gp["k"], gp["v"], gp["do"], node_off_p, parent_p,
+                                      scale, hmap)
+    rdq, rdk, rdv = oracle.tree_backward_inject(gp["q"], gp["k"], gp["v"], gp["do"], node_off_p,
+                                                parent_p, gk_ref, gv_ref, scale, hmap)
+    check("producer O", host(o_p), rp["o"], tol)
+    check("producer dQ", host(dq_p), rdq, tol)
+    check("producer dK (injected)", host(dk_p), rdk, tol)
+    check("producer dV (injected)", host(dv_p), rdv, tol)
+    # zero upstream: the injected gradients alone
+    dq0, dk0, dv0 = G.tree_bwd_inject(desc, node_off_p, parent_p, tp["q"], tp["k"], tp["v"], o_p,
+                                      lse_p, torch.empty(0, device="cuda"), gk, gv,
+                                      dkv_dtype=pf.PF_F32)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dq0).item() == 0
+    assert torch.equal(dk0, gk) and torch.equal(dv0, gv)
+    # one range [0, P) of a flat prefix is the window over that prefix
+    p = 300
+    g = random_small_group(43, hq, hkv, d, p, [1], dtype)
+    kp, vp = dev(g["k_p"], dtype), dev(g["v_p"], dtype)
+    node_off, parent = random_tree(62, 6, max_len=50, min_len=1)
+    tg = random_tree_group(62, node_off, hq, hkv, d, dtype)
+    tt = {k: dev(tg[k], dtype) for k in ("q", "k", "v", "do")}
+    o1, l1 = G.tree_suffix_fwd(desc, kp, vp, node_off, parent, tt["q"], tt["k"], tt["v"])
+    o2, l2 = G.tree_suffix_fwd_ranges(desc, kp, vp, [(0, p)], node_off, parent, tt["q"], tt["k"],
+                                      tt["v"])
+    a1 = torch.zeros(p, hkv, d, device="cuda")
+    b1 = torch.zeros_like(a1)
+    a2 = torch.zeros_like(a1)
+    b2 = torch.zeros_like(a1)
+    r1 = G.tree_suffix_bwd(desc, kp, vp, node_off, parent, tt["q"], tt["k"], tt["v"], o1, l1,
+                           tt["do"], a1, b1)
+    r2 = G.tree_suffix_bwd_ranges(desc, kp, vp, [(0, p)], node_off, parent, tt["q"], tt["k"],
+                                  tt["v"], o1, l1, tt["do"], a2, b2)
+    torch.cuda.synchronize()
+    for name, x, y in (("O", o2, o1), ("LSE", l2, l1), ("dQ", r2[0], r1[0]), ("dK", r2[1], r1[1]),
+                       ("dV", r2[2], r1[2]), ("gK", a2, a1), ("gV", b2, b1)):
+        check(f"one range vs flat prefix: {name}", host(x), host(y), 1e-6)
