@@ -44,8 +44,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2,
-                    help="workload (1..7; 6 is tree windows over a cached prefix, 7 compact "
-                         "log-probabilities); 2 is the headline")
+                    help="workload (1..8; 6 is tree windows over a cached prefix, 7 compact "
+                         "log-probabilities, 8 windows under a producer tree's nodes); 2 is "
+                         "the headline")
+    ap.add_argument("--separate-windows", action="store_true",
+                    help="config 6: one call per window instead of the four trees in one call")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample (0 disables)")
     ap.add_argument("--json-out", default=None)
@@ -90,6 +93,13 @@ def tree_pairs(node_off, parent):
         ln = int(node_off[v + 1] - node_off[v])
         total += ln * int(depth_rows[v]) + ln * (ln + 1) // 2
     return total
+
+
+def ranges_window_pairs(w):
+    """Visible pairs per query head of a window under a producer node: every
+    row sees every cached row of its ranges, plus its tree pairs."""
+    return int(w["node_off"][-1]) * sum(n for _, n in w["ranges"]) + tree_pairs(w["node_off"],
+                                                                                 w["parent"])
 
 
 def window_pairs(p, node_off, parent):
@@ -182,7 +192,7 @@ class KernelTimer:
         return out
 
 
-def run_gpu(cfg, data, steps, warmup, copy_mib=0):
+def run_gpu(cfg, data, steps, warmup, copy_mib=0, separate_windows=False):
     import torch
 
     import shared_prefix_attention_pf_amd as pf
@@ -198,7 +208,60 @@ def run_gpu(cfg, data, steps, warmup, copy_mib=0):
     stream = torch.cuda.current_stream()
     res = {}
     timer = KernelTimer(torch, reserve=64 * (min(steps, 10) + 1), streams=(stream,))
-    if cfg.is_windows:
+    if cfg.is_ranges:
+        # producer tree forward, the windows under its nodes, producer backward
+        node_off, parent = data["node_off"], data["parent"]
+        q_c, k_c, v_c, do_c = (to_dev(data[n]) for n in ("q", "k", "v", "do"))
+        c = q_c.shape[0]
+        o_c = torch.empty_like(q_c)
+        lse_c = torch.empty(cfg.num_q_heads, c, device=dev)
+        dq_c, dk_c, dv_c = torch.empty_like(q_c), torch.empty_like(k_c), torch.empty_like(v_c)
+        gk = torch.empty(c, cfg.num_kv_heads, cfg.head_dim, device=dev)
+        gv = torch.empty_like(gk)
+        wins = []
+        for wd in data["windows"]:
+            w = {n: to_dev(wd[n]) for n in ("q", "k", "v", "do")}
+            rw = w["q"].shape[0]
+            w.update(node_off=wd["node_off"], parent=wd["parent"],
+                     starts=[s for s, _ in wd["ranges"]], lens=[n for _, n in wd["ranges"]],
+                     o=torch.empty_like(w["q"]), lse=torch.empty(cfg.num_q_heads, rw, device=dev),
+                     dq=torch.empty_like(w["q"]), dk=torch.empty_like(w["k"]),
+                     dv=torch.empty_like(w["v"]))
+            wins.append(w)
+        ws_bytes = max(pf.pf_workspace_size(op, desc, pf.pf_ranges_cached_keys(w["lens"]),
+                                            int(w["node_off"][-1]))
+                       for w in wins for op in (pf.PF_OP_TREE_SUFFIX_FWD, pf.PF_OP_TREE_SUFFIX_BWD))
+        ws_bytes = max(ws_bytes, pf.pf_workspace_size(pf.PF_OP_TREE_BWD, desc, 0, c),
+                       pf.pf_workspace_size(pf.PF_OP_TREE_FWD, desc, 0, c))
+        ws = torch.empty(max(16, ws_bytes), dtype=torch.uint8, device=dev)
+
+        def step(ev=None):
+            gk.zero_()
+            gv.zero_()
+            timer.phase = "A"
+            if ev:
+                ev[0].record(stream)
+            pf.pf_tree_attn_fwd(desc, node_off, parent, q_c, k_c, v_c, o_c, lse_c, ws)
+            if ev:
+                ev[1].record(stream)
+            timer.phase = "B"
+            for w in wins:
+                pf.pf_tree_suffix_attn_fwd_ranges(desc, k_c, v_c, w["starts"], w["lens"],
+                                                  w["node_off"], w["parent"], w["q"], w["k"],
+                                                  w["v"], w["o"], w["lse"], ws)
+                pf.pf_tree_suffix_attn_bwd_accum_ranges(
+                    desc, k_c, v_c, w["starts"], w["lens"], w["node_off"], w["parent"], w["q"],
+                    w["k"], w["v"], w["o"], w["lse"], w["do"], w["dq"], w["dk"], w["dv"], gk, gv,
+                    ws)
+            timer.phase = "C"
+            if ev:
+                ev[2].record(stream)
+            pf.pf_tree_attn_bwd_inject(desc, node_off, parent, q_c, k_c, v_c, o_c, lse_c, do_c, gk,
+                                       gv, dq_c, dk_c, dv_c, pdt, ws)
+            if ev:
+                ev[3].record(stream)
+        phase_names = ("A", "B", "C")
+    elif cfg.is_windows:
         p = cfg.prefix_len
         q_p, k_p, v_p, do_p = (to_dev(data[n]) for n in ("q_p", "k_p", "v_p", "do_p"))
         o_p = torch.empty_like(q_p)
@@ -214,7 +277,16 @@ def run_gpu(cfg, data, steps, warmup, copy_mib=0):
                      lse=torch.empty(cfg.num_q_heads, c, device=dev), dq=torch.empty_like(w["q"]),
                      dk=torch.empty_like(w["k"]), dv=torch.empty_like(w["v"]))
             wins.append(w)
-        max_c = max(int(wd["node_off"][-1]) for wd in data["windows"])
+        if not separate_windows and cfg.window_calls == 1 and len(wins) > 1:
+            # every window's tree in one call: a forest over the prefix
+            from workloads.gen import forest
+            no, pa = forest([(w["node_off"], w["parent"]) for w in wins])
+            one = {n: torch.cat([w[n] for w in wins]) for n in ("q", "k", "v", "do", "o", "dq",
+                                                                 "dk", "dv")}
+            one.update(node_off=no, parent=pa,
+                       lse=torch.empty(cfg.num_q_heads, int(no[-1]), device=dev))
+            wins = [one]
+        max_c = max(int(w["node_off"][-1]) for w in wins)
         ws_bytes = max(pf.pf_workspace_size(op, desc, p, max_c) for op in
                        (pf.PF_OP_TREE_SUFFIX_FWD, pf.PF_OP_TREE_SUFFIX_BWD))
         ws_bytes = max(ws_bytes, pf.pf_workspace_size(pf.PF_OP_PREFIX_BWD, desc, p, p))
@@ -648,7 +720,17 @@ def cpu_baseline(cfg, data, target_s, group_flops, compact, expanded):
         heads = slice(kvh * g, (kvh + 1) * g)
         kv = slice(kvh, kvh + 1)
         t0 = time.perf_counter()
-        if cfg.is_windows:
+        if cfg.is_ranges:
+            oracle.tree_attention_direct(data["q"][:, heads], data["k"][:, kv], data["v"][:, kv],
+                                         data["do"][:, heads], data["node_off"], data["parent"],
+                                         scale, hmap, dtype=np.float32)
+            for w in data["windows"]:
+                oracle.tree_window_attention_ranges(data["k"][:, kv], data["v"][:, kv],
+                                                    w["ranges"], w["q"][:, heads], w["k"][:, kv],
+                                                    w["v"][:, kv], w["do"][:, heads],
+                                                    w["node_off"], w["parent"], scale, hmap,
+                                                    dtype=np.float32)
+        elif cfg.is_windows:
             q_ph = data["q_p"][:, heads]
             oracle.prefix_forward(q_ph, data["k_p"][:, kv], data["v_p"][:, kv], scale, hmap,
                                   dtype=np.float32)
@@ -678,6 +760,8 @@ def cpu_baseline(cfg, data, target_s, group_flops, compact, expanded):
             break
     full_s = elapsed * cfg.num_kv_heads / done_groups
     what = ("dense fwd+bwd of every root-to-leaf trajectory" if cfg.is_tree else
+            "dense producer tree fwd+bwd and every window over its gathered ancestor rows"
+            if cfg.is_ranges else
             "dense prefix fwd+bwd and every window over [prefix ; window rows]" if cfg.is_windows
             else
             "dense fwd+bwd of every trajectory [P || S_i], all rows")
@@ -935,9 +1019,17 @@ def main():
         run_offload(cfg, data, args)
         return
     print("[bench] running GPU steps", flush=True)
-    gres = run_gpu(cfg, data, args.steps, args.warmup, args.copy_probe_mib)
+    gres = run_gpu(cfg, data, args.steps, args.warmup, args.copy_probe_mib, args.separate_windows)
     d, hq = cfg.head_dim, cfg.num_q_heads
-    if cfg.is_windows:
+    if cfg.is_ranges:
+        from oracle import tree_trajectories
+        pairs_b = sum(ranges_window_pairs(w) for w in data["windows"])
+        pairs_a = tree_pairs(data["node_off"], data["parent"])
+        compact = int(data["node_off"][-1]) + sum(int(w["node_off"][-1]) for w in data["windows"])
+        expanded = int(sum(sum(n for _, n in w["ranges"]) + len(t) for w in data["windows"]
+                           for t in tree_trajectories(w["node_off"], w["parent"])))
+        b_ms = gres["phase_ms"]["B"]
+    elif cfg.is_windows:
         from oracle import tree_trajectories
         p = cfg.prefix_len
         pairs_b = sum(window_pairs(p, w["node_off"], w["parent"]) for w in data["windows"])
@@ -1024,12 +1116,16 @@ def main():
             "workload": f"config {cfg.cid}: {cfg.name}",
             "num_q_heads": hq, "num_kv_heads": cfg.num_kv_heads, "head_dim": d,
             "prefix_len": cfg.prefix_len,
-            "suffix_lens": (None if cfg.is_tree or cfg.is_windows else
+            "suffix_lens": (None if cfg.is_tree or cfg.is_windows or cfg.is_ranges else
                             np.diff(data["cu_seqlens"]).astype(int).tolist()),
-            "microbatches": (len(data["windows"]) if cfg.is_windows else
+            "microbatches": (len(data["windows"]) if cfg.is_windows or cfg.is_ranges else
                              None if cfg.is_tree else len(data["microbatches"])),
             "window_rows": ([int(w["node_off"][-1]) for w in data["windows"]]
-                            if cfg.is_windows else None),
+                            if cfg.is_windows or cfg.is_ranges else None),
+            "window_calls": (None if not cfg.is_windows else
+                             len(data["windows"]) if args.separate_windows or
+                             cfg.window_calls != 1 else 1),
+            "cached_ranges": ([w["ranges"] for w in data["windows"]] if cfg.is_ranges else None),
             "parallelism": "single GPU",
         },
         "pct_of_bf16_peak": round(100.0 * value / peak, 2),

@@ -220,7 +220,9 @@ pf_status pf_prefix_bwd_inject(const pf_attn_desc* desc, int32_t prefix_len, pf_
 /* Tree forward (HARTS §2.1: positions with equal token prefixes share one
  * compact row; §2.2: full attention reads ancestor K/V through a tree mask).
  * Nodes are numbered in DFS preorder: parent[0] = -1, parent[i] < i, and a
- * node's subtree occupies consecutive node numbers.  Node i owns compact
+ * node's subtree occupies consecutive node numbers.  A later node with
+ * parent -1 starts another tree of a forest; rows of different trees never
+ * see each other (several rollout trees in one call).  Node i owns compact
  * rows [node_off[i], node_off[i+1]).  A row sees the rows of every strict
  * ancestor of its node and the rows of its own node up to itself.
  *   node_off host [n_nodes + 1], parent host [n_nodes]   in

@@ -126,8 +126,9 @@ pf_status check_tree(int32_t n, const int32_t* node_off, const int32_t* parent, 
   if (node_off[0] != 0) return fail(PF_ERR_INVALID_ARG, "node_off[0] must be 0");
   for (int i = 0; i < n; ++i)
     if (node_off[i + 1] < node_off[i]) return fail(PF_ERR_INVALID_ARG, "node_off decreases at %d", i + 1);
-  if (parent[0] != -1) return fail(PF_ERR_INVALID_ARG, "parent[0] must be -1 (node 0 is the root)");
+  if (parent[0] != -1) return fail(PF_ERR_INVALID_ARG, "parent[0] must be -1 (node 0 is a root)");
   for (int i = 1; i < n; ++i) {
+    if (parent[i] == -1) continue;   // the root of the next tree of a forest
     if (parent[i] < 0 || parent[i] >= i)
       return fail(PF_ERR_INVALID_ARG, "parent[%d] = %d: nodes must be numbered in preorder", i, parent[i]);
     // preorder: the parent of node i is node i-1 or one of its ancestors
@@ -139,7 +140,8 @@ pf_status check_tree(int32_t n, const int32_t* node_off, const int32_t* parent, 
   }
   for (int i = 0; i < n; ++i) subtree_end[i] = node_off[i + 1];
   for (int i = n - 1; i >= 1; --i)
-    if (subtree_end[i] > subtree_end[parent[i]]) subtree_end[parent[i]] = subtree_end[i];
+    if (parent[i] >= 0 && subtree_end[i] > subtree_end[parent[i]])
+      subtree_end[parent[i]] = subtree_end[i];
   return PF_OK;
 }
 

@@ -135,6 +135,33 @@ def test_rejects_bad_trees():
     assert subtree([0, 4, 3], [-1, 0]) == pf.PF_ERR_INVALID_ARG          # offsets decrease
     # 0 -> 1 -> 2 and 0 -> 3, then node 4 claiming parent 1 breaks preorder
     assert subtree([0, 1, 2, 3, 4, 5], [-1, 0, 1, 0, 1]) == pf.PF_ERR_INVALID_ARG
+    # a forest: node 2 starts a second tree; node 3 may not reach into the first
+    assert subtree([0, 4, 6, 9], [-1, 0, -1]) == pf.PF_OK
+    assert subtree([0, 4, 6, 9, 10], [-1, 0, -1, 1]) == pf.PF_ERR_INVALID_ARG
+
+
+def test_forest_visibility_rule_matches_ancestor_mask():
+    """Several random trees numbered one after another (each root's parent -1):
+    the subtree-end rule equals the oracle's ancestor mask, so rows of
+    different trees never see each other."""
+    for seed in range(30):
+        rng = np.random.default_rng(100 + seed)
+        parent, node_off = [], [0]
+        for t in range(int(rng.integers(2, 5))):
+            no, pa = random_tree(1000 * seed + t, int(rng.integers(1, 7)), max_len=4, min_len=0)
+            base = len(parent)
+            parent += [x + base if x >= 0 else -1 for x in pa]
+            node_off += [int(x) + node_off[-1] for x in no[1:]]
+        node_off = np.asarray(node_off, dtype=np.int32)
+        parent = np.asarray(parent, dtype=np.int32)
+        if node_off[-1] == 0:
+            continue
+        end = pf.pf_tree_subtree_end(node_off, parent)
+        c = int(node_off[-1])
+        node = np.searchsorted(node_off, np.arange(c), side="right") - 1
+        rows = np.arange(c)
+        rule = (rows[None, :] <= rows[:, None]) & (rows[:, None] < end[node][None, :])
+        np.testing.assert_array_equal(rule, tree_ancestor_mask(node_off, parent), err_msg=str(seed))
 
 
 def test_tree_visibility_rule_matches_ancestor_mask():

@@ -43,3 +43,22 @@ def test_phase_b_work_at_the_headline_group():
     assert pairs * cfg.num_q_heads == 570_490_880
     flops = 12.0 * cfg.head_dim * pairs * cfg.num_q_heads
     assert round(flops / 1e9, 2) == 876.27
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_ranges_window_pairs_match_the_masks(seed):
+    """A window under a producer node sees every row of its cached ranges plus
+    its own tree pairs: brute force over the combined tree's ancestor mask
+    (the consumer's root a child of the node)."""
+    from workloads.gen import ancestor_row_ranges
+    node_off_p, parent_p = random_tree(30 + seed, 8, max_len=6, min_len=1)
+    u = int(np.argmax(np.arange(len(parent_p))))      # the last node
+    ranges = ancestor_row_ranges(node_off_p, parent_p, u)
+    no_c, pa_c = random_tree(40 + seed, 6, max_len=5, min_len=0)
+    cp = int(node_off_p[-1])
+    n_p = len(parent_p)
+    parent = np.concatenate([parent_p, np.where(pa_c < 0, u, pa_c + n_p)]).astype(np.int32)
+    node_off = np.concatenate([node_off_p, no_c[1:] + cp]).astype(np.int32)
+    vis = tree_ancestor_mask(node_off, parent)
+    w = {"node_off": no_c, "parent": pa_c, "ranges": ranges}
+    assert bench.ranges_window_pairs(w) == int(vis[cp:].sum())

@@ -330,6 +330,27 @@ def test_config6_tree_windows_full_size():
         ref_gv += ref["gv"]
     check("gK (4 windows)", gk[:, g:g + 1], ref_gk, tol)
     check("gV (4 windows)", gv[:, g:g + 1], ref_gv, tol)
+    # the benchmark runs the four trees as one call (a forest over the prefix)
+    from workloads.gen import forest
+    no, pa = forest([(wd["node_off"], wd["parent"]) for wd in data["windows"]])
+    cat = {n: np.concatenate([wd[n] for wd in data["windows"]], axis=0)
+           for n in ("q", "k", "v", "do")}
+    tt = {n: dev(x, cfg.dtype) for n, x in cat.items()}
+    fgk = torch.zeros(p, cfg.num_kv_heads, cfg.head_dim, device="cuda")
+    fgv = torch.zeros_like(fgk)
+    fo, flse = G.tree_suffix_fwd(desc, k_p, v_p, no, pa, tt["q"], tt["k"], tt["v"])
+    fdq, fdk, fdv = G.tree_suffix_bwd(desc, k_p, v_p, no, pa, tt["q"], tt["k"], tt["v"], fo, flse,
+                                      tt["do"], fgk, fgv)
+    torch.cuda.synchronize()
+    r0 = 0
+    for w, (o, lse, dq, dk, dv) in enumerate(outs):
+        r1 = r0 + o.shape[0]
+        for name, x, y in (("O", fo[r0:r1], o), ("dQ", fdq[r0:r1], dq), ("dK", fdk[r0:r1], dk),
+                           ("dV", fdv[r0:r1], dv), ("LSE", flse[:, r0:r1], lse)):
+            check(f"one call vs window {w}: {name}", host(x), y, tol)
+        r0 = r1
+    check("one call gK (g)", host(fgk)[:, g:g + 1], ref_gk, tol)
+    check("one call gV (g)", host(fgv)[:, g:g + 1], ref_gv, tol)
     print(f"  oracle Phase A/C, KV head {g}", flush=True)
     ro, rl = oracle.prefix_forward(data["q_p"][:, hs], kp, vp, scale, hmap)
     check("O_P", o_p[:, hs], ro, tol)
@@ -389,3 +410,72 @@ def test_config7_compact_logprob_full_size():
         check(f"logp[row {r}]", logp[torch.from_numpy(sub_pos.astype(np.int64)).cuda()]
               .cpu().double().numpy(), ref["logp"][sub_pos], tol)
         check(f"dz[{r}]", dz[r:r + 1].float().cpu().double().numpy(), ref["dz"], tol)
+
+
+@pytest.mark.timeout(1200)
+def test_config8_windows_under_producer_full_size():
+    """Per-node caches at the measured size: the producer tree (10240 compact
+    rows), its forward; 8 windows, each hung under a depth-2 node and reading
+    the 3584 rows of that node and its ancestors in place, adding into the
+    producer rows' gK/gV; the producer backward with them injected.  The
+    oracle recomputes one KV-head group: every window (gather, window
+    attention, scatter-add), the accumulated gK/gV, and the producer's
+    forward and injected backward."""
+    cfg = get_config(8)
+    print(f"\ngenerating config {cfg.cid}", flush=True)
+    data = generate(cfg)
+    desc = _desc(cfg)
+    node_off, parent = data["node_off"], data["parent"]
+    c = int(node_off[-1])
+    t = {n: dev(data[n], cfg.dtype) for n in ("q", "k", "v", "do")}
+    o_c, lse_c = G.tree_fwd(desc, node_off, parent, t["q"], t["k"], t["v"])
+    gk = torch.zeros(c, cfg.num_kv_heads, cfg.head_dim, device="cuda")
+    gv = torch.zeros_like(gk)
+    outs = []
+    for wd in data["windows"]:
+        tw = {n: dev(wd[n], cfg.dtype) for n in ("q", "k", "v", "do")}
+        o, lse = G.tree_suffix_fwd_ranges(desc, t["k"], t["v"], wd["ranges"], wd["node_off"],
+                                          wd["parent"], tw["q"], tw["k"], tw["v"])
+        dq, dk, dv = G.tree_suffix_bwd_ranges(desc, t["k"], t["v"], wd["ranges"], wd["node_off"],
+                                              wd["parent"], tw["q"], tw["k"], tw["v"], o, lse,
+                                              tw["do"], gk, gv)
+        outs.append(tuple(host(x) for x in (o, lse, dq, dk, dv)))
+    dq_c, dk_c, dv_c = G.tree_bwd_inject(desc, node_off, parent, t["q"], t["k"], t["v"], o_c,
+                                         lse_c, t["do"], gk, gv)
+    torch.cuda.synchronize()
+    o_c, dq_c, dk_c, dv_c, gk, gv = (host(x) for x in (o_c, dq_c, dk_c, dv_c, gk, gv))
+    for x in (o_c, dq_c, dk_c, dv_c, gk, gv):
+        assert np.all(np.isfinite(x))
+    g = 3
+    hs = _heads_of(cfg, g)
+    scale = 1.0 / math.sqrt(cfg.head_dim)
+    hmap = np.zeros(cfg.group_size, dtype=np.int64)
+    tol = TOL[cfg.dtype]
+    kc, vc = data["k"][:, g:g + 1], data["v"][:, g:g + 1]
+    ref_gk = np.zeros((c, 1, cfg.head_dim))
+    ref_gv = np.zeros_like(ref_gk)
+    for w, (wd, (o, lse, dq, dk, dv)) in enumerate(zip(data["windows"], outs)):
+        print(f"  oracle window {w} under node {wd['under']} ({int(wd['node_off'][-1])} rows), "
+              f"KV head {g}", flush=True)
+        ref = oracle.tree_window_attention_ranges(kc, vc, wd["ranges"], wd["q"][:, hs],
+                                                  wd["k"][:, g:g + 1], wd["v"][:, g:g + 1],
+                                                  wd["do"][:, hs], wd["node_off"], wd["parent"],
+                                                  scale, hmap)
+        check(f"O[w{w}]", o[:, hs], ref["o"], tol)
+        check(f"LSE[w{w}]", lse[hs], ref["lse"], tol)
+        check(f"dQ[w{w}]", dq[:, hs], ref["dq"], tol)
+        check(f"dK[w{w}]", dk[:, g:g + 1], ref["dk"], tol)
+        check(f"dV[w{w}]", dv[:, g:g + 1], ref["dv"], tol)
+        ref_gk += ref["gk"]
+        ref_gv += ref["gv"]
+    check("gK (8 windows)", gk[:, g:g + 1], ref_gk, tol)
+    check("gV (8 windows)", gv[:, g:g + 1], ref_gv, tol)
+    print(f"  oracle producer tree, KV head {g}", flush=True)
+    rp = oracle.tree_attention_direct(data["q"][:, hs], kc, vc, data["do"][:, hs], node_off,
+                                      parent, scale, hmap, backward=False)
+    check("producer O", o_c[:, hs], rp["o"], tol)
+    rdq, rdk, rdv = oracle.tree_backward_inject(data["q"][:, hs], kc, vc, data["do"][:, hs],
+                                                node_off, parent, ref_gk, ref_gv, scale, hmap)
+    check("producer dQ", dq_c[:, hs], rdq, tol)
+    check("producer dK (injected)", dk_c[:, g:g + 1], rdk, tol)
+    check("producer dV (injected)", dv_c[:, g:g + 1], rdv, tol)

@@ -14,6 +14,7 @@ import oracle
 from tests.gpu_util import TOL, check, dev, host
 from workloads.gen import (
     ancestor_row_ranges,
+    forest,
     node_depths,
     random_small_group,
     random_tree,
@@ -531,3 +532,48 @@ def test_windows_under_producer_nodes(hq, hkv):
     for name, x, y in (("O", o2, o1), ("LSE", l2, l1), ("dQ", r2[0], r1[0]), ("dK", r2[1], r1[1]),
                        ("dV", r2[2], r1[2]), ("gK", a2, a1), ("gV", b2, b1)):
         check(f"one range vs flat prefix: {name}", host(x), host(y), 1e-6)
+
+
+def test_forest_window_in_one_call():
+    """Three rollout trees over one cached prefix in one call (a forest): each
+    tree's rows against the oracle's forest window (rows of different trees
+    never see each other), the prefix gradients against the oracle, and the
+    same values as one call per tree to the bf16 bar."""
+    hq, hkv, d, dtype, p = 8, 2, 128, "bf16", 200
+    desc = _desc(hq, hkv, d, dtype)
+    scale = 1.0 / math.sqrt(d)
+    hmap = oracle.head_map(hq, hkv)
+    tol = TOL[dtype]
+    g = random_small_group(44, hq, hkv, d, p, [1], dtype)
+    kp, vp = dev(g["k_p"], dtype), dev(g["v_p"], dtype)
+    trees = [random_tree(s, n, max_len=ml, min_len=1) for s, n, ml in ((70, 7, 60), (71, 1, 90),
+                                                                      (72, 10, 30))]
+    groups = [random_tree_group(s, t[0], hq, hkv, d, dtype) for s, t in zip((70, 71, 72), trees)]
+    node_off, parent = forest(trees)
+    print(f"\nforest node_off {node_off.tolist()} parent {parent.tolist()}", flush=True)
+    cat = {k: np.concatenate([gg[k] for gg in groups], axis=0) for k in ("q", "k", "v", "do")}
+    tt = {k: dev(cat[k], dtype) for k in cat}
+    o, lse = G.tree_suffix_fwd(desc, kp, vp, node_off, parent, tt["q"], tt["k"], tt["v"])
+    gk = torch.zeros(p, hkv, d, device="cuda")
+    gv = torch.zeros_like(gk)
+    dq, dk, dv = G.tree_suffix_bwd(desc, kp, vp, node_off, parent, tt["q"], tt["k"], tt["v"], o, lse,
+                                   tt["do"], gk, gv)
+    gk1 = torch.zeros_like(gk)
+    gv1 = torch.zeros_like(gk)
+    sep = []
+    for (no, pa), gg in zip(trees, groups):
+        ts = {k: dev(gg[k], dtype) for k in ("q", "k", "v", "do")}
+        o1, l1 = G.tree_suffix_fwd(desc, kp, vp, no, pa, ts["q"], ts["k"], ts["v"])
+        r1 = G.tree_suffix_bwd(desc, kp, vp, no, pa, ts["q"], ts["k"], ts["v"], o1, l1, ts["do"],
+                               gk1, gv1)
+        sep.append((o1, l1) + tuple(r1))
+    torch.cuda.synchronize()
+    ref = oracle.tree_window_attention(g["k_p"], g["v_p"], cat["q"], cat["k"], cat["v"], cat["do"],
+                                       node_off, parent, scale, hmap)
+    for name, got in (("O", o), ("LSE", lse), ("dQ", dq), ("dK", dk), ("dV", dv), ("gK", gk),
+                      ("gV", gv)):
+        check(f"forest {name}", host(got), ref[name.lower()], tol)
+    cat_sep = [torch.cat([s[i] for s in sep], dim=1 if i == 1 else 0) for i in range(5)]
+    for name, x, y in zip(("O", "LSE", "dQ", "dK", "dV"), (o, lse, dq, dk, dv), cat_sep):
+        check(f"forest vs one call per tree: {name}", host(x), host(y), tol)
+    check("forest vs one call per tree: gK", host(gk), host(gk1), tol)

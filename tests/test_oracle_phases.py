@@ -409,3 +409,39 @@ def test_window_over_producer_ancestors_equals_combined_tree(seed):
     for s, n in ranges:
         used[s:s + n] = True
     assert np.all(win["gk"][~used] == 0) and np.abs(win["gk"][used]).max() > 0
+
+
+def test_forest_window_equals_separate_windows():
+    """Several rollout trees over one cached prefix in one call (a forest: each
+    root has parent -1) equal one window per tree: rows of different trees
+    never see each other (HARTS §2.1), every tree sees the whole prefix, and
+    the prefix-side gradients add."""
+    p = 5
+    hmap = head_map(4, 2)
+    rng = np.random.default_rng(7)
+    k_p, v_p = rng.standard_normal((p, 2, 8)), rng.standard_normal((p, 2, 8))
+    trees = [random_tree(s, n, max_len=4, min_len=1) for s, n in ((1, 4), (2, 1), (3, 5))]
+    groups = [{k: np.asarray(v, np.float64) for k, v in random_tree_group(s, t[0], 4, 2, 8).items()}
+              for s, t in zip((1, 2, 3), trees)]
+    parent, node_off, base_n, base_r = [], [0], 0, 0
+    for no, pa in trees:
+        parent += [x + base_n if x >= 0 else -1 for x in pa]
+        node_off += [int(x) + base_r for x in no[1:]]
+        base_n += len(pa)
+        base_r += int(no[-1])
+    parent = np.asarray(parent, np.int32)
+    node_off = np.asarray(node_off, np.int32)
+    cat = {k: np.concatenate([g[k] for g in groups], axis=0) for k in groups[0]}
+    f = tree_window_attention(k_p, v_p, cat["q"], cat["k"], cat["v"], cat["do"], node_off, parent,
+                              0.4, hmap)
+    r0 = 0
+    gk = np.zeros_like(k_p)
+    for (no, pa), g in zip(trees, groups):
+        r1 = r0 + int(no[-1])
+        s = tree_window_attention(k_p, v_p, g["q"], g["k"], g["v"], g["do"], no, pa, 0.4, hmap)
+        for key in ("o", "dq", "dk", "dv"):
+            np.testing.assert_allclose(f[key][r0:r1], s[key], atol=1e-12, err_msg=key)
+        np.testing.assert_allclose(f["lse"][:, r0:r1], s["lse"], atol=1e-12)
+        gk += s["gk"]
+        r0 = r1
+    np.testing.assert_allclose(f["gk"], gk, atol=1e-12)

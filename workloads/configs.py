@@ -32,6 +32,10 @@ class Config:
     windows: int = 0
     window_nodes: int = 0
     node_len_range: Optional[Tuple[int, int]] = None
+    window_calls: int = 0      # calls the windows are run in (0: one per window)
+    # windows under the deepest nodes of a producer tree (tree_levels) instead
+    # of over a flat prefix: each window reads its node's and ancestors' rows
+    under_producer: bool = False
     # compact log-probabilities: vocabulary of the compact-row logits (the
     # rows and positions are those of tree_levels)
     logprob_vocab: int = 0
@@ -40,11 +44,15 @@ class Config:
 
     @property
     def is_tree(self) -> bool:
-        return self.tree_levels is not None
+        return self.tree_levels is not None and not self.under_producer
 
     @property
     def is_windows(self) -> bool:
-        return self.windows > 0
+        return self.windows > 0 and not self.under_producer
+
+    @property
+    def is_ranges(self) -> bool:
+        return self.windows > 0 and self.under_producer
 
     @property
     def is_logprob(self) -> bool:
@@ -72,10 +80,20 @@ CONFIGS: List[Config] = [
            note="DFS-preorder compact rows: root 4096, 4 children of 1024, 4 leaves of 256 each; "
                 "12288 compact rows, 16 trajectories"),
     Config(6, "windows-bf16-p4096-4x24-irregular", "bf16", 32, 8, 128, 4096, windows=4,
-           window_nodes=24, node_len_range=(32, 256), seed=6,
+           window_nodes=24, node_len_range=(32, 256), window_calls=1, seed=6,
            note="the next row after the five groups: 4 sharing windows over one cached 4096-row "
                 "prefix, each an irregular tree of 24 nodes (each node's parent uniform over the "
-                "earlier nodes, lengths uniform on [32, 256]), one call per window"),
+                "earlier nodes, lengths uniform on [32, 256]); the 4 trees run as one call (a "
+                "forest over the prefix)"),
+    Config(8, "windows-under-tree-bf16-2048-4x1024-8x512", "bf16", 32, 8, 128, 0,
+           tree_levels=((1, 2048), (4, 1024), (2, 512)), windows=8, window_nodes=24,
+           node_len_range=(32, 256), under_producer=True, seed=8,
+           note="per-node caches: a producer rollout tree (root 2048 rows, 4 children of 1024, "
+                "each with 2 children of 512; 10240 compact rows) and 8 consumer windows, each an "
+                "irregular tree of 24 nodes hung under one of the 8 depth-2 nodes and reading the "
+                "3584 rows of that node and its ancestors in place; producer forward, the 8 "
+                "windows forward and backward adding into the producer rows' gK/gV, then the "
+                "producer backward with them injected"),
     Config(7, "logprob-bf16-tree5-v151936", "bf16", 16, 4, 128, 0,
            tree_levels=((1, 4096), (4, 1024), (4, 256)), logprob_vocab=151936, seed=7,
            note="compact log-probabilities of the config-5 tree: 12288 compact rows of bf16 "

@@ -110,6 +110,32 @@ def generate(cfg: Config, include_prefix_q: bool = True) -> Dict[str, np.ndarray
                          "do": _normal(rng, (c, hq, d), cfg.dtype)})
         out["windows"] = wins
         return out
+    if cfg.is_ranges:
+        # the producer tree's rows, then each window's tree (seed 100 seed + w)
+        # and rows; window w hangs under the w-th deepest node
+        node_off, parent = tree_layout(cfg.tree_levels)
+        c = int(node_off[-1])
+        out["node_off"], out["parent"] = node_off, parent
+        out["q"] = _normal(rng, (c, hq, d), cfg.dtype)
+        out["k"] = _normal(rng, (c, hkv, d), cfg.dtype)
+        out["v"] = _normal(rng, (c, hkv, d), cfg.dtype)
+        out["do"] = _normal(rng, (c, hq, d), cfg.dtype)
+        depth = node_depths(parent)
+        deepest = [int(x) for x in np.flatnonzero(depth == depth.max())]
+        lo, hi = cfg.node_len_range
+        wins = []
+        for w in range(cfg.windows):
+            u = deepest[w % len(deepest)]
+            wno, wpa = random_tree(100 * cfg.seed + w, cfg.window_nodes, max_len=hi, min_len=lo)
+            rows = int(wno[-1])
+            wins.append({"under": u, "ranges": ancestor_row_ranges(node_off, parent, u),
+                         "node_off": wno, "parent": wpa,
+                         "q": _normal(rng, (rows, hq, d), cfg.dtype),
+                         "k": _normal(rng, (rows, hkv, d), cfg.dtype),
+                         "v": _normal(rng, (rows, hkv, d), cfg.dtype),
+                         "do": _normal(rng, (rows, hq, d), cfg.dtype)})
+        out["windows"] = wins
+        return out
     if cfg.is_logprob:
         # structure only; the C x V logits are drawn on the device by the caller
         node_off, parent = tree_layout(cfg.tree_levels)
@@ -269,3 +295,14 @@ def node_depths(parent: np.ndarray) -> np.ndarray:
     for v in range(1, len(parent)):
         d[v] = d[parent[v]] + 1
     return d
+
+
+def forest(trees):
+    """One node table for several trees numbered one after another (each
+    root's parent -1): (node_off, parent)."""
+    parent, node_off = [], [0]
+    for no, pa in trees:
+        base = len(parent)
+        parent += [int(x) + base if x >= 0 else -1 for x in pa]
+        node_off += [int(x) + node_off[-1] for x in no[1:]]
+    return np.asarray(node_off, dtype=np.int32), np.asarray(parent, dtype=np.int32)
