@@ -271,13 +271,15 @@ __device__ __forceinline__ uint32_t dma_lane_off(int wave, int lane, uint32_t st
   return (uint32_t)r * st_b + ((((uint32_t)lane & 15) ^ swz(r)) << 4);
 }
 
-// ROWS rows (a multiple of 16) into `tile`, issued by every wave of the group
-template <int ROWS>
+// ROWS rows into `tile`, issued by every one of the group's WAVES waves (each
+// moves 4 rows per load)
+template <int ROWS, int WAVES = 4>
 __device__ __forceinline__ void dma_rows(Rsrc res, uint32_t lane_off, uint32_t st_b, lds_t* tile,
                                          int wave) {
+  static_assert(ROWS % (4 * WAVES) == 0, "rows must cover every wave");
 #pragma unroll
-  for (int i = 0; i < ROWS / 16; ++i)
-    lds_dma16(res, tile + (16 * i + 4 * wave) * kRowB, lane_off, i * 16 * st_b);
+  for (int i = 0; i < ROWS / (4 * WAVES); ++i)
+    lds_dma16(res, tile + (4 * WAVES * i + 4 * wave) * kRowB, lane_off, i * 4 * WAVES * st_b);
 }
 
 // completes this wave's staging loads (a barrier then publishes them)
@@ -1532,9 +1534,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_ds_kernel(AttnArgs a, Part
 // ---------------------------------------------------------------------------
 // Backward, KV-stationary: dK, dV.
 //
-// A workgroup owns 256 keys of one KV head (64 per wave, as two 32-key column
-// tiles) and walks query steps of 32 tokens x one query head over every head
-// of the group.  The query range of a key block is [0, rows) for external
+// A workgroup owns 256 keys of one KV head and walks query steps of 32 tokens
+// x one query head over every head of the group.  Each wave owns KT 32-key
+// column tiles: four waves of 64 keys (one per SIMD, 512 registers each, every
+// Q/dO fragment read from LDS feeding two products), or eight waves of 32 keys
+// (two per SIMD, 128 VGPRs and the 128 AGPRs of their dK/dV accumulators).  The query range of a key block is [0, rows) for external
 // keys and [k0, max kend) for own keys; it is split into chunks of the
 // (query tile, head) index space when the grid needs more workgroups, and each
 // chunk writes an fp32 partial that a fixed-order reduce sums.  K fragments
@@ -1550,8 +1554,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_ds_kernel(AttnArgs a, Part
 // load per M1 product pair.
 constexpr int kQStep = 32;
 static_assert(kQStep == kDsStep, "the dS^T store and the dQ pass share the step");
-constexpr int kKeysPerWave = 64;
-constexpr int kKeysPerWg = 4 * kKeysPerWave;
+constexpr int kKeysPerWg = 256;
+// 32-key tiles per wave: two (four waves, one per SIMD) when a call has
+// external keys, one (eight waves, two per SIMD) otherwise.  Measured on one
+// box at config 2: the eight-wave form takes the same time for Phase B's
+// dK/dV (0.658-0.664 ms against 0.651-0.660) and 6 % less for Phase C's
+// (0.330-0.334 against 0.350-0.355 ms).
+constexpr int kDkvKTExt = 2, kDkvKTOwn = 1;
 constexpr int kStepTile = kQStep * kRowB;
 constexpr int kDkvBufs = 4;
 constexpr int kDkvQ = 0;                                  // Q step buffers
@@ -1560,7 +1569,6 @@ constexpr int kDkvV = 2 * kDkvBufs * kStepTile;           // V rows of the workg
 constexpr int kDkvL = kDkvV + kKeysPerWg * kRowB;         // per buffer: 64 LSE values (log2)
 constexpr int kDkvD = kDkvL + kDkvBufs * 256;             // per buffer: 64 D values
 constexpr int kDkvBytes = kDkvD + kDkvBufs * 256;
-constexpr int kDkvDma = 2 * (kQStep / 16) + 2;            // staging loads per wave per step
 
 // value k of a packed bf16 fragment, as fp32
 __device__ __forceinline__ float unpack_bf16(const bf16x8& v, int k) { return (float)v[k]; }
@@ -1568,17 +1576,38 @@ __device__ __forceinline__ float unpack_bf16(const bf16x8& v, int k) { return (f
 // One workgroup's key block: external (prefix) keys, which every query row
 // sees unmasked, or own keys; the two are separate instantiations so the
 // external path carries no masking code.
-template <bool EXT>
+// The dK/dV accumulators stay in AGPRs for any KT: with two waves per SIMD
+// (KT = 1) the compiler gives a wave that uses AGPRs 128 of each file, and the
+// 32 keys' dK and dV accumulators are exactly 128 registers.
+template <int KT>
+__device__ __forceinline__ void fence_dkv(f32x16 (&x)[kD / 32][KT], f32x16 (&y)[kD / 32][KT]) {
+  if constexpr (KT == 2) {
+    fence_acc(x, y);
+  } else {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+a"(x[0][0]), "+a"(x[1][0]), "+a"(x[2][0]), "+a"(x[3][0]), "+a"(y[0][0]),
+                   "+a"(y[1][0]), "+a"(y[2][0]), "+a"(y[3][0]));
+  }
+}
+
+template <bool EXT, int KT>
 __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int chunk, int nch,
                                           char* smem) {
   constexpr bool ext = EXT;
+  constexpr int WAVES = 8 / KT;                   // waves of the workgroup
+  constexpr int KPW = 32 * KT;                    // keys per wave
+  constexpr int NQL = kQStep / (4 * WAVES);       // Q (and dO) staging loads per wave per step
+  constexpr int kDma = 2 * NQL + 2;               // staging loads per wave per step
+  constexpr int NE = 16 * KT;                     // P (or dS) values per lane per step
+  constexpr int RING = KT == 2 ? 3 : 2;           // fragment ring slots (read RING - 1 pairs ahead)
+  static_assert(WAVES * KPW == kKeysPerWg, "a workgroup holds kKeysPerWg keys");
   lds_t* const sb = (lds_t*)smem;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int col = lane & 31, h32 = lane >> 5;
   const int k0 = kb * kKeysPerWg;
   const int klim = ext ? a.n_ext : a.rows;
-  const int kw0 = k0 + wave * kKeysPerWave;      // this wave's first key
+  const int kw0 = k0 + wave * KPW;               // this wave's first key
 
   // query range (tokens) and the (tile, head) index range of this workgroup
   int qlo, qhi;
@@ -1606,10 +1635,10 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
   // wave's two 32-key tiles into registers; visibility bounds of the keys.
   // Keys past the end get zero K/V; their (discarded) gradients are the only
   // values they influence, so they need no mask.
-  bf16x8 kf[2][kD / 16];
-  int kend_k[2];
-  bool kvalid[2];
-  int krow[2];       // row of the lane's key in k/v (and gK/gV for external keys)
+  bf16x8 kf[KT][kD / 16];
+  int kend_k[KT];
+  bool kvalid[KT];
+  int krow[KT];       // row of the lane's key in k/v (and gK/gV for external keys)
   int wave_kend_min = 0x7fffffff;
   // external keys as row ranges of a larger tensor (tile table), or not
   const int2* tiles = ext ? a.ext_tiles : nullptr;
@@ -1622,26 +1651,28 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
       const uint32_t st_b = 2u * (uint32_t)vst;
       const uint32_t loff = dma_lane_off(wave, lane, st_b);
       if (tiles) {
-        // 16-row passes, each inside one 32-key tile and read from its rows
+        // passes of 4 WAVES rows, each inside one 32-key tile and read from its rows
         const __bf16* vg = vbase + (int64_t)g * vsh;
+        constexpr int VRS = 4 * WAVES;
 #pragma unroll
-        for (int i = 0; i < kKeysPerWg / 16; ++i) {
-          const int vr = k0 + 16 * i;
+        for (int i = 0; i < kKeysPerWg / VRS; ++i) {
+          const int vr = k0 + VRS * i;
           int first = 0, valid = 0;
           if (vr < klim) {
             first = ld_uniform((const int32_t*)tiles, 2 * (vr >> 5)) + (vr & 31);
             valid = ld_uniform((const int32_t*)tiles, 2 * (vr >> 5) + 1) - (vr & 31);
           }
           lds_dma16(row_rsrc(vg + (int64_t)first * vst, valid, st_b),
-                    sb + kDkvV + (16 * i + 4 * wave) * kRowB, loff, 0u);
+                    sb + kDkvV + (VRS * i + 4 * wave) * kRowB, loff, 0u);
         }
       } else {
-        dma_rows<kKeysPerWg>(row_rsrc(vbase + (int64_t)k0 * vst + (int64_t)g * vsh, klim - k0, st_b),
-                             loff, st_b, sb + kDkvV, wave);
+        dma_rows<kKeysPerWg, WAVES>(
+            row_rsrc(vbase + (int64_t)k0 * vst + (int64_t)g * vsh, klim - k0, st_b), loff, st_b,
+            sb + kDkvV, wave);
       }
     }
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < KT; ++kt) {
       const int kk = kw0 + kt * 32 + col;
       kvalid[kt] = kk < klim;
       krow[kt] = kk;
@@ -1657,7 +1688,7 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
       if (kvalid[kt]) wave_kend_min = min(wave_kend_min, kend_k[kt]);
     }
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
       for (int ds = 0; ds < kD / 16; ++ds)
         if (!kvalid[kt]) kf[kt][ds] = zero8();
@@ -1665,7 +1696,7 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1)
     wave_kend_min = min(wave_kend_min, __shfl_xor(wave_kend_min, off));
-  const int wave_khi = min(kw0 + kKeysPerWave, klim) - 1;   // last valid key of the wave
+  const int wave_khi = min(kw0 + KPW, klim) - 1;   // last valid key of the wave
 
   FragC f;
   {
@@ -1675,7 +1706,7 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
   }
   // this wave's V fragments: rows 64 wave + l % 32 (+ 32 per tile); the base
   // is a multiple of 256 bytes, so the XOR form applies to it as well
-  uint32_t vrow0 = kDkvV + wave * kKeysPerWave * kRowB + f.row8_0;
+  uint32_t vrow0 = kDkvV + wave * KPW * kRowB + f.row8_0;
 
   // staging sources: Q and dO rows of every query head (a step selects one
   // head and 32 tokens by the scalar offset; rows past the end read zero),
@@ -1713,16 +1744,18 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
       ++iss_qt;
     }
   };
-  // staging load k (0..kDkvDma-1) of the current step into buffer B
+  // staging load k (0..kDma-1) of the current step into buffer B: NQL loads
+  // of Q rows, NQL of dO rows (each wave moves 4 rows per load), then LSE, D
   auto stage_load = [&](auto bc, int k) {
     constexpr int B = decltype(bc)::value;
-    if (k < 2) {
-      lds_dma16(q_res, sb + kDkvQ + B * kStepTile + (16 * k + 4 * wave) * kRowB, q_loff,
-                st_q + 16u * (uint32_t)k * q_st_b);
-    } else if (k < 4) {
-      lds_dma16(do_res, sb + kDkvO + B * kStepTile + (16 * (k - 2) + 4 * wave) * kRowB, do_loff,
-                st_do + 16u * (uint32_t)(k - 2) * do_st_b);
-    } else if (k == 4) {
+    constexpr int RS = 4 * WAVES;                 // rows one load moves over the group
+    if (k < NQL) {
+      lds_dma16(q_res, sb + kDkvQ + B * kStepTile + (RS * k + 4 * wave) * kRowB, q_loff,
+                st_q + (uint32_t)(RS * k) * q_st_b);
+    } else if (k < 2 * NQL) {
+      lds_dma16(do_res, sb + kDkvO + B * kStepTile + (RS * (k - NQL) + 4 * wave) * kRowB,
+                do_loff, st_do + (uint32_t)(RS * (k - NQL)) * do_st_b);
+    } else if (k == 2 * NQL) {
       lds_dma4(l_res, sb + kDkvL + B * 256, 4u * lane, st_l);
     } else {
       lds_dma4(d_res, sb + kDkvD + B * 256, 4u * lane, st_l);
@@ -1731,24 +1764,24 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
   auto stage_all = [&](auto bc) {
     stage_begin();
 #pragma unroll
-    for (int k = 0; k < kDkvDma; ++k) stage_load(bc, k);
+    for (int k = 0; k < kDma; ++k) stage_load(bc, k);
   };
 
   const float c = a.scale_log2;
-  f32x16 dk[kD / 32][2], dv[kD / 32][2];
+  f32x16 dk[kD / 32][KT], dv[kD / 32][KT];
 #pragma unroll
   for (int dt = 0; dt < kD / 32; ++dt)
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < KT; ++kt) {
       dk[dt][kt] = zero16();
       dv[dt][kt] = zero16();
     }
-  fence_acc(dk, dv);
+  fence_dkv<KT>(dk, dv);
 
   // Per-lane elements of a step's 32 x 32 tiles (C layout): element (kt, i)
   // is query row 8 (i / 4) + 4 h32 + i % 4 of the step, key kw0 + 32 kt + col.
-  f32x16 s[2], dp[2];          // S then P (fp32) / dP then dS of a step
-  bf16x8 pb[2][2], db[2][2];   // packed P and dS: [key tile][query half]
+  f32x16 s[KT], dp[KT];        // S then P (fp32) / dP then dS of a step
+  bf16x8 pb[KT][2], db[KT][2]; // packed P and dS: [key tile][query half]
 
   // LSE (log2) and D of one 4-row group of a step (rows 8 (k & 3) + 4 h32 + r
   // of group k = 0..7, the same rows for both key tiles), double-buffered: each
@@ -1768,7 +1801,7 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
   auto p_elem = [&](auto blc, auto ec) {
     constexpr int e = decltype(ec)::value;
     constexpr int kt = e >> 4, i = e & 15, k = e >> 2, r = i & 3;
-    if constexpr (r == 0 && k + 1 < 8) ld_l(blc, std::integral_constant<int, k + 1>());
+    if constexpr (r == 0 && k + 1 < 4 * KT) ld_l(blc, std::integral_constant<int, k + 1>());
     s[kt][i] = fast_exp2(fmaf(s[kt][i], c, -lg[k & 1][r]));
     // formed here, beside this step's products (not moved to its first use)
     asm volatile("" : "+v"(s[kt][i]));
@@ -1782,7 +1815,7 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
   auto ds_elem = [&](auto bdc, auto ec) {
     constexpr int e = decltype(ec)::value;
     constexpr int kt = e >> 4, i = e & 15, k = e >> 2, r = i & 3;
-    if constexpr (r == 0 && k + 1 < 8) ld_d(bdc, std::integral_constant<int, k + 1>());
+    if constexpr (r == 0 && k + 1 < 4 * KT) ld_d(bdc, std::integral_constant<int, k + 1>());
     dp[kt][i] = unpack_bf16(pb[kt][i >> 3], i & 7) * (dp[kt][i] - dg[k & 1][r]);
     asm volatile("" : "+v"(dp[kt][i]));
     if constexpr ((i & 7) == 7) {
@@ -1793,12 +1826,12 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
   // invisible entries of a step's S (own keys) become -inf
   auto mask_s = [&](int t0) {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < KT; ++kt) {
       const int kk = kw0 + kt * 32 + col;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int tq = t0 + 8 * (i >> 2) + 4 * h32 + (i & 3);
-        const bool vis = kk <= tq && tq < kend_k[kt];
+        const int vis = (kk <= tq ? 1 : 0) & (tq < kend_k[kt] ? 1 : 0);
         s[kt][i] = vis ? s[kt][i] : -INFINITY;
       }
     }
@@ -1815,10 +1848,10 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
   //   pairs 24-31  dP of step t + 1        with  P of step t + 1 (second half)
   // Every pair's A fragment (and the two V fragments of a dP pair) is read
   // from LDS two pairs ahead through a three-slot ring, across the runs.
-  bf16x8 fr[3], vr[3][2];
+  bf16x8 fr[RING], vr[RING][KT];
   auto frag = [&](auto bc, auto pc) {
     constexpr int B = decltype(bc)::value, B1 = (B + 1) % kDkvBufs;
-    constexpr int p = decltype(pc)::value, run = p >> 3, idx = p & 7, sl = p % 3;
+    constexpr int p = decltype(pc)::value, run = p >> 3, idx = p & 7, sl = p % RING;
     if constexpr (run == 0) {
       fr[sl] = ld_row8(sb + kDkvQ + B1 * kStepTile + f.row8(idx));
     } else if constexpr (run == 1 || run == 2) {
@@ -1827,45 +1860,47 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
     } else {
       fr[sl] = ld_row8(sb + kDkvO + B1 * kStepTile + f.row8(idx));
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < KT; ++kt)
         vr[sl][kt] = ld_row8(sb + kt * 32 * kRowB + (vrow0 ^ (uint32_t)(idx << 5)));
     }
   };
   auto step = [&](auto bc, __bf16* ds_dst, int t0n) {
     constexpr int B = decltype(bc)::value;
     constexpr int B1 = (B + 1) % kDkvBufs, B3 = (B + 3) % kDkvBufs;
-    frag(bc, std::integral_constant<int, 0>());
-    frag(bc, std::integral_constant<int, 1>());
+    static_for<0, RING - 1>([&](auto pc) { frag(bc, pc); });
     static_for<0, 32>([&](auto pc) {
-      constexpr int p = decltype(pc)::value, run = p >> 3, idx = p & 7, sl = p % 3;
+      constexpr int p = decltype(pc)::value, run = p >> 3, idx = p & 7, sl = p % RING;
       constexpr int hf = idx >> 2, dt = idx & 3;
-      if constexpr (p + 2 < 32) frag(bc, std::integral_constant<int, p + 2>());
+      if constexpr (p + RING - 1 < 32) frag(bc, std::integral_constant<int, p + RING - 1>());
+      // this pair's share of the step's NE P or dS values: KT of them, from `base`
+      auto elems = [&](auto&& fn, auto base) {
+        static_for<0, KT>([&](auto jc) {
+          fn(std::integral_constant<int, decltype(base)::value + KT * idx + decltype(jc)::value>());
+        });
+      };
       if constexpr (run == 0) {
         if constexpr (idx == 0) {
-          s[0] = zero16();
-          s[1] = zero16();
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt) s[kt] = zero16();
         }
-        s[0] = mfma(fr[sl], kf[0][idx], s[0]);
-        s[1] = mfma(fr[sl], kf[1][idx], s[1]);
-        ds_elem(bc, std::integral_constant<int, 2 * idx>());
-        ds_elem(bc, std::integral_constant<int, 2 * idx + 1>());
-        if constexpr (idx < kDkvDma) stage_load(Buf<B3>(), idx);
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) s[kt] = mfma(fr[sl], kf[kt][idx], s[kt]);
+        elems([&](auto ec) { ds_elem(bc, ec); }, std::integral_constant<int, 0>());
+        if constexpr (idx < kDma) stage_load(Buf<B3>(), idx);
       } else if constexpr (run == 1) {
-        mfma_acc(dv[dt][0], fr[sl], pb[0][hf]);
-        mfma_acc(dv[dt][1], fr[sl], pb[1][hf]);
-        ds_elem(bc, std::integral_constant<int, 16 + 2 * idx>());
-        ds_elem(bc, std::integral_constant<int, 17 + 2 * idx>());
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) mfma_acc(dv[dt][kt], fr[sl], pb[kt][hf]);
+        elems([&](auto ec) { ds_elem(bc, ec); }, std::integral_constant<int, NE / 2>());
         // group 0 of the LSE of step t + 1 (lg[0] is free from here)
         if constexpr (idx == 4) ld_l(Buf<B1>(), std::integral_constant<int, 0>());
       } else if constexpr (run == 2) {
-        mfma_acc(dk[dt][0], fr[sl], db[0][hf]);
-        mfma_acc(dk[dt][1], fr[sl], db[1][hf]);
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) mfma_acc(dk[dt][kt], fr[sl], db[kt][hf]);
         if constexpr (idx == 0) {
           if (step_needs_mask(t0n)) mask_s(t0n);
         }
-        p_elem(Buf<B1>(), std::integral_constant<int, 2 * idx>());
-        p_elem(Buf<B1>(), std::integral_constant<int, 2 * idx + 1>());
-        if constexpr (idx < 4) {
+        elems([&](auto ec) { p_elem(Buf<B1>(), ec); }, std::integral_constant<int, 0>());
+        if constexpr (idx < 2 * KT) {
           // dS^T of this step for the dQ pass: key tile idx / 2, query half idx % 2
           if (ds_dst)
             *(bf16x8*)(ds_dst + (int64_t)(idx >> 1) * (a.ds_rows / kQStep) * 32 * kQStep +
@@ -1876,13 +1911,12 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
         if constexpr (idx == 4) ld_d(Buf<B1>(), std::integral_constant<int, 0>());
       } else {
         if constexpr (idx == 0) {
-          dp[0] = zero16();
-          dp[1] = zero16();
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt) dp[kt] = zero16();
         }
-        dp[0] = mfma(fr[sl], vr[sl][0], dp[0]);
-        dp[1] = mfma(fr[sl], vr[sl][1], dp[1]);
-        p_elem(Buf<B1>(), std::integral_constant<int, 16 + 2 * idx>());
-        p_elem(Buf<B1>(), std::integral_constant<int, 17 + 2 * idx>());
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) dp[kt] = mfma(fr[sl], vr[sl][kt], dp[kt]);
+        elems([&](auto ec) { p_elem(Buf<B1>(), ec); }, std::integral_constant<int, NE / 2>());
       }
       __builtin_amdgcn_sched_barrier(0);
     });
@@ -1894,22 +1928,23 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
     const lds_t* q_s = sb + kDkvQ + BQ * kStepTile;
     const lds_t* d_s = sb + kDkvO + BQ * kStepTile;
     ld_l(bqc, std::integral_constant<int, 0>());
-    s[0] = zero16();
-    s[1] = zero16();
-    dp[0] = zero16();
-    dp[1] = zero16();
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+      s[kt] = zero16();
+      dp[kt] = zero16();
+    }
 #pragma unroll
     for (int ds = 0; ds < kD / 16; ++ds) {
       const bf16x8 qa = ld_row8(q_s + f.row8(ds));
-      s[0] = mfma(qa, kf[0][ds], s[0]);
-      s[1] = mfma(qa, kf[1][ds], s[1]);
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) s[kt] = mfma(qa, kf[kt][ds], s[kt]);
       const bf16x8 da = ld_row8(d_s + f.row8(ds));
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < KT; ++kt)
         dp[kt] = mfma(da, ld_row8(sb + kt * 32 * kRowB + (vrow0 ^ (uint32_t)(ds << 5))), dp[kt]);
     }
     if (step_needs_mask(t0)) mask_s(t0);
-    static_for<0, 32>([&](auto ec) { p_elem(bqc, ec); });
+    static_for<0, NE>([&](auto ec) { p_elem(bqc, ec); });
     ld_d(bqc, std::integral_constant<int, 0>());
   };
 
@@ -1955,9 +1990,9 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
       // the vector memory counter also counts the dS^T stores issued after
       // this iteration's staging loads: leave both in flight
       if (ds_dst)
-        dma_wait_n<kDkvDma + 4>();
+        dma_wait_n<kDma + 2 * KT>();
       else
-        dma_wait_n<kDkvDma>();
+        dma_wait_n<kDma>();
       lds_barrier();
     };
     for (int it = it_lo; it < it_hi; it += kDkvBufs) {
@@ -1974,14 +2009,14 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
 
   // lane holds key kw0 + 32 kt + col, d = 32 dt + 8 j + 4 h32 + r.  One
   // (key tile, d tile) at a time, so the epilogue reads 32 accumulators at once.
-  fence_acc(dk, dv);
+  fence_dkv<KT>(dk, dv);
   // destination: 0 add into gK/gV, 1 external partial, 2 own partial, 3 own output.
   // The first query chunk of a split external block adds into gK/gV itself
   // (no other workgroup touches those elements during the launch); chunks
   // 1.. write partial planes 0.. that the finishing pass adds afterwards, so
   // every element is acc + c0 + (c1 + c2 + ...), a fixed order.
   const int mode = ext ? ((nch == 1 || chunk == 0) ? 0 : 1) : (nch > 1 ? 2 : 3);
-  static_for<0, 2>([&](auto ktc) {
+  static_for<0, KT>([&](auto ktc) {
     constexpr int kt = decltype(ktc)::value;
     const int kk = kw0 + kt * 32 + col;
     const int64_t base = ((int64_t)kk * a.hkv + g) * kD;         // partial planes: virtual keys
@@ -2038,7 +2073,8 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
   });
 }
 
-__global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(AttnArgs a, ItemOrder ord) {
+template <int KT>
+__global__ __launch_bounds__(64 * 8 / KT, 1) void bwd_dkv_kernel(AttnArgs a, ItemOrder ord) {
   __shared__ __attribute__((aligned(16))) char smem[kDkvBytes];
   const int n_ext_kb = (a.n_ext + kKeysPerWg - 1) / kKeysPerWg;
   const int n_own_kb = (a.rows + kKeysPerWg - 1) / kKeysPerWg;
@@ -2049,11 +2085,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(AttnArgs a, ItemOr
   if (ord.n == items) item = ord.item[item];
   if (item < n_ext_kb * a.n_chunks) {
     const int kb = item / a.n_chunks;
-    dkv_block<true>(a, g, kb, item - kb * a.n_chunks, a.n_chunks, smem);
+    dkv_block<true, KT>(a, g, kb, item - kb * a.n_chunks, a.n_chunks, smem);
   } else {
     const int oi = item - n_ext_kb * a.n_chunks;
     const int kb = oi / a.n_chunks_own;
-    dkv_block<false>(a, g, kb, oi - kb * a.n_chunks_own, a.n_chunks_own, smem);
+    dkv_block<false, KT>(a, g, kb, oi - kb * a.n_chunks_own, a.n_chunks_own, smem);
   }
 }
 
@@ -2141,8 +2177,12 @@ hipError_t launch_bwd_dkv_bf16(const AttnArgs& a, const ItemOrder& ord, int32_t 
   const int items = n_ext_kb * a.n_chunks + n_own_kb * a.n_chunks_own;
   if (items <= 0) return hipSuccess;
   if (ord.n != 0 && ord.n != items) return hipErrorInvalidValue;
-  PF_LAUNCH("pf_bwd_dkv_bf16", bwd_dkv_kernel, dim3(grid_for(a.hkv, items)), dim3(kThreads),
-            stream, a, ord);
+  if (a.n_ext > 0)
+    PF_LAUNCH("pf_bwd_dkv_bf16", bwd_dkv_kernel<kDkvKTExt>, dim3(grid_for(a.hkv, items)),
+              dim3(64 * 8 / kDkvKTExt), stream, a, ord);
+  else
+    PF_LAUNCH("pf_bwd_dkv_bf16", bwd_dkv_kernel<kDkvKTOwn>, dim3(grid_for(a.hkv, items)),
+              dim3(64 * 8 / kDkvKTOwn), stream, a, ord);
   return hipGetLastError();
 }
 
