@@ -9,14 +9,16 @@
 // so both directions stream C x V once or twice and never form S x V.
 // Positions come grouped by row: pos[row_ptr[c] .. row_ptr[c + 1]) (device).
 //
-// One workgroup per compact row, 256 threads, 16-byte loads; the HBM stream of
-// the row is the bound.  Index arrays live on the device, so the kernels
+// Forward: one workgroup per compact row; backward: one per chunk of a row
+// (the softmax needs only the row's lse and gradient sum); 256 threads,
+// 16-byte loads, the HBM stream of the logits is the bound.  Index arrays live on the device, so the kernels
 // check every index against its range and skip what falls outside (a position
 // with an out-of-range target gets NaN); nothing is read or written out of
 // bounds.  No atomics: the row sums are fixed-order reductions and each dz
-// element is written by one thread (target columns are rewritten, in the same
-// workgroup after a barrier, with their position terms added in position
-// order).
+// element is written by one thread (target columns are rewritten, by the
+// workgroup of their chunk after a barrier, with their position terms added in
+// position order).
+#include <float.h>
 #include <math.h>
 
 #include "pf_internal.h"
@@ -25,6 +27,11 @@ namespace pf {
 namespace {
 
 constexpr int kLpThreads = 256;
+// target 8-column vectors per backward workgroup.  Measured on 12288 rows of
+// 151936 bf16 logits: 768 (three vectors a thread) streams 5.9 TB/s; 512 loses
+// to each workgroup's set-up, 1024 to 8192 lose 2 to 10 % as fewer, longer
+// workgroups spread their streams over more rows at once.
+constexpr int kLpBwdChunkVec = 768;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -47,6 +54,53 @@ __device__ __forceinline__ void load8(const char* row, int v0, float (&x)[8]) {
   }
 }
 
+// the 16 (bf16) or 32 (fp32) raw bytes of eight consecutive logits, loaded
+// ahead of their use and converted later (raw keeps the bf16 form in 4 VGPRs)
+template <bool BF16>
+struct Raw8 {
+  uint4 w[BF16 ? 1 : 2];
+};
+template <bool BF16>
+__device__ __forceinline__ Raw8<BF16> load_raw8(const char* row, int v0) {
+  Raw8<BF16> r;
+  if constexpr (BF16) {
+    r.w[0] = *(const uint4*)(row + 2 * (int64_t)v0);
+  } else {
+    r.w[0] = *(const uint4*)(row + 4 * (int64_t)v0);
+    r.w[1] = *(const uint4*)(row + 4 * (int64_t)v0 + 16);
+  }
+  return r;
+}
+// the U vectors v0 + u * kLpThreads (u < U) of a group, the ones at or past
+// nvec left unloaded
+template <bool BF16, int U>
+__device__ __forceinline__ void load_group(const char* row, int v0, int nvec, Raw8<BF16> (&r)[U]);
+
+template <bool BF16>
+__device__ __forceinline__ void unpack8(const Raw8<BF16>& r, float (&x)[8]) {
+  if constexpr (BF16) {
+    const uint32_t u[4] = {r.w[0].x, r.w[0].y, r.w[0].z, r.w[0].w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      x[2 * k] = __uint_as_float(u[k] << 16);
+      x[2 * k + 1] = __uint_as_float(u[k] & 0xffff0000u);
+    }
+  } else {
+    const uint4 a = r.w[0], b = r.w[1];
+    x[0] = __uint_as_float(a.x); x[1] = __uint_as_float(a.y);
+    x[2] = __uint_as_float(a.z); x[3] = __uint_as_float(a.w);
+    x[4] = __uint_as_float(b.x); x[5] = __uint_as_float(b.y);
+    x[6] = __uint_as_float(b.z); x[7] = __uint_as_float(b.w);
+  }
+}
+
+template <bool BF16, int U>
+__device__ __forceinline__ void load_group(const char* row, int v0, int nvec, Raw8<BF16> (&r)[U]) {
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (v0 + u * kLpThreads < nvec) r[u] = load_raw8<BF16>(row, 8 * (v0 + u * kLpThreads));
+}
+
 template <bool BF16>
 __device__ __forceinline__ float load1(const char* row, int v) {
   if constexpr (BF16) return (float)*(const __bf16*)(row + 2 * (int64_t)v);
@@ -57,6 +111,25 @@ template <bool BF16>
 __device__ __forceinline__ void store1(char* row, int v, float x) {
   if constexpr (BF16) *(__bf16*)(row + 2 * (int64_t)v) = (__bf16)x;
   else *(float*)(row + 4 * (int64_t)v) = x;
+}
+
+// eight results as one streaming (non-temporal) store: dz is written once and
+// not read again by this kernel
+template <bool BF16>
+__device__ __forceinline__ void store8_nt(char* row, int v0, const float (&x)[8]) {
+  if constexpr (BF16) {
+    typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    bf16x8 w;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w[e] = (__bf16)x[e];
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, w), (u32x4*)(row + 2 * (int64_t)v0));
+  } else {
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store(f32x4{x[0], x[1], x[2], x[3]}, (f32x4*)(row + 4 * (int64_t)v0));
+    __builtin_nontemporal_store(f32x4{x[4], x[5], x[6], x[7]},
+                                (f32x4*)(row + 4 * (int64_t)v0 + 16));
+  }
 }
 
 template <bool BF16>
@@ -83,52 +156,66 @@ __device__ __forceinline__ Lse2 lse_merge(Lse2 a, Lse2 b) {
   return Lse2{m, a.l * fexp2(a.m - m) + b.l * fexp2(b.m - m)};
 }
 
-// the workgroup's sum of per-thread values, in a fixed order
-__device__ __forceinline__ float block_sum(float x, float* red) {
+// Adds the U vectors r (valid: the first n_valid of them) to the running
+// log-sum-exp acc of this thread (log2 units).  The running maximum moves
+// only when a value exceeds it by more than kLpRescale (then the sum is
+// rescaled once), so each logit costs one exponential, and every term stays
+// below 2^kLpRescale.  The raw vectors are converted twice (once for the
+// maximum, once for the sum) rather than held as U x 8 floats.
+constexpr float kLpRescale = 8.0f;
+template <bool BF16, int U>
+__device__ __forceinline__ void lse_add(Lse2& acc, const Raw8<BF16> (&r)[U], int n_valid) {
+  float m = -INFINITY;
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  if (lane == 0) red[wave] = x;
-  __syncthreads();
-  const float t = (red[0] + red[1]) + (red[2] + red[3]);
-  __syncthreads();
-  return t;
+  for (int u = 0; u < U; ++u) {
+    if (u < n_valid) {
+      float x[8];
+      unpack8<BF16>(r[u], x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m = fmaxf(m, x[e]);
+    }
+  }
+  m *= kLog2e;
+  if (m > acc.m + kLpRescale) {
+    acc.l *= fexp2(acc.m - m);   // 0 while acc.m is still -FLT_MAX
+    acc.m = m;
+  }
+  float l = 0.f;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (u < n_valid) {
+      float x[8];
+      unpack8<BF16>(r[u], x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) l += fexp2(fmaf(x[e], kLog2e, -acc.m));
+    }
+  }
+  acc.l += l;
 }
 
 // log-sum-exp (natural log) of one row, every thread of the workgroup
 template <bool BF16>
 __device__ float row_lse(const char* row, int vocab, float* red) {
-  Lse2 acc{-INFINITY, 0.f};
+  // -FLT_MAX, not -inf, so that a row of -inf logits sums to 0 without NaN
+  Lse2 acc{-FLT_MAX, 0.f};
   const int nvec = vocab / 8;
-  constexpr int U = 4;   // vectors in flight per thread
-  int i = threadIdx.x;
-  for (; i + (U - 1) * kLpThreads < nvec; i += U * kLpThreads) {
-    float x[U][8];
-#pragma unroll
-    for (int u = 0; u < U; ++u) load8<BF16>(row, 8 * (i + u * kLpThreads), x[u]);
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float m = x[u][0];
-#pragma unroll
-      for (int e = 1; e < 8; ++e) m = fmaxf(m, x[u][e]);
-      m *= kLog2e;
-      float l = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) l += fexp2(fmaf(x[u][e], kLog2e, -m));
-      acc = lse_merge(acc, Lse2{m, l});
+  constexpr int U = 4;   // vectors per group; the next group's loads are issued first
+  constexpr int G = U * kLpThreads;
+  // two register sets in turn, each refilled with the group two ahead as
+  // soon as its own group is summed
+  auto add_group = [&](const Raw8<BF16>(&r)[U], int i) {
+    lse_add<BF16, U>(acc, r, (nvec - i + kLpThreads - 1) / kLpThreads);
+  };
+  Raw8<BF16> ra[U], rb[U];
+  load_group<BF16, U>(row, threadIdx.x, nvec, ra);
+  load_group<BF16, U>(row, threadIdx.x + G, nvec, rb);
+  for (int i = threadIdx.x; i < nvec; i += 2 * G) {
+    add_group(ra, i);
+    if (i + 2 * G < nvec) load_group<BF16, U>(row, i + 2 * G, nvec, ra);
+    if (i + G < nvec) {
+      add_group(rb, i + G);
+      if (i + 3 * G < nvec) load_group<BF16, U>(row, i + 3 * G, nvec, rb);
     }
-  }
-  for (; i < nvec; i += kLpThreads) {
-    float x[8];
-    load8<BF16>(row, 8 * i, x);
-    float m = x[0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) m = fmaxf(m, x[e]);
-    m *= kLog2e;
-    float l = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) l += fexp2(fmaf(x[e], kLog2e, -m));
-    acc = lse_merge(acc, Lse2{m, l});
   }
   for (int v = 8 * nvec + threadIdx.x; v < vocab; v += kLpThreads) {
     const float m = load1<BF16>(row, v) * kLog2e;
@@ -189,56 +276,80 @@ __global__ __launch_bounds__(kLpThreads) void logprob_fwd_kernel(LpArgs a) {
   }
 }
 
+// Backward, one workgroup per chunk of a row: chunk k of row c covers the
+// 8-column vectors [k * chunk_vec, min(nvec, (k + 1) * chunk_vec)) (the last
+// chunk also the columns past the last whole vector).  Chunks of one row are
+// adjacent in dispatch order, so the workgroups in flight stream a window of
+// consecutive rows, as a plain elementwise pass does.
 template <bool BF16>
-__global__ __launch_bounds__(kLpThreads) void logprob_bwd_kernel(LpArgs a) {
-  __shared__ float red[8];
-  const int c = blockIdx.x;
+__global__ __launch_bounds__(kLpThreads) void logprob_bwd_kernel(LpArgs a, int32_t chunk_vec,
+                                                                 int32_t n_chunks) {
+  const int c = blockIdx.x / n_chunks;
+  const int k = blockIdx.x - c * n_chunks;
   const char* row = a.z + (int64_t)c * a.z_stride_b;
   char* drow = a.dz + (int64_t)c * a.dz_stride_b;
+  const int nvec = a.vocab / 8;
+  const int v_lo = k * chunk_vec;
+  const int v_hi = min(nvec, v_lo + chunk_vec);
+  const bool last = k == n_chunks - 1;
+  // the first two groups of logits are requested before anything else: they
+  // do not depend on the position gradients
+  constexpr int U = 4;
+  constexpr int G = U * kLpThreads;
+  Raw8<BF16> ra[U], rb[U];
+  load_group<BF16, U>(row, v_lo + threadIdx.x, v_hi, ra);
+  load_group<BF16, U>(row, v_lo + G + threadIdx.x, v_hi, rb);
   int b, e;
   row_range(a, c, b, e);
-  // g = sum of the row's position gradients (valid positions and targets)
+  // g = sum of the row's position gradients (valid positions and targets),
+  // summed by every wave on its own in the same order: no barrier
+  const int lane = threadIdx.x & 63;
   float part = 0.f;
-  for (int i = b + threadIdx.x; i < e; i += kLpThreads) {
+  for (int i = b + lane; i < e; i += 64) {
     const int p = a.pos[i];
     if (p < 0 || p >= a.n_pos) continue;
     const int t = a.y[p];
     if (t >= 0 && t < a.vocab) part += a.dlogp[p];
   }
-  const float g = block_sum(part, red);
-  const float lse2 = a.lse[c] * kLog2e;
-  // dense part: dz = -g softmax(z), four vectors in flight per thread
-  const int nvec = a.vocab / 8;
-  constexpr int U = 4;
-  int i = threadIdx.x;
-  for (; i + (U - 1) * kLpThreads < nvec; i += U * kLpThreads) {
-    float x[U][8];
 #pragma unroll
-    for (int u = 0; u < U; ++u) load8<BF16>(row, 8 * (i + u * kLpThreads), x[u]);
+  for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
+  const float g = part;
+  const float lse2 = a.lse[c] * kLog2e;
+  // dense part: dz = -g softmax(z) in groups of U vectors per thread, two
+  // register sets in turn: a set is refilled with the group two ahead as soon
+  // as its own group is written, so the other set's loads stay in flight
+  auto softmax_grad = [&](const Raw8<BF16>(&r)[U], int i) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      if (i + u * kLpThreads < v_hi) {
+        float x[8];
+        unpack8<BF16>(r[u], x);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) x[u][k] = -g * fexp2(fmaf(x[u][k], kLog2e, -lse2));
-      store8<BF16>(drow, 8 * (i + u * kLpThreads), x[u]);
+        for (int q = 0; q < 8; ++q) x[q] = -g * fexp2(fmaf(x[q], kLog2e, -lse2));
+        store8_nt<BF16>(drow, 8 * (i + u * kLpThreads), x);
+      }
+    }
+  };
+  for (int i = v_lo + threadIdx.x; i < v_hi; i += 2 * G) {
+    softmax_grad(ra, i);
+    if (i + 2 * G < v_hi) load_group<BF16, U>(row, i + 2 * G, v_hi, ra);
+    if (i + G < v_hi) {
+      softmax_grad(rb, i + G);
+      if (i + 3 * G < v_hi) load_group<BF16, U>(row, i + 3 * G, v_hi, rb);
     }
   }
-  for (; i < nvec; i += kLpThreads) {
-    float x[8];
-    load8<BF16>(row, 8 * i, x);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) x[k] = -g * fexp2(fmaf(x[k], kLog2e, -lse2));
-    store8<BF16>(drow, 8 * i, x);
-  }
-  for (int v = 8 * nvec + threadIdx.x; v < a.vocab; v += kLpThreads)
-    store1<BF16>(drow, v, -g * fexp2(fmaf(load1<BF16>(row, v), kLog2e, -lse2)));
+  if (last)
+    for (int v = 8 * nvec + threadIdx.x; v < a.vocab; v += kLpThreads)
+      store1<BF16>(drow, v, -g * fexp2(fmaf(load1<BF16>(row, v), kLog2e, -lse2)));
   __syncthreads();   // the dense stores above, then the target columns again
-  // target columns: the first position of each distinct target rewrites it
-  // with every position term of that target added in position order
+  // target columns of this chunk: the first position of each distinct target
+  // rewrites it with every position term of that target added in position order
+  const int col_lo = 8 * v_lo, col_hi = last ? a.vocab : 8 * v_hi;
   for (int i = b + threadIdx.x; i < e; i += kLpThreads) {
     const int p = a.pos[i];
     if (p < 0 || p >= a.n_pos) continue;
     const int t = a.y[p];
-    if (t < 0 || t >= a.vocab) continue;
+    if (t < col_lo || t >= col_hi) continue;
     bool first = true;
     for (int j = b; j < i && first; ++j) {
       const int pj = a.pos[j];
@@ -278,10 +389,20 @@ hipError_t launch_logprob_bwd(int32_t n_rows, int32_t vocab, const void* z, int6
   if (n_rows <= 0) return hipSuccess;
   LpArgs a{n_rows, vocab, n_pos, (const char*)z, z_stride_b, (char*)dz, dz_stride_b, row_ptr, pos,
            y, const_cast<float*>(lse), nullptr, dlogp};
+  // chunks of about kLpBwdChunkVec vectors (12 KB of bf16), equal in size and
+  // a whole number of vectors per thread
+  const int nvec = vocab / 8;
+  const int n_chunks = max(1, (nvec + kLpBwdChunkVec - 1) / kLpBwdChunkVec);
+  const int per = (nvec + n_chunks - 1) / n_chunks;
+  const int chunk_vec = max(kLpThreads, (per + kLpThreads - 1) / kLpThreads * kLpThreads);
+  const int64_t blocks = (int64_t)n_rows * n_chunks;
+  if (blocks > INT32_MAX / kLpThreads) return hipErrorInvalidValue;
   if (bf16)
-    PF_LAUNCH("pf_logprob_bwd", logprob_bwd_kernel<true>, dim3(n_rows), dim3(kLpThreads), stream, a);
+    PF_LAUNCH("pf_logprob_bwd", logprob_bwd_kernel<true>, dim3((uint32_t)blocks), dim3(kLpThreads),
+              stream, a, chunk_vec, n_chunks);
   else
-    PF_LAUNCH("pf_logprob_bwd", logprob_bwd_kernel<false>, dim3(n_rows), dim3(kLpThreads), stream, a);
+    PF_LAUNCH("pf_logprob_bwd", logprob_bwd_kernel<false>, dim3((uint32_t)blocks), dim3(kLpThreads),
+              stream, a, chunk_vec, n_chunks);
   return hipGetLastError();
 }
 

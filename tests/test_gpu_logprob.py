@@ -85,3 +85,38 @@ def test_out_of_range_indices_are_skipped():
     ok[[bad, skipped]] = False
     check("logp (valid positions)", out[ok].astype(np.float64), ref["logp"][ok], TOL["f32"])
     check("dz", dz.cpu().double().numpy(), ref["dz"], TOL["f32"])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_masked_vocabulary_columns(dtype):
+    """Logits of -inf (a padded vocabulary masked out, and scattered masked
+    columns, one whole 8-column vector among them) add nothing to the row's
+    sum and get a zero gradient; the rest matches the oracle.  Targets stay on
+    unmasked columns."""
+    c, v, s, v_real = 10, 9000, 60, 8190
+    g = random_logprob_case(77, c, v, s, dtype)
+    z = g["z"].copy()
+    z[:, v_real:] = -np.inf
+    z[:, 1000:1008] = -np.inf
+    z[:, 5::97] = -np.inf
+    y = (g["y"] % v_real).astype(np.int32)
+    keep = np.ones(v, dtype=bool)
+    keep[v_real:] = False
+    keep[1000:1008] = False
+    keep[5::97] = False
+    y = np.where(keep[y], y, 11).astype(np.int32)
+    zd = _dev_logits(z, dtype)
+    rp, pp, yy = (torch.from_numpy(a).cuda() for a in (g["row_ptr"], g["pos"], y))
+    lse = torch.empty(c, device="cuda")
+    logp = torch.empty(s, device="cuda")
+    pf.pf_compact_logprob_fwd(zd, rp, pp, yy, lse, logp)
+    dz = torch.empty_like(zd)
+    pf.pf_compact_logprob_bwd(zd, lse, rp, pp, yy, torch.from_numpy(g["dlogp"]).cuda(), dz)
+    torch.cuda.synchronize()
+    ref = compact_logprob(z, g["row_ptr"], g["pos"], y, g["dlogp"])
+    tol = TOL[dtype]
+    check("lse", lse.cpu().double().numpy(), ref["lse"], tol)
+    check("logp", logp.cpu().double().numpy(), ref["logp"], tol)
+    got = dz.float().cpu().double().numpy()
+    check("dz", got, ref["dz"], tol)
+    assert np.all(got[:, ~keep] == 0.0)
