@@ -1311,6 +1311,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(AttnArgs a) {
 // on to its last visible row; other steps of that block hold no values and
 // are read as zero here.
 constexpr int kDsStep = 32;                       // query rows per stored dS^T step
+// cache-policy operand of a buffer load: non-temporal (each dS^T value is
+// read once; streaming it measured 6 % off the Phase-B backward at config 2,
+// with the streaming store on the dK/dV side)
+constexpr int kCachePolicyNT = 2;
 constexpr int kDxBN = 32;
 constexpr int kDxTok = 256;
 constexpr int kDxTile = kDxBN * kRowB;
@@ -1400,7 +1404,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_ds_kernel(AttnArgs a, Part
 #pragma unroll
       for (int i = 0; i < BN / 16; ++i)
         r[d][i] = __builtin_amdgcn_raw_buffer_load_b128(
-            dres, (int)d_loff, ((kbs * n_steps + 4 * d) * 32 * kDsStep + 16 * i * 16) * 2, 0);
+            dres, (int)d_loff, ((kbs * n_steps + 4 * d) * 32 * kDsStep + 16 * i * 16) * 2,
+            kCachePolicyNT);
   };
   auto commit = [&](int buf, const u32x4 (&r)[2][BN / 16]) {
     lds_t* base = sb + buf * kDxBufBytes;
@@ -1901,10 +1906,13 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
         }
         elems([&](auto ec) { p_elem(Buf<B1>(), ec); }, std::integral_constant<int, 0>());
         if constexpr (idx < 2 * KT) {
-          // dS^T of this step for the dQ pass: key tile idx / 2, query half idx % 2
+          // dS^T of this step for the dQ pass: key tile idx / 2, query half idx
+          // % 2; a streaming store (read once, by the dQ pass, long after)
           if (ds_dst)
-            *(bf16x8*)(ds_dst + (int64_t)(idx >> 1) * (a.ds_rows / kQStep) * 32 * kQStep +
-                       16 * 32 * (idx & 1)) = db[idx >> 1][idx & 1];
+            __builtin_nontemporal_store(
+                db[idx >> 1][idx & 1],
+                (bf16x8*)(ds_dst + (int64_t)(idx >> 1) * (a.ds_rows / kQStep) * 32 * kQStep +
+                          16 * 32 * (idx & 1)));
         }
         // group 0 of the D of step t + 1, read by the next step's dS (dg[0] is
         // free from here)

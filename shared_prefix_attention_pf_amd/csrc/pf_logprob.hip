@@ -55,19 +55,27 @@ __device__ __forceinline__ void load8(const char* row, int v0, float (&x)[8]) {
 }
 
 // the 16 (bf16) or 32 (fp32) raw bytes of eight consecutive logits, loaded
-// ahead of their use and converted later (raw keeps the bf16 form in 4 VGPRs)
+// ahead of their use and converted later (raw keeps the bf16 form in 4 VGPRs).
+// Streaming (non-temporal) loads: each logit is read once per kernel, and
+// keeping the stream out of the caches' normal replacement measured 6.0 ->
+// 6.8 TB/s for the forward on 12288 x 151936 bf16.
 template <bool BF16>
 struct Raw8 {
   uint4 w[BF16 ? 1 : 2];
 };
+__device__ __forceinline__ uint4 load16_nt(const char* p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 t = __builtin_nontemporal_load((const u32x4*)p);
+  return make_uint4(t[0], t[1], t[2], t[3]);
+}
 template <bool BF16>
 __device__ __forceinline__ Raw8<BF16> load_raw8(const char* row, int v0) {
   Raw8<BF16> r;
   if constexpr (BF16) {
-    r.w[0] = *(const uint4*)(row + 2 * (int64_t)v0);
+    r.w[0] = load16_nt(row + 2 * (int64_t)v0);
   } else {
-    r.w[0] = *(const uint4*)(row + 4 * (int64_t)v0);
-    r.w[1] = *(const uint4*)(row + 4 * (int64_t)v0 + 16);
+    r.w[0] = load16_nt(row + 4 * (int64_t)v0);
+    r.w[1] = load16_nt(row + 4 * (int64_t)v0 + 16);
   }
   return r;
 }
