@@ -681,6 +681,12 @@ __global__ __launch_bounds__(64 * 8 / NT, 1) void fwd_kernel(AttnArgs a) {
     frag_init(ff, lane);
     f.init(ff);
   }
+  // V reads (the only users of the transposed offsets here): the V region's
+  // base folded into the lane offsets (it only sets bits above the swizzled
+  // ones), so buffer and slice offsets fit the LDS instructions' 16-bit
+  // immediate and need no address add
+  f.tr0[0] += (uint32_t)kFwdV;
+  f.tr0[1] += (uint32_t)kFwdV;
   const float c = a.scale_log2;
   float mrow[NT], lrow[NT];                 // running max (log2 units) in use; row-sum share
 #pragma unroll
@@ -874,7 +880,7 @@ __global__ __launch_bounds__(64 * 8 / NT, 1) void fwd_kernel(AttnArgs a) {
     // phase B: O^T += V_j^T P_j^T while the maxima of S_{j+1} are taken.
     // Sixteen steps, one per V fragment (fetched VPD steps ahead), each with
     // NT products and a sixteenth of that VALU work.
-    const lds_t* vt_s = sb + kFwdV + B * kFwdTile;
+    const lds_t* vt_s = sb + B * kFwdTile;   // kFwdV is in fv's offsets
     auto ldv = [&](int fi) {
       const int dt = fi >> 2, ks = fi & 3;
       const lds_t* vb = vt_s + ks * 16 * kRowB;
