@@ -133,22 +133,6 @@ size_t pf_workspace_size(int32_t op, const pf_attn_desc* desc, int32_t prefix_le
 size_t pf_workspace_size_min(int32_t op, const pf_attn_desc* desc, int32_t prefix_len,
                              int32_t rows);
 
-/* The workspace of a bf16 backward whose dS buffer holds a slab of slab_keys
- * keys (rounded up to a multiple of 256) instead of every key, plus an fp32
- * [rows, Hq, d] buffer of dQ sums: num_q_heads x slab x ceil256(rows) x 2 +
- * rows x num_q_heads x head_dim x 4 bytes over pf_workspace_size_min(), so
- * linear in the key count for a fixed slab (Phase C: prefix_len^2 with every
- * key, prefix_len x slab with a slab).  The keys (external, then own, in
- * 256-key blocks) are taken slab by slab: one dK/dV launch and one dQ launch
- * per slab, the dQ sums added in slab order (deterministic; they agree with
- * the one-slab result to rounding).  Any workspace from
- * pf_workspace_size_min() up runs the fastest path that fits it: every key
- * (pf_workspace_size()), else the widest slab whose workspace fits, else the
- * recompute path.  0 for bad arguments; pf_workspace_size_min() for ops that
- * keep no dS buffer. */
-size_t pf_workspace_size_sliced(int32_t op, const pf_attn_desc* desc, int32_t prefix_len,
-                                int32_t rows, int32_t slab_keys);
-
 /* Phase A (PrefixFlow §3.1 "Phase A: prefix forward"): causal attention of
  * the prefix over itself.
  *   q_p [P, Hq, d], k_p, v_p [P, Hkv, d]  in

@@ -25,7 +25,7 @@ PF_MAX_HEADS = 256
 PF_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 EXPORTED = (
-    "pf_workspace_size", "pf_workspace_size_min", "pf_workspace_size_sliced", "pf_prefix_fwd", "pf_suffix_attn_fwd", "pf_suffix_attn_bwd_accum",
+    "pf_workspace_size", "pf_workspace_size_min", "pf_prefix_fwd", "pf_suffix_attn_fwd", "pf_suffix_attn_bwd_accum",
     "pf_suffix_attn_bwd_accum_noalloc", "pf_prefix_bwd_inject", "pf_tree_attn_fwd", "pf_tree_attn_bwd", "pf_tree_suffix_attn_fwd",
     "pf_tree_suffix_attn_bwd_accum", "pf_tree_suffix_attn_fwd_ranges",
     "pf_tree_suffix_attn_bwd_accum_ranges", "pf_ranges_cached_keys", "pf_tree_attn_bwd_inject",
@@ -77,7 +77,6 @@ def _load():
     sigs = {
         "pf_workspace_size": (sz, [i32, D, i32, i32]),
         "pf_workspace_size_min": (sz, [i32, D, i32, i32]),
-        "pf_workspace_size_sliced": (sz, [i32, D, i32, i32, i32]),
         "pf_prefix_fwd": (i32, [D, i32, T, T, T, T, fp, P, sz, P]),
         "pf_suffix_attn_fwd": (i32, [D, i32, T, T, i32, ip, T, T, T, T, fp, P, sz, P]),
         "pf_suffix_attn_bwd_accum": (i32, [D, i32, T, T, i32, ip, T, T, T, T, fp, T, T, T, T,
@@ -200,13 +199,6 @@ def pf_workspace_size(op: int, desc: AttnDesc, prefix_len: int, rows: int) -> in
 def pf_workspace_size_min(op: int, desc: AttnDesc, prefix_len: int, rows: int) -> int:
     d, _keep = desc._c()
     return int(_lib.pf_workspace_size_min(op, ctypes.byref(d), prefix_len, rows))
-
-
-def pf_workspace_size_sliced(op: int, desc: AttnDesc, prefix_len: int, rows: int,
-                             slab_keys: int) -> int:
-    """Bytes of workspace for a backward whose dS buffer holds slab_keys keys."""
-    d, _keep = desc._c()
-    return int(_lib.pf_workspace_size_sliced(op, ctypes.byref(d), prefix_len, rows, slab_keys))
 
 
 def pf_tree_subtree_end(node_off, parent) -> np.ndarray:

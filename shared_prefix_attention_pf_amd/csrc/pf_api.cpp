@@ -7,7 +7,6 @@
 #include <stdio.h>
 #include <string.h>
 
-#include <algorithm>
 #include <mutex>
 #include <string>
 
@@ -229,36 +228,24 @@ struct WsLayout {
   bool use_ds = false;
   size_t ds_ext = 0;
   int32_t ds_keys = 0, ds_rows = 0, ds_own0 = 0;
-  // key slabs: the buffer holds ds_keys of the ds_total_keys keys; with more
-  // than one slab the dQ sums go through an fp32 [rows, Hq, d] buffer
-  int32_t ds_total_keys = 0;
-  size_t dq_acc = 0;
 };
 
 // A bf16 backward keeps dS^T when the workspace allows it (Phase B, Phase C
-// and trees): the buffer holds Hq x K keys x ceil256(rows) rows of bf16, of
-// which only the visible tiles are written and read.  K is every key,
-// ceil256(n_ext) + ceil256(rows), or a slab of them (a multiple of 256;
-// slab_keys, rounded up) taken in turn; one head's share must stay below
-// 2 GiB for 32-bit buffer offsets.
-int64_t ds_slab_keys(int32_t n_ext, int32_t rows, int32_t slab_keys) {
-  const int64_t r = ((int64_t)rows + 255) / 256 * 256;
-  const int64_t keys = ((int64_t)n_ext + 255) / 256 * 256 + r;
-  if (slab_keys <= 0) return keys;
-  return std::min<int64_t>(keys, ((int64_t)slab_keys + 255) / 256 * 256);
-}
-
-bool ds_eligible(int32_t op, const Desc& d, int32_t n_ext, int32_t rows, int32_t slab_keys = 0) {
+// and trees): the buffer holds Hq x (ceil256(n_ext) + ceil256(rows)) keys x
+// ceil256(rows) rows of bf16, of which only the visible tiles are written and
+// read (one head's share must stay below 2 GiB for 32-bit buffer offsets).
+bool ds_eligible(int32_t op, const Desc& d, int32_t n_ext, int32_t rows) {
   if (op != PF_OP_SUFFIX_BWD && op != PF_OP_PREFIX_BWD && op != PF_OP_TREE_BWD &&
       op != PF_OP_TREE_SUFFIX_BWD)
     return false;
   if (d.dtype != PF_BF16 || rows <= 0) return false;
   const int64_t r = ((int64_t)rows + 255) / 256 * 256;
-  return ds_slab_keys(n_ext, rows, slab_keys) * r * 2 < ((int64_t)1 << 31);
+  const int64_t keys = ((int64_t)n_ext + 255) / 256 * 256 + r;
+  return keys * r * 2 < ((int64_t)1 << 31);
 }
 
 WsLayout layout(int32_t op, const Desc& d, int32_t n_ext, int32_t rows, bool want_ds = false,
-                bool split = true, int32_t slab_keys = 0) {
+                bool split = true) {
   WsLayout w;
   size_t off = 0;
   const size_t nb = (size_t)((rows + 31) / 32);
@@ -294,18 +281,13 @@ WsLayout layout(int32_t op, const Desc& d, int32_t n_ext, int32_t rows, bool wan
       w.dv_part = off; off += align_up(part);
     }
   }
-  if (want_ds && ds_eligible(op, d, n_ext, rows, slab_keys)) {
+  if (want_ds && ds_eligible(op, d, n_ext, rows)) {
     w.use_ds = true;
     w.ds_rows = (rows + 255) / 256 * 256;
     w.ds_own0 = (n_ext + 255) / 256 * 256;
-    w.ds_total_keys = w.ds_own0 + w.ds_rows;
-    w.ds_keys = (int32_t)ds_slab_keys(n_ext, rows, slab_keys);
+    w.ds_keys = w.ds_own0 + w.ds_rows;
     w.ds_ext = off;
     off += align_up((size_t)d.hq * w.ds_keys * w.ds_rows * 2);
-    if (w.ds_keys < w.ds_total_keys) {
-      w.dq_acc = off;
-      off += align_up((size_t)rows * d.hq * d.d * 4);
-    }
   }
   w.total = rows > 0 ? off : 0;
   return w;
@@ -328,8 +310,6 @@ void set_ds(pf::AttnArgs& a, void* ws, const WsLayout& w) {
   a.ds_keys = w.ds_keys;
   a.ds_rows = w.ds_rows;
   a.ds_own0 = w.ds_own0;
-  a.ds_key0 = 0;
-  a.dq_acc = w.ds_keys < w.ds_total_keys ? (float*)((char*)ws + w.dq_acc) : nullptr;
 }
 
 // the tile table of a call whose external keys are row ranges
@@ -345,20 +325,7 @@ void set_tiles(pf::AttnArgs& a, void* ws, const WsLayout& w, const pf::RangeTabl
 WsLayout pick_layout(int32_t op, const Desc& d, int32_t n_ext, int32_t rows, size_t ws_bytes,
                      const WsLayout& w_min) {
   const WsLayout w_ds = layout(op, d, n_ext, rows, true);
-  if (w_ds.use_ds && ws_bytes >= w_ds.total) return w_ds;
-  // else the widest key slab that fits: the layout grows by Hq x ceil256(rows)
-  // x 2 bytes per key of the slab
-  if (!ds_eligible(op, d, n_ext, rows, 256)) return w_min;
-  const WsLayout w1 = layout(op, d, n_ext, rows, true, true, 256);
-  if (!w1.use_ds || ws_bytes < w1.total) return w_min;
-  const size_t per_key = (size_t)d.hq * w1.ds_rows * 2;
-  int64_t slab = 256 + (int64_t)((ws_bytes - w1.total) / per_key) / 256 * 256;
-  slab = std::min<int64_t>(slab, w1.ds_total_keys - 256);
-  for (; slab > 256; slab -= 256) {
-    const WsLayout w = layout(op, d, n_ext, rows, true, true, (int32_t)slab);
-    if (w.use_ds && w.total <= ws_bytes) return w;
-  }
-  return w1;
+  return (w_ds.use_ds && ws_bytes >= w_ds.total) ? w_ds : w_min;
 }
 
 void set_own_parts(pf::AttnArgs& a, void* ws, const WsLayout& w) {
@@ -494,35 +461,10 @@ pf_status run_bwd(const Desc& d, const pf::AttnArgs& a, const pf::SegTable& seg,
     // from it, with the split blocks' partial sums in the same launch
     e = pf::launch_prep_dsum_bf16(seg, d.heads, a, st);
     if (e != hipSuccess) return hip_fail(e, "prep");
-    const int32_t total_keys = a.ds_own0 + a.ds_rows;
-    if (a.ds_keys >= total_keys) {
-      e = pf::launch_bwd_dkv_bf16(a, ord, d.d, st);
-      if (e != hipSuccess) return hip_fail(e, "dkv");
-      e = pf::launch_bwd_dq_ds_bf16(a, ps, d.d, st);
-      if (e != hipSuccess) return hip_fail(e, "dq_ds");
-      return PF_OK;
-    }
-    // key slabs in turn: each slab's dK/dV pass fills the buffer with its
-    // keys' dS^T and its dQ pass adds their share into the fp32 sums; the
-    // last one writes dQ and runs the partial sums (every dK/dV pass, and so
-    // every partial plane, is done by then)
-    pf::PartialSums none;
-    memset(&none, 0, sizeof(none));
-    const int32_t n_slabs = (total_keys + a.ds_keys - 1) / a.ds_keys;
-    for (int32_t sl = 0; sl < n_slabs; ++sl) {
-      pf::AttnArgs as = a;
-      as.ds_key0 = sl * a.ds_keys;
-      as.slab_lo = as.ds_key0 / 256;
-      as.slab_hi = std::min(total_keys, as.ds_key0 + a.ds_keys) / 256;
-      as.dq_mode = sl == 0 ? 1 : (sl == n_slabs - 1 ? 3 : 2);
-      pf::ItemOrder so;
-      so.n = 0;
-      pf::dkv_item_order(as, seg, so);
-      e = pf::launch_bwd_dkv_bf16(as, so, d.d, st);
-      if (e != hipSuccess) return hip_fail(e, "dkv");
-      e = pf::launch_bwd_dq_ds_bf16(as, sl == n_slabs - 1 ? ps : none, d.d, st);
-      if (e != hipSuccess) return hip_fail(e, "dq_ds");
-    }
+    e = pf::launch_bwd_dkv_bf16(a, ord, d.d, st);
+    if (e != hipSuccess) return hip_fail(e, "dkv");
+    e = pf::launch_bwd_dq_ds_bf16(a, ps, d.d, st);
+    if (e != hipSuccess) return hip_fail(e, "dq_ds");
     return PF_OK;
   }
   e = pf::launch_prep(seg, d.heads, a.ri, st);
@@ -636,19 +578,6 @@ size_t pf_workspace_size_min(int32_t op, const pf_attn_desc* desc, int32_t prefi
                             : 0;
   if (op < PF_OP_PREFIX_FWD || op > PF_OP_TREE_SUFFIX_BWD) return 0;
   return layout(op, d, n_ext, rows, false).total;
-}
-
-size_t pf_workspace_size_sliced(int32_t op, const pf_attn_desc* desc, int32_t prefix_len,
-                                int32_t rows, int32_t slab_keys) {
-  Desc d;
-  if (check_desc(desc, &d) != PF_OK || rows < 0 || prefix_len < 0 || slab_keys <= 0) return 0;
-  if (op == PF_OP_PREFIX_FWD || op == PF_OP_PREFIX_BWD) rows = prefix_len;
-  const int32_t n_ext = (op == PF_OP_SUFFIX_FWD || op == PF_OP_SUFFIX_BWD ||
-                         op == PF_OP_TREE_SUFFIX_FWD || op == PF_OP_TREE_SUFFIX_BWD)
-                            ? prefix_len
-                            : 0;
-  if (op < PF_OP_PREFIX_FWD || op > PF_OP_TREE_SUFFIX_BWD) return 0;
-  return layout(op, d, n_ext, rows, true, true, slab_keys).total;
 }
 
 pf_status pf_tree_subtree_end(int32_t n_nodes, const int32_t* node_off, const int32_t* parent,

@@ -1384,22 +1384,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_ds_kernel(AttnArgs a, Part
     d_loff = (uint32_t)((lc >> 2) * 32 * kDsStep + ((lc & 3) >> 1) * 16 * 32 + r * 16 +
                         8 * (lc & 1)) * 2u;
   }
-  // key block b of the walk -> its 32-key block in the dS^T store (which
-  // starts at combined key ds_key0)
+  // key block b of the walk -> its 32-key block in the dS^T store
   auto ds_block = [&](int b) {
-    return (src.ext(b) ? b : a.ds_own0 / 32 + (b - walk.n_ext_blocks)) - a.ds_key0 / 32;
-  };
-  // the walk's blocks inside the store's keys [ds_key0, ds_key0 + ds_keys):
-  // [b_start, b_end) (keys are multiples of 256 there)
-  auto walk_index = [&](int key) {
-    return key < a.ds_own0 ? min(key / 32, walk.n_ext_blocks)
-                           : walk.n_ext_blocks + (key - a.ds_own0) / 32;
-  };
-  const int b_start = walk_index(a.ds_key0);
-  const int b_end = walk_index(a.ds_key0 + a.ds_keys);
-  auto next_in = [&](int b) {
-    const int r = b < b_end ? walk.next(b) : -1;
-    return r >= b_end ? -1 : r;
+    return src.ext(b) ? b : a.ds_own0 / 32 + (b - walk.n_ext_blocks);
   };
   // Block b's K rows go to LDS buffer `buf` by staging loads; its dS^T goes
   // through registers (plain loads, two blocks ahead in one of two register
@@ -1466,10 +1453,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_ds_kernel(AttnArgs a, Part
   const int step0 = s0 + 4 * (wave >> 1) + ct0;
   // cur is the block in buffer `buf`, n1 the next (its dS^T in register
   // stage RS ^ 1), n2 the one after (staged during this block into stage RS)
-  int cur = next_in(b_start);
-  // a middle slab with no key this tile sees leaves its dQ sums as they are
-  if (a.dq_mode == 2 && cur < 0) return;
-  int n1 = cur >= 0 ? next_in(cur + 1) : -1;
+  int cur = walk.next(0);
+  int n1 = cur >= 0 ? walk.next(cur + 1) : -1;
   stage(cur, 0, dsr[0]);
   stage(n1, 1, dsr[1]);
   dma_wait();
@@ -1478,7 +1463,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_ds_kernel(AttnArgs a, Part
   int buf = 0;
   auto block = [&](auto rsc) {
     constexpr int RS = decltype(rsc)::value;
-    const int n2 = n1 >= 0 ? next_in(n1 + 1) : -1;
+    const int n2 = n1 >= 0 ? walk.next(n1 + 1) : -1;
     f.fresh();
     stage(n2, buf == 0 ? 2 : buf - 1, dsr[RS]);
     // column tiles of steps this block holds no values for read as zero
@@ -1540,32 +1525,19 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_ds_kernel(AttnArgs a, Part
   dma_wait();
 
   fence_acc(acc);
-  // the slab's sums: alone, or added to the earlier slabs' fp32 sums, then
-  // kept in fp32 for the next slab or scaled and rounded into dQ
-  const int mode = a.dq_mode;
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     const int tok = t0 + 128 * (wave >> 1) + 32 * (ct0 + nt) + ds_col_row(col);
     if (tok >= a.rows) continue;
     __bf16* op = (__bf16*)a.out + (int64_t)tok * a.out_st + (int64_t)head * a.out_sh;
-    float* accp = a.dq_acc + ((int64_t)tok * a.hq + head) * kD;
 #pragma unroll
     for (int dt = 0; dt < kD / 32; ++dt)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const int d = dt * 32 + 8 * jj + 4 * h32;
-        f32x4 v;
+        bf16x4 w;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = acc[dt][nt][4 * jj + r];
-        if (mode >= 2) v += *(const f32x4*)(accp + d);
-        if (mode == 1 || mode == 2) {
-          *(f32x4*)(accp + d) = v;
-        } else {
-          bf16x4 w;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) w[r] = (__bf16)(v[r] * a.scale);
-          *(bf16x4*)(op + d) = w;
-        }
+        for (int r = 0; r < 4; ++r) w[r] = (__bf16)(acc[dt][nt][4 * jj + r] * a.scale);
+        *(bf16x4*)(op + dt * 32 + 8 * jj + 4 * h32) = w;
       }
   }
 }
@@ -1594,29 +1566,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_ds_kernel(AttnArgs a, Part
 constexpr int kQStep = 32;
 static_assert(kQStep == kDsStep, "the dS^T store and the dQ pass share the step");
 constexpr int kKeysPerWg = 256;
-
-// The 256-key blocks one dK/dV launch covers: external blocks [e_lo, e_hi)
-// and own blocks [o_lo, o_hi) (own block j is combined block n_ext_kb + j,
-// the dS store's key order), from the launch's slab [slab_lo, slab_hi).
-struct SlabBlocks {
-  int e_lo, e_hi, o_lo, o_hi;
-  __host__ __device__ int items(const AttnArgs& a) const {
-    return (e_hi - e_lo) * a.n_chunks + (o_hi - o_lo) * a.n_chunks_own;
-  }
-};
-__host__ __device__ inline SlabBlocks slab_blocks(const AttnArgs& a) {
-  const int n_ext_kb = (a.n_ext + kKeysPerWg - 1) / kKeysPerWg;
-  const int n_own_kb = (a.rows + kKeysPerWg - 1) / kKeysPerWg;
-  const int lo = a.slab_lo, hi = a.slab_hi > 0 ? a.slab_hi : n_ext_kb + n_own_kb;
-  auto mn = [](int x, int y) { return x < y ? x : y; };
-  auto mx = [](int x, int y) { return x > y ? x : y; };
-  SlabBlocks b;
-  b.e_lo = mn(lo, n_ext_kb);
-  b.e_hi = mn(hi, n_ext_kb);
-  b.o_hi = mn(mx(hi, n_ext_kb) - n_ext_kb, n_own_kb);
-  b.o_lo = mn(mx(lo, n_ext_kb) - n_ext_kb, b.o_hi);
-  return b;
-}
 // 32-key tiles per wave: two (four waves, one per SIMD) when a call has
 // external keys, one (eight waves, two per SIMD) otherwise.  Measured on one
 // box at config 2: the eight-wave form takes the same time for Phase B's
@@ -2044,7 +1993,7 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
       if (a.ds_ext) {
         const int head = ld_uniform(a.ri.qhead, g * a.group + cj);
         const int64_t n_steps = a.ds_rows / kQStep, nkb = a.ds_keys / 32;
-        const int kbs = ((EXT ? 0 : a.ds_own0) + kw0 - a.ds_key0) / 32;
+        const int kbs = ((EXT ? 0 : a.ds_own0) + kw0) / 32;
         ds_dst = a.ds_ext + (((int64_t)head * nkb + kbs) * n_steps + cqt) * 32 * kQStep + 16 * col +
                  8 * h32;
       }
@@ -2141,20 +2090,20 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
 template <int KT>
 __global__ __launch_bounds__(64 * 8 / KT, 1) void bwd_dkv_kernel(AttnArgs a, ItemOrder ord) {
   __shared__ __attribute__((aligned(16))) char smem[kDkvBytes];
-  const SlabBlocks sl = slab_blocks(a);
-  const int items = sl.items(a);   // per KV head
+  const int n_ext_kb = (a.n_ext + kKeysPerWg - 1) / kKeysPerWg;
+  const int n_own_kb = (a.rows + kKeysPerWg - 1) / kKeysPerWg;
+  const int items = n_ext_kb * a.n_chunks + n_own_kb * a.n_chunks_own;   // per KV head
   int g, item;
   map_block(blockIdx.x, a.hkv, items, g, item);
   if (g >= a.hkv) return;
   if (ord.n == items) item = ord.item[item];
-  const int ext_items = (sl.e_hi - sl.e_lo) * a.n_chunks;
-  if (item < ext_items) {
-    const int j = item / a.n_chunks;
-    dkv_block<true, KT>(a, g, sl.e_lo + j, item - j * a.n_chunks, a.n_chunks, smem);
+  if (item < n_ext_kb * a.n_chunks) {
+    const int kb = item / a.n_chunks;
+    dkv_block<true, KT>(a, g, kb, item - kb * a.n_chunks, a.n_chunks, smem);
   } else {
-    const int oi = item - ext_items;
-    const int j = oi / a.n_chunks_own;
-    dkv_block<false, KT>(a, g, sl.o_lo + j, oi - j * a.n_chunks_own, a.n_chunks_own, smem);
+    const int oi = item - n_ext_kb * a.n_chunks;
+    const int kb = oi / a.n_chunks_own;
+    dkv_block<false, KT>(a, g, kb, oi - kb * a.n_chunks_own, a.n_chunks_own, smem);
   }
 }
 
@@ -2214,9 +2163,10 @@ static int dkv_item_steps(const AttnArgs& a, const SegTable& seg, bool ext, int 
 
 void dkv_item_order(const AttnArgs& a, const SegTable& seg, ItemOrder& ord) {
   ord.n = 0;
-  const SlabBlocks sl = slab_blocks(a);
-  const int n_ext_items = (sl.e_hi - sl.e_lo) * a.n_chunks;
-  const int items = sl.items(a);
+  const int n_ext_kb = (a.n_ext + kKeysPerWg - 1) / kKeysPerWg;
+  const int n_own_kb = (a.rows + kKeysPerWg - 1) / kKeysPerWg;
+  const int n_ext_items = n_ext_kb * a.n_chunks;
+  const int items = n_ext_items + n_own_kb * a.n_chunks_own;
   if (items <= 0 || items > kMaxOrderedItems) return;
   // cost = query steps plus a fixed start-up (K/V loads, pipeline fill and
   // drain, the result write) of about four steps
@@ -2225,7 +2175,7 @@ void dkv_item_order(const AttnArgs& a, const SegTable& seg, ItemOrder& ord) {
     const bool ext = i < n_ext_items;
     const int j = ext ? i : i - n_ext_items;
     const int nch = ext ? a.n_chunks : a.n_chunks_own;
-    cost[i] = 4 + dkv_item_steps(a, seg, ext, (ext ? sl.e_lo : sl.o_lo) + j / nch, j % nch, nch);
+    cost[i] = 4 + dkv_item_steps(a, seg, ext, j / nch, j % nch, nch);
   }
   for (int i = 0; i < items; ++i) ord.item[i] = (uint16_t)i;
   std::stable_sort(ord.item, ord.item + items,
@@ -2236,7 +2186,9 @@ void dkv_item_order(const AttnArgs& a, const SegTable& seg, ItemOrder& ord) {
 hipError_t launch_bwd_dkv_bf16(const AttnArgs& a, const ItemOrder& ord, int32_t head_dim,
                                hipStream_t stream) {
   if (head_dim != kD) return hipErrorInvalidValue;
-  const int items = slab_blocks(a).items(a);
+  const int n_ext_kb = (a.n_ext + kKeysPerWg - 1) / kKeysPerWg;
+  const int n_own_kb = (a.rows + kKeysPerWg - 1) / kKeysPerWg;
+  const int items = n_ext_kb * a.n_chunks + n_own_kb * a.n_chunks_own;
   if (items <= 0) return hipSuccess;
   if (ord.n != 0 && ord.n != items) return hipErrorInvalidValue;
   if (a.n_ext > 0)

@@ -109,18 +109,6 @@ struct AttnArgs {
   // from ds_own0; ds_keys keys and ds_rows rows in all, layout in the
   // kernels) and dQ is then formed from it instead of by recomputing S, dP.
   __bf16* ds_ext; int32_t ds_keys, ds_rows, ds_own0;
-  // Key slabs (a dS buffer narrower than every key): one dK/dV launch and one
-  // dQ launch per slab of 256-key blocks.  The combined key index space is
-  // the one of the dS store (external keys from 0, own keys from ds_own0);
-  // this launch covers its 256-key blocks [slab_lo, slab_hi) (slab_hi == 0:
-  // all of them), and the buffer holds keys [ds_key0, ds_key0 + ds_keys).
-  int32_t slab_lo, slab_hi, ds_key0;
-  // dQ of a slab: 0 the only slab (bf16 dQ out), 1 the first of several
-  // (fp32 dq_acc written), 2 a middle one (dq_acc read, added, written), 3
-  // the last (dq_acc read and added, bf16 dQ out).  dq_acc is fp32 [rows,
-  // Hq, d], unscaled sums.
-  int32_t dq_mode;
-  float* dq_acc;
   RowInfo ri;
   int32_t rows;
   int32_t hq, hkv, group;                 // group = Hq / Hkv

@@ -121,47 +121,6 @@ def test_workspace_sizes():
     assert pf.pf_workspace_size(pf.PF_OP_SUFFIX_FWD, bad, 16, 16) == 0
 
 
-def test_sliced_workspace_sizes():
-    """A dS buffer of one key slab: Hq x slab x ceil256(rows) x 2 bytes plus
-    fp32 dQ sums over the minimal workspace, linear in the prefix length for a
-    fixed slab where every key's buffer grows with its square."""
-    d = pf.AttnDesc(32, 8, 128)
-    op = pf.PF_OP_PREFIX_BWD
-    for p in (4096, 16384):
-        mn = pf.pf_workspace_size_min(op, d, p, p)
-        full = pf.pf_workspace_size(op, d, p, p)
-        s1 = pf.pf_workspace_size_sliced(op, d, p, p, 1024)
-        s2 = pf.pf_workspace_size_sliced(op, d, p, p, 2048)
-        acc = p * 32 * 128 * 4
-        assert s1 - mn >= 32 * 1024 * p * 2 + acc and s1 - mn < 32 * 1024 * p * 2 + acc + 4096
-        assert s2 - s1 >= 32 * 1024 * p * 2 and s2 - s1 < 32 * 1024 * p * 2 + 4096
-        assert mn < s1 < s2 < full
-        # a slab of every key (or more) is the every-key layout
-        assert pf.pf_workspace_size_sliced(op, d, p, p, p) == full
-        assert pf.pf_workspace_size_sliced(op, d, p, p, 10 * p) == full
-        # slabs round up to 256 keys
-        assert pf.pf_workspace_size_sliced(op, d, p, p, 1000) == s1
-    ratio_full = (pf.pf_workspace_size(op, d, 16384, 16384)
-                  / pf.pf_workspace_size(op, d, 4096, 4096))
-    ratio_sliced = (pf.pf_workspace_size_sliced(op, d, 16384, 16384, 1024)
-                    / pf.pf_workspace_size_sliced(op, d, 4096, 4096, 1024))
-    assert ratio_full > 14 and ratio_sliced < 4.5
-    # Phase B: the store holds ceil256(P) external and ceil256(rows) own keys
-    ob = pf.PF_OP_SUFFIX_BWD
-    mn = pf.pf_workspace_size_min(ob, d, 4096, 4096)
-    s = pf.pf_workspace_size_sliced(ob, d, 4096, 4096, 512)
-    assert s - mn >= 32 * 512 * 4096 * 2 + 4096 * 32 * 128 * 4
-    assert pf.pf_workspace_size_sliced(ob, d, 4096, 4096, 8192) == pf.pf_workspace_size(
-        ob, d, 4096, 4096)
-    # forward ops and the fp32 family keep no dS buffer; bad arguments give 0
-    assert pf.pf_workspace_size_sliced(pf.PF_OP_SUFFIX_FWD, d, 64, 64, 256) == \
-        pf.pf_workspace_size_min(pf.PF_OP_SUFFIX_FWD, d, 64, 64)
-    f = pf.AttnDesc(2, 2, 64, pf.PF_F32)
-    assert pf.pf_workspace_size_sliced(ob, f, 256, 256, 256) == pf.pf_workspace_size_min(
-        ob, f, 256, 256)
-    assert pf.pf_workspace_size_sliced(ob, d, 64, 64, 0) == 0
-
-
 def test_rejects_bad_trees():
     def subtree(node_off, parent):
         no = np.asarray(node_off, dtype=np.int32)
