@@ -590,7 +590,7 @@ def stats_summary(stats_csv, out_md, cid, command):
              "|---|---|---|---|---|---|---|"]
     for r in rows:
         name = r["Name"]
-        m = re.search(r"\w*kernel\w*", name)
+        m = re.search(r"\w*kernel\w*(<\d+>)?", name)
         short = m.group(0) if m else name[:60]
         fn = re.search(r"\w+Functor", name)
         if fn:
@@ -598,6 +598,20 @@ def stats_summary(stats_csv, out_md, cid, command):
         lines.append(f"| {short} | {r['Calls']} | {float(r['TotalDurationNs']) / 1e3:.1f} | "
                      f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
                      f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
+    # a kernel built in several template forms (one per call kind) is one
+    # launch label to bench.py's per-kernel pass: its combined average
+    forms = {}
+    for r in rows:
+        m = re.search(r"(\w*kernel\w*)<\d+>", r["Name"])
+        if m:
+            f = forms.setdefault(m.group(1), [0, 0.0])
+            f[0] += int(r["Calls"])
+            f[1] += float(r["TotalDurationNs"])
+    comb = [f"- {k} (all forms): {n} calls, average {t / n / 1e3:.1f} us" for k, (n, t) in
+            sorted(forms.items()) if n]
+    if comb:
+        lines += ["", "Combined over template forms (what bench.py's per-kernel pass averages):",
+                  ""] + comb
     lines += ["", f"kernel sources sha256: `{kernel_source_hash()}`", ""]
     with open(out_md, "w") as f:
         f.write("\n".join(lines))
