@@ -968,21 +968,36 @@ def run_offload(cfg, data, args):
     res["h2d_ms"] = a.elapsed_time(b)
     dormant = holder.get()
     del holder
-    # one Phase B with the offload running beside it on the copy stream
-    torch.cuda.synchronize()
-    a, b, c0, c1 = ev(), ev(), ev(), ev()
-    c0.record(cs)
-    holder = pool.offload(dormant, cs)
-    # the copy stream's event right behind the copies (recorded before Phase B
-    # is enqueued, so host time spent enqueuing Phase B does not count)
-    c1.record(cps)
-    del dormant
-    a.record(cs)
-    phase_b()
-    b.record(cs)
-    torch.cuda.synchronize()
-    res["phase_b_ms_beside_d2h"] = a.elapsed_time(b)
-    res["d2h_done_ms_after_phase_b_start"] = c0.elapsed_time(c1)
+    # Phase B with the offload running beside it on the copy stream: one
+    # untimed round (its first time through this path can stall the host for
+    # milliseconds), then `reps` timed rounds, each offloading and bringing
+    # the tensors back; median and range reported
+    beside, done = [], []
+    for i in range(reps + 1):
+        torch.cuda.synchronize()
+        a, b, c0, c1 = ev(), ev(), ev(), ev()
+        c0.record(cs)
+        holder = pool.offload(dormant, cs)
+        # the copy stream's event right behind the copies (recorded before
+        # Phase B is enqueued, so host time spent enqueuing Phase B does not
+        # count)
+        c1.record(cps)
+        del dormant
+        a.record(cs)
+        phase_b()
+        b.record(cs)
+        torch.cuda.synchronize()
+        if i > 0:
+            beside.append(a.elapsed_time(b))
+            done.append(c0.elapsed_time(c1))
+        if i < reps:
+            dormant = holder.get()
+            del holder
+            torch.cuda.synchronize()
+    res["phase_b_ms_beside_d2h"] = round(float(np.median(beside)), 4)
+    res["d2h_done_ms_after_phase_b_start"] = round(float(np.median(done)), 4)
+    res["d2h_done_ms_after_phase_b_start_range"] = [round(min(done), 4), round(max(done), 4)]
+    res["d2h_rounds"] = reps
     # dormant tensors in host memory through Phase B
     steady_phase_b("offloaded")
     # Phase C's inputs come back
@@ -1024,9 +1039,10 @@ def run_offload(cfg, data, args):
         "phase_b_peak_hbm_saved_mib": round(res["phase_b_peak_mib_resident"] -
                                             res["phase_b_peak_mib_offloaded"], 2),
         "pool_bytes": pool.capacity, "pool_over_dormant": round(pool.capacity / nbytes, 3),
-        "pinned_allocations": pool.pinned_allocations, "groups_through_pool": n_groups + 2,
+        "pinned_allocations": pool.pinned_allocations,
+        "groups_through_pool": n_groups + reps + 2,
         "resident_fallbacks": pool.resident_fallbacks,
-        **{k: round(v, 4) for k, v in res.items()},
+        **{k: (round(v, 4) if isinstance(v, float) else v) for k, v in res.items()},
     }
     print(json.dumps(out), flush=True)
 
