@@ -29,7 +29,10 @@ def _dev_logits(z, dtype, pad_to=None):
 
 
 CASES = [(37, 1000, 120, "f32", None), (50, 4099, 200, "bf16", 4104), (9, 64, 40, "bf16", None),
-         (16, 152000, 64, "bf16", None), (12, 3001, 30, "f32", 3004)]
+         (16, 152000, 64, "bf16", None), (12, 3001, 30, "f32", 3004),
+         # fewer than eight columns (no whole vector), exactly one vector, and
+         # a vocabulary whose backward chunks end in a partial group
+         (7, 5, 20, "bf16", 8), (6, 8, 12, "f32", None), (11, 6150, 50, "bf16", 6152)]
 
 
 @pytest.mark.parametrize("c,v,s,dtype,pad", CASES, ids=lambda x: str(x))
