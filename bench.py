@@ -424,6 +424,11 @@ def run_gpu(cfg, data, steps, warmup, copy_mib=0, separate_windows=False):
     phase_ms = phases_of(evs)
     res["wall_ms_per_step"] = wall * 1e3 / steps
     res["phase_ms"] = phase_ms
+    # the headline phase step by step: its median and fastest step
+    key = (0, 1) if cfg.is_tree else (1, 2)
+    per_step = sorted(e[key[0]].elapsed_time(e[key[1]]) for e in evs)
+    res["headline_phase_ms_median"] = float(np.median(per_step))
+    res["headline_phase_ms_min"] = per_step[0]
     res["steps_total_ms"] = evs[0][0].elapsed_time(evs[-1][3])
     res["kernels"], res["kernel_pass"] = kernel_pass(torch, pf, timer, step, phases_of, phase_ms,
                                                      min(steps, 10))
@@ -1115,6 +1120,11 @@ def main():
     flops_b = 12.0 * d * pairs_b * hq
     step_ms = sum(gres["phase_ms"].values())
     value = flops_b / (b_ms * 1e-3) / 1e12
+    # the same phase by other conventions: the median and fastest step, and the
+    # FlashAttention count (backward 10 d per pair: dQ's product included)
+    extra = {"value_median_step": round(flops_b / (gres["headline_phase_ms_median"] * 1e-3) / 1e12, 3),
+             "value_fastest_step": round(flops_b / (gres["headline_phase_ms_min"] * 1e-3) / 1e12, 3),
+             "value_fa_convention": round(14.0 / 12.0 * value, 3)}
 
     # roofline of the kernel with the largest total time
     kern = gres["kernels"]
@@ -1204,6 +1214,16 @@ def main():
         "device": gres["device"], "compute_units": gres["cus"],
     }
     out["group_tflops"] = round(group_flops / (step_ms * 1e-3) / 1e12, 3)
+    out.update(extra)
+    # the D / LSE pre-pass (HBM-bound): dO and O read (bf16), D and LSE log2(e)
+    # written (fp32), per row and query head of the Phase-B call
+    kd = kern.get("pf_prep_dsum")
+    if kd and "B" in kd.get("phase_avg_ms", {}) and not (cfg.is_tree or cfg.is_ranges):
+        # Phase-B rows, over the Phase-B launches of one step (one per call)
+        per_step = kd["phases"]["B"] / gres["kernel_pass"]["steps"]
+        rows_b = (compact - cfg.prefix_len) / per_step
+        nbytes = rows_b * hq * (2 * d * (2 if cfg.dtype == "bf16" else 4) + 8)
+        out["prep_dsum_phase_b_gbs"] = round(nbytes / (kd["phase_avg_ms"]["B"] * 1e-3) / 1e9, 1)
     if cpu:
         # the same group on both sides: algorithmic TFLOP/s and group tokens/s
         ratio = out["group_tflops"] / cpu["value"] if cpu["value"] > 0 else None
