@@ -1031,6 +1031,49 @@ def run_offload(cfg, data, args):
     b.record(cs)
     torch.cuda.synchronize()
     res["group_ms_through_pool"] = a.elapsed_time(b) / n_groups
+
+    # Two layers of one group, in a trainer's order: both layers' Phase A (each
+    # offloading its dormant tensors right after it), both layers' Phase B,
+    # then the prefix backward in reverse layer order with the next layer's
+    # prefetch issued before this layer's Phase C, so that the copy back runs
+    # beside it (PrefixFlow §4.2: prefetched before the matching prefix-backward
+    # layer).  The same sequence with the tensors resident is the comparison.
+    # The pool holds both layers' tensors (1.5x of two layers).
+    pool2 = PinnedPool.for_footprint(2 * nbytes, copy_stream=cps)
+
+    def two_layers(offload):
+        held = []
+        for _ in range(2):
+            o_p, lse_p = G.prefix_fwd(desc_c, q_keep, t["k_p"], t["v_p"])
+            tens = {"q_p": q_keep, "o_p": o_p, "lse_p": lse_p}
+            held.append(pool2.offload(tens, cs) if offload else tens)
+            del o_p, lse_p, tens
+        for _ in range(2):
+            phase_b()
+        if offload:
+            held[1].prefetch()
+        for layer in (1, 0):
+            if offload:
+                if layer == 1:
+                    held[0].prefetch()
+                back = held[layer].get(cs)
+            else:
+                back = held[layer]
+            G.prefix_bwd(desc_c, back["q_p"], t["k_p"], t["v_p"], back["o_p"], back["lse_p"],
+                         t["do_p"], gk, gv)
+            del back
+
+    for mode in (False, True):
+        two_layers(mode)
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record(cs)
+        for _ in range(reps):
+            two_layers(mode)
+        b.record(cs)
+        torch.cuda.synchronize()
+        res["two_layer_ms_offloaded" if mode else "two_layer_ms_resident"] = \
+            a.elapsed_time(b) / reps
     out = {
         "metric": "dormant prefix offload across Phase B (host link)",
         "config": {"workload": f"config {cfg.cid}: {cfg.name}"},
@@ -1047,6 +1090,9 @@ def run_offload(cfg, data, args):
         "pinned_allocations": pool.pinned_allocations,
         "groups_through_pool": n_groups + reps + 2,
         "resident_fallbacks": pool.resident_fallbacks,
+        "two_layer_pool_fallbacks": pool2.resident_fallbacks,
+        "two_layer_overhead_ratio": round(res["two_layer_ms_offloaded"] /
+                                          res["two_layer_ms_resident"], 4),
         **{k: (round(v, 4) if isinstance(v, float) else v) for k, v in res.items()},
     }
     print(json.dumps(out), flush=True)
