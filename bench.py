@@ -42,7 +42,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2,
                     help="workload (1..8; 6 is tree windows over a cached prefix, 7 compact "
                          "log-probabilities, 8 windows under a producer tree's nodes); 2 is "
@@ -395,10 +395,6 @@ def run_gpu(cfg, data, steps, warmup, copy_mib=0, separate_windows=False):
                 ev[3].record(stream)
         phase_names = ("A", "B", "C")
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-
     def phases_of(evs):
         n = len(evs)
         if cfg.is_tree:
@@ -410,10 +406,15 @@ def run_gpu(cfg, data, steps, warmup, copy_mib=0, separate_windows=False):
     # timed region: K steps with HIP events at the phase boundaries only (no
     # per-kernel events: an event record between two kernels adds its own
     # cost, and host-side bookkeeping per launch can leave the GPU idle)
+    # (the collection and the event creation come before the warm-up, so the
+    # GPU goes from the warm-up steps to the timed ones without an idle gap)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     gc.collect()
     gc.disable()
     try:
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(steps):
             step(evs[i])
@@ -426,9 +427,11 @@ def run_gpu(cfg, data, steps, warmup, copy_mib=0, separate_windows=False):
     res["phase_ms"] = phase_ms
     # the headline phase step by step: its median and fastest step
     key = (0, 1) if cfg.is_tree else (1, 2)
-    per_step = sorted(e[key[0]].elapsed_time(e[key[1]]) for e in evs)
+    in_order = [e[key[0]].elapsed_time(e[key[1]]) for e in evs]
+    per_step = sorted(in_order)
     res["headline_phase_ms_median"] = float(np.median(per_step))
     res["headline_phase_ms_min"] = per_step[0]
+    res["headline_phase_ms_steps"] = [round(x, 4) for x in in_order]
     res["steps_total_ms"] = evs[0][0].elapsed_time(evs[-1][3])
     res["kernels"], res["kernel_pass"] = kernel_pass(torch, pf, timer, step, phases_of, phase_ms,
                                                      min(steps, 10))
@@ -1170,7 +1173,8 @@ def main():
     # FlashAttention count (backward 10 d per pair: dQ's product included)
     extra = {"value_median_step": round(flops_b / (gres["headline_phase_ms_median"] * 1e-3) / 1e12, 3),
              "value_fastest_step": round(flops_b / (gres["headline_phase_ms_min"] * 1e-3) / 1e12, 3),
-             "value_fa_convention": round(14.0 / 12.0 * value, 3)}
+             "value_fa_convention": round(14.0 / 12.0 * value, 3),
+             "headline_phase_ms_steps": gres["headline_phase_ms_steps"]}
 
     # roofline of the kernel with the largest total time
     kern = gres["kernels"]
