@@ -1,9 +1,28 @@
-// fp32 attention kernels (head_dim 64 or 128): the same three kernels as the
-// bf16 family with fp32 inputs, fp32 products and fp32 accumulation, so fp32
-// groups are never rounded to bf16.  One thread owns one query row (forward,
-// dQ) or one key row (dK/dV); K/V or Q/dO tiles of 64 rows are staged in LDS
-// and read by broadcast.  These kernels serve small fp32 groups; the bf16
-// MFMA kernels carry the large workloads.
+// fp32 attention kernels (head_dim 64 or 128) on the matrix cores: every
+// product is v_mfma_f32_32x32x2_f32 with fp32 inputs and fp32 accumulation,
+// so fp32 groups are never rounded to bf16.  The three kernels compute what
+// the bf16 family computes (forward; dQ with D = rowsum(dO o O); dK/dV, with
+// the external keys' gradients added into the fp32 accumulators).
+//
+// Layout of one 32x32x2 product for lane l (half h = l / 32, column l % 32):
+//   A operand: lane l supplies A[l % 32][h]; B operand: B[h][l % 32];
+//   C register r holds C[crow(r, h)][l % 32], crow(r, h) = 8 (r / 4) + 4 h + r % 4.
+// A product's contraction index may be taken in any order, so each one is
+// ordered to fit what the wave already holds:
+//   - over head_dim (S, dP): step s of lane half h takes d = (D / 2) h + s,
+//     so a stationary operand is D / 2 consecutive values of the lane's row;
+//   - over keys or queries (O, dQ, dK, dV): step s of lane half h takes index
+//     crow(s, h), so the B operand of step s is C register s of the score
+//     tile the lane already holds; nothing is transposed.
+// Forward and dQ are Q-stationary and form S^T = K Q^T: one query per lane
+// column, so its LSE and D are one value per lane.  dK/dV is KV-stationary
+// and forms S = Q K^T: one key per lane column, whose P and dS then feed
+// dV^T += dO^T P and dK^T += Q^T dS.
+// K/V (or Q/dO) tiles of 32 rows reach LDS through buffer-to-LDS loads,
+// double buffered, with rows padded to D + 4 floats: the row-sliced reads
+// (16 bytes of 32 rows) and the column-sliced ones (32 floats of a row) then
+// both spread over the banks, and every read is a per-lane base plus a
+// constant offset.
 #include <math.h>
 
 #include "pf_internal.h"
@@ -11,266 +30,561 @@
 namespace pf {
 namespace {
 
-constexpr int kT = 64;   // rows per tile, threads per workgroup
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+using Rsrc = __amdgpu_buffer_rsrc_t;
 
-// key block kb (64 keys) of the own rows holds a key visible to a token >= t0
-__device__ __forceinline__ bool own_block_live(const AttnArgs& a, int kb, int t0) {
-  int m = -1;
-  for (int b = 2 * kb; b < 2 * kb + 2 && b * 32 < a.rows; ++b) m = max(m, a.ri.bmax[b]);
-  return m > t0;
+constexpr int kWaves = 4;                 // waves per workgroup
+constexpr int kThreads = 64 * kWaves;
+constexpr int kDkvKeys = 32 * kWaves;     // keys per KV-stationary workgroup
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kLn2 = 0.69314718055994530942f;
+
+__device__ __forceinline__ f32x16 mm(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
-template <int D>
-__global__ __launch_bounds__(kT) void fwd_f32_kernel(AttnArgs a) {
-  __shared__ float ks[kT][D + 1];
-  __shared__ float vs[kT][D + 1];
-  __shared__ int kend_s[kT];
-  const int head = blockIdx.y;
-  // KV head of this query head: position of `head` in the grouped table
-  int kvh = 0;
-  for (int i = 0; i < a.hq; ++i)
-    if (a.ri.qhead[i] == head) kvh = i / a.group;
-  const int t0 = blockIdx.x * kT;
-  const int tok = t0 + threadIdx.x;
-  const bool valid = tok < a.rows;
-  const int t1 = min(t0 + kT, a.rows);
+__host__ __device__ constexpr int crow(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
-  float q[D], o[D];
-  const float* qp = (const float*)a.q + (int64_t)tok * a.q_st + (int64_t)head * a.q_sh;
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
 #pragma unroll
-  for (int d = 0; d < D; ++d) {
-    q[d] = valid ? qp[d] : 0.f;
-    o[d] = 0.f;
-  }
-  float m = -INFINITY, l = 0.f;
-  const int n_ext_b = (a.n_ext + kT - 1) / kT;
-  const int n_own_b = (t1 + kT - 1) / kT;
-  for (int blk = 0; blk < n_ext_b + n_own_b; ++blk) {
-    const bool ext = blk < n_ext_b;
-    const int k0 = (ext ? blk : blk - n_ext_b) * kT;
-    if (!ext && !own_block_live(a, blk - n_ext_b, t0)) continue;
-    const int klim = ext ? a.n_ext : a.rows;
-    const float* kb = (const float*)(ext ? a.k_ext : a.k_own);
-    const float* vb = (const float*)(ext ? a.v_ext : a.v_own);
-    const int64_t kst = ext ? a.kx_st : a.ko_st, ksh = ext ? a.kx_sh : a.ko_sh;
-    const int64_t vst = ext ? a.vx_st : a.vo_st, vsh = ext ? a.vx_sh : a.vo_sh;
-    __syncthreads();
-    for (int e = threadIdx.x; e < kT * D; e += kT) {
-      const int r = e / D, d = e % D, kk = k0 + r;
-      ks[r][d] = kk < klim ? kb[(int64_t)kk * kst + (int64_t)kvh * ksh + d] : 0.f;
-      vs[r][d] = kk < klim ? vb[(int64_t)kk * vst + (int64_t)kvh * vsh + d] : 0.f;
-    }
-    if (!ext) kend_s[threadIdx.x] = (k0 + threadIdx.x < a.rows) ? a.ri.kend[k0 + threadIdx.x] : -1;
-    __syncthreads();
-    for (int r = 0; r < kT; ++r) {
-      const int kk = k0 + r;
-      bool vis = kk < klim;
-      if (!ext) vis = vis && kk <= tok && tok < kend_s[r];
-      if (!vis) continue;
-      float s = 0.f;
-#pragma unroll
-      for (int d = 0; d < D; ++d) s = fmaf(q[d], ks[r][d], s);
-      s *= a.scale;
-      const float mn = fmaxf(m, s);
-      const float alpha = expf(m - mn);
-      const float p = expf(s - mn);
-      l = l * alpha + p;
-#pragma unroll
-      for (int d = 0; d < D; ++d) o[d] = fmaf(o[d], alpha, p * vs[r][d]);
-      m = mn;
-    }
-  }
-  if (!valid) return;
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-  float* op = (float*)a.out + (int64_t)tok * a.out_st + (int64_t)head * a.out_sh;
-#pragma unroll
-  for (int d = 0; d < D; ++d) op[d] = o[d] * inv;
-  a.lse[(int64_t)head * a.rows + tok] = l > 0.f ? m + logf(l) : -INFINITY;
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
 }
 
-template <int D>
-__global__ __launch_bounds__(kT) void dq_f32_kernel(AttnArgs a) {
-  __shared__ float ks[kT][D + 1];
-  __shared__ float vs[kT][D + 1];
-  __shared__ int kend_s[kT];
-  const int head = blockIdx.y;
-  int kvh = 0;
-  for (int i = 0; i < a.hq; ++i)
-    if (a.ri.qhead[i] == head) kvh = i / a.group;
-  const int t0 = blockIdx.x * kT;
-  const int tok = t0 + threadIdx.x;
-  const bool valid = tok < a.rows;
-  const int t1 = min(t0 + kT, a.rows);
+// keep a stationary operand in the AGPR file; the products read it there
+__device__ __forceinline__ void pin_agpr(float& x) { asm("" : "+a"(x)); }
 
-  float q[D], dout[D], dq[D];
-  float dsum = 0.f;
-  const int64_t qo = (int64_t)tok * a.q_st + (int64_t)head * a.q_sh;
-  const int64_t doo = (int64_t)tok * a.do_st + (int64_t)head * a.do_sh;
-  const int64_t oo = (int64_t)tok * a.o_st + (int64_t)head * a.o_sh;
-#pragma unroll
-  for (int d = 0; d < D; ++d) {
-    q[d] = valid ? ((const float*)a.q)[qo + d] : 0.f;
-    dout[d] = valid ? ((const float*)a.dout)[doo + d] : 0.f;
-    const float ov = valid ? ((const float*)a.o)[oo + d] : 0.f;
-    dsum = fmaf(dout[d], ov, dsum);
-    dq[d] = 0.f;
-  }
-  const float lse = valid ? a.lse[(int64_t)head * a.rows + tok] : 0.f;
-  if (valid) a.dsum[(int64_t)head * a.rows + tok] = dsum;
+__device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
 
-  const int n_ext_b = (a.n_ext + kT - 1) / kT;
-  const int n_own_b = (t1 + kT - 1) / kT;
-  for (int blk = 0; blk < n_ext_b + n_own_b; ++blk) {
-    const bool ext = blk < n_ext_b;
-    const int k0 = (ext ? blk : blk - n_ext_b) * kT;
-    if (!ext && !own_block_live(a, blk - n_ext_b, t0)) continue;
-    const int klim = ext ? a.n_ext : a.rows;
-    const float* kb = (const float*)(ext ? a.k_ext : a.k_own);
-    const float* vb = (const float*)(ext ? a.v_ext : a.v_own);
-    const int64_t kst = ext ? a.kx_st : a.ko_st, ksh = ext ? a.kx_sh : a.ko_sh;
-    const int64_t vst = ext ? a.vx_st : a.vo_st, vsh = ext ? a.vx_sh : a.vo_sh;
-    __syncthreads();
-    for (int e = threadIdx.x; e < kT * D; e += kT) {
-      const int r = e / D, d = e % D, kk = k0 + r;
-      ks[r][d] = kk < klim ? kb[(int64_t)kk * kst + (int64_t)kvh * ksh + d] : 0.f;
-      vs[r][d] = kk < klim ? vb[(int64_t)kk * vst + (int64_t)kvh * vsh + d] : 0.f;
-    }
-    if (!ext) kend_s[threadIdx.x] = (k0 + threadIdx.x < a.rows) ? a.ri.kend[k0 + threadIdx.x] : -1;
-    __syncthreads();
-    if (!valid) continue;
-    for (int r = 0; r < kT; ++r) {
-      const int kk = k0 + r;
-      bool vis = kk < klim;
-      if (!ext) vis = vis && kk <= tok && tok < kend_s[r];
-      if (!vis) continue;
-      float s = 0.f, dp = 0.f;
-#pragma unroll
-      for (int d = 0; d < D; ++d) {
-        s = fmaf(q[d], ks[r][d], s);
-        dp = fmaf(dout[d], vs[r][d], dp);
-      }
-      const float p = expf(s * a.scale - lse);
-      const float ds = p * (dp - dsum);
-#pragma unroll
-      for (int d = 0; d < D; ++d) dq[d] = fmaf(ds, ks[r][d], dq[d]);
-    }
-  }
-  if (!valid) return;
-  float* op = (float*)a.out + (int64_t)tok * a.out_st + (int64_t)head * a.out_sh;
-#pragma unroll
-  for (int d = 0; d < D; ++d) op[d] = dq[d] * a.scale;
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           (int)(bytes > 0 ? bytes : 0), 0x00020000);
 }
 
-// One thread per key of one KV head; external keys (blockIdx.x < n_ext
-// blocks) walk every row, own keys the rows [k, kend[k]).
+// rows [0, valid) of D floats each, row stride st floats, from `base`; loads
+// of later rows fall outside the resource and read zero
 template <int D>
-__global__ __launch_bounds__(kT) void dkv_f32_kernel(AttnArgs a) {
-  __shared__ float qs[kT][D + 1];
-  __shared__ float ds_s[kT][D + 1];
-  __shared__ float lse_s[kT];
-  __shared__ float dsum_s[kT];
-  const int g = blockIdx.y;
-  const int n_ext_b = (a.n_ext + kT - 1) / kT;
-  const bool ext = (int)blockIdx.x < n_ext_b;
-  const int k0 = (ext ? blockIdx.x : blockIdx.x - n_ext_b) * kT;
-  const int kk = k0 + threadIdx.x;
-  const int klim = ext ? a.n_ext : a.rows;
-  const bool kvalid = kk < klim;
-  const float* kb = (const float*)(ext ? a.k_ext : a.k_own);
-  const float* vb = (const float*)(ext ? a.v_ext : a.v_own);
+__device__ __forceinline__ Rsrc rows_rsrc(const float* base, int valid, int64_t st) {
+  return make_rsrc(base, valid > 0 ? (int64_t)(valid - 1) * st * 4 + D * 4 : 0);
+}
+
+// A 32-row LDS tile of D floats per row, rows padded to D + 4 floats.  A
+// buffer-to-LDS load writes 64 consecutive 16-byte chunks (one per lane), so a
+// tile takes kNi such loads; lanes whose chunk is padding, or past the last
+// row, fetch from an offset past every resource's end and write zero.
+template <int D>
+struct Tile {
+  static constexpr int kRs = D + 4;                  // row stride (floats)
+  static constexpr int kCpr = kRs / 4;               // chunks per row, padding included
+  static constexpr int kNi = (32 * kCpr + 63) / 64;  // loads per tile
+  static constexpr int kFloats = 256 * kNi;          // floats the loads write
+};
+
+// The 32 rows of a tile (row r at byte r * st_b of the resource; rows past
+// its end read zero) into a padded LDS tile, the loads dealt round the
+// workgroup's waves.
+template <int D>
+__device__ __forceinline__ void dma_tile(Rsrc r, float* tile, uint32_t st_b, int wave, int lane) {
+  using T = Tile<D>;
+#pragma unroll
+  for (int j = 0; j < (T::kNi + kWaves - 1) / kWaves; ++j) {
+    const int i = wave + kWaves * j;
+    if (i < T::kNi) {
+      const int c = 64 * i + lane, row = c / T::kCpr, ch = c % T::kCpr;
+      const uint32_t off =
+          (row < 32 && ch < T::kCpr - 1) ? (uint32_t)row * st_b + 16u * (uint32_t)ch : 0x80000000u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(tile + 256 * i), 16, (int)off, 0, 0,
+                                               0);
+    }
+  }
+}
+
+// 64 consecutive 4-byte values (past the resource's end: zero) into LDS
+__device__ __forceinline__ void dma_vec(Rsrc r, void* dst, int lane) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 4, 4 * lane, 0, 0, 0);
+}
+
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// The Q-stationary kernels' share of the work: workgroup x of KV head g holds
+// the (32-token tile, query head) pairs 4 x .. 4 x + 3 of that KV head, one per
+// wave, pairs ordered tile-major; the tiles of keys it walks are the external
+// ones, then the own ones that some of its rows may see.
+struct QTiles {
+  int g, head, t0, tok;
+  bool active, tvalid;
+  int wt_hi;                 // last token of the wave's tile
+  int tmin;                  // first token of the workgroup
+  int n_ext_t, n_t;          // external tiles; all tiles (external, then own)
+
+  __device__ QTiles(const AttnArgs& a, int wave, int col) {
+    g = blockIdx.y;
+    const int n_pairs = ((a.rows + 31) / 32) * a.group;
+    const int p0 = blockIdx.x * kWaves;
+    const int p = p0 + wave;
+    active = p < n_pairs;
+    const int j = active ? p % a.group : 0;
+    t0 = active ? (p / a.group) * 32 : 0;
+    head = a.ri.qhead[g * a.group + j];
+    tok = t0 + col;
+    tvalid = active && tok < a.rows;
+    wt_hi = min(a.rows, t0 + 32) - 1;
+    tmin = (p0 / a.group) * 32;
+    const int tmax = min(a.rows, ((min(p0 + kWaves, n_pairs) - 1) / a.group) * 32 + 32) - 1;
+    n_ext_t = (a.n_ext + 31) / 32;
+    n_t = n_ext_t + tmax / 32 + 1;
+  }
+  // some row of the workgroup may see a key of tile i
+  __device__ bool live(const AttnArgs& a, int i) const {
+    return i < n_ext_t || a.ri.bmax[i - n_ext_t] > tmin;
+  }
+  __device__ int next(const AttnArgs& a, int i) const {
+    for (++i; i < n_t; ++i)
+      if (live(a, i)) return i;
+    return -1;
+  }
+  // some row of this wave may see a key of tile i
+  __device__ bool wave_sees(const AttnArgs& a, int i) const {
+    if (!active) return false;
+    if (i < n_ext_t) return true;
+    const int b = i - n_ext_t;
+    return 32 * b <= wt_hi && a.ri.bmax[b] > t0;
+  }
+  __device__ int key0(int i) const { return (i < n_ext_t ? i : i - n_ext_t) * 32; }
+};
+
+// K/V tile i of a Q-stationary workgroup (and the kend values of own keys)
+// into LDS buffer b
+template <int D>
+__device__ __forceinline__ void stage_kv(const AttnArgs& a, const QTiles& w, int i, float* k_s,
+                                         float* v_s, int32_t* kend_s, int wave, int lane) {
+  const bool ext = i < w.n_ext_t;
+  const int k0 = w.key0(i);
+  const int valid = (ext ? a.n_ext : a.rows) - k0;
   const int64_t kst = ext ? a.kx_st : a.ko_st, ksh = ext ? a.kx_sh : a.ko_sh;
   const int64_t vst = ext ? a.vx_st : a.vo_st, vsh = ext ? a.vx_sh : a.vo_sh;
+  const float* kb = (const float*)(ext ? a.k_ext : a.k_own) + (int64_t)k0 * kst + (int64_t)w.g * ksh;
+  const float* vb = (const float*)(ext ? a.v_ext : a.v_own) + (int64_t)k0 * vst + (int64_t)w.g * vsh;
+  dma_tile<D>(rows_rsrc<D>(kb, valid, kst), k_s, 4u * (uint32_t)kst, wave, lane);
+  dma_tile<D>(rows_rsrc<D>(vb, valid, vst), v_s, 4u * (uint32_t)vst, wave, lane);
+  if (!ext && wave == kWaves - 1) dma_vec(make_rsrc(a.ri.kend + k0, 4LL * valid), kend_s, lane);
+}
 
-  float k[D], v[D], dk[D], dv[D];
+// The scores of one K tile against the wave's queries, in log2 units, with the
+// keys the lane's query cannot see at -inf: register r is key k0 + crow(r, h).
+template <int D>
+__device__ __forceinline__ void visible_scores(const AttnArgs& a, bool ext, int k0, int tok, int h,
+                                               const f32x16& s, const int32_t* kend_s,
+                                               float (&x)[16]) {
+  const float c = a.scale_log2;
+  if (ext) {
 #pragma unroll
-  for (int d = 0; d < D; ++d) {
-    k[d] = kvalid ? kb[(int64_t)kk * kst + (int64_t)g * ksh + d] : 0.f;
-    v[d] = kvalid ? vb[(int64_t)kk * vst + (int64_t)g * vsh + d] : 0.f;
-    dk[d] = 0.f;
-    dv[d] = 0.f;
+    for (int r = 0; r < 16; ++r) x[r] = (k0 + crow(r, h) < a.n_ext) ? s[r] * c : -INFINITY;
+  } else {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const i32x4 ke = *(const i32x4*)(kend_s + 8 * q4 + 4 * h);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * q4 + e, kk = k0 + crow(r, h);
+        x[r] = (kk <= tok && tok < ke[e]) ? s[r] * c : -INFINITY;
+      }
+    }
   }
-  const int kend = (!ext && kvalid) ? a.ri.kend[kk] : 0;
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void fwd_f32_kernel(AttnArgs a) {
+  constexpr int H = D / 2, NT = D / 32, RS = Tile<D>::kRs;
+  __shared__ __attribute__((aligned(16))) float kv_s[2][2][Tile<D>::kFloats];
+  __shared__ __attribute__((aligned(16))) int32_t kend_s[2][64];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, col = lane & 31, h = lane >> 5;
+  const QTiles w(a, wave, col);
+
+  // the lane's half of its query row: B operand of S^T = K Q^T
+  float q[H];
+  {
+    const float* qp = (const float*)a.q + (int64_t)(w.tvalid ? w.tok : 0) * a.q_st +
+                      (int64_t)w.head * a.q_sh + H * h;
+#pragma unroll
+    for (int u = 0; u < H / 4; ++u) {
+      f32x4 v = {0.f, 0.f, 0.f, 0.f};
+      if (w.tvalid) v = *(const f32x4*)(qp + 4 * u);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) q[4 * u + e] = v[e];
+    }
+#pragma unroll
+    for (int s = 0; s < H; ++s) pin_agpr(q[s]);
+  }
+
+  f32x16 o[NT];
+#pragma unroll
+  for (int dt = 0; dt < NT; ++dt) o[dt] = zero16();
+  float m = -INFINITY, lsum = 0.f;   // running max (log2 units) and this half's sum
+
+  int cur = w.live(a, 0) ? 0 : w.next(a, 0);
+  if (w.n_t <= 0) cur = -1;
+  if (cur >= 0) stage_kv<D>(a, w, cur, kv_s[0][0], kv_s[0][1], kend_s[0], wave, lane);
+  for (int b = 0; cur >= 0; b ^= 1) {
+    const int nxt = w.next(a, cur);
+    wait_dma();
+    __syncthreads();
+    if (nxt >= 0) stage_kv<D>(a, w, nxt, kv_s[b ^ 1][0], kv_s[b ^ 1][1], kend_s[b ^ 1], wave, lane);
+    if (w.wave_sees(a, cur)) {
+      const float* ks = kv_s[b][0];
+      const float* vs = kv_s[b][1];
+      f32x16 s = zero16();
+#pragma unroll
+      for (int u = 0; u < H / 4; ++u) {
+        const f32x4 kv = *(const f32x4*)(ks + col * RS + H * h + 4 * u);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s = mm(kv[e], q[4 * u + e], s);
+      }
+      float x[16];
+      visible_scores<D>(a, cur < w.n_ext_t, w.key0(cur), w.tok, h, s, kend_s[b], x);
+      float mx = x[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, x[r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mn = fmaxf(m, mx);
+      const float ms = mn == -INFINITY ? 0.f : mn;
+      const float alpha = exp2_(m - ms);
+      float ps = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        x[r] = exp2_(x[r] - ms);
+        ps += x[r];
+      }
+      lsum = lsum * alpha + ps;
+      m = mn;
+#pragma unroll
+      for (int dt = 0; dt < NT; ++dt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+#pragma unroll
+        for (int s2 = 0; s2 < 16; ++s2) o[dt] = mm(vs[crow(s2, h) * RS + 32 * dt + col], x[s2], o[dt]);
+      }
+    }
+    cur = nxt;
+  }
+
+  const float lt = lsum + __shfl_xor(lsum, 32);
+  if (!w.tvalid) return;
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  float* op = (float*)a.out + (int64_t)w.tok * a.out_st + (int64_t)w.head * a.out_sh;
+#pragma unroll
+  for (int dt = 0; dt < NT; ++dt)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      f32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = o[dt][4 * q4 + e] * inv;
+      *(f32x4*)(op + 32 * dt + 8 * q4 + 4 * h) = v;
+    }
+  if (h == 0)
+    a.lse[(int64_t)w.head * a.rows + w.tok] = lt > 0.f ? (m + log2f(lt)) * kLn2 : -INFINITY;
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 1) void dq_f32_kernel(AttnArgs a) {
+  constexpr int H = D / 2, NT = D / 32, RS = Tile<D>::kRs;
+  __shared__ __attribute__((aligned(16))) float kv_s[2][2][Tile<D>::kFloats];
+  __shared__ __attribute__((aligned(16))) int32_t kend_s[2][64];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, col = lane & 31, h = lane >> 5;
+  const QTiles w(a, wave, col);
+
+  // the lane's halves of its Q and dO rows (B operands of S^T and dP^T) and
+  // D = rowsum(dO o O) of its row
+  float q[H], dov[H];
+  float dsum;
+  {
+    const int64_t t = w.tvalid ? w.tok : 0;
+    const float* qp = (const float*)a.q + t * a.q_st + (int64_t)w.head * a.q_sh + H * h;
+    const float* dp = (const float*)a.dout + t * a.do_st + (int64_t)w.head * a.do_sh + H * h;
+    const float* opp = (const float*)a.o + t * a.o_st + (int64_t)w.head * a.o_sh + H * h;
+    float acc = 0.f;
+#pragma unroll
+    for (int u = 0; u < H / 4; ++u) {
+      f32x4 qv = {0.f, 0.f, 0.f, 0.f}, dv = qv, ov = qv;
+      if (w.tvalid) {
+        qv = *(const f32x4*)(qp + 4 * u);
+        dv = *(const f32x4*)(dp + 4 * u);
+        ov = *(const f32x4*)(opp + 4 * u);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        q[4 * u + e] = qv[e];
+        dov[4 * u + e] = dv[e];
+        acc = fmaf(dv[e], ov[e], acc);
+      }
+    }
+    dsum = acc + __shfl_xor(acc, 32);
+#pragma unroll
+    for (int s = 0; s < H; ++s) {
+      pin_agpr(q[s]);
+      pin_agpr(dov[s]);
+    }
+  }
+  if (w.tvalid && h == 0) a.dsum[(int64_t)w.head * a.rows + w.tok] = dsum;
+  // LSE in log2 units; rows that see no key (LSE -inf) and rows past the end
+  // take +inf, so every P of theirs is zero
+  float lse2 = INFINITY;
+  if (w.tvalid) {
+    const float l = a.lse[(int64_t)w.head * a.rows + w.tok];
+    if (l != -INFINITY) lse2 = l * kLog2e;
+  }
+
+  f32x16 dq[NT];
+#pragma unroll
+  for (int dt = 0; dt < NT; ++dt) dq[dt] = zero16();
+
+  int cur = w.live(a, 0) ? 0 : w.next(a, 0);
+  if (w.n_t <= 0) cur = -1;
+  if (cur >= 0) stage_kv<D>(a, w, cur, kv_s[0][0], kv_s[0][1], kend_s[0], wave, lane);
+  for (int b = 0; cur >= 0; b ^= 1) {
+    const int nxt = w.next(a, cur);
+    wait_dma();
+    __syncthreads();
+    if (nxt >= 0) stage_kv<D>(a, w, nxt, kv_s[b ^ 1][0], kv_s[b ^ 1][1], kend_s[b ^ 1], wave, lane);
+    if (w.wave_sees(a, cur)) {
+      const float* ks = kv_s[b][0];
+      const float* vs = kv_s[b][1];
+      f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+      for (int u = 0; u < H / 4; ++u) {
+        const f32x4 kv = *(const f32x4*)(ks + col * RS + H * h + 4 * u);
+        const f32x4 vv = *(const f32x4*)(vs + col * RS + H * h + 4 * u);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          s = mm(kv[e], q[4 * u + e], s);
+          dp = mm(vv[e], dov[4 * u + e], dp);
+        }
+      }
+      float x[16];
+      visible_scores<D>(a, cur < w.n_ext_t, w.key0(cur), w.tok, h, s, kend_s[b], x);
+      // dS^T = P^T o (dP^T - D), P^T = 2^(x - LSE2); invisible entries are 0
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = x[r] == -INFINITY ? 0.f : exp2_(x[r] - lse2);
+        x[r] = p * (dp[r] - dsum);
+      }
+#pragma unroll
+      for (int dt = 0; dt < NT; ++dt)
+#pragma unroll
+        for (int s2 = 0; s2 < 16; ++s2)
+          dq[dt] = mm(ks[crow(s2, h) * RS + 32 * dt + col], x[s2], dq[dt]);
+    }
+    cur = nxt;
+  }
+
+  if (!w.tvalid) return;
+  float* op = (float*)a.out + (int64_t)w.tok * a.out_st + (int64_t)w.head * a.out_sh;
+#pragma unroll
+  for (int dt = 0; dt < NT; ++dt)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      f32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = dq[dt][4 * q4 + e] * a.scale;
+      *(f32x4*)(op + 32 * dt + 8 * q4 + 4 * h) = v;
+    }
+}
+
+// KV-stationary: workgroup x of KV head y holds 128 keys (external blocks
+// first, then own), 32 per wave; it walks every (32-token tile, query head)
+// step whose rows may see its keys: all rows for external keys, rows from the
+// block's first key to the largest visibility end of its keys for own keys.
+template <int D>
+__global__ __launch_bounds__(kThreads, 1) void dkv_f32_kernel(AttnArgs a) {
+  constexpr int H = D / 2, NT = D / 32, RS = Tile<D>::kRs;
+  __shared__ __attribute__((aligned(16))) float qd_s[2][2][Tile<D>::kFloats];   // [buffer][Q, dO]
+  __shared__ __attribute__((aligned(16))) float ld_s[2][2][64];       // [buffer][LSE, D]
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, col = lane & 31, h = lane >> 5;
+  const int g = blockIdx.y;
+  const int n_ext_b = (a.n_ext + kDkvKeys - 1) / kDkvKeys;
+  const bool ext = (int)blockIdx.x < n_ext_b;
+  const int k0 = (ext ? (int)blockIdx.x : (int)blockIdx.x - n_ext_b) * kDkvKeys;
+  const int kw0 = k0 + 32 * wave;
+  const int kk = kw0 + col;
+  const int klim = ext ? a.n_ext : a.rows;
+  const bool kvalid = kk < klim;
+
+  // the lane's halves of its K and V rows: B operands of S = Q K^T, dP = dO V^T
+  float kr[H], vr[H];
+  {
+    const int64_t kst = ext ? a.kx_st : a.ko_st, ksh = ext ? a.kx_sh : a.ko_sh;
+    const int64_t vst = ext ? a.vx_st : a.vo_st, vsh = ext ? a.vx_sh : a.vo_sh;
+    const int64_t r = kvalid ? kk : 0;
+    const float* kp = (const float*)(ext ? a.k_ext : a.k_own) + r * kst + (int64_t)g * ksh + H * h;
+    const float* vp = (const float*)(ext ? a.v_ext : a.v_own) + r * vst + (int64_t)g * vsh + H * h;
+#pragma unroll
+    for (int u = 0; u < H / 4; ++u) {
+      f32x4 kv = {0.f, 0.f, 0.f, 0.f}, vv = kv;
+      if (kvalid) {
+        kv = *(const f32x4*)(kp + 4 * u);
+        vv = *(const f32x4*)(vp + 4 * u);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kr[4 * u + e] = kv[e];
+        vr[4 * u + e] = vv[e];
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < H; ++s) {
+      pin_agpr(kr[s]);
+      pin_agpr(vr[s]);
+    }
+  }
+  const int kend_k = (!ext && kvalid) ? a.ri.kend[kk] : -1;
+  // rows that may see the wave's keys end before wave_hi (own keys)
+  const int wave_hi = (!ext && kw0 < a.rows) ? a.ri.bmax[kw0 / 32] : 0;
+
   int qlo = 0, qhi = a.rows;
   if (!ext) {
     qlo = k0;
-    int m = -1;
-    for (int b = k0 / 32; b * 32 < min(k0 + kT, a.rows); ++b) m = max(m, a.ri.bmax[b]);
-    qhi = min(m, a.rows);
+    int mx = -1;
+    for (int b = k0 / 32; b < k0 / 32 + kWaves && b * 32 < a.rows; ++b) mx = max(mx, a.ri.bmax[b]);
+    qhi = min(mx, a.rows);
   }
-  for (int j = 0; j < a.group; ++j) {
-    const int head = a.ri.qhead[g * a.group + j];
-    for (int t0 = qlo; t0 < qhi; t0 += kT) {
-      __syncthreads();
-      for (int e = threadIdx.x; e < kT * D; e += kT) {
-        const int r = e / D, d = e % D, tok = t0 + r;
-        const bool ok = tok < a.rows;
-        qs[r][d] = ok ? ((const float*)a.q)[(int64_t)tok * a.q_st + (int64_t)head * a.q_sh + d]
-                      : 0.f;
-        ds_s[r][d] = ok ? ((const float*)a.dout)[(int64_t)tok * a.do_st +
-                                                 (int64_t)head * a.do_sh + d]
-                        : 0.f;
-      }
-      {
-        const int tok = t0 + threadIdx.x;
-        const bool ok = tok < a.rows;
-        lse_s[threadIdx.x] = ok ? a.lse[(int64_t)head * a.rows + tok] : INFINITY;
-        dsum_s[threadIdx.x] = ok ? a.dsum[(int64_t)head * a.rows + tok] : 0.f;
-      }
-      __syncthreads();
-      if (!kvalid) continue;
-      for (int r = 0; r < kT; ++r) {
-        const int tok = t0 + r;
-        if (tok >= a.rows) break;
-        if (!ext && !(kk <= tok && tok < kend)) continue;
-        float s = 0.f, dp = 0.f;
+  const int qt_lo = qlo / 32;
+  const int n_qt = qhi > qlo ? (qhi - 1) / 32 - qt_lo + 1 : 0;
+  const int n_it = n_qt * a.group;
+
+  auto stage = [&](int it, int b) {
+    const int t0 = (qt_lo + it / a.group) * 32;
+    const int head = a.ri.qhead[g * a.group + it % a.group];
+    const int valid = a.rows - t0;
+    const float* qb = (const float*)a.q + (int64_t)t0 * a.q_st + (int64_t)head * a.q_sh;
+    const float* db = (const float*)a.dout + (int64_t)t0 * a.do_st + (int64_t)head * a.do_sh;
+    dma_tile<D>(rows_rsrc<D>(qb, valid, a.q_st), qd_s[b][0], 4u * (uint32_t)a.q_st, wave, lane);
+    dma_tile<D>(rows_rsrc<D>(db, valid, a.do_st), qd_s[b][1], 4u * (uint32_t)a.do_st, wave, lane);
+    if (wave == kWaves - 1)
+      dma_vec(make_rsrc(a.lse + (int64_t)head * a.rows + t0, 4LL * valid), ld_s[b][0], lane);
+    if (wave == kWaves - 2)
+      dma_vec(make_rsrc(a.dsum + (int64_t)head * a.rows + t0, 4LL * valid), ld_s[b][1], lane);
+  };
+
+  f32x16 dk[NT], dv[NT];
 #pragma unroll
-        for (int d = 0; d < D; ++d) {
-          s = fmaf(qs[r][d], k[d], s);
-          dp = fmaf(ds_s[r][d], v[d], dp);
-        }
-        const float p = expf(s * a.scale - lse_s[r]);
-        const float dsv = p * (dp - dsum_s[r]);
+  for (int dt = 0; dt < NT; ++dt) {
+    dk[dt] = zero16();
+    dv[dt] = zero16();
+  }
+  const float c = a.scale_log2;
+
+  if (n_it > 0) stage(0, 0);
+  for (int it = 0, b = 0; it < n_it; ++it, b ^= 1) {
+    wait_dma();
+    __syncthreads();
+    if (it + 1 < n_it) stage(it + 1, b ^ 1);
+    const int t0 = (qt_lo + it / a.group) * 32;
+    // own keys: the step's rows may see some key of the wave
+    if (!ext && (t0 + 31 < kw0 || t0 >= wave_hi)) continue;
+    const float* qs = qd_s[b][0];
+    const float* ds = qd_s[b][1];
+    f32x16 s = zero16(), dp = zero16();
 #pragma unroll
-        for (int d = 0; d < D; ++d) {
-          dv[d] = fmaf(p, ds_s[r][d], dv[d]);
-          dk[d] = fmaf(dsv, qs[r][d], dk[d]);
-        }
+    for (int u = 0; u < H / 4; ++u) {
+      const f32x4 qv = *(const f32x4*)(qs + col * RS + H * h + 4 * u);
+      const f32x4 dv4 = *(const f32x4*)(ds + col * RS + H * h + 4 * u);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s = mm(qv[e], kr[4 * u + e], s);
+        dp = mm(dv4[e], vr[4 * u + e], dp);
       }
     }
+    // register r: query row t0 + crow(r, h) against the lane's key; P in s,
+    // dS in dp
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const f32x4 lv = *(const f32x4*)(ld_s[b][0] + 8 * q4 + 4 * h);
+      const f32x4 dsv = *(const f32x4*)(ld_s[b][1] + 8 * q4 + 4 * h);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * q4 + e, tq = t0 + crow(r, h);
+        const bool vis = tq < a.rows && (ext || (kk <= tq && tq < kend_k));
+        // a visible row sees at least this key, so its LSE is finite
+        const float p = vis ? exp2_(s[r] * c - lv[e] * kLog2e) : 0.f;
+        s[r] = p;
+        dp[r] = p * (dp[r] - dsv[e]);
+      }
+    }
+#pragma unroll
+    for (int dt = 0; dt < NT; ++dt)
+#pragma unroll
+      for (int s2 = 0; s2 < 16; ++s2) {
+        const int at = crow(s2, h) * RS + 32 * dt + col;
+        dv[dt] = mm(ds[at], s[s2], dv[dt]);
+        dk[dt] = mm(qs[at], dp[s2], dk[dt]);
+      }
   }
+
   if (!kvalid) return;
+  // dK^T / dV^T register r: head_dim index 32 dt + crow(r, h) of the lane's key
   const int64_t base = ((int64_t)kk * a.hkv + g) * D;
   if (ext) {
 #pragma unroll
-    for (int d = 0; d < D; ++d) {
-      a.gk_acc[base + d] += dk[d] * a.scale;
-      a.gv_acc[base + d] += dv[d];
-    }
+    for (int dt = 0; dt < NT; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = 32 * dt + 8 * q4 + 4 * h;
+        f32x4* pk = (f32x4*)(a.gk_acc + base + d0);
+        f32x4* pv = (f32x4*)(a.gv_acc + base + d0);
+        f32x4 xk = *pk, xv = *pv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          xk[e] += dk[dt][4 * q4 + e] * a.scale;
+          xv[e] += dv[dt][4 * q4 + e];
+        }
+        *pk = xk;
+        *pv = xv;
+      }
     return;
   }
   float* dkp = (float*)a.dk_own + (int64_t)kk * a.dko_st + (int64_t)g * a.dko_sh;
   float* dvp = (float*)a.dv_own + (int64_t)kk * a.dvo_st + (int64_t)g * a.dvo_sh;
 #pragma unroll
-  for (int d = 0; d < D; ++d) {
-    float x = dk[d] * a.scale, y = dv[d];
-    if (a.gk_init) {
-      x += a.gk_init[base + d];
-      y += a.gv_init[base + d];
+  for (int dt = 0; dt < NT; ++dt)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d0 = 32 * dt + 8 * q4 + 4 * h;
+      f32x4 xk, xv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        xk[e] = dk[dt][4 * q4 + e] * a.scale;
+        xv[e] = dv[dt][4 * q4 + e];
+      }
+      if (a.gk_init) {
+        xk += *(const f32x4*)(a.gk_init + base + d0);
+        xv += *(const f32x4*)(a.gv_init + base + d0);
+      }
+      *(f32x4*)(dkp + d0) = xk;
+      *(f32x4*)(dvp + d0) = xv;
     }
-    dkp[d] = x;
-    dvp[d] = y;
-  }
+}
+
+// Q-stationary grid: per KV head, one workgroup per 4 (tile, query head) pairs
+dim3 q_grid(const AttnArgs& a) {
+  const int pairs = ((a.rows + 31) / 32) * a.group;
+  return dim3((pairs + kWaves - 1) / kWaves, a.hkv);
 }
 
 }  // namespace
 
 hipError_t launch_fwd_f32(const AttnArgs& a, int32_t head_dim, hipStream_t stream) {
   if (a.rows <= 0) return hipSuccess;
-  dim3 grid((a.rows + kT - 1) / kT, a.hq);
   if (head_dim == 64)
-    PF_LAUNCH("pf_fwd_f32", fwd_f32_kernel<64>, grid, dim3(kT), stream, a);
+    PF_LAUNCH("pf_fwd_f32", fwd_f32_kernel<64>, q_grid(a), dim3(kThreads), stream, a);
   else if (head_dim == 128)
-    PF_LAUNCH("pf_fwd_f32", fwd_f32_kernel<128>, grid, dim3(kT), stream, a);
+    PF_LAUNCH("pf_fwd_f32", fwd_f32_kernel<128>, q_grid(a), dim3(kThreads), stream, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -278,24 +592,23 @@ hipError_t launch_fwd_f32(const AttnArgs& a, int32_t head_dim, hipStream_t strea
 
 hipError_t launch_bwd_dq_f32(const AttnArgs& a, int32_t head_dim, hipStream_t stream) {
   if (a.rows <= 0) return hipSuccess;
-  dim3 grid((a.rows + kT - 1) / kT, a.hq);
   if (head_dim == 64)
-    PF_LAUNCH("pf_bwd_dq_f32", dq_f32_kernel<64>, grid, dim3(kT), stream, a);
+    PF_LAUNCH("pf_bwd_dq_f32", dq_f32_kernel<64>, q_grid(a), dim3(kThreads), stream, a);
   else if (head_dim == 128)
-    PF_LAUNCH("pf_bwd_dq_f32", dq_f32_kernel<128>, grid, dim3(kT), stream, a);
+    PF_LAUNCH("pf_bwd_dq_f32", dq_f32_kernel<128>, q_grid(a), dim3(kThreads), stream, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_dkv_f32(const AttnArgs& a, int32_t head_dim, hipStream_t stream) {
-  const int blocks = (a.n_ext + kT - 1) / kT + (a.rows + kT - 1) / kT;
+  const int blocks = (a.n_ext + kDkvKeys - 1) / kDkvKeys + (a.rows + kDkvKeys - 1) / kDkvKeys;
   if (blocks <= 0) return hipSuccess;
   dim3 grid(blocks, a.hkv);
   if (head_dim == 64)
-    PF_LAUNCH("pf_bwd_dkv_f32", dkv_f32_kernel<64>, grid, dim3(kT), stream, a);
+    PF_LAUNCH("pf_bwd_dkv_f32", dkv_f32_kernel<64>, grid, dim3(kThreads), stream, a);
   else if (head_dim == 128)
-    PF_LAUNCH("pf_bwd_dkv_f32", dkv_f32_kernel<128>, grid, dim3(kT), stream, a);
+    PF_LAUNCH("pf_bwd_dkv_f32", dkv_f32_kernel<128>, grid, dim3(kThreads), stream, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -46,6 +46,13 @@ SUFFIX_CASES = [
     (16, 16, 128, "bf16", 64, [40, 90], None),
     (2, 2, 64, "f32", 256, [64, 64, 64, 64], None),
     (4, 2, 128, "f32", 100, [3, 70, 0], None),
+    # fp32 matrix-core kernels: several 128-key blocks and 32-row tiles with
+    # ragged tails, query-head groups of 1, 2, 4 and 8, a permuted head map
+    (8, 2, 128, "f32", 300, [1, 77, 130, 0, 64], None),
+    (6, 3, 64, "f32", 130, [70, 33], None),
+    (4, 2, 128, "f32", 96, [40, 41], [1, 0, 0, 1]),
+    (8, 1, 64, "f32", 129, [33, 257], None),
+    (3, 3, 128, "f32", 0, [100, 30], None),
 ]
 
 
@@ -132,6 +139,8 @@ PREFIX_CASES = [
     (8, 2, 128, "bf16", 257, False),
     (2, 2, 64, "f32", 256, True),
     (4, 2, 128, "f32", 77, False),
+    (8, 2, 128, "f32", 300, True),
+    (6, 2, 64, "f32", 257, False),
 ]
 
 
