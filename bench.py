@@ -34,7 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA
-PEAK_F32_TFLOPS = 157.3        # MI355X fp32 vector
+PEAK_F32_TFLOPS = 157.3        # MI355X dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0
 
 
@@ -44,9 +44,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2,
-                    help="workload (1..8; 6 is tree windows over a cached prefix, 7 compact "
-                         "log-probabilities, 8 windows under a producer tree's nodes); 2 is "
-                         "the headline")
+                    help="workload (1..9; 6 is tree windows over a cached prefix, 7 compact "
+                         "log-probabilities, 8 windows under a producer tree's nodes, 9 the "
+                         "headline group in fp32); 2 is the headline")
     ap.add_argument("--separate-windows", action="store_true",
                     help="config 6: one call per window instead of the four trees in one call")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -494,17 +494,36 @@ KERNEL_SYMBOL = {"pf_fwd_bf16": "fwd_kernel", "pf_bwd_dq_bf16": "bwd_dq_kernel",
 COPY_SYMBOL = "neg_kernel"       # the elementwise copy run by --copy-probe-mib
 
 
-def kernel_source_hash():
-    """sha256 over the library's kernel and launch sources: a stored traffic
-    figure only applies to the kernels it was measured on."""
+# Each kernel family's own source file; the rest of csrc/ (launch code, shared
+# headers, the prep kernels) is common to every family.
+FAMILY_SOURCES = {"bf16": "pf_attn_bf16.hip", "f32": "pf_attn_f32.hip",
+                  "logprob": "pf_logprob.hip"}
+
+
+def config_family(cid):
+    from workloads import get_config
+    cfg = get_config(cid)
+    return "logprob" if cfg.is_logprob else cfg.dtype
+
+
+def kernel_source_hash(family):
+    """sha256 over the sources a kernel family's launches depend on (its own
+    file and the common ones): a stored traffic figure only applies to the
+    kernels it was measured on."""
     import hashlib
+    others = {f for fam, f in FAMILY_SOURCES.items() if fam != family}
     h = hashlib.sha256()
     cdir = os.path.join(ROOT, "shared_prefix_attention_pf_amd", "csrc")
     for name in sorted(os.listdir(cdir)):
-        if name.endswith((".hip", ".cpp", ".h")):
+        if name.endswith((".hip", ".cpp", ".h")) and name not in others:
             with open(os.path.join(cdir, name), "rb") as f:
                 h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
+
+
+def source_hash_line(cid):
+    fam = config_family(cid)
+    return f"kernel sources sha256 ({fam} family): `{kernel_source_hash(fam)}`"
 
 
 def traffic_path(cid):
@@ -582,7 +601,7 @@ def traffic_summary(fetch_dir, write_dir, out_md, cid, copy_mib, command):
             continue
         rb, wb = fk[0] * 1024 * f_fac, wk[0] * 1024 * w_fac
         lines.append(f"| {label} | {sym} | {fk[1]} | {fk[0]:.1f} | {wk[0]:.1f} | {rb:.6g} | {wb:.6g} |")
-    lines += ["", f"kernel sources sha256: `{kernel_source_hash()}`", ""]
+    lines += ["", source_hash_line(cid), ""]
     with open(out_md, "w") as f:
         f.write("\n".join(lines))
     print("\n".join(lines))
@@ -620,7 +639,7 @@ def stats_summary(stats_csv, out_md, cid, command):
     if comb:
         lines += ["", "Combined over template forms (what bench.py's per-kernel pass averages):",
                   ""] + comb
-    lines += ["", f"kernel sources sha256: `{kernel_source_hash()}`", ""]
+    lines += ["", source_hash_line(cid), ""]
     with open(out_md, "w") as f:
         f.write("\n".join(lines))
     print("\n".join(lines))
@@ -688,7 +707,7 @@ def counter_summary(run_dirs, out_md, cid, command):
         lines.append(f"| {k} ({ph}) | " + " | ".join("-" if v is None else f"{v:.4g}" for v in vals)
                      + f" | {vpm} | {busy} | {share(c.get('SQ_ACTIVE_INST_ANY'))} | "
                      f"{share(c.get('SQ_WAIT_ANY'))} | {share(c.get('SQ_WAIT_INST_ANY'))} |")
-    lines += ["", f"kernel sources sha256: `{kernel_source_hash()}`", ""]
+    lines += ["", source_hash_line(cid), ""]
     with open(out_md, "w") as f:
         f.write("\n".join(lines))
     print("\n".join(lines))
@@ -701,7 +720,7 @@ def load_traffic(cid, label):
     if not os.path.exists(path):
         return None, "no counter summary"
     text = open(path).read()
-    if f"`{kernel_source_hash()}`" not in text:
+    if source_hash_line(cid) not in text:
         return None, "kernel sources changed since the counters were taken"
     for ln in text.splitlines():
         cells = [c.strip() for c in ln.strip().strip("|").split("|")]
@@ -1200,7 +1219,7 @@ def main():
         achieved = flops_per_launch / (kn["avg_ms"] * 1e-3) / 1e12
         peak = PEAK_BF16_TFLOPS if "bf16" in dom else PEAK_F32_TFLOPS
         traffic, traffic_src = load_traffic(cfg.cid, dom)
-        roofline = {"bound": "mfma" if "bf16" in dom else "alu", "kernel": dom,
+        roofline = {"bound": "mfma", "kernel": dom,
                     "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                     "frac": round(achieved / peak, 4),
                     "traffic": None if traffic is None else round(traffic),
@@ -1221,7 +1240,8 @@ def main():
 
     peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
     out = {
-        "metric": "suffix attn fwd+bwd TFLOP/s & % bf16 MFMA peak; group tokens/s vs oracle",
+        "metric": (f"suffix attn fwd+bwd TFLOP/s & % {cfg.dtype} MFMA peak; group tokens/s vs "
+                   "oracle"),
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -1249,7 +1269,7 @@ def main():
             "cached_ranges": ([w["ranges"] for w in data["windows"]] if cfg.is_ranges else None),
             "parallelism": "single GPU",
         },
-        "pct_of_bf16_peak": round(100.0 * value / peak, 2),
+        f"pct_of_{cfg.dtype}_peak": round(100.0 * value / peak, 2),
         "phase_ms": {k: round(v, 4) for k, v in gres["phase_ms"].items()},
         "phase_b_gflop": round(flops_b / 1e9, 2),
         "group_tokens_per_s": {"compact": round(compact / (step_ms * 1e-3), 1),

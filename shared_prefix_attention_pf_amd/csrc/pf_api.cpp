@@ -502,8 +502,8 @@ void launch_hook(const char* kernel, hipStream_t stream, int end) {
 int32_t ext_chunks(int32_t n_ext, int32_t rows, int32_t hq, int32_t hkv, int32_t head_dim,
                    int32_t dtype) {
   (void)head_dim;
-  if (dtype != PF_BF16 || n_ext <= 0 || rows <= 0) return 1;
-  const int kb = dkv_keys_per_workgroup_bf16();
+  if (n_ext <= 0 || rows <= 0) return 1;
+  const int kb = dtype == PF_BF16 ? dkv_keys_per_workgroup_bf16() : dkv_keys_per_workgroup_f32();
   const int64_t wgs = (int64_t)((n_ext + kb - 1) / kb) * hkv;
   const int64_t steps = (int64_t)((rows + 31) / 32) * (hq / hkv);
   int32_t nc = 1;
@@ -520,10 +520,10 @@ int32_t ext_chunks(int32_t n_ext, int32_t rows, int32_t hq, int32_t hkv, int32_t
 int32_t own_chunks(int32_t op, int32_t n_ext, int32_t rows, int32_t hq, int32_t hkv,
                    int32_t head_dim, int32_t dtype) {
   (void)head_dim;
-  if (dtype != PF_BF16 || rows <= 0) return 1;
+  if (rows <= 0) return 1;
   if (op == PF_OP_SUFFIX_BWD) return (n_ext > 0 && rows >= 512) ? 2 : 1;
   if (op != PF_OP_PREFIX_BWD && op != PF_OP_TREE_BWD && op != PF_OP_TREE_SUFFIX_BWD) return 1;
-  const int kb = dkv_keys_per_workgroup_bf16();
+  const int kb = dtype == PF_BF16 ? dkv_keys_per_workgroup_bf16() : dkv_keys_per_workgroup_f32();
   const int64_t wgs = (int64_t)((rows + kb - 1) / kb) * hkv;
   const int64_t steps = (int64_t)((rows / 2 + 31) / 32) * (hq / hkv);
   int32_t nc = 1;

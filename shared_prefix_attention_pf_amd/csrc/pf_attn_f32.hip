@@ -396,10 +396,12 @@ __global__ __launch_bounds__(kThreads, 1) void dq_f32_kernel(AttnArgs a) {
     }
 }
 
-// KV-stationary: workgroup x of KV head y holds 128 keys (external blocks
-// first, then own), 32 per wave; it walks every (32-token tile, query head)
-// step whose rows may see its keys: all rows for external keys, rows from the
-// block's first key to the largest visibility end of its keys for own keys.
+// KV-stationary: a workgroup holds 128 keys of KV head y, 32 per wave, and
+// walks the (32-token tile, query head) steps whose rows may see them: all
+// rows for external keys, rows from the block's first key to the largest
+// visibility end of its keys for own keys.  A block's steps may be split into
+// query chunks (a.n_chunks external, a.n_chunks_own own), one workgroup each;
+// item x is (external block, chunk) pairs first, then (own block, chunk).
 template <int D>
 __global__ __launch_bounds__(kThreads, 1) void dkv_f32_kernel(AttnArgs a) {
   constexpr int H = D / 2, NT = D / 32, RS = Tile<D>::kRs;
@@ -409,8 +411,12 @@ __global__ __launch_bounds__(kThreads, 1) void dkv_f32_kernel(AttnArgs a) {
   const int lane = threadIdx.x & 63, col = lane & 31, h = lane >> 5;
   const int g = blockIdx.y;
   const int n_ext_b = (a.n_ext + kDkvKeys - 1) / kDkvKeys;
-  const bool ext = (int)blockIdx.x < n_ext_b;
-  const int k0 = (ext ? (int)blockIdx.x : (int)blockIdx.x - n_ext_b) * kDkvKeys;
+  const int n_ext_items = n_ext_b * a.n_chunks;
+  const bool ext = (int)blockIdx.x < n_ext_items;
+  const int nch = ext ? a.n_chunks : a.n_chunks_own;
+  const int item = ext ? (int)blockIdx.x : (int)blockIdx.x - n_ext_items;
+  const int chunk = item % nch;
+  const int k0 = (item / nch) * kDkvKeys;
   const int kw0 = k0 + 32 * wave;
   const int kk = kw0 + col;
   const int klim = ext ? a.n_ext : a.rows;
@@ -456,7 +462,13 @@ __global__ __launch_bounds__(kThreads, 1) void dkv_f32_kernel(AttnArgs a) {
   }
   const int qt_lo = qlo / 32;
   const int n_qt = qhi > qlo ? (qhi - 1) / 32 - qt_lo + 1 : 0;
-  const int n_it = n_qt * a.group;
+  // this chunk's steps [it_lo, it_hi) of the block's n_qt * group
+  int it_lo = 0, it_hi = n_qt * a.group;
+  if (nch > 1) {
+    const int per = (it_hi + nch - 1) / nch;
+    it_lo = min(it_hi, chunk * per);
+    it_hi = min(it_hi, it_lo + per);
+  }
 
   auto stage = [&](int it, int b) {
     const int t0 = (qt_lo + it / a.group) * 32;
@@ -480,11 +492,11 @@ __global__ __launch_bounds__(kThreads, 1) void dkv_f32_kernel(AttnArgs a) {
   }
   const float c = a.scale_log2;
 
-  if (n_it > 0) stage(0, 0);
-  for (int it = 0, b = 0; it < n_it; ++it, b ^= 1) {
+  if (it_lo < it_hi) stage(it_lo, 0);
+  for (int it = it_lo, b = 0; it < it_hi; ++it, b ^= 1) {
     wait_dma();
     __syncthreads();
-    if (it + 1 < n_it) stage(it + 1, b ^ 1);
+    if (it + 1 < it_hi) stage(it + 1, b ^ 1);
     const int t0 = (qt_lo + it / a.group) * 32;
     // own keys: the step's rows may see some key of the wave
     if (!ext && (t0 + 31 < kw0 || t0 >= wave_hi)) continue;
@@ -528,29 +540,31 @@ __global__ __launch_bounds__(kThreads, 1) void dkv_f32_kernel(AttnArgs a) {
   }
 
   if (!kvalid) return;
-  // dK^T / dV^T register r: head_dim index 32 dt + crow(r, h) of the lane's key
+  // dK^T / dV^T register r: head_dim index 32 dt + crow(r, h) of the lane's
+  // key.  Destination: 0 add into gK/gV (an unsplit external block, or the
+  // first chunk of a split one: no other workgroup touches those elements in
+  // the launch), 1 external partial plane chunk - 1, 2 own partial plane
+  // chunk, 3 own output (+ gk_init / gv_init).  The finishing pass adds the
+  // planes in a fixed order, so every result is the same run to run.
+  const int mode = ext ? (chunk == 0 ? 0 : 1) : (nch > 1 ? 2 : 3);
   const int64_t base = ((int64_t)kk * a.hkv + g) * D;
-  if (ext) {
-#pragma unroll
-    for (int dt = 0; dt < NT; ++dt)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d0 = 32 * dt + 8 * q4 + 4 * h;
-        f32x4* pk = (f32x4*)(a.gk_acc + base + d0);
-        f32x4* pv = (f32x4*)(a.gv_acc + base + d0);
-        f32x4 xk = *pk, xv = *pv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          xk[e] += dk[dt][4 * q4 + e] * a.scale;
-          xv[e] += dv[dt][4 * q4 + e];
-        }
-        *pk = xk;
-        *pv = xv;
-      }
-    return;
+  float* pk = nullptr;
+  float* pv = nullptr;
+  if (mode == 0) {
+    pk = a.gk_acc + base;
+    pv = a.gv_acc + base;
+  } else if (mode == 1) {
+    const int64_t pb = (int64_t)(chunk - 1) * a.n_ext * a.hkv * D + base;
+    pk = a.gk_part + pb;
+    pv = a.gv_part + pb;
+  } else if (mode == 2) {
+    const int64_t pb = (int64_t)chunk * a.rows * a.hkv * D + base;
+    pk = a.dk_part + pb;
+    pv = a.dv_part + pb;
+  } else {
+    pk = (float*)a.dk_own + (int64_t)kk * a.dko_st + (int64_t)g * a.dko_sh;
+    pv = (float*)a.dv_own + (int64_t)kk * a.dvo_st + (int64_t)g * a.dvo_sh;
   }
-  float* dkp = (float*)a.dk_own + (int64_t)kk * a.dko_st + (int64_t)g * a.dko_sh;
-  float* dvp = (float*)a.dv_own + (int64_t)kk * a.dvo_st + (int64_t)g * a.dvo_sh;
 #pragma unroll
   for (int dt = 0; dt < NT; ++dt)
 #pragma unroll
@@ -562,12 +576,15 @@ __global__ __launch_bounds__(kThreads, 1) void dkv_f32_kernel(AttnArgs a) {
         xk[e] = dk[dt][4 * q4 + e] * a.scale;
         xv[e] = dv[dt][4 * q4 + e];
       }
-      if (a.gk_init) {
+      if (mode == 0) {
+        xk += *(const f32x4*)(pk + d0);
+        xv += *(const f32x4*)(pv + d0);
+      } else if (mode == 3 && a.gk_init) {
         xk += *(const f32x4*)(a.gk_init + base + d0);
         xv += *(const f32x4*)(a.gv_init + base + d0);
       }
-      *(f32x4*)(dkp + d0) = xk;
-      *(f32x4*)(dvp + d0) = xv;
+      *(f32x4*)(pk + d0) = xk;
+      *(f32x4*)(pv + d0) = xv;
     }
 }
 
@@ -601,8 +618,11 @@ hipError_t launch_bwd_dq_f32(const AttnArgs& a, int32_t head_dim, hipStream_t st
   return hipGetLastError();
 }
 
+int32_t dkv_keys_per_workgroup_f32() { return kDkvKeys; }
+
 hipError_t launch_bwd_dkv_f32(const AttnArgs& a, int32_t head_dim, hipStream_t stream) {
-  const int blocks = (a.n_ext + kDkvKeys - 1) / kDkvKeys + (a.rows + kDkvKeys - 1) / kDkvKeys;
+  const int blocks = (a.n_ext + kDkvKeys - 1) / kDkvKeys * a.n_chunks +
+                     (a.rows + kDkvKeys - 1) / kDkvKeys * a.n_chunks_own;
   if (blocks <= 0) return hipSuccess;
   dim3 grid(blocks, a.hkv);
   if (head_dim == 64)

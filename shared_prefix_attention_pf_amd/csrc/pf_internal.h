@@ -197,6 +197,8 @@ hipError_t launch_bwd_dkv_bf16(const AttnArgs& a, const ItemOrder& ord, int32_t 
 hipError_t launch_fwd_f32(const AttnArgs& a, int32_t head_dim, hipStream_t stream);
 hipError_t launch_bwd_dq_f32(const AttnArgs& a, int32_t head_dim, hipStream_t stream);
 hipError_t launch_bwd_dkv_f32(const AttnArgs& a, int32_t head_dim, hipStream_t stream);
+// keys one workgroup of the fp32 KV-stationary backward holds
+int32_t dkv_keys_per_workgroup_f32();
 
 // Compact log-probabilities (pf_logprob.hip); strides in bytes, bf16 != 0
 // selects bf16 logits (else fp32)

@@ -98,7 +98,8 @@ def _check_phase_b_group(cfg, data, res, g):
 
 
 def _desc(cfg):
-    return pf.AttnDesc(cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, pf.PF_BF16)
+    return pf.AttnDesc(cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim,
+                       pf.PF_BF16 if cfg.dtype == "bf16" else pf.PF_F32)
 
 
 def test_config1_fp32_all_phases():
@@ -138,10 +139,12 @@ def test_config1_fp32_all_phases():
     check("dV_P", host(dv_p), rdv, tol)
 
 
-def test_config2_all_phases_full_size():
+@pytest.mark.parametrize("cid", [2, 9])
+def test_config2_all_phases_full_size(cid):
     """Phase A, one Phase-B call over all 8 suffixes, Phase C with the
-    accumulated gK/gV injected: the benchmark's step at config 2."""
-    cfg = get_config(2)
+    accumulated gK/gV injected: the benchmark's step at config 2 (bf16) and at
+    config 9 (the same shapes in fp32)."""
+    cfg = get_config(cid)
     print(f"\ngenerating config {cfg.cid}", flush=True)
     data = generate(cfg)
     desc = _desc(cfg)

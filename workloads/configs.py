@@ -1,5 +1,5 @@
 """The synthetic group shapes the path is tested and measured on (five groups,
-and a sixth workload of tree windows over a cached prefix).
+the next rows' workloads, and the headline group in fp32).
 
 Shapes follow the workloads the PrefixFlow page trains on (flat GRPO groups
 [P || S_i], PrefixFlow §2.1; long-prefix RAG groups, §5.2 Claim 2.1; the
@@ -94,6 +94,10 @@ CONFIGS: List[Config] = [
                 "3584 rows of that node and its ancestors in place; producer forward, the 8 "
                 "windows forward and backward adding into the producer rows' gK/gV, then the "
                 "producer backward with them injected"),
+    Config(9, "gqa-f32-p4096-n8x512", "f32", 32, 8, 128, 4096, n_suffix=8, suffix_len=512,
+           seed=9,
+           note="the config-2 group with fp32 tensors end to end: the fp32 kernels (matrix-core "
+                "products in fp32) at the headline shape; one Phase-B call with all 8 suffixes"),
     Config(7, "logprob-bf16-tree5-v151936", "bf16", 16, 4, 128, 0,
            tree_levels=((1, 4096), (4, 1024), (4, 256)), logprob_vocab=151936, seed=7,
            note="compact log-probabilities of the config-5 tree: 12288 compact rows of bf16 "
