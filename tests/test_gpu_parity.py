@@ -53,6 +53,9 @@ SUFFIX_CASES = [
     (4, 2, 128, "f32", 96, [40, 41], [1, 0, 0, 1]),
     (8, 1, 64, "f32", 129, [33, 257], None),
     (3, 3, 128, "f32", 0, [100, 30], None),
+    # one KV head with eight query heads over 1024 rows: the prefix blocks split
+    # into eight query chunks, the own blocks into two
+    (8, 1, 64, "f32", 200, [600, 424], None),
 ]
 
 
@@ -193,18 +196,20 @@ def test_tree(seed, hq, hkv, dtype):
     _tree_case(seed, hq, hkv, dtype, 9, 90)
 
 
-def test_maximum_sizes():
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_maximum_sizes(dtype):
     """The limits the boundary accepts: PF_MAX_SEGMENTS suffixes in one call
     (ragged, a quarter of them empty) and a tree of PF_MAX_SEGMENTS nodes,
     PF_MAX_HEADS query heads as 128 per KV head and as one per KV head."""
+    d = 128 if dtype == "bf16" else 64
     rng = np.random.Generator(np.random.PCG64(77))
     lens = rng.integers(0, 10, size=pf.PF_MAX_SEGMENTS)
     lens[rng.permutation(pf.PF_MAX_SEGMENTS)[:pf.PF_MAX_SEGMENTS // 4]] = 0
-    _suffix_case((4, 2, 128, "bf16", 100, lens.tolist(), None))
-    _tree_case(11, 4, 2, "bf16", pf.PF_MAX_SEGMENTS, 6)
+    _suffix_case((4, 2, d, dtype, 100, lens.tolist(), None))
+    _tree_case(11, 4, 2, dtype, pf.PF_MAX_SEGMENTS, 6)
     for hkv in (2, pf.PF_MAX_HEADS):
-        _suffix_case((pf.PF_MAX_HEADS, hkv, 128, "bf16", 40, [30, 0, 17], None))
-        _prefix_case((pf.PF_MAX_HEADS, hkv, 128, "bf16", 45, True))
+        _suffix_case((pf.PF_MAX_HEADS, hkv, d, dtype, 40, [30, 0, 17], None))
+        _prefix_case((pf.PF_MAX_HEADS, hkv, d, dtype, 45, True))
 
 
 def _tree_case(seed, hq, hkv, dtype, n_nodes, max_len):
