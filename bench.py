@@ -488,7 +488,8 @@ def kernel_pass(torch, pf, timer, step, phases_of, timed_phase_ms, n_steps, lead
 KERNEL_SYMBOL = {"pf_fwd_bf16": "fwd_kernel", "pf_bwd_dq_bf16": "bwd_dq_kernel",
                  "pf_bwd_dq_ds_bf16": "bwd_dq_ds_kernel", "pf_bwd_dkv_bf16": "bwd_dkv_kernel",
                  "pf_fwd_f32": "fwd_f32_kernel", "pf_bwd_dq_f32": "dq_f32_kernel",
-                 "pf_bwd_dkv_f32": "dkv_f32_kernel", "pf_prep_dsum": "prep_dsum_kernel",
+                 "pf_bwd_dkv_f32": "dkv_f32_kernel", "pf_bwd_dq_ds_f32": "dq_ds_f32_kernel",
+                 "pf_prep_dsum": "prep_dsum_kernel",
                  "pf_partials": "partial_sums_kernel", "pf_logprob_fwd": "logprob_fwd_kernel",
                  "pf_logprob_bwd": "logprob_bwd_kernel"}
 COPY_SYMBOL = "neg_kernel"       # the elementwise copy run by --copy-probe-mib
@@ -1203,7 +1204,7 @@ def main():
     # recompute of S and dP is not counted); dK/dV kernel 6d (dV, dP, dK)
     per_pair = {"pf_fwd_bf16": 4, "pf_bwd_dq_bf16": 2, "pf_bwd_dq_ds_bf16": 2,
                 "pf_bwd_dkv_bf16": 6, "pf_fwd_f32": 4, "pf_bwd_dq_f32": 2,
-                "pf_bwd_dkv_f32": 6}
+                "pf_bwd_dq_ds_f32": 2, "pf_bwd_dkv_f32": 6}
     # a kernel launched in a phase covers every visible pair of that phase
     phase_pairs = {"A": pairs_a, "B": pairs_b, "C": pairs_a, "tree": pairs_b}
     for label, kn in kern.items():

@@ -230,18 +230,19 @@ struct WsLayout {
   int32_t ds_keys = 0, ds_rows = 0, ds_own0 = 0;
 };
 
-// A bf16 backward keeps dS^T when the workspace allows it (Phase B, Phase C
-// and trees): the buffer holds Hq x (ceil256(n_ext) + ceil256(rows)) keys x
-// ceil256(rows) rows of bf16, of which only the visible tiles are written and
-// read (one head's share must stay below 2 GiB for 32-bit buffer offsets).
+// A backward keeps dS when the workspace allows it (Phase B, Phase C and
+// trees): the buffer holds Hq x (ceil256(n_ext) + ceil256(rows)) keys x
+// ceil256(rows) rows in the input dtype (bf16 or fp32), of which only the
+// visible tiles are written and read (one head's share must stay below 2 GiB
+// for 32-bit buffer offsets).
 bool ds_eligible(int32_t op, const Desc& d, int32_t n_ext, int32_t rows) {
   if (op != PF_OP_SUFFIX_BWD && op != PF_OP_PREFIX_BWD && op != PF_OP_TREE_BWD &&
       op != PF_OP_TREE_SUFFIX_BWD)
     return false;
-  if (d.dtype != PF_BF16 || rows <= 0) return false;
+  if (rows <= 0) return false;
   const int64_t r = ((int64_t)rows + 255) / 256 * 256;
   const int64_t keys = ((int64_t)n_ext + 255) / 256 * 256 + r;
-  return keys * r * 2 < ((int64_t)1 << 31);
+  return keys * r * elem_bytes(d.dtype) < ((int64_t)1 << 31);
 }
 
 WsLayout layout(int32_t op, const Desc& d, int32_t n_ext, int32_t rows, bool want_ds = false,
@@ -287,7 +288,7 @@ WsLayout layout(int32_t op, const Desc& d, int32_t n_ext, int32_t rows, bool wan
     w.ds_own0 = (n_ext + 255) / 256 * 256;
     w.ds_keys = w.ds_own0 + w.ds_rows;
     w.ds_ext = off;
-    off += align_up((size_t)d.hq * w.ds_keys * w.ds_rows * 2);
+    off += align_up((size_t)d.hq * w.ds_keys * w.ds_rows * elem_bytes(d.dtype));
   }
   w.total = rows > 0 ? off : 0;
   return w;
@@ -457,13 +458,16 @@ pf_status run_bwd(const Desc& d, const pf::AttnArgs& a, const pf::SegTable& seg,
   if (d.dtype == PF_BF16) pf::dkv_item_order(a, seg, ord);
   const pf::PartialSums ps = partial_sums_of(d, a);
   if (a.ds_ext) {
-    // prep with D and LSE first; the dK/dV pass stores dS^T, then dQ is read
-    // from it, with the split blocks' partial sums in the same launch
-    e = pf::launch_prep_dsum_bf16(seg, d.heads, a, st);
+    // prep with D and LSE first; the dK/dV pass stores dS, then dQ is read
+    // from it, followed by the split blocks' partial sums (bf16: in the same
+    // launch)
+    const bool bf16 = d.dtype == PF_BF16;
+    e = bf16 ? pf::launch_prep_dsum_bf16(seg, d.heads, a, st)
+             : pf::launch_prep_dsum_f32(seg, d.heads, a, d.d, st);
     if (e != hipSuccess) return hip_fail(e, "prep");
-    e = pf::launch_bwd_dkv_bf16(a, ord, d.d, st);
+    e = bf16 ? pf::launch_bwd_dkv_bf16(a, ord, d.d, st) : pf::launch_bwd_dkv_f32(a, d.d, st);
     if (e != hipSuccess) return hip_fail(e, "dkv");
-    e = pf::launch_bwd_dq_ds_bf16(a, ps, d.d, st);
+    e = bf16 ? pf::launch_bwd_dq_ds_bf16(a, ps, d.d, st) : pf::launch_bwd_dq_ds_f32(a, ps, d.d, st);
     if (e != hipSuccess) return hip_fail(e, "dq_ds");
     return PF_OK;
   }

@@ -491,6 +491,11 @@ __global__ __launch_bounds__(kThreads, 1) void dkv_f32_kernel(AttnArgs a) {
     dv[dt] = zero16();
   }
   const float c = a.scale_log2;
+  // the dS buffer (fp32): 32 x 32 tiles [query head][query step][key tile],
+  // each row-major over (query, key); own keys from key tile ds_own0 / 32
+  float* const dsb = (float*)a.ds_ext;
+  const int ds_qt = a.ds_rows / 32, ds_kt = a.ds_keys / 32;
+  const int ds_k0 = ext ? 0 : a.ds_own0 / 32;
 
   if (it_lo < it_hi) stage(it_lo, 0);
   for (int it = it_lo, b = 0; it < it_hi; ++it, b ^= 1) {
@@ -522,12 +527,20 @@ __global__ __launch_bounds__(kThreads, 1) void dkv_f32_kernel(AttnArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * q4 + e, tq = t0 + crow(r, h);
-        const bool vis = tq < a.rows && (ext || (kk <= tq && tq < kend_k));
+        const bool vis = tq < a.rows && kvalid && (ext || (kk <= tq && tq < kend_k));
         // a visible row sees at least this key, so its LSE is finite
         const float p = vis ? exp2_(s[r] * c - lv[e] * kLog2e) : 0.f;
         s[r] = p;
         dp[r] = p * (dp[r] - dsv[e]);
       }
+    }
+    if (dsb) {
+      // this wave's dS tile of the step for the dQ pass: rows are the step's
+      // queries, columns the wave's keys (a streaming store, read once later)
+      const int head = a.ri.qhead[g * a.group + it % a.group];
+      float* tile = dsb + ((int64_t)(head * ds_qt + t0 / 32) * ds_kt + ds_k0 + kw0 / 32) * 1024;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) __builtin_nontemporal_store(dp[r], tile + crow(r, h) * 32 + col);
     }
 #pragma unroll
     for (int dt = 0; dt < NT; ++dt)
@@ -588,6 +601,86 @@ __global__ __launch_bounds__(kThreads, 1) void dkv_f32_kernel(AttnArgs a) {
     }
 }
 
+// K tile i of a Q-stationary workgroup into LDS
+template <int D>
+__device__ __forceinline__ void stage_k(const AttnArgs& a, const QTiles& w, int i, float* k_s,
+                                        int wave, int lane) {
+  const bool ext = i < w.n_ext_t;
+  const int k0 = w.key0(i);
+  const int valid = (ext ? a.n_ext : a.rows) - k0;
+  const int64_t kst = ext ? a.kx_st : a.ko_st, ksh = ext ? a.kx_sh : a.ko_sh;
+  const float* kb = (const float*)(ext ? a.k_ext : a.k_own) + (int64_t)k0 * kst + (int64_t)w.g * ksh;
+  dma_tile<D>(rows_rsrc<D>(kb, valid, kst), k_s, 4u * (uint32_t)kst, wave, lane);
+}
+
+// dQ from the stored dS: Q-stationary like dq_f32_kernel, over the same key
+// tiles, with dQ^T += K^T dS^T and dS^T read from the buffer instead of
+// recomputed.  A lane's 16 values of a tile (its query's row, keys crow(s, h))
+// are four 16-byte loads, issued one tile ahead.  Every tile a wave reads is
+// one the dK/dV pass wrote: both skip exactly the own tiles none of the wave's
+// rows can see, and the entries of invisible pairs are zero.
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void dq_ds_f32_kernel(AttnArgs a) {
+  constexpr int NT = D / 32, RS = Tile<D>::kRs;
+  __shared__ __attribute__((aligned(16))) float k_s[2][Tile<D>::kFloats];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, col = lane & 31, h = lane >> 5;
+  const QTiles w(a, wave, col);
+  const float* const dsb = (const float*)a.ds_ext;
+  const int64_t row_tiles = (int64_t)(w.head * (a.ds_rows / 32) + w.t0 / 32) * (a.ds_keys / 32);
+  auto load_ds = [&](int i, f32x4 (&dst)[4]) {
+    const int kt = i < w.n_ext_t ? i : a.ds_own0 / 32 + (i - w.n_ext_t);
+    const float* t = dsb + (row_tiles + kt) * 1024 + col * 32 + 4 * h;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dst[j] = __builtin_nontemporal_load((const f32x4*)(t + 8 * j));
+  };
+
+  f32x16 dq[NT];
+#pragma unroll
+  for (int dt = 0; dt < NT; ++dt) dq[dt] = zero16();
+  f32x4 cur[4], nxt[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) cur[j] = nxt[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  int ci = w.live(a, 0) ? 0 : w.next(a, 0);
+  if (ci >= 0) {
+    stage_k<D>(a, w, ci, k_s[0], wave, lane);
+    if (w.wave_sees(a, ci)) load_ds(ci, cur);
+  }
+  for (int b = 0; ci >= 0; b ^= 1) {
+    const int ni = w.next(a, ci);
+    wait_dma();
+    __syncthreads();
+    if (ni >= 0) {
+      stage_k<D>(a, w, ni, k_s[b ^ 1], wave, lane);
+      if (w.wave_sees(a, ni)) load_ds(ni, nxt);
+    }
+    if (w.wave_sees(a, ci)) {
+      const float* ks = k_s[b];
+#pragma unroll
+      for (int dt = 0; dt < NT; ++dt)
+#pragma unroll
+        for (int s2 = 0; s2 < 16; ++s2)
+          dq[dt] = mm(ks[crow(s2, h) * RS + 32 * dt + col], cur[s2 >> 2][s2 & 3], dq[dt]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) cur[j] = nxt[j];
+    ci = ni;
+  }
+
+  if (!w.tvalid) return;
+  float* op = (float*)a.out + (int64_t)w.tok * a.out_st + (int64_t)w.head * a.out_sh;
+#pragma unroll
+  for (int dt = 0; dt < NT; ++dt)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      f32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = dq[dt][4 * q4 + e] * a.scale;
+      *(f32x4*)(op + 32 * dt + 8 * q4 + 4 * h) = v;
+    }
+}
+
 // Q-stationary grid: per KV head, one workgroup per 4 (tile, query head) pairs
 dim3 q_grid(const AttnArgs& a) {
   const int pairs = ((a.rows + 31) / 32) * a.group;
@@ -616,6 +709,21 @@ hipError_t launch_bwd_dq_f32(const AttnArgs& a, int32_t head_dim, hipStream_t st
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq_ds_f32(const AttnArgs& a, const PartialSums& ps, int32_t head_dim,
+                                hipStream_t stream) {
+  if (a.rows > 0) {
+    if (head_dim == 64)
+      PF_LAUNCH("pf_bwd_dq_ds_f32", dq_ds_f32_kernel<64>, q_grid(a), dim3(kThreads), stream, a);
+    else if (head_dim == 128)
+      PF_LAUNCH("pf_bwd_dq_ds_f32", dq_ds_f32_kernel<128>, q_grid(a), dim3(kThreads), stream, a);
+    else
+      return hipErrorInvalidValue;
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return launch_partial_sums(ps, stream);
 }
 
 int32_t dkv_keys_per_workgroup_f32() { return kDkvKeys; }

@@ -104,10 +104,11 @@ struct AttnArgs {
   // chunks: fp32 [n_chunks_own, rows, Hkv, d], finished by launch_partial_sums
   float* dk_part; float* dv_part;
   int32_t n_chunks_own;
-  // Phase B with a dS buffer: the dK/dV pass stores dS^T of every key block
-  // it processes (bf16; external keys at key indices [0, ds_own0), own keys
-  // from ds_own0; ds_keys keys and ds_rows rows in all, layout in the
-  // kernels) and dQ is then formed from it instead of by recomputing S, dP.
+  // A backward with a dS buffer: the dK/dV pass stores dS of every key block
+  // it processes (bf16 for bf16 inputs, fp32 for fp32 ones, where ds_ext is
+  // read as float*; external keys at key indices [0, ds_own0), own keys from
+  // ds_own0; ds_keys keys and ds_rows rows in all, layout in the kernels) and
+  // dQ is then formed from it instead of by recomputing S, dP.
   __bf16* ds_ext; int32_t ds_keys, ds_rows, ds_own0;
   RowInfo ri;
   int32_t rows;
@@ -133,6 +134,9 @@ hipError_t launch_prep(const SegTable& seg, const HeadTable& heads, RowInfo ri, 
 // a.dsum / a.lse2 (bf16 inputs).
 hipError_t launch_prep_dsum_bf16(const SegTable& seg, const HeadTable& heads, const AttnArgs& a,
                                  hipStream_t stream);
+// the same for fp32 inputs (head_dim 64 or 128)
+hipError_t launch_prep_dsum_f32(const SegTable& seg, const HeadTable& heads, const AttnArgs& a,
+                                int32_t head_dim, hipStream_t stream);
 // ext_tiles[0 .. rt.vt0[rt.n]) from the range table
 hipError_t launch_ext_tiles(const RangeTable& rt, int2* tiles, hipStream_t stream);
 hipError_t launch_fill_zero(void* dst, int64_t rows, int32_t heads, int32_t d, int64_t st,
@@ -199,6 +203,10 @@ hipError_t launch_bwd_dq_f32(const AttnArgs& a, int32_t head_dim, hipStream_t st
 hipError_t launch_bwd_dkv_f32(const AttnArgs& a, int32_t head_dim, hipStream_t stream);
 // keys one workgroup of the fp32 KV-stationary backward holds
 int32_t dkv_keys_per_workgroup_f32();
+// fp32 dQ from the dS buffer the fp32 dK/dV pass stored (then the partial sums
+// `ps`, which may be empty, in a launch of their own)
+hipError_t launch_bwd_dq_ds_f32(const AttnArgs& a, const PartialSums& ps, int32_t head_dim,
+                                hipStream_t stream);
 
 // Compact log-probabilities (pf_logprob.hip); strides in bytes, bf16 != 0
 // selects bf16 logits (else fp32)

@@ -86,33 +86,43 @@ hipError_t launch_ext_tiles(const RangeTable& rt, int2* tiles, hipStream_t strea
 }
 
 // D and LSE (log2) per (row, query head): 16 lanes per pair, each lane
-// reading 8 head_dim values of dO and O (head_dim 128); a 16-lane group
+// reading D / 16 head_dim values of dO and O in 16-byte loads; a 16-lane group
 // covers kDsumPairs consecutive pairs, all of whose loads are issued before
 // the first product so that enough bytes are in flight to stream from HBM;
 // block `blk` covers 16 kDsumPairs pairs.
 constexpr int kDsumPairs = 4;
+template <typename T, int D>
 __device__ __forceinline__ void dsum_body(const AttnArgs& a, int blk) {
-  typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+  constexpr int PER = D / 16;                  // values per lane
+  constexpr int VEC = 16 / (int)sizeof(T);     // values per 16-byte load
+  constexpr int NV = PER / VEC;                // loads per lane per tensor
+  typedef T vec_t __attribute__((ext_vector_type(VEC)));
+  static_assert(NV * VEC == PER, "head_dim / 16 values per lane in whole 16-byte loads");
   const int sub = threadIdx.x & 15;
   const int64_t n = (int64_t)a.rows * a.hq;
   const int64_t p0 = ((int64_t)blk * 16 + (threadIdx.x >> 4)) * kDsumPairs;
-  bf16x8 dv[kDsumPairs], ov[kDsumPairs];
+  vec_t dv[kDsumPairs][NV], ov[kDsumPairs][NV];
   int hh[kDsumPairs], tt[kDsumPairs];
 #pragma unroll
   for (int u = 0; u < kDsumPairs; ++u) {
     const int64_t pc = p0 + u < n ? p0 + u : n - 1;
     hh[u] = (int)(pc / a.rows);
     tt[u] = (int)(pc - (int64_t)hh[u] * a.rows);
-    dv[u] = *(const bf16x8*)((const __bf16*)a.dout + (int64_t)tt[u] * a.do_st +
-                             (int64_t)hh[u] * a.do_sh + 8 * sub);
-    ov[u] = *(const bf16x8*)((const __bf16*)a.o + (int64_t)tt[u] * a.o_st +
-                             (int64_t)hh[u] * a.o_sh + 8 * sub);
+    const T* dp = (const T*)a.dout + (int64_t)tt[u] * a.do_st + (int64_t)hh[u] * a.do_sh + PER * sub;
+    const T* op = (const T*)a.o + (int64_t)tt[u] * a.o_st + (int64_t)hh[u] * a.o_sh + PER * sub;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      dv[u][v] = *(const vec_t*)(dp + VEC * v);
+      ov[u][v] = *(const vec_t*)(op + VEC * v);
+    }
   }
 #pragma unroll
   for (int u = 0; u < kDsumPairs; ++u) {
     float dot = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) dot = fmaf((float)dv[u][e], (float)ov[u][e], dot);
+    for (int v = 0; v < NV; ++v)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) dot = fmaf((float)dv[u][v][e], (float)ov[u][v][e], dot);
 #pragma unroll
     for (int off = 8; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 16);
     if (sub == 0 && p0 + u < n) {
@@ -126,24 +136,38 @@ __device__ __forceinline__ void dsum_body(const AttnArgs& a, int blk) {
 
 // the prep grid followed by the D/LSE grid, in one launch (neither reads
 // what the other writes)
+template <typename T, int D>
 __global__ __launch_bounds__(256) void prep_dsum_kernel(SegTable seg, HeadTable heads, RowInfo ri,
                                                         AttnArgs a, int n_prep) {
   if ((int)blockIdx.x < n_prep)
     prep_body(seg, heads, ri, blockIdx.x);
   else
-    dsum_body(a, blockIdx.x - n_prep);
+    dsum_body<T, D>(a, blockIdx.x - n_prep);
 }
 
-hipError_t launch_prep_dsum_bf16(const SegTable& seg, const HeadTable& heads, const AttnArgs& a,
-                                 hipStream_t stream) {
+template <typename T, int D>
+static hipError_t launch_prep_dsum(const SegTable& seg, const HeadTable& heads, const AttnArgs& a,
+                                   hipStream_t stream) {
   const int64_t n = (int64_t)a.rows * a.hq;
   if (n <= 0) return hipSuccess;
   const int np = prep_blocks(seg, heads);
   const int64_t per_blk = 16 * kDsumPairs;
-  PF_LAUNCH("pf_prep_dsum", prep_dsum_kernel, dim3((unsigned)(np + (n + per_blk - 1) / per_blk)),
-            dim3(256),
-            stream, seg, heads, a.ri, a, np);
+  PF_LAUNCH("pf_prep_dsum", (prep_dsum_kernel<T, D>),
+            dim3((unsigned)(np + (n + per_blk - 1) / per_blk)), dim3(256), stream, seg, heads,
+            a.ri, a, np);
   return hipGetLastError();
+}
+
+hipError_t launch_prep_dsum_bf16(const SegTable& seg, const HeadTable& heads, const AttnArgs& a,
+                                 hipStream_t stream) {
+  return launch_prep_dsum<__bf16, 128>(seg, heads, a, stream);
+}
+
+hipError_t launch_prep_dsum_f32(const SegTable& seg, const HeadTable& heads, const AttnArgs& a,
+                                int32_t head_dim, hipStream_t stream) {
+  if (head_dim == 64) return launch_prep_dsum<float, 64>(seg, heads, a, stream);
+  if (head_dim == 128) return launch_prep_dsum<float, 128>(seg, heads, a, stream);
+  return hipErrorInvalidValue;
 }
 
 // Sums of the split key blocks' partial planes (PartialSums); blockIdx.y + y0

@@ -114,9 +114,18 @@ def test_workspace_sizes():
     small = pf.pf_workspace_size(pf.PF_OP_SUFFIX_BWD, d, 4096, 512)
     big = pf.pf_workspace_size(pf.PF_OP_SUFFIX_BWD, d, 4096, 4096)
     assert big >= small > 0
-    # the fp32 family never splits the prefix keys into chunks: no partials
+    # fp32: the full workspace adds the fp32 dS buffer, Hq x (ceil256(P) +
+    # ceil256(rows)) keys x ceil256(rows) rows of 4 bytes, twice the bf16 one;
+    # the minimal one (dQ recomputes S and dP) has neither it nor partials here
     f = pf.AttnDesc(2, 2, 64, pf.PF_F32)
-    assert pf.pf_workspace_size(pf.PF_OP_SUFFIX_BWD, f, 256, 256) < 64 * 1024
+    fb = pf.AttnDesc(2, 2, 128, pf.PF_BF16)
+    full = pf.pf_workspace_size(pf.PF_OP_SUFFIX_BWD, f, 256, 256)
+    low = pf.pf_workspace_size_min(pf.PF_OP_SUFFIX_BWD, f, 256, 256)
+    assert low < 64 * 1024
+    assert full - low >= 2 * 512 * 256 * 4
+    assert (full - low) - (pf.pf_workspace_size(pf.PF_OP_SUFFIX_BWD, fb, 256, 256) -
+                           pf.pf_workspace_size_min(pf.PF_OP_SUFFIX_BWD, fb, 256, 256)) \
+        >= 2 * 512 * 256 * 2
     bad = pf.AttnDesc(3, 2, 128)
     assert pf.pf_workspace_size(pf.PF_OP_SUFFIX_FWD, bad, 16, 16) == 0
 

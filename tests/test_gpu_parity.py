@@ -94,7 +94,8 @@ def _suffix_case(case):
         check("gV", host(gv), ref["gv"], tol)
 
 
-@pytest.mark.parametrize("case", [SUFFIX_CASES[0], SUFFIX_CASES[2]],
+@pytest.mark.parametrize("case", [SUFFIX_CASES[0], SUFFIX_CASES[2], SUFFIX_CASES[11],
+                                  SUFFIX_CASES[15]],
                          ids=lambda c: f"{c[3]}-h{c[0]}x{c[1]}-P{c[4]}-{c[5]}")
 def test_suffix_phase_b_min_workspace(case):
     """The backward with the smallest workspace (no dS buffer: dQ recomputes
@@ -131,7 +132,8 @@ def test_suffix_phase_b_min_workspace(case):
     check("dV_S (min ws)", mn["dv"], ref["dv_s"], tol)
     check("gK (min ws)", mn["gk"], ref["gk"], tol)
     check("gV (min ws)", mn["gv"], ref["gv"], tol)
-    # the two paths differ only in rounding (dS rounded to bf16 either way)
+    # the two paths differ only in rounding (for bf16, dS is rounded to bf16
+    # either way)
     for k in ("dq", "dk", "dv", "gk", "gv"):
         check(f"{k}: min ws vs dS buffer", mn[k], outs[1][k], tol)
 
@@ -234,19 +236,21 @@ def _tree_case(seed, hq, hkv, dtype, n_nodes, max_len):
         check(name, host(got), ref[name.lower()], tol)
 
 
-def test_phase_c_and_tree_min_workspace():
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_phase_c_and_tree_min_workspace(dtype):
     """Phase C and the tree backward with the smallest workspace (dQ recomputes
     S and dP) and with the full one (dQ from the stored dS), each against the
     oracle and against each other."""
-    hq, hkv, d, p = 8, 2, 128, 300
-    g = random_small_group(23, hq, hkv, d, p, [1], "bf16")
-    desc = _desc(hq, hkv, d, "bf16")
+    hq, hkv, p = 8, 2, 300
+    d = 128 if dtype == "bf16" else 64
+    g = random_small_group(23, hq, hkv, d, p, [1], dtype)
+    desc = _desc(hq, hkv, d, dtype)
     scale = 1.0 / math.sqrt(d)
     hmap = oracle.head_map(hq, hkv)
     rng = np.random.default_rng(5)
     gk_np = rng.standard_normal((p, hkv, d)).astype(np.float32)
     gv_np = rng.standard_normal((p, hkv, d)).astype(np.float32)
-    t = {k: dev(g[k], "bf16") for k in ("q_p", "k_p", "v_p", "do_p")}
+    t = {k: dev(g[k], dtype) for k in ("q_p", "k_p", "v_p", "do_p")}
     o_p, lse_p = G.prefix_fwd(desc, t["q_p"], t["k_p"], t["v_p"])
     gk, gv = torch.from_numpy(gk_np).cuda(), torch.from_numpy(gv_np).cuda()
     n_min = pf.pf_workspace_size_min(pf.PF_OP_PREFIX_BWD, desc, p, p)
@@ -261,15 +265,15 @@ def test_phase_c_and_tree_min_workspace():
     ref = oracle.prefix_backward_inject(g["q_p"], g["k_p"], g["v_p"], g["do_p"], gk_np, gv_np,
                                         scale, hmap)
     for name, mn, full, r in zip(("dQ_P", "dK_P", "dV_P"), outs[0], outs[1], ref):
-        check(f"{name} (min ws)", mn, r, TOL["bf16"])
-        check(f"{name} (dS buffer)", full, r, TOL["bf16"])
-        check(f"{name}: min ws vs dS buffer", mn, full, TOL["bf16"])
+        check(f"{name} (min ws)", mn, r, TOL[dtype])
+        check(f"{name} (dS buffer)", full, r, TOL[dtype])
+        check(f"{name}: min ws vs dS buffer", mn, full, TOL[dtype])
 
     node_off, parent = random_tree(4, 9, max_len=90, min_len=0)
     print(f"\ntree node_off {node_off.tolist()} parent {parent.tolist()}", flush=True)
     rows = int(node_off[-1])
-    tg = random_tree_group(4, node_off, hq, hkv, d, "bf16")
-    tt = {k: dev(tg[k], "bf16") for k in ("q", "k", "v", "do")}
+    tg = random_tree_group(4, node_off, hq, hkv, d, dtype)
+    tt = {k: dev(tg[k], dtype) for k in ("q", "k", "v", "do")}
     o, lse = G.tree_fwd(desc, node_off, parent, tt["q"], tt["k"], tt["v"])
     n_min = pf.pf_workspace_size_min(pf.PF_OP_TREE_BWD, desc, 0, rows)
     n_full = pf.pf_workspace_size(pf.PF_OP_TREE_BWD, desc, 0, rows)
@@ -283,9 +287,9 @@ def test_phase_c_and_tree_min_workspace():
     ref = oracle.tree_attention_direct(tg["q"], tg["k"], tg["v"], tg["do"], node_off, parent,
                                        scale, hmap)
     for name, mn, full in zip(("dq", "dk", "dv"), outs[0], outs[1]):
-        check(f"tree {name} (min ws)", mn, ref[name], TOL["bf16"])
-        check(f"tree {name} (dS buffer)", full, ref[name], TOL["bf16"])
-        check(f"tree {name}: min ws vs dS buffer", mn, full, TOL["bf16"])
+        check(f"tree {name} (min ws)", mn, ref[name], TOL[dtype])
+        check(f"tree {name} (dS buffer)", full, ref[name], TOL[dtype])
+        check(f"tree {name}: min ws vs dS buffer", mn, full, TOL[dtype])
 
 
 @pytest.mark.parametrize("dtype,p", [("bf16", 300), ("bf16", 0), ("f32", 70)])
