@@ -122,12 +122,14 @@ typedef struct {
  * for the tree and tree-window ops.  Pure host arithmetic; never fails (0 for bad args). */
 size_t pf_workspace_size(int32_t op, const pf_attn_desc* desc, int32_t prefix_len, int32_t rows);
 
-/* The smallest workspace `op` accepts (same arguments).  For the bf16
- * backward ops, pf_workspace_size() adds a buffer for dS (num_q_heads x
- * (ceil256(prefix_len) + ceil256(rows)) x ceil256(rows) bf16 values; prefix_len
- * counts as 0 for Phase C and trees): with it the backward stores dS once and
- * forms dQ from it instead of recomputing S and dP.  A workspace of at least
- * this size but smaller than pf_workspace_size() runs the recompute path.
+/* The smallest workspace `op` accepts (same arguments).  For the backward
+ * ops, pf_workspace_size() adds a buffer for dS (num_q_heads x
+ * (ceil256(prefix_len) + ceil256(rows)) x ceil256(rows) values of the input
+ * dtype, bf16 or fp32; prefix_len counts as 0 for Phase C and trees): with it
+ * the backward stores dS once and forms dQ from it instead of recomputing S
+ * and dP.  The buffer is used only while one query head's share stays below
+ * 2 GiB.  A workspace of at least this size but smaller than
+ * pf_workspace_size() runs the recompute path.
  * Results agree to rounding; each path is deterministic.  Forward ops: equal
  * to pf_workspace_size(). */
 size_t pf_workspace_size_min(int32_t op, const pf_attn_desc* desc, int32_t prefix_len,
