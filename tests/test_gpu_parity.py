@@ -292,6 +292,38 @@ def test_phase_c_and_tree_min_workspace(dtype):
         check(f"tree {name}: min ws vs dS buffer", mn, full, TOL[dtype])
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_tree_bwd_inject_f32(d):
+    """The tree backward with gK/gV injected (a producer tree after its
+    windows) for an fp32 tree against the oracle, with the full and the
+    smallest workspace."""
+    hq, hkv = 4, 2
+    node_off, parent = random_tree(31, 9, max_len=70, min_len=1)
+    rows = int(node_off[-1])
+    print(f"\ntree node_off {node_off.tolist()} parent {parent.tolist()}", flush=True)
+    tg = random_tree_group(31, node_off, hq, hkv, d, "f32")
+    desc = _desc(hq, hkv, d, "f32")
+    scale = 1.0 / math.sqrt(d)
+    hmap = oracle.head_map(hq, hkv)
+    rng = np.random.default_rng(9)
+    gk_np = rng.standard_normal((rows, hkv, d)).astype(np.float32)
+    gv_np = rng.standard_normal((rows, hkv, d)).astype(np.float32)
+    t = {k: dev(tg[k], "f32") for k in ("q", "k", "v", "do")}
+    o, lse = G.tree_fwd(desc, node_off, parent, t["q"], t["k"], t["v"])
+    gk, gv = torch.from_numpy(gk_np).cuda(), torch.from_numpy(gv_np).cuda()
+    rdq, rdk, rdv = oracle.tree_backward_inject(tg["q"], tg["k"], tg["v"], tg["do"], node_off,
+                                                parent, gk_np, gv_np, scale, hmap)
+    n_min = pf.pf_workspace_size_min(pf.PF_OP_TREE_BWD, desc, 0, rows)
+    for ws in (None, torch.empty(n_min, dtype=torch.uint8, device="cuda")):
+        dq, dk, dv = G.tree_bwd_inject(desc, node_off, parent, t["q"], t["k"], t["v"], o, lse,
+                                       t["do"], gk, gv, ws=ws)
+        torch.cuda.synchronize()
+        what = "full ws" if ws is None else "min ws"
+        check(f"dQ ({what})", host(dq), rdq, TOL["f32"])
+        check(f"dK ({what})", host(dk), rdk, TOL["f32"])
+        check(f"dV ({what})", host(dv), rdv, TOL["f32"])
+
+
 @pytest.mark.parametrize("dtype,p", [("bf16", 300), ("bf16", 0), ("f32", 70)])
 def test_tree_windows_over_a_prefix(dtype, p):
     """Two sharing windows of irregular rollout trees over one cached prefix:
