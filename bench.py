@@ -544,6 +544,21 @@ def copy_probe(torch, mib):
     del src, dst
 
 
+def plain_name(name):
+    """A kernel name as the profiler printed it, with the identifiers of a
+    symbol it could not demangle (a template over __bf16 stays mangled) joined
+    by '::', so that names like prep_dsum_kernel can be found in it."""
+    import re
+    if not name.startswith("_Z"):
+        return name
+    parts = []
+    for m in re.finditer(r"\d+", name):
+        ident = name[m.end():m.end() + int(m.group(0))]
+        if len(ident) == int(m.group(0)) and re.fullmatch(r"[A-Za-z_]\w*", ident):
+            parts.append(ident)
+    return "::".join(parts) if parts else name
+
+
 def _counter_means(run_dir, counter):
     """{kernel symbol: mean of `counter` per dispatch} from a rocprofv3 csv run."""
     import csv
@@ -558,8 +573,9 @@ def _counter_means(run_dir, counter):
                 if r["Counter_Name"] != counter:
                     continue
                 key = (fn, r["Dispatch_Id"])
-                per.setdefault(r["Kernel_Name"], {}).setdefault(key, 0.0)
-                per[r["Kernel_Name"]][key] += float(r["Counter_Value"])
+                kname = plain_name(r["Kernel_Name"])
+                per.setdefault(kname, {}).setdefault(key, 0.0)
+                per[kname][key] += float(r["Counter_Value"])
     return {k: (sum(v.values()) / len(v), len(v)) for k, v in per.items()}
 
 
@@ -617,7 +633,7 @@ def stats_summary(stats_csv, out_md, cid, command):
              "```", "", "| kernel | calls | total (us) | average (us) | min (us) | max (us) | share |",
              "|---|---|---|---|---|---|---|"]
     for r in rows:
-        name = r["Name"]
+        name = plain_name(r["Name"])
         m = re.search(r"\w*kernel\w*(<\d+>)?", name)
         short = m.group(0) if m else name[:60]
         fn = re.search(r"\w+Functor", name)
@@ -630,7 +646,7 @@ def stats_summary(stats_csv, out_md, cid, command):
     # launch label to bench.py's per-kernel pass: its combined average
     forms = {}
     for r in rows:
-        m = re.search(r"(\w*kernel\w*)<\d+>", r["Name"])
+        m = re.search(r"(\w*kernel\w*)<\d+>", plain_name(r["Name"]))
         if m:
             f = forms.setdefault(m.group(1), [0, 0.0])
             f[0] += int(r["Calls"])
@@ -663,7 +679,7 @@ def counter_summary(run_dirs, out_md, cid, command):
         for fn in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             disp = {}
             for r in csv.DictReader(open(fn)):
-                m = re.search(r"(\w+_kernel)", r["Kernel_Name"])
+                m = re.search(r"(\w+_kernel)", plain_name(r["Kernel_Name"]))
                 if not m or m.group(1) not in KERNEL_SYMBOL.values():
                     continue
                 did = int(r["Dispatch_Id"])
