@@ -56,6 +56,8 @@ SUFFIX_CASES = [
     # one KV head with eight query heads over 1024 rows: the prefix blocks split
     # into eight query chunks, the own blocks into two
     (8, 1, 64, "f32", 200, [600, 424], None),
+    # a one-row prefix and one-row suffixes
+    (2, 1, 128, "f32", 1, [1, 2, 0, 1], None),
 ]
 
 
