@@ -19,6 +19,8 @@ import sys
 # XDL write -> VALU/memory access of the result: 8-pass products need 11 wait
 # states on gfx940-class hardware; allow margin for gfx950's extra pass.
 WAIT_STATES = 12
+# the same for 16-pass products (v_mfma_f32_32x32x2_f32): 19, with margin
+WAIT_STATES_16PASS = 20
 
 _AREG = re.compile(r"\ba(\d+)\b|\ba\[(\d+):(\d+)\]")
 _MFMA_DST = re.compile(r"^\s*v_mfma\w*\s+a\[(\d+):(\d+)\],\s*(\S+),\s*(\S+),\s*a\[(\d+):(\d+)\]")
@@ -44,8 +46,10 @@ def _wait_states(line):
     return 1
 
 
-def check(lines):
-    """Returns a list of (line number, message) violations."""
+def check(lines, wait_states=WAIT_STATES):
+    """Returns a list of (line number, message) violations; `wait_states` is
+    the distance an asm product's destination must be left alone (12 for the
+    8-pass bf16 products, more for the 16-pass fp32 ones)."""
     bad = []
     in_asm = False
     pending = []   # [dst register set, remaining wait states, line number]
@@ -72,14 +76,14 @@ def check(lines):
                 if regs & (dst | src_c) and not (regs == dst and dst == src_c):
                     bad.append((no, f"asm MFMA partially overlaps the product of line {at}"))
             pending = [p for p in pending if not (p[0] == dst)]
-            pending.append([dst, WAIT_STATES, no])
+            pending.append([dst, wait_states, no])
             # the product's own issue does not count toward later wait states
             continue
         used = _aregs(code)
         for regs, _left, at in pending:
             if regs & used:
                 bad.append((no, f"'{code}' touches the destination of the asm MFMA at line {at} "
-                                f"within {WAIT_STATES} wait states"))
+                                f"within {wait_states} wait states"))
         ws = _wait_states(code)
         for p in pending:
             p[1] -= ws

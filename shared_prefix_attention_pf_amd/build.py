@@ -41,26 +41,32 @@ def common_flags():
 
 
 def check_wait_states(cc: str, tmp: str, verbose: bool = False) -> None:
-    """Generate the gfx950 assembly of the bf16 kernels and check that no
-    instruction touches an inline-asm MFMA's destination within its latency
-    (see asm_check.py).  Raises on a violation."""
+    """Generate the gfx950 assembly of the bf16 and fp32 attention kernels and
+    check that no instruction touches an inline-asm MFMA's destination within
+    its latency (see asm_check.py), and that nothing spills to scratch.
+    Raises on a violation."""
     sys.path.insert(0, PKG)
     import asm_check  # noqa: E402  (module beside this file)
-    src = os.path.join(CSRC, "pf_attn_bf16.hip")
-    asm = os.path.join(tmp, "pf_attn_bf16.s")
-    cmd = [cc] + common_flags() + ["--cuda-device-only", "-S", src, "-o", asm]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    with open(asm) as fh:
-        lines = fh.readlines()
-    bad = asm_check.check(lines)
-    bad += asm_check.check_no_stack(lines)
-    bad += asm_check.check_m0(lines)
-    if bad:
-        for no, msg in bad[:20]:
-            print(f"pf_attn_bf16.s:{no}: {msg}", file=sys.stderr)
-        raise RuntimeError(f"{len(bad)} MFMA wait-state violation(s) in the bf16 kernels")
+    for name, wait_states, own_m0 in (("pf_attn_bf16", asm_check.WAIT_STATES, True),
+                                      ("pf_attn_f32", asm_check.WAIT_STATES_16PASS, False)):
+        src = os.path.join(CSRC, name + ".hip")
+        asm = os.path.join(tmp, name + ".s")
+        cmd = [cc] + common_flags() + ["--cuda-device-only", "-S", src, "-o", asm]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        with open(asm) as fh:
+            lines = fh.readlines()
+        bad = asm_check.check(lines, wait_states)
+        bad += asm_check.check_no_stack(lines)
+        # the bf16 kernels set M0 in their own staging asm; the fp32 kernels
+        # stage through builtins, for which the compiler sets M0 itself
+        if own_m0:
+            bad += asm_check.check_m0(lines)
+        if bad:
+            for no, msg in bad[:20]:
+                print(f"{name}.s:{no}: {msg}", file=sys.stderr)
+            raise RuntimeError(f"{len(bad)} MFMA wait-state violation(s) in {name}.hip")
 
 
 def build(verbose: bool = False, resource_usage: bool = False) -> str:
