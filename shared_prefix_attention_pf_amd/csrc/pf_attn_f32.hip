@@ -38,12 +38,19 @@ using Rsrc = __amdgpu_buffer_rsrc_t;
 
 constexpr int kWaves = 4;                 // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
-constexpr int kDkvKeys = 32 * kWaves;     // keys per KV-stationary workgroup
+constexpr int kDkvKeys = 16 * kWaves;     // keys per KV-stationary workgroup
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kLn2 = 0.69314718055994530942f;
 
 __device__ __forceinline__ f32x16 mm(float a, float b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// 16x16x4 product: lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16];
+// C register r holds C[4 (l / 16) + r][l % 16].  Same rate as the 32x32x2
+// form (32 cycles for half the work), on tiles a quarter the size.
+__device__ __forceinline__ f32x4 mm16(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
 __host__ __device__ constexpr int crow(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
@@ -396,19 +403,25 @@ __global__ __launch_bounds__(kThreads, 1) void dq_f32_kernel(AttnArgs a) {
     }
 }
 
-// KV-stationary: a workgroup holds 128 keys of KV head y, 32 per wave, and
+// KV-stationary: a workgroup holds 64 keys of KV head y, 16 per wave, and
 // walks the (32-token tile, query head) steps whose rows may see them: all
 // rows for external keys, rows from the block's first key to the largest
 // visibility end of its keys for own keys.  A block's steps may be split into
 // query chunks (a.n_chunks external, a.n_chunks_own own), one workgroup each;
 // item x is (external block, chunk) pairs first, then (own block, chunk).
+// The products are 16x16x4: a wave's 16 keys are the columns of its S and dP
+// tiles (two 16-query halves of the step), so the lane holding P or dS of
+// (query, key) supplies it as the B operand of dV^T += dO^T P and
+// dK^T += Q^T dS; contraction step (half, r) of lane group g takes query
+// 16 half + 4 g + r.  Everything stays in VGPRs (about 200 at head_dim 128),
+// two workgroups per CU: two waves per SIMD cover each other's waits.
 template <int D>
-__global__ __launch_bounds__(kThreads, 1) void dkv_f32_kernel(AttnArgs a) {
-  constexpr int H = D / 2, NT = D / 32, RS = Tile<D>::kRs;
+__global__ __launch_bounds__(kThreads, 2) void dkv_f32_kernel(AttnArgs a) {
+  constexpr int Q4 = D / 4, NTD = D / 16, RS = Tile<D>::kRs;
   __shared__ __attribute__((aligned(16))) float qd_s[2][2][Tile<D>::kFloats];   // [buffer][Q, dO]
   __shared__ __attribute__((aligned(16))) float ld_s[2][2][64];       // [buffer][LSE, D]
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63, col = lane & 31, h = lane >> 5;
+  const int lane = threadIdx.x & 63, j16 = lane & 15, g4 = lane >> 4;
   const int g = blockIdx.y;
   const int n_ext_b = (a.n_ext + kDkvKeys - 1) / kDkvKeys;
   const int n_ext_items = n_ext_b * a.n_chunks;
@@ -417,21 +430,24 @@ __global__ __launch_bounds__(kThreads, 1) void dkv_f32_kernel(AttnArgs a) {
   const int item = ext ? (int)blockIdx.x : (int)blockIdx.x - n_ext_items;
   const int chunk = item % nch;
   const int k0 = (item / nch) * kDkvKeys;
-  const int kw0 = k0 + 32 * wave;
-  const int kk = kw0 + col;
+  const int kw0 = k0 + 16 * wave;
+  const int kk = kw0 + j16;
   const int klim = ext ? a.n_ext : a.rows;
   const bool kvalid = kk < klim;
 
-  // the lane's halves of its K and V rows: B operands of S = Q K^T, dP = dO V^T
-  float kr[H], vr[H];
+  // the lane's quarter of its K and V rows (head_dim Q4 g .. Q4 g + Q4 - 1):
+  // B operands of S = Q K^T and dP = dO V^T
+  float kr[Q4], vr[Q4];
   {
     const int64_t kst = ext ? a.kx_st : a.ko_st, ksh = ext ? a.kx_sh : a.ko_sh;
     const int64_t vst = ext ? a.vx_st : a.vo_st, vsh = ext ? a.vx_sh : a.vo_sh;
     const int64_t r = kvalid ? kk : 0;
-    const float* kp = (const float*)(ext ? a.k_ext : a.k_own) + r * kst + (int64_t)g * ksh + H * h;
-    const float* vp = (const float*)(ext ? a.v_ext : a.v_own) + r * vst + (int64_t)g * vsh + H * h;
+    const float* kp =
+        (const float*)(ext ? a.k_ext : a.k_own) + r * kst + (int64_t)g * ksh + Q4 * g4;
+    const float* vp =
+        (const float*)(ext ? a.v_ext : a.v_own) + r * vst + (int64_t)g * vsh + Q4 * g4;
 #pragma unroll
-    for (int u = 0; u < H / 4; ++u) {
+    for (int u = 0; u < Q4 / 4; ++u) {
       f32x4 kv = {0.f, 0.f, 0.f, 0.f}, vv = kv;
       if (kvalid) {
         kv = *(const f32x4*)(kp + 4 * u);
@@ -443,21 +459,18 @@ __global__ __launch_bounds__(kThreads, 1) void dkv_f32_kernel(AttnArgs a) {
         vr[4 * u + e] = vv[e];
       }
     }
-#pragma unroll
-    for (int s = 0; s < H; ++s) {
-      pin_agpr(kr[s]);
-      pin_agpr(vr[s]);
-    }
   }
   const int kend_k = (!ext && kvalid) ? a.ri.kend[kk] : -1;
-  // rows that may see the wave's keys end before wave_hi (own keys)
+  // rows that may see the wave's keys end before wave_hi (own keys; the
+  // largest visibility end over the 32-key block holding them)
   const int wave_hi = (!ext && kw0 < a.rows) ? a.ri.bmax[kw0 / 32] : 0;
 
   int qlo = 0, qhi = a.rows;
   if (!ext) {
     qlo = k0;
     int mx = -1;
-    for (int b = k0 / 32; b < k0 / 32 + kWaves && b * 32 < a.rows; ++b) mx = max(mx, a.ri.bmax[b]);
+    for (int b = k0 / 32; b < (k0 + kDkvKeys) / 32 && b * 32 < a.rows; ++b)
+      mx = max(mx, a.ri.bmax[b]);
     qhi = min(mx, a.rows);
   }
   const int qt_lo = qlo / 32;
@@ -484,11 +497,11 @@ __global__ __launch_bounds__(kThreads, 1) void dkv_f32_kernel(AttnArgs a) {
       dma_vec(make_rsrc(a.dsum + (int64_t)head * a.rows + t0, 4LL * valid), ld_s[b][1], lane);
   };
 
-  f32x16 dk[NT], dv[NT];
+  f32x4 dk[NTD], dv[NTD];   // dK^T, dV^T: register r is head_dim 16 dt + 4 g + r
 #pragma unroll
-  for (int dt = 0; dt < NT; ++dt) {
-    dk[dt] = zero16();
-    dv[dt] = zero16();
+  for (int dt = 0; dt < NTD; ++dt) {
+    dk[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    dv[dt] = dk[dt];
   }
   const float c = a.scale_log2;
   // the dS buffer (fp32): 32 x 32 tiles [query head][query step][key tile],
@@ -507,58 +520,76 @@ __global__ __launch_bounds__(kThreads, 1) void dkv_f32_kernel(AttnArgs a) {
     if (!ext && (t0 + 31 < kw0 || t0 >= wave_hi)) continue;
     const float* qs = qd_s[b][0];
     const float* ds = qd_s[b][1];
-    f32x16 s = zero16(), dp = zero16();
+    // S and dP of the two 16-query halves, four independent chains
+    f32x4 s[2], dp[2];
 #pragma unroll
-    for (int u = 0; u < H / 4; ++u) {
-      const f32x4 qv = *(const f32x4*)(qs + col * RS + H * h + 4 * u);
-      const f32x4 dv4 = *(const f32x4*)(ds + col * RS + H * h + 4 * u);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        s = mm(qv[e], kr[4 * u + e], s);
-        dp = mm(dv4[e], vr[4 * u + e], dp);
-      }
+    for (int hf = 0; hf < 2; ++hf) {
+      s[hf] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dp[hf] = s[hf];
     }
-    // register r: query row t0 + crow(r, h) against the lane's key; P in s,
-    // dS in dp
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const f32x4 lv = *(const f32x4*)(ld_s[b][0] + 8 * q4 + 4 * h);
-      const f32x4 dsv = *(const f32x4*)(ld_s[b][1] + 8 * q4 + 4 * h);
+    for (int u = 0; u < Q4 / 4; ++u) {
+      f32x4 qv[2], dv4[2];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * q4 + e, tq = t0 + crow(r, h);
+      for (int hf = 0; hf < 2; ++hf) {
+        qv[hf] = *(const f32x4*)(qs + (16 * hf + j16) * RS + Q4 * g4 + 4 * u);
+        dv4[hf] = *(const f32x4*)(ds + (16 * hf + j16) * RS + Q4 * g4 + 4 * u);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          s[hf] = mm16(qv[hf][e], kr[4 * u + e], s[hf]);
+          dp[hf] = mm16(dv4[hf][e], vr[4 * u + e], dp[hf]);
+        }
+    }
+    // register (hf, r): query row t0 + 16 hf + 4 g + r against the lane's
+    // key; P in s, dS in dp
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const f32x4 lv = *(const f32x4*)(ld_s[b][0] + 16 * hf + 4 * g4);
+      const f32x4 dsv = *(const f32x4*)(ld_s[b][1] + 16 * hf + 4 * g4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tq = t0 + 16 * hf + 4 * g4 + r;
         const bool vis = tq < a.rows && kvalid && (ext || (kk <= tq && tq < kend_k));
         // a visible row sees at least this key, so its LSE is finite
-        const float p = vis ? exp2_(s[r] * c - lv[e] * kLog2e) : 0.f;
-        s[r] = p;
-        dp[r] = p * (dp[r] - dsv[e]);
+        const float p = vis ? exp2_(s[hf][r] * c - lv[r] * kLog2e) : 0.f;
+        s[hf][r] = p;
+        dp[hf][r] = p * (dp[hf][r] - dsv[r]);
       }
     }
     if (dsb) {
-      // this wave's dS tile of the step for the dQ pass: rows are the step's
-      // queries, columns the wave's keys (a streaming store, read once later)
+      // this wave's 16 columns of the step's dS tile for the dQ pass: rows are
+      // the step's queries, columns the tile's 32 keys (streaming stores, read
+      // once later)
       const int head = a.ri.qhead[g * a.group + it % a.group];
-      float* tile = dsb + ((int64_t)(head * ds_qt + t0 / 32) * ds_kt + ds_k0 + kw0 / 32) * 1024;
+      float* tile = dsb + ((int64_t)(head * ds_qt + t0 / 32) * ds_kt + ds_k0 + kw0 / 32) * 1024 +
+                    (kw0 & 31) + j16;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) __builtin_nontemporal_store(dp[r], tile + crow(r, h) * 32 + col);
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          __builtin_nontemporal_store(dp[hf][r], tile + (16 * hf + 4 * g4 + r) * 32);
     }
 #pragma unroll
-    for (int dt = 0; dt < NT; ++dt)
+    for (int dt = 0; dt < NTD; ++dt)
 #pragma unroll
-      for (int s2 = 0; s2 < 16; ++s2) {
-        const int at = crow(s2, h) * RS + 32 * dt + col;
-        dv[dt] = mm(ds[at], s[s2], dv[dt]);
-        dk[dt] = mm(qs[at], dp[s2], dk[dt]);
-      }
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int at = (16 * hf + 4 * g4 + r) * RS + 16 * dt + j16;
+          dv[dt] = mm16(ds[at], s[hf][r], dv[dt]);
+          dk[dt] = mm16(qs[at], dp[hf][r], dk[dt]);
+        }
   }
 
   if (!kvalid) return;
-  // dK^T / dV^T register r: head_dim index 32 dt + crow(r, h) of the lane's
-  // key.  Destination: 0 add into gK/gV (an unsplit external block, or the
-  // first chunk of a split one: no other workgroup touches those elements in
-  // the launch), 1 external partial plane chunk - 1, 2 own partial plane
-  // chunk, 3 own output (+ gk_init / gv_init).  The finishing pass adds the
-  // planes in a fixed order, so every result is the same run to run.
+  // Destination: 0 add into gK/gV (an unsplit external block, or the first
+  // chunk of a split one: no other workgroup touches those elements in the
+  // launch), 1 external partial plane chunk - 1, 2 own partial plane chunk,
+  // 3 own output (+ gk_init / gv_init).  The finishing pass adds the planes
+  // in a fixed order, so every result is the same run to run.
   const int mode = ext ? (chunk == 0 ? 0 : 1) : (nch > 1 ? 2 : 3);
   const int64_t base = ((int64_t)kk * a.hkv + g) * D;
   float* pk = nullptr;
@@ -579,26 +610,19 @@ __global__ __launch_bounds__(kThreads, 1) void dkv_f32_kernel(AttnArgs a) {
     pv = (float*)a.dv_own + (int64_t)kk * a.dvo_st + (int64_t)g * a.dvo_sh;
   }
 #pragma unroll
-  for (int dt = 0; dt < NT; ++dt)
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int d0 = 32 * dt + 8 * q4 + 4 * h;
-      f32x4 xk, xv;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        xk[e] = dk[dt][4 * q4 + e] * a.scale;
-        xv[e] = dv[dt][4 * q4 + e];
-      }
-      if (mode == 0) {
-        xk += *(const f32x4*)(pk + d0);
-        xv += *(const f32x4*)(pv + d0);
-      } else if (mode == 3 && a.gk_init) {
-        xk += *(const f32x4*)(a.gk_init + base + d0);
-        xv += *(const f32x4*)(a.gv_init + base + d0);
-      }
-      *(f32x4*)(pk + d0) = xk;
-      *(f32x4*)(pv + d0) = xv;
+  for (int dt = 0; dt < NTD; ++dt) {
+    const int d0 = 16 * dt + 4 * g4;
+    f32x4 xk = dk[dt] * a.scale, xv = dv[dt];
+    if (mode == 0) {
+      xk += *(const f32x4*)(pk + d0);
+      xv += *(const f32x4*)(pv + d0);
+    } else if (mode == 3 && a.gk_init) {
+      xk += *(const f32x4*)(a.gk_init + base + d0);
+      xv += *(const f32x4*)(a.gv_init + base + d0);
     }
+    *(f32x4*)(pk + d0) = xk;
+    *(f32x4*)(pv + d0) = xv;
+  }
 }
 
 // K tile i of a Q-stationary workgroup into LDS
