@@ -118,9 +118,9 @@ __device__ __forceinline__ void dma_vec(Rsrc r, void* dst, int lane) {
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // The Q-stationary kernels' share of the work: workgroup x of KV head g holds
-// the (32-token tile, query head) pairs 4 x .. 4 x + 3 of that KV head, one per
-// wave, pairs ordered tile-major; the tiles of keys it walks are the external
-// ones, then the own ones that some of its rows may see.
+// four consecutive (32-token tile, query head) pairs of that KV head, one per
+// wave, pairs ordered tile-major and taken from the last; the tiles of keys it
+// walks are the external ones, then the own ones that some of its rows may see.
 struct QTiles {
   int g, head, t0, tok;
   bool active, tvalid;
@@ -129,9 +129,14 @@ struct QTiles {
   int n_ext_t, n_t;          // external tiles; all tiles (external, then own)
 
   __device__ QTiles(const AttnArgs& a, int wave, int col) {
-    g = blockIdx.y;
+    // block x: KV head x % Hkv, rank x / Hkv; rank 0 holds the last pairs of
+    // its head.  Later tokens see more keys (causal prefix, trees) and
+    // workgroups start in index order, so this is a longest-first schedule
+    // over all heads; with 8 KV heads each head's workgroups share one XCD.
+    g = (int)blockIdx.x % a.hkv;
+    const int rank = (int)blockIdx.x / a.hkv;
     const int n_pairs = ((a.rows + 31) / 32) * a.group;
-    const int p0 = blockIdx.x * kWaves;
+    const int p0 = ((n_pairs + kWaves - 1) / kWaves - 1 - rank) * kWaves;
     const int p = p0 + wave;
     active = p < n_pairs;
     const int j = active ? p % a.group : 0;
@@ -422,12 +427,15 @@ __global__ __launch_bounds__(kThreads, 2) void dkv_f32_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) float ld_s[2][2][64];       // [buffer][LSE, D]
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, j16 = lane & 15, g4 = lane >> 4;
-  const int g = blockIdx.y;
+  // block x: KV head x % Hkv, item x / Hkv (the heads interleaved: external
+  // items, the longest, start first on every head)
+  const int g = (int)blockIdx.x % a.hkv;
+  const int bx = (int)blockIdx.x / a.hkv;
   const int n_ext_b = (a.n_ext + kDkvKeys - 1) / kDkvKeys;
   const int n_ext_items = n_ext_b * a.n_chunks;
-  const bool ext = (int)blockIdx.x < n_ext_items;
+  const bool ext = bx < n_ext_items;
   const int nch = ext ? a.n_chunks : a.n_chunks_own;
-  const int item = ext ? (int)blockIdx.x : (int)blockIdx.x - n_ext_items;
+  const int item = ext ? bx : bx - n_ext_items;
   const int chunk = item % nch;
   const int k0 = (item / nch) * kDkvKeys;
   const int kw0 = k0 + 16 * wave;
@@ -705,10 +713,11 @@ __global__ __launch_bounds__(kThreads, 2) void dq_ds_f32_kernel(AttnArgs a) {
     }
 }
 
-// Q-stationary grid: per KV head, one workgroup per 4 (tile, query head) pairs
+// Q-stationary grid: per KV head, one workgroup per 4 (tile, query head) pairs,
+// the heads interleaved (see QTiles)
 dim3 q_grid(const AttnArgs& a) {
   const int pairs = ((a.rows + 31) / 32) * a.group;
-  return dim3((pairs + kWaves - 1) / kWaves, a.hkv);
+  return dim3((unsigned)(((pairs + kWaves - 1) / kWaves) * a.hkv));
 }
 
 }  // namespace
@@ -756,7 +765,7 @@ hipError_t launch_bwd_dkv_f32(const AttnArgs& a, int32_t head_dim, hipStream_t s
   const int blocks = (a.n_ext + kDkvKeys - 1) / kDkvKeys * a.n_chunks +
                      (a.rows + kDkvKeys - 1) / kDkvKeys * a.n_chunks_own;
   if (blocks <= 0) return hipSuccess;
-  dim3 grid(blocks, a.hkv);
+  dim3 grid((unsigned)(blocks * a.hkv));
   if (head_dim == 64)
     PF_LAUNCH("pf_bwd_dkv_f32", dkv_f32_kernel<64>, grid, dim3(kThreads), stream, a);
   else if (head_dim == 128)
