@@ -128,13 +128,14 @@ struct QTiles {
   int tmin;                  // first token of the workgroup
   int n_ext_t, n_t;          // external tiles; all tiles (external, then own)
 
-  __device__ QTiles(const AttnArgs& a, int wave, int col) {
-    // block x: KV head x % Hkv, rank x / Hkv; rank 0 holds the last pairs of
-    // its head.  Later tokens see more keys (causal prefix, trees) and
-    // workgroups start in index order, so this is a longest-first schedule
-    // over all heads; with 8 KV heads each head's workgroups share one XCD.
-    g = (int)blockIdx.x % a.hkv;
-    const int rank = (int)blockIdx.x / a.hkv;
+  // block x: KV head x % Hkv, rank x / Hkv; rank 0 holds the last pairs of
+  // its head.  Later tokens see more keys (causal prefix, trees) and
+  // workgroups start in index order, so this is a longest-first schedule over
+  // all heads; with 8 KV heads each head's workgroups share one XCD.  With
+  // head_major (a 2-D grid, y the KV head) the heads go one after another.
+  __device__ QTiles(const AttnArgs& a, int wave, int col, bool head_major = false) {
+    g = head_major ? (int)blockIdx.y : (int)blockIdx.x % a.hkv;
+    const int rank = head_major ? (int)blockIdx.x : (int)blockIdx.x / a.hkv;
     const int n_pairs = ((a.rows + 31) / 32) * a.group;
     const int p0 = ((n_pairs + kWaves - 1) / kWaves - 1 - rank) * kWaves;
     const int p = p0 + wave;
@@ -657,7 +658,7 @@ __global__ __launch_bounds__(kThreads, 2) void dq_ds_f32_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) float k_s[2][Tile<D>::kFloats];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, col = lane & 31, h = lane >> 5;
-  const QTiles w(a, wave, col);
+  const QTiles w(a, wave, col, a.n_ext > 0);
   const float* const dsb = (const float*)a.ds_ext;
   const int64_t row_tiles = (int64_t)(w.head * (a.ds_rows / 32) + w.t0 / 32) * (a.ds_keys / 32);
   auto load_ds = [&](int i, f32x4 (&dst)[4]) {
@@ -720,6 +721,11 @@ dim3 q_grid(const AttnArgs& a) {
   return dim3((unsigned)(((pairs + kWaves - 1) / kWaves) * a.hkv));
 }
 
+dim3 q_grid_head_major(const AttnArgs& a) {
+  const int pairs = ((a.rows + 31) / 32) * a.group;
+  return dim3((pairs + kWaves - 1) / kWaves, a.hkv);
+}
+
 }  // namespace
 
 hipError_t launch_fwd_f32(const AttnArgs& a, int32_t head_dim, hipStream_t stream) {
@@ -747,10 +753,14 @@ hipError_t launch_bwd_dq_f32(const AttnArgs& a, int32_t head_dim, hipStream_t st
 hipError_t launch_bwd_dq_ds_f32(const AttnArgs& a, const PartialSums& ps, int32_t head_dim,
                                 hipStream_t stream) {
   if (a.rows > 0) {
+    // measured at the config-2 shape in fp32: with external keys (Phase B)
+    // the heads one after another read the dS stream faster (1.25 against
+    // 1.45 ms); without (Phase C) one head per XCD does (0.76 against 1.02)
+    const dim3 grid = a.n_ext > 0 ? q_grid_head_major(a) : q_grid(a);
     if (head_dim == 64)
-      PF_LAUNCH("pf_bwd_dq_ds_f32", dq_ds_f32_kernel<64>, q_grid(a), dim3(kThreads), stream, a);
+      PF_LAUNCH("pf_bwd_dq_ds_f32", dq_ds_f32_kernel<64>, grid, dim3(kThreads), stream, a);
     else if (head_dim == 128)
-      PF_LAUNCH("pf_bwd_dq_ds_f32", dq_ds_f32_kernel<128>, q_grid(a), dim3(kThreads), stream, a);
+      PF_LAUNCH("pf_bwd_dq_ds_f32", dq_ds_f32_kernel<128>, grid, dim3(kThreads), stream, a);
     else
       return hipErrorInvalidValue;
     const hipError_t e = hipGetLastError();
