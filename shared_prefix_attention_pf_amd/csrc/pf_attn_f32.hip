@@ -180,8 +180,10 @@ __device__ __forceinline__ void stage_kv(const AttnArgs& a, const QTiles& w, int
   const int valid = (ext ? a.n_ext : a.rows) - k0;
   const int64_t kst = ext ? a.kx_st : a.ko_st, ksh = ext ? a.kx_sh : a.ko_sh;
   const int64_t vst = ext ? a.vx_st : a.vo_st, vsh = ext ? a.vx_sh : a.vo_sh;
-  const float* kb = (const float*)(ext ? a.k_ext : a.k_own) + (int64_t)k0 * kst + (int64_t)w.g * ksh;
-  const float* vb = (const float*)(ext ? a.v_ext : a.v_own) + (int64_t)k0 * vst + (int64_t)w.g * vsh;
+  const float* kb =
+      (const float*)(ext ? a.k_ext : a.k_own) + (int64_t)k0 * kst + (int64_t)w.g * ksh;
+  const float* vb =
+      (const float*)(ext ? a.v_ext : a.v_own) + (int64_t)k0 * vst + (int64_t)w.g * vsh;
   dma_tile<D>(rows_rsrc<D>(kb, valid, kst), k_s, 4u * (uint32_t)kst, wave, lane);
   dma_tile<D>(rows_rsrc<D>(vb, valid, vst), v_s, 4u * (uint32_t)vst, wave, lane);
   if (!ext && wave == kWaves - 1) dma_vec(make_rsrc(a.ri.kend + k0, 4LL * valid), kend_s, lane);
@@ -280,7 +282,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_f32_kernel(AttnArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
 #pragma unroll
-        for (int s2 = 0; s2 < 16; ++s2) o[dt] = mm(vs[crow(s2, h) * RS + 32 * dt + col], x[s2], o[dt]);
+        for (int s2 = 0; s2 < 16; ++s2)
+          o[dt] = mm(vs[crow(s2, h) * RS + 32 * dt + col], x[s2], o[dt]);
       }
     }
     cur = nxt;
@@ -642,7 +645,8 @@ __device__ __forceinline__ void stage_k(const AttnArgs& a, const QTiles& w, int 
   const int k0 = w.key0(i);
   const int valid = (ext ? a.n_ext : a.rows) - k0;
   const int64_t kst = ext ? a.kx_st : a.ko_st, ksh = ext ? a.kx_sh : a.ko_sh;
-  const float* kb = (const float*)(ext ? a.k_ext : a.k_own) + (int64_t)k0 * kst + (int64_t)w.g * ksh;
+  const float* kb =
+      (const float*)(ext ? a.k_ext : a.k_own) + (int64_t)k0 * kst + (int64_t)w.g * ksh;
   dma_tile<D>(rows_rsrc<D>(kb, valid, kst), k_s, 4u * (uint32_t)kst, wave, lane);
 }
 
