@@ -200,6 +200,13 @@ def test_tree(seed, hq, hkv, dtype):
     _tree_case(seed, hq, hkv, dtype, 9, 90)
 
 
+def test_tree_f32_many_tiles():
+    """An fp32 tree of about 1500 rows with GQA 8/2 at head_dim 128: many
+    key and query tiles under the tree mask, own key blocks split into query
+    chunks, and the dS buffer."""
+    _tree_case(5, 8, 2, "f32", 24, 120, d=128)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_maximum_sizes(dtype):
     """The limits the boundary accepts: PF_MAX_SEGMENTS suffixes in one call
@@ -216,9 +223,10 @@ def test_maximum_sizes(dtype):
         _prefix_case((pf.PF_MAX_HEADS, hkv, d, dtype, 45, True))
 
 
-def _tree_case(seed, hq, hkv, dtype, n_nodes, max_len):
+def _tree_case(seed, hq, hkv, dtype, n_nodes, max_len, d=None):
     """Tree forward and backward of a random tree against the oracle."""
-    d = 128 if dtype == "bf16" else 64
+    if d is None:
+        d = 128 if dtype == "bf16" else 64
     node_off, parent = random_tree(seed, n_nodes, max_len=max_len, min_len=0)
     if n_nodes <= 16:
         print(f"\ntree seed {seed}: node_off {node_off.tolist()} parent {parent.tolist()}",
