@@ -1,8 +1,10 @@
 // fp32 attention kernels (head_dim 64 or 128) on the matrix cores: every
-// product is v_mfma_f32_32x32x2_f32 with fp32 inputs and fp32 accumulation,
-// so fp32 groups are never rounded to bf16.  The three kernels compute what
-// the bf16 family computes (forward; dQ with D = rowsum(dO o O); dK/dV, with
-// the external keys' gradients added into the fp32 accumulators).
+// product is an fp32 MFMA with fp32 inputs and fp32 accumulation
+// (v_mfma_f32_32x32x2_f32 in the forward and dQ kernels, v_mfma_f32_16x16x4_f32
+// in dK/dV), so fp32 groups are never rounded to bf16.  The kernels compute
+// what the bf16 family computes (forward; dQ with D = rowsum(dO o O), from a
+// stored dS or recomputing S and dP; dK/dV, with the external keys' gradients
+// added into the fp32 accumulators).
 //
 // Layout of one 32x32x2 product for lane l (half h = l / 32, column l % 32):
 //   A operand: lane l supplies A[l % 32][h]; B operand: B[h][l % 32];
@@ -17,7 +19,8 @@
 // Forward and dQ are Q-stationary and form S^T = K Q^T: one query per lane
 // column, so its LSE and D are one value per lane.  dK/dV is KV-stationary
 // and forms S = Q K^T: one key per lane column, whose P and dS then feed
-// dV^T += dO^T P and dK^T += Q^T dS.
+// dV^T += dO^T P and dK^T += Q^T dS (the same ordering on 16x16 tiles; see
+// dkv_f32_kernel).
 // K/V (or Q/dO) tiles of 32 rows reach LDS through buffer-to-LDS loads,
 // double buffered, with rows padded to D + 4 floats: the row-sliced reads
 // (16 bytes of 32 rows) and the column-sliced ones (32 floats of a row) then
