@@ -498,8 +498,12 @@ void launch_hook(const char* kernel, hipStream_t stream, int end) {
   if (h) h(kernel, (void*)stream, end, g_hook_user);
 }
 
+// Workgroups of the KV-stationary backward that run at once on the chip: one
+// per CU for the bf16 kernel (its LDS), two for the fp32 one.
+int64_t dkv_slots(int32_t dtype) { return dtype == PF_BF16 ? 256 : 512; }
+
 // External key blocks are split into query chunks until there is about one
-// workgroup per CU (256) while each chunk keeps at least 32 query steps of 32
+// workgroup per slot while each chunk keeps at least 32 query steps of 32
 // rows; the own key blocks (and any second round) fill in behind them in
 // longest-first order.  Fewer chunks means fewer fp32 partials to write and
 // reduce.
@@ -511,7 +515,7 @@ int32_t ext_chunks(int32_t n_ext, int32_t rows, int32_t hq, int32_t hkv, int32_t
   const int64_t wgs = (int64_t)((n_ext + kb - 1) / kb) * hkv;
   const int64_t steps = (int64_t)((rows + 31) / 32) * (hq / hkv);
   int32_t nc = 1;
-  while (nc < 8 && wgs * nc < 256 && steps / (2 * nc) >= 32) nc *= 2;
+  while (nc < 8 && wgs * nc < dkv_slots(dtype) && steps / (2 * nc) >= 32) nc *= 2;
   return nc;
 }
 
@@ -531,7 +535,7 @@ int32_t own_chunks(int32_t op, int32_t n_ext, int32_t rows, int32_t hq, int32_t 
   const int64_t wgs = (int64_t)((rows + kb - 1) / kb) * hkv;
   const int64_t steps = (int64_t)((rows / 2 + 31) / 32) * (hq / hkv);
   int32_t nc = 1;
-  while (nc < 8 && wgs * nc < 512 && steps / (2 * nc) >= 32) nc *= 2;
+  while (nc < 8 && wgs * nc < 2 * dkv_slots(dtype) && steps / (2 * nc) >= 32) nc *= 2;
   return nc;
 }
 
