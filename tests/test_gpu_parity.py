@@ -148,6 +148,9 @@ PREFIX_CASES = [
     (4, 2, 128, "f32", 77, False),
     (8, 2, 128, "f32", 300, True),
     (6, 2, 64, "f32", 257, False),
+    # one KV head, eight query heads: the causal prefix's key blocks split into
+    # four query chunks with partial planes
+    (8, 1, 64, "f32", 1100, True),
 ]
 
 
