@@ -62,3 +62,40 @@ def test_ranges_window_pairs_match_the_masks(seed):
     vis = tree_ancestor_mask(node_off, parent)
     w = {"node_off": no_c, "parent": pa_c, "ranges": ranges}
     assert bench.ranges_window_pairs(w) == int(vis[cp:].sum())
+
+
+def test_profiler_names_are_recovered():
+    """rocprofv3 leaves a template over __bf16 mangled; the summaries find the
+    kernel's name in it, and leave demangled names alone."""
+    mangled = ("_ZN2pf16prep_dsum_kernelIDF16bLi128EEEvNS_8SegTableENS_9HeadTableENS_7RowInfo"
+               "ENS_8AttnArgsEi")
+    plain = bench.plain_name(mangled)
+    assert "prep_dsum_kernel" in plain.split("::")
+    assert bench._pick({plain: (5.0, 2)}, "prep_dsum_kernel", whole=True) == (5.0, 2)
+    demangled = "void pf::(anonymous namespace)::fwd_kernel<1>(pf::AttnArgs)"
+    assert bench.plain_name(demangled) == demangled
+    # a whole-identifier match: fwd_kernel is not logprob_fwd_kernel
+    assert bench._pick({"pf::logprob_fwd_kernel(int)": (1.0, 1)}, "fwd_kernel", whole=True) is None
+
+
+def test_stored_figures_are_keyed_to_their_kernel_family(tmp_path, monkeypatch):
+    """A stored counter figure carries a hash of its family's kernel file and
+    the common sources: editing another family's kernel file keeps it, editing
+    its own or a common file does not."""
+    assert bench.config_family(2) == "bf16"
+    assert bench.config_family(9) == "f32"
+    assert bench.config_family(7) == "logprob"
+    csrc = tmp_path / "shared_prefix_attention_pf_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    for name in ("pf_attn_bf16.hip", "pf_attn_f32.hip", "pf_logprob.hip", "pf_api.cpp",
+                 "pf_internal.h"):
+        (csrc / name).write_text(name)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    before = {f: bench.kernel_source_hash(f) for f in ("bf16", "f32", "logprob")}
+    assert len(set(before.values())) == 3
+    (csrc / "pf_attn_f32.hip").write_text("changed")
+    after = {f: bench.kernel_source_hash(f) for f in ("bf16", "f32", "logprob")}
+    assert after["bf16"] == before["bf16"] and after["logprob"] == before["logprob"]
+    assert after["f32"] != before["f32"]
+    (csrc / "pf_api.cpp").write_text("changed")
+    assert all(bench.kernel_source_hash(f) != after[f] for f in after)
