@@ -293,11 +293,11 @@ pf_status pf_tree_suffix_attn_bwd_accum(const pf_attn_desc* desc, int32_t prefix
  * and v_c instead of one prefix block; nothing is gathered or copied.
  *   k_c, v_c [c_rows, Hkv, d]             in  (the producer's compact K/V)
  *   n_ranges <= PF_MAX_SEGMENTS; range_start, range_len host [n_ranges]  in
- *     (inside [0, c_rows); empty ranges are ignored)
+ *     (inside [0, c_rows), pairwise disjoint: PF_ERR_INVALID_ARG otherwise;
+ *     empty ranges are ignored)
  *   (tree and window tensors as for pf_tree_suffix_attn_fwd)
  * Workspace: pf_workspace_size(PF_OP_TREE_SUFFIX_FWD, desc, prefix_len, C)
- * with prefix_len = pf_ranges_cached_keys(n_ranges, range_len).
- * bf16 only (PF_ERR_UNSUPPORTED for fp32).                                  */
+ * with prefix_len = pf_ranges_cached_keys(n_ranges, range_len).          */
 pf_status pf_tree_suffix_attn_fwd_ranges(const pf_attn_desc* desc, int32_t c_rows, pf_tensor k_c,
                                          pf_tensor v_c, int32_t n_ranges,
                                          const int32_t* range_start, const int32_t* range_len,

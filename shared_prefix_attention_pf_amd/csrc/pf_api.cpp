@@ -162,6 +162,12 @@ pf_status check_ranges(int32_t n, const int32_t* start, const int32_t* len, int3
       return fail(PF_ERR_INVALID_ARG, "range %d = [%d, %d + %d) is outside the %d producer rows", i,
                   start[i], start[i], len[i], c_rows);
     if (len[i] == 0) continue;
+    // every cached row is one key: overlapping ranges would also make two
+    // workgroups add into the same gK/gV rows
+    for (int j = 0; j < rt->n; ++j)
+      if (start[i] < rt->start[j] + rt->len[j] && rt->start[j] < start[i] + len[i])
+        return fail(PF_ERR_INVALID_ARG, "range %d = [%d, %d + %d) overlaps an earlier range", i,
+                    start[i], start[i], len[i]);
     const int j = rt->n++;
     rt->start[j] = start[i];
     rt->len[j] = len[i];
@@ -637,8 +643,6 @@ pf_status suffix_fwd_impl(int32_t op, const Desc& d, int32_t prefix_len, pf_tens
                           void* workspace, size_t workspace_bytes, void* stream,
                           const pf::RangeTable* rt = nullptr, int32_t c_rows = 0) {
   pf_status s;
-  if (rt && d.dtype != PF_BF16)
-    return fail(PF_ERR_UNSUPPORTED, "cached row ranges need bf16 (the fp32 kernels read one span)");
   const int32_t x_rows = rt ? c_rows : prefix_len;
   if ((s = check_tensor("k_p", k_p, x_rows, d.hkv, d, d.dtype)) != PF_OK) return s;
   if ((s = check_tensor("v_p", v_p, x_rows, d.hkv, d, d.dtype)) != PF_OK) return s;
@@ -674,8 +678,6 @@ pf_status suffix_bwd_impl(int32_t op, const Desc& d, int32_t prefix_len, pf_tens
                           void* stream, bool use_scratch = false,
                           const pf::RangeTable* rt = nullptr, int32_t c_rows = 0) {
   pf_status s;
-  if (rt && d.dtype != PF_BF16)
-    return fail(PF_ERR_UNSUPPORTED, "cached row ranges need bf16 (the fp32 kernels read one span)");
   const int32_t x_rows = rt ? c_rows : prefix_len;
   if ((s = check_tensor("k_p", k_p, x_rows, d.hkv, d, d.dtype)) != PF_OK) return s;
   if ((s = check_tensor("v_p", v_p, x_rows, d.hkv, d, d.dtype)) != PF_OK) return s;

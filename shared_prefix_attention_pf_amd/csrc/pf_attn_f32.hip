@@ -173,36 +173,56 @@ struct QTiles {
   __device__ int key0(int i) const { return (i < n_ext_t ? i : i - n_ext_t) * 32; }
 };
 
+// External key tile t (32 keys): the row of its first key in k_ext / v_ext
+// (and in gK/gV) and how many of its keys are real.  With a tile table the
+// external keys are row ranges of a larger tensor, each padded to whole tiles;
+// without one they are rows 0 .. n_ext - 1.  t is uniform over the wave.
+__device__ __forceinline__ int2 ext_tile(const AttnArgs& a, int t) {
+  if (a.ext_tiles) return a.ext_tiles[t];
+  return int2{32 * t, min(32, a.n_ext - 32 * t)};
+}
+
+// Key tile i of a Q-stationary workgroup: the row of its first key in its
+// tensor and how many of its keys are real
+__device__ __forceinline__ int2 key_tile(const AttnArgs& a, const QTiles& w, int i) {
+  if (i < w.n_ext_t) return ext_tile(a, i);
+  const int k0 = w.key0(i);
+  return int2{k0, a.rows - k0};
+}
+
 // K/V tile i of a Q-stationary workgroup (and the kend values of own keys)
 // into LDS buffer b
 template <int D>
 __device__ __forceinline__ void stage_kv(const AttnArgs& a, const QTiles& w, int i, float* k_s,
                                          float* v_s, int32_t* kend_s, int wave, int lane) {
   const bool ext = i < w.n_ext_t;
-  const int k0 = w.key0(i);
-  const int valid = (ext ? a.n_ext : a.rows) - k0;
+  const int2 kt = key_tile(a, w, i);
   const int64_t kst = ext ? a.kx_st : a.ko_st, ksh = ext ? a.kx_sh : a.ko_sh;
   const int64_t vst = ext ? a.vx_st : a.vo_st, vsh = ext ? a.vx_sh : a.vo_sh;
   const float* kb =
-      (const float*)(ext ? a.k_ext : a.k_own) + (int64_t)k0 * kst + (int64_t)w.g * ksh;
+      (const float*)(ext ? a.k_ext : a.k_own) + (int64_t)kt.x * kst + (int64_t)w.g * ksh;
   const float* vb =
-      (const float*)(ext ? a.v_ext : a.v_own) + (int64_t)k0 * vst + (int64_t)w.g * vsh;
-  dma_tile<D>(rows_rsrc<D>(kb, valid, kst), k_s, 4u * (uint32_t)kst, wave, lane);
-  dma_tile<D>(rows_rsrc<D>(vb, valid, vst), v_s, 4u * (uint32_t)vst, wave, lane);
-  if (!ext && wave == kWaves - 1) dma_vec(make_rsrc(a.ri.kend + k0, 4LL * valid), kend_s, lane);
+      (const float*)(ext ? a.v_ext : a.v_own) + (int64_t)kt.x * vst + (int64_t)w.g * vsh;
+  dma_tile<D>(rows_rsrc<D>(kb, kt.y, kst), k_s, 4u * (uint32_t)kst, wave, lane);
+  dma_tile<D>(rows_rsrc<D>(vb, kt.y, vst), v_s, 4u * (uint32_t)vst, wave, lane);
+  if (!ext && wave == kWaves - 1) dma_vec(make_rsrc(a.ri.kend + kt.x, 4LL * kt.y), kend_s, lane);
 }
 
-// The scores of one K tile against the wave's queries, in log2 units, with the
-// keys the lane's query cannot see at -inf: register r is key k0 + crow(r, h).
+// The scores of key tile i against the wave's queries, in log2 units, with
+// the keys the lane's query cannot see at -inf: register r is the tile's key
+// crow(r, h).
 template <int D>
-__device__ __forceinline__ void visible_scores(const AttnArgs& a, bool ext, int k0, int tok, int h,
+__device__ __forceinline__ void visible_scores(const AttnArgs& a, const QTiles& w, int i, int h,
                                                const f32x16& s, const int32_t* kend_s,
                                                float (&x)[16]) {
   const float c = a.scale_log2;
-  if (ext) {
+  const int tok = w.tok;
+  if (i < w.n_ext_t) {
+    const int n_valid = ext_tile(a, i).y;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) x[r] = (k0 + crow(r, h) < a.n_ext) ? s[r] * c : -INFINITY;
+    for (int r = 0; r < 16; ++r) x[r] = crow(r, h) < n_valid ? s[r] * c : -INFINITY;
   } else {
+    const int k0 = w.key0(i);
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       const i32x4 ke = *(const i32x4*)(kend_s + 8 * q4 + 4 * h);
@@ -264,7 +284,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_f32_kernel(AttnArgs a) {
         for (int e = 0; e < 4; ++e) s = mm(kv[e], q[4 * u + e], s);
       }
       float x[16];
-      visible_scores<D>(a, cur < w.n_ext_t, w.key0(cur), w.tok, h, s, kend_s[b], x);
+      visible_scores<D>(a, w, cur, h, s, kend_s[b], x);
       float mx = x[0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) mx = fmaxf(mx, x[r]);
@@ -386,7 +406,7 @@ __global__ __launch_bounds__(kThreads, 1) void dq_f32_kernel(AttnArgs a) {
         }
       }
       float x[16];
-      visible_scores<D>(a, cur < w.n_ext_t, w.key0(cur), w.tok, h, s, kend_s[b], x);
+      visible_scores<D>(a, w, cur, h, s, kend_s[b], x);
       // dS^T = P^T o (dP^T - D), P^T = 2^(x - LSE2); invisible entries are 0
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -447,8 +467,18 @@ __global__ __launch_bounds__(kThreads, 2) void dkv_f32_kernel(AttnArgs a) {
   const int k0 = (item / nch) * kDkvKeys;
   const int kw0 = k0 + 16 * wave;
   const int kk = kw0 + j16;
-  const int klim = ext ? a.n_ext : a.rows;
-  const bool kvalid = kk < klim;
+  // the lane's key: its row in k/v (and in gK/gV for external keys), and
+  // whether it is real (a wave's 16 keys lie in one 32-key tile)
+  int krow = kk;
+  bool kvalid = kk < a.rows;
+  if (ext) {
+    kvalid = false;
+    if (kw0 < a.n_ext) {   // the last block's second tile may lie past the keys
+      const int2 et = ext_tile(a, kw0 >> 5);
+      krow = et.x + (kk & 31);
+      kvalid = (kk & 31) < et.y;
+    }
+  }
 
   // the lane's quarter of its K and V rows (head_dim Q4 g .. Q4 g + Q4 - 1):
   // B operands of S = Q K^T and dP = dO V^T
@@ -456,7 +486,7 @@ __global__ __launch_bounds__(kThreads, 2) void dkv_f32_kernel(AttnArgs a) {
   {
     const int64_t kst = ext ? a.kx_st : a.ko_st, ksh = ext ? a.kx_sh : a.ko_sh;
     const int64_t vst = ext ? a.vx_st : a.vo_st, vsh = ext ? a.vx_sh : a.vo_sh;
-    const int64_t r = kvalid ? kk : 0;
+    const int64_t r = kvalid ? krow : 0;
     const float* kp =
         (const float*)(ext ? a.k_ext : a.k_own) + r * kst + (int64_t)g * ksh + Q4 * g4;
     const float* vp =
@@ -605,13 +635,16 @@ __global__ __launch_bounds__(kThreads, 2) void dkv_f32_kernel(AttnArgs a) {
   // launch), 1 external partial plane chunk - 1, 2 own partial plane chunk,
   // 3 own output (+ gk_init / gv_init).  The finishing pass adds the planes
   // in a fixed order, so every result is the same run to run.
+  // The partial planes are indexed by the key's position among the external
+  // keys; gK/gV by its row.
   const int mode = ext ? (chunk == 0 ? 0 : 1) : (nch > 1 ? 2 : 3);
   const int64_t base = ((int64_t)kk * a.hkv + g) * D;
   float* pk = nullptr;
   float* pv = nullptr;
   if (mode == 0) {
-    pk = a.gk_acc + base;
-    pv = a.gv_acc + base;
+    const int64_t abase = ((int64_t)krow * a.hkv + g) * D;
+    pk = a.gk_acc + abase;
+    pv = a.gv_acc + abase;
   } else if (mode == 1) {
     const int64_t pb = (int64_t)(chunk - 1) * a.n_ext * a.hkv * D + base;
     pk = a.gk_part + pb;
@@ -645,12 +678,11 @@ template <int D>
 __device__ __forceinline__ void stage_k(const AttnArgs& a, const QTiles& w, int i, float* k_s,
                                         int wave, int lane) {
   const bool ext = i < w.n_ext_t;
-  const int k0 = w.key0(i);
-  const int valid = (ext ? a.n_ext : a.rows) - k0;
+  const int2 kt = key_tile(a, w, i);
   const int64_t kst = ext ? a.kx_st : a.ko_st, ksh = ext ? a.kx_sh : a.ko_sh;
   const float* kb =
-      (const float*)(ext ? a.k_ext : a.k_own) + (int64_t)k0 * kst + (int64_t)w.g * ksh;
-  dma_tile<D>(rows_rsrc<D>(kb, valid, kst), k_s, 4u * (uint32_t)kst, wave, lane);
+      (const float*)(ext ? a.k_ext : a.k_own) + (int64_t)kt.x * kst + (int64_t)w.g * ksh;
+  dma_tile<D>(rows_rsrc<D>(kb, kt.y, kst), k_s, 4u * (uint32_t)kst, wave, lane);
 }
 
 // dQ from the stored dS: Q-stationary like dq_f32_kernel, over the same key

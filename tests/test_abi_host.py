@@ -264,9 +264,11 @@ def test_noalloc_rejects_a_call_beyond_its_scratch():
 
 def test_ranges_entry_points_validate_on_the_host():
     """The windows over producer row ranges reject a range outside the
-    producer, fp32 inputs and a short workspace before any launch; the
-    padded key count that sizes their workspace rounds each range to 32; the
-    injected tree backward needs both accumulators."""
+    producer, overlapping ranges (each cached row is one key, and two
+    workgroups would add into the same gK/gV rows) and a short workspace
+    before any launch, in both dtypes; the padded key count that sizes their
+    workspace rounds each range to 32; the injected tree backward needs both
+    accumulators."""
     assert pf.pf_ranges_cached_keys([100, 0, 32, 1]) == 128 + 0 + 32 + 32
     assert pf.pf_ranges_cached_keys([]) == 0
     p32 = ctypes.POINTER(ctypes.c_int32)
@@ -285,11 +287,16 @@ def test_ranges_entry_points_validate_on_the_host():
     assert call([990], [20]) == pf.PF_ERR_INVALID_ARG
     assert call([-1], [5]) == pf.PF_ERR_INVALID_ARG
     assert call([0], [-5]) == pf.PF_ERR_INVALID_ARG
-    assert call([0, 500], [100, 40], dtype=pf.PF_F32) == pf.PF_ERR_UNSUPPORTED
-    desc = pf.AttnDesc(32, 8, 128)
-    need = pf.pf_workspace_size(pf.PF_OP_TREE_SUFFIX_FWD, desc, pf.pf_ranges_cached_keys([100, 40]),
-                                6)
-    assert call([0, 500], [100, 40], ws_bytes=need - 1) == pf.PF_ERR_WORKSPACE
+    assert call([0, 50], [100, 40]) == pf.PF_ERR_INVALID_ARG          # overlap
+    assert call([100, 0], [40, 101]) == pf.PF_ERR_INVALID_ARG         # overlaps a later start
+    for dtype in (pf.PF_BF16, pf.PF_F32):
+        desc = pf.AttnDesc(32, 8, 128, dtype=dtype)
+        need = pf.pf_workspace_size(pf.PF_OP_TREE_SUFFIX_FWD, desc,
+                                    pf.pf_ranges_cached_keys([100, 40]), 6)
+        assert call([0, 500], [100, 40], dtype=dtype, ws_bytes=need - 1) == pf.PF_ERR_WORKSPACE
+        # adjacent ranges and an empty range inside another are not overlaps
+        assert call([100, 0, 50], [40, 100, 0], dtype=dtype, ws_bytes=need - 1) == \
+            pf.PF_ERR_WORKSPACE
     d, _keep = _desc()
     no = np.asarray([0, 4, 6], dtype=np.int32)
     pa = np.asarray([-1, 0], dtype=np.int32)

@@ -488,8 +488,9 @@ def test_empty_call_is_noop():
     assert o.shape[0] == 0 and torch.all(gk == 3.0)
 
 
-@pytest.mark.parametrize("hq,hkv", [(8, 2), (16, 4)])
-def test_windows_under_producer_nodes(hq, hkv):
+@pytest.mark.parametrize("hq,hkv,dtype,d", [(8, 2, "bf16", 128), (16, 4, "bf16", 128),
+                                            (8, 2, "f32", 128), (4, 1, "f32", 64)])
+def test_windows_under_producer_nodes(hq, hkv, dtype, d):
     """Consumer windows attached under internal nodes of a producer rollout
     tree, each reading the rows of its node and the node's ancestors in place
     (row ranges of the producer's K/V, not 32-aligned), adding its gradients
@@ -498,7 +499,6 @@ def test_windows_under_producer_nodes(hq, hkv):
     window attention, scatter-add; tree backward plus the injection).  The
     first window's backward also runs with the smallest workspace (recompute
     dQ), and one range [0, P) equals the window over a flat prefix."""
-    d, dtype = 128, "bf16"
     desc = _desc(hq, hkv, d, dtype)
     scale = 1.0 / math.sqrt(d)
     hmap = oracle.head_map(hq, hkv)
@@ -597,12 +597,13 @@ def test_windows_under_producer_nodes(hq, hkv):
         check(f"one range vs flat prefix: {name}", host(x), host(y), 1e-6)
 
 
-def test_forest_window_in_one_call():
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_forest_window_in_one_call(dtype):
     """Three rollout trees over one cached prefix in one call (a forest): each
     tree's rows against the oracle's forest window (rows of different trees
     never see each other), the prefix gradients against the oracle, and the
-    same values as one call per tree to the bf16 bar."""
-    hq, hkv, d, dtype, p = 8, 2, 128, "bf16", 200
+    same values as one call per tree to the dtype's bar."""
+    hq, hkv, d, p = 8, 2, 128, 200
     desc = _desc(hq, hkv, d, dtype)
     scale = 1.0 / math.sqrt(d)
     hmap = oracle.head_map(hq, hkv)
