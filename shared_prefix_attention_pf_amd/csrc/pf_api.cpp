@@ -727,7 +727,7 @@ pf_status suffix_bwd_impl(int32_t op, const Desc& d, int32_t prefix_len, pf_tens
     a.gk_part = (float*)((char*)workspace + w.gk_part);
     a.gv_part = (float*)((char*)workspace + w.gv_part);
   }
-  a.dsum = (float*)((char*)workspace + w.dsum);
+  a.neg_dsum = (float*)((char*)workspace + w.dsum);
   a.lse2 = (float*)((char*)workspace + w.lse2);
   set_ds(a, workspace, w);
   set_own_parts(a, workspace, w);
@@ -934,7 +934,7 @@ pf_status pf_prefix_bwd_inject(const pf_attn_desc* desc, int32_t prefix_len, pf_
   a.gk_init = gk_acc;
   a.gv_init = gv_acc;
   a.lse = const_cast<float*>(lse_p);
-  a.dsum = (float*)((char*)workspace + w.dsum);
+  a.neg_dsum = (float*)((char*)workspace + w.dsum);
   a.lse2 = (float*)((char*)workspace + w.lse2);
   set_ds(a, workspace, w);
   set_own_parts(a, workspace, w);
@@ -1033,7 +1033,7 @@ pf_status tree_bwd_impl(const Desc& d, int32_t n_nodes, const int32_t* node_off,
   a.gk_init = gk_acc;
   a.gv_init = gv_acc;
   a.lse = const_cast<float*>(lse);
-  a.dsum = (float*)((char*)workspace + w.dsum);
+  a.neg_dsum = (float*)((char*)workspace + w.dsum);
   a.lse2 = (float*)((char*)workspace + w.lse2);
   set_ds(a, workspace, w);
   set_own_parts(a, workspace, w);

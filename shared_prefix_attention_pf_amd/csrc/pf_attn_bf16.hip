@@ -1049,7 +1049,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(AttnArgs a) {
       const float l = qc[nt].valid ? a.lse[(int64_t)qc[nt].head * a.rows + qc[nt].tok] : 0.f;
       lse2[nt] = (l == -INFINITY) ? INFINITY : l * kLog2e;
       if (qc[nt].valid && h32 == 0) {
-        a.dsum[(int64_t)qc[nt].head * a.rows + qc[nt].tok] = dot;
+        a.neg_dsum[(int64_t)qc[nt].head * a.rows + qc[nt].tok] = -dot;
         a.lse2[(int64_t)qc[nt].head * a.rows + qc[nt].tok] = lse2[nt];
       }
     }
@@ -1730,7 +1730,7 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
   const Rsrc q_res = make_rsrc(a.q, q_bytes);
   const Rsrc do_res = make_rsrc(a.dout, do_bytes);
   const Rsrc l_res = make_rsrc(a.lse2, l_bytes);
-  const Rsrc d_res = make_rsrc(a.dsum, l_bytes);
+  const Rsrc d_res = make_rsrc(a.neg_dsum, l_bytes);
   const uint32_t q_loff = dma_lane_off(wave, lane, q_st_b);
   const uint32_t do_loff = dma_lane_off(wave, lane, do_st_b);
 
@@ -1794,17 +1794,23 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
   f32x16 s[KT], dp[KT];        // S then P (fp32) / dP then dS of a step
   bf16x8 pb[KT][2], db[KT][2]; // packed P and dS: [key tile][query half]
 
-  // LSE (log2) and D of one 4-row group of a step (rows 8 (k & 3) + 4 h32 + r
-  // of group k = 0..7, the same rows for both key tiles), double-buffered: each
+  // LSE (log2) of one 4-row group of a step (rows 8 (k & 3) + 4 h32 + r of
+  // group k = 0..7, the same rows for both key tiles), double-buffered: each
   // group's values are read from LDS while the group before it is in use
-  f32x4 lg[2], dg[2];
+  f32x4 lg[2];
   auto ld_l = [&](auto blc, auto kc) {
     constexpr int BL = decltype(blc)::value, k = decltype(kc)::value;
     lg[k & 1] = *(const lds_f32x4*)(sb + kDkvL + BL * 256 + 4 * (8 * (k & 3) + 4 * h32));
   };
-  auto ld_d = [&](auto bdc, auto kc) {
-    constexpr int BD = decltype(bdc)::value, k = decltype(kc)::value;
-    dg[k & 1] = *(const lds_f32x4*)(sb + kDkvD + BD * 256 + 4 * (8 * (k & 3) + 4 * h32));
+  // -D of a step's rows in C layout (element i: row 8 (i / 4) + 4 h32 + i % 4),
+  // the starting value of both key tiles' dP sums, which so end as dP - D;
+  // quarter q is elements 4q .. 4q + 3
+  f32x16 nd;
+  auto ld_nd = [&](auto bdc, auto qc) {
+    constexpr int BD = decltype(bdc)::value, q = decltype(qc)::value;
+    const f32x4 v = *(const lds_f32x4*)(sb + kDkvD + BD * 256 + 4 * (8 * q + 4 * h32));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) nd[4 * q + r] = v[r];
   };
 
   // P element e of the step whose LSE is in buffer BL (in place in s); group
@@ -1821,13 +1827,11 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
       asm volatile("" : "+v"(pb[kt][i >> 3]));
     }
   };
-  // dS element e of the step whose D is in buffer BD (in place in dp); group
-  // 0's D must have been read (ld_d) beforehand
-  auto ds_elem = [&](auto bdc, auto ec) {
+  // dS element e of a step (in place in dp, which holds dP - D)
+  auto ds_elem = [&](auto ec) {
     constexpr int e = decltype(ec)::value;
-    constexpr int kt = e >> 4, i = e & 15, k = e >> 2, r = i & 3;
-    if constexpr (r == 0 && k + 1 < 4 * KT) ld_d(bdc, std::integral_constant<int, k + 1>());
-    dp[kt][i] = unpack_bf16(pb[kt][i >> 3], i & 7) * (dp[kt][i] - dg[k & 1][r]);
+    constexpr int kt = e >> 4, i = e & 15;
+    dp[kt][i] = unpack_bf16(pb[kt][i >> 3], i & 7) * dp[kt][i];
     asm volatile("" : "+v"(dp[kt][i]));
     if constexpr ((i & 7) == 7) {
       db[kt][i >> 3] = pack_half(dp[kt], i >> 3);
@@ -1896,12 +1900,12 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
         }
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt) s[kt] = mfma(fr[sl], kf[kt][idx], s[kt]);
-        elems([&](auto ec) { ds_elem(bc, ec); }, std::integral_constant<int, 0>());
+        elems([&](auto ec) { ds_elem(ec); }, std::integral_constant<int, 0>());
         if constexpr (idx < kDma) stage_load(Buf<B3>(), idx);
       } else if constexpr (run == 1) {
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt) mfma_acc(dv[dt][kt], fr[sl], pb[kt][hf]);
-        elems([&](auto ec) { ds_elem(bc, ec); }, std::integral_constant<int, NE / 2>());
+        elems([&](auto ec) { ds_elem(ec); }, std::integral_constant<int, NE / 2>());
         // group 0 of the LSE of step t + 1 (lg[0] is free from here)
         if constexpr (idx == 4) ld_l(Buf<B1>(), std::integral_constant<int, 0>());
       } else if constexpr (run == 2) {
@@ -1920,32 +1924,29 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
                 (bf16x8*)(ds_dst + (int64_t)(idx >> 1) * (a.ds_rows / kQStep) * 32 * kQStep +
                           16 * 32 * (idx & 1)));
         }
-        // group 0 of the D of step t + 1, read by the next step's dS (dg[0] is
-        // free from here)
-        if constexpr (idx == 4) ld_d(Buf<B1>(), std::integral_constant<int, 0>());
+        // -D of step t + 1, a quarter per pair, for its dP sums (this step's
+        // dS, formed in runs 0-1, no longer needs dp)
+        if constexpr (idx >= 4) ld_nd(Buf<B1>(), std::integral_constant<int, idx - 4>());
       } else {
-        if constexpr (idx == 0) {
 #pragma unroll
-          for (int kt = 0; kt < KT; ++kt) dp[kt] = zero16();
-        }
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt) dp[kt] = mfma(fr[sl], vr[sl][kt], dp[kt]);
+        for (int kt = 0; kt < KT; ++kt)
+          dp[kt] = mfma(fr[sl], vr[sl][kt], idx == 0 ? nd : dp[kt]);
         elems([&](auto ec) { p_elem(Buf<B1>(), ec); }, std::integral_constant<int, NE / 2>());
       }
       __builtin_amdgcn_sched_barrier(0);
     });
   };
-  // S, P and dP of the step in buffer BQ without overlap (pipeline fill); it
-  // leaves group 0 of that step's D read for the first step's dS
+  // S, P and dP - D of the step in buffer BQ without overlap (pipeline fill)
   auto fill = [&](auto bqc, int t0) {
     constexpr int BQ = decltype(bqc)::value;
     const lds_t* q_s = sb + kDkvQ + BQ * kStepTile;
     const lds_t* d_s = sb + kDkvO + BQ * kStepTile;
     ld_l(bqc, std::integral_constant<int, 0>());
+    static_for<0, 4>([&](auto qc) { ld_nd(bqc, qc); });
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
       s[kt] = zero16();
-      dp[kt] = zero16();
+      dp[kt] = nd;
     }
 #pragma unroll
     for (int ds = 0; ds < kD / 16; ++ds) {
@@ -1959,7 +1960,6 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
     }
     if (step_needs_mask(t0)) mask_s(t0);
     static_for<0, NE>([&](auto ec) { p_elem(bqc, ec); });
-    ld_d(bqc, std::integral_constant<int, 0>());
   };
 
   if (it_lo < it_hi) {

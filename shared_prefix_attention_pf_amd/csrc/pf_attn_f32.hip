@@ -370,7 +370,7 @@ __global__ __launch_bounds__(kThreads, 1) void dq_f32_kernel(AttnArgs a) {
       pin_agpr(dov[s]);
     }
   }
-  if (w.tvalid && h == 0) a.dsum[(int64_t)w.head * a.rows + w.tok] = dsum;
+  if (w.tvalid && h == 0) a.neg_dsum[(int64_t)w.head * a.rows + w.tok] = -dsum;
   // LSE in log2 units; rows that see no key (LSE -inf) and rows past the end
   // take +inf, so every P of theirs is zero
   float lse2 = INFINITY;
@@ -451,7 +451,7 @@ template <int D>
 __global__ __launch_bounds__(kThreads, 2) void dkv_f32_kernel(AttnArgs a) {
   constexpr int Q4 = D / 4, NTD = D / 16, RS = Tile<D>::kRs;
   __shared__ __attribute__((aligned(16))) float qd_s[2][2][Tile<D>::kFloats];   // [buffer][Q, dO]
-  __shared__ __attribute__((aligned(16))) float ld_s[2][2][64];       // [buffer][LSE, D]
+  __shared__ __attribute__((aligned(16))) float ld_s[2][2][64];       // [buffer][LSE, -D]
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, j16 = lane & 15, g4 = lane >> 4;
   // block x: KV head x % Hkv, item x / Hkv (the heads interleaved: external
@@ -539,7 +539,7 @@ __global__ __launch_bounds__(kThreads, 2) void dkv_f32_kernel(AttnArgs a) {
     if (wave == kWaves - 1)
       dma_vec(make_rsrc(a.lse + (int64_t)head * a.rows + t0, 4LL * valid), ld_s[b][0], lane);
     if (wave == kWaves - 2)
-      dma_vec(make_rsrc(a.dsum + (int64_t)head * a.rows + t0, 4LL * valid), ld_s[b][1], lane);
+      dma_vec(make_rsrc(a.neg_dsum + (int64_t)head * a.rows + t0, 4LL * valid), ld_s[b][1], lane);
   };
 
   f32x4 dk[NTD], dv[NTD];   // dK^T, dV^T: register r is head_dim 16 dt + 4 g + r
@@ -593,7 +593,7 @@ __global__ __launch_bounds__(kThreads, 2) void dkv_f32_kernel(AttnArgs a) {
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       const f32x4 lv = *(const f32x4*)(ld_s[b][0] + 16 * hf + 4 * g4);
-      const f32x4 dsv = *(const f32x4*)(ld_s[b][1] + 16 * hf + 4 * g4);
+      const f32x4 ndv = *(const f32x4*)(ld_s[b][1] + 16 * hf + 4 * g4);   // -D
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int tq = t0 + 16 * hf + 4 * g4 + r;
@@ -601,7 +601,7 @@ __global__ __launch_bounds__(kThreads, 2) void dkv_f32_kernel(AttnArgs a) {
         // a visible row sees at least this key, so its LSE is finite
         const float p = vis ? exp2_(s[hf][r] * c - lv[r] * kLog2e) : 0.f;
         s[hf][r] = p;
-        dp[hf][r] = p * (dp[hf][r] - dsv[r]);
+        dp[hf][r] = p * (dp[hf][r] + ndv[r]);
       }
     }
     if (dsb) {

@@ -72,7 +72,8 @@ struct AttnArgs {
   const void* dout; int64_t do_st, do_sh; // upstream gradient
   void* out; int64_t out_st, out_sh;      // O (forward) or dQ (backward)
   float* lse;                             // [Hq, rows]
-  float* dsum;                            // [Hq, rows] D = rowsum(dO * O), workspace
+  float* neg_dsum;                        // [Hq, rows] -D = -rowsum(dO * O), workspace (negated:
+                                          //   the dK/dV kernels start their dP sums from it)
   float* lse2;                            // [Hq, rows] LSE log2(e) (+inf for rows that see no key),
                                           //   written by the dQ pass for the dK/dV pass, workspace
   // external keys (every query row sees all of them), [n_ext, Hkv, d]
@@ -131,7 +132,7 @@ void launch_hook(const char* kernel, hipStream_t stream, int end);
 hipError_t launch_prep(const SegTable& seg, const HeadTable& heads, RowInfo ri, hipStream_t stream);
 // launch_prep's work and, in the same launch, D = rowsum(dO * O) and LSE
 // log2(e) (+inf for rows that see no key) of every (row, query head) into
-// a.dsum / a.lse2 (bf16 inputs).
+// a.neg_dsum (as -D) / a.lse2 (bf16 inputs).
 hipError_t launch_prep_dsum_bf16(const SegTable& seg, const HeadTable& heads, const AttnArgs& a,
                                  hipStream_t stream);
 // the same for fp32 inputs (head_dim 64 or 128)

@@ -128,7 +128,7 @@ __device__ __forceinline__ void dsum_body(const AttnArgs& a, int blk) {
     if (sub == 0 && p0 + u < n) {
       const int64_t i = (int64_t)hh[u] * a.rows + tt[u];
       const float l = a.lse[i];
-      a.dsum[i] = dot;
+      a.neg_dsum[i] = -dot;
       a.lse2[i] = (l == -INFINITY) ? INFINITY : l * 1.4426950408889634f;
     }
   }
