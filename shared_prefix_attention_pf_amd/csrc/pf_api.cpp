@@ -1,7 +1,8 @@
 // Host side of the C ABI declared in include/pf.h: argument validation,
 // workspace layout, and the launch sequence of each entry point.  No entry
-// point allocates, synchronises or keeps state; every check runs before the
-// first HIP call.
+// point allocates or synchronises, and every check runs before the first HIP
+// call.  The only state is the optional launch hook and, per device, the
+// address of the static scratch of pf_suffix_attn_bwd_accum_noalloc.
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -225,7 +226,7 @@ pf_status scratch_of_current_device(void** out) {
 // ------------------------------------------------------------- workspace
 
 struct WsLayout {
-  size_t kend = 0, bmax = 0, bmin = 0, qhead = 0, dsum = 0, lse2 = 0, gk_part = 0, gv_part = 0;
+  size_t kend = 0, bmax = 0, bmin = 0, qhead = 0, neg_dsum = 0, lse2 = 0, gk_part = 0, gv_part = 0;
   size_t ext_tiles = 0;   // window ops: (first row, valid rows) per 32 cached keys
   size_t total = 0;
   size_t dk_part = 0, dv_part = 0;
@@ -267,7 +268,7 @@ WsLayout layout(int32_t op, const Desc& d, int32_t n_ext, int32_t rows, bool wan
   const bool bwd = op == PF_OP_SUFFIX_BWD || op == PF_OP_PREFIX_BWD || op == PF_OP_TREE_BWD ||
                    op == PF_OP_TREE_SUFFIX_BWD;
   if (bwd) {
-    w.dsum = off;
+    w.neg_dsum = off;   // -D per (query head, row)
     off += align_up((size_t)d.hq * rows * 4);
     w.lse2 = off;
     off += align_up((size_t)d.hq * rows * 4);
@@ -727,7 +728,7 @@ pf_status suffix_bwd_impl(int32_t op, const Desc& d, int32_t prefix_len, pf_tens
     a.gk_part = (float*)((char*)workspace + w.gk_part);
     a.gv_part = (float*)((char*)workspace + w.gv_part);
   }
-  a.neg_dsum = (float*)((char*)workspace + w.dsum);
+  a.neg_dsum = (float*)((char*)workspace + w.neg_dsum);
   a.lse2 = (float*)((char*)workspace + w.lse2);
   set_ds(a, workspace, w);
   set_own_parts(a, workspace, w);
@@ -934,7 +935,7 @@ pf_status pf_prefix_bwd_inject(const pf_attn_desc* desc, int32_t prefix_len, pf_
   a.gk_init = gk_acc;
   a.gv_init = gv_acc;
   a.lse = const_cast<float*>(lse_p);
-  a.neg_dsum = (float*)((char*)workspace + w.dsum);
+  a.neg_dsum = (float*)((char*)workspace + w.neg_dsum);
   a.lse2 = (float*)((char*)workspace + w.lse2);
   set_ds(a, workspace, w);
   set_own_parts(a, workspace, w);
@@ -1033,7 +1034,7 @@ pf_status tree_bwd_impl(const Desc& d, int32_t n_nodes, const int32_t* node_off,
   a.gk_init = gk_acc;
   a.gv_init = gv_acc;
   a.lse = const_cast<float*>(lse);
-  a.neg_dsum = (float*)((char*)workspace + w.dsum);
+  a.neg_dsum = (float*)((char*)workspace + w.neg_dsum);
   a.lse2 = (float*)((char*)workspace + w.lse2);
   set_ds(a, workspace, w);
   set_own_parts(a, workspace, w);
