@@ -288,6 +288,8 @@ def test_ranges_entry_points_validate_on_the_host():
     assert call([-1], [5]) == pf.PF_ERR_INVALID_ARG
     assert call([0], [-5]) == pf.PF_ERR_INVALID_ARG
     assert call([0, 50], [100, 40]) == pf.PF_ERR_INVALID_ARG          # overlap
+    n = pf.PF_MAX_SEGMENTS + 1
+    assert call(list(range(0, 2 * n, 2)), [1] * n, c_rows=2 * n) == pf.PF_ERR_UNSUPPORTED
     assert call([100, 0], [40, 101]) == pf.PF_ERR_INVALID_ARG         # overlaps a later start
     for dtype in (pf.PF_BF16, pf.PF_F32):
         desc = pf.AttnDesc(32, 8, 128, dtype=dtype)

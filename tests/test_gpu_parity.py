@@ -641,3 +641,49 @@ def test_forest_window_in_one_call(dtype):
     for name, x, y in zip(("O", "LSE", "dQ", "dK", "dV"), (o, lse, dq, dk, dv), cat_sep):
         check(f"forest vs one call per tree: {name}", host(x), host(y), tol)
     check("forest vs one call per tree: gK", host(gk), host(gk1), tol)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_many_shuffled_ranges(dtype):
+    """A window over 200 disjoint row ranges of 1-40 rows each (5 of them
+    start on a 32-row boundary), listed out of row order, with empty ranges among them: every
+    range a padded tile run of its own in the tile table, split key blocks,
+    and gK/gV scattered back through the table.  Against the oracle's gather,
+    window attention and scatter-add."""
+    hq, hkv = 4, 2
+    d = 128 if dtype == "bf16" else 64
+    rng = np.random.default_rng(77)
+    lens = rng.integers(1, 41, size=200)
+    gaps = rng.integers(0, 5, size=200)
+    starts = np.cumsum(np.concatenate([[3], (lens + gaps)[:-1]])) + gaps[0]
+    cp = int(starts[-1] + lens[-1] + 7)
+    order = rng.permutation(200)
+    ranges = [(int(starts[i]), int(lens[i])) for i in order]
+    ranges[5:5] = [(int(starts[0]), 0)]           # empty ranges are ignored
+    ranges.append((cp, 0))
+    print(f"\n{len(ranges)} ranges over {cp} producer rows, {sum(n for _, n in ranges)} cached",
+          flush=True)
+    gp = random_tree_group(78, np.array([0, cp], np.int32), hq, hkv, d, dtype)
+    node_off, parent = random_tree(79, 6, max_len=60, min_len=1)
+    tg = random_tree_group(79, node_off, hq, hkv, d, dtype)
+    desc = _desc(hq, hkv, d, dtype)
+    kc, vc = dev(gp["k"], dtype), dev(gp["v"], dtype)
+    tt = {k: dev(tg[k], dtype) for k in ("q", "k", "v", "do")}
+    o, lse = G.tree_suffix_fwd_ranges(desc, kc, vc, ranges, node_off, parent, tt["q"], tt["k"],
+                                      tt["v"])
+    gk = torch.zeros(cp, hkv, d, dtype=torch.float32, device="cuda")
+    gv = torch.zeros_like(gk)
+    dq, dk, dv = G.tree_suffix_bwd_ranges(desc, kc, vc, ranges, node_off, parent, tt["q"], tt["k"],
+                                          tt["v"], o, lse, tt["do"], gk, gv)
+    torch.cuda.synchronize()
+    ref = oracle.tree_window_attention_ranges(gp["k"], gp["v"], ranges, tg["q"], tg["k"], tg["v"],
+                                              tg["do"], node_off, parent, 1.0 / math.sqrt(d),
+                                              oracle.head_map(hq, hkv))
+    tol = TOL[dtype]
+    for name, got in (("O", o), ("LSE", lse), ("dQ", dq), ("dK", dk), ("dV", dv), ("gK", gk),
+                      ("gV", gv)):
+        check(name, host(got), ref[name.lower()], tol)
+    used = np.zeros(cp, dtype=bool)
+    for s, n in ranges:
+        used[s:s + n] = True
+    assert np.all(host(gk)[~used] == 0) and np.all(host(gv)[~used] == 0)
