@@ -663,9 +663,11 @@ def stats_summary(stats_csv, out_md, cid, command):
 
 
 # phases a single-call group step launches each kernel in (full workspace)
+# the phases a flat group's step launches each kernel in, in launch order
 PHASES_OF = {"fwd_kernel": ("A", "B"), "bwd_dkv_kernel": ("B", "C"),
              "bwd_dq_ds_kernel": ("B", "C"), "prep_dsum_kernel": ("B", "C"),
-             "partial_sums_kernel": ("B", "C")}
+             "partial_sums_kernel": ("B", "C"), "fwd_f32_kernel": ("A", "B"),
+             "dkv_f32_kernel": ("B", "C"), "dq_ds_f32_kernel": ("B", "C")}
 
 
 def counter_summary(run_dirs, out_md, cid, command):

@@ -99,3 +99,18 @@ def test_stored_figures_are_keyed_to_their_kernel_family(tmp_path, monkeypatch):
     assert after["f32"] != before["f32"]
     (csrc / "pf_api.cpp").write_text("changed")
     assert all(bench.kernel_source_hash(f) != after[f] for f in after)
+
+
+def test_counter_phases_cover_both_families():
+    """The SQ counter summary labels a kernel's dispatches by the phases a flat
+    group's step runs it in; every kernel a flat group launches in more than
+    one phase, in either dtype family, must be listed, or its last (Phase C)
+    dispatch would be labelled Phase B."""
+    two_phase = {"fwd_kernel", "bwd_dkv_kernel", "bwd_dq_ds_kernel", "fwd_f32_kernel",
+                 "dkv_f32_kernel", "dq_ds_f32_kernel", "prep_dsum_kernel", "partial_sums_kernel"}
+    assert two_phase <= set(bench.PHASES_OF)
+    assert set(bench.PHASES_OF) <= set(bench.KERNEL_SYMBOL.values())
+    for k in ("fwd_kernel", "fwd_f32_kernel"):
+        assert bench.PHASES_OF[k] == ("A", "B")
+    for k in ("bwd_dkv_kernel", "dkv_f32_kernel", "bwd_dq_ds_kernel", "dq_ds_f32_kernel"):
+        assert bench.PHASES_OF[k] == ("B", "C")
