@@ -2,28 +2,27 @@
 // workspace layout, and the launch sequence of each entry point.  No entry
 // point allocates or synchronises, and every check runs before the first HIP
 // call.  The only state is the optional launch hook and, per device, the
-// address of the static scratch of pf_suffix_attn_bwd_accum_noalloc.
+// address of the static scratch of pf_suffix_attn_bwd_accum_noalloc.  No C++
+// exception can leave an entry point: nothing here allocates on the heap or
+// takes a lock (the error text is a fixed thread-local buffer).
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
 
-#include <mutex>
-#include <string>
+#include <atomic>
 
 #include "pf_internal.h"
 
 namespace {
 
-thread_local std::string g_last_error;
+thread_local char g_last_error[512];
 
 pf_status fail(pf_status s, const char* fmt, ...) {
-  char buf[512];
   va_list ap;
   va_start(ap, fmt);
-  vsnprintf(buf, sizeof(buf), fmt, ap);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
   va_end(ap);
-  g_last_error = buf;
   return s;
 }
 
@@ -199,8 +198,9 @@ constexpr size_t kScratchBytes = PF_NOALLOC_SCRATCH_BYTES;
 static __device__ __align__(256) char scratch[kScratchBytes];
 
 constexpr int kMaxDevices = 64;
-std::mutex g_scratch_mu;
-void* g_scratch_addr[kMaxDevices];
+// hipGetSymbolAddress returns the same address every time on a device, so
+// two threads that both look it up store the same value
+std::atomic<void*> g_scratch_addr[kMaxDevices];
 
 // The device address of `scratch` on the calling thread's current device.
 pf_status scratch_of_current_device(void** out) {
@@ -210,16 +210,17 @@ pf_status scratch_of_current_device(void** out) {
   if (dev < 0 || dev >= kMaxDevices)
     return fail(PF_ERR_UNSUPPORTED, "device %d is beyond the %d devices the scratch tracks", dev,
                 kMaxDevices);
-  std::lock_guard<std::mutex> lock(g_scratch_mu);
-  if (!g_scratch_addr[dev]) {
+  void* known = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!known) {
     void* p = nullptr;
     e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
     if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
     if (!p || (uintptr_t)p % 256)
       return fail(PF_ERR_HIP, "hipGetSymbolAddress(scratch) returned an unaligned address");
-    g_scratch_addr[dev] = p;
+    g_scratch_addr[dev].store(p, std::memory_order_release);
+    known = p;
   }
-  *out = g_scratch_addr[dev];
+  *out = known;
   return PF_OK;
 }
 
@@ -496,13 +497,15 @@ pf_status run_bwd(const Desc& d, const pf::AttnArgs& a, const pf::SegTable& seg,
 namespace pf {
 
 namespace {
-pf_launch_hook g_hook = nullptr;
-void* g_hook_user = nullptr;
+// the user pointer is stored before the hook and read after it, so a launch
+// that sees a hook sees its user pointer
+std::atomic<pf_launch_hook> g_hook{nullptr};
+std::atomic<void*> g_hook_user{nullptr};
 }  // namespace
 
 void launch_hook(const char* kernel, hipStream_t stream, int end) {
-  const pf_launch_hook h = g_hook;
-  if (h) h(kernel, (void*)stream, end, g_hook_user);
+  const pf_launch_hook h = g_hook.load(std::memory_order_acquire);
+  if (h) h(kernel, (void*)stream, end, g_hook_user.load(std::memory_order_relaxed));
 }
 
 // Workgroups of the KV-stationary backward that run at once on the chip: one
@@ -553,11 +556,11 @@ extern "C" {
 int32_t pf_abi_version(void) { return PF_ABI_VERSION; }
 
 void pf_set_launch_hook(pf_launch_hook hook, void* user) {
-  pf::g_hook_user = user;
-  pf::g_hook = hook;
+  pf::g_hook_user.store(user, std::memory_order_relaxed);
+  pf::g_hook.store(hook, std::memory_order_release);
 }
 
-const char* pf_last_error(void) { return g_last_error.c_str(); }
+const char* pf_last_error(void) { return g_last_error; }
 
 const char* pf_status_string(pf_status s) {
   switch (s) {
