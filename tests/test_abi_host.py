@@ -308,3 +308,39 @@ def test_ranges_entry_points_validate_on_the_host():
         ctypes.c_void_p(FAKE), q, None, ctypes.c_void_p(FAKE), q, kv, kv, pf.PF_BF16,
         ctypes.c_void_p(FAKE), 1 << 30, ctypes.c_void_p(0))
     assert st == pf.PF_ERR_INVALID_ARG
+
+
+def test_last_error_is_per_thread_and_bounded():
+    """pf_last_error is the calling thread's message of its last failing call,
+    kept in a fixed thread-local buffer."""
+    import threading
+    pf._lib.pf_last_error.restype = ctypes.c_char_p
+    got = {}
+
+    def other():
+        assert _suffix_fwd(_desc(hq=6, hkv=4), [0, 4]) == pf.PF_ERR_INVALID_ARG
+        got["other"] = pf._lib.pf_last_error().decode()
+
+    assert _suffix_fwd(_desc(), [0, 5, 3]) == pf.PF_ERR_INVALID_ARG
+    mine = pf._lib.pf_last_error().decode()
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert "cu_seqlens" in mine and "not a multiple" in got["other"]
+    assert pf._lib.pf_last_error().decode() == mine
+    # overlapping row ranges: the message names the range and fits the buffer
+    d, _keep = _desc()
+    long_ranges = [(0, 5)] * 3
+    rs = np.asarray([r[0] for r in long_ranges], np.int32)
+    rl = np.asarray([r[1] for r in long_ranges], np.int32)
+    p32 = ctypes.POINTER(ctypes.c_int32)
+    no = np.asarray([0, 4], np.int32)
+    pa = np.asarray([-1], np.int32)
+    q, kv = _t(heads=32), _t()
+    st = pf._lib.pf_tree_suffix_attn_fwd_ranges(
+        ctypes.byref(d), 100, kv, kv, 3, rs.ctypes.data_as(p32), rl.ctypes.data_as(p32), 1,
+        no.ctypes.data_as(p32), pa.ctypes.data_as(p32), q, kv, kv, q, ctypes.c_void_p(FAKE),
+        ctypes.c_void_p(FAKE), 1 << 30, ctypes.c_void_p(0))
+    assert st == pf.PF_ERR_INVALID_ARG
+    msg = pf._lib.pf_last_error().decode()
+    assert "overlaps" in msg and len(msg) < 512
