@@ -54,7 +54,8 @@
  *    and is asynchronous: a return of PF_OK means "launched".
  *  - Every argument is validated before anything is launched.  On an error
  *    return no HIP call has been made (except PF_ERR_HIP) and no output has
- *    been touched; pf_last_error() gives a message (thread-local).
+ *    been touched; pf_last_error() gives a message (thread-local).  No C++
+ *    exception leaves an entry point.
  *  - Results are bitwise identical from run to run for the same inputs,
  *    call sequence and device; there are no floating-point atomics.
  *  - Calls on different streams may run concurrently unless they write the
