@@ -687,3 +687,99 @@ def test_many_shuffled_ranges(dtype):
     for s, n in ranges:
         used[s:s + n] = True
     assert np.all(host(gk)[~used] == 0) and np.all(host(gv)[~used] == 0)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_strided_layouts(dtype):
+    """Phases A, B and C with every tensor a strided view, as a training step
+    hands them over: Q/K/V sliced out of one fused projection output
+    [T, Hq + 2 Hkv, d], dO and O with padded rows, dQ starting two heads into
+    a wider buffer, dK/dV sharing one fused buffer.  Every output bitwise equal
+    to the contiguous run (the arithmetic does not depend on strides) and
+    within the bar of the oracle."""
+    hq, hkv, d, p, lens = 8, 2, 128, 200, [70, 1, 130]
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    g = random_small_group(47, hq, hkv, d, p, lens, dtype)
+    cu = g["cu_seqlens"]
+    rows = int(cu[-1])
+    desc = _desc(hq, hkv, d, dtype)
+    t = {k: dev(g[k], dtype) for k in ("q_p", "k_p", "v_p", "do_p", "q_s", "k_s", "v_s", "do_s")}
+
+    def fused(q, k, v):
+        buf = torch.zeros(q.shape[0], hq + 2 * hkv, d, dtype=tdt, device="cuda")
+        buf[:, :hq] = q
+        buf[:, hq:hq + hkv] = k
+        buf[:, hq + hkv:] = v
+        return buf[:, :hq], buf[:, hq:hq + hkv], buf[:, hq + hkv:]
+
+    def padded(n, heads, pad):
+        return torch.full((n, heads, d + pad), 7.0, dtype=tdt, device="cuda")[:, :, :d]
+
+    def fused_kv(n):
+        buf = torch.full((n, 2 * hkv, d), 7.0, dtype=tdt, device="cuda")
+        return buf[:, :hkv], buf[:, hkv:]
+
+    qs, ks, vs = fused(t["q_s"], t["k_s"], t["v_s"])
+    qp, kp, vp = fused(t["q_p"], t["k_p"], t["v_p"])
+    do_s = padded(rows, hq, 8)
+    do_s.copy_(t["do_s"])
+    do_p = padded(p, hq, 8)
+    do_p.copy_(t["do_p"])
+    assert not qs.is_contiguous() and not do_s.is_contiguous()
+
+    # Phase A
+    o_p = padded(p, hq, 16)
+    lse_p = torch.empty(hq, p, device="cuda")
+    pf.pf_prefix_fwd(desc, p, qp, kp, vp, o_p, lse_p, G.workspace(pf.PF_OP_PREFIX_FWD, desc, p, p,
+                                                                 "cuda"))
+    # Phase B
+    o_s = padded(rows, hq, 16)
+    lse_s = torch.empty(hq, rows, device="cuda")
+    pf.pf_suffix_attn_fwd(desc, p, kp, vp, cu, qs, ks, vs, o_s, lse_s,
+                          G.workspace(pf.PF_OP_SUFFIX_FWD, desc, p, rows, "cuda"))
+    dq_buf = torch.full((rows, hq + 4, d), 7.0, dtype=tdt, device="cuda")
+    dq_s = dq_buf[:, 2:2 + hq]
+    dk_s, dv_s = fused_kv(rows)
+    gk = torch.zeros(p, hkv, d, device="cuda")
+    gv = torch.zeros_like(gk)
+    pf.pf_suffix_attn_bwd_accum(desc, p, kp, vp, cu, qs, ks, vs, o_s, lse_s, do_s, dq_s, dk_s,
+                                dv_s, gk, gv, G.workspace(pf.PF_OP_SUFFIX_BWD, desc, p, rows,
+                                                          "cuda"))
+    # Phase C
+    dq_p = padded(p, hq, 24)
+    dk_p, dv_p = fused_kv(p)
+    pf.pf_prefix_bwd_inject(desc, p, qp, kp, vp, o_p, lse_p, do_p, gk, gv, dq_p, dk_p, dv_p,
+                            desc.dtype, G.workspace(pf.PF_OP_PREFIX_BWD, desc, p, p, "cuda"))
+    torch.cuda.synchronize()
+
+    # the same calls on contiguous tensors
+    c_op, c_lp = G.prefix_fwd(desc, t["q_p"], t["k_p"], t["v_p"])
+    c_os, c_ls = G.suffix_fwd(desc, t["k_p"], t["v_p"], cu, t["q_s"], t["k_s"], t["v_s"])
+    c_gk = torch.zeros_like(gk)
+    c_gv = torch.zeros_like(gk)
+    c_dq, c_dk, c_dv = G.suffix_bwd(desc, t["k_p"], t["v_p"], cu, t["q_s"], t["k_s"], t["v_s"],
+                                    c_os, c_ls, t["do_s"], c_gk, c_gv)
+    c_dqp, c_dkp, c_dvp = G.prefix_bwd(desc, t["q_p"], t["k_p"], t["v_p"], c_op, c_lp, t["do_p"],
+                                       c_gk, c_gv)
+    torch.cuda.synchronize()
+    for name, x, y in (("O_P", o_p, c_op), ("LSE_P", lse_p, c_lp), ("O_S", o_s, c_os),
+                       ("LSE_S", lse_s, c_ls), ("dQ_S", dq_s, c_dq), ("dK_S", dk_s, c_dk),
+                       ("dV_S", dv_s, c_dv), ("gK", gk, c_gk), ("gV", gv, c_gv),
+                       ("dQ_P", dq_p, c_dqp), ("dK_P", dk_p, c_dkp), ("dV_P", dv_p, c_dvp)):
+        assert torch.equal(x, y), f"{name}: strided run differs from the contiguous one"
+    # nothing outside the views was written
+    assert torch.all(dq_buf[:, :2] == 7.0) and torch.all(dq_buf[:, 2 + hq:] == 7.0)
+    assert torch.all(o_s.as_strided((rows, hq, 16), (hq * (d + 16), d + 16, 1), d) == 7.0)
+    scale = 1.0 / math.sqrt(d)
+    hmap = oracle.head_map(hq, hkv)
+    tol = TOL[dtype]
+    ref = oracle.suffix_attention(g["k_p"], g["v_p"], g["q_s"], g["k_s"], g["v_s"], g["do_s"], cu,
+                                  scale, hmap)
+    for name, x, key in (("O_S", o_s, "o_s"), ("dQ_S", dq_s, "dq_s"), ("dK_S", dk_s, "dk_s"),
+                         ("dV_S", dv_s, "dv_s"), ("gK", gk, "gk"), ("gV", gv, "gv")):
+        check(name, host(x), ref[key], tol)
+    rdq, rdk, rdv = oracle.prefix_backward_inject(g["q_p"], g["k_p"], g["v_p"], g["do_p"],
+                                                  ref["gk"], ref["gv"], scale, hmap)
+    check("dQ_P", host(dq_p), rdq, tol)
+    check("dK_P", host(dk_p), rdk, tol)
+    check("dV_P", host(dv_p), rdv, tol)
