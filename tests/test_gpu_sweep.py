@@ -4,7 +4,8 @@ The fixed cases of test_gpu_parity.py pick shapes by hand; these draw them:
 dtype and head_dim, KV heads and query-head group size, a permuted head map,
 prefix lengths on and off the 32- and 64-key tile edges (0 included), one to
 five suffixes of ragged lengths (0 and 1 included), a sharper softmax (Q
-scaled by 3, so the running maximum moves and the lazy rescale runs), and
+scaled by 3, so the running maximum moves and the lazy rescale runs), a
+softmax scale of the caller's (0.05 or 0.2) or the 1/sqrt(d) default, and
 the smallest workspace (recompute dQ) or the full one (dQ from stored dS).
 Each draw is printed before it runs.  Tolerances as in test_gpu_parity.py.
 """
@@ -45,8 +46,14 @@ def _dtype_dim(rng):
     return "f32", int(rng.choice([64, 128]))
 
 
-def _desc(hq, hkv, d, dtype, qmap=None):
-    return pf.AttnDesc(hq, hkv, d, pf.PF_BF16 if dtype == "bf16" else pf.PF_F32, 0.0, qmap)
+def _desc(hq, hkv, d, dtype, qmap=None, softmax_scale=0.0):
+    return pf.AttnDesc(hq, hkv, d, pf.PF_BF16 if dtype == "bf16" else pf.PF_F32, softmax_scale,
+                       qmap)
+
+
+def _scale(c):
+    """the descriptor's softmax scale and the one the oracle applies"""
+    return c["softmax_scale"], c["softmax_scale"] or 1.0 / math.sqrt(c["d"])
 
 
 def draw_suffix_case(seed):
@@ -60,8 +67,10 @@ def draw_suffix_case(seed):
         lens[0] = 1 + int(rng.integers(0, 90))
     scale_q = float(rng.choice([1.0, 3.0]))
     min_ws = bool(rng.random() < 0.35)
+    # drawn last, so the fields above are the same as without it
+    softmax_scale = float(rng.choice([0.0, 0.0, 0.05, 0.2]))
     return dict(dtype=dtype, d=d, hq=hq, hkv=hkv, qmap=qmap, p=p, lens=lens, scale_q=scale_q,
-                min_ws=min_ws)
+                min_ws=min_ws, softmax_scale=softmax_scale)
 
 
 @pytest.mark.parametrize("seed", range(24))
@@ -73,8 +82,8 @@ def test_random_suffix_group(seed):
     g = random_small_group(500 + seed, hq, hkv, d, p, c["lens"], dtype, scale_q=c["scale_q"])
     cu = g["cu_seqlens"]
     rows = int(cu[-1])
-    desc = _desc(hq, hkv, d, dtype, c["qmap"])
-    scale = 1.0 / math.sqrt(d)
+    ds, scale = _scale(c)
+    desc = _desc(hq, hkv, d, dtype, c["qmap"], ds)
     t = {k: dev(g[k], dtype) for k in ("k_p", "v_p", "q_s", "k_s", "v_s", "do_s")}
     o, lse = G.suffix_fwd(desc, t["k_p"], t["v_p"], cu, t["q_s"], t["k_s"], t["v_s"])
     rng = np.random.default_rng(seed)
@@ -104,9 +113,11 @@ def draw_prefix_case(seed):
     dtype, d = _dtype_dim(rng)
     hq, hkv, qmap = _heads(rng)
     p = int(rng.choice([1, 2, 31, 33, 64, 65, 130, 255, 257, 384, 511]))
-    return dict(dtype=dtype, d=d, hq=hq, hkv=hkv, qmap=qmap, p=p,
-                with_do=bool(rng.random() < 0.8), scale_q=float(rng.choice([1.0, 3.0])),
-                min_ws=bool(rng.random() < 0.35))
+    c = dict(dtype=dtype, d=d, hq=hq, hkv=hkv, qmap=qmap, p=p,
+             with_do=bool(rng.random() < 0.8), scale_q=float(rng.choice([1.0, 3.0])),
+             min_ws=bool(rng.random() < 0.35))
+    c["softmax_scale"] = float(rng.choice([0.0, 0.0, 0.05, 0.2]))
+    return c
 
 
 @pytest.mark.parametrize("seed", range(10))
@@ -116,8 +127,8 @@ def test_random_prefix_group(seed):
     print(f"\nsweep prefix seed {seed}: {c}", flush=True)
     dtype, d, hq, hkv, p = c["dtype"], c["d"], c["hq"], c["hkv"], c["p"]
     g = random_small_group(600 + seed, hq, hkv, d, p, [1], dtype, scale_q=c["scale_q"])
-    desc = _desc(hq, hkv, d, dtype, c["qmap"])
-    scale = 1.0 / math.sqrt(d)
+    ds, scale = _scale(c)
+    desc = _desc(hq, hkv, d, dtype, c["qmap"], ds)
     hmap = oracle.head_map(hq, hkv, c["qmap"])
     rng = np.random.default_rng(seed)
     gk_np = rng.standard_normal((p, hkv, d)).astype(np.float32)

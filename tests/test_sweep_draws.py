@@ -15,6 +15,8 @@ def test_draws_are_fixed_and_cover_the_edges():
     assert {c["hq"] // c["hkv"] for c in s} >= {1, 2, 3, 4}
     assert any(c["scale_q"] > 1 for c in s) and any(c["min_ws"] for c in s)
     assert all(sum(c["lens"]) > 0 for c in s)
+    assert {c["softmax_scale"] for c in s} == {0.0, 0.05, 0.2}
+    assert len({c["softmax_scale"] for c in (draw_prefix_case(i) for i in range(10))}) > 1
     for c in s:
         if c["qmap"] is not None:
             group = c["hq"] // c["hkv"]
