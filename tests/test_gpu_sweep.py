@@ -210,3 +210,55 @@ def test_random_window_under_a_producer_node(seed):
     for s, n in ranges:
         used[s:s + n] = True
     assert np.all(host(gk)[~used] == 0) and np.all(host(gv)[~used] == 0)
+
+
+def draw_tree_case(seed):
+    rng = np.random.default_rng(9900 + seed)
+    dtype, d = _dtype_dim(rng)
+    hq, hkv, qmap = _heads(rng)
+    return dict(dtype=dtype, d=d, hq=hq, hkv=hkv, qmap=qmap, n=int(rng.integers(1, 20)),
+                max_len=int(rng.choice([1, 20, 64, 130])), min_len=int(rng.choice([0, 1])),
+                min_ws=bool(rng.random() < 0.35),
+                softmax_scale=float(rng.choice([0.0, 0.0, 0.05, 0.2])))
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_random_tree(seed):
+    """Tree attention forward and backward over a random tree (node lengths
+    from 0, fan-out random), and the backward with random gK/gV injected."""
+    c = draw_tree_case(seed)
+    print(f"\nsweep tree seed {seed}: {c}", flush=True)
+    dtype, d, hq, hkv = c["dtype"], c["d"], c["hq"], c["hkv"]
+    node_off, parent = random_tree(900 + seed, c["n"], max_len=c["max_len"], min_len=c["min_len"])
+    rows = int(node_off[-1])
+    print(f"  node_off {node_off.tolist()} parent {parent.tolist()}", flush=True)
+    if rows == 0:
+        pytest.skip("the drawn tree has no rows")
+    tg = random_tree_group(900 + seed, node_off, hq, hkv, d, dtype)
+    ds, scale = _scale(c)
+    desc = _desc(hq, hkv, d, dtype, c["qmap"], ds)
+    hmap = oracle.head_map(hq, hkv, c["qmap"])
+    t = {k: dev(tg[k], dtype) for k in ("q", "k", "v", "do")}
+    o, lse = G.tree_fwd(desc, node_off, parent, t["q"], t["k"], t["v"])
+    ws = None
+    if c["min_ws"]:
+        ws = torch.empty(pf.pf_workspace_size_min(pf.PF_OP_TREE_BWD, desc, 0, rows),
+                         dtype=torch.uint8, device="cuda")
+    dq, dk, dv = G.tree_bwd(desc, node_off, parent, t["q"], t["k"], t["v"], o, lse, t["do"], ws=ws)
+    rng = np.random.default_rng(seed)
+    gk_np = rng.standard_normal((rows, hkv, d)).astype(np.float32)
+    gv_np = rng.standard_normal((rows, hkv, d)).astype(np.float32)
+    gk, gv = torch.from_numpy(gk_np).cuda(), torch.from_numpy(gv_np).cuda()
+    iq, ik, iv = G.tree_bwd_inject(desc, node_off, parent, t["q"], t["k"], t["v"], o, lse, t["do"],
+                                   gk, gv, dkv_dtype=pf.PF_F32, ws=ws)
+    torch.cuda.synchronize()
+    ref = oracle.tree_attention_direct(tg["q"], tg["k"], tg["v"], tg["do"], node_off, parent,
+                                       scale, hmap)
+    tol = TOL[dtype]
+    for name, got in (("O", o), ("LSE", lse), ("dQ", dq), ("dK", dk), ("dV", dv)):
+        check(name, host(got), ref[name.lower()], tol)
+    rdq, rdk, rdv = oracle.tree_backward_inject(tg["q"], tg["k"], tg["v"], tg["do"], node_off,
+                                                parent, gk_np, gv_np, scale, hmap)
+    check("dQ (injected)", host(iq), rdq, tol)
+    check("dK (injected, fp32 out)", host(ik), rdk, tol)
+    check("dV (injected, fp32 out)", host(iv), rdv, tol)

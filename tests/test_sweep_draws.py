@@ -1,6 +1,7 @@
 """The random GPU sweep's draws (host only): the same cases every run, and
 the shapes its docstring promises are among them."""
-from tests.test_gpu_sweep import draw_prefix_case, draw_suffix_case, draw_window_case
+from tests.test_gpu_sweep import (draw_prefix_case, draw_suffix_case, draw_tree_case,
+                                  draw_window_case)
 
 
 def test_draws_are_fixed_and_cover_the_edges():
@@ -27,3 +28,7 @@ def test_draws_are_fixed_and_cover_the_edges():
     w = [draw_window_case(i) for i in range(10)]
     assert any(c["node"] == 0 for c in w) and any(c["node"] > 0 for c in w)
     assert {c["dtype"] for c in w} == {"bf16", "f32"} and any(c["min_ws"] for c in w)
+    t = [draw_tree_case(i) for i in range(10)]
+    assert {c["dtype"] for c in t} == {"bf16", "f32"} and any(c["min_ws"] for c in t)
+    assert any(c["n"] == 1 for c in t) and max(c["n"] for c in t) >= 16
+    assert any(c["qmap"] is not None for c in t) and any(c["softmax_scale"] for c in t)
