@@ -1017,7 +1017,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(AttnArgs a) {
   const int t1 = min(t0 + tq, a.rows);
 
   // stationary Q and dO fragments (AGPRs), D = rowsum(dO * O) and LSE (log2)
-  // per query column; D and LSE (log2) are also written for the dK/dV pass
+  // per query column; -D and LSE (log2) are also written for the dK/dV pass
   QCol qc[2];
   bf16x8 qf[2][kD / 16], df[2][kD / 16];
   float lse2[2], dsum[2];
@@ -1560,7 +1560,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_ds_kernel(AttnArgs a, Part
 // Q^T dS (matrix cores).  The steps are software-pipelined so the VALU work
 // of one step runs beside the products of another (the four runs of MFMA
 // pairs described at `step` below).  dS reads P back from its packed bf16
-// form, so one set of S/dP registers serves every step.  Q/dO tiles and the steps' LSE (log2 units) and D rotate
+// form, so one set of S/dP registers serves every step.  Q/dO tiles and the steps' LSE (log2 units) and -D rotate
 // through four LDS buffers; step t + 3 is staged during step t, one staging
 // load per M1 product pair.
 constexpr int kQStep = 32;
@@ -1578,7 +1578,7 @@ constexpr int kDkvQ = 0;                                  // Q step buffers
 constexpr int kDkvO = kDkvBufs * kStepTile;               // dO step buffers
 constexpr int kDkvV = 2 * kDkvBufs * kStepTile;           // V rows of the workgroup
 constexpr int kDkvL = kDkvV + kKeysPerWg * kRowB;         // per buffer: 64 LSE values (log2)
-constexpr int kDkvD = kDkvL + kDkvBufs * 256;             // per buffer: 64 D values
+constexpr int kDkvD = kDkvL + kDkvBufs * 256;             // per buffer: 64 -D values
 constexpr int kDkvBytes = kDkvD + kDkvBufs * 256;
 
 // value k of a packed bf16 fragment, as fp32
@@ -1721,7 +1721,7 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
 
   // staging sources: Q and dO rows of every query head (a step selects one
   // head and 32 tokens by the scalar offset; rows past the end read zero),
-  // and the steps' LSE (log2) and D values, 64 per step (the 32 of the step
+  // and the steps' LSE (log2) and -D values, 64 per step (the 32 of the step
   // and 32 that are not used), every wave loading the same values
   const uint32_t q_st_b = 2u * (uint32_t)a.q_st, do_st_b = 2u * (uint32_t)a.do_st;
   const uint32_t q_bytes = (uint32_t)(((int64_t)(a.rows - 1) * a.q_st + (int64_t)(a.hq - 1) * a.q_sh) * 2 + kRowB);
@@ -1756,7 +1756,7 @@ __device__ __forceinline__ void dkv_block(const AttnArgs& a, int g, int kb, int 
     }
   };
   // staging load k (0..kDma-1) of the current step into buffer B: NQL loads
-  // of Q rows, NQL of dO rows (each wave moves 4 rows per load), then LSE, D
+  // of Q rows, NQL of dO rows (each wave moves 4 rows per load), then LSE, -D
   auto stage_load = [&](auto bc, int k) {
     constexpr int B = decltype(bc)::value;
     constexpr int RS = 4 * WAVES;                 // rows one load moves over the group

@@ -370,6 +370,7 @@ __global__ __launch_bounds__(kThreads, 1) void dq_f32_kernel(AttnArgs a) {
       pin_agpr(dov[s]);
     }
   }
+  // -D for the dK/dV pass, which starts from the workspace's negated D
   if (w.tvalid && h == 0) a.neg_dsum[(int64_t)w.head * a.rows + w.tok] = -dsum;
   // LSE in log2 units; rows that see no key (LSE -inf) and rows past the end
   // take +inf, so every P of theirs is zero

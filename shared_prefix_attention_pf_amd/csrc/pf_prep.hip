@@ -6,7 +6,8 @@
 //     accumulation of PrefixFlow §3.1 "Savings over the baseline", an
 //     element-wise O(|P| d) add), and dK/dV of split own key blocks = init +
 //     sum of their partials, converted to the output dtype;
-//   - D = rowsum(dO * O) and LSE in log2 units for the backward passes;
+//   - D = rowsum(dO * O), stored negated, and LSE in log2 units for the
+//     backward passes;
 //   - zero fill and fp32 -> output conversion for Phase C with no upstream.
 #include <math.h>
 
